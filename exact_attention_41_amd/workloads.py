@@ -1,0 +1,148 @@
+"""Seeded synthetic inputs for the attention workloads.
+
+This module only draws random numbers and rounds them to the storage type.
+It holds none of the attention arithmetic, so that both the fp64 oracle (test
+infrastructure) and the HIP path can be fed from it without sharing any of the
+method's code.
+
+Recipe (the same for every workload):
+  * generator ``numpy.random.Generator(PCG64(seed))``;
+  * ``standard_normal(dtype=float32)`` draws, tensor by tensor in the order
+    q, k, v, then dO, each of shape [B, H, N, d] (row-major);
+  * an optional fp32 multiplier on q and k (the sharpened-softmax workload);
+  * one round-to-nearest-even cast to bfloat16 (except fp32 workloads).
+
+The attention problem is the scaled dot-product attention of the
+"FlashAttention" page (systems-analysis.ru), section "Problem of standard
+attention": O = softmax(Q K^T / sqrt(d_k)) V, per batch entry and head.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, Optional
+
+import numpy as np
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: str          # "bf16" or "f32": storage and MFMA operand type
+    causal: bool
+    seed: int
+    qk_mult: float = 1.0
+    backward: bool = False
+    description: str = ""
+
+    @property
+    def scale(self) -> float:
+        """1/sqrt(d) rounded to fp32, the value passed through the C ABI."""
+        return float(np.float32(1.0 / math.sqrt(self.d)))
+
+    def fwd_flops(self) -> float:
+        """Counted forward flops: 4*B*H*N^2*d, halved when causal."""
+        f = 4.0 * self.B * self.H * self.N * self.N * self.d
+        return f / 2.0 if self.causal else f
+
+    def bwd_flops(self) -> float:
+        """Counted backward flops: 2.5x the forward count (five N^2*d GEMMs)."""
+        return 2.5 * self.fwd_flops()
+
+
+# The five synthetic workloads: sizes, value distributions and masks.
+WORKLOADS: Dict[str, Workload] = {
+    w.name: w
+    for w in [
+        Workload("fp32_b1h1n256d64", 1, 1, 256, 64, "f32", False, 1,
+                 description="non-causal fp32 forward, B=1 H=1 N=256 d=64"),
+        Workload("bf16_b8h16n2048d64", 8, 16, 2048, 64, "bf16", False, 2,
+                 description="non-causal bf16 forward, B=8 H=16 N=2048 d=64"),
+        Workload("bf16_b8h16n2048d64_causal", 8, 16, 2048, 64, "bf16", True, 2,
+                 description="causal bf16 forward, same tensors as the non-causal case"),
+        Workload("bf16_b2h32n8192d128_causal_x3", 2, 32, 8192, 128, "bf16", True, 3,
+                 qk_mult=3.0,
+                 description="causal bf16 forward, q and k scaled by 3 (sharp softmax)"),
+        Workload("bf16_b1h16n16384d128_causal", 1, 16, 16384, 128, "bf16", True, 4,
+                 description="long-sequence causal bf16 forward, O(N) extra memory"),
+        Workload("bf16_b4h16n4096d128_causal_bwd", 4, 16, 4096, 128, "bf16", True, 5,
+                 backward=True,
+                 description="causal bf16 forward + backward with upstream dO"),
+    ]
+}
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bfloat16 (ties to even).
+
+    Returns a float32 array whose values are exactly representable in bf16.
+    NaN/Inf are not expected in these inputs.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32).reshape(x.shape)
+
+
+def bf16_bits(x_rounded: np.ndarray) -> np.ndarray:
+    """Upper 16 bits of bf16-representable float32 values (the bf16 storage)."""
+    u = np.ascontiguousarray(x_rounded, dtype=np.float32).view(np.uint32)
+    return (u >> 16).astype(np.uint16)
+
+
+@dataclasses.dataclass
+class Inputs:
+    """Quantised inputs as float32 arrays (values exact in the storage type)."""
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    do: Optional[np.ndarray]
+    dtype: str
+
+    def as_float64(self):
+        out = [self.q.astype(np.float64), self.k.astype(np.float64),
+               self.v.astype(np.float64)]
+        out.append(None if self.do is None else self.do.astype(np.float64))
+        return tuple(out)
+
+
+def make_inputs(B: int, H: int, N: int, d: int, dtype: str, seed: int,
+                qk_mult: float = 1.0, with_do: bool = False) -> Inputs:
+    """Draw q, k, v (and dO) following the recipe in the module docstring."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    shape = (B, H, N, d)
+    q = rng.standard_normal(shape, dtype=np.float32)
+    k = rng.standard_normal(shape, dtype=np.float32)
+    v = rng.standard_normal(shape, dtype=np.float32)
+    do = rng.standard_normal(shape, dtype=np.float32) if with_do else None
+    if qk_mult != 1.0:
+        q = q * np.float32(qk_mult)
+        k = k * np.float32(qk_mult)
+    if dtype == "bf16":
+        q, k, v = bf16_round(q), bf16_round(k), bf16_round(v)
+        if do is not None:
+            do = bf16_round(do)
+    elif dtype != "f32":
+        raise ValueError(f"unknown dtype {dtype!r}")
+    return Inputs(q, k, v, do, dtype)
+
+
+def workload_inputs(w: Workload) -> Inputs:
+    return make_inputs(w.B, w.H, w.N, w.d, w.dtype, w.seed, w.qk_mult,
+                       with_do=w.backward)
+
+
+def to_device(x: np.ndarray, dtype: str, device="cuda"):
+    """Copy a quantised float32 array to a torch tensor of the storage type."""
+    import torch
+    if dtype == "bf16":
+        bits = bf16_bits(x).view(np.int16)
+        t = torch.from_numpy(bits).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(device)

@@ -1,0 +1,363 @@
+"""Pins for the fp64 oracle: each check ties it to something other than itself.
+
+Definition pinned: the "FlashAttention" page (systems-analysis.ru), section
+"Problem of standard attention" (softmax(Q K^T / sqrt(d_k)) V); block-wise
+exactness from its section "Online softmax"; gradients by finite differences
+of the forward (the pages describe no backward).
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import attention as ora
+from oracle import brute
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def _frac(s):
+    return float(Fraction(s))
+
+
+# --------------------------------------------------------------- golden example
+@pytest.mark.parametrize("mask", ["noncausal", "causal"])
+def test_hand_worked_example(mask):
+    g = json.load(open(os.path.join(GOLDEN, "hand_3keys_d1.json")))
+    q, k, v, do = (np.array(g[x], dtype=np.float64)[None, None] for x in ("q", "k", "v", "do"))
+    scale = math.log(2.0)
+    causal = mask == "causal"
+    exp = g[mask]
+    o, lse = ora.attention_fwd(q, k, v, causal, scale)
+    np.testing.assert_allclose(o[0, 0, :, 0], [_frac(x) for x in exp["o"]], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse[0, 0], [math.log(_frac(x)) for x in exp["lse_exp"]],
+                               rtol=0, atol=1e-14)
+    dq, dk, dv = ora.attention_bwd(q, k, v, do, causal, scale)
+    np.testing.assert_allclose(dv[0, 0, :, 0], [_frac(x) for x in exp["dv"]], atol=1e-14)
+    np.testing.assert_allclose(dq[0, 0, :, 0], [_frac(x) * scale for x in exp["dq_over_ln2"]],
+                               atol=1e-14)
+    np.testing.assert_allclose(dk[0, 0, :, 0], [_frac(x) * scale for x in exp["dk_over_ln2"]],
+                               atol=1e-14)
+
+
+# ------------------------------------------------------------------ brute force
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n", [1, 2, 3, 5, 8, 16])
+@pytest.mark.parametrize("d", [1, 2, 4, 8])
+def test_matches_scalar_brute_force(causal, n, d):
+    r = _rng(100 + 7 * n + d)
+    q, k, v = (r.standard_normal((n, d)) for _ in range(3))
+    v = np.concatenate([v, r.standard_normal((n, 3))], axis=1)  # d_v != d_k
+    scale = 1.0 / math.sqrt(d)
+    o, lse = ora.head_fwd(q, k, v, causal, scale)
+    ob, lb = brute.attention(q.tolist(), k.tolist(), v.tolist(), causal, scale)
+    np.testing.assert_allclose(o, np.array(ob), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse, np.array(lb), rtol=0, atol=1e-13)
+
+
+def test_rectangular_keys_brute_force():
+    # More keys than queries, non-causal: catches a transposed operand.
+    r = _rng(5)
+    q, k, v = r.standard_normal((3, 4)), r.standard_normal((7, 4)), r.standard_normal((7, 2))
+    o, lse = ora.head_fwd(q, k, v, False, 0.37)
+    ob, lb = brute.attention(q.tolist(), k.tolist(), v.tolist(), False, 0.37)
+    np.testing.assert_allclose(o, np.array(ob), atol=1e-13)
+    np.testing.assert_allclose(lse, np.array(lb), atol=1e-13)
+
+
+# ----------------------------------------------------------------- closed forms
+def test_single_key_gives_v_and_logit():
+    r = _rng(1)
+    q, k, v = r.standard_normal((1, 8)), r.standard_normal((1, 8)), r.standard_normal((1, 8))
+    for causal in (False, True):
+        o, lse = ora.head_fwd(q, k, v, causal, 0.3)
+        np.testing.assert_allclose(o, v, atol=1e-15)
+        np.testing.assert_allclose(lse, [0.3 * float(q[0] @ k[0])], atol=1e-14)
+
+
+def test_zero_queries_give_means():
+    r = _rng(2)
+    n = 12
+    q = np.zeros((n, 4))
+    k, v = r.standard_normal((n, 4)), r.standard_normal((n, 5))
+    o, lse = ora.head_fwd(q, k, v, False, 0.5)
+    np.testing.assert_allclose(o, np.tile(v.mean(axis=0), (n, 1)), atol=1e-14)
+    np.testing.assert_allclose(lse, np.full(n, math.log(n)), atol=1e-14)
+    o, lse = ora.head_fwd(q, k, v, True, 0.5)
+    prefix = np.cumsum(v, axis=0) / np.arange(1, n + 1)[:, None]
+    np.testing.assert_allclose(o, prefix, atol=1e-14)
+    np.testing.assert_allclose(lse, np.log(np.arange(1, n + 1)), atol=1e-14)
+
+
+def test_causal_first_row_is_first_value():
+    r = _rng(3)
+    q, k, v = (r.standard_normal((9, 6)) for _ in range(3))
+    o, _ = ora.head_fwd(q, k, v, True, 0.4)
+    np.testing.assert_allclose(o[0], v[0], atol=1e-15)
+
+
+def test_dominant_key_selects_its_value():
+    r = _rng(4)
+    n, d = 10, 8
+    q, k, v = (r.standard_normal((n, d)) for _ in range(3))
+    k[6] = 60.0 * q[2] / np.linalg.norm(q[2])   # logit for (2, 6) far above the rest
+    o, _ = ora.head_fwd(q, k, v, False, 1.0)
+    np.testing.assert_allclose(o[2], v[6], atol=1e-6)
+
+
+# ------------------------------------------------------------------- invariants
+@pytest.mark.parametrize("causal", [False, True])
+def test_probability_rows_sum_to_one(causal):
+    r = _rng(6)
+    q, k = r.standard_normal((33, 16)), r.standard_normal((33, 16))
+    p = ora.head_probs(q, k, causal, 0.25)
+    np.testing.assert_allclose(p.sum(axis=1), 1.0, atol=1e-14)
+    assert np.all(p >= 0)
+    if causal:
+        assert np.all(np.triu(p, 1) == 0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_value_invariants(causal):
+    r = _rng(7)
+    n, d = 40, 8
+    q, k, v = (r.standard_normal((n, d)) for _ in range(3))
+    const = np.tile(r.standard_normal(d), (n, 1))
+    o, _ = ora.head_fwd(q, k, const, causal, 0.35)
+    np.testing.assert_allclose(o, const, atol=1e-13)
+    o, _ = ora.head_fwd(q, k, v, causal, 0.35)
+    a, b = 2.5, r.standard_normal(d)
+    o2, _ = ora.head_fwd(q, k, a * v + b, causal, 0.35)
+    np.testing.assert_allclose(o2, a * o + b, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_key_shift_changes_only_lse(causal):
+    r = _rng(8)
+    n, d = 30, 8
+    q, k, v = (r.standard_normal((n, d)) for _ in range(3))
+    u = r.standard_normal(d)
+    o, lse = ora.head_fwd(q, k, v, causal, 0.3)
+    o2, lse2 = ora.head_fwd(q, k + u, v, causal, 0.3)
+    np.testing.assert_allclose(o2, o, atol=1e-13)
+    np.testing.assert_allclose(lse2, lse + 0.3 * (q @ u), atol=1e-12)
+
+
+def test_joint_key_permutation_noncausal():
+    r = _rng(9)
+    n, d = 25, 8
+    q, k, v = (r.standard_normal((n, d)) for _ in range(3))
+    perm = r.permutation(n)
+    o, lse = ora.head_fwd(q, k, v, False, 0.3)
+    o2, lse2 = ora.head_fwd(q, k[perm], v[perm], False, 0.3)
+    np.testing.assert_allclose(o2, o, atol=1e-13)
+    np.testing.assert_allclose(lse2, lse, atol=1e-13)
+
+
+def test_row_blocking_is_invisible(monkeypatch):
+    r = _rng(10)
+    q, k, v = (r.standard_normal((50, 8)) for _ in range(3))
+    o, lse = ora.head_fwd(q, k, v, True, 0.3)
+    monkeypatch.setattr(ora, "ROW_BLOCK", 7)
+    o2, lse2 = ora.head_fwd(q, k, v, True, 0.3)
+    np.testing.assert_allclose(o, o2, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse, lse2, rtol=0, atol=1e-14)
+
+
+def test_selected_rows_and_heads_match_full():
+    r = _rng(11)
+    q, k, v = (r.standard_normal((2, 3, 20, 8)) for _ in range(3))
+    o, lse = ora.attention_fwd(q, k, v, True, 0.3)
+    rows = np.array([0, 5, 19])
+    heads = [(1, 2), (0, 1)]
+    o2, lse2 = ora.attention_fwd(q, k, v, True, 0.3, heads=heads, rows=rows, workers=2)
+    for t, (b, h) in enumerate(heads):
+        np.testing.assert_allclose(o2[t], o[b, h, rows], rtol=0, atol=1e-14)
+        np.testing.assert_allclose(lse2[t], lse[b, h, rows], rtol=0, atol=1e-14)
+
+
+# ------------------------------------------------------- online softmax model
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("trial", range(6))
+def test_block_split_equals_one_shot(causal, trial):
+    r = _rng(200 + trial)
+    n = 48
+    q, k, v = (3.0 * r.standard_normal((n, 16)) for _ in range(3))
+    o, lse = ora.head_fwd(q, k, v, causal, 0.25)
+    if trial == 0:
+        cuts = []                                  # one block
+    elif trial == 1:
+        cuts = list(range(1, n))                   # n blocks of one key
+    else:
+        cuts = sorted(r.choice(np.arange(1, n), size=int(r.integers(1, 12)), replace=False))
+    o2, lse2 = ora.online_softmax_attention(q, k, v, causal, 0.25, cuts)
+    np.testing.assert_allclose(o2, o, atol=1e-12)
+    np.testing.assert_allclose(lse2, lse, atol=1e-12)
+
+
+# ------------------------------------------------------------------- backward
+def _fd_check(causal, seed):
+    r = _rng(seed)
+    n, d = 9, 4
+    q, k, v, do = (r.standard_normal((n, d)) for _ in range(4))
+    scale = 0.6
+    dq, dk, dv = ora.head_bwd(q, k, v, do, causal, scale)
+
+    def loss(qq, kk, vv):
+        o, _ = ora.head_fwd(qq, kk, vv, causal, scale)
+        return float(np.sum(o * do))
+
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        idx = [(i, c) for i in range(n) for c in range(d)]
+        for (i, c) in idx:
+            xp, xm = x.copy(), x.copy()
+            xp[i, c] += h
+            xm[i, c] -= h
+            args_p = {"q": q, "k": k, "v": v}
+            args_m = dict(args_p)
+            args_p[name], args_m[name] = xp, xm
+            fd = (loss(args_p["q"], args_p["k"], args_p["v"])
+                  - loss(args_m["q"], args_m["k"], args_m["v"])) / (2 * h)
+            assert abs(fd - g[i, c]) <= 1e-6 * max(1.0, abs(g[i, c])), (name, i, c, fd, g[i, c])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gradients_match_finite_differences(causal):
+    _fd_check(causal, 300 + int(causal))
+
+
+def test_gradient_against_scalar_brute_force_loss():
+    # Central differences of the pure-Python loss pin dQ/dK/dV independently
+    # of the numpy forward as well.
+    r = _rng(12)
+    n, d = 5, 3
+    q, k, v, do = (r.standard_normal((n, d)) for _ in range(4))
+    scale = 0.7
+    dq, dk, dv = ora.head_bwd(q, k, v, do, True, scale)
+    h = 1e-6
+    for x, g in ((q, dq), (k, dk), (v, dv)):
+        for (i, c) in [(0, 0), (2, 1), (4, 2), (3, 0)]:
+            xp, xm = x.copy(), x.copy()
+            xp[i, c] += h
+            xm[i, c] -= h
+            def L(z):
+                qq, kk, vv = (z if x is q else q), (z if x is k else k), (z if x is v else v)
+                return brute.loss(qq.tolist(), kk.tolist(), vv.tolist(), do.tolist(), True, scale)
+            fd = (L(xp) - L(xm)) / (2 * h)
+            assert abs(fd - g[i, c]) <= 1e-6 * max(1.0, abs(g[i, c]))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_invariants(causal):
+    r = _rng(13)
+    n, d = 37, 8
+    q, k, v, do = (r.standard_normal((n, d)) for _ in range(4))
+    dq, dk, dv = ora.head_bwd(q, k, v, do, causal, 0.3)
+    np.testing.assert_allclose(dk.sum(axis=0), 0.0, atol=1e-12)
+    np.testing.assert_allclose(dv.sum(axis=0), do.sum(axis=0), atol=1e-12)
+    u = r.standard_normal(d)
+    dq2, _, _ = ora.head_bwd(q, k + u, v, do, causal, 0.3)
+    np.testing.assert_allclose(dq2, dq, atol=1e-12)
+
+
+def test_backward_row_blocking_is_invisible(monkeypatch):
+    r = _rng(14)
+    q, k, v, do = (r.standard_normal((30, 4)) for _ in range(4))
+    ref = ora.head_bwd(q, k, v, do, True, 0.5)
+    monkeypatch.setattr(ora, "ROW_BLOCK", 4)
+    got = ora.head_bwd(q, k, v, do, True, 0.5)
+    for a, b in zip(ref, got):
+        np.testing.assert_allclose(a, b, atol=1e-13)
+
+
+# ------------------------------------------------- library special case (torch)
+@pytest.mark.parametrize("causal", [False, True])
+def test_against_torch_float64_sdpa_and_autograd(causal):
+    torch = pytest.importorskip("torch")
+    r = _rng(15)
+    B, H, N, d = 2, 2, 19, 8
+    q, k, v, do = (r.standard_normal((B, H, N, d)) for _ in range(4))
+    scale = 1.0 / math.sqrt(d)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    to = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=scale)
+    to.backward(torch.tensor(do))
+    o, _ = ora.attention_fwd(q, k, v, causal, scale)
+    dq, dk, dv = ora.attention_bwd(q, k, v, do, causal, scale)
+    np.testing.assert_allclose(o, to.detach().numpy(), atol=1e-12)
+    np.testing.assert_allclose(dq, tq.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), atol=1e-12)
+
+
+# ------------------------------------------------------ planted-mistake checks
+def _brute_mismatch():
+    r = _rng(16)
+    q, k, v = r.standard_normal((6, 3)), r.standard_normal((6, 3)), r.standard_normal((6, 2))
+    try:
+        o, lse = ora.head_fwd(q, k, v, True, 0.8)
+    except Exception:
+        return True
+    ob, lb = brute.attention(q.tolist(), k.tolist(), v.tolist(), True, 0.8)
+    return not (np.allclose(o, ob, atol=1e-12) and np.allclose(lse, lb, atol=1e-12))
+
+
+@pytest.mark.parametrize("mutation", ["no_scale", "no_mask", "mask_upper", "transpose_k",
+                                      "lse_without_max"])
+def test_pins_catch_planted_forward_mistakes(monkeypatch, mutation):
+    orig_scores, orig_softmax = ora._scores, ora._softmax_rows
+
+    def scores(q_rows, k, rows, causal, scale):
+        if mutation == "no_scale":
+            return orig_scores(q_rows, k, rows, causal, 1.0)
+        if mutation == "no_mask":
+            return orig_scores(q_rows, k, rows, False, scale)
+        if mutation == "mask_upper":
+            s = scale * (q_rows @ k.T)
+            j = np.arange(k.shape[0])
+            return np.where(j[None, :] < rows[:, None], -np.inf, s)
+        if mutation == "transpose_k":
+            return orig_scores(q_rows, k[::-1], rows, causal, scale)
+        return orig_scores(q_rows, k, rows, causal, scale)
+
+    def softmax(s):
+        p, lse = orig_softmax(s)
+        if mutation == "lse_without_max":
+            m = np.max(s, axis=1)
+            lse = lse - m
+        return p, lse
+
+    monkeypatch.setattr(ora, "_scores", scores)
+    monkeypatch.setattr(ora, "_softmax_rows", softmax)
+    assert _brute_mismatch()
+
+
+@pytest.mark.parametrize("mutation", ["no_D", "dk_unscaled", "dv_not_transposed", "ds_sign"])
+def test_pins_catch_planted_backward_mistakes(monkeypatch, mutation):
+    orig = ora.head_bwd
+
+    def head_bwd(q, k, v, do, causal, scale):
+        dq, dk, dv = orig(q, k, v, do, causal, scale)
+        if mutation == "no_D":
+            p = ora.head_probs(q, k, causal, scale)
+            ds = p * (do @ v.T)
+            dq = scale * ds @ k
+        elif mutation == "dk_unscaled":
+            dk = dk / scale
+        elif mutation == "dv_not_transposed":
+            p = ora.head_probs(q, k, causal, scale)
+            dv = p @ do
+        elif mutation == "ds_sign":
+            dq = -dq
+        return dq, dk, dv
+
+    monkeypatch.setattr(ora, "head_bwd", head_bwd)
+    with pytest.raises(AssertionError):
+        _fd_check(True, 301)

@@ -1,0 +1,43 @@
+"""Seeded input generation: determinism, shapes and the bf16 rounding rule."""
+import numpy as np
+import pytest
+
+from exact_attention_41_amd import workloads as wl
+
+
+def test_bf16_round_is_round_to_nearest_even():
+    torch = pytest.importorskip("torch")
+    r = np.random.Generator(np.random.PCG64(0))
+    x = r.standard_normal(100000, dtype=np.float32) * np.float32(7.0)
+    # exact ties: the low 16 bits are 0x8000
+    ties = (np.arange(1, 2001, dtype=np.uint32) << 16 | np.uint32(0x8000)).view(np.float32)
+    x = np.concatenate([x, ties, -ties, np.float32([0.0, -0.0, 1.0, 65504.0])])
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    np.testing.assert_array_equal(wl.bf16_round(x), ref)
+
+
+def test_inputs_are_seeded_and_quantised():
+    a = wl.make_inputs(1, 2, 16, 8, "bf16", seed=3, with_do=True)
+    b = wl.make_inputs(1, 2, 16, 8, "bf16", seed=3, with_do=True)
+    for x, y in zip((a.q, a.k, a.v, a.do), (b.q, b.k, b.v, b.do)):
+        np.testing.assert_array_equal(x, y)
+        assert x.shape == (1, 2, 16, 8)
+        np.testing.assert_array_equal(wl.bf16_round(x), x)
+    c = wl.make_inputs(1, 2, 16, 8, "bf16", seed=4)
+    assert not np.array_equal(a.q, c.q)
+    assert c.do is None
+
+
+def test_qk_multiplier_applies_before_rounding():
+    raw = wl.make_inputs(1, 1, 8, 4, "f32", seed=9)
+    x3 = wl.make_inputs(1, 1, 8, 4, "bf16", seed=9, qk_mult=3.0)
+    np.testing.assert_array_equal(x3.q, wl.bf16_round(raw.q * np.float32(3)))
+    np.testing.assert_array_equal(x3.v, wl.bf16_round(raw.v))
+
+
+def test_workload_registry():
+    w = wl.WORKLOADS["bf16_b4h16n4096d128_causal_bwd"]
+    assert (w.B, w.H, w.N, w.d, w.causal, w.backward) == (4, 16, 4096, 128, True, True)
+    assert w.fwd_flops() == 4 * 4 * 16 * 4096 ** 2 * 128 / 2
+    assert w.bwd_flops() == 2.5 * w.fwd_flops()
+    assert wl.WORKLOADS["bf16_b8h16n2048d64"].scale == 0.125
