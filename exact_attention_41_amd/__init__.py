@@ -1,0 +1,138 @@
+"""MI355X (gfx950) fused exact attention: thin Python binding of libfa.so.
+
+The functions below carry the names of the C entry points in include/fa.h and
+only marshal torch tensors (device memory and the current stream) into those
+calls; every step of the computation runs in the HIP kernels of libfa.so.
+If the library is not built, every call raises: there is no fallback.
+
+    o, lse = fa_fwd(q, k, v, causal=True)                  # bf16 [B,H,N,d]
+    o, lse = fa_fwd_f32(q, k, v, causal=False)             # fp32 [B,H,N,d]
+    dq, dk, dv = fa_bwd(q, k, v, o, do, lse, causal=True)  # bf16
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Tuple
+
+from . import _lib
+
+__all__ = ["fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_bwd_workspace_size", "fa_status_str",
+           "FAError", "library_path"]
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where} failed: {fa_status_str(status)}")
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+def fa_status_str(status: int) -> str:
+    return _lib.load().fa_status_str(int(status)).decode()
+
+
+def fa_bwd_workspace_size(B: int, H: int, N: int, d: int) -> int:
+    return int(_lib.load().fa_bwd_workspace_size(B, H, N, d))
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _check(t, name, dtype, shape=None, device=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _stream_ptr(device):
+    return _torch().cuda.current_stream(device).cuda_stream
+
+
+def _scale(scale, d):
+    return 1.0 / math.sqrt(d) if scale is None else float(scale)
+
+
+def _fwd(entry, dtype, q, k, v, causal, scale, out, lse):
+    torch = _torch()
+    _check(q, "q", dtype)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    _check(k, "k", dtype, q.shape, q.device)
+    _check(v, "v", dtype, q.shape, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check(out, "out", dtype, q.shape, q.device)
+    _check(lse, "lse", torch.float32, (B, H, N), q.device)
+    fn = getattr(_lib.load(), entry)
+    with torch.cuda.device(q.device):
+        st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                B, H, N, d, int(bool(causal)), _scale(scale, d), _stream_ptr(q.device))
+    if st != _lib.FA_OK:
+        raise FAError(st, entry)
+    return out, lse
+
+
+def fa_fwd(q, k, v, causal: bool = False, scale: Optional[float] = None,
+           out=None, lse=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
+    """bf16 forward: returns (O, logsumexp). Calls fa_fwd of libfa.so."""
+    return _fwd("fa_fwd", _torch().bfloat16, q, k, v, causal, scale, out, lse)
+
+
+def fa_fwd_f32(q, k, v, causal: bool = False, scale: Optional[float] = None,
+               out=None, lse=None):
+    """fp32 forward: returns (O, logsumexp). Calls fa_fwd_f32 of libfa.so."""
+    return _fwd("fa_fwd_f32", _torch().float32, q, k, v, causal, scale, out, lse)
+
+
+def fa_bwd(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = None,
+           dq=None, dk=None, dv=None, workspace=None):
+    """bf16 backward: returns (dQ, dK, dV). Calls fa_bwd of libfa.so.
+
+    ``workspace`` may be a uint8 device tensor of at least
+    fa_bwd_workspace_size(B, H, N, d) bytes; one is allocated otherwise.
+    """
+    torch = _torch()
+    bf = torch.bfloat16
+    _check(q, "q", bf)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    for t, n in ((k, "k"), (v, "v"), (o, "o"), (do, "do")):
+        _check(t, n, bf, q.shape, q.device)
+    _check(lse, "lse", torch.float32, (B, H, N), q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _check(t, n, bf, q.shape, q.device)
+    need = fa_bwd_workspace_size(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    lib = _lib.load()
+    with torch.cuda.device(q.device):
+        st = lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                        lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                        workspace.data_ptr(), ws_bytes, B, H, N, d, int(bool(causal)),
+                        _scale(scale, d), _stream_ptr(q.device))
+    if st != _lib.FA_OK:
+        raise FAError(st, "fa_bwd")
+    return dq, dk, dv

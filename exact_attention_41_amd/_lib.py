@@ -1,0 +1,48 @@
+"""ctypes loader for libfa.so and the raw C signatures declared in include/fa.h."""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+FA_OK = 0
+STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_INVALID_ARG", 2: "FA_ERR_UNSUPPORTED",
+                3: "FA_ERR_WORKSPACE", 4: "FA_ERR_HIP"}
+
+EXPORTED = ("fa_status_str", "fa_fwd", "fa_fwd_f32", "fa_bwd_workspace_size", "fa_bwd")
+
+_lock = threading.Lock()
+_lib = None
+
+
+class LibraryMissing(RuntimeError):
+    pass
+
+
+def load() -> ctypes.CDLL:
+    """Load libfa.so once; raise loudly if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise LibraryMissing(
+                f"{LIB_PATH} is not built; run `python -m exact_attention_41_amd.build` "
+                "(or __graft_entry__.build()). There is no fallback path.")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        lib.fa_status_str.argtypes = [i]
+        lib.fa_status_str.restype = ctypes.c_char_p
+        lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+        lib.fa_fwd.restype = i
+        lib.fa_fwd_f32.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+        lib.fa_fwd_f32.restype = i
+        lib.fa_bwd_workspace_size.argtypes = [i, i, i, i]
+        lib.fa_bwd_workspace_size.restype = ctypes.c_size_t
+        lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                               i, i, i, i, i, f, vp]
+        lib.fa_bwd.restype = i
+        _lib = lib
+        return lib

@@ -1,0 +1,128 @@
+// C-ABI entry points of libfa.so: argument validation, then kernel launch.
+// Every check happens before anything is enqueued, so an error status means
+// no work was launched.
+#include <math.h>
+#include <stdint.h>
+
+#include "fa.h"
+#include "fa_kernels.hpp"
+
+namespace {
+
+constexpr int kMaxN = 1 << 26;
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Shared size/scale checks. Returns FA_OK and sets *empty when B*H*N == 0.
+fa_status_t check_common(int B, int H, int N, int d, float scale, bool* empty) {
+    if (B < 0 || H < 0 || N < 0) return FA_ERR_INVALID_ARG;
+    if (!isfinite(scale) || scale < 0.f) return FA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    *empty = (B == 0 || H == 0 || N == 0);
+    if (*empty) return FA_OK;
+    if (N > kMaxN) return FA_ERR_UNSUPPORTED;
+    // Grid = (query blocks of >= 32 rows) x B x H must fit a 32-bit grid.
+    const long long bh = (long long)B * (long long)H;
+    const long long blocks = bh * (((long long)N + 31) / 32);
+    if (bh > (1LL << 30) || blocks > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+    return FA_OK;
+}
+
+fa_status_t check_tensor(const void* p) {
+    if (!p) return FA_ERR_INVALID_ARG;
+    if (!aligned(p, 16)) return FA_ERR_UNSUPPORTED;
+    return FA_OK;
+}
+
+fa_status_t check_lse(const void* p) {
+    if (!p) return FA_ERR_INVALID_ARG;
+    if (!aligned(p, 4)) return FA_ERR_UNSUPPORTED;
+    return FA_OK;
+}
+
+#define FA_TRY(expr)                       \
+    do {                                   \
+        fa_status_t st_ = (expr);          \
+        if (st_ != FA_OK) return st_;      \
+    } while (0)
+
+fa_status_t check_fwd(const void* q, const void* k, const void* v, const void* o,
+                      const void* lse, int B, int H, int N, int d, float scale, bool* empty) {
+    FA_TRY(check_common(B, H, N, d, scale, empty));
+    if (*empty) return FA_OK;
+    // Null pointers are argument errors, checked before alignment.
+    if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+    FA_TRY(check_tensor(q));
+    FA_TRY(check_tensor(k));
+    FA_TRY(check_tensor(v));
+    FA_TRY(check_tensor(o));
+    FA_TRY(check_lse(lse));
+    return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_str(fa_status_t status) {
+    switch (status) {
+        case FA_OK: return "FA_OK";
+        case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG";
+        case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
+        case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE";
+        case FA_ERR_HIP: return "FA_ERR_HIP";
+    }
+    return "FA_ERR_UNKNOWN";
+}
+
+fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int N, int d, int causal, float scale, hipStream_t stream) {
+    bool empty = false;
+    FA_TRY(check_fwd(q, k, v, o, lse, B, H, N, d, scale, &empty));
+    if (empty) return FA_OK;
+    fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, causal != 0, scale, stream};
+    return fa::launch_fwd_bf16(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status_t fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                       int B, int H, int N, int d, int causal, float scale, hipStream_t stream) {
+    bool empty = false;
+    FA_TRY(check_fwd(q, k, v, o, lse, B, H, N, d, scale, &empty));
+    if (empty) return FA_OK;
+    fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, causal != 0, scale, stream};
+    return fa::launch_fwd_f32(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
+    (void)d;
+    if (B <= 0 || H <= 0 || N <= 0) return 0;
+    const size_t rows = (size_t)B * (size_t)H * (size_t)N;
+    return ((rows * sizeof(float) + 255) / 256) * 256;
+}
+
+fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o,
+                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                   void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                   int causal, float scale, hipStream_t stream) {
+    bool empty = false;
+    FA_TRY(check_common(B, H, N, d, scale, &empty));
+    if (empty) return FA_OK;
+    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
+    FA_TRY(check_tensor(q));
+    FA_TRY(check_tensor(k));
+    FA_TRY(check_tensor(v));
+    FA_TRY(check_tensor(o));
+    FA_TRY(check_tensor(dout));
+    FA_TRY(check_lse(lse));
+    FA_TRY(check_tensor(dq));
+    FA_TRY(check_tensor(dk));
+    FA_TRY(check_tensor(dv));
+    if (!workspace || !aligned(workspace, 16) ||
+        workspace_bytes < fa_bwd_workspace_size(B, H, N, d))
+        return FA_ERR_WORKSPACE;
+    fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace,
+                  B, H, N, d, causal != 0, scale, stream};
+    return fa::launch_bwd_bf16(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,124 @@
+/*
+ * fa.h - C ABI of the MI355X (gfx950) exact-attention library libfa.so.
+ *
+ * The operation is exact scaled dot-product attention, defined on the
+ * "FlashAttention" page (systems-analysis.ru), section "Problem of standard
+ * attention":  O = softmax(scale * Q K^T) V  per batch entry b and head h,
+ * with scale = 1/sqrt(d) in the usual case. The library computes it in one
+ * fused, tiled kernel with a block-wise ("online") softmax (same page,
+ * sections "Tiling", "Online softmax" and "Fusing into one CUDA kernel"), so
+ * the N x N score matrix is never written to memory and the only extra output
+ * is one logsumexp value per query row (O(N) memory, section "Complexity and
+ * optimality"). The backward recomputes the probabilities from that
+ * logsumexp.
+ *
+ * Common conventions for every entry point:
+ *   Layout     q, k, v, o, dout, dq, dk, dv are contiguous row-major
+ *              [B][H][N][d] arrays (element (b,h,i,c) at ((b*H+h)*N+i)*d+c);
+ *              lse is a contiguous [B][H][N] float array.
+ *   Memory     every pointer is a DEVICE pointer on the current HIP device.
+ *              The caller allocates and owns every buffer, including the
+ *              backward workspace; the library never allocates or frees
+ *              memory and keeps no mutable global state, so calls are
+ *              re-entrant and thread-safe.
+ *   Alignment  tensor pointers must be 16-byte aligned, lse 4-byte aligned.
+ *   Masking    causal != 0 keeps key j for query i only when j <= i (square,
+ *              top-left aligned); causal == 0 keeps every key.
+ *   Scale      any finite scale >= 0 (1/sqrt(d) for the standard attention).
+ *   Sizes      B, H, N >= 0; if any of them is 0 the call does nothing and
+ *              returns FA_OK. N may be any positive value (no multiple of a
+ *              tile size is required). d must be 64 or 128.
+ *   Async      work is enqueued on `stream` (0 = the null stream) and the call
+ *              returns; results are valid once the stream has synchronised.
+ *   Errors     every argument is checked before anything is enqueued, so on
+ *              an error status nothing has been launched:
+ *                FA_ERR_INVALID_ARG  null pointer with non-empty sizes,
+ *                                    negative size, non-finite or negative
+ *                                    scale;
+ *                FA_ERR_UNSUPPORTED  d not 64/128, misaligned pointer, or a
+ *                                    size whose index arithmetic would
+ *                                    overflow (grid or N beyond 2^26);
+ *                FA_ERR_WORKSPACE    backward workspace too small or null;
+ *                FA_ERR_HIP          the HIP runtime refused the launch.
+ *   Aliasing   outputs must not overlap inputs or each other.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same definition as the HIP runtime header (a typedef may be repeated). */
+typedef struct ihipStream_t* hipStream_t;
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_INVALID_ARG = 1,
+    FA_ERR_UNSUPPORTED = 2,
+    FA_ERR_WORKSPACE = 3,
+    FA_ERR_HIP = 4
+} fa_status_t;
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* fa_status_str(fa_status_t status);
+
+/*
+ * Forward, bfloat16 storage.
+ *   q, k, v  (in)  bf16 [B][H][N][d].
+ *   o        (out) bf16 [B][H][N][d]: O = P V with P = softmax(scale Q K^T)
+ *                  (masked when causal), rounded to nearest even once.
+ *   lse      (out) fp32 [B][H][N]: natural-log logsumexp of the scaled,
+ *                  masked logits of each query row, ln sum_j exp(scale q_i.k_j);
+ *                  the backward consumes it.
+ * Products run on bf16 MFMA with fp32 accumulation; the softmax statistics,
+ * probabilities and the output accumulator are fp32; P is rounded to bf16
+ * only as the operand of the P V product.
+ */
+fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int N, int d, int causal, float scale,
+                   hipStream_t stream);
+
+/*
+ * Forward, fp32 storage and fp32 arithmetic throughout (no reduced-precision
+ * operands). Same layout, masking, outputs and errors as fa_fwd.
+ */
+fa_status_t fa_fwd_f32(const float* q, const float* k, const float* v, float* o,
+                       float* lse, int B, int H, int N, int d, int causal,
+                       float scale, hipStream_t stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs for these sizes (0 if a size is
+ * negative or the problem is empty). The workspace holds one fp32 value per
+ * query row, D_i = sum_c dO_ic O_ic, so it is O(B*H*N).
+ */
+size_t fa_bwd_workspace_size(int B, int H, int N, int d);
+
+/*
+ * Backward, bfloat16 storage: the gradients of the scalar
+ * L = sum_{b,h,i,c} O_bhic dO_bhic with respect to q, k and v.
+ *   q, k, v   (in)  bf16 [B][H][N][d], the forward inputs.
+ *   o         (in)  bf16 [B][H][N][d], the forward output.
+ *   dout      (in)  bf16 [B][H][N][d], dL/dO.
+ *   lse       (in)  fp32 [B][H][N], the forward's logsumexp.
+ *   dq,dk,dv  (out) bf16 [B][H][N][d].
+ *   workspace (scratch) device buffer of at least
+ *             fa_bwd_workspace_size(B, H, N, d) bytes, 16-byte aligned; its
+ *             contents on entry do not matter and are clobbered.
+ * P is recomputed from lse, never stored. The result is deterministic: no
+ * floating-point atomics are used, so repeated calls give identical bits.
+ * causal, scale and the remaining conventions must match the forward call.
+ */
+fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o,
+                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                   void* workspace, size_t workspace_bytes,
+                   int B, int H, int N, int d, int causal, float scale,
+                   hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -118,6 +118,22 @@ def head_bwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
     return dq, dk, dv
 
 
+def head_dq_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
+                 causal: bool, scale: float, rows: np.ndarray) -> np.ndarray:
+    """dQ of selected query rows of one head (the backward formulas above,
+    restricted to those rows: row i of dQ only needs row i of P and dP)."""
+    rows = np.asarray(rows)
+    dq = np.zeros((len(rows), q.shape[1]))
+    for r0 in range(0, len(rows), ROW_BLOCK):
+        rr = rows[r0:r0 + ROW_BLOCK]
+        p, _ = _softmax_rows(_scores(q[rr], k, rr, causal, scale))
+        dp = do[rr] @ v.T
+        dsum = np.sum(p * dp, axis=1)
+        ds = p * (dp - dsum[:, None])
+        dq[r0:r0 + len(rr)] = scale * (ds @ k)
+    return dq
+
+
 def _heads(B: int, H: int, heads: Optional[Iterable[Tuple[int, int]]]):
     return [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
 

@@ -361,3 +361,13 @@ def test_pins_catch_planted_backward_mistakes(monkeypatch, mutation):
     monkeypatch.setattr(ora, "head_bwd", head_bwd)
     with pytest.raises(AssertionError):
         _fd_check(True, 301)
+
+
+def test_dq_rows_match_full_backward():
+    r = _rng(17)
+    q, k, v, do = (r.standard_normal((40, 8)) for _ in range(4))
+    rows = np.array([0, 3, 17, 39])
+    for causal in (False, True):
+        dq, _, _ = ora.head_bwd(q, k, v, do, causal, 0.4)
+        np.testing.assert_allclose(ora.head_dq_rows(q, k, v, do, causal, 0.4, rows), dq[rows],
+                                   rtol=0, atol=1e-13)

@@ -1,0 +1,102 @@
+"""Backward parity: fa_bwd (through the C ABI) against the fp64 oracle.
+
+The GPU backward consumes the GPU forward's O and logsumexp, as a caller
+would; the oracle computes the exact gradients of sum(O * dO) from q, k, v
+and dO alone. One isolation case feeds the GPU backward the oracle's own O
+(rounded to bf16) and logsumexp (rounded to fp32) instead.
+"""
+import numpy as np
+import pytest
+
+from exact_attention_41_amd import workloads as wl
+from oracle import attention as ora
+from parity_util import check_bf16, sample_rows, say, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    import exact_attention_41_amd as fa
+    from exact_attention_41_amd import _lib
+    _lib.load()
+    return fa
+
+
+def _gpu_fwd_bwd(fa, inp, causal, scale):
+    import torch
+    q, k, v, do = (wl.to_device(x, "bf16") for x in (inp.q, inp.k, inp.v, inp.do))
+    o, lse = fa.fa_fwd(q, k, v, causal=causal, scale=scale)
+    dq, dk, dv = fa.fa_bwd(q, k, v, o, do, lse, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+SMALL = [(1, 1, 1, 64), (1, 1, 40, 128), (2, 2, 64, 64), (1, 2, 129, 128), (2, 1, 300, 64),
+         (1, 2, 300, 128), (1, 1, 700, 128)]
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("B,H,N,d", SMALL)
+def test_bf16_backward_small(fa, B, H, N, d, causal):
+    say(f"fa_bwd bf16 B={B} H={H} N={N} d={d} causal={causal} seed=21")
+    inp = wl.make_inputs(B, H, N, d, "bf16", seed=21, with_do=True)
+    scale = float(np.float32(1 / np.sqrt(d)))
+    dq, dk, dv = _gpu_fwd_bwd(fa, inp, causal, scale)
+    q64, k64, v64, do64 = inp.as_float64()
+    rq, rk, rv = ora.attention_bwd(q64, k64, v64, do64, causal, scale, workers=None)
+    check_bf16("dQ", to_np(dq), rq)
+    check_bf16("dK", to_np(dk), rk)
+    check_bf16("dV", to_np(dv), rv)
+
+
+def test_bf16_backward_with_oracle_forward_outputs(fa):
+    """Isolation: the backward fed the oracle's O (bf16) and lse (fp32)."""
+    import torch
+    B, H, N, d, causal = 1, 2, 200, 128, True
+    say(f"fa_bwd isolation B={B} H={H} N={N} d={d} causal={causal} seed=22")
+    inp = wl.make_inputs(B, H, N, d, "bf16", seed=22, with_do=True)
+    scale = float(np.float32(1 / np.sqrt(d)))
+    q64, k64, v64, do64 = inp.as_float64()
+    ro, rl = ora.attention_fwd(q64, k64, v64, causal, scale)
+    q, k, v, do = (wl.to_device(x, "bf16") for x in (inp.q, inp.k, inp.v, inp.do))
+    o = wl.to_device(wl.bf16_round(ro.astype(np.float32)), "bf16")
+    lse = torch.from_numpy(rl.astype(np.float32)).cuda()
+    dq, dk, dv = fa.fa_bwd(q, k, v, o, do, lse, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    rq, rk, rv = ora.attention_bwd(q64, k64, v64, do64, causal, scale)
+    check_bf16("dQ", to_np(dq), rq)
+    check_bf16("dK", to_np(dk), rk)
+    check_bf16("dV", to_np(dv), rv)
+
+
+def test_bf16_backward_workload(fa):
+    """Causal fwd+bwd, B=4 H=16 N=4096 d=128: four whole heads element by
+    element, plus dQ on sampled rows of every head."""
+    w = wl.WORKLOADS["bf16_b4h16n4096d128_causal_bwd"]
+    say(f"fa_bwd workload {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} seed={w.seed}")
+    inp = wl.workload_inputs(w)
+    dq, dk, dv = _gpu_fwd_bwd(fa, inp, w.causal, w.scale)
+    gq, gk, gv = (to_np(x).reshape(w.B * w.H, w.N, w.d) for x in (dq, dk, dv))
+    q64, k64, v64, do64 = (x.astype(np.float64) for x in (inp.q, inp.k, inp.v, inp.do))
+    heads = [(0, 0), (1, 7), (2, 12), (3, 15)]
+    rq, rk, rv = ora.attention_bwd(q64, k64, v64, do64, w.causal, w.scale, heads=heads,
+                                   workers=None)
+    idx = [b * w.H + h for b, h in heads]
+    check_bf16("dQ (4 heads)", gq[idx], rq)
+    check_bf16("dK (4 heads)", gk[idx], rk)
+    check_bf16("dV (4 heads)", gv[idx], rv)
+    rows = sample_rows(w.N, 48, seed=w.seed)
+    import concurrent.futures as cf
+    pairs = [(b, h) for b in range(w.B) for h in range(w.H)]
+
+    def one(bh):
+        b, h = bh
+        return ora.head_dq_rows(q64[b, h], k64[b, h], v64[b, h], do64[b, h], w.causal,
+                                w.scale, rows)
+
+    with cf.ThreadPoolExecutor(8) as ex:
+        ref = np.stack(list(ex.map(one, pairs)))
+    check_bf16("dQ (sampled rows, all heads)", gq[:, rows], ref)
