@@ -1,0 +1,266 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused exact-attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of seeded synthetic
+input: the fused forward (fa_fwd) and the backward (fa_bwd's three phases:
+per-head scale factors, dQ with D, dK/dV) on the causal bf16 workload B=4 H=16 N=4096
+d=128 with upstream gradient dO. ``value`` is counted TFLOP/s of that step,
+with the counted flops 4*B*H*N^2*d (halved for causal) for the forward and
+2.5x that for the backward. Inputs are resident in HBM before timing starts.
+
+Prints exactly one JSON line (on rank 0). Options:
+  --gpus N        only N=1 is meaningful: this path runs on one GPU
+  --steps K       timed steps (default 20)
+  --warmup W      untimed warm-up steps (default 5)
+  --no-sweep      skip the forward-only timing of the other workloads
+  --no-cpu        skip the CPU oracle baseline
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd/bwd TFLOP/s and % of bf16 MFMA peak at N=2k–16k, d=64/128"
+# MI355X dense bf16 MFMA: 256 CUs x 4096 flop/clk x 2.4 GHz (AMD's 2.5 PFLOP/s).
+PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
+HEADLINE = "bf16_b4h16n4096d128_causal_bwd"
+SWEEP = ["bf16_b8h16n2048d64", "bf16_b8h16n2048d64_causal", "bf16_b2h32n8192d128_causal_x3",
+         "bf16_b1h16n16384d128_causal", "bf16_b4h16n4096d128_causal_bwd"]
+KERNEL_SOURCES = ["fa_device.hpp", "fa_kernels.hpp", "fa_fwd.hip", "fa_bwd.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "exact_attention_41_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+def gpu_step_timing(w, steps: int, warmup: int):
+    import torch
+
+    import exact_attention_41_amd as fa
+    from exact_attention_41_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    inp = wl.workload_inputs(w)
+    q, k, v, do = (wl.to_device(x, "bf16", dev) for x in (inp.q, inp.k, inp.v, inp.do))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty(fa.fa_bwd_workspace_size(w.B, w.H, w.N, w.d), dtype=torch.uint8, device=dev)
+    names = ["fwd", "bwd_preprocess", "bwd_dq", "bwd_dkdv"]
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        fa.fa_fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+        if ev is not None:
+            ev[1].record()
+        fa.fa_bwd_preprocess(q, k, v, do, ws)
+        if ev is not None:
+            ev[2].record()
+        fa.fa_bwd_dq(q, k, v, do, lse, ws, dq, causal=w.causal, scale=w.scale)
+        if ev is not None:
+            ev[3].record()
+        fa.fa_bwd_dkdv(k, v, lse, ws, dk, dv, causal=w.causal, scale=w.scale)
+        if ev is not None:
+            ev[4].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for s in range(steps):
+        step(events[s])
+    torch.cuda.synchronize(dev)
+    t1 = time.perf_counter()
+    per_kernel = {n: 0.0 for n in names}
+    for ev in events:
+        for i, n in enumerate(names):
+            per_kernel[n] += ev[i].elapsed_time(ev[i + 1])
+    per_kernel = {n: t / steps for n, t in per_kernel.items()}
+    ms_per_step = (t1 - t0) * 1000.0 / steps
+    return ms_per_step, per_kernel
+
+
+def gpu_forward_sweep(names, iters=10, warmup=3):
+    import torch
+
+    import exact_attention_41_amd as fa
+    from exact_attention_41_amd import workloads as wl
+
+    out = []
+    dev = torch.device("cuda:0")
+    for name in names:
+        w = wl.WORKLOADS[name]
+        inp = wl.make_inputs(w.B, w.H, w.N, w.d, "bf16", w.seed, w.qk_mult)
+        q, k, v = (wl.to_device(x, "bf16", dev) for x in (inp.q, inp.k, inp.v))
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+        for _ in range(warmup):
+            fa.fa_fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
+        times = []
+        for i in range(iters):
+            ev[i].record()
+            fa.fa_fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+            ev[i + 1].record()
+        torch.cuda.synchronize(dev)
+        times = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(iters))
+        med = times[len(times) // 2]
+        tf = w.fwd_flops() / (med * 1e-3) / 1e12
+        out.append({"workload": name, "pass": "fwd", "ms": round(med, 4),
+                    "tflops": round(tf, 1), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
+        log(f"  fwd {name}: {med:.3f} ms  {tf:.1f} TFLOP/s  {100 * tf / PEAK_BF16_TFLOPS:.1f}%")
+        del q, k, v, o, lse
+    return out
+
+
+# ---------------------------------------------------------------------------
+def cpu_baseline(w, min_seconds: float = 10.0):
+    """The fp64 oracle, as it stands, on the host cores: fwd + bwd per head."""
+    import concurrent.futures as cf
+
+    import numpy as np
+
+    from exact_attention_41_amd import workloads as wl
+    from oracle import attention as ora
+
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    cores = min(len(os.sched_getaffinity(0)), 16)
+    inp = wl.workload_inputs(w)
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+
+    def one(bh):
+        b, h = bh
+        q, k, v, do = (x[b, h].astype(np.float64) for x in (inp.q, inp.k, inp.v, inp.do))
+        ora.head_fwd(q, k, v, w.causal, w.scale)
+        ora.head_bwd(q, k, v, do, w.causal, w.scale)
+
+    done = 0
+    ctx = threadpool_limits(1) if threadpool_limits else None
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(max_workers=cores) as ex:
+        while done < len(heads):
+            batch = heads[done:done + cores]
+            list(ex.map(one, batch))
+            done += len(batch)
+            if time.perf_counter() - t0 >= min_seconds:
+                break
+    elapsed = time.perf_counter() - t0
+    if ctx is not None:
+        ctx.unregister()
+    per_head = (w.fwd_flops() + w.bwd_flops()) / len(heads)
+    tflops = per_head * done / elapsed / 1e12
+    return {"value": round(tflops, 5), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} of {len(heads)} heads of {w.name} (fwd+bwd, fp64 numpy, "
+                      f"S/P materialised), {elapsed:.1f} s wall; counted flops as on the GPU"}
+
+
+# ---------------------------------------------------------------------------
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported: this attention path is measured "
+              "on one GPU only (heads shard across GPUs with no communication; see the design "
+              "notes). Run with --gpus 1.", file=sys.stderr, flush=True)
+        return 2
+    rank = int(os.environ.get("RANK", "0"))
+
+    import torch
+
+    from exact_attention_41_amd import _lib
+    from exact_attention_41_amd import workloads as wl
+
+    _lib.load()   # raises if libfa.so was not built: there is no fallback
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    w = wl.WORKLOADS[HEADLINE]
+    log(f"bench: workload {w.name} steps={args.steps} warmup={args.warmup}")
+    ms, per_kernel = gpu_step_timing(w, args.steps, args.warmup)
+    fwd_f, bwd_f = w.fwd_flops(), w.bwd_flops()
+    value = (fwd_f + bwd_f) / (ms * 1e-3) / 1e12
+    log(f"bench: {ms:.3f} ms/step, {value:.1f} TFLOP/s; per kernel (ms): "
+        + ", ".join(f"{k}={v:.3f}" for k, v in per_kernel.items()))
+
+    # Algorithmic MFMA flops each kernel performs over the unmasked score
+    # elements (counted convention N^2/2 when causal): 4d per score forward
+    # (Q K^T, P V), 8d for dQ (S, dP, sum P*dP*K, sum P*K), 8d for dK/dV
+    # (S, dP, dV, dK).
+    alg = {"fwd": fwd_f, "bwd_dq": 2.0 * fwd_f, "bwd_dkdv": 2.0 * fwd_f}
+    dominant = max(alg, key=lambda n: per_kernel[n])
+    achieved = alg[dominant] / (per_kernel[dominant] * 1e-3) / 1e12
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        try:
+            t = json.load(open(TRAFFIC_FILE))
+            if t.get("source_sha") == kernel_source_sha() and dominant in t.get("kernels", {}):
+                traffic = t["kernels"][dominant]["hbm_bytes_per_launch"]
+        except (ValueError, KeyError, TypeError):
+            traffic = None
+    roofline = {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 1),
+                "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
+
+    fwd_tf = fwd_f / (per_kernel["fwd"] * 1e-3) / 1e12
+    bwd_ms = per_kernel["bwd_preprocess"] + per_kernel["bwd_dkdv"] + per_kernel["bwd_dq"]
+    bwd_tf = bwd_f / (bwd_ms * 1e-3) / 1e12
+    sweep = [] if args.no_sweep else gpu_forward_sweep(SWEEP)
+    cpu = None
+    if not args.no_cpu and rank == 0:
+        log("bench: timing the fp64 oracle on host cores")
+        cpu = cpu_baseline(w)
+
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) q, k, v, dO; PCG64 seed 5; bf16 RNE)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "causal": w.causal, "pass": "fwd+bwd", "parallelism": "single GPU"},
+        "frac_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "fwd": {"ms": round(per_kernel["fwd"], 4), "tflops": round(fwd_tf, 1),
+                "frac_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4)},
+        "bwd": {"ms": round(bwd_ms, 4), "tflops": round(bwd_tf, 1),
+                "frac_peak": round(bwd_tf / PEAK_BF16_TFLOPS, 4)},
+        "kernel_ms": {k: round(v, 4) for k, v in per_kernel.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "forward_workloads": sweep,
+        "kernel_source_sha": kernel_source_sha(),
+    }
+    if rank == 0:
+        print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

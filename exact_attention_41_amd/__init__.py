@@ -17,7 +17,7 @@ from typing import Optional, Tuple
 from . import _lib
 
 __all__ = ["fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_bwd_workspace_size", "fa_status_str",
-           "FAError", "library_path"]
+           "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "FAError", "library_path"]
 
 
 class FAError(RuntimeError):
@@ -136,3 +136,61 @@ def fa_bwd(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = N
     if st != _lib.FA_OK:
         raise FAError(st, "fa_bwd")
     return dq, dk, dv
+
+
+def _bwd_common(ref, tensors, lse, workspace):
+    torch = _torch()
+    bf = torch.bfloat16
+    _check(ref, "k", bf)
+    if ref.dim() != 4:
+        raise ValueError("tensors must be [B, H, N, d]")
+    B, H, N, d = ref.shape
+    for t, n in tensors:
+        _check(t, n, bf, ref.shape, ref.device)
+    if lse is not None:
+        _check(lse, "lse", torch.float32, (B, H, N), ref.device)
+    if workspace is None:
+        raise ValueError("workspace is required (a uint8 device tensor of "
+                         "fa_bwd_workspace_size(B, H, N, d) bytes)")
+    if workspace.device != ref.device:
+        raise ValueError("workspace must be on the device of the inputs")
+    return B, H, N, d, workspace.numel() * workspace.element_size()
+
+
+def fa_bwd_preprocess(q, k, v, do, workspace):
+    """Phase 1 of fa_bwd: per-head scale factors into ``workspace``."""
+    torch = _torch()
+    B, H, N, d, ws = _bwd_common(k, [(q, "q"), (v, "v"), (do, "do")], None, workspace)
+    with torch.cuda.device(k.device):
+        st = _lib.load().fa_bwd_preprocess(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                           do.data_ptr(), workspace.data_ptr(), ws,
+                                           B, H, N, d, _stream_ptr(k.device))
+    if st != _lib.FA_OK:
+        raise FAError(st, "fa_bwd_preprocess")
+
+
+def fa_bwd_dq(q, k, v, do, lse, workspace, dq, causal=False, scale=None):
+    """Phase 2 of fa_bwd: dQ (plus D and scaled fp16 q, dO in ``workspace``)."""
+    torch = _torch()
+    B, H, N, d, ws = _bwd_common(k, [(q, "q"), (v, "v"), (do, "do"), (dq, "dq")], lse,
+                                 workspace)
+    with torch.cuda.device(k.device):
+        st = _lib.load().fa_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(),
+                                   lse.data_ptr(), workspace.data_ptr(), ws, dq.data_ptr(),
+                                   B, H, N, d, int(bool(causal)), _scale(scale, d),
+                                   _stream_ptr(k.device))
+    if st != _lib.FA_OK:
+        raise FAError(st, "fa_bwd_dq")
+
+
+def fa_bwd_dkdv(k, v, lse, workspace, dk, dv, causal=False, scale=None):
+    """Phase 3 of fa_bwd: dK and dV from k, v, lse and the workspace."""
+    torch = _torch()
+    B, H, N, d, ws = _bwd_common(k, [(v, "v"), (dk, "dk"), (dv, "dv")], lse, workspace)
+    with torch.cuda.device(k.device):
+        st = _lib.load().fa_bwd_dkdv(k.data_ptr(), v.data_ptr(), lse.data_ptr(),
+                                     workspace.data_ptr(), ws, dk.data_ptr(), dv.data_ptr(),
+                                     B, H, N, d, int(bool(causal)), _scale(scale, d),
+                                     _stream_ptr(k.device))
+    if st != _lib.FA_OK:
+        raise FAError(st, "fa_bwd_dkdv")

@@ -11,7 +11,8 @@ FA_OK = 0
 STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_INVALID_ARG", 2: "FA_ERR_UNSUPPORTED",
                 3: "FA_ERR_WORKSPACE", 4: "FA_ERR_HIP"}
 
-EXPORTED = ("fa_status_str", "fa_fwd", "fa_fwd_f32", "fa_bwd_workspace_size", "fa_bwd")
+EXPORTED = ("fa_status_str", "fa_fwd", "fa_fwd_f32", "fa_bwd_workspace_size", "fa_bwd",
+            "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq")
 
 _lock = threading.Lock()
 _lib = None
@@ -44,5 +45,13 @@ def load() -> ctypes.CDLL:
         lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                i, i, i, i, i, f, vp]
         lib.fa_bwd.restype = i
+        lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, vp, vp, ctypes.c_size_t, i, i, i, i, vp]
+        lib.fa_bwd_preprocess.restype = i
+        lib.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, ctypes.c_size_t, vp, vp,
+                                    i, i, i, i, i, f, vp]
+        lib.fa_bwd_dkdv.restype = i
+        lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp,
+                                  i, i, i, i, i, f, vp]
+        lib.fa_bwd_dq.restype = i
         _lib = lib
         return lib

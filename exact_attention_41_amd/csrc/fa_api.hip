@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <initializer_list>
+
 #include "fa.h"
 #include "fa_kernels.hpp"
 
@@ -94,10 +96,79 @@ fa_status_t fa_fwd_f32(const float* q, const float* k, const float* v, float* o,
 }
 
 size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
-    (void)d;
-    if (B <= 0 || H <= 0 || N <= 0) return 0;
-    const size_t rows = (size_t)B * (size_t)H * (size_t)N;
-    return ((rows * sizeof(float) + 255) / 256) * 256;
+    if (B <= 0 || H <= 0 || N <= 0 || (d != 64 && d != 128)) return 0;
+    return fa::bwd_workspace_layout(B, H, N, d).total;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the backward entry points: null tensor pointers (or a null
+// lse when `need_lse`) are argument errors, misaligned ones unsupported, and
+// the workspace is checked last.
+fa_status_t check_bwd(std::initializer_list<const void*> tensors, bool need_lse, const void* lse,
+                      const void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                      float scale, bool* empty) {
+    FA_TRY(check_common(B, H, N, d, scale, empty));
+    if (*empty) return FA_OK;
+    for (const void* p : tensors)
+        if (!p) return FA_ERR_INVALID_ARG;
+    if (need_lse && !lse) return FA_ERR_INVALID_ARG;
+    for (const void* p : tensors) FA_TRY(check_tensor(p));
+    if (need_lse) FA_TRY(check_lse(lse));
+    if (!workspace || !aligned(workspace, 256) ||
+        workspace_bytes < fa_bwd_workspace_size(B, H, N, d))
+        return FA_ERR_WORKSPACE;
+    return FA_OK;
+}
+
+fa::BwdArgs bwd_args(const void* q, const void* k, const void* v, const void* dout,
+                     const float* lse, void* dq, void* dk, void* dv, void* workspace, int B,
+                     int H, int N, int d, int causal, float scale, hipStream_t stream) {
+    return fa::BwdArgs{q, k, v, dout, lse, dq, dk, dv, workspace,
+                       B, H, N, d, causal != 0, scale, stream};
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status_t fa_bwd_preprocess(const void* q, const void* k, const void* v, const void* dout,
+                              void* workspace, size_t workspace_bytes, int B, int H, int N,
+                              int d, hipStream_t stream) {
+    bool empty = false;
+    FA_TRY(check_bwd({q, k, v, dout}, false, nullptr, workspace, workspace_bytes, B, H, N, d,
+                     1.f, &empty));
+    if (empty) return FA_OK;
+    const fa::BwdArgs a = bwd_args(q, k, v, dout, nullptr, nullptr, nullptr, nullptr, workspace,
+                                   B, H, N, d, 0, 1.f, stream);
+    return fa::launch_bwd_scales(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status_t fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
+                      const float* lse, void* workspace, size_t workspace_bytes, void* dq,
+                      int B, int H, int N, int d, int causal, float scale, hipStream_t stream) {
+    bool empty = false;
+    FA_TRY(check_bwd({q, k, v, dout, dq}, true, lse, workspace, workspace_bytes, B, H, N, d,
+                     scale, &empty));
+    if (empty) return FA_OK;
+    const fa::BwdArgs a = bwd_args(q, k, v, dout, lse, dq, nullptr, nullptr, workspace,
+                                   B, H, N, d, causal, scale, stream);
+    return fa::launch_bwd_dq(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status_t fa_bwd_dkdv(const void* k, const void* v, const float* lse, const void* workspace,
+                        size_t workspace_bytes, void* dk, void* dv, int B, int H, int N, int d,
+                        int causal, float scale, hipStream_t stream) {
+    bool empty = false;
+    FA_TRY(check_bwd({k, v, dk, dv}, true, lse, workspace, workspace_bytes, B, H, N, d, scale,
+                     &empty));
+    if (empty) return FA_OK;
+    const fa::BwdArgs a = bwd_args(nullptr, k, v, nullptr, lse, nullptr, dk, dv,
+                                   const_cast<void*>(workspace), B, H, N, d, causal, scale,
+                                   stream);
+    return fa::launch_bwd_dkdv(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o,
@@ -105,24 +176,15 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o,
                    void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
                    int causal, float scale, hipStream_t stream) {
     bool empty = false;
-    FA_TRY(check_common(B, H, N, d, scale, &empty));
+    FA_TRY(check_bwd({q, k, v, o, dout, dq, dk, dv}, true, lse, workspace, workspace_bytes, B, H,
+                     N, d, scale, &empty));
     if (empty) return FA_OK;
-    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
-    FA_TRY(check_tensor(q));
-    FA_TRY(check_tensor(k));
-    FA_TRY(check_tensor(v));
-    FA_TRY(check_tensor(o));
-    FA_TRY(check_tensor(dout));
-    FA_TRY(check_lse(lse));
-    FA_TRY(check_tensor(dq));
-    FA_TRY(check_tensor(dk));
-    FA_TRY(check_tensor(dv));
-    if (!workspace || !aligned(workspace, 16) ||
-        workspace_bytes < fa_bwd_workspace_size(B, H, N, d))
-        return FA_ERR_WORKSPACE;
-    fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace,
-                  B, H, N, d, causal != 0, scale, stream};
-    return fa::launch_bwd_bf16(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+    const fa::BwdArgs a = bwd_args(q, k, v, dout, lse, dq, dk, dv, workspace, B, H, N, d,
+                                   causal, scale, stream);
+    if (fa::launch_bwd_scales(a) != hipSuccess) return FA_ERR_HIP;
+    if (fa::launch_bwd_dq(a) != hipSuccess) return FA_ERR_HIP;
+    if (fa::launch_bwd_dkdv(a) != hipSuccess) return FA_ERR_HIP;
+    return FA_OK;
 }
 
 }  // extern "C"

@@ -1,54 +1,128 @@
 // Exact-attention backward kernels for gfx950 (bf16 storage, fp32 accumulate).
 //
 // The pages describe the forward only; the backward here is the exact
-// gradient of L = sum(O * dO) with P recomputed from the forward's
+// gradient of L = sum(O * dO), with P recomputed from the forward's
 // logsumexp instead of stored (the O(N) memory property of the "FlashAttention"
 // page, systems-analysis.ru, section "Complexity and optimality"):
-//   D_i  = sum_c dO_ic O_ic                       (preprocess kernel)
-//   P_ij = exp(scale q_i.k_j - lse_i)             (recomputed, masked)
-//   dV   = P^T dO,  dP = dO V^T,  dS = P * (dP - D)
-//   dK   = scale dS^T Q                           (key-block kernel)
-//   dQ   = scale dS K                             (query-block kernel)
-// dK/dV and dQ are produced by two separate passes, so every output element
-// is written by exactly one workgroup and no floating-point atomics are used:
-// the result is bitwise reproducible ("FlashAttention-2" page,
-// systems-analysis.info, section "Performance": exact and deterministic).
+//   P_ij = exp(scale q_i.k_j - lse_i)  (masked),   dP = dO V^T
+//   D_i  = sum_j P_ij dP_ij,   dS = P * (dP - D)
+//   dV = P^T dO,   dK = scale dS^T Q,   dQ = scale dS K
+//
+// Three phases, all deterministic (each output element is written by exactly
+// one workgroup, no floating-point atomics: the "FlashAttention-2" page,
+// systems-analysis.info, section "Performance", calls the method exact and
+// deterministic):
+//   1. scales:  per head, the largest |x| of Q, K, V and dO, turned into
+//      power-of-two factors so that every fp16 operand below is exact (the
+//      bf16 inputs scaled by a power of two) and in range.
+//   2. dQ pass: one workgroup per query block, over the key tiles. D_i is not
+//      known before the pass, so it uses
+//          dQ_i = scale * (sum_j P_ij dP_ij K_j - D_i sum_j P_ij K_j)
+//      and accumulates both sums and D_i = sum_j P_ij dP_ij in the same pass;
+//      D is exact (not taken from the rounded O). It also leaves D and scaled
+//      fp16 copies of Q and dO in the workspace for the next pass.
+//   3. dK/dV pass: one workgroup per key block, over the query tiles, all
+//      products on fp16 operands.
+// The probabilities and dS enter the gradient products as fp16 (11-bit
+// significand) rather than bf16 (8-bit): this keeps dQ, dK and dV within
+// 1e-2 of the exact gradients where bf16 operands do not.
 #include "fa_kernels.hpp"
 #include "fa_device.hpp"
 
 namespace fa {
 
 // ---------------------------------------------------------------------------
-// D_i = dO_i . O_i, one fp32 value per query row.
+// Workspace layout (byte offsets; every block 256-byte aligned).
 // ---------------------------------------------------------------------------
-template <int D>
-__global__ void __launch_bounds__(256)
-bwd_delta_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
-                 float* __restrict__ delta, long long rows) {
-    constexpr int TPR = D / 8;        // threads per row, 16 bytes each
-    constexpr int RPB = 256 / TPR;    // rows per block
-    const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
-    const int ch = threadIdx.x % TPR;
-    float acc = 0.f;
-    if (row < rows) {
-        const u32x4_t a = *(const u32x4_t*)(O + row * D + ch * 8);
-        const u32x4_t b = *(const u32x4_t*)(dO + row * D + ch * 8);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            acc = __builtin_fmaf(bf16_lo(a[w]), bf16_lo(b[w]), acc);
-            acc = __builtin_fmaf(bf16_hi(a[w]), bf16_hi(b[w]), acc);
-        }
-    }
-#pragma unroll
-    for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-    if (ch == 0 && row < rows) delta[row] = acc;
+static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+BwdWorkspace bwd_workspace_layout(long long B, long long H, long long N, long long d) {
+    BwdWorkspace w;
+    const size_t bh = (size_t)(B * H);
+    const size_t rows = bh * (size_t)N;
+    const size_t chunks = (size_t)((N + kScaleRows - 1) / kScaleRows);
+    w.delta = 0;
+    w.scales = w.delta + align256(rows * 4);
+    w.partial = w.scales + align256(bh * 4 * 4);
+    w.q16 = w.partial + align256(bh * chunks * 4 * 4);
+    w.do16 = w.q16 + align256(rows * (size_t)d * 2);
+    w.total = w.do16 + align256(rows * (size_t)d * 2);
+    return w;
 }
 
 // ---------------------------------------------------------------------------
-// Staging helpers: a 64-row bf16 tile [64][D] moved from global memory to LDS
-// as 4-row x 8-column micro-tiles, written both row-major (swizzled 16-byte
-// chunks) and/or transposed ([D][64] with the permuted key order and slot
-// swizzle of fa_device.hpp). Rows at or past N are zero-filled.
+// Phase 1a: per (head, chunk of kScaleRows rows), the largest |x| of Q, K, V
+// and dO, as bf16 magnitude bits (for finite values the integer order of
+// (bits & 0x7fff) is the order of |x|).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ void __launch_bounds__(256)
+bwd_absmax_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                  const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+                  uint32_t* __restrict__ partial, int N, int chunks) {
+    constexpr int DCH = D / 8;
+    const int bid = blockIdx.x;
+    const int bh = bid / chunks, ch = bid % chunks;
+    const int row0 = ch * kScaleRows;
+    const int nrows = min(kScaleRows, N - row0);
+    const size_t base = ((size_t)bh * N + row0) * D;
+    const uint16_t* src[4] = {Q + base, K + base, V + base, dO + base};
+    uint32_t m[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        for (int idx = threadIdx.x; idx < nrows * DCH; idx += 256) {
+            const u32x4_t w = *(const u32x4_t*)(src[t] + (size_t)idx * 8);
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                m[t] = max(m[t], max(w[c] & 0x7fffu, (w[c] >> 16) & 0x7fffu));
+        }
+    }
+    __shared__ uint32_t red[4][4];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) m[t] = max(m[t], (uint32_t)__shfl_xor((int)m[t], off));
+        if (lane == 0) red[wave][t] = m[t];
+    }
+    __syncthreads();
+    if (threadIdx.x < 4) {
+        const int t = threadIdx.x;
+        const uint32_t r = max(max(red[0][t], red[1][t]), max(red[2][t], red[3][t]));
+        partial[((size_t)bh * chunks + ch) * 4 + t] = r;
+    }
+}
+
+// Phase 1b: per head, the power-of-two factor 2^-(e+1) for a largest
+// magnitude in [2^e, 2^(e+1)), so the scaled tensor has |x| < 1 (1 for an
+// all-zero tensor); factors are kept within [2^-60, 2^60].
+__global__ void __launch_bounds__(64)
+bwd_scale_kernel(const uint32_t* __restrict__ partial, float* __restrict__ scales, int BH,
+                 int chunks) {
+    const int bh = blockIdx.x * 64 + threadIdx.x;
+    if (bh >= BH) return;
+    uint32_t m[4] = {0u, 0u, 0u, 0u};
+    for (int c = 0; c < chunks; ++c)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) m[t] = max(m[t], partial[((size_t)bh * chunks + c) * 4 + t]);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        float s = 1.f;
+        if (m[t] != 0u) {
+            int e = (int)(m[t] >> 7) - 127;          // floor(log2 max) (subnormals: -127)
+            e = min(max(e + 1, -60), 60);
+            s = __uint_as_float((uint32_t)(127 - e) << 23);
+        }
+        scales[(size_t)bh * 4 + t] = s;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Staging of a 64-row, 16-bit tile [64][D] from global memory into LDS as
+// 4-row x 8-column micro-tiles: row-major (swizzled 16-byte chunks) and/or
+// transposed ([D][64], permuted key order and slot swizzle of fa_device.hpp).
+// With CVT the source is bf16 and the transposed copy is fp16 of the value
+// times a power of two. Rows at or past N are zero-filled.
 // ---------------------------------------------------------------------------
 template <int D, int NT>
 struct Tile64 {
@@ -87,25 +161,30 @@ struct Tile64 {
         }
     }
 
-    __device__ __forceinline__ void store_transposed(char* dst, int tid) const {
+    template <bool CVT>
+    __device__ __forceinline__ void store_transposed(char* dst, int tid, float s = 1.f) const {
 #pragma unroll
         for (int it = 0; it < LOADS; ++it) {
             const int u = tid + it * NT;
             if (UNITS % NT == 0 || u < UNITS) {
                 const int ch = u % DCH, rg = u / DCH;
                 const int slot = tr_key_position(4 * rg) >> 2;
+                u32x4_t x[4];
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+                    for (int w = 0; w < 4; ++w)
+                        x[rr][w] = CVT ? bf16x2_to_f16x2(r[it][rr][w], s) : r[it][rr][w];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int w = e >> 1;
-                    const uint32_t r0 = r[it][0][w], r1 = r[it][1][w];
-                    const uint32_t r2 = r[it][2][w], r3 = r[it][3][w];
                     u32x2_t col;
                     if (e & 1) {
-                        col[0] = (r0 >> 16) | (r1 & 0xffff0000u);
-                        col[1] = (r2 >> 16) | (r3 & 0xffff0000u);
+                        col[0] = (x[0][w] >> 16) | (x[1][w] & 0xffff0000u);
+                        col[1] = (x[2][w] >> 16) | (x[3][w] & 0xffff0000u);
                     } else {
-                        col[0] = (r0 & 0xffffu) | (r1 << 16);
-                        col[1] = (r2 & 0xffffu) | (r3 << 16);
+                        col[0] = (x[0][w] & 0xffffu) | (x[1][w] << 16);
+                        col[1] = (x[2][w] & 0xffffu) | (x[3][w] << 16);
                     }
                     *(u32x2_t*)(dst + tr_slot_offset(ch * 8 + e, slot)) = col;
                 }
@@ -126,197 +205,21 @@ __device__ __forceinline__ u32x4_t lds_tr_frag(const char* base, int n, int q) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: one workgroup per block of NW*32 keys; each wave owns 32 keys and
-// walks the query tiles (64 rows each) that can see them.
-// Products (lane = key column j, registers = query rows i):
-//   S  = Q K^T        A = Q tile (LDS, row-major)   B = K^T (VGPRs)
-//   dP = dO V^T       A = dO tile (LDS, row-major)  B = V^T (VGPRs)
-//   dV^T += dO^T P    A = dO^T (LDS, transposed)    B = P  (registers)
-//   dK^T += Q^T dS    A = Q^T (LDS, transposed)     B = dS (registers)
-// ---------------------------------------------------------------------------
-template <int D, int NW, bool CAUSAL>
-__global__ void __launch_bounds__(NW * 64, 1)
-bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-                const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-                const float* __restrict__ LSE, const float* __restrict__ delta,
-                uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
-                int BH, int N, float c, float scale) {
-    constexpr int BQ = 64;
-    constexpr int NT = NW * 64;
-    constexpr int BKV = NW * 32;
-    constexpr int KS = D / 16;
-    constexpr int NB = D / 32;
-    using TileT = Tile64<D, NT>;
-    constexpr int TB = TileT::BYTES;
-    constexpr int OFF_Q = 0, OFF_QT = TB, OFF_DO = 2 * TB, OFF_DOT = 3 * TB;
-    constexpr int OFF_LSE = 4 * TB, OFF_DEL = 4 * TB + BQ * 4;
-    constexpr int BUF = 4 * TB + 2 * BQ * 4;
-    __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int g = lane >> 5, l32 = lane & 31;
-    const int bid = blockIdx.x;
-    const int bh = bid % BH;
-    const int kb = bid / BH;              // low key blocks see the most queries: first
-    const size_t head = (size_t)bh * (size_t)N * D;
-    const uint16_t* Qh = Q + head;
-    const uint16_t* dOh = dO + head;
-    const float* lse_h = LSE + (size_t)bh * N;
-    const float* del_h = delta + (size_t)bh * N;
-
-    const int k0 = kb * BKV;
-    const int kw0 = k0 + wave * 32;
-    const int kj = kw0 + l32;             // this lane's key
-
-    u32x4_t kf[KS], vf[KS];
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-        if (kj < N) {
-            kf[s] = *(const u32x4_t*)(K + head + (size_t)kj * D + 16 * s + 8 * g);
-            vf[s] = *(const u32x4_t*)(V + head + (size_t)kj * D + 16 * s + 8 * g);
-        } else {
-            kf[s] = vf[s] = u32x4_t{0u, 0u, 0u, 0u};
-        }
-    }
-
-    f32x16_t acc_dk[NB], acc_dv[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc_dk[nb][r] = acc_dv[nb][r] = 0.f;
-
-    const int n_tiles = (N + BQ - 1) / BQ;
-    const int t0 = CAUSAL ? (k0 / BQ) : 0;
-
-    TileT qt, dot;
-    float stat = 0.f;   // lse*log2e (threads 0..63) or delta (64..127) of the next tile
-
-    auto load = [&](int i0) {
-        qt.load(Qh, i0, N, tid);
-        dot.load(dOh, i0, N, tid);
-        if (tid < 2 * BQ) {
-            const int i = i0 + (tid & (BQ - 1));
-            if (tid < BQ) stat = (i < N) ? lse_h[i] * kLog2e : __builtin_huge_valf();
-            else stat = (i < N) ? del_h[i] : 0.f;
-        }
-    };
-    auto store = [&](int buf) {
-        char* b = smem + buf * BUF;
-        qt.store_rowmajor(b + OFF_Q, tid);
-        qt.store_transposed(b + OFF_QT, tid);
-        dot.store_rowmajor(b + OFF_DO, tid);
-        dot.store_transposed(b + OFF_DOT, tid);
-        if (tid < 2 * BQ) ((float*)(b + OFF_LSE))[tid] = stat;
-    };
-
-    if (t0 < n_tiles) {
-        load(t0 * BQ);
-        store(0);
-    }
-    __syncthreads();
-
-    for (int t = t0; t < n_tiles; ++t) {
-        const int i0 = t * BQ;
-        const int buf = (t - t0) & 1;
-        if (t + 1 < n_tiles) load(i0 + BQ);
-        const char* b = smem + buf * BUF;
-
-        if (!CAUSAL || i0 + BQ - 1 >= kw0) {
-            f32x16_t acc_s[2], acc_dp[2];
-#pragma unroll
-            for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc_s[ib][r] = acc_dp[ib][r] = 0.f;
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-#pragma unroll
-                for (int ib = 0; ib < 2; ++ib) {
-                    const u32x4_t qa = lds_row_frag<D>(b + OFF_Q, 32 * ib + l32, 2 * s + g);
-                    acc_s[ib] = mfma_32x32x16(qa, kf[s], acc_s[ib]);
-                    const u32x4_t da = lds_row_frag<D>(b + OFF_DO, 32 * ib + l32, 2 * s + g);
-                    acc_dp[ib] = mfma_32x32x16(da, vf[s], acc_dp[ib]);
-                }
-            }
-
-            const bool need_mask = CAUSAL && (i0 < kw0 + 31);
-            const float* lse_t = (const float*)(b + OFF_LSE);
-            const float* del_t = (const float*)(b + OFF_DEL);
-            u32x4_t pp[4], dsp[4];
-#pragma unroll
-            for (int ib = 0; ib < 2; ++ib) {
-                float pv[16], dsv[16];
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const int ii = 32 * ib + 8 * q4 + 4 * g;
-                    const f32x4_t l4 = *(const f32x4_t*)(lse_t + ii);
-                    const f32x4_t d4 = *(const f32x4_t*)(del_t + ii);
-#pragma unroll
-                    for (int r4 = 0; r4 < 4; ++r4) {
-                        const int r = 4 * q4 + r4;
-                        float p = fast_exp2(__builtin_fmaf(acc_s[ib][r], c, -l4[r4]));
-                        if (need_mask && kj > i0 + ii + r4) p = 0.f;
-                        pv[r] = p;
-                        dsv[r] = p * (acc_dp[ib][r] - d4[r4]);
-                    }
-                }
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int rb = 8 * h;
-                    pp[2 * ib + h] = u32x4_t{pack_bf16x2(pv[rb + 0], pv[rb + 1]), pack_bf16x2(pv[rb + 2], pv[rb + 3]),
-                                             pack_bf16x2(pv[rb + 4], pv[rb + 5]), pack_bf16x2(pv[rb + 6], pv[rb + 7])};
-                    dsp[2 * ib + h] = u32x4_t{pack_bf16x2(dsv[rb + 0], dsv[rb + 1]), pack_bf16x2(dsv[rb + 2], dsv[rb + 3]),
-                                              pack_bf16x2(dsv[rb + 4], dsv[rb + 5]), pack_bf16x2(dsv[rb + 6], dsv[rb + 7])};
-                }
-            }
-
-#pragma unroll
-            for (int t4 = 0; t4 < 4; ++t4) {
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    const u32x4_t a1 = lds_tr_frag(b + OFF_DOT, 32 * nb + l32, 2 * t4 + g);
-                    acc_dv[nb] = mfma_32x32x16(a1, pp[t4], acc_dv[nb]);
-                    const u32x4_t a2 = lds_tr_frag(b + OFF_QT, 32 * nb + l32, 2 * t4 + g);
-                    acc_dk[nb] = mfma_32x32x16(a2, dsp[t4], acc_dk[nb]);
-                }
-            }
-        }
-
-        if (t + 1 < n_tiles) store(buf ^ 1);
-        __syncthreads();
-    }
-
-    if (kj < N) {
-        uint16_t* dkrow = dK + head + (size_t)kj * D;
-        uint16_t* dvrow = dV + head + (size_t)kj * D;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                u32x2_t wk, wv;
-                wk[0] = pack_bf16x2(acc_dk[nb][4 * q4 + 0] * scale, acc_dk[nb][4 * q4 + 1] * scale);
-                wk[1] = pack_bf16x2(acc_dk[nb][4 * q4 + 2] * scale, acc_dk[nb][4 * q4 + 3] * scale);
-                wv[0] = pack_bf16x2(acc_dv[nb][4 * q4 + 0], acc_dv[nb][4 * q4 + 1]);
-                wv[1] = pack_bf16x2(acc_dv[nb][4 * q4 + 2], acc_dv[nb][4 * q4 + 3]);
-                *(u32x2_t*)(dkrow + 32 * nb + 8 * q4 + 4 * g) = wk;
-                *(u32x2_t*)(dvrow + 32 * nb + 8 * q4 + 4 * g) = wv;
-            }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// dQ: one workgroup per block of NW*32 queries; each wave owns 32 query rows
-// and walks the key tiles (64 keys each) they can see.
-// Products (lane = query column i, registers = key rows j):
-//   S^T  = K Q^T       A = K tile (LDS, row-major)   B = Q^T (VGPRs)
-//   dP^T = V dO^T      A = V tile (LDS, row-major)   B = dO^T (VGPRs)
-//   dQ^T += K^T dS^T   A = K^T (LDS, transposed)     B = dS^T (registers)
+// Phase 2: dQ (and D, and the fp16 copies of Q and dO).
+// One workgroup per block of NW*32 queries; each wave owns 32 query rows,
+// one per lane pair. Products (lane = query column i, registers = key rows j):
+//   S^T  = K Q^T               A = K tile (LDS, bf16)     B = Q^T (VGPRs)
+//   dP~^T = V (sE dO)^T        A = V tile (LDS, bf16)     B = sE dO^T (VGPRs)
+//   A~^T += K~^T (P*dP~)^T     A = sK K^T (LDS, fp16)     B = P*dP~ (fp16)
+//   B~^T += K~^T P^T           A = sK K^T (LDS, fp16)     B = P (fp16)
+// with sE = s_dO * s_V; finally dQ = scale/(sK sE) (A~ - D~ B~), D~ = sE D.
 // ---------------------------------------------------------------------------
 template <int D, int NW, bool CAUSAL>
 __global__ void __launch_bounds__(NW * 64, 1)
 bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-              const float* __restrict__ LSE, const float* __restrict__ delta,
+              const float* __restrict__ LSE, const float* __restrict__ scales,
+              float* __restrict__ delta, uint16_t* __restrict__ q16, uint16_t* __restrict__ do16,
               uint16_t* __restrict__ dQ, int BH, int N, float c, float scale, int nqb) {
     constexpr int BC = 64;
     constexpr int NT = NW * 64;
@@ -342,24 +245,39 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const int wq0 = q0 + wave * 32;
     const int qi = wq0 + l32;             // this lane's query row
 
+    const float sQ = scales[bh * 4 + 0], sK = scales[bh * 4 + 1];
+    const float sV = scales[bh * 4 + 2], sDO = scales[bh * 4 + 3];
+    const float sE = sDO * sV;
+
     u32x4_t qf[KS], of[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
         if (qi < N) {
-            qf[s] = *(const u32x4_t*)(Q + head + (size_t)qi * D + 16 * s + 8 * g);
-            of[s] = *(const u32x4_t*)(dO + head + (size_t)qi * D + 16 * s + 8 * g);
+            const size_t off = head + (size_t)qi * D + 16 * s + 8 * g;
+            const u32x4_t qv = *(const u32x4_t*)(Q + off);
+            const u32x4_t ov = *(const u32x4_t*)(dO + off);
+            u32x4_t qh, oh;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                qh[w] = bf16x2_to_f16x2(qv[w], sQ);
+                oh[w] = bf16x2_to_f16x2(ov[w], sDO);
+                of[s][w] = bf16x2_scale(ov[w], sE);
+            }
+            qf[s] = qv;
+            *(u32x4_t*)(q16 + off) = qh;
+            *(u32x4_t*)(do16 + off) = oh;
         } else {
             qf[s] = of[s] = u32x4_t{0u, 0u, 0u, 0u};
         }
     }
     const float lse2 = (qi < N) ? LSE[(size_t)bh * N + qi] * kLog2e : __builtin_huge_valf();
-    const float dl = (qi < N) ? delta[(size_t)bh * N + qi] : 0.f;
 
-    f32x16_t acc_dq[NB];
+    f32x16_t acc_a[NB], acc_b[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc_dq[nb][r] = 0.f;
+        for (int r = 0; r < 16; ++r) acc_a[nb][r] = acc_b[nb][r] = 0.f;
+    float dsum = 0.f;
 
     const int n_all = (N + BC - 1) / BC;
     const int q_last = min(q0 + BQ, N) - 1;
@@ -373,7 +291,7 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     auto store = [&](int buf) {
         char* b = smem + buf * BUF;
         kt.store_rowmajor(b + OFF_K, tid);
-        kt.store_transposed(b + OFF_KT, tid);
+        kt.template store_transposed<true>(b + OFF_KT, tid, sK);
         vt.store_rowmajor(b + OFF_V, tid);
     };
 
@@ -405,22 +323,27 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             }
 
             const bool need_mask = (j0 + BC > N) || (CAUSAL && j0 + BC - 1 > wq0);
-            u32x4_t dsp[4];
+            u32x4_t pf[4], ef[4];
 #pragma unroll
             for (int jb = 0; jb < 2; ++jb) {
-                float dsv[16];
+                float pv[16], ev[16];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int j = j0 + 32 * jb + 8 * (r >> 2) + 4 * g + (r & 3);
                     float p = fast_exp2(__builtin_fmaf(acc_s[jb][r], c, -lse2));
                     if (need_mask && (j >= N || (CAUSAL && j > qi))) p = 0.f;
-                    dsv[r] = p * (acc_dp[jb][r] - dl);
+                    const float e = p * acc_dp[jb][r];
+                    dsum += e;
+                    pv[r] = p;
+                    ev[r] = e;
                 }
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int rb = 8 * h;
-                    dsp[2 * jb + h] = u32x4_t{pack_bf16x2(dsv[rb + 0], dsv[rb + 1]), pack_bf16x2(dsv[rb + 2], dsv[rb + 3]),
-                                              pack_bf16x2(dsv[rb + 4], dsv[rb + 5]), pack_bf16x2(dsv[rb + 6], dsv[rb + 7])};
+                    pf[2 * jb + h] = u32x4_t{pack_f16x2(pv[rb + 0], pv[rb + 1]), pack_f16x2(pv[rb + 2], pv[rb + 3]),
+                                             pack_f16x2(pv[rb + 4], pv[rb + 5]), pack_f16x2(pv[rb + 6], pv[rb + 7])};
+                    ef[2 * jb + h] = u32x4_t{pack_f16x2(ev[rb + 0], ev[rb + 1]), pack_f16x2(ev[rb + 2], ev[rb + 3]),
+                                             pack_f16x2(ev[rb + 4], ev[rb + 5]), pack_f16x2(ev[rb + 6], ev[rb + 7])};
                 }
             }
 
@@ -429,7 +352,8 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
                     const u32x4_t a = lds_tr_frag(b + OFF_KT, 32 * nb + l32, 2 * t4 + g);
-                    acc_dq[nb] = mfma_32x32x16(a, dsp[t4], acc_dq[nb]);
+                    acc_a[nb] = mfma_32x32x16_f16(a, ef[t4], acc_a[nb]);
+                    acc_b[nb] = mfma_32x32x16_f16(a, pf[t4], acc_b[nb]);
                 }
             }
         }
@@ -438,50 +362,287 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         __syncthreads();
     }
 
+    const float dt = sum_with_partner32(dsum);    // D~ = sE * D
     if (qi < N) {
+        if (g == 0) delta[(size_t)bh * N + qi] = dt / sE;
+        const float f = scale / (sK * sE);
         uint16_t* row = dQ + head + (size_t)qi * D;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
+                float x[4];
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const int r = 4 * q4 + r4;
+                    x[r4] = f * __builtin_fmaf(-dt, acc_b[nb][r], acc_a[nb][r]);
+                }
                 u32x2_t w;
-                w[0] = pack_bf16x2(acc_dq[nb][4 * q4 + 0] * scale, acc_dq[nb][4 * q4 + 1] * scale);
-                w[1] = pack_bf16x2(acc_dq[nb][4 * q4 + 2] * scale, acc_dq[nb][4 * q4 + 3] * scale);
+                w[0] = pack_bf16x2(x[0], x[1]);
+                w[1] = pack_bf16x2(x[2], x[3]);
                 *(u32x2_t*)(row + 32 * nb + 8 * q4 + 4 * g) = w;
             }
     }
 }
 
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
-static hipError_t launch_bwd_t(const BwdArgs& a) {
-    constexpr int NW = 4;
+// Phase 3: dK, dV. One workgroup per block of NW*32 keys; each wave owns 32
+// keys (one per lane pair) and walks the query tiles (64 rows) that see them.
+// All operands fp16: Q~ = sQ Q, dO~ = sDO dO (from the workspace), K~ = sK K,
+// V~ = sV V (resident). Products (lane = key column j, registers = rows i):
+//   S~  = Q~ K~^T        A = Q~ tile (LDS)            B = K~^T (VGPRs)
+//   dP~ = dO~ V~^T       A = dO~ tile (LDS)           B = V~^T (VGPRs)
+//   dV^T += dO~^T P      A = dO~^T (LDS, transposed)  B = P (fp16)
+//   dK^T += Q~^T dS~     A = Q~^T (LDS, transposed)   B = dS~ = P (dP~ - sE D)
+// ---------------------------------------------------------------------------
+template <int D, int NW, bool CAUSAL>
+__global__ void __launch_bounds__(NW * 64, 1)
+bwd_dkdv_kernel(const uint16_t* __restrict__ q16, const uint16_t* __restrict__ K,
+                const uint16_t* __restrict__ V, const uint16_t* __restrict__ do16,
+                const float* __restrict__ LSE, const float* __restrict__ delta,
+                const float* __restrict__ scales, uint16_t* __restrict__ dK,
+                uint16_t* __restrict__ dV, int BH, int N, float c, float scale) {
+    constexpr int BQ = 64;
+    constexpr int NT = NW * 64;
+    constexpr int BKV = NW * 32;
+    constexpr int KS = D / 16;
+    constexpr int NB = D / 32;
+    using TileT = Tile64<D, NT>;
+    constexpr int TB = TileT::BYTES;
+    constexpr int OFF_Q = 0, OFF_QT = TB, OFF_DO = 2 * TB, OFF_DOT = 3 * TB;
+    constexpr int OFF_LSE = 4 * TB, OFF_DEL = 4 * TB + BQ * 4;
+    constexpr int BUF = 4 * TB + 2 * BQ * 4;
+    __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 5, l32 = lane & 31;
+    const int bid = blockIdx.x;
+    const int bh = bid % BH;
+    const int kb = bid / BH;              // low key blocks see the most queries: first
+    const size_t head = (size_t)bh * (size_t)N * D;
+    const uint16_t* Qh = q16 + head;
+    const uint16_t* dOh = do16 + head;
+    const float* lse_h = LSE + (size_t)bh * N;
+    const float* del_h = delta + (size_t)bh * N;
+
+    const float sQ = scales[bh * 4 + 0], sK = scales[bh * 4 + 1];
+    const float sV = scales[bh * 4 + 2], sDO = scales[bh * 4 + 3];
+    const float sE = sDO * sV;
+    const float cs = c / (sQ * sK);       // S = S~ / (sQ sK), exactly
+
+    const int k0 = kb * BKV;
+    const int kw0 = k0 + wave * 32;
+    const int kj = kw0 + l32;             // this lane's key
+
+    u32x4_t kf[KS], vf[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        if (kj < N) {
+            const u32x4_t kv = *(const u32x4_t*)(K + head + (size_t)kj * D + 16 * s + 8 * g);
+            const u32x4_t vv = *(const u32x4_t*)(V + head + (size_t)kj * D + 16 * s + 8 * g);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                kf[s][w] = bf16x2_to_f16x2(kv[w], sK);
+                vf[s][w] = bf16x2_to_f16x2(vv[w], sV);
+            }
+        } else {
+            kf[s] = vf[s] = u32x4_t{0u, 0u, 0u, 0u};
+        }
+    }
+
+    f32x16_t acc_dk[NB], acc_dv[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc_dk[nb][r] = acc_dv[nb][r] = 0.f;
+
+    const int n_tiles = (N + BQ - 1) / BQ;
+    const int t0 = CAUSAL ? (k0 / BQ) : 0;
+
+    TileT qt, dot;
+    float stat = 0.f;   // lse*log2e (threads 0..63) or sE*D (64..127) of the next tile
+
+    auto load = [&](int i0) {
+        qt.load(Qh, i0, N, tid);
+        dot.load(dOh, i0, N, tid);
+        if (tid < 2 * BQ) {
+            const int i = i0 + (tid & (BQ - 1));
+            if (tid < BQ) stat = (i < N) ? lse_h[i] * kLog2e : __builtin_huge_valf();
+            else stat = (i < N) ? del_h[i] * sE : 0.f;
+        }
+    };
+    auto store = [&](int buf) {
+        char* b = smem + buf * BUF;
+        qt.store_rowmajor(b + OFF_Q, tid);
+        qt.template store_transposed<false>(b + OFF_QT, tid);
+        dot.store_rowmajor(b + OFF_DO, tid);
+        dot.template store_transposed<false>(b + OFF_DOT, tid);
+        if (tid < 2 * BQ) ((float*)(b + OFF_LSE))[tid] = stat;
+    };
+
+    if (t0 < n_tiles) {
+        load(t0 * BQ);
+        store(0);
+    }
+    __syncthreads();
+
+    for (int t = t0; t < n_tiles; ++t) {
+        const int i0 = t * BQ;
+        const int buf = (t - t0) & 1;
+        if (t + 1 < n_tiles) load(i0 + BQ);
+        const char* b = smem + buf * BUF;
+
+        if (!CAUSAL || i0 + BQ - 1 >= kw0) {
+            f32x16_t acc_s[2], acc_dp[2];
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc_s[ib][r] = acc_dp[ib][r] = 0.f;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+#pragma unroll
+                for (int ib = 0; ib < 2; ++ib) {
+                    const u32x4_t qa = lds_row_frag<D>(b + OFF_Q, 32 * ib + l32, 2 * s + g);
+                    acc_s[ib] = mfma_32x32x16_f16(qa, kf[s], acc_s[ib]);
+                    const u32x4_t da = lds_row_frag<D>(b + OFF_DO, 32 * ib + l32, 2 * s + g);
+                    acc_dp[ib] = mfma_32x32x16_f16(da, vf[s], acc_dp[ib]);
+                }
+            }
+
+            const bool need_mask = CAUSAL && (i0 < kw0 + 31);
+            const float* lse_t = (const float*)(b + OFF_LSE);
+            const float* del_t = (const float*)(b + OFF_DEL);
+            u32x4_t pp[4], dsp[4];
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib) {
+                float pv[16], dsv[16];
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int ii = 32 * ib + 8 * q4 + 4 * g;
+                    const f32x4_t l4 = *(const f32x4_t*)(lse_t + ii);
+                    const f32x4_t d4 = *(const f32x4_t*)(del_t + ii);
+#pragma unroll
+                    for (int r4 = 0; r4 < 4; ++r4) {
+                        const int r = 4 * q4 + r4;
+                        float p = fast_exp2(__builtin_fmaf(acc_s[ib][r], cs, -l4[r4]));
+                        if (need_mask && kj > i0 + ii + r4) p = 0.f;
+                        pv[r] = p;
+                        dsv[r] = p * (acc_dp[ib][r] - d4[r4]);
+                    }
+                }
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int rb = 8 * h;
+                    pp[2 * ib + h] = u32x4_t{pack_f16x2(pv[rb + 0], pv[rb + 1]), pack_f16x2(pv[rb + 2], pv[rb + 3]),
+                                             pack_f16x2(pv[rb + 4], pv[rb + 5]), pack_f16x2(pv[rb + 6], pv[rb + 7])};
+                    dsp[2 * ib + h] = u32x4_t{pack_f16x2(dsv[rb + 0], dsv[rb + 1]), pack_f16x2(dsv[rb + 2], dsv[rb + 3]),
+                                              pack_f16x2(dsv[rb + 4], dsv[rb + 5]), pack_f16x2(dsv[rb + 6], dsv[rb + 7])};
+                }
+            }
+
+#pragma unroll
+            for (int t4 = 0; t4 < 4; ++t4) {
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    const u32x4_t a1 = lds_tr_frag(b + OFF_DOT, 32 * nb + l32, 2 * t4 + g);
+                    acc_dv[nb] = mfma_32x32x16_f16(a1, pp[t4], acc_dv[nb]);
+                    const u32x4_t a2 = lds_tr_frag(b + OFF_QT, 32 * nb + l32, 2 * t4 + g);
+                    acc_dk[nb] = mfma_32x32x16_f16(a2, dsp[t4], acc_dk[nb]);
+                }
+            }
+        }
+
+        if (t + 1 < n_tiles) store(buf ^ 1);
+        __syncthreads();
+    }
+
+    if (kj < N) {
+        const float fk = scale / (sQ * sE), fv = 1.f / sDO;
+        uint16_t* dkrow = dK + head + (size_t)kj * D;
+        uint16_t* dvrow = dV + head + (size_t)kj * D;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                u32x2_t wk, wv;
+                wk[0] = pack_bf16x2(acc_dk[nb][4 * q4 + 0] * fk, acc_dk[nb][4 * q4 + 1] * fk);
+                wk[1] = pack_bf16x2(acc_dk[nb][4 * q4 + 2] * fk, acc_dk[nb][4 * q4 + 3] * fk);
+                wv[0] = pack_bf16x2(acc_dv[nb][4 * q4 + 0] * fv, acc_dv[nb][4 * q4 + 1] * fv);
+                wv[1] = pack_bf16x2(acc_dv[nb][4 * q4 + 2] * fv, acc_dv[nb][4 * q4 + 3] * fv);
+                *(u32x2_t*)(dkrow + 32 * nb + 8 * q4 + 4 * g) = wk;
+                *(u32x2_t*)(dvrow + 32 * nb + 8 * q4 + 4 * g) = wv;
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers (arguments already validated by the C-ABI layer).
+// ---------------------------------------------------------------------------
+constexpr int kBwdWaves = 4;
+
+static BwdWorkspace ws_of(const BwdArgs& a) { return bwd_workspace_layout(a.B, a.H, a.N, a.d); }
+
+template <typename T>
+static T* ws_ptr(const BwdArgs& a, size_t off) { return (T*)((char*)a.workspace + off); }
+
+hipError_t launch_bwd_scales(const BwdArgs& a) {
+    const BwdWorkspace w = ws_of(a);
     const int BH = a.B * a.H;
-    const long long rows = (long long)BH * a.N;
-    const float c = a.scale * kLog2e;
-    constexpr int RPB = 256 / (D / 8);
-    hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
-                       a.stream, (const uint16_t*)a.o, (const uint16_t*)a.dout, a.delta, rows);
+    const int chunks = (a.N + kScaleRows - 1) / kScaleRows;
+    uint32_t* partial = ws_ptr<uint32_t>(a, w.partial);
+    if (a.d == 128)
+        hipLaunchKernelGGL((bwd_absmax_kernel<128>), dim3(BH * chunks), dim3(256), 0, a.stream,
+                           (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                           (const uint16_t*)a.dout, partial, a.N, chunks);
+    else
+        hipLaunchKernelGGL((bwd_absmax_kernel<64>), dim3(BH * chunks), dim3(256), 0, a.stream,
+                           (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                           (const uint16_t*)a.dout, partial, a.N, chunks);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int nkb = (a.N + NW * 32 - 1) / (NW * 32);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, CAUSAL>), dim3(nkb * BH), dim3(NW * 64), 0, a.stream,
-                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                       (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv,
-                       BH, a.N, c, a.scale);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int nqb = (a.N + NW * 32 - 1) / (NW * 32);
-    hipLaunchKernelGGL((bwd_dq_kernel<D, NW, CAUSAL>), dim3(nqb * BH), dim3(NW * 64), 0, a.stream,
-                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                       (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dq, BH, a.N, c,
-                       a.scale, nqb);
+    hipLaunchKernelGGL(bwd_scale_kernel, dim3((BH + 63) / 64), dim3(64), 0, a.stream,
+                       (const uint32_t*)partial, ws_ptr<float>(a, w.scales), BH, chunks);
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_bf16(const BwdArgs& a) {
-    if (a.d == 128) return a.causal ? launch_bwd_t<128, true>(a) : launch_bwd_t<128, false>(a);
-    return a.causal ? launch_bwd_t<64, true>(a) : launch_bwd_t<64, false>(a);
+template <int D, bool CAUSAL>
+static hipError_t launch_dq_t(const BwdArgs& a) {
+    constexpr int NW = kBwdWaves;
+    const BwdWorkspace w = ws_of(a);
+    const int BH = a.B * a.H;
+    const int nqb = (a.N + NW * 32 - 1) / (NW * 32);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, NW, CAUSAL>), dim3(nqb * BH), dim3(NW * 64), 0,
+                       a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                       (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse,
+                       ws_ptr<const float>(a, w.scales), ws_ptr<float>(a, w.delta),
+                       ws_ptr<uint16_t>(a, w.q16), ws_ptr<uint16_t>(a, w.do16),
+                       (uint16_t*)a.dq, BH, a.N, a.scale * kLog2e, a.scale, nqb);
+    return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+static hipError_t launch_dkdv_t(const BwdArgs& a) {
+    constexpr int NW = kBwdWaves;
+    const BwdWorkspace w = ws_of(a);
+    const int BH = a.B * a.H;
+    const int nkb = (a.N + NW * 32 - 1) / (NW * 32);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, CAUSAL>), dim3(nkb * BH), dim3(NW * 64), 0,
+                       a.stream, ws_ptr<const uint16_t>(a, w.q16), (const uint16_t*)a.k,
+                       (const uint16_t*)a.v, ws_ptr<const uint16_t>(a, w.do16), a.lse,
+                       ws_ptr<const float>(a, w.delta), ws_ptr<const float>(a, w.scales),
+                       (uint16_t*)a.dk, (uint16_t*)a.dv, BH, a.N, a.scale * kLog2e, a.scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq(const BwdArgs& a) {
+    if (a.d == 128) return a.causal ? launch_dq_t<128, true>(a) : launch_dq_t<128, false>(a);
+    return a.causal ? launch_dq_t<64, true>(a) : launch_dq_t<64, false>(a);
+}
+
+hipError_t launch_bwd_dkdv(const BwdArgs& a) {
+    if (a.d == 128) return a.causal ? launch_dkdv_t<128, true>(a) : launch_dkdv_t<128, false>(a);
+    return a.causal ? launch_dkdv_t<64, true>(a) : launch_dkdv_t<64, false>(a);
 }
 
 }  // namespace fa

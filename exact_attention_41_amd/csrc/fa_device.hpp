@@ -10,6 +10,8 @@ namespace fa {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
@@ -30,6 +32,32 @@ __device__ __forceinline__ f32x16_t mfma_32x32x16(const u32x4_t& a, const u32x4_
                                                   const f32x16_t& c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Same product with fp16 operands (same rate on gfx950, 3 more mantissa bits).
+__device__ __forceinline__ f32x16_t mfma_32x32x16_f16(const u32x4_t& a, const u32x4_t& b,
+                                                      const f32x16_t& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+// Two fp32 values -> packed fp16 pair, round to nearest even (v_cvt_pk_f16_f32).
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+    f16x2_t p = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(uint32_t, p);
+}
+
+// A packed bf16 pair times s (a power of two), as a packed fp16 pair.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w, float s) {
+    return pack_f16x2(__uint_as_float(w << 16) * s, __uint_as_float(w & 0xffff0000u) * s);
+}
+
+// A packed bf16 pair times s (a power of two), still bf16 (exact unless the
+// result leaves the fp32 exponent range).
+__device__ __forceinline__ uint32_t bf16x2_scale(uint32_t w, float s) {
+    const uint32_t lo = __float_as_uint(__uint_as_float(w << 16) * s) >> 16;
+    const uint32_t hi = __float_as_uint(__uint_as_float(w & 0xffff0000u) * s) & 0xffff0000u;
+    return lo | hi;
 }
 
 // Two fp32 values -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).

@@ -38,7 +38,8 @@
  *                FA_ERR_UNSUPPORTED  d not 64/128, misaligned pointer, or a
  *                                    size whose index arithmetic would
  *                                    overflow (grid or N beyond 2^26);
- *                FA_ERR_WORKSPACE    backward workspace too small or null;
+ *                FA_ERR_WORKSPACE    backward workspace too small, null or not
+ *                                    256-byte aligned;
  *                FA_ERR_HIP          the HIP runtime refused the launch.
  *   Aliasing   outputs must not overlap inputs or each other.
  */
@@ -90,9 +91,10 @@ fa_status_t fa_fwd_f32(const float* q, const float* k, const float* v, float* o,
                        float scale, hipStream_t stream);
 
 /*
- * Bytes of device workspace fa_bwd needs for these sizes (0 if a size is
- * negative or the problem is empty). The workspace holds one fp32 value per
- * query row, D_i = sum_c dO_ic O_ic, so it is O(B*H*N).
+ * Bytes of device workspace fa_bwd needs for these sizes (0 if a size is not
+ * positive or d is unsupported). The workspace is O(B*H*N*d): per query row
+ * it holds D_i (fp32) and power-of-two-scaled fp16 copies of that row of q
+ * and dout, plus a few values per head (see fa_bwd).
  */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d);
 
@@ -100,22 +102,54 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d);
  * Backward, bfloat16 storage: the gradients of the scalar
  * L = sum_{b,h,i,c} O_bhic dO_bhic with respect to q, k and v.
  *   q, k, v   (in)  bf16 [B][H][N][d], the forward inputs.
- *   o         (in)  bf16 [B][H][N][d], the forward output.
+ *   o         (in)  bf16 [B][H][N][d], the forward output. Checked like the
+ *                   other tensors but not read: D_i = sum_j P_ij dP_ij is
+ *                   recomputed exactly from P and dP = dO V^T instead of as
+ *                   dO_i . O_i from the rounded bf16 O.
  *   dout      (in)  bf16 [B][H][N][d], dL/dO.
  *   lse       (in)  fp32 [B][H][N], the forward's logsumexp.
  *   dq,dk,dv  (out) bf16 [B][H][N][d].
  *   workspace (scratch) device buffer of at least
- *             fa_bwd_workspace_size(B, H, N, d) bytes, 16-byte aligned; its
- *             contents on entry do not matter and are clobbered.
- * P is recomputed from lse, never stored. The result is deterministic: no
- * floating-point atomics are used, so repeated calls give identical bits.
- * causal, scale and the remaining conventions must match the forward call.
+ *             fa_bwd_workspace_size(B, H, N, d) bytes, 256-byte aligned; its
+ *             contents on entry do not matter and are overwritten.
+ * P = exp(scale Q K^T - lse) is recomputed, never stored. The products that
+ * form dQ, dK and dV take P and dS = P * (dP - D) as fp16 operands and q, k,
+ * v, dout multiplied by per-head powers of two (exact), fp32 accumulation.
+ * The result is deterministic: no floating-point atomics are used, so
+ * repeated calls give identical bits. causal and scale must match the
+ * forward call. The inputs must be finite.
  */
 fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o,
                    const void* dout, const float* lse, void* dq, void* dk, void* dv,
                    void* workspace, size_t workspace_bytes,
                    int B, int H, int N, int d, int causal, float scale,
                    hipStream_t stream);
+
+/*
+ * The three phases of fa_bwd, for callers that schedule or time them
+ * separately. fa_bwd(...) is exactly fa_bwd_preprocess, fa_bwd_dq and
+ * fa_bwd_dkdv, in this order, on one stream; each phase reads what the
+ * previous ones left in the workspace, so they must run in this order.
+ * Arguments mean what they mean for fa_bwd.
+ *   fa_bwd_preprocess  per-head largest magnitudes of q, k, v, dout and the
+ *                      power-of-two factors derived from them -> workspace.
+ *   fa_bwd_dq          writes dq; leaves D and the scaled fp16 copies of q
+ *                      and dout in the workspace.
+ *   fa_bwd_dkdv        writes dk and dv from k, v, lse and the workspace.
+ */
+fa_status_t fa_bwd_preprocess(const void* q, const void* k, const void* v, const void* dout,
+                              void* workspace, size_t workspace_bytes,
+                              int B, int H, int N, int d, hipStream_t stream);
+
+fa_status_t fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
+                      const float* lse, void* workspace, size_t workspace_bytes, void* dq,
+                      int B, int H, int N, int d, int causal, float scale,
+                      hipStream_t stream);
+
+fa_status_t fa_bwd_dkdv(const void* k, const void* v, const float* lse,
+                        const void* workspace, size_t workspace_bytes, void* dk, void* dv,
+                        int B, int H, int N, int d, int causal, float scale,
+                        hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -61,8 +61,11 @@ def test_status_strings(lib):
 
 
 def test_workspace_size(lib):
-    assert lib.fa_bwd_workspace_size(4, 16, 4096, 128) >= 4 * 16 * 4096 * 4
+    rows = 4 * 16 * 4096
+    assert lib.fa_bwd_workspace_size(4, 16, 4096, 128) >= rows * (4 + 2 * 2 * 128)
     assert lib.fa_bwd_workspace_size(4, 16, 4096, 128) % 256 == 0
+    assert lib.fa_bwd_workspace_size(4, 16, 4096, 64) < lib.fa_bwd_workspace_size(4, 16, 4096, 128)
+    assert lib.fa_bwd_workspace_size(4, 16, 4096, 96) == 0
     assert lib.fa_bwd_workspace_size(0, 16, 4096, 128) == 0
     assert lib.fa_bwd_workspace_size(-1, 16, 4096, 128) == 0
 
@@ -102,7 +105,7 @@ def test_forward_empty_problem_is_a_no_op(lib, entry):
     assert fwd(lib, entry, q=None, k=None, v=None, o=None, lse=None, N=0) == OK
 
 
-def bwd(lib, ws=A, ws_bytes=None, B=1, H=2, N=100, d=128, **ptrs):
+def bwd(lib, ws=0x200000, ws_bytes=None, B=1, H=2, N=100, d=128, **ptrs):
     p = dict(q=A, k=A, v=A, o=A, do=A, lse=A, dq=A, dk=A, dv=A)
     p.update(ptrs)
     if ws_bytes is None:
@@ -119,7 +122,8 @@ def test_backward_rejects_bad_arguments(lib):
     assert bwd(lib, dk=MIS) == UNSUPPORTED
     assert bwd(lib, ws=None) == WORKSPACE
     assert bwd(lib, ws=MIS) == WORKSPACE
-    assert bwd(lib, ws_bytes=100 * 2 * 4 - 4) == WORKSPACE
+    assert bwd(lib, ws=0x200000 + 128) == WORKSPACE
+    assert bwd(lib, ws_bytes=lib.fa_bwd_workspace_size(1, 2, 100, 128) - 1) == WORKSPACE
     assert bwd(lib, B=0, ws=None, ws_bytes=0) == OK
 
 
@@ -131,3 +135,19 @@ def test_python_binding_refuses_without_gpu_tensors():
         fa.fa_fwd(x, x, x)
     with pytest.raises(TypeError):
         fa.fa_fwd(x.float(), x.float(), x.float())
+
+
+def test_backward_phases_reject_bad_arguments(lib):
+    ws = lib.fa_bwd_workspace_size(1, 2, 100, 128)
+    W = 0x200000     # 256-byte aligned fake workspace
+    assert lib.fa_bwd_preprocess(None, A, A, A, W, ws, 1, 2, 100, 128, None) == INVALID
+    assert lib.fa_bwd_preprocess(A, A, A, A, W, ws - 4, 1, 2, 100, 128, None) == WORKSPACE
+    assert lib.fa_bwd_preprocess(A, A, A, A, W + 16, ws, 1, 2, 100, 128, None) == WORKSPACE
+    assert lib.fa_bwd_preprocess(A, MIS, A, A, W, ws, 1, 2, 100, 128, None) == UNSUPPORTED
+    assert lib.fa_bwd_dq(A, A, A, A, None, W, ws, A, 1, 2, 100, 128, 1, 0.1, None) == INVALID
+    assert lib.fa_bwd_dq(A, A, A, A, A, W, ws, MIS, 1, 2, 100, 128, 1, 0.1, None) == UNSUPPORTED
+    assert lib.fa_bwd_dq(A, A, A, A, A, W, ws, A, 1, 2, 100, 96, 1, 0.1, None) == UNSUPPORTED
+    assert lib.fa_bwd_dq(A, A, A, A, A, W, ws, A, 0, 2, 100, 128, 1, 0.1, None) == OK
+    assert lib.fa_bwd_dkdv(A, A, A, W, ws, A, None, 1, 2, 100, 128, 1, 0.1, None) == INVALID
+    assert lib.fa_bwd_dkdv(A, A, A, None, ws, A, A, 1, 2, 100, 128, 1, 0.1, None) == WORKSPACE
+    assert lib.fa_bwd_dkdv(A, A, A, W, ws, A, A, 1, 2, 100, 128, 1, -1.0, None) == INVALID

@@ -100,3 +100,23 @@ def test_bf16_backward_workload(fa):
     with cf.ThreadPoolExecutor(8) as ex:
         ref = np.stack(list(ex.map(one, pairs)))
     check_bf16("dQ (sampled rows, all heads)", gq[:, rows], ref)
+
+
+def test_backward_phases_equal_fa_bwd(fa):
+    """fa_bwd is exactly its three phases, and repeated calls give equal bits."""
+    import torch
+    B, H, N, d, causal = 2, 2, 333, 128, True
+    say(f"fa_bwd phases B={B} H={H} N={N} d={d} causal={causal} seed=23")
+    inp = wl.make_inputs(B, H, N, d, "bf16", seed=23, with_do=True)
+    q, k, v, do = (wl.to_device(x, "bf16") for x in (inp.q, inp.k, inp.v, inp.do))
+    o, lse = fa.fa_fwd(q, k, v, causal=causal)
+    dq1, dk1, dv1 = fa.fa_bwd(q, k, v, o, do, lse, causal=causal)
+    dq2, dk2, dv2 = fa.fa_bwd(q, k, v, o, do, lse, causal=causal)
+    ws = torch.empty(fa.fa_bwd_workspace_size(B, H, N, d), dtype=torch.uint8, device=q.device)
+    dq3, dk3, dv3 = (torch.empty_like(q) for _ in range(3))
+    fa.fa_bwd_preprocess(q, k, v, do, ws)
+    fa.fa_bwd_dq(q, k, v, do, lse, ws, dq3, causal=causal)
+    fa.fa_bwd_dkdv(k, v, lse, ws, dk3, dv3, causal=causal)
+    torch.cuda.synchronize()
+    for a, b, c in ((dq1, dq2, dq3), (dk1, dk2, dk3), (dv1, dv2, dv3)):
+        assert torch.equal(a, b) and torch.equal(a, c)
