@@ -124,4 +124,86 @@ __device__ __forceinline__ int tr_slot_offset(int n, int slot) {
     return n * 128 + ((slot ^ tr_slot_swizzle(n)) << 3);
 }
 
+// ---------------------------------------------------------------------------
+// Direct global -> LDS staging (buffer_load_dwordx4 ... lds) of a [64][D]
+// bf16 tile into a row-major LDS tile with XOR-swizzled 16-byte chunks. Each
+// wave instruction fills 1 KB of LDS contiguously, lane l writing bytes
+// [16l, 16l+16); the swizzle is applied by choosing which global chunk each
+// lane fetches. The buffer resource covers only the rows of the tile that
+// exist, so rows at or past N read as zeros.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((ext_vector_type(4))) short i16x4_t;
+
+constexpr int kBufferFlags = 0x00020000;   // raw buffer, 32-bit data format
+
+// K-type tiles: chunk c of row r is stored at chunk c ^ row_chunk_swizzle(r).
+// V-type tiles: chunk c of row r is stored at chunk c ^ (2 * (r & 3)), which
+// makes the transposed 8-byte reads below conflict-free.
+__device__ __forceinline__ int v_chunk_swizzle(int row) { return (row & 3) << 1; }
+
+// Byte offset, inside the global tile, of the chunk that lane `lane` of the
+// wave filling 1 KB block `b` must fetch.
+template <int D, bool VTYPE>
+__device__ __forceinline__ uint32_t stage_src_offset(int b, int lane) {
+    constexpr int DCH = D / 8;
+    constexpr int RPK = 1024 / (2 * D);        // rows per 1 KB block
+    const int row = b * RPK + lane / DCH;
+    const int phys = lane % DCH;
+    const int logical = phys ^ (VTYPE ? v_chunk_swizzle(row) : row_chunk_swizzle<D>(row));
+    return (uint32_t)(row * D + logical * 8) * 2u;
+}
+
+// Stage blocks b = first, first + stride, ... (< 64 * D * 2 / 1024) of the
+// tile starting at row row0 of `src` (a [N][D] bf16 array).
+template <int D, int COUNT, int STRIDE, bool VTYPE>
+__device__ __forceinline__ void stage_tile_lds(const uint16_t* __restrict__ src, lds_char* tile,
+                                               int row0, int N, int first, int lane) {
+#if defined(__HIP_DEVICE_COMPILE__)   // buffer resources exist only in the device pass
+    const int rows = min(64, N - row0);
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(src + (size_t)row0 * D), (short)0, rows * D * 2, kBufferFlags);
+#pragma unroll
+    for (int k = 0; k < COUNT; ++k) {
+        const int b = first + STRIDE * k;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsrc, (__attribute__((address_space(3))) void*)(tile + b * 1024), 16,
+            stage_src_offset<D, VTYPE>(b, lane), 0, 0, 0);
+    }
+#endif
+}
+
+// 16-byte A/B fragment of a K-type tile: row `row`, logical chunk `ch`.
+template <int D>
+__device__ __forceinline__ u32x4_t lds_k_frag(const lds_char* tile, int row, int ch) {
+    return *(const __attribute__((address_space(3))) u32x4_t*)(tile + row_chunk_offset<D>(row, ch));
+}
+
+// Transposed MFMA A fragment from a V-type tile [64 keys][D]: lane l gets
+// rows n = n0 + l%32 of V^T and the eight keys 16t + {4g..4g+3, 8+4g..8+4g+3}
+// (g = l/32), in that element order; two ds_read_b64_tr_b16. Within a group of
+// 16 lanes, ds_read_b64_tr_b16 returns to lane i element e of the 8 bytes
+// addressed by lane 4e + i/4, at position i%4; so lane i addresses key row
+// base + i/4, columns c0 + 4(i%4) .. +3.
+template <int D>
+__device__ __forceinline__ u32x4_t lds_vt_frag(const lds_char* tile, int n0, int t, int lane) {
+    const int g = lane >> 5, half = (lane >> 4) & 1, i = lane & 15;
+    const int col = n0 + 16 * half + 4 * (i & 3);
+    const int r1 = 16 * t + 4 * g + (i >> 2), r2 = r1 + 8;
+    const int o1 = r1 * (2 * D) + ((((col >> 3) ^ v_chunk_swizzle(r1))) << 4) + ((col & 7) << 1);
+    const int o2 = r2 * (2 * D) + ((((col >> 3) ^ v_chunk_swizzle(r2))) << 4) + ((col & 7) << 1);
+    const i16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4_t*)(tile + o1));
+    const i16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4_t*)(tile + o2));
+    const u32x2_t ua = __builtin_bit_cast(u32x2_t, a), ub = __builtin_bit_cast(u32x2_t, b);
+    return u32x4_t{ua[0], ua[1], ub[0], ub[1]};
+}
+
+// Sum of a packed bf16 pair added to acc (v_dot2_f32_bf16 with (1, 1)).
+__device__ __forceinline__ float add_bf16x2(uint32_t w, float acc) {
+    const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), one, acc, false);
+}
+
 }  // namespace fa

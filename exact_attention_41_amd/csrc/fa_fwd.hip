@@ -12,6 +12,8 @@
 // non-matrix operations" and "3. Improved work partitioning within the
 // block"); the grid spreads the query blocks of one head over many compute
 // units (section "2. Improved parallelism").
+#include <type_traits>
+
 #include "fa_kernels.hpp"
 #include "fa_device.hpp"
 
@@ -20,39 +22,63 @@ namespace fa {
 // ---------------------------------------------------------------------------
 // bf16 forward.
 //
-// Per wave: IB blocks of 32 query rows. Per iteration: a tile of 64 keys.
-//   S^T (keys x queries) = K * Q^T      A = K tile from LDS, B = Q^T in VGPRs
-//   P^T = exp2(S^T*c - m*c)             column i of S^T sits in one lane pair
-//   O^T (d x queries)   += V^T * P^T    A = V^T from LDS, B = P^T from the
-//                                        S^T accumulators, rounded to bf16
-// Computing the transposed products puts one query row per lane (pair), so the
-// row max, row sum and the rescaling of O need no cross-lane traffic except
-// one v_permlane32_swap per row and tile.
+// Workgroup: 8 waves, 32 query rows per wave, 256 rows in all; tiles of 64
+// keys. Products (transposed, so that a query row lives in one lane pair):
+//   S^T (keys x queries) = K * Q^T      A = K tile (LDS), B = Q^T (VGPRs)
+//   P^T = exp2(S^T*c - m*c)             row max/sum: registers + one
+//                                        v_permlane32_swap per row and tile
+//   O^T (d x queries)   += V^T * P^T    A = V^T (LDS, transposed reads),
+//                                        B = P^T from the S^T accumulators (bf16)
+//
+// Schedule ("ping-pong"): waves 0-3 (group A) and 4-7 (group B) share the
+// four SIMDs, one of each per SIMD. Time is cut into slots separated by
+// workgroup barriers; in every slot one group runs its matrix slot
+//     S(t) = K(t) Q^T  and  O += V(t-1)^T P(t-1)      (32 MFMAs, priority 1)
+// while the other runs its vector slot
+//     mask, row max, rare rescale, P(t) = exp2(...), row sums, bf16 packing,
+// and the roles swap each slot (B runs one slot behind A). So the matrix cores
+// of a SIMD work on one wave while the vector unit serves the other.
+// K tiles go straight from global memory into LDS (buffer_load ... lds) and V
+// tiles go through group A's registers into a transposed LDS layout, so every
+// MFMA operand comes from a plain 16-byte LDS read; double buffered: in its
+// matrix slot for tile t group A issues the loads of K(t+1) and V(t), in its
+// vector slot it writes V(t) to LDS, and both are first read in slot 2t+2.
 // ---------------------------------------------------------------------------
-template <int D, int IB, int NW, bool CAUSAL>
-__global__ void __launch_bounds__(NW * 64, 1)
+
+// Rescale threshold of the online softmax, in log2 units: the reference
+// maximum of a row is moved only when a tile's maximum exceeds it by more than
+// this, so probabilities stay below 2^8 and the accumulator is rescaled rarely.
+// The result is the same function (every term and the normaliser carry the
+// same factor); only the rounding differs.
+constexpr float kRescaleLog2 = 8.f;
+constexpr int kFwdWaves = 8;
+
+__device__ __forceinline__ void wg_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+}
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }   // lgkmcnt(0)
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(kFwdWaves * 64, 1)
 fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                 float* __restrict__ LSE, int BH, int N, float c, int nqb) {
     constexpr int BC = 64;                 // keys per tile
-    constexpr int NT = NW * 64;            // threads per workgroup
-    constexpr int BR = NW * IB * 32;       // query rows per workgroup
-    constexpr int DCH = D / 8;             // 16-byte chunks per row
+    constexpr int BR = kFwdWaves * 32;     // query rows per workgroup
     constexpr int KS = D / 16;             // MFMA k-steps over d
     constexpr int NB = D / 32;             // 32-wide blocks of the output columns
-    constexpr int KT_BYTES = BC * D * 2;
-    constexpr int VT_BYTES = D * BC * 2;
-    constexpr int BUF_BYTES = KT_BYTES + VT_BYTES;
-    constexpr int K_LOADS = BC * DCH / NT;             // 16-byte K chunks per thread
-    constexpr int V_UNITS = (BC / 4) * DCH;            // 4-key x 8-column V micro-tiles
-    constexpr int V_LOADS = (V_UNITS + NT - 1) / NT;
-    static_assert(BC * DCH % NT == 0, "K tile must split evenly over the threads");
+    constexpr int TILE = BC * D * 2;
+    constexpr int BLOCKS = TILE / 1024;    // 1 KB staging blocks per tile
 
-    __shared__ __attribute__((aligned(16))) char smem[2 * BUF_BYTES];
+    __shared__ __attribute__((aligned(16))) char kb0[TILE], kb1[TILE], vb0[TILE], vb1[TILE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2;             // 0: group A, 1: group B
     const int g = lane >> 5;
     const int l32 = lane & 31;
 
@@ -70,227 +96,233 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* Kh = K + head;
     const uint16_t* Vh = V + head;
     const int q0 = qb * BR;
-    const int wq0 = q0 + wave * IB * 32;
+    const int wq0 = q0 + wave * 32;
+    const int qi = wq0 + l32;              // this lane's query row
 
-    // Q^T operand fragments, resident for the whole kernel.
-    u32x4_t qf[IB][KS];
+    // Q^T operand fragments, resident for the whole kernel. Rows past the end
+    // read row N-1 (finite data, never stored).
+    u32x4_t qf[KS];
+    {
+        const int qr = min(qi, N - 1);
 #pragma unroll
-    for (int ib = 0; ib < IB; ++ib) {
-        const int qi = wq0 + 32 * ib + l32;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            if (qi < N)
-                qf[ib][s] = *(const u32x4_t*)(Qh + (size_t)qi * D + 16 * s + 8 * g);
-            else
-                qf[ib][s] = u32x4_t{0u, 0u, 0u, 0u};
-        }
+        for (int s = 0; s < KS; ++s)
+            qf[s] = *(const u32x4_t*)(Qh + (size_t)qr * D + 16 * s + 8 * g);
     }
 
     const int n_all = (N + BC - 1) / BC;
     const int q_last = min(q0 + BR, N) - 1;
     const int n_tiles = CAUSAL ? min(n_all, q_last / BC + 1) : n_all;
 
-    u32x4_t kreg[K_LOADS];
-    u32x4_t vreg[V_LOADS][4];
+    // Buffer i of K / V (selects, not an array: LDS addresses stay scalar).
+    auto Kb = [&](int i) { return i ? (lds_char*)kb1 : (lds_char*)kb0; };
+    auto Vb = [&](int i) { return i ? (lds_char*)vb1 : (lds_char*)vb0; };
 
-    auto load_tile = [&](int kv0) {
+    // m_ref: reference maximum (raw score units) of this lane's row; the
+    // probabilities of a tile are exp2((s - m_ref) c) <= 2^kRescaleLog2.
+    const float thresh = kRescaleLog2 / c;
+    float m_ref = kNegInf, l_run = 0.f;
+    f32x16_t acc_o[NB], acc_s[2];
+    u32x4_t pf[4];
 #pragma unroll
-        for (int it = 0; it < K_LOADS; ++it) {
-            const int cidx = tid + it * NT;
-            const int row = cidx / DCH, ch = cidx % DCH;
-            const int j = kv0 + row;
-            kreg[it] = (j < N) ? *(const u32x4_t*)(Kh + (size_t)j * D + ch * 8)
-                               : u32x4_t{0u, 0u, 0u, 0u};
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc_o[nb][r] = 0.f;
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) pf[t4] = u32x4_t{0u, 0u, 0u, 0u};
+
+    // K(t+1) goes straight into LDS (group A, buffer_load ... lds). V(t) goes
+    // through registers into a transposed layout ([d][64 keys], the permuted
+    // key order of fa_device.hpp) so the matrix slot reads V^T fragments with
+    // plain 16-byte LDS reads: each group moves half of the 4-key x 8-column
+    // micro-tiles, loading them in its matrix slot and writing them in its
+    // next vector slot. Rows past N read row N-1 (masked keys).
+    constexpr int DCH = D / 8;
+    constexpr int V_UNITS = 16 * DCH;                  // 4-key x 8-column micro-tiles
+    constexpr int V_HALF = V_UNITS / 2;                // per group
+    constexpr int V_PER_LANE = (V_HALF + 255) / 256;
+    u32x4_t vreg[V_PER_LANE][4];
+    const int vbase = grp * V_HALF + (wave & 3) * 64 + lane;
+    auto v_load = [&](int t) {
+#pragma unroll
+        for (int k = 0; k < V_PER_LANE; ++k) {
+            const int u = vbase + 256 * k;
+            if (V_HALF % 256 != 0 && u >= grp * V_HALF + V_HALF) continue;
+            const int ch = u % DCH, rg = u / DCH;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int j = min(t * BC + 4 * rg + rr, N - 1);
+                vreg[k][rr] = *(const u32x4_t*)(Vh + (size_t)j * D + ch * 8);
+            }
         }
+    };
+    auto v_store = [&](int t) {
+        lds_char* vl = Vb(t & 1);
 #pragma unroll
-        for (int it = 0; it < V_LOADS; ++it) {
-            const int u = tid + it * NT;
-            if (V_UNITS % NT == 0 || u < V_UNITS) {
-                const int ch = u % DCH, rg = u / DCH;
+        for (int k = 0; k < V_PER_LANE; ++k) {
+            const int u = vbase + 256 * k;
+            if (V_HALF % 256 != 0 && u >= grp * V_HALF + V_HALF) continue;
+            const int ch = u % DCH, rg = u / DCH;
+            const int slot = tr_key_position(4 * rg) >> 2;
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const int j = kv0 + 4 * rg + rr;
-                    vreg[it][rr] = (j < N) ? *(const u32x4_t*)(Vh + (size_t)j * D + ch * 8)
-                                           : u32x4_t{0u, 0u, 0u, 0u};
+            for (int e = 0; e < 8; ++e) {
+                const int w = e >> 1;
+                const uint32_t r0 = vreg[k][0][w], r1 = vreg[k][1][w];
+                const uint32_t r2 = vreg[k][2][w], r3 = vreg[k][3][w];
+                u32x2_t col;
+                if (e & 1) {
+                    col[0] = (r0 >> 16) | (r1 & 0xffff0000u);
+                    col[1] = (r2 >> 16) | (r3 & 0xffff0000u);
+                } else {
+                    col[0] = (r0 & 0xffffu) | (r1 << 16);
+                    col[1] = (r2 & 0xffffu) | (r3 << 16);
                 }
+                *(__attribute__((address_space(3))) u32x2_t*)(vl + tr_slot_offset(ch * 8 + e, slot)) = col;
             }
         }
     };
 
-    auto store_tile = [&](int buf) {
-        char* kl = smem + buf * BUF_BYTES;
-        char* vl = kl + KT_BYTES;
+    // Matrix slot of tile t: S(t) = K(t) Q^T and O += V(t-1)^T P(t-1),
+    // interleaved MFMA by MFMA, each MFMA's 16-byte LDS fragment read four
+    // MFMAs ahead. In the first slot P = 0 and the V buffer holds zeros; in
+    // the last one S reads a stale K buffer and is discarded.
+    auto matrix_slot = [&](int t) {
+        __builtin_amdgcn_s_setprio(1);
+        const lds_char* kt = Kb(t & 1);
+        const lds_char* vt = Vb((t + 1) & 1);      // V(t-1)
 #pragma unroll
-        for (int it = 0; it < K_LOADS; ++it) {
-            const int cidx = tid + it * NT;
-            const int row = cidx / DCH, ch = cidx % DCH;
-            *(u32x4_t*)(kl + row_chunk_offset<D>(row, ch)) = kreg[it];
-        }
+        for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
-        for (int it = 0; it < V_LOADS; ++it) {
-            const int u = tid + it * NT;
-            if (V_UNITS % NT == 0 || u < V_UNITS) {
-                const int ch = u % DCH, rg = u / DCH;
-                const int slot = tr_key_position(4 * rg) >> 2;
+            for (int r = 0; r < 16; ++r) acc_s[jb][r] = 0.f;
+        constexpr int NS = 2 * KS, NP = 4 * NB;       // MFMAs of S(t) and of P V
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int w = e >> 1;
-                    const uint32_t r0 = vreg[it][0][w], r1 = vreg[it][1][w];
-                    const uint32_t r2 = vreg[it][2][w], r3 = vreg[it][3][w];
-                    u32x2_t col;
-                    if (e & 1) {
-                        col[0] = (r0 >> 16) | (r1 & 0xffff0000u);
-                        col[1] = (r2 >> 16) | (r3 & 0xffff0000u);
-                    } else {
-                        col[0] = (r0 & 0xffffu) | (r1 << 16);
-                        col[1] = (r2 & 0xffffu) | (r3 << 16);
-                    }
-                    *(u32x2_t*)(vl + tr_slot_offset(ch * 8 + e, slot)) = col;
-                }
+        for (int x = 0; x < (NS > NP ? NS : NP); ++x) {
+            if (x < NS) {
+                const int s = x >> 1, jb = x & 1;
+                acc_s[jb] = mfma_32x32x16(lds_k_frag<D>(kt, 32 * jb + l32, 2 * s + g), qf[s],
+                                          acc_s[jb]);
+            }
+            if (x < NP) {
+                const int t4 = x / NB, nb = x % NB;
+                const u32x4_t vf = *(const __attribute__((address_space(3))) u32x4_t*)(
+                    vt + tr_slot_offset(32 * nb + l32, 4 * t4 + 2 * g));
+                acc_o[nb] = mfma_32x32x16(vf, pf[t4], acc_o[nb]);
             }
         }
+        // One LDS read per MFMA: four reads ahead, then alternate.
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int x = 0; x < NS + NP - 4; ++x) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        __builtin_amdgcn_s_setprio(0);
+        wait_lds();
     };
 
-    float m_run[IB], l_run[IB];
-    f32x16_t acc_o[NB][IB];
-#pragma unroll
-    for (int ib = 0; ib < IB; ++ib) {
-        m_run[ib] = kNegInf;
-        l_run[ib] = 0.f;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc_o[nb][ib][r] = 0.f;
-    }
-
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-
-    const int wave_last = wq0 + IB * 32 - 1;
-    for (int t = 0; t < n_tiles; ++t) {
+    // Vector slot of tile t: softmax of S(t) into P(t).
+    auto vector_slot = [&](int t) {
         const int kv0 = t * BC;
-        if (t + 1 < n_tiles) load_tile(kv0 + BC);
-        const char* kl = smem + (t & 1) * BUF_BYTES;
-        const char* vl = kl + KT_BYTES;
-
-        if (!CAUSAL || kv0 <= wave_last) {
-            // ---- S^T = K Q^T -------------------------------------------------
-            f32x16_t acc_s[2][IB];
+        const bool need_mask = (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > q0);
+        if (need_mask) {
 #pragma unroll
             for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
-                for (int ib = 0; ib < IB; ++ib)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc_s[jb][ib][r] = 0.f;
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-#pragma unroll
-                for (int jb = 0; jb < 2; ++jb) {
-                    const u32x4_t kf =
-                        *(const u32x4_t*)(kl + row_chunk_offset<D>(32 * jb + l32, 2 * s + g));
-#pragma unroll
-                    for (int ib = 0; ib < IB; ++ib)
-                        acc_s[jb][ib] = mfma_32x32x16(kf, qf[ib][s], acc_s[jb][ib]);
+                for (int r = 0; r < 16; ++r) {
+                    const int j = kv0 + 32 * jb + 8 * (r >> 2) + 4 * g + (r & 3);
+                    if ((j >= N) || (CAUSAL && j > qi)) acc_s[jb][r] = kNegInf;
                 }
-            }
-
-            // ---- mask: keys past the end, and keys after the query (causal) --
-            const bool need_mask = (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > wq0);
-            if (need_mask) {
-#pragma unroll
-                for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-                    for (int ib = 0; ib < IB; ++ib) {
-                        const int qi = wq0 + 32 * ib + l32;
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int j = kv0 + 32 * jb + 8 * (r >> 2) + 4 * g + (r & 3);
-                            const bool masked = (j >= N) || (CAUSAL && j > qi);
-                            if (masked) acc_s[jb][ib][r] = kNegInf;
-                        }
-                    }
-            }
-
-            // ---- online softmax (one query row per lane pair) -----------------
-            u32x4_t pf[IB][4];
-#pragma unroll
-            for (int ib = 0; ib < IB; ++ib) {
-                float mt = acc_s[0][ib][0];
-#pragma unroll
-                for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) mt = fmaxf(mt, acc_s[jb][ib][r]);
-                mt = max_with_partner32(mt);
-                const float m_new = fmaxf(m_run[ib], mt);
-                const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-                const float alpha =
-                    (m_run[ib] == kNegInf) ? 0.f : fast_exp2((m_run[ib] - m_use) * c);
-                const float mc = m_use * c;
-                float ls = 0.f;
-#pragma unroll
-                for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const float p = fast_exp2(__builtin_fmaf(acc_s[jb][ib][r], c, -mc));
-                        acc_s[jb][ib][r] = p;
-                        ls += p;
-                    }
-                l_run[ib] = l_run[ib] * alpha + ls;
-                m_run[ib] = m_new;
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc_o[nb][ib][r] *= alpha;
-#pragma unroll
-                for (int t4 = 0; t4 < 4; ++t4) {
-                    const int jb = t4 >> 1, rb = 8 * (t4 & 1);
-                    pf[ib][t4] = u32x4_t{pack_bf16x2(acc_s[jb][ib][rb + 0], acc_s[jb][ib][rb + 1]),
-                                         pack_bf16x2(acc_s[jb][ib][rb + 2], acc_s[jb][ib][rb + 3]),
-                                         pack_bf16x2(acc_s[jb][ib][rb + 4], acc_s[jb][ib][rb + 5]),
-                                         pack_bf16x2(acc_s[jb][ib][rb + 6], acc_s[jb][ib][rb + 7])};
-                }
-            }
-
-            // ---- O^T += V^T P^T ----------------------------------------------
-#pragma unroll
-            for (int t4 = 0; t4 < 4; ++t4) {
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    const u32x4_t vf =
-                        *(const u32x4_t*)(vl + tr_slot_offset(32 * nb + l32, 4 * t4 + 2 * g));
-#pragma unroll
-                    for (int ib = 0; ib < IB; ++ib)
-                        acc_o[nb][ib] = mfma_32x32x16(vf, pf[ib][t4], acc_o[nb][ib]);
-                }
-            }
         }
-
-        if (t + 1 < n_tiles) store_tile((t + 1) & 1);
-        __syncthreads();
-    }
-
-    // ---- epilogue: deferred normalisation, logsumexp, bf16 store ------------
+        float m = fmaxf(acc_s[0][0], acc_s[0][1]);
 #pragma unroll
-    for (int ib = 0; ib < IB; ++ib) {
-        const float l = sum_with_partner32(l_run[ib]);
-        const int qi = wq0 + 32 * ib + l32;
-        if (qi < N) {
-            const float inv = (l > 0.f) ? 1.f / l : 0.f;
-            const float m_use = (m_run[ib] == kNegInf) ? 0.f : m_run[ib];
-            if (g == 0)
-                LSE[(size_t)bh * N + qi] = (l > 0.f) ? (m_use * c + fast_log2(l)) * kLn2 : kNegInf;
-            uint16_t* orow = O + head + (size_t)qi * D;
+        for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) m = fmaxf(m, acc_s[jb][r]);
+        const float mt = max_with_partner32(m);
+        if (__any(mt > m_ref + thresh)) {
+            // Rare: move the reference maximum up and rescale what has been
+            // accumulated so far by exp2((m_old - m_new) c).
+            const float m_new = fmaxf(m_ref, mt);
+            const float alpha = (m_ref == kNegInf) ? 0.f : fast_exp2((m_ref - m_new) * c);
+            l_run *= alpha;
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    u32x2_t w;
-                    w[0] = pack_bf16x2(acc_o[nb][ib][4 * q4 + 0] * inv, acc_o[nb][ib][4 * q4 + 1] * inv);
-                    w[1] = pack_bf16x2(acc_o[nb][ib][4 * q4 + 2] * inv, acc_o[nb][ib][4 * q4 + 3] * inv);
-                    *(u32x2_t*)(orow + 32 * nb + 8 * q4 + 4 * g) = w;
-                }
+                for (int r = 0; r < 16; ++r) acc_o[nb][r] *= alpha;
+            m_ref = m_new;
         }
+        const float mc = (m_ref == kNegInf) ? 0.f : m_ref * c;
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4) {
+            const int jb = t4 >> 1, rb = 8 * (t4 & 1);
+            float p[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                p[e] = fast_exp2(__builtin_fmaf(acc_s[jb][rb + e], c, -mc));
+                l_run += p[e];      // fp32 sum of the unrounded probabilities
+            }
+            pf[t4] = u32x4_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                             pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+        }
+    };
+
+    // ---- prologue: K(0) into LDS, zeros into the V buffer of "tile -1" -----
+    if (grp == 0) stage_tile_lds<D, BLOCKS / 4, 4, false>(Kh, Kb(0), 0, N, wave, lane);
+    for (int i = tid; i < TILE / 16; i += kFwdWaves * 64)
+        *(__attribute__((address_space(3))) u32x4_t*)(Vb(1) + 16 * i) = u32x4_t{0u, 0u, 0u, 0u};
+    wait_vmem();
+    __syncthreads();
+    if (grp == 1) {                        // group B runs one slot behind; it
+        v_load(0);                         // writes its half of V(0) meanwhile
+        v_store(0);
+        wait_vmem();
+        wg_barrier();
+    }
+
+    // Slot 2t: A matrix(t), B vector(t-1); slot 2t+1: A vector(t), B matrix(t).
+    // V(t) is written in slots 2t+1 (A's half) and 2t (B's half, loaded in
+    // slot 2t-1; V(0) in the prologue) into the buffer V(t-2) left; K(t+1) is
+    // loaded by A in slot 2t. All of them are first read in slot 2t+2.
+    for (int t = 0; t <= n_tiles; ++t) {
+        matrix_slot(t);
+        if (t < n_tiles) {
+            if (grp == 0) {
+                if (t + 1 < n_tiles)
+                    stage_tile_lds<D, BLOCKS / 4, 4, false>(Kh, Kb((t + 1) & 1), (t + 1) * BC, N,
+                                                            wave, lane);
+                v_load(t);
+            } else if (t + 1 < n_tiles) {
+                v_load(t + 1);
+            }
+        }
+        wg_barrier();
+        if (t < n_tiles) {
+            vector_slot(t);
+            if (grp == 0) v_store(t);
+            else if (t + 1 < n_tiles) v_store(t + 1);
+            wait_vmem();
+            wg_barrier();
+        }
+    }
+    if (grp == 0) wg_barrier();            // same number of barriers in both groups
+
+    // ---- epilogue: deferred normalisation, logsumexp, bf16 store ------------
+    const float l = sum_with_partner32(l_run);
+    if (qi < N) {
+        const float inv = (l > 0.f) ? 1.f / l : 0.f;
+        const float mc = (m_ref == kNegInf) ? 0.f : m_ref * c;
+        if (g == 0)
+            LSE[(size_t)bh * N + qi] = (l > 0.f) ? (mc + fast_log2(l)) * kLn2 : kNegInf;
+        uint16_t* orow = O + head + (size_t)qi * D;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                u32x2_t w;
+                w[0] = pack_bf16x2(acc_o[nb][4 * q4 + 0] * inv, acc_o[nb][4 * q4 + 1] * inv);
+                w[1] = pack_bf16x2(acc_o[nb][4 * q4 + 2] * inv, acc_o[nb][4 * q4 + 3] * inv);
+                *(u32x2_t*)(orow + 32 * nb + 8 * q4 + 4 * g) = w;
+            }
     }
 }
 
@@ -399,13 +431,11 @@ fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
 static hipError_t launch_fwd_bf16_t(const FwdArgs& a) {
-    constexpr int IB = FwdBf16Config<D>::IB;
-    constexpr int NW = FwdBf16Config<D>::NW;
-    constexpr int BR = NW * IB * 32;
+    constexpr int BR = kFwdWaves * 32;
     const int BH = a.B * a.H;
     const int nqb = (a.N + BR - 1) / BR;
     const float c = a.scale * kLog2e;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, IB, NW, CAUSAL>), dim3(nqb * BH), dim3(NW * 64), 0,
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3(nqb * BH), dim3(kFwdWaves * 64), 0,
                        a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                        (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, BH, a.N, c, nqb);
     return hipGetLastError();

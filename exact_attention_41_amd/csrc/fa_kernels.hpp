@@ -50,10 +50,6 @@ struct BwdWorkspace {
 BwdWorkspace bwd_workspace_layout(long long B, long long H, long long N, long long d);
 
 
-// Tile shape of the bf16 forward: IB blocks of 32 query rows per wave,
-// NW waves per workgroup.
-template <int D> struct FwdBf16Config { static constexpr int IB = 2; static constexpr int NW = 4; };
-
 hipError_t launch_fwd_bf16(const FwdArgs& a);
 hipError_t launch_fwd_f32(const FwdArgs& a);
 hipError_t launch_bwd_scales(const BwdArgs& a);
