@@ -120,7 +120,7 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     // m_ref: reference maximum (raw score units) of this lane's row; the
     // probabilities of a tile are exp2((s - m_ref) c) <= 2^kRescaleLog2.
     const float thresh = kRescaleLog2 / c;
-    float m_ref = kNegInf, l_run = 0.f;
+    float m_ref = kNegInf, l_run = 0.f, l_rnd = 0.f;
     f32x16_t acc_o[NB], acc_s[2];
     u32x4_t pf[4];
 #pragma unroll
@@ -245,6 +245,7 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             const float m_new = fmaxf(m_ref, mt);
             const float alpha = (m_ref == kNegInf) ? 0.f : fast_exp2((m_ref - m_new) * c);
             l_run *= alpha;
+            l_rnd *= alpha;
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -259,10 +260,15 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 p[e] = fast_exp2(__builtin_fmaf(acc_s[jb][rb + e], c, -mc));
-                l_run += p[e];      // fp32 sum of the unrounded probabilities
+                l_run += p[e];      // fp32 sum of the unrounded probabilities (lse)
             }
             pf[t4] = u32x4_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
                              pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+            // Sum of the bf16 probabilities that multiply V: normalising O by
+            // it makes the rounding error of P scale with (v_j - O) instead of
+            // v_j (zero for a row dominated by one key).
+#pragma unroll
+            for (int w = 0; w < 4; ++w) l_rnd = add_bf16x2(pf[t4][w], l_rnd);
         }
     };
 
@@ -308,8 +314,9 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
     // ---- epilogue: deferred normalisation, logsumexp, bf16 store ------------
     const float l = sum_with_partner32(l_run);
+    const float lr = sum_with_partner32(l_rnd);
     if (qi < N) {
-        const float inv = (l > 0.f) ? 1.f / l : 0.f;
+        const float inv = (lr > 0.f) ? 1.f / lr : 0.f;
         const float mc = (m_ref == kNegInf) ? 0.f : m_ref * c;
         if (g == 0)
             LSE[(size_t)bh * N + qi] = (l > 0.f) ? (mc + fast_log2(l)) * kLn2 : kNegInf;
