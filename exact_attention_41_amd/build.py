@@ -17,6 +17,14 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libfa.so")
 SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_bwd.hip"]
+# Per-source flags. The backward kernels keep their gradient accumulators in
+# AGPRs through inline assembly; every other matrix product there should
+# write VGPRs, where the VALU reads its results, rather than the compiler's
+# AGPR form for kernels that own a whole SIMD. Their per-tile software
+# pipeline is one fully unrolled loop, larger than the default size limit
+# for an unroll pragma.
+SOURCE_FLAGS = {"fa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1",
+                               "-mllvm", "-pragma-unroll-threshold=100000"]}
 ARCH = "gfx950"
 
 
@@ -60,7 +68,8 @@ def build(verbose: bool = False, extra_flags=(), out_path: str = LIB_PATH) -> st
         for src in SOURCES:
             obj = os.path.join(tmp, src.replace(".hip", ".o"))
             objs.append(obj)
-            cmds.append([cc, *compile_flags(extra_flags), "-c", os.path.join(CSRC, src), "-o", obj])
+            flags = compile_flags([*SOURCE_FLAGS.get(src, []), *extra_flags])
+            cmds.append([cc, *flags, "-c", os.path.join(CSRC, src), "-o", obj])
         with cf.ThreadPoolExecutor(max_workers=len(cmds)) as ex:
             list(ex.map(lambda c: _run(c, verbose), cmds))
         tmp_out = out_path + ".tmp"
@@ -75,7 +84,7 @@ def resource_report(src: str = "fa_fwd.hip") -> str:
     """Per-kernel register/LDS/scratch report of one source (device pass only)."""
     cc = hipcc()
     with tempfile.TemporaryDirectory() as tmp:
-        cmd = [cc, *compile_flags(["-Rpass-analysis=kernel-resource-usage"]),
+        cmd = [cc, *compile_flags([*SOURCE_FLAGS.get(src, []), "-Rpass-analysis=kernel-resource-usage"]),
                "--cuda-device-only", "-c", os.path.join(CSRC, src), "-o", os.path.join(tmp, "x.o")]
         res = subprocess.run(cmd, capture_output=True, text=True)
         if res.returncode != 0:

@@ -122,7 +122,8 @@ bwd_scale_kernel(const uint32_t* __restrict__ partial, float* __restrict__ scale
 // 4-row x 8-column micro-tiles: row-major (swizzled 16-byte chunks) and/or
 // transposed ([D][64], permuted key order and slot swizzle of fa_device.hpp).
 // With CVT the source is bf16 and the transposed copy is fp16 of the value
-// times a power of two. Rows at or past N are zero-filled.
+// times a power of two. Rows at or past N repeat row N-1 (finite values that
+// the callers' masks multiply by zero).
 // ---------------------------------------------------------------------------
 template <int D, int NT>
 struct Tile64 {
@@ -140,9 +141,8 @@ struct Tile64 {
                 const int ch = u % DCH, rg = u / DCH;
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) {
-                    const int row = row0 + 4 * rg + rr;
-                    r[it][rr] = (row < N) ? *(const u32x4_t*)(src + (size_t)row * D + ch * 8)
-                                          : u32x4_t{0u, 0u, 0u, 0u};
+                    const int row = min(row0 + 4 * rg + rr, N - 1);
+                    r[it][rr] = *(const u32x4_t*)(src + (size_t)row * D + ch * 8);
                 }
             }
         }
@@ -233,7 +233,7 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, l32 = lane & 31;
     const int bid = blockIdx.x;
     const int bh = bid % BH;
@@ -299,62 +299,80 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     store(0);
     __syncthreads();
 
-    const int wave_last = wq0 + 31;
     for (int t = 0; t < n_tiles; ++t) {
         const int j0 = t * BC;
         if (t + 1 < n_tiles) load(j0 + BC);
         const char* b = smem + (t & 1) * BUF;
 
-        if (!CAUSAL || j0 <= wave_last) {
-            f32x16_t acc_s[2], acc_dp[2];
-#pragma unroll
-            for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc_s[jb][r] = acc_dp[jb][r] = 0.f;
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-#pragma unroll
-                for (int jb = 0; jb < 2; ++jb) {
-                    const u32x4_t ka = lds_row_frag<D>(b + OFF_K, 32 * jb + l32, 2 * s + g);
-                    acc_s[jb] = mfma_32x32x16(ka, qf[s], acc_s[jb]);
-                    const u32x4_t va = lds_row_frag<D>(b + OFF_V, 32 * jb + l32, 2 * s + g);
-                    acc_dp[jb] = mfma_32x32x16(va, of[s], acc_dp[jb]);
-                }
-            }
-
+        {   // waves whose rows all precede the tile compute it fully masked
             const bool need_mask = (j0 + BC > N) || (CAUSAL && j0 + BC - 1 > wq0);
-            u32x4_t pf[4], ef[4];
-#pragma unroll
-            for (int jb = 0; jb < 2; ++jb) {
-                float pv[16], ev[16];
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int j = j0 + 32 * jb + 8 * (r >> 2) + 4 * g + (r & 3);
-                    float p = fast_exp2(__builtin_fmaf(acc_s[jb][r], c, -lse2));
-                    if (need_mask && (j >= N || (CAUSAL && j > qi))) p = 0.f;
-                    const float e = p * acc_dp[jb][r];
-                    dsum += e;
-                    pv[r] = p;
-                    ev[r] = e;
+            // One software pipeline per key tile: S, dP of key half 0, then of
+            // half 1 (while half 0 is exponentiated), then the two dQ sums
+            // over four 16-key steps (the first two while half 1 is
+            // exponentiated); a dQ step's K~^T fragment feeds both sums.
+            // Fragments are read LA steps ahead; sched_barrier keeps that order.
+            constexpr int NSD = 2 * KS;
+            constexpr int NOPS = 2 * NSD + 4 * NB;
+            constexpr int LA = 4;
+            constexpr int EPO_A = 16 / NSD;
+            constexpr int EPO_B = 16 / (2 * NB);
+            auto frag_ptr = [&](int o) -> const char* {
+                if (o < 2 * NSD) {
+                    const int jb = o / NSD, w = o % NSD;
+                    return b + ((w & 1) ? OFF_V : OFF_K) +
+                           row_chunk_offset<D>(32 * jb + l32, 2 * (w >> 1) + g);
                 }
+                const int w = o - 2 * NSD, t4 = w / NB, nb = w % NB;
+                return b + OFF_KT + tr_slot_offset(32 * nb + l32, 2 * (2 * t4 + g));
+            };
+
+            u32x4_t fr[LA + 1];
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int rb = 8 * h;
+            for (int o = 0; o < LA; ++o) fr[o] = *(const u32x4_t*)frag_ptr(o);
+
+            const f32x16_t zero16 = {};
+            f32x16_t sa[2], da[2];
+            float pv[16], ev[16];
+            u32x4_t pf[4], ef[4];
+            auto softmax_elem = [&](int jb, int r) {
+                const int j = j0 + 32 * jb + 8 * (r >> 2) + 4 * g + (r & 3);
+                float p = fast_exp2(__builtin_fmaf(sa[jb][r], c, -lse2));
+                if (need_mask && (j >= N || (CAUSAL && j > qi))) p = 0.f;
+                const float e = p * da[jb][r];
+                dsum += e;
+                pv[r] = p;
+                ev[r] = e;
+                if ((r & 7) == 7) {
+                    const int h = r >> 3, rb = 8 * h;
                     pf[2 * jb + h] = u32x4_t{pack_f16x2(pv[rb + 0], pv[rb + 1]), pack_f16x2(pv[rb + 2], pv[rb + 3]),
                                              pack_f16x2(pv[rb + 4], pv[rb + 5]), pack_f16x2(pv[rb + 6], pv[rb + 7])};
                     ef[2 * jb + h] = u32x4_t{pack_f16x2(ev[rb + 0], ev[rb + 1]), pack_f16x2(ev[rb + 2], ev[rb + 3]),
                                              pack_f16x2(ev[rb + 4], ev[rb + 5]), pack_f16x2(ev[rb + 6], ev[rb + 7])};
                 }
-            }
+            };
 
 #pragma unroll
-            for (int t4 = 0; t4 < 4; ++t4) {
+            for (int o = 0; o < NOPS; ++o) {
+                if (o + LA < NOPS) fr[(o + LA) % (LA + 1)] = *(const u32x4_t*)frag_ptr(o + LA);
+                const u32x4_t a = fr[o % (LA + 1)];
+                if (o < 2 * NSD) {
+                    const int jb = o / NSD, w = o % NSD, st = w >> 1;
+                    if (w & 1) da[jb] = mfma_32x32x16(a, of[st], st == 0 ? zero16 : da[jb]);
+                    else sa[jb] = mfma_32x32x16(a, qf[st], st == 0 ? zero16 : sa[jb]);
+                    if (jb == 1) {
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    const u32x4_t a = lds_tr_frag(b + OFF_KT, 32 * nb + l32, 2 * t4 + g);
-                    acc_a[nb] = mfma_32x32x16_f16(a, ef[t4], acc_a[nb]);
-                    acc_b[nb] = mfma_32x32x16_f16(a, pf[t4], acc_b[nb]);
+                        for (int e = 0; e < EPO_A; ++e) softmax_elem(0, w * EPO_A + e);
+                    }
+                } else {
+                    const int w = o - 2 * NSD, t4 = w / NB, nb = w % NB;
+                    mfma_f16_agpr(acc_a[nb], a, ef[t4]);
+                    mfma_f16_agpr(acc_b[nb], a, pf[t4]);
+                    if (t4 < 2) {
+#pragma unroll
+                        for (int e = 0; e < EPO_B; ++e) softmax_elem(1, w * EPO_B + e);
+                    }
                 }
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
 
@@ -362,6 +380,11 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         __syncthreads();
     }
 
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        agpr_settle(acc_a[nb]);
+        agpr_settle(acc_b[nb]);
+    }
     const float dt = sum_with_partner32(dsum);    // D~ = sE * D
     if (qi < N) {
         if (g == 0) delta[(size_t)bh * N + qi] = dt / sE;
@@ -415,7 +438,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q16, const uint16_t* __restrict__ K
     __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, l32 = lane & 31;
     const int bid = blockIdx.x;
     const int bh = bid % BH;
@@ -461,16 +484,18 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q16, const uint16_t* __restrict__ K
     const int t0 = CAUSAL ? (k0 / BQ) : 0;
 
     TileT qt, dot;
-    float stat = 0.f;   // lse*log2e (threads 0..63) or sE*D (64..127) of the next tile
+    // Threads 0..63 carry the next tile's lse, 64..127 its D (the others load
+    // a harmless copy); the value is scaled only when stored, so that the
+    // load is waited for at the end of the tile, not at its start.
+    float stat = 0.f;
+    int stat_row = 0;
+    const float* stat_src = (tid < BQ) ? lse_h : del_h;
 
     auto load = [&](int i0) {
         qt.load(Qh, i0, N, tid);
         dot.load(dOh, i0, N, tid);
-        if (tid < 2 * BQ) {
-            const int i = i0 + (tid & (BQ - 1));
-            if (tid < BQ) stat = (i < N) ? lse_h[i] * kLog2e : __builtin_huge_valf();
-            else stat = (i < N) ? del_h[i] * sE : 0.f;
-        }
+        stat_row = i0 + (tid & (BQ - 1));
+        stat = stat_src[min(stat_row, N - 1)];
     };
     auto store = [&](int buf) {
         char* b = smem + buf * BUF;
@@ -478,7 +503,12 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q16, const uint16_t* __restrict__ K
         qt.template store_transposed<false>(b + OFF_QT, tid);
         dot.store_rowmajor(b + OFF_DO, tid);
         dot.template store_transposed<false>(b + OFF_DOT, tid);
-        if (tid < 2 * BQ) ((float*)(b + OFF_LSE))[tid] = stat;
+        if (tid < 2 * BQ) {
+            const bool in = stat_row < N;
+            const float v = (tid < BQ) ? (in ? stat * kLog2e : __builtin_huge_valf())
+                                       : (in ? stat * sE : 0.f);
+            ((float*)(b + OFF_LSE))[tid] = v;
+        }
     };
 
     if (t0 < n_tiles) {
@@ -493,63 +523,86 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q16, const uint16_t* __restrict__ K
         if (t + 1 < n_tiles) load(i0 + BQ);
         const char* b = smem + buf * BUF;
 
-        if (!CAUSAL || i0 + BQ - 1 >= kw0) {
-            f32x16_t acc_s[2], acc_dp[2];
-#pragma unroll
-            for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc_s[ib][r] = acc_dp[ib][r] = 0.f;
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-#pragma unroll
-                for (int ib = 0; ib < 2; ++ib) {
-                    const u32x4_t qa = lds_row_frag<D>(b + OFF_Q, 32 * ib + l32, 2 * s + g);
-                    acc_s[ib] = mfma_32x32x16_f16(qa, kf[s], acc_s[ib]);
-                    const u32x4_t da = lds_row_frag<D>(b + OFF_DO, 32 * ib + l32, 2 * s + g);
-                    acc_dp[ib] = mfma_32x32x16_f16(da, vf[s], acc_dp[ib]);
-                }
-            }
-
+        {   // waves whose keys all follow the tile compute it fully masked
             const bool need_mask = CAUSAL && (i0 < kw0 + 31);
             const float* lse_t = (const float*)(b + OFF_LSE);
             const float* del_t = (const float*)(b + OFF_DEL);
-            u32x4_t pp[4], dsp[4];
-#pragma unroll
-            for (int ib = 0; ib < 2; ++ib) {
-                float pv[16], dsv[16];
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const int ii = 32 * ib + 8 * q4 + 4 * g;
-                    const f32x4_t l4 = *(const f32x4_t*)(lse_t + ii);
-                    const f32x4_t d4 = *(const f32x4_t*)(del_t + ii);
-#pragma unroll
-                    for (int r4 = 0; r4 < 4; ++r4) {
-                        const int r = 4 * q4 + r4;
-                        float p = fast_exp2(__builtin_fmaf(acc_s[ib][r], cs, -l4[r4]));
-                        if (need_mask && kj > i0 + ii + r4) p = 0.f;
-                        pv[r] = p;
-                        dsv[r] = p * (acc_dp[ib][r] - d4[r4]);
-                    }
+            // The tile's 2*NSD + 4*NG products run as one software pipeline:
+            // S, dP of query half 0, then of half 1 (while half 0 is
+            // exponentiated), then dV, dK over four 16-query steps (the first
+            // two while half 1 is exponentiated). Each product's LDS fragment
+            // is read LA products ahead; sched_barrier keeps that order.
+            constexpr int NSD = 2 * KS;
+            constexpr int NG = 2 * NB;
+            constexpr int NOPS = 2 * NSD + 4 * NG;
+            constexpr int LA = 4;
+            constexpr int EPO_A = 16 / NSD;
+            constexpr int EPO_B = 16 / (2 * NG);
+            auto frag_ptr = [&](int o) -> const char* {
+                if (o < 2 * NSD) {
+                    const int ib = o / NSD, w = o % NSD;
+                    return b + ((w & 1) ? OFF_DO : OFF_Q) +
+                           row_chunk_offset<D>(32 * ib + l32, 2 * (w >> 1) + g);
                 }
+                const int w = o - 2 * NSD, t4 = w / NG, nb = (w % NG) >> 1;
+                return b + ((w & 1) ? OFF_QT : OFF_DOT) + tr_slot_offset(32 * nb + l32, 2 * (2 * t4 + g));
+            };
+
+            u32x4_t fr[LA + 1];
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int rb = 8 * h;
+            for (int o = 0; o < LA; ++o) fr[o] = *(const u32x4_t*)frag_ptr(o);
+
+            const f32x16_t zero16 = {};
+            f32x16_t sa[2], da[2];
+            f32x4_t l4[4], d4[4];     // lse*log2e and sE*D of the half being exponentiated
+            float pv[16], dsv[16];
+            u32x4_t pp[4], dsp[4];
+            auto read_stats = [&](int ib, int q4) {
+                l4[q4] = *(const f32x4_t*)(lse_t + 32 * ib + 8 * q4 + 4 * g);
+                d4[q4] = *(const f32x4_t*)(del_t + 32 * ib + 8 * q4 + 4 * g);
+            };
+            auto softmax_elem = [&](int ib, int r) {
+                const int q4 = r >> 2, r4 = r & 3;
+                float p = fast_exp2(__builtin_fmaf(sa[ib][r], cs, -l4[q4][r4]));
+                if (need_mask && kj > i0 + 32 * ib + 8 * q4 + 4 * g + r4) p = 0.f;
+                pv[r] = p;
+                dsv[r] = p * (da[ib][r] - d4[q4][r4]);
+                if (ib == 0 && r4 == 3) read_stats(1, q4);
+                if ((r & 7) == 7) {
+                    const int h = r >> 3, rb = 8 * h;
                     pp[2 * ib + h] = u32x4_t{pack_f16x2(pv[rb + 0], pv[rb + 1]), pack_f16x2(pv[rb + 2], pv[rb + 3]),
                                              pack_f16x2(pv[rb + 4], pv[rb + 5]), pack_f16x2(pv[rb + 6], pv[rb + 7])};
                     dsp[2 * ib + h] = u32x4_t{pack_f16x2(dsv[rb + 0], dsv[rb + 1]), pack_f16x2(dsv[rb + 2], dsv[rb + 3]),
                                               pack_f16x2(dsv[rb + 4], dsv[rb + 5]), pack_f16x2(dsv[rb + 6], dsv[rb + 7])};
                 }
-            }
+            };
 
 #pragma unroll
-            for (int t4 = 0; t4 < 4; ++t4) {
+            for (int o = 0; o < NOPS; ++o) {
+                if (o + LA < NOPS) fr[(o + LA) % (LA + 1)] = *(const u32x4_t*)frag_ptr(o + LA);
+                const u32x4_t a = fr[o % (LA + 1)];
+                if (o == 0) {
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    const u32x4_t a1 = lds_tr_frag(b + OFF_DOT, 32 * nb + l32, 2 * t4 + g);
-                    acc_dv[nb] = mfma_32x32x16_f16(a1, pp[t4], acc_dv[nb]);
-                    const u32x4_t a2 = lds_tr_frag(b + OFF_QT, 32 * nb + l32, 2 * t4 + g);
-                    acc_dk[nb] = mfma_32x32x16_f16(a2, dsp[t4], acc_dk[nb]);
+                    for (int q4 = 0; q4 < 4; ++q4) read_stats(0, q4);
                 }
+                if (o < 2 * NSD) {
+                    const int ib = o / NSD, w = o % NSD, st = w >> 1;
+                    if (w & 1) da[ib] = mfma_32x32x16_f16(a, vf[st], st == 0 ? zero16 : da[ib]);
+                    else sa[ib] = mfma_32x32x16_f16(a, kf[st], st == 0 ? zero16 : sa[ib]);
+                    if (ib == 1) {
+#pragma unroll
+                        for (int e = 0; e < EPO_A; ++e) softmax_elem(0, w * EPO_A + e);
+                    }
+                } else {
+                    const int w = o - 2 * NSD, t4 = w / NG, nb = (w % NG) >> 1;
+                    if (w & 1) mfma_f16_agpr(acc_dk[nb], a, dsp[t4]);
+                    else mfma_f16_agpr(acc_dv[nb], a, pp[t4]);
+                    if (t4 < 2) {
+#pragma unroll
+                        for (int e = 0; e < EPO_B; ++e) softmax_elem(1, w * EPO_B + e);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
 
@@ -557,6 +610,11 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q16, const uint16_t* __restrict__ K
         __syncthreads();
     }
 
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        agpr_settle(acc_dk[nb]);
+        agpr_settle(acc_dv[nb]);
+    }
     if (kj < N) {
         const float fk = scale / (sQ * sE), fv = 1.f / sDO;
         uint16_t* dkrow = dK + head + (size_t)kj * D;

@@ -41,6 +41,24 @@ __device__ __forceinline__ f32x16_t mfma_32x32x16_f16(const u32x4_t& a, const u3
                                                   __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
 
+// fp16 product accumulated in place into an accumulator held in AGPRs.
+// When one wave owns a SIMD's whole register file the compiler keeps every
+// matrix result in AGPRs and copies operands and results between the two
+// files around each product; written as inline assembly, the accumulator
+// stays in AGPRs and the operands stay in VGPRs. The leading s_nop supplies
+// the two wait states a matrix instruction needs after a VALU write of one
+// of its sources; SrcC is vDst, which dependent products forward in
+// hardware. Read the accumulator only after agpr_settle().
+__device__ __forceinline__ void mfma_f16_agpr(f32x16_t& acc, const u32x4_t& a, const u32x4_t& b) {
+    asm("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// Wait states between the last matrix write of an AGPR accumulator and any
+// other read of it (more than the 8-pass product needs).
+__device__ __forceinline__ void agpr_settle(f32x16_t& acc) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc));
+}
+
 // Two fp32 values -> packed fp16 pair, round to nearest even (v_cvt_pk_f16_f32).
 __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
     f16x2_t p = {(_Float16)lo, (_Float16)hi};
