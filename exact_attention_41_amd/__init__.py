@@ -158,7 +158,8 @@ def _bwd_common(ref, tensors, lse, workspace):
 
 
 def fa_bwd_preprocess(q, k, v, do, workspace):
-    """Phase 1 of fa_bwd: per-head scale factors into ``workspace``."""
+    """Phase 1 of fa_bwd: per-head scale factors and the scaled fp16 transposed
+    copies of q, dO and k into ``workspace``."""
     torch = _torch()
     B, H, N, d, ws = _bwd_common(k, [(q, "q"), (v, "v"), (do, "do")], None, workspace)
     with torch.cuda.device(k.device):
@@ -170,7 +171,7 @@ def fa_bwd_preprocess(q, k, v, do, workspace):
 
 
 def fa_bwd_dq(q, k, v, do, lse, workspace, dq, causal=False, scale=None):
-    """Phase 2 of fa_bwd: dQ (plus D and scaled fp16 q, dO in ``workspace``)."""
+    """Phase 2 of fa_bwd: dQ (plus lse and D per query row in ``workspace``)."""
     torch = _torch()
     B, H, N, d, ws = _bwd_common(k, [(q, "q"), (v, "v"), (do, "do"), (dq, "dq")], lse,
                                  workspace)
@@ -183,12 +184,13 @@ def fa_bwd_dq(q, k, v, do, lse, workspace, dq, causal=False, scale=None):
         raise FAError(st, "fa_bwd_dq")
 
 
-def fa_bwd_dkdv(k, v, lse, workspace, dk, dv, causal=False, scale=None):
-    """Phase 3 of fa_bwd: dK and dV from k, v, lse and the workspace."""
+def fa_bwd_dkdv(q, k, v, do, workspace, dk, dv, causal=False, scale=None):
+    """Phase 3 of fa_bwd: dK and dV from q, k, v, dO and the workspace."""
     torch = _torch()
-    B, H, N, d, ws = _bwd_common(k, [(v, "v"), (dk, "dk"), (dv, "dv")], lse, workspace)
+    B, H, N, d, ws = _bwd_common(k, [(q, "q"), (v, "v"), (do, "do"), (dk, "dk"), (dv, "dv")],
+                                 None, workspace)
     with torch.cuda.device(k.device):
-        st = _lib.load().fa_bwd_dkdv(k.data_ptr(), v.data_ptr(), lse.data_ptr(),
+        st = _lib.load().fa_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(),
                                      workspace.data_ptr(), ws, dk.data_ptr(), dv.data_ptr(),
                                      B, H, N, d, int(bool(causal)), _scale(scale, d),
                                      _stream_ptr(k.device))

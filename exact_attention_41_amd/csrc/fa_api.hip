@@ -143,7 +143,7 @@ fa_status_t fa_bwd_preprocess(const void* q, const void* k, const void* v, const
     if (empty) return FA_OK;
     const fa::BwdArgs a = bwd_args(q, k, v, dout, nullptr, nullptr, nullptr, nullptr, workspace,
                                    B, H, N, d, 0, 1.f, stream);
-    return fa::launch_bwd_scales(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+    return fa::launch_bwd_prepare(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 fa_status_t fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
@@ -158,14 +158,14 @@ fa_status_t fa_bwd_dq(const void* q, const void* k, const void* v, const void* d
     return fa::launch_bwd_dq(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-fa_status_t fa_bwd_dkdv(const void* k, const void* v, const float* lse, const void* workspace,
-                        size_t workspace_bytes, void* dk, void* dv, int B, int H, int N, int d,
-                        int causal, float scale, hipStream_t stream) {
+fa_status_t fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
+                        const void* workspace, size_t workspace_bytes, void* dk, void* dv,
+                        int B, int H, int N, int d, int causal, float scale, hipStream_t stream) {
     bool empty = false;
-    FA_TRY(check_bwd({k, v, dk, dv}, true, lse, workspace, workspace_bytes, B, H, N, d, scale,
-                     &empty));
+    FA_TRY(check_bwd({q, k, v, dout, dk, dv}, false, nullptr, workspace, workspace_bytes, B, H,
+                     N, d, scale, &empty));
     if (empty) return FA_OK;
-    const fa::BwdArgs a = bwd_args(nullptr, k, v, nullptr, lse, nullptr, dk, dv,
+    const fa::BwdArgs a = bwd_args(q, k, v, dout, nullptr, nullptr, dk, dv,
                                    const_cast<void*>(workspace), B, H, N, d, causal, scale,
                                    stream);
     return fa::launch_bwd_dkdv(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
@@ -181,7 +181,7 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o,
     if (empty) return FA_OK;
     const fa::BwdArgs a = bwd_args(q, k, v, dout, lse, dq, dk, dv, workspace, B, H, N, d,
                                    causal, scale, stream);
-    if (fa::launch_bwd_scales(a) != hipSuccess) return FA_ERR_HIP;
+    if (fa::launch_bwd_prepare(a) != hipSuccess) return FA_ERR_HIP;
     if (fa::launch_bwd_dq(a) != hipSuccess) return FA_ERR_HIP;
     if (fa::launch_bwd_dkdv(a) != hipSuccess) return FA_ERR_HIP;
     return FA_OK;

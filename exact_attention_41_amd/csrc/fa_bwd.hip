@@ -12,24 +12,37 @@
 // one workgroup, no floating-point atomics: the "FlashAttention-2" page,
 // systems-analysis.info, section "Performance", calls the method exact and
 // deterministic):
-//   1. scales:  per head, the largest |x| of Q, K, V and dO, turned into
+//   1. prepare: per head, the largest |x| of Q, K, V and dO, turned into
 //      power-of-two factors so that every fp16 operand below is exact (the
-//      bf16 inputs scaled by a power of two) and in range.
+//      bf16 inputs scaled by a power of two) and in range; then, per 64-row
+//      tile, fp16 images of (s_Q Q)^T, (s_dO dO)^T and (s_K K)^T laid out
+//      exactly as the transposed LDS tiles the next phases read.
 //   2. dQ pass: one workgroup per query block, over the key tiles. D_i is not
 //      known before the pass, so it uses
 //          dQ_i = scale * (sum_j P_ij dP_ij K_j - D_i sum_j P_ij K_j)
 //      and accumulates both sums and D_i = sum_j P_ij dP_ij in the same pass;
-//      D is exact (not taken from the rounded O). It also leaves D and scaled
-//      fp16 copies of Q and dO in the workspace for the next pass.
-//   3. dK/dV pass: one workgroup per key block, over the query tiles, all
-//      products on fp16 operands.
-// The probabilities and dS enter the gradient products as fp16 (11-bit
-// significand) rather than bf16 (8-bit): this keeps dQ, dK and dV within
+//      D is exact (not taken from the rounded O). It leaves lse and D per
+//      query tile in the workspace for the next pass.
+//   3. dK/dV pass: one workgroup per key block, over the query tiles.
+// S and dP are products of the bf16 inputs themselves. The probabilities and
+// dS enter the gradient products as fp16 (11-bit significand) rather than
+// bf16 (8-bit), against the fp16 images: this keeps dQ, dK and dV within
 // 1e-2 of the exact gradients where bf16 operands do not.
+//
+// Every tile reaches LDS by direct buffer-to-LDS loads (row-major bf16 tiles
+// from the inputs, with the chunk swizzle applied through the source
+// addresses; transposed tiles as straight copies of their images), issued a
+// tile ahead into the second of two buffers; no tile passes through VGPRs.
 #include "fa_kernels.hpp"
 #include "fa_device.hpp"
 
 namespace fa {
+
+#ifndef FA_BWD_FRAG_AHEAD
+#define FA_BWD_FRAG_AHEAD 4
+#endif
+// LDS fragments are read this many products ahead of their use.
+constexpr int kFragAhead = FA_BWD_FRAG_AHEAD;
 
 // ---------------------------------------------------------------------------
 // Workspace layout (byte offsets; every block 256-byte aligned).
@@ -39,14 +52,16 @@ static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 BwdWorkspace bwd_workspace_layout(long long B, long long H, long long N, long long d) {
     BwdWorkspace w;
     const size_t bh = (size_t)(B * H);
-    const size_t rows = bh * (size_t)N;
     const size_t chunks = (size_t)((N + kScaleRows - 1) / kScaleRows);
-    w.delta = 0;
-    w.scales = w.delta + align256(rows * 4);
+    const size_t tiles = (size_t)((N + 63) / 64);
+    const size_t image = bh * tiles * 64 * (size_t)d * 2;
+    w.scales = 0;
     w.partial = w.scales + align256(bh * 4 * 4);
-    w.q16 = w.partial + align256(bh * chunks * 4 * 4);
-    w.do16 = w.q16 + align256(rows * (size_t)d * 2);
-    w.total = w.do16 + align256(rows * (size_t)d * 2);
+    w.stats = w.partial + align256(bh * chunks * 4 * 4);
+    w.qt = w.stats + align256(bh * tiles * 128 * 4);
+    w.ot = w.qt + align256(image);
+    w.kt = w.ot + align256(image);
+    w.total = w.kt + align256(image);
     return w;
 }
 
@@ -118,12 +133,12 @@ bwd_scale_kernel(const uint32_t* __restrict__ partial, float* __restrict__ scale
 }
 
 // ---------------------------------------------------------------------------
-// Staging of a 64-row, 16-bit tile [64][D] from global memory into LDS as
-// 4-row x 8-column micro-tiles: row-major (swizzled 16-byte chunks) and/or
-// transposed ([D][64], permuted key order and slot swizzle of fa_device.hpp).
-// With CVT the source is bf16 and the transposed copy is fp16 of the value
-// times a power of two. Rows at or past N repeat row N-1 (finite values that
-// the callers' masks multiply by zero).
+// A 64-row, 16-bit tile [64][D] read as 4-row x 8-column micro-tiles and
+// written transposed ([D][64], the permuted row order and slot swizzle of
+// fa_device.hpp), to LDS or to a global image of that layout. With CVT the
+// source is bf16 and the copy is fp16 of the value times a power of two.
+// Rows at or past N repeat row N-1 (finite values that the consumers' masks
+// multiply by zero).
 // ---------------------------------------------------------------------------
 template <int D, int NT>
 struct Tile64 {
@@ -144,19 +159,6 @@ struct Tile64 {
                     const int row = min(row0 + 4 * rg + rr, N - 1);
                     r[it][rr] = *(const u32x4_t*)(src + (size_t)row * D + ch * 8);
                 }
-            }
-        }
-    }
-
-    __device__ __forceinline__ void store_rowmajor(char* dst, int tid) const {
-#pragma unroll
-        for (int it = 0; it < LOADS; ++it) {
-            const int u = tid + it * NT;
-            if (UNITS % NT == 0 || u < UNITS) {
-                const int ch = u % DCH, rg = u / DCH;
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr)
-                    *(u32x4_t*)(dst + row_chunk_offset<D>(4 * rg + rr, ch)) = r[it][rr];
             }
         }
     }
@@ -193,25 +195,36 @@ struct Tile64 {
     }
 };
 
-// Row-major 16-byte fragment of a [64][D] swizzled tile: row `row`, chunk `ch`.
-template <int D>
-__device__ __forceinline__ u32x4_t lds_row_frag(const char* base, int row, int ch) {
-    return *(const u32x4_t*)(base + row_chunk_offset<D>(row, ch));
-}
 
-// Transposed fragment: row n of a [D][64] tile, positions [8q, 8q+8).
-__device__ __forceinline__ u32x4_t lds_tr_frag(const char* base, int n, int q) {
-    return *(const u32x4_t*)(base + tr_slot_offset(n, 2 * q));
+// Phase 1c: fp16 transposed images. One workgroup per (head, 64-row tile,
+// tensor), tensor 0 = Q, 1 = dO, 2 = K.
+template <int D>
+__global__ void __launch_bounds__(256)
+bwd_image_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                 const uint16_t* __restrict__ dO, const float* __restrict__ scales,
+                 char* __restrict__ qt, char* __restrict__ ot, char* __restrict__ kt, int N,
+                 int T) {
+    using TileT = Tile64<D, 256>;
+    const int bid = blockIdx.x;
+    const int which = bid % 3, rest = bid / 3;
+    const int tile = rest % T, bh = rest / T;
+    const uint16_t* src = which == 0 ? Q : (which == 1 ? dO : K);
+    char* dst = which == 0 ? qt : (which == 1 ? ot : kt);
+    const float s = scales[bh * 4 + (which == 0 ? 0 : (which == 1 ? 3 : 1))];
+    TileT tl;
+    tl.load(src + (size_t)bh * N * D, tile * 64, N, threadIdx.x);
+    tl.template store_transposed<true>(dst + ((size_t)bh * T + tile) * TileT::BYTES,
+                                       threadIdx.x, s);
 }
 
 // ---------------------------------------------------------------------------
-// Phase 2: dQ (and D, and the fp16 copies of Q and dO).
+// Phase 2: dQ (and the per-tile lse and D for phase 3).
 // One workgroup per block of NW*32 queries; each wave owns 32 query rows,
 // one per lane pair. Products (lane = query column i, registers = key rows j):
-//   S^T  = K Q^T               A = K tile (LDS, bf16)     B = Q^T (VGPRs)
-//   dP~^T = V (sE dO)^T        A = V tile (LDS, bf16)     B = sE dO^T (VGPRs)
-//   A~^T += K~^T (P*dP~)^T     A = sK K^T (LDS, fp16)     B = P*dP~ (fp16)
-//   B~^T += K~^T P^T           A = sK K^T (LDS, fp16)     B = P (fp16)
+//   S^T  = K Q^T               A = K tile (LDS, bf16)      B = Q^T (VGPRs)
+//   dP~^T = V (sE dO)^T        A = V tile (LDS, bf16)      B = sE dO^T (VGPRs)
+//   A~^T += K~^T (P*dP~)^T     A = (sK K)^T (LDS, fp16)    B = P*dP~ (fp16)
+//   B~^T += K~^T P^T           A = (sK K)^T (LDS, fp16)    B = P (fp16)
 // with sE = s_dO * s_V; finally dQ = scale/(sK sE) (A~ - D~ B~), D~ = sE D.
 // ---------------------------------------------------------------------------
 template <int D, int NW, bool CAUSAL>
@@ -219,16 +232,15 @@ __global__ void __launch_bounds__(NW * 64, 1)
 bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
               const float* __restrict__ LSE, const float* __restrict__ scales,
-              float* __restrict__ delta, uint16_t* __restrict__ q16, uint16_t* __restrict__ do16,
-              uint16_t* __restrict__ dQ, int BH, int N, float c, float scale, int nqb) {
+              const char* __restrict__ kt_img, float* __restrict__ stats,
+              uint16_t* __restrict__ dQ, int BH, int N, int T, float c, float scale, int nqb) {
     constexpr int BC = 64;
-    constexpr int NT = NW * 64;
     constexpr int BQ = NW * 32;
     constexpr int KS = D / 16;
     constexpr int NB = D / 32;
-    using TileT = Tile64<D, NT>;
-    constexpr int TB = TileT::BYTES;
-    constexpr int OFF_K = 0, OFF_KT = TB, OFF_V = 2 * TB;
+    constexpr int TB = 64 * D * 2;         // bytes of one 64-row tile
+    constexpr int BLK = TB / 1024;         // its 1 KB staging blocks
+    constexpr int OFF_K = 0, OFF_V = TB, OFF_KT = 2 * TB;
     constexpr int BUF = 3 * TB;
     __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
 
@@ -241,11 +253,12 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const size_t head = (size_t)bh * (size_t)N * D;
     const uint16_t* Kh = K + head;
     const uint16_t* Vh = V + head;
+    const char* kt_h = kt_img + (size_t)bh * T * TB;
     const int q0 = qb * BQ;
     const int wq0 = q0 + wave * 32;
     const int qi = wq0 + l32;             // this lane's query row
 
-    const float sQ = scales[bh * 4 + 0], sK = scales[bh * 4 + 1];
+    const float sK = scales[bh * 4 + 1];
     const float sV = scales[bh * 4 + 2], sDO = scales[bh * 4 + 3];
     const float sE = sDO * sV;
 
@@ -256,19 +269,14 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             const size_t off = head + (size_t)qi * D + 16 * s + 8 * g;
             const u32x4_t qv = *(const u32x4_t*)(Q + off);
             const u32x4_t ov = *(const u32x4_t*)(dO + off);
-            u32x4_t qh, oh;
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                qh[w] = bf16x2_to_f16x2(qv[w], sQ);
-                oh[w] = bf16x2_to_f16x2(ov[w], sDO);
-                of[s][w] = bf16x2_scale(ov[w], sE);
-            }
+            for (int w = 0; w < 4; ++w) of[s][w] = bf16x2_scale(ov[w], sE);
             qf[s] = qv;
-            *(u32x4_t*)(q16 + off) = qh;
-            *(u32x4_t*)(do16 + off) = oh;
         } else {
             qf[s] = of[s] = u32x4_t{0u, 0u, 0u, 0u};
         }
+        park_in_agprs(qf[s]);
+        park_in_agprs(of[s]);
     }
     const float lse2 = (qi < N) ? LSE[(size_t)bh * N + qi] * kLog2e : __builtin_huge_valf();
 
@@ -283,61 +291,81 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const int q_last = min(q0 + BQ, N) - 1;
     const int n_tiles = CAUSAL ? min(n_all, q_last / BC + 1) : n_all;
 
-    TileT kt, vt;
-    auto load = [&](int j0) {
-        kt.load(Kh, j0, N, tid);
-        vt.load(Vh, j0, N, tid);
-    };
-    auto store = [&](int buf) {
-        char* b = smem + buf * BUF;
-        kt.store_rowmajor(b + OFF_K, tid);
-        kt.template store_transposed<true>(b + OFF_KT, tid, sK);
-        vt.store_rowmajor(b + OFF_V, tid);
+    // Key tile t into buffer buf: K and V rows (bf16, swizzled) and the
+    // (sK K)^T image, BLK 1 KB blocks each, spread over the NW waves; part k
+    // of NPART is one block of this wave. Past the last tile nothing is read
+    // (the idle buffer is zero-filled).
+    constexpr int PPT = BLK / NW;            // blocks per wave and tensor
+    constexpr int NPART = 3 * PPT;
+    auto stage_part = [&](int t, int buf, int k) {
+        lds_char* base = (lds_char*)(smem + buf * BUF);
+        const int tensor = k / PPT, b = wave + NW * (k % PPT);
+        const bool live = t < n_tiles;
+        if (tensor < 2)
+            stage_tile_block<D>(tensor == 0 ? Kh : Vh, base + (tensor == 0 ? OFF_K : OFF_V),
+                                t * BC, live ? min(BC, N - t * BC) : 0, b, lane);
+        else
+            stage_image_block(kt_h + (size_t)t * TB, live ? TB : 0, base + OFF_KT, b, lane);
     };
 
-    load(0);
-    store(0);
+    // Lane-dependent LDS bases of buffer 0: pb[k], k < 8, for the row-major
+    // S/dP fragments (chunk step s; for d = 64 also the key half) and
+    // pb[8 + 2 t4 + (nb & 1)] for the transposed dQ fragments; the rest of
+    // each fragment address is an immediate offset.
+    lds_char* const s0 = (lds_char*)smem;
+    lds_char* pb[16];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int jb = (D == 64) ? k / KS : 0, st = (D == 64) ? k % KS : k;
+        pb[k] = s0 + row_chunk_offset<D>(32 * jb + l32, 2 * st + g);
+        pb[8 + k] = s0 + tr_slot_offset(32 * (k & 1) + l32, 2 * (2 * (k >> 1) + g));
+    }
+
+#pragma unroll
+    for (int k = 0; k < NPART; ++k) stage_part(0, 0, k);
     __syncthreads();
 
-    for (int t = 0; t < n_tiles; ++t) {
+    // One key tile: stage the next one, run the pipeline, move the bases.
+    auto iteration = [&](int t, auto mask_tag) {
         const int j0 = t * BC;
-        if (t + 1 < n_tiles) load(j0 + BC);
-        const char* b = smem + (t & 1) * BUF;
 
-        {   // waves whose rows all precede the tile compute it fully masked
-            const bool need_mask = (j0 + BC > N) || (CAUSAL && j0 + BC - 1 > wq0);
-            // One software pipeline per key tile: S, dP of key half 0, then of
-            // half 1 (while half 0 is exponentiated), then the two dQ sums
-            // over four 16-key steps (the first two while half 1 is
-            // exponentiated); a dQ step's K~^T fragment feeds both sums.
-            // Fragments are read LA steps ahead; sched_barrier keeps that order.
+        // One software pipeline per key tile: S, dP of key half 0, then of
+        // half 1 (while half 0 is exponentiated), then the two dQ sums over
+        // four 16-key steps (the first two while half 1 is exponentiated);
+        // a dQ step's K~^T fragment feeds both sums. Fragments are read LA
+        // steps ahead; sched_barrier keeps that order. Only tiles that cross
+        // N or reach past a wave's first row take the mask.
+        auto tile_body = [&](auto mask_tag) {
+            constexpr bool MASK = decltype(mask_tag)::value;
             constexpr int NSD = 2 * KS;
             constexpr int NOPS = 2 * NSD + 4 * NB;
-            constexpr int LA = 4;
+            constexpr int LA = kFragAhead;
             constexpr int EPO_A = 16 / NSD;
             constexpr int EPO_B = 16 / (2 * NB);
-            auto frag_ptr = [&](int o) -> const char* {
+            lds_char* const* bb = pb;
+            auto frag = [&](int o) -> u32x4_t {
                 if (o < 2 * NSD) {
-                    const int jb = o / NSD, w = o % NSD;
-                    return b + ((w & 1) ? OFF_V : OFF_K) +
-                           row_chunk_offset<D>(32 * jb + l32, 2 * (w >> 1) + g);
+                    const int jb = o / NSD, w = o % NSD, st = w >> 1;
+                    const int k = (D == 64) ? jb * KS + st : st;
+                    const int off = ((w & 1) ? OFF_V : OFF_K) + ((D == 64) ? 0 : jb * 32 * D * 2);
+                    return *(const lds_u32x4_t*)(bb[k] + off);
                 }
                 const int w = o - 2 * NSD, t4 = w / NB, nb = w % NB;
-                return b + OFF_KT + tr_slot_offset(32 * nb + l32, 2 * (2 * t4 + g));
+                const int off = OFF_KT + (nb - (nb & 1)) * 32 * 128;
+                return *(const lds_u32x4_t*)(bb[8 + 2 * t4 + (nb & 1)] + off);
             };
 
             u32x4_t fr[LA + 1];
 #pragma unroll
-            for (int o = 0; o < LA; ++o) fr[o] = *(const u32x4_t*)frag_ptr(o);
+            for (int o = 0; o < LA; ++o) fr[o] = frag(o);
 
-            const f32x16_t zero16 = {};
             f32x16_t sa[2], da[2];
             float pv[16], ev[16];
             u32x4_t pf[4], ef[4];
             auto softmax_elem = [&](int jb, int r) {
                 const int j = j0 + 32 * jb + 8 * (r >> 2) + 4 * g + (r & 3);
                 float p = fast_exp2(__builtin_fmaf(sa[jb][r], c, -lse2));
-                if (need_mask && (j >= N || (CAUSAL && j > qi))) p = 0.f;
+                if (MASK && (j >= N || (CAUSAL && j > qi))) p = 0.f;
                 const float e = p * da[jb][r];
                 dsum += e;
                 pv[r] = p;
@@ -353,12 +381,15 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
 #pragma unroll
             for (int o = 0; o < NOPS; ++o) {
-                if (o + LA < NOPS) fr[(o + LA) % (LA + 1)] = *(const u32x4_t*)frag_ptr(o + LA);
+                if (o + LA < NOPS) fr[(o + LA) % (LA + 1)] = frag(o + LA);
                 const u32x4_t a = fr[o % (LA + 1)];
                 if (o < 2 * NSD) {
                     const int jb = o / NSD, w = o % NSD, st = w >> 1;
-                    if (w & 1) da[jb] = mfma_32x32x16(a, of[st], st == 0 ? zero16 : da[jb]);
-                    else sa[jb] = mfma_32x32x16(a, qf[st], st == 0 ? zero16 : sa[jb]);
+                    f32x16_t& acc = (w & 1) ? da[jb] : sa[jb];
+                    const u32x4_t& bop = (w & 1) ? of[st] : qf[st];
+                    if (st == 0) mfma_bf16_first(acc, a, bop);
+                    else if (st == KS - 1) mfma_bf16_last(acc, a, bop);
+                    else mfma_bf16_next(acc, a, bop);
                     if (jb == 1) {
 #pragma unroll
                         for (int e = 0; e < EPO_A; ++e) softmax_elem(0, w * EPO_A + e);
@@ -372,13 +403,27 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                         for (int e = 0; e < EPO_B; ++e) softmax_elem(1, w * EPO_B + e);
                     }
                 }
+                // The next tile's loads, in the VALU-free dQ steps.
+                constexpr int O0 = 2 * NSD + 2 * NB;
+#pragma unroll
+                for (int k = 0; k < NPART; ++k)
+                    if (o == O0 + k * (NOPS - O0) / NPART) stage_part(t + 1, (t + 1) & 1, k);
                 __builtin_amdgcn_sched_barrier(0);
             }
-        }
+        };
+        tile_body(mask_tag);
+        // the bases move to the other buffer
+        const int step = (t & 1) ? -BUF : BUF;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) pb[k] += step;
 
-        if (t + 1 < n_tiles) store((t + 1) & 1);
-        __syncthreads();
-    }
+        __syncthreads();   // tile t+1 has landed; every wave is done with tile t
+    };
+    // Tiles from t_mask on cross N or reach past the block's first row (a
+    // wave whose rows all precede such a tile computes it fully masked).
+    const int t_mask = min(CAUSAL ? (q0 + 1) / BC : n_tiles, N / BC);
+    for (int t = 0; t < min(t_mask, n_tiles); ++t) iteration(t, BoolTag<false>{});
+    for (int t = max(t_mask, 0); t < n_tiles; ++t) iteration(t, BoolTag<true>{});
 
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -386,8 +431,12 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         agpr_settle(acc_b[nb]);
     }
     const float dt = sum_with_partner32(dsum);    // D~ = sE * D
+    if (g == 0 && qi < T * 64) {
+        float* st = stats + ((size_t)bh * T + (qi >> 6)) * 128;
+        st[qi & 63] = lse2;
+        st[64 + (qi & 63)] = (qi < N) ? dt : 0.f;
+    }
     if (qi < N) {
-        if (g == 0) delta[(size_t)bh * N + qi] = dt / sE;
         const float f = scale / (sK * sE);
         uint16_t* row = dQ + head + (size_t)qi * D;
 #pragma unroll
@@ -411,30 +460,28 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 // ---------------------------------------------------------------------------
 // Phase 3: dK, dV. One workgroup per block of NW*32 keys; each wave owns 32
 // keys (one per lane pair) and walks the query tiles (64 rows) that see them.
-// All operands fp16: Q~ = sQ Q, dO~ = sDO dO (from the workspace), K~ = sK K,
-// V~ = sV V (resident). Products (lane = key column j, registers = rows i):
-//   S~  = Q~ K~^T        A = Q~ tile (LDS)            B = K~^T (VGPRs)
-//   dP~ = dO~ V~^T       A = dO~ tile (LDS)           B = V~^T (VGPRs)
-//   dV^T += dO~^T P      A = dO~^T (LDS, transposed)  B = P (fp16)
-//   dK^T += Q~^T dS~     A = Q~^T (LDS, transposed)   B = dS~ = P (dP~ - sE D)
+// Products (lane = key column j, registers = query rows i):
+//   S   = Q K^T              A = Q tile (LDS, bf16)         B = K^T (VGPRs)
+//   dP  = dO V^T             A = dO tile (LDS, bf16)        B = V^T (VGPRs)
+//   dV^T += dO~^T P          A = (s_dO dO)^T (LDS, fp16)    B = P (fp16)
+//   dK^T += Q~^T dS~         A = (s_Q Q)^T (LDS, fp16)      B = dS~ = P (sE dP - sE D)
 // ---------------------------------------------------------------------------
 template <int D, int NW, bool CAUSAL>
 __global__ void __launch_bounds__(NW * 64, 1)
-bwd_dkdv_kernel(const uint16_t* __restrict__ q16, const uint16_t* __restrict__ K,
-                const uint16_t* __restrict__ V, const uint16_t* __restrict__ do16,
-                const float* __restrict__ LSE, const float* __restrict__ delta,
-                const float* __restrict__ scales, uint16_t* __restrict__ dK,
-                uint16_t* __restrict__ dV, int BH, int N, float c, float scale) {
+bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+                const float* __restrict__ scales, const float* __restrict__ stats,
+                const char* __restrict__ qt_img, const char* __restrict__ ot_img,
+                uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int BH, int N, int T,
+                float c, float scale) {
     constexpr int BQ = 64;
-    constexpr int NT = NW * 64;
     constexpr int BKV = NW * 32;
     constexpr int KS = D / 16;
     constexpr int NB = D / 32;
-    using TileT = Tile64<D, NT>;
-    constexpr int TB = TileT::BYTES;
-    constexpr int OFF_Q = 0, OFF_QT = TB, OFF_DO = 2 * TB, OFF_DOT = 3 * TB;
-    constexpr int OFF_LSE = 4 * TB, OFF_DEL = 4 * TB + BQ * 4;
-    constexpr int BUF = 4 * TB + 2 * BQ * 4;
+    constexpr int TB = 64 * D * 2;
+    constexpr int BLK = TB / 1024;
+    constexpr int OFF_Q = 0, OFF_DO = TB, OFF_QT = 2 * TB, OFF_DOT = 3 * TB, OFF_ST = 4 * TB;
+    constexpr int BUF = 4 * TB + 1024;
     __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
 
     const int tid = threadIdx.x;
@@ -444,15 +491,15 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q16, const uint16_t* __restrict__ K
     const int bh = bid % BH;
     const int kb = bid / BH;              // low key blocks see the most queries: first
     const size_t head = (size_t)bh * (size_t)N * D;
-    const uint16_t* Qh = q16 + head;
-    const uint16_t* dOh = do16 + head;
-    const float* lse_h = LSE + (size_t)bh * N;
-    const float* del_h = delta + (size_t)bh * N;
+    const uint16_t* Qh = Q + head;
+    const uint16_t* dOh = dO + head;
+    const char* qt_h = qt_img + (size_t)bh * T * TB;
+    const char* ot_h = ot_img + (size_t)bh * T * TB;
+    const float* st_h = stats + (size_t)bh * T * 128;
 
-    const float sQ = scales[bh * 4 + 0], sK = scales[bh * 4 + 1];
+    const float sQ = scales[bh * 4 + 0];
     const float sV = scales[bh * 4 + 2], sDO = scales[bh * 4 + 3];
     const float sE = sDO * sV;
-    const float cs = c / (sQ * sK);       // S = S~ / (sQ sK), exactly
 
     const int k0 = kb * BKV;
     const int kw0 = k0 + wave * 32;
@@ -462,16 +509,13 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q16, const uint16_t* __restrict__ K
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
         if (kj < N) {
-            const u32x4_t kv = *(const u32x4_t*)(K + head + (size_t)kj * D + 16 * s + 8 * g);
-            const u32x4_t vv = *(const u32x4_t*)(V + head + (size_t)kj * D + 16 * s + 8 * g);
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                kf[s][w] = bf16x2_to_f16x2(kv[w], sK);
-                vf[s][w] = bf16x2_to_f16x2(vv[w], sV);
-            }
+            kf[s] = *(const u32x4_t*)(K + head + (size_t)kj * D + 16 * s + 8 * g);
+            vf[s] = *(const u32x4_t*)(V + head + (size_t)kj * D + 16 * s + 8 * g);
         } else {
             kf[s] = vf[s] = u32x4_t{0u, 0u, 0u, 0u};
         }
+        park_in_agprs(kf[s]);
+        park_in_agprs(vf[s]);
     }
 
     f32x16_t acc_dk[NB], acc_dv[NB];
@@ -483,90 +527,100 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q16, const uint16_t* __restrict__ K
     const int n_tiles = (N + BQ - 1) / BQ;
     const int t0 = CAUSAL ? (k0 / BQ) : 0;
 
-    TileT qt, dot;
-    // Threads 0..63 carry the next tile's lse, 64..127 its D (the others load
-    // a harmless copy); the value is scaled only when stored, so that the
-    // load is waited for at the end of the tile, not at its start.
-    float stat = 0.f;
-    int stat_row = 0;
-    const float* stat_src = (tid < BQ) ? lse_h : del_h;
-
-    auto load = [&](int i0) {
-        qt.load(Qh, i0, N, tid);
-        dot.load(dOh, i0, N, tid);
-        stat_row = i0 + (tid & (BQ - 1));
-        stat = stat_src[min(stat_row, N - 1)];
+    // Query tile t into buffer buf: Q and dO rows (bf16, swizzled) and the
+    // two transposed fp16 images, BLK 1 KB blocks each spread over the NW
+    // waves (part k of NPART is one block of this wave), and the tile's 128
+    // statistics (wave 0). Past the last tile nothing is read.
+    constexpr int PPT = BLK / NW;
+    constexpr int NPART = 4 * PPT;
+    auto stage_part = [&](int t, int buf, int k) {
+        lds_char* base = (lds_char*)(smem + buf * BUF);
+        const int tensor = k / PPT, b = wave + NW * (k % PPT);
+        const bool live = t < n_tiles;
+        if (tensor < 2)
+            stage_tile_block<D>(tensor == 0 ? Qh : dOh, base + (tensor == 0 ? OFF_Q : OFF_DO),
+                                t * BQ, live ? min(BQ, N - t * BQ) : 0, b, lane);
+        else
+            stage_image_block((tensor == 2 ? qt_h : ot_h) + (size_t)t * TB, live ? TB : 0,
+                              base + (tensor == 2 ? OFF_QT : OFF_DOT), b, lane);
     };
-    auto store = [&](int buf) {
-        char* b = smem + buf * BUF;
-        qt.store_rowmajor(b + OFF_Q, tid);
-        qt.template store_transposed<false>(b + OFF_QT, tid);
-        dot.store_rowmajor(b + OFF_DO, tid);
-        dot.template store_transposed<false>(b + OFF_DOT, tid);
-        if (tid < 2 * BQ) {
-            const bool in = stat_row < N;
-            const float v = (tid < BQ) ? (in ? stat * kLog2e : __builtin_huge_valf())
-                                       : (in ? stat * sE : 0.f);
-            ((float*)(b + OFF_LSE))[tid] = v;
-        }
+    auto stage_stats = [&](int t, int buf) {
+        lds_char* base = (lds_char*)(smem + buf * BUF);
+        if (wave == 0) stage_image_block(st_h + (size_t)t * 128, t < n_tiles ? 512 : 0,
+                                         base + OFF_ST, 0, lane);
     };
 
-    if (t0 < n_tiles) {
-        load(t0 * BQ);
-        store(0);
+    // Lane-dependent LDS bases of buffer 0: pb[k], k < 8, for the row-major
+    // S/dP fragments (chunk step s; for d = 64 also the query half) and
+    // pb[8 + 2 t4 + (nb & 1)] for the transposed dV/dK fragments; everything
+    // else in a fragment address is a compile-time offset, so each read is
+    // one ds_read with an immediate offset from a base moved once per tile.
+    lds_char* const s0 = (lds_char*)smem;
+    lds_char* pb[16];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int ib = (D == 64) ? k / KS : 0, st = (D == 64) ? k % KS : k;
+        pb[k] = s0 + row_chunk_offset<D>(32 * ib + l32, 2 * st + g);
+        pb[8 + k] = s0 + tr_slot_offset(32 * (k & 1) + l32, 2 * (2 * (k >> 1) + g));
     }
+    lds_char* pst = s0 + OFF_ST + 16 * g;
+
+#pragma unroll
+    for (int k = 0; k < NPART; ++k) stage_part(t0, 0, k);
+    stage_stats(t0, 0);
     __syncthreads();
 
-    for (int t = t0; t < n_tiles; ++t) {
+    // One query tile: stage the next one, run the pipeline, move the bases.
+    auto iteration = [&](int t, auto mask_tag) {
         const int i0 = t * BQ;
         const int buf = (t - t0) & 1;
-        if (t + 1 < n_tiles) load(i0 + BQ);
-        const char* b = smem + buf * BUF;
 
-        {   // waves whose keys all follow the tile compute it fully masked
-            const bool need_mask = CAUSAL && (i0 < kw0 + 31);
-            const float* lse_t = (const float*)(b + OFF_LSE);
-            const float* del_t = (const float*)(b + OFF_DEL);
-            // The tile's 2*NSD + 4*NG products run as one software pipeline:
-            // S, dP of query half 0, then of half 1 (while half 0 is
-            // exponentiated), then dV, dK over four 16-query steps (the first
-            // two while half 1 is exponentiated). Each product's LDS fragment
-            // is read LA products ahead; sched_barrier keeps that order.
+        // The tile's 2*NSD + 4*NG products run as one software pipeline:
+        // S, dP of query half 0, then of half 1 (while half 0 is
+        // exponentiated), then dV, dK over four 16-query steps (the first
+        // two while half 1 is exponentiated). Each product's LDS fragment
+        // is read LA products ahead; sched_barrier keeps that order. Only
+        // tiles that reach above a wave's first key take the causal mask.
+        auto tile_body = [&](auto mask_tag) {
+            constexpr bool MASK = decltype(mask_tag)::value;
             constexpr int NSD = 2 * KS;
             constexpr int NG = 2 * NB;
             constexpr int NOPS = 2 * NSD + 4 * NG;
-            constexpr int LA = 4;
+            constexpr int LA = kFragAhead;
             constexpr int EPO_A = 16 / NSD;
             constexpr int EPO_B = 16 / (2 * NG);
-            auto frag_ptr = [&](int o) -> const char* {
+            lds_char* const* bb = pb;
+            lds_char* const bst = pst;
+            auto frag = [&](int o) -> u32x4_t {
                 if (o < 2 * NSD) {
-                    const int ib = o / NSD, w = o % NSD;
-                    return b + ((w & 1) ? OFF_DO : OFF_Q) +
-                           row_chunk_offset<D>(32 * ib + l32, 2 * (w >> 1) + g);
+                    const int ib = o / NSD, w = o % NSD, st = w >> 1;
+                    const int k = (D == 64) ? ib * KS + st : st;
+                    const int off = ((w & 1) ? OFF_DO : OFF_Q) + ((D == 64) ? 0 : ib * 32 * D * 2);
+                    return *(const lds_u32x4_t*)(bb[k] + off);
                 }
                 const int w = o - 2 * NSD, t4 = w / NG, nb = (w % NG) >> 1;
-                return b + ((w & 1) ? OFF_QT : OFF_DOT) + tr_slot_offset(32 * nb + l32, 2 * (2 * t4 + g));
+                const int off = ((w & 1) ? OFF_QT : OFF_DOT) + (nb - (nb & 1)) * 32 * 128;
+                return *(const lds_u32x4_t*)(bb[8 + 2 * t4 + (nb & 1)] + off);
             };
 
             u32x4_t fr[LA + 1];
 #pragma unroll
-            for (int o = 0; o < LA; ++o) fr[o] = *(const u32x4_t*)frag_ptr(o);
+            for (int o = 0; o < LA; ++o) fr[o] = frag(o);
 
-            const f32x16_t zero16 = {};
             f32x16_t sa[2], da[2];
             f32x4_t l4[4], d4[4];     // lse*log2e and sE*D of the half being exponentiated
             float pv[16], dsv[16];
             u32x4_t pp[4], dsp[4];
             auto read_stats = [&](int ib, int q4) {
-                l4[q4] = *(const f32x4_t*)(lse_t + 32 * ib + 8 * q4 + 4 * g);
-                d4[q4] = *(const f32x4_t*)(del_t + 32 * ib + 8 * q4 + 4 * g);
+                l4[q4] = *(const lds_f32x4_t*)(bst + (32 * ib + 8 * q4) * 4);
+                d4[q4] = *(const lds_f32x4_t*)(bst + 256 + (32 * ib + 8 * q4) * 4);
             };
             auto softmax_elem = [&](int ib, int r) {
                 const int q4 = r >> 2, r4 = r & 3;
-                float p = fast_exp2(__builtin_fmaf(sa[ib][r], cs, -l4[q4][r4]));
-                if (need_mask && kj > i0 + 32 * ib + 8 * q4 + 4 * g + r4) p = 0.f;
+                float p = fast_exp2(__builtin_fmaf(sa[ib][r], c, -l4[q4][r4]));
+                if (MASK && kj > i0 + 32 * ib + 8 * q4 + 4 * g + r4) p = 0.f;
                 pv[r] = p;
-                dsv[r] = p * (da[ib][r] - d4[q4][r4]);
+                dsv[r] = p * __builtin_fmaf(da[ib][r], sE, -d4[q4][r4]);
                 if (ib == 0 && r4 == 3) read_stats(1, q4);
                 if ((r & 7) == 7) {
                     const int h = r >> 3, rb = 8 * h;
@@ -579,7 +633,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q16, const uint16_t* __restrict__ K
 
 #pragma unroll
             for (int o = 0; o < NOPS; ++o) {
-                if (o + LA < NOPS) fr[(o + LA) % (LA + 1)] = *(const u32x4_t*)frag_ptr(o + LA);
+                if (o + LA < NOPS) fr[(o + LA) % (LA + 1)] = frag(o + LA);
                 const u32x4_t a = fr[o % (LA + 1)];
                 if (o == 0) {
 #pragma unroll
@@ -587,8 +641,11 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q16, const uint16_t* __restrict__ K
                 }
                 if (o < 2 * NSD) {
                     const int ib = o / NSD, w = o % NSD, st = w >> 1;
-                    if (w & 1) da[ib] = mfma_32x32x16_f16(a, vf[st], st == 0 ? zero16 : da[ib]);
-                    else sa[ib] = mfma_32x32x16_f16(a, kf[st], st == 0 ? zero16 : sa[ib]);
+                    f32x16_t& acc = (w & 1) ? da[ib] : sa[ib];
+                    const u32x4_t& bop = (w & 1) ? vf[st] : kf[st];
+                    if (st == 0) mfma_bf16_first(acc, a, bop);
+                    else if (st == KS - 1) mfma_bf16_last(acc, a, bop);
+                    else mfma_bf16_next(acc, a, bop);
                     if (ib == 1) {
 #pragma unroll
                         for (int e = 0; e < EPO_A; ++e) softmax_elem(0, w * EPO_A + e);
@@ -602,13 +659,29 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q16, const uint16_t* __restrict__ K
                         for (int e = 0; e < EPO_B; ++e) softmax_elem(1, w * EPO_B + e);
                     }
                 }
+                // The next tile's loads, in the VALU-free dV/dK steps.
+                constexpr int O0 = 2 * NSD + 2 * NG;
+#pragma unroll
+                for (int k = 0; k < NPART; ++k)
+                    if (o == O0 + k * (NOPS - O0) / NPART) stage_part(t + 1, buf ^ 1, k);
+                if (o == O0 + 1) stage_stats(t + 1, buf ^ 1);
                 __builtin_amdgcn_sched_barrier(0);
             }
-        }
+        };
+        tile_body(mask_tag);
+        // the bases move to the other buffer
+        const int step = buf ? -BUF : BUF;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) pb[k] += step;
+        pst += step;
 
-        if (t + 1 < n_tiles) store(buf ^ 1);
-        __syncthreads();
-    }
+        __syncthreads();   // tile t+1 has landed; every wave is done with tile t
+    };
+    // Causal: only the first two query tiles reach above some wave's keys
+    // (a wave whose keys all follow such a tile computes it fully masked).
+    const int t_free = CAUSAL ? min(t0 + 2, n_tiles) : t0;
+    for (int t = t0; t < t_free; ++t) iteration(t, BoolTag<true>{});
+    for (int t = t_free; t < n_tiles; ++t) iteration(t, BoolTag<false>{});
 
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -644,23 +717,28 @@ static BwdWorkspace ws_of(const BwdArgs& a) { return bwd_workspace_layout(a.B, a
 template <typename T>
 static T* ws_ptr(const BwdArgs& a, size_t off) { return (T*)((char*)a.workspace + off); }
 
-hipError_t launch_bwd_scales(const BwdArgs& a) {
+static int n_tiles64(const BwdArgs& a) { return (a.N + 63) / 64; }
+
+template <int D>
+static hipError_t launch_prepare_t(const BwdArgs& a) {
     const BwdWorkspace w = ws_of(a);
     const int BH = a.B * a.H;
     const int chunks = (a.N + kScaleRows - 1) / kScaleRows;
+    const int T = n_tiles64(a);
     uint32_t* partial = ws_ptr<uint32_t>(a, w.partial);
-    if (a.d == 128)
-        hipLaunchKernelGGL((bwd_absmax_kernel<128>), dim3(BH * chunks), dim3(256), 0, a.stream,
-                           (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                           (const uint16_t*)a.dout, partial, a.N, chunks);
-    else
-        hipLaunchKernelGGL((bwd_absmax_kernel<64>), dim3(BH * chunks), dim3(256), 0, a.stream,
-                           (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                           (const uint16_t*)a.dout, partial, a.N, chunks);
+    hipLaunchKernelGGL((bwd_absmax_kernel<D>), dim3(BH * chunks), dim3(256), 0, a.stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                       (const uint16_t*)a.dout, partial, a.N, chunks);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_scale_kernel, dim3((BH + 63) / 64), dim3(64), 0, a.stream,
                        (const uint32_t*)partial, ws_ptr<float>(a, w.scales), BH, chunks);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_image_kernel<D>), dim3(BH * T * 3), dim3(256), 0, a.stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.dout,
+                       ws_ptr<const float>(a, w.scales), ws_ptr<char>(a, w.qt),
+                       ws_ptr<char>(a, w.ot), ws_ptr<char>(a, w.kt), a.N, T);
     return hipGetLastError();
 }
 
@@ -673,9 +751,9 @@ static hipError_t launch_dq_t(const BwdArgs& a) {
     hipLaunchKernelGGL((bwd_dq_kernel<D, NW, CAUSAL>), dim3(nqb * BH), dim3(NW * 64), 0,
                        a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                        (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse,
-                       ws_ptr<const float>(a, w.scales), ws_ptr<float>(a, w.delta),
-                       ws_ptr<uint16_t>(a, w.q16), ws_ptr<uint16_t>(a, w.do16),
-                       (uint16_t*)a.dq, BH, a.N, a.scale * kLog2e, a.scale, nqb);
+                       ws_ptr<const float>(a, w.scales), ws_ptr<const char>(a, w.kt),
+                       ws_ptr<float>(a, w.stats), (uint16_t*)a.dq, BH, a.N, n_tiles64(a),
+                       a.scale * kLog2e, a.scale, nqb);
     return hipGetLastError();
 }
 
@@ -686,11 +764,17 @@ static hipError_t launch_dkdv_t(const BwdArgs& a) {
     const int BH = a.B * a.H;
     const int nkb = (a.N + NW * 32 - 1) / (NW * 32);
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, CAUSAL>), dim3(nkb * BH), dim3(NW * 64), 0,
-                       a.stream, ws_ptr<const uint16_t>(a, w.q16), (const uint16_t*)a.k,
-                       (const uint16_t*)a.v, ws_ptr<const uint16_t>(a, w.do16), a.lse,
-                       ws_ptr<const float>(a, w.delta), ws_ptr<const float>(a, w.scales),
-                       (uint16_t*)a.dk, (uint16_t*)a.dv, BH, a.N, a.scale * kLog2e, a.scale);
+                       a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                       (const uint16_t*)a.v, (const uint16_t*)a.dout,
+                       ws_ptr<const float>(a, w.scales), ws_ptr<const float>(a, w.stats),
+                       ws_ptr<const char>(a, w.qt), ws_ptr<const char>(a, w.ot),
+                       (uint16_t*)a.dk, (uint16_t*)a.dv, BH, a.N, n_tiles64(a),
+                       a.scale * kLog2e, a.scale);
     return hipGetLastError();
+}
+
+hipError_t launch_bwd_prepare(const BwdArgs& a) {
+    return a.d == 128 ? launch_prepare_t<128>(a) : launch_prepare_t<64>(a);
 }
 
 hipError_t launch_bwd_dq(const BwdArgs& a) {

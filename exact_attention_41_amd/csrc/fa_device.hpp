@@ -41,6 +41,15 @@ __device__ __forceinline__ f32x16_t mfma_32x32x16_f16(const u32x4_t& a, const u3
                                                   __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
 
+// Compile-time flag carried into a generic lambda.
+template <bool B>
+struct BoolTag {
+    static constexpr bool value = B;
+};
+
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
+typedef __attribute__((address_space(3))) f32x4_t lds_f32x4_t;
+
 // fp16 product accumulated in place into an accumulator held in AGPRs.
 // When one wave owns a SIMD's whole register file the compiler keeps every
 // matrix result in AGPRs and copies operands and results between the two
@@ -52,6 +61,29 @@ __device__ __forceinline__ f32x16_t mfma_32x32x16_f16(const u32x4_t& a, const u3
 __device__ __forceinline__ void mfma_f16_agpr(f32x16_t& acc, const u32x4_t& a, const u32x4_t& b) {
     asm("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
+
+// bf16 product into a VGPR accumulator with the B operand held in AGPRs (a
+// loop-invariant operand parked outside the VGPR file). A chain of products
+// into one accumulator is mfma_bf16_first (SrcC = 0), mfma_bf16_next and
+// mfma_bf16_last; SrcC = vDst within the chain, which dependent products
+// forward in hardware, and the last one is followed by the wait states the
+// VALU needs before it may read a matrix result (more than an 8-pass
+// product requires).
+__device__ __forceinline__ void mfma_bf16_first(f32x16_t& acc, const u32x4_t& a, const u32x4_t& b) {
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_bf16_next(f32x16_t& acc, const u32x4_t& a, const u32x4_t& b) {
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_bf16_last(f32x16_t& acc, const u32x4_t& a, const u32x4_t& b) {
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7"
+        : "+v"(acc) : "v"(a), "a"(b));
+}
+
+// Moves a loop-invariant matrix operand into AGPRs once, so that products
+// taking it through an "a" operand read it there instead of copying it from
+// VGPRs at every use.
+__device__ __forceinline__ void park_in_agprs(u32x4_t& x) { asm("" : "+a"(x)); }
 
 // Wait states between the last matrix write of an AGPR accumulator and any
 // other read of it (more than the 8-pass product needs).
@@ -188,6 +220,52 @@ __device__ __forceinline__ void stage_tile_lds(const uint16_t* __restrict__ src,
             rsrc, (__attribute__((address_space(3))) void*)(tile + b * 1024), 16,
             stage_src_offset<D, VTYPE>(b, lane), 0, 0, 0);
     }
+#endif
+}
+
+// Stage 1 KB blocks b = first, first + STRIDE, ... of a tile image that is
+// already laid out as the LDS tile (a byte-for-byte copy of `bytes` bytes at
+// `src`); bytes past `bytes` read as zeros.
+template <int COUNT, int STRIDE>
+__device__ __forceinline__ void stage_image_lds(const void* src, int bytes, lds_char* tile,
+                                                int first, int lane) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, bytes, kBufferFlags);
+#pragma unroll
+    for (int k = 0; k < COUNT; ++k) {
+        const int b = first + STRIDE * k;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsrc, (__attribute__((address_space(3))) void*)(tile + b * 1024), 16,
+            (uint32_t)(b * 1024 + lane * 16), 0, 0, 0);
+    }
+#endif
+}
+
+// Single-block forms of the two staging helpers above, for spreading a
+// tile's loads over a longer stretch of other work: 1 KB block b of a
+// K-type tile with `rows` valid rows (rows <= 0: nothing is read and the
+// block is zero-filled), or of an image of `bytes` bytes.
+template <int D>
+__device__ __forceinline__ void stage_tile_block(const uint16_t* __restrict__ src, lds_char* tile,
+                                                 int row0, int rows, int b, int lane) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(src + (size_t)row0 * D), (short)0, max(rows, 0) * D * 2, kBufferFlags);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rsrc, (__attribute__((address_space(3))) void*)(tile + b * 1024), 16,
+        stage_src_offset<D, false>(b, lane), 0, 0, 0);
+#endif
+}
+
+__device__ __forceinline__ void stage_image_block(const void* src, int bytes, lds_char* tile,
+                                                  int b, int lane) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, bytes, kBufferFlags);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rsrc, (__attribute__((address_space(3))) void*)(tile + b * 1024), 16,
+        (uint32_t)(b * 1024 + lane * 16), 0, 0, 0);
 #endif
 }
 

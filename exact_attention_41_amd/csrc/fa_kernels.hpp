@@ -38,21 +38,23 @@ struct BwdArgs {
 // Rows per chunk of the max-abs pre-pass of the backward.
 constexpr int kScaleRows = 256;
 
-// Byte offsets of the backward workspace blocks:
-//   delta   fp32 [B][H][N]      D_i = sum_j P_ij dP_ij (written by the dQ pass)
-//   scales  fp32 [B][H][4]      power-of-two factors for Q, K, V, dO
-//   partial u32 [B][H][chunks][4] per-chunk largest |x| (bf16 magnitude bits)
-//   q16     fp16 [B][H][N][d]   Q times its factor (written by the dQ pass)
-//   do16    fp16 [B][H][N][d]   dO times its factor (written by the dQ pass)
+// Byte offsets of the backward workspace blocks (T = ceil(N / 64) tiles of
+// 64 rows per head; an image is the byte layout of one transposed LDS tile):
+//   scales  fp32 [B][H][4]           power-of-two factors for Q, K, V, dO
+//   partial u32  [B][H][chunks][4]   per-chunk largest |x| (bf16 magnitude bits)
+//   stats   fp32 [B][H][T][128]      per query tile: lse*log2(e) of its 64 rows,
+//                                    then sE*D (sE = s_dO*s_V); from the dQ pass
+//   qt      fp16 [B][H][T][64*d]     images of (s_Q Q)^T, one per 64-row tile
+//   ot      fp16 [B][H][T][64*d]     images of (s_dO dO)^T
+//   kt      fp16 [B][H][T][64*d]     images of (s_K K)^T
 struct BwdWorkspace {
-    size_t delta, scales, partial, q16, do16, total;
+    size_t scales, partial, stats, qt, ot, kt, total;
 };
 BwdWorkspace bwd_workspace_layout(long long B, long long H, long long N, long long d);
 
-
 hipError_t launch_fwd_bf16(const FwdArgs& a);
 hipError_t launch_fwd_f32(const FwdArgs& a);
-hipError_t launch_bwd_scales(const BwdArgs& a);
+hipError_t launch_bwd_prepare(const BwdArgs& a);
 hipError_t launch_bwd_dq(const BwdArgs& a);
 hipError_t launch_bwd_dkdv(const BwdArgs& a);
 

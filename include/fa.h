@@ -92,9 +92,10 @@ fa_status_t fa_fwd_f32(const float* q, const float* k, const float* v, float* o,
 
 /*
  * Bytes of device workspace fa_bwd needs for these sizes (0 if a size is not
- * positive or d is unsupported). The workspace is O(B*H*N*d): per query row
- * it holds D_i (fp32) and power-of-two-scaled fp16 copies of that row of q
- * and dout, plus a few values per head (see fa_bwd).
+ * positive or d is unsupported). The workspace is O(B*H*N*d): per row it
+ * holds power-of-two-scaled fp16 copies of that row of q, dout and k (stored
+ * transposed per 64-row tile) and, per query row, lse and D_i (fp32), plus a
+ * few values per head (see fa_bwd).
  */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d);
 
@@ -131,11 +132,13 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o,
  * fa_bwd_dkdv, in this order, on one stream; each phase reads what the
  * previous ones left in the workspace, so they must run in this order.
  * Arguments mean what they mean for fa_bwd.
- *   fa_bwd_preprocess  per-head largest magnitudes of q, k, v, dout and the
- *                      power-of-two factors derived from them -> workspace.
- *   fa_bwd_dq          writes dq; leaves D and the scaled fp16 copies of q
- *                      and dout in the workspace.
- *   fa_bwd_dkdv        writes dk and dv from k, v, lse and the workspace.
+ *   fa_bwd_preprocess  per-head largest magnitudes of q, k, v, dout, the
+ *                      power-of-two factors derived from them, and the scaled
+ *                      fp16 transposed copies of q, dout and k -> workspace.
+ *   fa_bwd_dq          writes dq; leaves lse and D per query row in the
+ *                      workspace.
+ *   fa_bwd_dkdv        writes dk and dv from q, k, v, dout and the workspace
+ *                      (lse is taken from the workspace).
  */
 fa_status_t fa_bwd_preprocess(const void* q, const void* k, const void* v, const void* dout,
                               void* workspace, size_t workspace_bytes,
@@ -146,7 +149,7 @@ fa_status_t fa_bwd_dq(const void* q, const void* k, const void* v, const void* d
                       int B, int H, int N, int d, int causal, float scale,
                       hipStream_t stream);
 
-fa_status_t fa_bwd_dkdv(const void* k, const void* v, const float* lse,
+fa_status_t fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
                         const void* workspace, size_t workspace_bytes, void* dk, void* dv,
                         int B, int H, int N, int d, int causal, float scale,
                         hipStream_t stream);

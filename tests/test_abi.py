@@ -148,6 +148,7 @@ def test_backward_phases_reject_bad_arguments(lib):
     assert lib.fa_bwd_dq(A, A, A, A, A, W, ws, MIS, 1, 2, 100, 128, 1, 0.1, None) == UNSUPPORTED
     assert lib.fa_bwd_dq(A, A, A, A, A, W, ws, A, 1, 2, 100, 96, 1, 0.1, None) == UNSUPPORTED
     assert lib.fa_bwd_dq(A, A, A, A, A, W, ws, A, 0, 2, 100, 128, 1, 0.1, None) == OK
-    assert lib.fa_bwd_dkdv(A, A, A, W, ws, A, None, 1, 2, 100, 128, 1, 0.1, None) == INVALID
-    assert lib.fa_bwd_dkdv(A, A, A, None, ws, A, A, 1, 2, 100, 128, 1, 0.1, None) == WORKSPACE
-    assert lib.fa_bwd_dkdv(A, A, A, W, ws, A, A, 1, 2, 100, 128, 1, -1.0, None) == INVALID
+    assert lib.fa_bwd_dkdv(A, A, A, A, W, ws, A, None, 1, 2, 100, 128, 1, 0.1, None) == INVALID
+    assert lib.fa_bwd_dkdv(A, A, None, A, W, ws, A, A, 1, 2, 100, 128, 1, 0.1, None) == INVALID
+    assert lib.fa_bwd_dkdv(A, A, A, A, None, ws, A, A, 1, 2, 100, 128, 1, 0.1, None) == WORKSPACE
+    assert lib.fa_bwd_dkdv(A, A, A, A, W, ws, A, A, 1, 2, 100, 128, 1, -1.0, None) == INVALID

@@ -116,7 +116,7 @@ def test_backward_phases_equal_fa_bwd(fa):
     dq3, dk3, dv3 = (torch.empty_like(q) for _ in range(3))
     fa.fa_bwd_preprocess(q, k, v, do, ws)
     fa.fa_bwd_dq(q, k, v, do, lse, ws, dq3, causal=causal)
-    fa.fa_bwd_dkdv(k, v, lse, ws, dk3, dv3, causal=causal)
+    fa.fa_bwd_dkdv(q, k, v, do, ws, dk3, dv3, causal=causal)
     torch.cuda.synchronize()
     for a, b, c in ((dq1, dq2, dq3), (dk1, dk2, dk3), (dv1, dv2, dv3)):
         assert torch.equal(a, b) and torch.equal(a, c)
