@@ -3,7 +3,7 @@
 
 One step = one pass of the whole path over one batch of seeded synthetic
 input: the fused forward (fa_fwd) and the backward (fa_bwd's three phases:
-per-head scale factors, dQ with D, dK/dV) on the causal bf16 workload B=4 H=16 N=4096
+per-head scale factors and fp16 tile images, dQ with D, dK/dV) on the causal bf16 workload B=4 H=16 N=4096
 d=128 with upstream gradient dO. ``value`` is counted TFLOP/s of that step,
 with the counted flops 4*B*H*N^2*d (halved for causal) for the forward and
 2.5x that for the backward. Inputs are resident in HBM before timing starts.
@@ -14,6 +14,13 @@ Prints exactly one JSON line (on rank 0). Options:
   --warmup W      untimed warm-up steps (default 5)
   --no-sweep      skip the forward-only timing of the other workloads
   --no-cpu        skip the CPU oracle baseline
+  --counters      instead: run two steps and a plain 512 MiB device copy and
+                  exit (the program to run under rocprofv3 --pmc FETCH_SIZE,
+                  then --pmc WRITE_SIZE)
+  --write-traffic FETCH_DIR WRITE_DIR
+                  instead: turn the two counter runs' CSV output into
+                  profiles/traffic.json (HBM bytes per launch, scaled by what
+                  the counters read for the copy of known size)
 """
 from __future__ import annotations
 
@@ -36,6 +43,11 @@ SWEEP = ["bf16_b8h16n2048d64", "bf16_b8h16n2048d64_causal", "bf16_b2h32n8192d128
          "bf16_b1h16n16384d128_causal", "bf16_b4h16n4096d128_causal_bwd"]
 KERNEL_SOURCES = ["fa_device.hpp", "fa_kernels.hpp", "fa_fwd.hip", "fa_bwd.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+COPY_BYTES = 512 << 20          # the calibration copy reads and writes this much
+# Kernel-name fragments -> the step's kernel names.
+KERNEL_KEYS = {"fwd_bf16_kernel": "fwd", "bwd_dq_kernel": "bwd_dq", "bwd_dkdv_kernel": "bwd_dkdv",
+               "bwd_absmax_kernel": "bwd_absmax", "bwd_scale_kernel": "bwd_scale",
+               "bwd_image_kernel": "bwd_image"}
 
 
 def kernel_source_sha() -> str:
@@ -78,7 +90,7 @@ def gpu_step_timing(w, steps: int, warmup: int):
         fa.fa_bwd_dq(q, k, v, do, lse, ws, dq, causal=w.causal, scale=w.scale)
         if ev is not None:
             ev[3].record()
-        fa.fa_bwd_dkdv(k, v, lse, ws, dk, dv, causal=w.causal, scale=w.scale)
+        fa.fa_bwd_dkdv(q, k, v, do, ws, dk, dv, causal=w.causal, scale=w.scale)
         if ev is not None:
             ev[4].record()
 
@@ -134,6 +146,67 @@ def gpu_forward_sweep(names, iters=10, warmup=3):
     return out
 
 
+def counter_pass(w) -> int:
+    """Two steps of the path, then a plain copy of COPY_BYTES (torch.neg, one
+    read and one write per element) whose counter readings calibrate the
+    HBM byte counts."""
+    import torch
+
+    ms, _ = gpu_step_timing(w, steps=2, warmup=1)
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    log(f"bench --counters: 2 steps ({ms:.3f} ms/step) and 2 copies of {COPY_BYTES >> 20} MiB done")
+    return 0
+
+
+def _counter_means(run_dir: str, counter: str):
+    """Mean per dispatch of one derived counter, by kernel key (and the copy)."""
+    import csv
+    import glob
+
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {run_dir}")
+    per_dispatch = {}
+    for f in files:
+        for row in csv.DictReader(open(f)):
+            if row["Counter_Name"] != counter:
+                continue
+            name = row["Kernel_Name"]
+            key = next((v for k, v in KERNEL_KEYS.items() if k in name), None)
+            if key is None and "neg" in name:
+                key = "copy"
+            if key is None:
+                continue
+            d = per_dispatch.setdefault(key, {})
+            d[row["Dispatch_Id"]] = d.get(row["Dispatch_Id"], 0.0) + float(row["Counter_Value"])
+    return {k: sum(v.values()) / len(v) for k, v in per_dispatch.items()}
+
+
+def write_traffic(fetch_dir: str, write_dir: str) -> int:
+    fetch = _counter_means(fetch_dir, "FETCH_SIZE")
+    write = _counter_means(write_dir, "WRITE_SIZE")
+    known_kib = COPY_BYTES / 1024.0
+    fs, ws = known_kib / fetch["copy"], known_kib / write["copy"]
+    kernels = {}
+    for key in sorted(set(fetch) & set(write) - {"copy"}):
+        kernels[key] = {"fetch_kib": round(fetch[key], 1), "write_kib": round(write[key], 1),
+                        "hbm_bytes_per_launch": int(round((fetch[key] * fs + write[key] * ws) * 1024))}
+    out = {"source_sha": kernel_source_sha(), "workload": HEADLINE,
+           "copy_probe": {"bytes_each_way": COPY_BYTES, "fetch_kib": round(fetch["copy"], 1),
+                          "write_kib": round(write["copy"], 1), "fetch_scale": round(fs, 4),
+                          "write_scale": round(ws, 4)},
+           "kernels": kernels}
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    log(f"wrote {TRAFFIC_FILE}")
+    return 0
+
+
 # ---------------------------------------------------------------------------
 def cpu_baseline(w, min_seconds: float = 10.0):
     """The fp64 oracle, as it stands, on the host cores: fwd + bwd per head."""
@@ -186,7 +259,11 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--counters", action="store_true")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
+    if args.write_traffic:
+        return write_traffic(*args.write_traffic)
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported: this attention path is measured "
               "on one GPU only (heads shard across GPUs with no communication; see the design "
@@ -204,6 +281,8 @@ def main() -> int:
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
     w = wl.WORKLOADS[HEADLINE]
+    if args.counters:
+        return counter_pass(w)
     log(f"bench: workload {w.name} steps={args.steps} warmup={args.warmup}")
     ms, per_kernel = gpu_step_timing(w, args.steps, args.warmup)
     fwd_f, bwd_f = w.fwd_flops(), w.bwd_flops()
