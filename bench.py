@@ -12,7 +12,8 @@ Prints exactly one JSON line (on rank 0). Options:
   --gpus N        only N=1 is meaningful: this path runs on one GPU
   --steps K       timed steps (default 20)
   --warmup W      untimed warm-up steps (default 5)
-  --no-sweep      skip the forward-only timing of the other workloads
+  --no-sweep      skip the forward-only timing of the other workloads and the
+                  shared-K/V-head (grouped-query) workload
   --no-cpu        skip the CPU oracle baseline
   --counters      instead: run two steps and a plain 512 MiB device copy and
                   exit (the program to run under rocprofv3 --pmc FETCH_SIZE,
@@ -207,6 +208,59 @@ def write_traffic(fetch_dir: str, write_dir: str) -> int:
     return 0
 
 
+def gpu_gqa_timing(names, iters=10, warmup=3):
+    """Forward and backward of the shared-K/V-head workloads (fa_fwd_gqa,
+    fa_bwd_gqa), median of ``iters`` calls each; flops counted as for the
+    other workloads (over the H query heads)."""
+    import torch
+
+    import exact_attention_41_amd as fa
+    from exact_attention_41_amd import workloads as wl
+
+    out = []
+    dev = torch.device("cuda:0")
+    for name in names:
+        w = wl.GQA_WORKLOADS[name]
+        inp = wl.workload_inputs(w)
+        q, k, v, do = (wl.to_device(x, "bf16", dev) for x in (inp.q, inp.k, inp.v, inp.do))
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = torch.empty(fa.fa_bwd_gqa_workspace_size(w.B, w.H, w.kv_heads, w.N, w.d),
+                         dtype=torch.uint8, device=dev)
+
+        def fwd():
+            fa.fa_fwd_gqa(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+
+        def bwd():
+            fa.fa_bwd_gqa(q, k, v, o, do, lse, causal=w.causal, scale=w.scale, dq=dq, dk=dk,
+                          dv=dv, workspace=ws)
+
+        res = {}
+        for label, fn in (("fwd", fwd), ("bwd", bwd)):
+            for _ in range(warmup):
+                fn()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
+            for i in range(iters):
+                ev[i].record()
+                fn()
+                ev[i + 1].record()
+            torch.cuda.synchronize(dev)
+            times = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(iters))
+            res[label] = times[len(times) // 2]
+        ftf = w.fwd_flops() / (res["fwd"] * 1e-3) / 1e12
+        btf = w.bwd_flops() / (res["bwd"] * 1e-3) / 1e12
+        out.append({"workload": name, "H": w.H, "Hkv": w.kv_heads,
+                    "fwd_ms": round(res["fwd"], 4), "fwd_tflops": round(ftf, 1),
+                    "fwd_frac_peak": round(ftf / PEAK_BF16_TFLOPS, 4),
+                    "bwd_ms": round(res["bwd"], 4), "bwd_tflops": round(btf, 1),
+                    "bwd_frac_peak": round(btf / PEAK_BF16_TFLOPS, 4)})
+        log(f"  gqa {name}: fwd {res['fwd']:.3f} ms {ftf:.1f} TFLOP/s, "
+            f"bwd {res['bwd']:.3f} ms {btf:.1f} TFLOP/s")
+        del q, k, v, do, o, lse, dq, dk, dv, ws
+    return out
+
+
 # ---------------------------------------------------------------------------
 def cpu_baseline(w, min_seconds: float = 10.0):
     """The fp64 oracle, as it stands, on the host cores: fwd + bwd per head."""
@@ -313,6 +367,7 @@ def main() -> int:
     bwd_ms = per_kernel["bwd_preprocess"] + per_kernel["bwd_dkdv"] + per_kernel["bwd_dq"]
     bwd_tf = bwd_f / (bwd_ms * 1e-3) / 1e12
     sweep = [] if args.no_sweep else gpu_forward_sweep(SWEEP)
+    gqa = [] if args.no_sweep else gpu_gqa_timing(list(wl.GQA_WORKLOADS))
     cpu = None
     if not args.no_cpu and rank == 0:
         log("bench: timing the fp64 oracle on host cores")
@@ -334,6 +389,7 @@ def main() -> int:
         "roofline": roofline,
         "cpu_baseline": cpu,
         "forward_workloads": sweep,
+        "gqa_workloads": gqa,
         "kernel_source_sha": kernel_source_sha(),
     }
     if rank == 0:

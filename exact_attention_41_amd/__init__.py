@@ -8,6 +8,8 @@ If the library is not built, every call raises: there is no fallback.
     o, lse = fa_fwd(q, k, v, causal=True)                  # bf16 [B,H,N,d]
     o, lse = fa_fwd_f32(q, k, v, causal=False)             # fp32 [B,H,N,d]
     dq, dk, dv = fa_bwd(q, k, v, o, do, lse, causal=True)  # bf16
+    o, lse = fa_fwd_gqa(q, k, v, causal=True)              # k, v: [B,Hkv,N,d]
+    dq, dk, dv = fa_bwd_gqa(q, k, v, o, do, lse, causal=True)
 """
 from __future__ import annotations
 
@@ -17,7 +19,8 @@ from typing import Optional, Tuple
 from . import _lib
 
 __all__ = ["fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_bwd_workspace_size", "fa_status_str",
-           "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "FAError", "library_path"]
+           "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_gqa", "fa_bwd_gqa",
+           "fa_bwd_gqa_workspace_size", "FAError", "library_path"]
 
 
 class FAError(RuntimeError):
@@ -36,6 +39,10 @@ def fa_status_str(status: int) -> str:
 
 def fa_bwd_workspace_size(B: int, H: int, N: int, d: int) -> int:
     return int(_lib.load().fa_bwd_workspace_size(B, H, N, d))
+
+
+def fa_bwd_gqa_workspace_size(B: int, H: int, Hkv: int, N: int, d: int) -> int:
+    return int(_lib.load().fa_bwd_gqa_workspace_size(B, H, Hkv, N, d))
 
 
 def _torch():
@@ -67,14 +74,27 @@ def _scale(scale, d):
     return 1.0 / math.sqrt(d) if scale is None else float(scale)
 
 
-def _fwd(entry, dtype, q, k, v, causal, scale, out, lse):
+def _kv_heads(q, k, grouped):
+    """Hkv from k's shape: equal to H unless ``grouped`` (then dividing H)."""
+    if k.dim() != 4:
+        raise ValueError("k must be [B, Hkv, N, d]")
+    B, H, N, d = q.shape
+    Hkv = k.shape[1] if grouped else H
+    if Hkv < 1 or H % Hkv != 0:
+        raise ValueError(f"k has {k.shape[1]} heads, which does not divide H = {H}")
+    return Hkv
+
+
+def _fwd(entry, dtype, q, k, v, causal, scale, out, lse, grouped=False):
     torch = _torch()
     _check(q, "q", dtype)
     if q.dim() != 4:
         raise ValueError("q must be [B, H, N, d]")
     B, H, N, d = q.shape
-    _check(k, "k", dtype, q.shape, q.device)
-    _check(v, "v", dtype, q.shape, q.device)
+    Hkv = _kv_heads(q, k, grouped)
+    kv_shape = (B, Hkv, N, d)
+    _check(k, "k", dtype, kv_shape, q.device)
+    _check(v, "v", dtype, kv_shape, q.device)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
@@ -82,9 +102,10 @@ def _fwd(entry, dtype, q, k, v, causal, scale, out, lse):
     _check(out, "out", dtype, q.shape, q.device)
     _check(lse, "lse", torch.float32, (B, H, N), q.device)
     fn = getattr(_lib.load(), entry)
+    heads = (B, H, Hkv) if grouped else (B, H)
     with torch.cuda.device(q.device):
         st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                B, H, N, d, int(bool(causal)), _scale(scale, d), _stream_ptr(q.device))
+                *heads, N, d, int(bool(causal)), _scale(scale, d), _stream_ptr(q.device))
     if st != _lib.FA_OK:
         raise FAError(st, entry)
     return out, lse
@@ -96,10 +117,52 @@ def fa_fwd(q, k, v, causal: bool = False, scale: Optional[float] = None,
     return _fwd("fa_fwd", _torch().bfloat16, q, k, v, causal, scale, out, lse)
 
 
+def fa_fwd_gqa(q, k, v, causal: bool = False, scale: Optional[float] = None,
+               out=None, lse=None):
+    """bf16 forward with shared K/V heads: q [B,H,N,d], k and v [B,Hkv,N,d]
+    (Hkv dividing H; query head h uses K/V head h // (H // Hkv)). Returns
+    (O, logsumexp). Calls fa_fwd_gqa of libfa.so."""
+    return _fwd("fa_fwd_gqa", _torch().bfloat16, q, k, v, causal, scale, out, lse, grouped=True)
+
+
 def fa_fwd_f32(q, k, v, causal: bool = False, scale: Optional[float] = None,
                out=None, lse=None):
     """fp32 forward: returns (O, logsumexp). Calls fa_fwd_f32 of libfa.so."""
     return _fwd("fa_fwd_f32", _torch().float32, q, k, v, causal, scale, out, lse)
+
+
+def _bwd(entry, q, k, v, o, do, lse, causal, scale, dq, dk, dv, workspace, grouped):
+    torch = _torch()
+    bf = torch.bfloat16
+    _check(q, "q", bf)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    Hkv = _kv_heads(q, k, grouped)
+    kv_shape = (B, Hkv, N, d)
+    for t, n, shp in ((k, "k", kv_shape), (v, "v", kv_shape), (o, "o", q.shape),
+                      (do, "do", q.shape)):
+        _check(t, n, bf, shp, q.device)
+    _check(lse, "lse", torch.float32, (B, H, N), q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for t, n, shp in ((dq, "dq", q.shape), (dk, "dk", kv_shape), (dv, "dv", kv_shape)):
+        _check(t, n, bf, shp, q.device)
+    need = fa_bwd_gqa_workspace_size(B, H, Hkv, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    heads = (B, H, Hkv) if grouped else (B, H)
+    fn = getattr(_lib.load(), entry)
+    with torch.cuda.device(q.device):
+        st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                workspace.data_ptr(), ws_bytes, *heads, N, d, int(bool(causal)),
+                _scale(scale, d), _stream_ptr(q.device))
+    if st != _lib.FA_OK:
+        raise FAError(st, entry)
+    return dq, dk, dv
 
 
 def fa_bwd(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = None,
@@ -109,33 +172,16 @@ def fa_bwd(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = N
     ``workspace`` may be a uint8 device tensor of at least
     fa_bwd_workspace_size(B, H, N, d) bytes; one is allocated otherwise.
     """
-    torch = _torch()
-    bf = torch.bfloat16
-    _check(q, "q", bf)
-    if q.dim() != 4:
-        raise ValueError("q must be [B, H, N, d]")
-    B, H, N, d = q.shape
-    for t, n in ((k, "k"), (v, "v"), (o, "o"), (do, "do")):
-        _check(t, n, bf, q.shape, q.device)
-    _check(lse, "lse", torch.float32, (B, H, N), q.device)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(q) if dk is None else dk
-    dv = torch.empty_like(q) if dv is None else dv
-    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
-        _check(t, n, bf, q.shape, q.device)
-    need = fa_bwd_workspace_size(B, H, N, d)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    ws_bytes = workspace.numel() * workspace.element_size()
-    lib = _lib.load()
-    with torch.cuda.device(q.device):
-        st = lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
-                        lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                        workspace.data_ptr(), ws_bytes, B, H, N, d, int(bool(causal)),
-                        _scale(scale, d), _stream_ptr(q.device))
-    if st != _lib.FA_OK:
-        raise FAError(st, "fa_bwd")
-    return dq, dk, dv
+    return _bwd("fa_bwd", q, k, v, o, do, lse, causal, scale, dq, dk, dv, workspace, False)
+
+
+def fa_bwd_gqa(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = None,
+               dq=None, dk=None, dv=None, workspace=None):
+    """bf16 backward of fa_fwd_gqa: returns (dQ [B,H,N,d], dK and dV [B,Hkv,N,d],
+    each K/V head's gradient summed over the query heads that share it).
+    Calls fa_bwd_gqa of libfa.so; ``workspace`` as for fa_bwd, of
+    fa_bwd_gqa_workspace_size(B, H, Hkv, N, d) bytes."""
+    return _bwd("fa_bwd_gqa", q, k, v, o, do, lse, causal, scale, dq, dk, dv, workspace, True)
 
 
 def _bwd_common(ref, tensors, lse, workspace):

@@ -12,7 +12,8 @@ STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_INVALID_ARG", 2: "FA_ERR_UNSUPPORTED",
                 3: "FA_ERR_WORKSPACE", 4: "FA_ERR_HIP"}
 
 EXPORTED = ("fa_status_str", "fa_fwd", "fa_fwd_f32", "fa_bwd_workspace_size", "fa_bwd",
-            "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq")
+            "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_gqa",
+            "fa_bwd_gqa_workspace_size", "fa_bwd_gqa")
 
 _lock = threading.Lock()
 _lib = None
@@ -53,5 +54,12 @@ def load() -> ctypes.CDLL:
         lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp,
                                   i, i, i, i, i, f, vp]
         lib.fa_bwd_dq.restype = i
+        lib.fa_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+        lib.fa_fwd_gqa.restype = i
+        lib.fa_bwd_gqa_workspace_size.argtypes = [i, i, i, i, i]
+        lib.fa_bwd_gqa_workspace_size.restype = ctypes.c_size_t
+        lib.fa_bwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                   i, i, i, i, i, i, f, vp]
+        lib.fa_bwd_gqa.restype = i
         _lib = lib
         return lib

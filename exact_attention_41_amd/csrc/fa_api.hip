@@ -30,6 +30,13 @@ fa_status_t check_common(int B, int H, int N, int d, float scale, bool* empty) {
     return FA_OK;
 }
 
+// K/V head count: 1 <= Hkv, Hkv divides H (anything when H == 0).
+fa_status_t check_heads(int H, int Hkv) {
+    if (Hkv < 0) return FA_ERR_INVALID_ARG;
+    if (H > 0 && (Hkv == 0 || H % Hkv != 0)) return FA_ERR_INVALID_ARG;
+    return FA_OK;
+}
+
 fa_status_t check_tensor(const void* p) {
     if (!p) return FA_ERR_INVALID_ARG;
     if (!aligned(p, 16)) return FA_ERR_UNSUPPORTED;
@@ -77,13 +84,20 @@ const char* fa_status_str(fa_status_t status) {
     return "FA_ERR_UNKNOWN";
 }
 
-fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                   int B, int H, int N, int d, int causal, float scale, hipStream_t stream) {
+fa_status_t fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int B, int H, int Hkv, int N, int d, int causal, float scale,
+                       hipStream_t stream) {
     bool empty = false;
     FA_TRY(check_fwd(q, k, v, o, lse, B, H, N, d, scale, &empty));
+    FA_TRY(check_heads(H, Hkv));
     if (empty) return FA_OK;
-    fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, causal != 0, scale, stream};
+    fa::FwdArgs a{q, k, v, o, lse, B, H, Hkv, N, d, causal != 0, scale, stream};
     return fa::launch_fwd_bf16(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int N, int d, int causal, float scale, hipStream_t stream) {
+    return fa_fwd_gqa(q, k, v, o, lse, B, H, H, N, d, causal, scale, stream);
 }
 
 fa_status_t fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
@@ -91,13 +105,18 @@ fa_status_t fa_fwd_f32(const float* q, const float* k, const float* v, float* o,
     bool empty = false;
     FA_TRY(check_fwd(q, k, v, o, lse, B, H, N, d, scale, &empty));
     if (empty) return FA_OK;
-    fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, causal != 0, scale, stream};
+    fa::FwdArgs a{q, k, v, o, lse, B, H, H, N, d, causal != 0, scale, stream};
     return fa::launch_fwd_f32(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
+size_t fa_bwd_gqa_workspace_size(int B, int H, int Hkv, int N, int d) {
     if (B <= 0 || H <= 0 || N <= 0 || (d != 64 && d != 128)) return 0;
-    return fa::bwd_workspace_layout(B, H, N, d).total;
+    if (Hkv <= 0 || H % Hkv != 0) return 0;
+    return fa::bwd_workspace_layout(B, H, Hkv, N, d).total;
+}
+
+size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
+    return fa_bwd_gqa_workspace_size(B, H, H, N, d);
 }
 
 }  // extern "C"
@@ -108,9 +127,10 @@ namespace {
 // lse when `need_lse`) are argument errors, misaligned ones unsupported, and
 // the workspace is checked last.
 fa_status_t check_bwd(std::initializer_list<const void*> tensors, bool need_lse, const void* lse,
-                      const void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
-                      float scale, bool* empty) {
+                      const void* workspace, size_t workspace_bytes, int B, int H, int Hkv,
+                      int N, int d, float scale, bool* empty) {
     FA_TRY(check_common(B, H, N, d, scale, empty));
+    FA_TRY(check_heads(H, Hkv));
     if (*empty) return FA_OK;
     for (const void* p : tensors)
         if (!p) return FA_ERR_INVALID_ARG;
@@ -118,16 +138,17 @@ fa_status_t check_bwd(std::initializer_list<const void*> tensors, bool need_lse,
     for (const void* p : tensors) FA_TRY(check_tensor(p));
     if (need_lse) FA_TRY(check_lse(lse));
     if (!workspace || !aligned(workspace, 256) ||
-        workspace_bytes < fa_bwd_workspace_size(B, H, N, d))
+        workspace_bytes < fa_bwd_gqa_workspace_size(B, H, Hkv, N, d))
         return FA_ERR_WORKSPACE;
     return FA_OK;
 }
 
 fa::BwdArgs bwd_args(const void* q, const void* k, const void* v, const void* dout,
                      const float* lse, void* dq, void* dk, void* dv, void* workspace, int B,
-                     int H, int N, int d, int causal, float scale, hipStream_t stream) {
+                     int H, int Hkv, int N, int d, int causal, float scale,
+                     hipStream_t stream) {
     return fa::BwdArgs{q, k, v, dout, lse, dq, dk, dv, workspace,
-                       B, H, N, d, causal != 0, scale, stream};
+                       B, H, Hkv, N, d, causal != 0, scale, stream};
 }
 
 }  // namespace
@@ -138,11 +159,11 @@ fa_status_t fa_bwd_preprocess(const void* q, const void* k, const void* v, const
                               void* workspace, size_t workspace_bytes, int B, int H, int N,
                               int d, hipStream_t stream) {
     bool empty = false;
-    FA_TRY(check_bwd({q, k, v, dout}, false, nullptr, workspace, workspace_bytes, B, H, N, d,
-                     1.f, &empty));
+    FA_TRY(check_bwd({q, k, v, dout}, false, nullptr, workspace, workspace_bytes, B, H, H, N,
+                     d, 1.f, &empty));
     if (empty) return FA_OK;
     const fa::BwdArgs a = bwd_args(q, k, v, dout, nullptr, nullptr, nullptr, nullptr, workspace,
-                                   B, H, N, d, 0, 1.f, stream);
+                                   B, H, H, N, d, 0, 1.f, stream);
     return fa::launch_bwd_prepare(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -150,11 +171,11 @@ fa_status_t fa_bwd_dq(const void* q, const void* k, const void* v, const void* d
                       const float* lse, void* workspace, size_t workspace_bytes, void* dq,
                       int B, int H, int N, int d, int causal, float scale, hipStream_t stream) {
     bool empty = false;
-    FA_TRY(check_bwd({q, k, v, dout, dq}, true, lse, workspace, workspace_bytes, B, H, N, d,
+    FA_TRY(check_bwd({q, k, v, dout, dq}, true, lse, workspace, workspace_bytes, B, H, H, N, d,
                      scale, &empty));
     if (empty) return FA_OK;
     const fa::BwdArgs a = bwd_args(q, k, v, dout, lse, dq, nullptr, nullptr, workspace,
-                                   B, H, N, d, causal, scale, stream);
+                                   B, H, H, N, d, causal, scale, stream);
     return fa::launch_bwd_dq(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -163,28 +184,36 @@ fa_status_t fa_bwd_dkdv(const void* q, const void* k, const void* v, const void*
                         int B, int H, int N, int d, int causal, float scale, hipStream_t stream) {
     bool empty = false;
     FA_TRY(check_bwd({q, k, v, dout, dk, dv}, false, nullptr, workspace, workspace_bytes, B, H,
-                     N, d, scale, &empty));
+                     H, N, d, scale, &empty));
     if (empty) return FA_OK;
     const fa::BwdArgs a = bwd_args(q, k, v, dout, nullptr, nullptr, dk, dv,
-                                   const_cast<void*>(workspace), B, H, N, d, causal, scale,
+                                   const_cast<void*>(workspace), B, H, H, N, d, causal, scale,
                                    stream);
     return fa::launch_bwd_dkdv(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status_t fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o,
+                       const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                       void* workspace, size_t workspace_bytes, int B, int H, int Hkv, int N,
+                       int d, int causal, float scale, hipStream_t stream) {
+    bool empty = false;
+    FA_TRY(check_bwd({q, k, v, o, dout, dq, dk, dv}, true, lse, workspace, workspace_bytes, B, H,
+                     Hkv, N, d, scale, &empty));
+    if (empty) return FA_OK;
+    const fa::BwdArgs a = bwd_args(q, k, v, dout, lse, dq, dk, dv, workspace, B, H, Hkv, N, d,
+                                   causal, scale, stream);
+    if (fa::launch_bwd_prepare(a) != hipSuccess) return FA_ERR_HIP;
+    if (fa::launch_bwd_dq(a) != hipSuccess) return FA_ERR_HIP;
+    if (fa::launch_bwd_dkdv(a) != hipSuccess) return FA_ERR_HIP;
+    return FA_OK;
 }
 
 fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o,
                    const void* dout, const float* lse, void* dq, void* dk, void* dv,
                    void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
                    int causal, float scale, hipStream_t stream) {
-    bool empty = false;
-    FA_TRY(check_bwd({q, k, v, o, dout, dq, dk, dv}, true, lse, workspace, workspace_bytes, B, H,
-                     N, d, scale, &empty));
-    if (empty) return FA_OK;
-    const fa::BwdArgs a = bwd_args(q, k, v, dout, lse, dq, dk, dv, workspace, B, H, N, d,
-                                   causal, scale, stream);
-    if (fa::launch_bwd_prepare(a) != hipSuccess) return FA_ERR_HIP;
-    if (fa::launch_bwd_dq(a) != hipSuccess) return FA_ERR_HIP;
-    if (fa::launch_bwd_dkdv(a) != hipSuccess) return FA_ERR_HIP;
-    return FA_OK;
+    return fa_bwd_gqa(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, H, N,
+                      d, causal, scale, stream);
 }
 
 }  // extern "C"

@@ -49,42 +49,45 @@ constexpr int kFragAhead = FA_BWD_FRAG_AHEAD;
 // ---------------------------------------------------------------------------
 static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-BwdWorkspace bwd_workspace_layout(long long B, long long H, long long N, long long d) {
+BwdWorkspace bwd_workspace_layout(long long B, long long H, long long Hkv, long long N,
+                                  long long d) {
     BwdWorkspace w;
-    const size_t bh = (size_t)(B * H);
+    const size_t bh = (size_t)(B * H), bhkv = (size_t)(B * Hkv);
     const size_t chunks = (size_t)((N + kScaleRows - 1) / kScaleRows);
     const size_t tiles = (size_t)((N + 63) / 64);
-    const size_t image = bh * tiles * 64 * (size_t)d * 2;
+    const size_t image = tiles * 64 * (size_t)d * 2;     // per head
     w.scales = 0;
     w.partial = w.scales + align256(bh * 4 * 4);
-    w.stats = w.partial + align256(bh * chunks * 4 * 4);
+    w.stats = w.partial + align256((bh + bhkv) * chunks * 2 * 4);
     w.qt = w.stats + align256(bh * tiles * 128 * 4);
-    w.ot = w.qt + align256(image);
-    w.kt = w.ot + align256(image);
-    w.total = w.kt + align256(image);
+    w.ot = w.qt + align256(bh * image);
+    w.kt = w.ot + align256(bh * image);
+    w.total = w.kt + align256(bhkv * image);
     return w;
 }
 
 // ---------------------------------------------------------------------------
-// Phase 1a: per (head, chunk of kScaleRows rows), the largest |x| of Q, K, V
-// and dO, as bf16 magnitude bits (for finite values the integer order of
-// (bits & 0x7fff) is the order of |x|).
+// Phase 1a: per (head, chunk of kScaleRows rows), the largest |x| of two
+// tensors, as bf16 magnitude bits (for finite values the integer order of
+// (bits & 0x7fff) is the order of |x|): Q and dO for the BH query heads
+// (rows r < BH of the grid), K and V for the BHkv K/V heads (rows r >= BH).
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ void __launch_bounds__(256)
 bwd_absmax_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                   const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-                  uint32_t* __restrict__ partial, int N, int chunks) {
+                  uint32_t* __restrict__ partial, int BH, int N, int chunks) {
     constexpr int DCH = D / 8;
     const int bid = blockIdx.x;
-    const int bh = bid / chunks, ch = bid % chunks;
+    const int r = bid / chunks, ch = bid % chunks;
+    const bool kv = r >= BH;
     const int row0 = ch * kScaleRows;
     const int nrows = min(kScaleRows, N - row0);
-    const size_t base = ((size_t)bh * N + row0) * D;
-    const uint16_t* src[4] = {Q + base, K + base, V + base, dO + base};
-    uint32_t m[4] = {0u, 0u, 0u, 0u};
+    const size_t base = ((size_t)(kv ? r - BH : r) * N + row0) * D;
+    const uint16_t* src[2] = {(kv ? K : Q) + base, (kv ? V : dO) + base};
+    uint32_t m[2] = {0u, 0u};
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < 2; ++t) {
         for (int idx = threadIdx.x; idx < nrows * DCH; idx += 256) {
             const u32x4_t w = *(const u32x4_t*)(src[t] + (size_t)idx * 8);
 #pragma unroll
@@ -92,44 +95,54 @@ bwd_absmax_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
                 m[t] = max(m[t], max(w[c] & 0x7fffu, (w[c] >> 16) & 0x7fffu));
         }
     }
-    __shared__ uint32_t red[4][4];
+    __shared__ uint32_t red[4][2];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < 2; ++t) {
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) m[t] = max(m[t], (uint32_t)__shfl_xor((int)m[t], off));
         if (lane == 0) red[wave][t] = m[t];
     }
     __syncthreads();
-    if (threadIdx.x < 4) {
+    if (threadIdx.x < 2) {
         const int t = threadIdx.x;
-        const uint32_t r = max(max(red[0][t], red[1][t]), max(red[2][t], red[3][t]));
-        partial[((size_t)bh * chunks + ch) * 4 + t] = r;
+        const uint32_t v = max(max(red[0][t], red[1][t]), max(red[2][t], red[3][t]));
+        partial[((size_t)r * chunks + ch) * 2 + t] = v;
     }
 }
 
-// Phase 1b: per head, the power-of-two factor 2^-(e+1) for a largest
+// Phase 1b: per query head, the power-of-two factor 2^-(e+1) for a largest
 // magnitude in [2^e, 2^(e+1)), so the scaled tensor has |x| < 1 (1 for an
-// all-zero tensor); factors are kept within [2^-60, 2^60].
+// all-zero tensor); factors are kept within [2^-60, 2^60]. Q and dO take the
+// largest magnitude over the G query heads that share a K/V head, so one
+// factor serves the whole group; K and V take their K/V head's.
+__device__ __forceinline__ float pow2_factor(uint32_t m) {
+    if (m == 0u) return 1.f;
+    int e = (int)(m >> 7) - 127;          // floor(log2 max) (subnormals: -127)
+    e = min(max(e + 1, -60), 60);
+    return __uint_as_float((uint32_t)(127 - e) << 23);
+}
+
 __global__ void __launch_bounds__(64)
 bwd_scale_kernel(const uint32_t* __restrict__ partial, float* __restrict__ scales, int BH,
-                 int chunks) {
+                 int G, int chunks) {
     const int bh = blockIdx.x * 64 + threadIdx.x;
     if (bh >= BH) return;
-    uint32_t m[4] = {0u, 0u, 0u, 0u};
-    for (int c = 0; c < chunks; ++c)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) m[t] = max(m[t], partial[((size_t)bh * chunks + c) * 4 + t]);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        float s = 1.f;
-        if (m[t] != 0u) {
-            int e = (int)(m[t] >> 7) - 127;          // floor(log2 max) (subnormals: -127)
-            e = min(max(e + 1, -60), 60);
-            s = __uint_as_float((uint32_t)(127 - e) << 23);
+    const int g0 = bh - bh % G, kvh = bh / G;
+    uint32_t mq = 0u, mo = 0u, mk = 0u, mv = 0u;
+    for (int h = g0; h < g0 + G; ++h)
+        for (int c = 0; c < chunks; ++c) {
+            mq = max(mq, partial[((size_t)h * chunks + c) * 2 + 0]);
+            mo = max(mo, partial[((size_t)h * chunks + c) * 2 + 1]);
         }
-        scales[(size_t)bh * 4 + t] = s;
+    for (int c = 0; c < chunks; ++c) {
+        mk = max(mk, partial[((size_t)(BH + kvh) * chunks + c) * 2 + 0]);
+        mv = max(mv, partial[((size_t)(BH + kvh) * chunks + c) * 2 + 1]);
     }
+    scales[(size_t)bh * 4 + 0] = pow2_factor(mq);
+    scales[(size_t)bh * 4 + 1] = pow2_factor(mk);
+    scales[(size_t)bh * 4 + 2] = pow2_factor(mv);
+    scales[(size_t)bh * 4 + 3] = pow2_factor(mo);
 }
 
 // ---------------------------------------------------------------------------
@@ -196,24 +209,27 @@ struct Tile64 {
 };
 
 
-// Phase 1c: fp16 transposed images. One workgroup per (head, 64-row tile,
-// tensor), tensor 0 = Q, 1 = dO, 2 = K.
+// Phase 1c: fp16 transposed images. One workgroup per (head, 64-row tile):
+// grid rows r < BH are the Q images of the query heads, the next BH the dO
+// images, the last BHkv the K images of the K/V heads.
 template <int D>
 __global__ void __launch_bounds__(256)
 bwd_image_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                  const uint16_t* __restrict__ dO, const float* __restrict__ scales,
-                 char* __restrict__ qt, char* __restrict__ ot, char* __restrict__ kt, int N,
-                 int T) {
+                 char* __restrict__ qt, char* __restrict__ ot, char* __restrict__ kt, int BH,
+                 int G, int N, int T) {
     using TileT = Tile64<D, 256>;
     const int bid = blockIdx.x;
-    const int which = bid % 3, rest = bid / 3;
-    const int tile = rest % T, bh = rest / T;
+    const int r = bid / T, tile = bid % T;
+    const int which = r < BH ? 0 : (r < 2 * BH ? 1 : 2);
+    const int head = r - which * BH;           // query head (Q, dO) or K/V head (K)
     const uint16_t* src = which == 0 ? Q : (which == 1 ? dO : K);
     char* dst = which == 0 ? qt : (which == 1 ? ot : kt);
-    const float s = scales[bh * 4 + (which == 0 ? 0 : (which == 1 ? 3 : 1))];
+    const float s = which == 0 ? scales[head * 4 + 0]
+                  : (which == 1 ? scales[head * 4 + 3] : scales[head * G * 4 + 1]);
     TileT tl;
-    tl.load(src + (size_t)bh * N * D, tile * 64, N, threadIdx.x);
-    tl.template store_transposed<true>(dst + ((size_t)bh * T + tile) * TileT::BYTES,
+    tl.load(src + (size_t)head * N * D, tile * 64, N, threadIdx.x);
+    tl.template store_transposed<true>(dst + ((size_t)head * T + tile) * TileT::BYTES,
                                        threadIdx.x, s);
 }
 
@@ -233,7 +249,8 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
               const float* __restrict__ LSE, const float* __restrict__ scales,
               const char* __restrict__ kt_img, float* __restrict__ stats,
-              uint16_t* __restrict__ dQ, int BH, int N, int T, float c, float scale, int nqb) {
+              uint16_t* __restrict__ dQ, int BH, int G, int N, int T, float c, float scale,
+              int nqb) {
     constexpr int BC = 64;
     constexpr int BQ = NW * 32;
     constexpr int KS = D / 16;
@@ -251,9 +268,10 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const int bh = bid % BH;
     const int qb = CAUSAL ? (nqb - 1 - bid / BH) : bid / BH;
     const size_t head = (size_t)bh * (size_t)N * D;
-    const uint16_t* Kh = K + head;
-    const uint16_t* Vh = V + head;
-    const char* kt_h = kt_img + (size_t)bh * T * TB;
+    const size_t kvhead = (size_t)(bh / G) * (size_t)N * D;   // K/V head of this query head
+    const uint16_t* Kh = K + kvhead;
+    const uint16_t* Vh = V + kvhead;
+    const char* kt_h = kt_img + (size_t)(bh / G) * T * TB;
     const int q0 = qb * BQ;
     const int wq0 = q0 + wave * 32;
     const int qi = wq0 + l32;             // this lane's query row
@@ -472,8 +490,8 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                 const float* __restrict__ scales, const float* __restrict__ stats,
                 const char* __restrict__ qt_img, const char* __restrict__ ot_img,
-                uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int BH, int N, int T,
-                float c, float scale) {
+                uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int BHkv, int G, int N,
+                int T, float c, float scale) {
     constexpr int BQ = 64;
     constexpr int BKV = NW * 32;
     constexpr int KS = D / 16;
@@ -488,17 +506,14 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, l32 = lane & 31;
     const int bid = blockIdx.x;
-    const int bh = bid % BH;
-    const int kb = bid / BH;              // low key blocks see the most queries: first
-    const size_t head = (size_t)bh * (size_t)N * D;
-    const uint16_t* Qh = Q + head;
-    const uint16_t* dOh = dO + head;
-    const char* qt_h = qt_img + (size_t)bh * T * TB;
-    const char* ot_h = ot_img + (size_t)bh * T * TB;
-    const float* st_h = stats + (size_t)bh * T * 128;
+    const int bkv = bid % BHkv;           // K/V head
+    const int kb = bid / BHkv;            // low key blocks see the most queries: first
+    const size_t head = (size_t)bkv * (size_t)N * D;
+    const int qh0 = bkv * G;              // its first query head; the group is qh0 .. qh0+G-1
 
-    const float sQ = scales[bh * 4 + 0];
-    const float sV = scales[bh * 4 + 2], sDO = scales[bh * 4 + 3];
+    // One factor each for Q and dO serves the whole group of query heads.
+    const float sQ = scales[qh0 * 4 + 0];
+    const float sV = scales[qh0 * 4 + 2], sDO = scales[qh0 * 4 + 3];
     const float sE = sDO * sV;
 
     const int k0 = kb * BKV;
@@ -527,26 +542,31 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const int n_tiles = (N + BQ - 1) / BQ;
     const int t0 = CAUSAL ? (k0 / BQ) : 0;
 
-    // Query tile t into buffer buf: Q and dO rows (bf16, swizzled) and the
-    // two transposed fp16 images, BLK 1 KB blocks each spread over the NW
-    // waves (part k of NPART is one block of this wave), and the tile's 128
-    // statistics (wave 0). Past the last tile nothing is read.
+    // Query tile t of group member gq (query head qh0 + gq) into buffer buf:
+    // Q and dO rows (bf16, swizzled) and the two transposed fp16 images, BLK
+    // 1 KB blocks each spread over the NW waves (part k of NPART is one block
+    // of this wave), and the tile's 128 statistics (wave 0). Past the last
+    // tile of the last member nothing is read.
     constexpr int PPT = BLK / NW;
     constexpr int NPART = 4 * PPT;
-    auto stage_part = [&](int t, int buf, int k) {
+    auto stage_part = [&](int gq, int t, int buf, int k) {
         lds_char* base = (lds_char*)(smem + buf * BUF);
         const int tensor = k / PPT, b = wave + NW * (k % PPT);
-        const bool live = t < n_tiles;
+        const bool live = gq < G && t < n_tiles;
+        const size_t qh = (size_t)(qh0 + (live ? gq : 0));
         if (tensor < 2)
-            stage_tile_block<D>(tensor == 0 ? Qh : dOh, base + (tensor == 0 ? OFF_Q : OFF_DO),
-                                t * BQ, live ? min(BQ, N - t * BQ) : 0, b, lane);
+            stage_tile_block<D>((tensor == 0 ? Q : dO) + qh * N * D,
+                                base + (tensor == 0 ? OFF_Q : OFF_DO), t * BQ,
+                                live ? min(BQ, N - t * BQ) : 0, b, lane);
         else
-            stage_image_block((tensor == 2 ? qt_h : ot_h) + (size_t)t * TB, live ? TB : 0,
-                              base + (tensor == 2 ? OFF_QT : OFF_DOT), b, lane);
+            stage_image_block((tensor == 2 ? qt_img : ot_img) + (qh * T + t) * TB,
+                              live ? TB : 0, base + (tensor == 2 ? OFF_QT : OFF_DOT), b, lane);
     };
-    auto stage_stats = [&](int t, int buf) {
+    auto stage_stats = [&](int gq, int t, int buf) {
         lds_char* base = (lds_char*)(smem + buf * BUF);
-        if (wave == 0) stage_image_block(st_h + (size_t)t * 128, t < n_tiles ? 512 : 0,
+        const bool live = gq < G && t < n_tiles;
+        const size_t qh = (size_t)(qh0 + (live ? gq : 0));
+        if (wave == 0) stage_image_block(stats + (qh * T + t) * 128, live ? 512 : 0,
                                          base + OFF_ST, 0, lane);
     };
 
@@ -566,14 +586,18 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     lds_char* pst = s0 + OFF_ST + 16 * g;
 
 #pragma unroll
-    for (int k = 0; k < NPART; ++k) stage_part(t0, 0, k);
-    stage_stats(t0, 0);
+    for (int k = 0; k < NPART; ++k) stage_part(0, t0, 0, k);
+    stage_stats(0, t0, 0);
     __syncthreads();
 
-    // One query tile: stage the next one, run the pipeline, move the bases.
-    auto iteration = [&](int t, auto mask_tag) {
+    // One query tile of group member gq: stage the next tile (the member's
+    // next, or the next member's first), run the pipeline, move the bases.
+    const int nt = n_tiles - t0;
+    auto iteration = [&](int gq, int t, auto mask_tag) {
         const int i0 = t * BQ;
-        const int buf = (t - t0) & 1;
+        const int buf = (gq * nt + t - t0) & 1;
+        const int ngq = (t + 1 < n_tiles) ? gq : gq + 1;
+        const int nt1 = (t + 1 < n_tiles) ? t + 1 : t0;
 
         // The tile's 2*NSD + 4*NG products run as one software pipeline:
         // S, dP of query half 0, then of half 1 (while half 0 is
@@ -663,8 +687,8 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 constexpr int O0 = 2 * NSD + 2 * NG;
 #pragma unroll
                 for (int k = 0; k < NPART; ++k)
-                    if (o == O0 + k * (NOPS - O0) / NPART) stage_part(t + 1, buf ^ 1, k);
-                if (o == O0 + 1) stage_stats(t + 1, buf ^ 1);
+                    if (o == O0 + k * (NOPS - O0) / NPART) stage_part(ngq, nt1, buf ^ 1, k);
+                if (o == O0 + 1) stage_stats(ngq, nt1, buf ^ 1);
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
@@ -679,9 +703,12 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     };
     // Causal: only the first two query tiles reach above some wave's keys
     // (a wave whose keys all follow such a tile computes it fully masked).
+    // dK and dV sum over the G query heads that share this K/V head.
     const int t_free = CAUSAL ? min(t0 + 2, n_tiles) : t0;
-    for (int t = t0; t < t_free; ++t) iteration(t, BoolTag<true>{});
-    for (int t = t_free; t < n_tiles; ++t) iteration(t, BoolTag<false>{});
+    for (int gq = 0; gq < G; ++gq) {
+        for (int t = t0; t < t_free; ++t) iteration(gq, t, BoolTag<true>{});
+        for (int t = t_free; t < n_tiles; ++t) iteration(gq, t, BoolTag<false>{});
+    }
 
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -712,7 +739,9 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 // ---------------------------------------------------------------------------
 constexpr int kBwdWaves = 4;
 
-static BwdWorkspace ws_of(const BwdArgs& a) { return bwd_workspace_layout(a.B, a.H, a.N, a.d); }
+static BwdWorkspace ws_of(const BwdArgs& a) {
+    return bwd_workspace_layout(a.B, a.H, a.Hkv, a.N, a.d);
+}
 
 template <typename T>
 static T* ws_ptr(const BwdArgs& a, size_t off) { return (T*)((char*)a.workspace + off); }
@@ -722,23 +751,24 @@ static int n_tiles64(const BwdArgs& a) { return (a.N + 63) / 64; }
 template <int D>
 static hipError_t launch_prepare_t(const BwdArgs& a) {
     const BwdWorkspace w = ws_of(a);
-    const int BH = a.B * a.H;
+    const int BH = a.B * a.H, BHkv = a.B * a.Hkv, G = a.H / a.Hkv;
     const int chunks = (a.N + kScaleRows - 1) / kScaleRows;
     const int T = n_tiles64(a);
     uint32_t* partial = ws_ptr<uint32_t>(a, w.partial);
-    hipLaunchKernelGGL((bwd_absmax_kernel<D>), dim3(BH * chunks), dim3(256), 0, a.stream,
-                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                       (const uint16_t*)a.dout, partial, a.N, chunks);
+    hipLaunchKernelGGL((bwd_absmax_kernel<D>), dim3((BH + BHkv) * chunks), dim3(256), 0,
+                       a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                       (const uint16_t*)a.v, (const uint16_t*)a.dout, partial, BH, a.N, chunks);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_scale_kernel, dim3((BH + 63) / 64), dim3(64), 0, a.stream,
-                       (const uint32_t*)partial, ws_ptr<float>(a, w.scales), BH, chunks);
+                       (const uint32_t*)partial, ws_ptr<float>(a, w.scales), BH, G, chunks);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_image_kernel<D>), dim3(BH * T * 3), dim3(256), 0, a.stream,
-                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.dout,
-                       ws_ptr<const float>(a, w.scales), ws_ptr<char>(a, w.qt),
-                       ws_ptr<char>(a, w.ot), ws_ptr<char>(a, w.kt), a.N, T);
+    hipLaunchKernelGGL((bwd_image_kernel<D>), dim3((2 * BH + BHkv) * T), dim3(256), 0,
+                       a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                       (const uint16_t*)a.dout, ws_ptr<const float>(a, w.scales),
+                       ws_ptr<char>(a, w.qt), ws_ptr<char>(a, w.ot), ws_ptr<char>(a, w.kt), BH,
+                       G, a.N, T);
     return hipGetLastError();
 }
 
@@ -752,8 +782,8 @@ static hipError_t launch_dq_t(const BwdArgs& a) {
                        a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                        (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse,
                        ws_ptr<const float>(a, w.scales), ws_ptr<const char>(a, w.kt),
-                       ws_ptr<float>(a, w.stats), (uint16_t*)a.dq, BH, a.N, n_tiles64(a),
-                       a.scale * kLog2e, a.scale, nqb);
+                       ws_ptr<float>(a, w.stats), (uint16_t*)a.dq, BH, a.H / a.Hkv, a.N,
+                       n_tiles64(a), a.scale * kLog2e, a.scale, nqb);
     return hipGetLastError();
 }
 
@@ -761,14 +791,14 @@ template <int D, bool CAUSAL>
 static hipError_t launch_dkdv_t(const BwdArgs& a) {
     constexpr int NW = kBwdWaves;
     const BwdWorkspace w = ws_of(a);
-    const int BH = a.B * a.H;
+    const int BHkv = a.B * a.Hkv;
     const int nkb = (a.N + NW * 32 - 1) / (NW * 32);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, CAUSAL>), dim3(nkb * BH), dim3(NW * 64), 0,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, CAUSAL>), dim3(nkb * BHkv), dim3(NW * 64), 0,
                        a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                        (const uint16_t*)a.v, (const uint16_t*)a.dout,
                        ws_ptr<const float>(a, w.scales), ws_ptr<const float>(a, w.stats),
                        ws_ptr<const char>(a, w.qt), ws_ptr<const char>(a, w.ot),
-                       (uint16_t*)a.dk, (uint16_t*)a.dv, BH, a.N, n_tiles64(a),
+                       (uint16_t*)a.dk, (uint16_t*)a.dv, BHkv, a.H / a.Hkv, a.N, n_tiles64(a),
                        a.scale * kLog2e, a.scale);
     return hipGetLastError();
 }

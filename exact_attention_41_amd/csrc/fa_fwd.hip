@@ -65,7 +65,7 @@ template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(kFwdWaves * 64, 1)
 fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
-                float* __restrict__ LSE, int BH, int N, float c, int nqb) {
+                float* __restrict__ LSE, int BH, int G, int N, float c, int nqb) {
     constexpr int BC = 64;                 // keys per tile
     constexpr int BR = kFwdWaves * 32;     // query rows per workgroup
     constexpr int KS = D / 16;             // MFMA k-steps over d
@@ -82,19 +82,23 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const int g = lane >> 5;
     const int l32 = lane & 31;
 
-    // Longest query blocks first (causal), heads fastest: consecutive
-    // workgroup ids take different heads, so with the round-robin dispatch over
-    // the eight XCDs every XCD keeps to a fixed subset of heads and their K/V
-    // stays in that XCD's L2.
+    // Longest query blocks first (causal), heads fastest. Workgroup ids are
+    // dispatched round-robin over the eight XCDs, so id mod 8 picks the XCD;
+    // when BH is a multiple of 8 the heads are renumbered so that XCD x runs
+    // the contiguous heads [x BH/8, (x+1) BH/8): every XCD keeps to a fixed
+    // set of heads, and the G query heads that share a K/V head (G dividing
+    // BH/8) read it from the same L2.
     const int bid = blockIdx.x;
-    const int bh = bid % BH;
+    const int hh = bid % BH;
+    const int bh = (BH & 7) ? hh : (hh & 7) * (BH >> 3) + (hh >> 3);
     const int qb_rank = bid / BH;
     const int qb = CAUSAL ? (nqb - 1 - qb_rank) : qb_rank;
 
     const size_t head = (size_t)bh * (size_t)N * D;
+    const size_t kvhead = (size_t)(bh / G) * (size_t)N * D;   // K/V head of this query head
     const uint16_t* Qh = Q + head;
-    const uint16_t* Kh = K + head;
-    const uint16_t* Vh = V + head;
+    const uint16_t* Kh = K + kvhead;
+    const uint16_t* Vh = V + kvhead;
     const int q0 = qb * BR;
     const int wq0 = q0 + wave * 32;
     const int qi = wq0 + l32;              // this lane's query row
@@ -444,7 +448,8 @@ static hipError_t launch_fwd_bf16_t(const FwdArgs& a) {
     const float c = a.scale * kLog2e;
     hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3(nqb * BH), dim3(kFwdWaves * 64), 0,
                        a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                       (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, BH, a.N, c, nqb);
+                       (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, BH, a.H / a.Hkv, a.N, c,
+                       nqb);
     return hipGetLastError();
 }
 

@@ -7,13 +7,15 @@
 
 namespace fa {
 
+// H query heads; K/V have Hkv heads (Hkv divides H), query head h using K/V
+// head h / (H / Hkv). Hkv == H is ordinary multi-head attention.
 struct FwdArgs {
     const void* q;
     const void* k;
     const void* v;
     void* o;
     float* lse;
-    int B, H, N, d;
+    int B, H, Hkv, N, d;
     bool causal;
     float scale;
     hipStream_t stream;
@@ -29,7 +31,7 @@ struct BwdArgs {
     void* dk;
     void* dv;
     void* workspace;
-    int B, H, N, d;
+    int B, H, Hkv, N, d;
     bool causal;
     float scale;
     hipStream_t stream;
@@ -39,18 +41,24 @@ struct BwdArgs {
 constexpr int kScaleRows = 256;
 
 // Byte offsets of the backward workspace blocks (T = ceil(N / 64) tiles of
-// 64 rows per head; an image is the byte layout of one transposed LDS tile):
-//   scales  fp32 [B][H][4]           power-of-two factors for Q, K, V, dO
-//   partial u32  [B][H][chunks][4]   per-chunk largest |x| (bf16 magnitude bits)
-//   stats   fp32 [B][H][T][128]      per query tile: lse*log2(e) of its 64 rows,
+// 64 rows per head; an image is the byte layout of one transposed LDS tile;
+// BH = B*H query heads, BHkv = B*Hkv K/V heads):
+//   scales  fp32 [BH][4]             power-of-two factors for Q, K, V, dO as
+//                                    seen by each query head (Q and dO common
+//                                    to the query heads of one K/V head)
+//   partial u32  [BH + BHkv][chunks][2] per-chunk largest |x| (bf16 magnitude
+//                                    bits): (Q, dO) per query head, then (K, V)
+//                                    per K/V head
+//   stats   fp32 [BH][T][128]        per query tile: lse*log2(e) of its 64 rows,
 //                                    then sE*D (sE = s_dO*s_V); from the dQ pass
-//   qt      fp16 [B][H][T][64*d]     images of (s_Q Q)^T, one per 64-row tile
-//   ot      fp16 [B][H][T][64*d]     images of (s_dO dO)^T
-//   kt      fp16 [B][H][T][64*d]     images of (s_K K)^T
+//   qt      fp16 [BH][T][64*d]       images of (s_Q Q)^T, one per 64-row tile
+//   ot      fp16 [BH][T][64*d]       images of (s_dO dO)^T
+//   kt      fp16 [BHkv][T][64*d]     images of (s_K K)^T
 struct BwdWorkspace {
     size_t scales, partial, stats, qt, ot, kt, total;
 };
-BwdWorkspace bwd_workspace_layout(long long B, long long H, long long N, long long d);
+BwdWorkspace bwd_workspace_layout(long long B, long long H, long long Hkv, long long N,
+                                  long long d);
 
 hipError_t launch_fwd_bf16(const FwdArgs& a);
 hipError_t launch_fwd_f32(const FwdArgs& a);

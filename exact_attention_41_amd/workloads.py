@@ -8,7 +8,8 @@ method's code.
 Recipe (the same for every workload):
   * generator ``numpy.random.Generator(PCG64(seed))``;
   * ``standard_normal(dtype=float32)`` draws, tensor by tensor in the order
-    q, k, v, then dO, each of shape [B, H, N, d] (row-major);
+    q, k, v, then dO, each of shape [B, H, N, d] (row-major; k and v have
+    [B, Hkv, N, d] when Hkv K/V heads are shared by the H query heads);
   * an optional fp32 multiplier on q and k (the sharpened-softmax workload);
   * one round-to-nearest-even cast to bfloat16 (except fp32 workloads).
 
@@ -38,6 +39,11 @@ class Workload:
     qk_mult: float = 1.0
     backward: bool = False
     description: str = ""
+    Hkv: Optional[int] = None      # K/V heads (None: H, ordinary multi-head)
+
+    @property
+    def kv_heads(self) -> int:
+        return self.H if self.Hkv is None else self.Hkv
 
     @property
     def scale(self) -> float:
@@ -72,6 +78,16 @@ WORKLOADS: Dict[str, Workload] = {
         Workload("bf16_b4h16n4096d128_causal_bwd", 4, 16, 4096, 128, "bf16", True, 5,
                  backward=True,
                  description="causal bf16 forward + backward with upstream dO"),
+    ]
+}
+
+# Shared K/V heads: 32 query heads over 8 K/V heads (groups of 4).
+GQA_WORKLOADS: Dict[str, Workload] = {
+    w.name: w
+    for w in [
+        Workload("bf16_b2h32kv8n4096d128_causal_gqa", 2, 32, 4096, 128, "bf16", True, 6,
+                 backward=True, Hkv=8,
+                 description="causal bf16 forward + backward, 32 query heads sharing 8 K/V heads"),
     ]
 }
 
@@ -112,13 +128,15 @@ class Inputs:
 
 
 def make_inputs(B: int, H: int, N: int, d: int, dtype: str, seed: int,
-                qk_mult: float = 1.0, with_do: bool = False) -> Inputs:
+                qk_mult: float = 1.0, with_do: bool = False,
+                Hkv: Optional[int] = None) -> Inputs:
     """Draw q, k, v (and dO) following the recipe in the module docstring."""
     rng = np.random.Generator(np.random.PCG64(seed))
     shape = (B, H, N, d)
+    kv_shape = (B, H if Hkv is None else Hkv, N, d)
     q = rng.standard_normal(shape, dtype=np.float32)
-    k = rng.standard_normal(shape, dtype=np.float32)
-    v = rng.standard_normal(shape, dtype=np.float32)
+    k = rng.standard_normal(kv_shape, dtype=np.float32)
+    v = rng.standard_normal(kv_shape, dtype=np.float32)
     do = rng.standard_normal(shape, dtype=np.float32) if with_do else None
     if qk_mult != 1.0:
         q = q * np.float32(qk_mult)
@@ -134,7 +152,7 @@ def make_inputs(B: int, H: int, N: int, d: int, dtype: str, seed: int,
 
 def workload_inputs(w: Workload) -> Inputs:
     return make_inputs(w.B, w.H, w.N, w.d, w.dtype, w.seed, w.qk_mult,
-                       with_do=w.backward)
+                       with_do=w.backward, Hkv=w.Hkv)
 
 
 def to_device(x: np.ndarray, dtype: str, device="cuda"):

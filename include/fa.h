@@ -83,6 +83,21 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
                    hipStream_t stream);
 
 /*
+ * Forward with shared K/V heads (multi-query and grouped-query attention; the
+ * "FlashAttention" page, systems-analysis.ru, section "FlashAttention-2
+ * (2023)", names multi-query attention among the extensions).
+ *   q, o     bf16 [B][H][N][d], lse fp32 [B][H][N], as for fa_fwd.
+ *   k, v     bf16 [B][Hkv][N][d]: Hkv K/V heads, Hkv >= 1 dividing H.
+ * Query head h attends with K/V head h / (H / Hkv): consecutive groups of
+ * H / Hkv query heads share one K/V head (Hkv == 1 is multi-query attention,
+ * Hkv == H is fa_fwd). Hkv < 1 or not dividing H -> FA_ERR_INVALID_ARG.
+ * Everything else as for fa_fwd.
+ */
+fa_status_t fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int B, int H, int Hkv, int N, int d, int causal, float scale,
+                       hipStream_t stream);
+
+/*
  * Forward, fp32 storage and fp32 arithmetic throughout (no reduced-precision
  * operands). Same layout, masking, outputs and errors as fa_fwd.
  */
@@ -98,6 +113,10 @@ fa_status_t fa_fwd_f32(const float* q, const float* k, const float* v, float* o,
  * few values per head (see fa_bwd).
  */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d);
+
+/* Workspace bytes for fa_bwd_gqa (0 also when Hkv < 1 or Hkv does not divide
+ * H). fa_bwd_workspace_size(B, H, N, d) equals this with Hkv == H. */
+size_t fa_bwd_gqa_workspace_size(int B, int H, int Hkv, int N, int d);
 
 /*
  * Backward, bfloat16 storage: the gradients of the scalar
@@ -125,6 +144,21 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o,
                    void* workspace, size_t workspace_bytes,
                    int B, int H, int N, int d, int causal, float scale,
                    hipStream_t stream);
+
+/*
+ * Backward of fa_fwd_gqa. q, o, dout, dq bf16 [B][H][N][d] and lse fp32
+ * [B][H][N] as for fa_bwd; k, v, dk, dv bf16 [B][Hkv][N][d]. dk and dv of a
+ * K/V head are the sums over its H / Hkv query heads (the chain rule through
+ * the shared head), accumulated in a fixed order, so the result is still
+ * deterministic. workspace: fa_bwd_gqa_workspace_size(B, H, Hkv, N, d) bytes.
+ * Hkv < 1 or not dividing H -> FA_ERR_INVALID_ARG. Everything else as for
+ * fa_bwd; fa_bwd is this with Hkv == H.
+ */
+fa_status_t fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o,
+                       const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                       void* workspace, size_t workspace_bytes,
+                       int B, int H, int Hkv, int N, int d, int causal, float scale,
+                       hipStream_t stream);
 
 /*
  * The three phases of fa_bwd, for callers that schedule or time them

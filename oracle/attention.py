@@ -39,6 +39,13 @@ materialised. This is still the one-shot definition, not an online softmax.
 Arrays are float64 numpy arrays of shape [B, H, N, d]; lse is [B, H, N].
 A row with every key masked (impossible for the square causal case) gets
 O = 0 and lse = -inf.
+
+Shared K/V heads (the "FlashAttention" page, section "FlashAttention-2
+(2023)", names multi-query attention among the extensions; grouped heads are
+the plainest generalisation): k and v may have Hkv heads, Hkv dividing H, and
+query head h then uses K/V head h // (H // Hkv). Each query head's forward is
+the definition above with that K/V head; the gradient of a shared K/V head is
+the sum of its query heads' gradients (the chain rule through a shared input).
 """
 from __future__ import annotations
 
@@ -134,6 +141,14 @@ def head_dq_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
     return dq
 
 
+def _group(H: int, k: np.ndarray) -> int:
+    """Query heads per K/V head (k has shape [B, Hkv, N, d], Hkv dividing H)."""
+    Hkv = k.shape[1]
+    if Hkv < 1 or H % Hkv:
+        raise ValueError(f"{Hkv} K/V heads do not divide {H} query heads")
+    return H // Hkv
+
+
 def _heads(B: int, H: int, heads: Optional[Iterable[Tuple[int, int]]]):
     return [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
 
@@ -158,12 +173,13 @@ def attention_fwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool,
     Without either, the result has the input's [B, H, N, d] shape.
     """
     B, H, N, d = q.shape
+    G = _group(H, k)
     hs = _heads(B, H, heads)
     rr = np.arange(N) if rows is None else np.asarray(rows)
 
     def one(bh):
         b, h = bh
-        return head_fwd(q[b, h], k[b, h], v[b, h], causal, scale, rr)
+        return head_fwd(q[b, h], k[b, h // G], v[b, h // G], causal, scale, rr)
 
     res = _pool_map(one, hs, workers)
     o = np.stack([r[0] for r in res]) if res else np.zeros((0, len(rr), v.shape[-1]))
@@ -177,21 +193,29 @@ def attention_bwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
                   causal: bool, scale: float,
                   heads: Optional[Sequence[Tuple[int, int]]] = None,
                   workers: Optional[int] = 1):
-    """Backward over [B, H, N, d] arrays; ``heads`` as in :func:`attention_fwd`."""
+    """Backward over [B, H, N, d] arrays (k, v: [B, Hkv, N, d]).
+
+    Without ``heads``: dQ [B, H, N, d] and dK, dV [B, Hkv, N, d], a shared
+    K/V head's gradient being the sum over its query heads. With ``heads`` (a
+    list of query heads (b, h)): each listed query head's own dQ, dK, dV
+    contributions, stacked, before any summing.
+    """
     B, H, N, d = q.shape
+    G = _group(H, k)
     hs = _heads(B, H, heads)
 
     def one(bh):
         b, h = bh
-        return head_bwd(q[b, h], k[b, h], v[b, h], do[b, h], causal, scale)
+        return head_bwd(q[b, h], k[b, h // G], v[b, h // G], do[b, h], causal, scale)
 
     res = _pool_map(one, hs, workers)
     dq = np.stack([r[0] for r in res])
     dk = np.stack([r[1] for r in res])
     dv = np.stack([r[2] for r in res])
     if heads is None:
-        shape = (B, H, N, d)
-        return dq.reshape(shape), dk.reshape(shape), dv.reshape(shape)
+        kv_shape = (B, H // G, G, N, d)
+        return (dq.reshape(B, H, N, d), dk.reshape(kv_shape).sum(axis=2),
+                dv.reshape(kv_shape).sum(axis=2))
     return dq, dk, dv
 
 

@@ -127,6 +127,35 @@ def test_backward_rejects_bad_arguments(lib):
     assert bwd(lib, B=0, ws=None, ws_bytes=0) == OK
 
 
+def test_grouped_heads_arguments(lib):
+    """fa_fwd_gqa / fa_bwd_gqa: Hkv must be >= 1 and divide H."""
+    def f(Hkv, H=4, **kw):
+        return lib.fa_fwd_gqa(A, A, A, A, A, 1, H, Hkv, 64, 64, 0, 0.125, None)
+    assert f(0) == INVALID
+    assert f(-1) == INVALID
+    assert f(3) == INVALID
+    assert f(8) == INVALID
+    assert lib.fa_fwd_gqa(None, A, A, A, A, 1, 4, 2, 64, 64, 0, 0.125, None) == INVALID
+    assert lib.fa_fwd_gqa(A, A, A, A, A, 1, 4, 2, 64, 96, 0, 0.125, None) == UNSUPPORTED
+    assert lib.fa_fwd_gqa(A, A, A, A, A, 0, 4, 2, 64, 64, 0, 0.125, None) == OK
+    assert lib.fa_bwd_gqa_workspace_size(2, 32, 8, 4096, 128) > 0
+    assert lib.fa_bwd_gqa_workspace_size(2, 32, 5, 4096, 128) == 0
+    assert lib.fa_bwd_gqa_workspace_size(2, 32, 0, 4096, 128) == 0
+    assert lib.fa_bwd_gqa_workspace_size(4, 16, 16, 4096, 128) == \
+        lib.fa_bwd_workspace_size(4, 16, 4096, 128)
+    # fewer K/V heads: smaller workspace (one K image per K/V head)
+    assert lib.fa_bwd_gqa_workspace_size(4, 16, 4, 4096, 128) < \
+        lib.fa_bwd_workspace_size(4, 16, 4096, 128)
+    ws = lib.fa_bwd_gqa_workspace_size(1, 4, 2, 100, 128)
+
+    def b(Hkv=2, ws_bytes=ws, **kw):
+        return lib.fa_bwd_gqa(A, A, A, A, A, A, A, A, A, 0x200000, ws_bytes, 1, 4, Hkv, 100, 128,
+                              1, 0.088, None)
+    assert b(Hkv=3) == INVALID
+    assert b(Hkv=0) == INVALID
+    assert b(ws_bytes=ws - 1) == WORKSPACE
+
+
 def test_python_binding_refuses_without_gpu_tensors():
     torch = pytest.importorskip("torch")
     import exact_attention_41_amd as fa

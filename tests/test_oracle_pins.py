@@ -297,6 +297,95 @@ def test_against_torch_float64_sdpa_and_autograd(causal):
     np.testing.assert_allclose(dv, tv.grad.numpy(), atol=1e-12)
 
 
+# ------------------------------------------- shared K/V heads (MQA / GQA)
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("H,Hkv", [(4, 1), (4, 2), (6, 3), (3, 3)])
+def test_grouped_heads_against_torch_sdpa_enable_gqa(causal, H, Hkv):
+    """torch's fp64 SDPA with enable_gqa (K/V heads repeated so that
+    consecutive query heads share one) and its autograd, as the library
+    special case for grouped heads."""
+    torch = pytest.importorskip("torch")
+    r = _rng(30 + H + Hkv)
+    B, N, d = 2, 13, 4
+    q, do = (r.standard_normal((B, H, N, d)) for _ in range(2))
+    k, v = (r.standard_normal((B, Hkv, N, d)) for _ in range(2))
+    scale = 0.7
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    to = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk, tv, is_causal=causal, scale=scale, enable_gqa=True)
+    to.backward(torch.tensor(do))
+    o, _ = ora.attention_fwd(q, k, v, causal, scale)
+    dq, dk, dv = ora.attention_bwd(q, k, v, do, causal, scale)
+    assert dk.shape == k.shape and dv.shape == v.shape
+    np.testing.assert_allclose(o, to.detach().numpy(), atol=1e-12)
+    np.testing.assert_allclose(dq, tq.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_grouped_heads_gradients_match_finite_differences(causal):
+    """dK, dV of a shared K/V head against central differences of the loss
+    sum(O * dO) taken through the forward (which reads that head G times)."""
+    r = _rng(41)
+    B, H, Hkv, N, d = 1, 4, 2, 7, 3
+    q, do = (r.standard_normal((B, H, N, d)) for _ in range(2))
+    k, v = (r.standard_normal((B, Hkv, N, d)) for _ in range(2))
+    scale, h = 0.6, 1e-6
+    _, dk, dv = ora.attention_bwd(q, k, v, do, causal, scale)
+
+    def loss(kk, vv):
+        o, _ = ora.attention_fwd(q, kk, vv, causal, scale)
+        return float(np.sum(o * do))
+
+    for _ in range(24):
+        idx = tuple(int(r.integers(0, n)) for n in k.shape)
+        for which, grad in (("k", dk), ("v", dv)):
+            kp, km, vp, vm = k.copy(), k.copy(), v.copy(), v.copy()
+            if which == "k":
+                kp[idx] += h
+                km[idx] -= h
+            else:
+                vp[idx] += h
+                vm[idx] -= h
+            fd = (loss(kp, vp) - loss(km, vm)) / (2 * h)
+            assert abs(fd - grad[idx]) <= 1e-6 * max(1.0, abs(fd)), (which, idx, fd, grad[idx])
+
+
+def test_identical_query_heads_share_results():
+    """Multi-query attention with every query head (and dO) equal: every head
+    gives the single-head result, and the shared K/V head's gradient is G times
+    the single-head gradient (scalar brute force for the forward)."""
+    r = _rng(42)
+    G, N, d = 3, 6, 2
+    q1, do1 = r.standard_normal((N, d)), r.standard_normal((N, d))
+    k1, v1 = r.standard_normal((N, d)), r.standard_normal((N, d))
+    q = np.broadcast_to(q1, (1, G, N, d)).copy()
+    do = np.broadcast_to(do1, (1, G, N, d)).copy()
+    k, v = k1[None, None], v1[None, None]
+    o, lse = ora.attention_fwd(q, k, v, True, 0.9)
+    ob, lb = brute.attention(q1.tolist(), k1.tolist(), v1.tolist(), True, 0.9)
+    for g in range(G):
+        np.testing.assert_allclose(o[0, g], ob, atol=1e-13)
+        np.testing.assert_allclose(lse[0, g], lb, atol=1e-13)
+    _, dk, dv = ora.attention_bwd(q, k, v, do, True, 0.9)
+    _, dk1, dv1 = ora.head_bwd(q1, k1, v1, do1, True, 0.9)
+    np.testing.assert_allclose(dk[0, 0], G * dk1, atol=1e-12)
+    np.testing.assert_allclose(dv[0, 0], G * dv1, atol=1e-12)
+
+
+def test_group_mapping_is_pinned():
+    """The torch pin tells the consecutive-heads mapping (h // G) apart from an
+    interleaved one (h % Hkv): on the same inputs the two disagree."""
+    r = _rng(43)
+    q = r.standard_normal((1, 4, 5, 2))
+    k, v = r.standard_normal((1, 2, 5, 2)), r.standard_normal((1, 2, 5, 2))
+    o, _ = ora.attention_fwd(q, k, v, False, 1.0)
+    o_interleaved = np.stack([ora.head_fwd(q[0, h], k[0, h % 2], v[0, h % 2], False, 1.0,
+                                           np.arange(5))[0] for h in range(4)])
+    assert not np.allclose(o[0], o_interleaved)
+
+
 # ------------------------------------------------------ planted-mistake checks
 def _brute_mismatch():
     r = _rng(16)
