@@ -12,8 +12,8 @@ Prints exactly one JSON line (on rank 0). Options:
   --gpus N        only N=1 is meaningful: this path runs on one GPU
   --steps K       timed steps (default 20)
   --warmup W      untimed warm-up steps (default 5)
-  --no-sweep      skip the forward-only timing of the other workloads and the
-                  shared-K/V-head (grouped-query) workload
+  --no-sweep      skip the forward-only timing of the other workloads, the
+                  shared-K/V-head (grouped-query) workload and decoding
   --no-cpu        skip the CPU oracle baseline
   --counters      instead: run two steps and a plain 512 MiB device copy and
                   exit (the program to run under rocprofv3 --pmc FETCH_SIZE,
@@ -261,6 +261,50 @@ def gpu_gqa_timing(names, iters=10, warmup=3):
     return out
 
 
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+
+
+def gpu_decode_timing(names, iters=20, warmup=5):
+    """Split-K/V decoding (fa_decode): median time per call and the rate at
+    which it moves its algorithmic bytes (K and V once, q, O, lse), against
+    the HBM roof."""
+    import torch
+
+    import exact_attention_41_amd as fa
+    from exact_attention_41_amd import workloads as wl
+
+    out = []
+    dev = torch.device("cuda:0")
+    for name in names:
+        w = wl.DECODE_WORKLOADS[name]
+        inp = wl.make_decode_inputs(w.B, w.H, w.Hkv, w.Nq, w.Nk, w.d, w.seed)
+        q, k, v = (wl.to_device(x, "bf16", dev) for x in (inp.q, inp.k, inp.v))
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+        ws = torch.empty(fa.fa_decode_workspace_size(w.B, w.H, w.Hkv, w.Nq, w.Nk, w.d),
+                         dtype=torch.uint8, device=dev)
+        for _ in range(warmup):
+            fa.fa_decode(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, workspace=ws)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
+        for i in range(iters):
+            ev[i].record()
+            fa.fa_decode(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, workspace=ws)
+            ev[i + 1].record()
+        torch.cuda.synchronize(dev)
+        times = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(iters))
+        med = times[len(times) // 2]
+        gbs = w.io_bytes() / (med * 1e-3) / 1e9
+        out.append({"workload": name, "B": w.B, "H": w.H, "Hkv": w.Hkv, "Nq": w.Nq, "Nk": w.Nk,
+                    "d": w.d, "ms": round(med, 4), "bytes": w.io_bytes(),
+                    "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
+                                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                 "frac": round(gbs / HBM_PEAK_GBS, 4)}})
+        log(f"  decode {name}: {med * 1000:.1f} us  {gbs:.0f} GB/s  "
+            f"{100 * gbs / HBM_PEAK_GBS:.1f}% of HBM")
+        del q, k, v, o, lse, ws
+    return out
+
+
 # ---------------------------------------------------------------------------
 def cpu_baseline(w, min_seconds: float = 10.0):
     """The fp64 oracle, as it stands, on the host cores: fwd + bwd per head."""
@@ -368,6 +412,7 @@ def main() -> int:
     bwd_tf = bwd_f / (bwd_ms * 1e-3) / 1e12
     sweep = [] if args.no_sweep else gpu_forward_sweep(SWEEP)
     gqa = [] if args.no_sweep else gpu_gqa_timing(list(wl.GQA_WORKLOADS))
+    decode = [] if args.no_sweep else gpu_decode_timing(list(wl.DECODE_WORKLOADS))
     cpu = None
     if not args.no_cpu and rank == 0:
         log("bench: timing the fp64 oracle on host cores")
@@ -390,6 +435,7 @@ def main() -> int:
         "cpu_baseline": cpu,
         "forward_workloads": sweep,
         "gqa_workloads": gqa,
+        "decode_workloads": decode,
         "kernel_source_sha": kernel_source_sha(),
     }
     if rank == 0:

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libfa.so")
-SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_bwd.hip"]
+SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_bwd.hip", "fa_decode.hip"]
 # Per-source flags. The backward kernels keep their gradient accumulators in
 # AGPRs through inline assembly; every other matrix product there should
 # write VGPRs, where the VALU reads its results, rather than the compiler's

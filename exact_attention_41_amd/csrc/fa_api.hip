@@ -216,4 +216,35 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o,
                       d, causal, scale, stream);
 }
 
+size_t fa_decode_workspace_size(int B, int H, int Hkv, int Nq, int Nk, int d) {
+    if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || (d != 64 && d != 128)) return 0;
+    if (Hkv <= 0 || H % Hkv != 0 || Nq > Nk || (H / Hkv) * Nq > 32) return 0;
+    return fa::decode_workspace_layout(B, Hkv, Nk, d).total;
+}
+
+fa_status_t fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                      void* workspace, size_t workspace_bytes, int B, int H, int Hkv, int Nq,
+                      int Nk, int d, int causal, float scale, hipStream_t stream) {
+    if (B < 0 || H < 0 || Nq < 0 || Nk < 0) return FA_ERR_INVALID_ARG;
+    if (!isfinite(scale) || scale < 0.f) return FA_ERR_INVALID_ARG;
+    FA_TRY(check_heads(H, Hkv));
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (B == 0 || H == 0 || Nq == 0) return FA_OK;
+    if (Nq > Nk) return FA_ERR_INVALID_ARG;
+    if (Nk > kMaxN || (H / Hkv) * Nq > 32) return FA_ERR_UNSUPPORTED;
+    if ((long long)B * H > (1LL << 30) || (long long)B * Hkv > 65535) return FA_ERR_UNSUPPORTED;
+    if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+    FA_TRY(check_tensor(q));
+    FA_TRY(check_tensor(k));
+    FA_TRY(check_tensor(v));
+    FA_TRY(check_tensor(o));
+    FA_TRY(check_lse(lse));
+    if (!workspace || !aligned(workspace, 256) ||
+        workspace_bytes < fa_decode_workspace_size(B, H, Hkv, Nq, Nk, d))
+        return FA_ERR_WORKSPACE;
+    const fa::DecArgs a{q, k, v, o, lse, workspace, B, H, Hkv, Nq, Nk, d, causal != 0, scale,
+                        stream};
+    return fa::launch_decode(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 }  // extern "C"

@@ -60,10 +60,34 @@ struct BwdWorkspace {
 BwdWorkspace bwd_workspace_layout(long long B, long long H, long long Hkv, long long N,
                                   long long d);
 
+// Decoding: Nq query rows per query head (the last Nq positions) against Nk
+// keys; q, o [B][H][Nq][d], k, v [B][Hkv][Nk][d], lse [B][H][Nq].
+struct DecArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    void* workspace;
+    int B, H, Hkv, Nq, Nk, d;
+    bool causal;
+    float scale;
+    hipStream_t stream;
+};
+
+// Decoding workspace: the key ranges and their partial results
+// (fp32 O [B*Hkv][nsplit][32][d], then (m, l) [B*Hkv][nsplit][32][2]).
+struct DecodeWorkspace {
+    int nsplit, split_len;
+    size_t part_o, part_ml, total;
+};
+DecodeWorkspace decode_workspace_layout(long long B, long long Hkv, long long Nk, long long d);
+
 hipError_t launch_fwd_bf16(const FwdArgs& a);
 hipError_t launch_fwd_f32(const FwdArgs& a);
 hipError_t launch_bwd_prepare(const BwdArgs& a);
 hipError_t launch_bwd_dq(const BwdArgs& a);
 hipError_t launch_bwd_dkdv(const BwdArgs& a);
+hipError_t launch_decode(const DecArgs& a);
 
 }  // namespace fa

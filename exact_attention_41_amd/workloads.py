@@ -92,6 +92,55 @@ GQA_WORKLOADS: Dict[str, Workload] = {
 }
 
 
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    """Decoding: Nq query rows per head (the last Nq positions) against Nk keys,
+    K/V shared by groups of H / Hkv query heads."""
+    name: str
+    B: int
+    H: int
+    Hkv: int
+    Nq: int
+    Nk: int
+    d: int
+    causal: bool
+    seed: int
+    description: str = ""
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / math.sqrt(self.d)))
+
+    def kv_bytes(self) -> int:
+        """bf16 K and V, read once: the bulk of the algorithmic traffic."""
+        return 2 * self.B * self.Hkv * self.Nk * self.d * 2
+
+    def io_bytes(self) -> int:
+        """All algorithmic bytes: K, V, q and O (bf16), lse (fp32)."""
+        rows = self.B * self.H * self.Nq
+        return self.kv_bytes() + 2 * rows * self.d * 2 + rows * 4
+
+
+# A decoding step at a 32k-token context: 32 query heads over 8 K/V heads.
+DECODE_WORKLOADS: Dict[str, DecodeWorkload] = {
+    w.name: w
+    for w in [
+        DecodeWorkload("bf16_decode_b8h32kv8q1k32768d128", 8, 32, 8, 1, 32768, 128, False, 7,
+                       "one new token per sequence, 8 sequences of 32768 cached keys"),
+    ]
+}
+
+
+def make_decode_inputs(B: int, H: int, Hkv: int, Nq: int, Nk: int, d: int, seed: int) -> Inputs:
+    """Decoding inputs: q [B,H,Nq,d], then k and v [B,Hkv,Nk,d], drawn in that
+    order with the recipe of the module docstring and rounded to bf16."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = rng.standard_normal((B, H, Nq, d), dtype=np.float32)
+    k = rng.standard_normal((B, Hkv, Nk, d), dtype=np.float32)
+    v = rng.standard_normal((B, Hkv, Nk, d), dtype=np.float32)
+    return Inputs(bf16_round(q), bf16_round(k), bf16_round(v), None, "bf16")
+
+
 def bf16_round(x: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bfloat16 (ties to even).
 

@@ -161,6 +161,32 @@ fa_status_t fa_bwd_gqa(const void* q, const void* k, const void* v, const void* 
                        hipStream_t stream);
 
 /*
+ * Decoding: attention of the last Nq positions of a sequence against all of
+ * its Nk keys (Nq <= Nk), the step an inference system repeats per token,
+ * with the keys split into ranges whose partial results are merged with the
+ * online-softmax statistics (the "FlashAttention" page, section "Online
+ * softmax"; split-K/V decoding is what the inference systems that the
+ * "FlashAttention-2" page lists under "Performance" do).
+ *   q        (in)  bf16 [B][H][Nq][d]; row i is position Nk - Nq + i.
+ *   k, v     (in)  bf16 [B][Hkv][Nk][d]; K/V heads shared as in fa_fwd_gqa.
+ *   o        (out) bf16 [B][H][Nq][d]; lse (out) fp32 [B][H][Nq], as fa_fwd.
+ *   causal   row i keeps keys j <= Nk - Nq + i (bottom-right alignment);
+ *            otherwise every row sees all Nk keys. With Nq == 1 the two agree.
+ *   workspace (scratch) fa_decode_workspace_size(B, H, Hkv, Nq, Nk, d) bytes,
+ *            256-byte aligned.
+ * Limits: (H / Hkv) * Nq <= 32 (the query rows that read one K/V head are
+ * packed into one 32-row block) and d in {64, 128}, else
+ * FA_ERR_UNSUPPORTED; Nq > Nk or Hkv not dividing H -> FA_ERR_INVALID_ARG.
+ * B, H or Nq == 0 is a no-op.
+ */
+size_t fa_decode_workspace_size(int B, int H, int Hkv, int Nq, int Nk, int d);
+
+fa_status_t fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                      void* workspace, size_t workspace_bytes,
+                      int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                      hipStream_t stream);
+
+/*
  * The three phases of fa_bwd, for callers that schedule or time them
  * separately. fa_bwd(...) is exactly fa_bwd_preprocess, fa_bwd_dq and
  * fa_bwd_dkdv, in this order, on one stream; each phase reads what the

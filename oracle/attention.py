@@ -81,9 +81,12 @@ def _softmax_rows(s: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
 
 
 def head_fwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool,
-             scale: float, rows: Optional[np.ndarray] = None
+             scale: float, rows: Optional[np.ndarray] = None, pos0: int = 0
              ) -> Tuple[np.ndarray, np.ndarray]:
-    """Forward for one (b, h) head: q [Nq, d] (rows selected), k, v [Nk, d]."""
+    """Forward for one (b, h) head: q [Nq, d] (rows selected), k, v [Nk, d].
+
+    Query row i sits at sequence position pos0 + i: with ``causal`` it keeps
+    the keys j <= pos0 + i (pos0 = 0: the square, top-left aligned case)."""
     n = q.shape[0]
     if rows is None:
         rows = np.arange(n)
@@ -91,7 +94,7 @@ def head_fwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool,
     lse = np.zeros(len(rows))
     for r0 in range(0, len(rows), ROW_BLOCK):
         rr = rows[r0:r0 + ROW_BLOCK]
-        s = _scores(q[rr], k, rr, causal, scale)
+        s = _scores(q[rr], k, rr + pos0, causal, scale)
         p, ls = _softmax_rows(s)
         o[r0:r0 + len(rr)] = p @ v
         lse[r0:r0 + len(rr)] = ls
@@ -217,6 +220,30 @@ def attention_bwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
         return (dq.reshape(B, H, N, d), dk.reshape(kv_shape).sum(axis=2),
                 dv.reshape(kv_shape).sum(axis=2))
     return dq, dk, dv
+
+
+def decode_fwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool, scale: float,
+               workers: Optional[int] = 1) -> Tuple[np.ndarray, np.ndarray]:
+    """Attention of the last Nq positions of a sequence of Nk >= Nq keys (the
+    decoding step of an inference system): q [B, H, Nq, d], k and v
+    [B, Hkv, Nk, d] (shared heads as for attention_fwd). Query row i sits at
+    position Nk - Nq + i, so with ``causal`` it keeps the keys
+    j <= Nk - Nq + i (bottom-right alignment); without, every key. Returns
+    O [B, H, Nq, d] and lse [B, H, Nq]."""
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if Nq > Nk:
+        raise ValueError("decoding needs Nq <= Nk")
+    G = _group(H, k)
+
+    def one(bh):
+        b, h = bh
+        return head_fwd(q[b, h], k[b, h // G], v[b, h // G], causal, scale, pos0=Nk - Nq)
+
+    res = _pool_map(one, _heads(B, H, None), workers)
+    o = np.stack([r[0] for r in res]).reshape(B, H, Nq, v.shape[-1])
+    lse = np.stack([r[1] for r in res]).reshape(B, H, Nq)
+    return o, lse
 
 
 def online_softmax_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,

@@ -156,6 +156,28 @@ def test_grouped_heads_arguments(lib):
     assert b(ws_bytes=ws - 1) == WORKSPACE
 
 
+def test_decode_arguments(lib):
+    ws = lib.fa_decode_workspace_size(2, 8, 2, 4, 1000, 128)
+    assert ws > 0 and ws % 256 == 0
+    assert lib.fa_decode_workspace_size(2, 8, 2, 5, 4, 128) == 0      # Nq > Nk
+    assert lib.fa_decode_workspace_size(2, 8, 3, 1, 100, 128) == 0     # Hkv does not divide H
+    assert lib.fa_decode_workspace_size(1, 64, 1, 1, 100, 128) == 0    # 64 rows per K/V head
+
+    def dec(B=2, H=8, Hkv=2, Nq=4, Nk=1000, d=128, ws_bytes=ws, o=A, wsp=0x200000, scale=0.1):
+        return lib.fa_decode(A, A, A, o, A, wsp, ws_bytes, B, H, Hkv, Nq, Nk, d, 1, scale, None)
+    assert dec(Hkv=3) == INVALID
+    assert dec(Nq=1001) == INVALID
+    assert dec(scale=float("nan")) == INVALID
+    assert dec(o=None) == INVALID
+    assert dec(d=96) == UNSUPPORTED
+    assert dec(H=64, Hkv=1, Nq=1) == UNSUPPORTED
+    assert dec(o=MIS) == UNSUPPORTED
+    assert dec(wsp=None) == WORKSPACE
+    assert dec(ws_bytes=ws - 1) == WORKSPACE
+    assert dec(B=0, wsp=None, ws_bytes=0) == OK
+    assert dec(Nq=0, wsp=None, ws_bytes=0) == OK
+
+
 def test_python_binding_refuses_without_gpu_tensors():
     torch = pytest.importorskip("torch")
     import exact_attention_41_amd as fa

@@ -386,6 +386,36 @@ def test_group_mapping_is_pinned():
     assert not np.allclose(o[0], o_interleaved)
 
 
+# ------------------------------------------------ decoding (queries at the end)
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Nq,Nk", [(1, 1), (1, 9), (3, 9), (4, 4), (5, 37)])
+def test_decode_equals_last_rows_of_square_problem(causal, Nq, Nk):
+    """Decoding Nq queries against Nk keys equals the last Nq rows of the square
+    problem whose last Nq query rows are those queries (earlier rows arbitrary);
+    the square problem is pinned above."""
+    r = _rng(50 + Nq + Nk)
+    B, H, Hkv, d = 1, 4, 2, 3
+    q = r.standard_normal((B, H, Nq, d))
+    k, v = r.standard_normal((B, Hkv, Nk, d)), r.standard_normal((B, Hkv, Nk, d))
+    full = r.standard_normal((B, H, Nk, d))
+    full[:, :, Nk - Nq:] = q
+    o, lse = ora.decode_fwd(q, k, v, causal, 0.8)
+    fo, fl = ora.attention_fwd(full, k, v, causal, 0.8)
+    np.testing.assert_allclose(o, fo[:, :, Nk - Nq:], atol=1e-13)
+    np.testing.assert_allclose(lse, fl[:, :, Nk - Nq:], atol=1e-13)
+
+
+def test_decode_single_query_sees_every_key():
+    """One query: causal or not, it attends to all Nk keys (scalar brute force)."""
+    r = _rng(56)
+    q, k, v = r.standard_normal((1, 4)), r.standard_normal((11, 4)), r.standard_normal((11, 2))
+    ob, lb = brute.attention(q.tolist(), k.tolist(), v.tolist(), False, 0.6)
+    for causal in (False, True):
+        o, lse = ora.decode_fwd(q[None, None], k[None, None], v[None, None], causal, 0.6)
+        np.testing.assert_allclose(o[0, 0], ob, atol=1e-13)
+        np.testing.assert_allclose(lse[0, 0], lb, atol=1e-13)
+
+
 # ------------------------------------------------------ planted-mistake checks
 def _brute_mismatch():
     r = _rng(16)
