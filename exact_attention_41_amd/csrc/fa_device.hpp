@@ -205,12 +205,13 @@ __device__ __forceinline__ uint32_t stage_src_offset(int b, int lane) {
 }
 
 // Stage blocks b = first, first + stride, ... (< 64 * D * 2 / 1024) of the
-// tile starting at row row0 of `src` (a [N][D] bf16 array).
+// tile starting at row row0 of `src` (a [N][D] bf16 array); rows at or past N
+// (all of them when row0 >= N) read as zeros.
 template <int D, int COUNT, int STRIDE, bool VTYPE>
 __device__ __forceinline__ void stage_tile_lds(const uint16_t* __restrict__ src, lds_char* tile,
                                                int row0, int N, int first, int lane) {
 #if defined(__HIP_DEVICE_COMPILE__)   // buffer resources exist only in the device pass
-    const int rows = min(64, N - row0);
+    const int rows = max(0, min(64, N - row0));   // a tile past N reads nothing
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(src + (size_t)row0 * D), (short)0, rows * D * 2, kBufferFlags);
 #pragma unroll
