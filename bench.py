@@ -13,7 +13,8 @@ Prints exactly one JSON line (on rank 0). Options:
   --steps K       timed steps (default 20)
   --warmup W      untimed warm-up steps (default 5)
   --no-sweep      skip the forward-only timing of the other workloads, the
-                  shared-K/V-head (grouped-query) workload and decoding
+                  shared-K/V-head (grouped-query) workload, decoding and the
+                  chunked-prefill (Nq != Nk) forward
   --no-cpu        skip the CPU oracle baseline
   --counters      instead: run two steps and a plain 512 MiB device copy and
                   exit (the program to run under rocprofv3 --pmc FETCH_SIZE,
@@ -261,6 +262,41 @@ def gpu_gqa_timing(names, iters=10, warmup=3):
     return out
 
 
+def gpu_rect_timing(names, iters=10, warmup=3):
+    """Forward with Nq query rows against Nk keys (fa_fwd_rect), median of
+    ``iters`` calls; flops counted over the unmasked score elements."""
+    import torch
+
+    import exact_attention_41_amd as fa
+    from exact_attention_41_amd import workloads as wl
+
+    out = []
+    dev = torch.device("cuda:0")
+    for name in names:
+        w = wl.RECT_WORKLOADS[name]
+        inp = wl.make_decode_inputs(w.B, w.H, w.Hkv, w.Nq, w.Nk, w.d, w.seed)
+        q, k, v = (wl.to_device(x, "bf16", dev) for x in (inp.q, inp.k, inp.v))
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+        for _ in range(warmup):
+            fa.fa_fwd_rect(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
+        for i in range(iters):
+            ev[i].record()
+            fa.fa_fwd_rect(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+            ev[i + 1].record()
+        torch.cuda.synchronize(dev)
+        times = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(iters))
+        med = times[len(times) // 2]
+        tf = wl.rect_flops(w) / (med * 1e-3) / 1e12
+        out.append({"workload": name, "Nq": w.Nq, "Nk": w.Nk, "H": w.H, "Hkv": w.Hkv,
+                    "ms": round(med, 4), "tflops": round(tf, 1),
+                    "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
+        log(f"  rect {name}: {med:.3f} ms  {tf:.1f} TFLOP/s  {100 * tf / PEAK_BF16_TFLOPS:.1f}%")
+        del q, k, v, o, lse
+    return out
+
+
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 
 
@@ -413,6 +449,7 @@ def main() -> int:
     sweep = [] if args.no_sweep else gpu_forward_sweep(SWEEP)
     gqa = [] if args.no_sweep else gpu_gqa_timing(list(wl.GQA_WORKLOADS))
     decode = [] if args.no_sweep else gpu_decode_timing(list(wl.DECODE_WORKLOADS))
+    rect = [] if args.no_sweep else gpu_rect_timing(list(wl.RECT_WORKLOADS))
     cpu = None
     if not args.no_cpu and rank == 0:
         log("bench: timing the fp64 oracle on host cores")
@@ -436,6 +473,7 @@ def main() -> int:
         "forward_workloads": sweep,
         "gqa_workloads": gqa,
         "decode_workloads": decode,
+        "rect_workloads": rect,
         "kernel_source_sha": kernel_source_sha(),
     }
     if rank == 0:

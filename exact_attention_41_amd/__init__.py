@@ -11,6 +11,7 @@ If the library is not built, every call raises: there is no fallback.
     o, lse = fa_fwd_gqa(q, k, v, causal=True)              # k, v: [B,Hkv,N,d]
     dq, dk, dv = fa_bwd_gqa(q, k, v, o, do, lse, causal=True)
     o, lse = fa_decode(q, k, v)          # q [B,H,Nq,d], k, v [B,Hkv,Nk,d]
+    o, lse = fa_fwd_rect(q, k, v, causal=True)   # any Nq, Nk; bottom-right causal
 """
 from __future__ import annotations
 
@@ -21,8 +22,8 @@ from . import _lib
 
 __all__ = ["fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_bwd_workspace_size", "fa_status_str",
            "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_gqa", "fa_bwd_gqa",
-           "fa_bwd_gqa_workspace_size", "fa_decode", "fa_decode_workspace_size", "FAError",
-           "library_path"]
+           "fa_bwd_gqa_workspace_size", "fa_decode", "fa_decode_workspace_size", "fa_fwd_rect",
+           "FAError", "library_path"]
 
 
 class FAError(RuntimeError):
@@ -282,4 +283,34 @@ def fa_decode(q, k, v, causal: bool = False, scale: Optional[float] = None, out=
                                    _stream_ptr(q.device))
     if st != _lib.FA_OK:
         raise FAError(st, "fa_decode")
+    return out, lse
+
+
+def fa_fwd_rect(q, k, v, causal: bool = False, scale: Optional[float] = None, out=None,
+                lse=None):
+    """bf16 forward with Nq query rows against Nk keys: q [B,H,Nq,d], k and v
+    [B,Hkv,Nk,d] (Hkv dividing H). Query row i sits at position Nk - Nq + i
+    (bottom-right causal alignment). Returns (O [B,H,Nq,d], lse [B,H,Nq]).
+    Calls fa_fwd_rect of libfa.so."""
+    torch = _torch()
+    bf = torch.bfloat16
+    _check(q, "q", bf)
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, H, Nq, d] and k, v [B, Hkv, Nk, d]")
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    _check(k, "k", bf, (B, Hkv, Nk, d), q.device)
+    _check(v, "v", bf, (B, Hkv, Nk, d), q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    _check(out, "out", bf, q.shape, q.device)
+    _check(lse, "lse", torch.float32, (B, H, Nq), q.device)
+    with torch.cuda.device(q.device):
+        st = _lib.load().fa_fwd_rect(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                     lse.data_ptr(), B, H, Hkv, Nq, Nk, d, int(bool(causal)),
+                                     _scale(scale, d), _stream_ptr(q.device))
+    if st != _lib.FA_OK:
+        raise FAError(st, "fa_fwd_rect")
     return out, lse

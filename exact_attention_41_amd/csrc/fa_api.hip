@@ -84,15 +84,24 @@ const char* fa_status_str(fa_status_t status) {
     return "FA_ERR_UNKNOWN";
 }
 
+fa_status_t fa_fwd_rect(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                        hipStream_t stream) {
+    bool empty = false;
+    if (Nk < 0) return FA_ERR_INVALID_ARG;
+    FA_TRY(check_fwd(q, k, v, o, lse, B, H, Nq, d, scale, &empty));
+    FA_TRY(check_heads(H, Hkv));
+    if (empty) return FA_OK;
+    if (Nk == 0) return FA_ERR_INVALID_ARG;      // query rows but no keys
+    if (Nk > kMaxN) return FA_ERR_UNSUPPORTED;
+    fa::FwdArgs a{q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, causal != 0, scale, stream};
+    return fa::launch_fwd_bf16(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 fa_status_t fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
                        int B, int H, int Hkv, int N, int d, int causal, float scale,
                        hipStream_t stream) {
-    bool empty = false;
-    FA_TRY(check_fwd(q, k, v, o, lse, B, H, N, d, scale, &empty));
-    FA_TRY(check_heads(H, Hkv));
-    if (empty) return FA_OK;
-    fa::FwdArgs a{q, k, v, o, lse, B, H, Hkv, N, d, causal != 0, scale, stream};
-    return fa::launch_fwd_bf16(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+    return fa_fwd_rect(q, k, v, o, lse, B, H, Hkv, N, N, d, causal, scale, stream);
 }
 
 fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -105,7 +114,7 @@ fa_status_t fa_fwd_f32(const float* q, const float* k, const float* v, float* o,
     bool empty = false;
     FA_TRY(check_fwd(q, k, v, o, lse, B, H, N, d, scale, &empty));
     if (empty) return FA_OK;
-    fa::FwdArgs a{q, k, v, o, lse, B, H, H, N, d, causal != 0, scale, stream};
+    fa::FwdArgs a{q, k, v, o, lse, B, H, H, N, N, d, causal != 0, scale, stream};
     return fa::launch_fwd_f32(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

@@ -65,7 +65,7 @@ template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(kFwdWaves * 64, 1)
 fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
-                float* __restrict__ LSE, int BH, int G, int N, float c, int nqb) {
+                float* __restrict__ LSE, int BH, int G, int N, int Nk, float c, int nqb) {
     constexpr int BC = 64;                 // keys per tile
     constexpr int BR = kFwdWaves * 32;     // query rows per workgroup
     constexpr int KS = D / 16;             // MFMA k-steps over d
@@ -95,13 +95,16 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const int qb = CAUSAL ? (nqb - 1 - qb_rank) : qb_rank;
 
     const size_t head = (size_t)bh * (size_t)N * D;
-    const size_t kvhead = (size_t)(bh / G) * (size_t)N * D;   // K/V head of this query head
+    const size_t kvhead = (size_t)(bh / G) * (size_t)Nk * D;  // K/V head of this query head
     const uint16_t* Qh = Q + head;
     const uint16_t* Kh = K + kvhead;
     const uint16_t* Vh = V + kvhead;
     const int q0 = qb * BR;
     const int wq0 = q0 + wave * 32;
     const int qi = wq0 + l32;              // this lane's query row
+    // Query row i sits at position i + off: with the causal mask it keeps the
+    // keys j <= i + off (off = 0 for the square problem).
+    const int off = Nk - N;
 
     // Q^T operand fragments, resident for the whole kernel. Rows past the end
     // read row N-1 (finite data, never stored).
@@ -113,9 +116,9 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             qf[s] = *(const u32x4_t*)(Qh + (size_t)qr * D + 16 * s + 8 * g);
     }
 
-    const int n_all = (N + BC - 1) / BC;
-    const int q_last = min(q0 + BR, N) - 1;
-    const int n_tiles = CAUSAL ? min(n_all, q_last / BC + 1) : n_all;
+    const int n_all = (Nk + BC - 1) / BC;
+    const int q_last = min(q0 + BR, N) - 1 + off;       // last position of the block
+    const int n_tiles = CAUSAL ? min(n_all, max(q_last, 0) / BC + 1) : n_all;
 
     // Buffer i of K / V (selects, not an array: LDS addresses stay scalar).
     auto Kb = [&](int i) { return i ? (lds_char*)kb1 : (lds_char*)kb0; };
@@ -154,7 +157,7 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             const int ch = u % DCH, rg = u / DCH;
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
-                const int j = min(t * BC + 4 * rg + rr, N - 1);
+                const int j = min(t * BC + 4 * rg + rr, Nk - 1);
                 vreg[k][rr] = *(const u32x4_t*)(Vh + (size_t)j * D + ch * 8);
             }
         }
@@ -227,14 +230,14 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     // Vector slot of tile t: softmax of S(t) into P(t).
     auto vector_slot = [&](int t) {
         const int kv0 = t * BC;
-        const bool need_mask = (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > q0);
+        const bool need_mask = (kv0 + BC > Nk) || (CAUSAL && kv0 + BC - 1 > q0 + off);
         if (need_mask) {
 #pragma unroll
             for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int j = kv0 + 32 * jb + 8 * (r >> 2) + 4 * g + (r & 3);
-                    if ((j >= N) || (CAUSAL && j > qi)) acc_s[jb][r] = kNegInf;
+                    if ((j >= Nk) || (CAUSAL && j > qi + off)) acc_s[jb][r] = kNegInf;
                 }
         }
         float m = fmaxf(acc_s[0][0], acc_s[0][1]);
@@ -277,7 +280,7 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     };
 
     // ---- prologue: K(0) into LDS, zeros into the V buffer of "tile -1" -----
-    if (grp == 0) stage_tile_lds<D, BLOCKS / 4, 4, false>(Kh, Kb(0), 0, N, wave, lane);
+    if (grp == 0) stage_tile_lds<D, BLOCKS / 4, 4, false>(Kh, Kb(0), 0, Nk, wave, lane);
     for (int i = tid; i < TILE / 16; i += kFwdWaves * 64)
         *(__attribute__((address_space(3))) u32x4_t*)(Vb(1) + 16 * i) = u32x4_t{0u, 0u, 0u, 0u};
     wait_vmem();
@@ -298,7 +301,7 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         if (t < n_tiles) {
             if (grp == 0) {
                 if (t + 1 < n_tiles)
-                    stage_tile_lds<D, BLOCKS / 4, 4, false>(Kh, Kb((t + 1) & 1), (t + 1) * BC, N,
+                    stage_tile_lds<D, BLOCKS / 4, 4, false>(Kh, Kb((t + 1) & 1), (t + 1) * BC, Nk,
                                                             wave, lane);
                 v_load(t);
             } else if (t + 1 < n_tiles) {
@@ -448,8 +451,8 @@ static hipError_t launch_fwd_bf16_t(const FwdArgs& a) {
     const float c = a.scale * kLog2e;
     hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3(nqb * BH), dim3(kFwdWaves * 64), 0,
                        a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                       (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, BH, a.H / a.Hkv, a.N, c,
-                       nqb);
+                       (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, BH, a.H / a.Hkv, a.N, a.Nk,
+                       c, nqb);
     return hipGetLastError();
 }
 

@@ -8,14 +8,16 @@
 namespace fa {
 
 // H query heads; K/V have Hkv heads (Hkv divides H), query head h using K/V
-// head h / (H / Hkv). Hkv == H is ordinary multi-head attention.
+// head h / (H / Hkv). Hkv == H is ordinary multi-head attention. N query rows
+// per head, Nk keys; query row i sits at position Nk - N + i (Nk == N: the
+// square case).
 struct FwdArgs {
     const void* q;
     const void* k;
     const void* v;
     void* o;
     float* lse;
-    int B, H, Hkv, N, d;
+    int B, H, Hkv, N, Nk, d;
     bool causal;
     float scale;
     hipStream_t stream;

@@ -131,6 +131,28 @@ DECODE_WORKLOADS: Dict[str, DecodeWorkload] = {
 }
 
 
+# A chunk of new queries against a longer cached key sequence (chunked prefill).
+RECT_WORKLOADS: Dict[str, DecodeWorkload] = {
+    w.name: w
+    for w in [
+        DecodeWorkload("bf16_prefill_b1h32kv8q4096k16384d128_causal", 1, 32, 8, 4096, 16384, 128,
+                       True, 8, "4096 new tokens after 12288 cached ones, bottom-right causal"),
+    ]
+}
+
+
+def rect_flops(w: DecodeWorkload) -> float:
+    """Counted forward flops: 4*d per unmasked score element (query row i at
+    position Nk - Nq + i keeps min(Nk, Nk - Nq + i + 1) keys when causal)."""
+    off = w.Nk - w.Nq
+    if w.causal:
+        i = np.arange(w.Nq, dtype=np.float64)
+        elems = float(np.clip(off + i + 1, 0, w.Nk).sum())
+    else:
+        elems = float(w.Nq) * w.Nk
+    return 4.0 * w.d * w.B * w.H * elems
+
+
 def make_decode_inputs(B: int, H: int, Hkv: int, Nq: int, Nk: int, d: int, seed: int) -> Inputs:
     """Decoding inputs: q [B,H,Nq,d], then k and v [B,Hkv,Nk,d], drawn in that
     order with the recipe of the module docstring and rounded to bf16."""

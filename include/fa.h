@@ -98,6 +98,22 @@ fa_status_t fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, flo
                        hipStream_t stream);
 
 /*
+ * Forward with Nq query rows and Nk keys per head (a rectangular score
+ * matrix: a chunk of new queries against a longer key sequence, or the
+ * reverse). Query row i sits at sequence position Nk - Nq + i, so with
+ * causal set it keeps the keys j <= Nk - Nq + i (bottom-right alignment; if
+ * Nq > Nk the first Nq - Nk rows keep no key and get O = 0, lse = -inf).
+ *   q, o     bf16 [B][H][Nq][d], lse fp32 [B][H][Nq].
+ *   k, v     bf16 [B][Hkv][Nk][d], K/V heads shared as in fa_fwd_gqa.
+ * Nq == Nk is fa_fwd_gqa. Nk < 0, or Nk == 0 with query rows to compute ->
+ * FA_ERR_INVALID_ARG; Nk beyond 2^26 -> FA_ERR_UNSUPPORTED. Everything else
+ * as for fa_fwd.
+ */
+fa_status_t fa_fwd_rect(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                        hipStream_t stream);
+
+/*
  * Forward, fp32 storage and fp32 arithmetic throughout (no reduced-precision
  * operands). Same layout, masking, outputs and errors as fa_fwd.
  */

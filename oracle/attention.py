@@ -222,6 +222,33 @@ def attention_bwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
     return dq, dk, dv
 
 
+def rect_fwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool, scale: float,
+             heads: Optional[Sequence[Tuple[int, int]]] = None,
+             workers: Optional[int] = 1) -> Tuple[np.ndarray, np.ndarray]:
+    """Attention of Nq query rows against Nk keys, the queries being the last
+    Nq positions: q [B, H, Nq, d], k and v [B, Hkv, Nk, d] (shared heads as for
+    attention_fwd). Query row i sits at position Nk - Nq + i, so with
+    ``causal`` it keeps the keys j <= Nk - Nq + i (bottom-right alignment;
+    when Nq > Nk the first Nq - Nk rows keep none: O = 0, lse = -inf); without,
+    every key. Returns O [B, H, Nq, d] and lse [B, H, Nq] (with ``heads``: the
+    listed query heads, stacked)."""
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    G = _group(H, k)
+    hs = _heads(B, H, heads)
+
+    def one(bh):
+        b, h = bh
+        return head_fwd(q[b, h], k[b, h // G], v[b, h // G], causal, scale, pos0=Nk - Nq)
+
+    res = _pool_map(one, hs, workers)
+    o = np.stack([r[0] for r in res])
+    lse = np.stack([r[1] for r in res])
+    if heads is None:
+        return o.reshape(B, H, Nq, v.shape[-1]), lse.reshape(B, H, Nq)
+    return o, lse
+
+
 def decode_fwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool, scale: float,
                workers: Optional[int] = 1) -> Tuple[np.ndarray, np.ndarray]:
     """Attention of the last Nq positions of a sequence of Nk >= Nq keys (the

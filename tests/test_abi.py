@@ -178,6 +178,19 @@ def test_decode_arguments(lib):
     assert dec(Nq=0, wsp=None, ws_bytes=0) == OK
 
 
+def test_rect_forward_arguments(lib):
+    def f(B=1, H=2, Hkv=1, Nq=100, Nk=300, d=128, q=A, scale=0.1):
+        return lib.fa_fwd_rect(q, A, A, A, A, B, H, Hkv, Nq, Nk, d, 1, scale, None)
+    assert f(Nk=-1) == INVALID
+    assert f(Nk=0) == INVALID
+    assert f(Hkv=3) == INVALID
+    assert f(q=None) == INVALID
+    assert f(d=256 + 32) == UNSUPPORTED
+    assert f(Nk=(1 << 26) + 1) == UNSUPPORTED
+    assert f(Nq=0, Nk=0, q=None) == OK          # nothing to compute
+    assert f(B=0) == OK
+
+
 def test_python_binding_refuses_without_gpu_tensors():
     torch = pytest.importorskip("torch")
     import exact_attention_41_amd as fa

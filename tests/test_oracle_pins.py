@@ -416,6 +416,38 @@ def test_decode_single_query_sees_every_key():
         np.testing.assert_allclose(lse[0, 0], lb, atol=1e-13)
 
 
+# ----------------------------------------- rectangular score matrices (Nq != Nk)
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Nq,Nk", [(3, 9), (9, 3), (1, 4), (4, 1), (7, 7)])
+def test_rect_against_square_problem(causal, Nq, Nk):
+    """Nq <= Nk: the last Nq rows of the square problem whose last query rows
+    are these. Nq > Nk: with the mask the first Nq - Nk rows see no key (O = 0,
+    lse = -inf) and the rest are the square problem of size Nk; without it
+    every row is the square problem's row with the same keys (brute force)."""
+    r = _rng(70 + 10 * Nq + Nk)
+    B, H, Hkv, d = 1, 2, 1, 3
+    q = r.standard_normal((B, H, Nq, d))
+    k, v = r.standard_normal((B, Hkv, Nk, d)), r.standard_normal((B, Hkv, Nk, d))
+    o, lse = ora.rect_fwd(q, k, v, causal, 0.7)
+    if Nq <= Nk:
+        full = r.standard_normal((B, H, Nk, d))
+        full[:, :, Nk - Nq:] = q
+        fo, fl = ora.attention_fwd(full, k, v, causal, 0.7)
+        np.testing.assert_allclose(o, fo[:, :, Nk - Nq:], atol=1e-13)
+        np.testing.assert_allclose(lse, fl[:, :, Nk - Nq:], atol=1e-13)
+    elif causal:
+        np.testing.assert_array_equal(o[:, :, :Nq - Nk], 0.0)
+        assert np.all(np.isneginf(lse[:, :, :Nq - Nk]))
+        fo, fl = ora.attention_fwd(q[:, :, Nq - Nk:], k, v, True, 0.7)
+        np.testing.assert_allclose(o[:, :, Nq - Nk:], fo, atol=1e-13)
+        np.testing.assert_allclose(lse[:, :, Nq - Nk:], fl, atol=1e-13)
+    else:
+        for h in range(H):
+            ob, lb = brute.attention(q[0, h].tolist(), k[0, 0].tolist(), v[0, 0].tolist(), False, 0.7)
+            np.testing.assert_allclose(o[0, h], ob, atol=1e-13)
+            np.testing.assert_allclose(lse[0, h], lb, atol=1e-13)
+
+
 # ------------------------------------------------------ planted-mistake checks
 def _brute_mismatch():
     r = _rng(16)
