@@ -12,9 +12,10 @@ Prints exactly one JSON line (on rank 0). Options:
   --gpus N        only N=1 is meaningful: this path runs on one GPU
   --steps K       timed steps (default 20)
   --warmup W      untimed warm-up steps (default 5)
-  --no-sweep      skip the forward-only timing of the other workloads, the
-                  shared-K/V-head (grouped-query) workload, decoding and the
-                  chunked-prefill (Nq != Nk) forward
+  --no-sweep      skip the forward-only timing of the other workloads (head
+                  sizes 64, 128 and 256), the shared-K/V-head (grouped-query)
+                  workload, decoding and the chunked-prefill (Nq != Nk)
+                  forward
   --no-cpu        skip the CPU oracle baseline
   --counters      instead: run two steps and a plain 512 MiB device copy and
                   exit (the program to run under rocprofv3 --pmc FETCH_SIZE,
@@ -43,7 +44,8 @@ PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
 HEADLINE = "bf16_b4h16n4096d128_causal_bwd"
 SWEEP = ["bf16_b8h16n2048d64", "bf16_b8h16n2048d64_causal", "bf16_b2h32n8192d128_causal_x3",
          "bf16_b1h16n16384d128_causal", "bf16_b4h16n4096d128_causal_bwd"]
-KERNEL_SOURCES = ["fa_device.hpp", "fa_kernels.hpp", "fa_fwd.hip", "fa_bwd.hip"]
+KERNEL_SOURCES = ["fa_device.hpp", "fa_kernels.hpp", "fa_fwd.hip", "fa_fwd256.hip", "fa_bwd.hip",
+                  "fa_decode.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 COPY_BYTES = 512 << 20          # the calibration copy reads and writes this much
 # Kernel-name fragments -> the step's kernel names.
@@ -124,7 +126,7 @@ def gpu_forward_sweep(names, iters=10, warmup=3):
     out = []
     dev = torch.device("cuda:0")
     for name in names:
-        w = wl.WORKLOADS[name]
+        w = wl.WORKLOADS[name] if name in wl.WORKLOADS else wl.WIDE_WORKLOADS[name]
         inp = wl.make_inputs(w.B, w.H, w.N, w.d, "bf16", w.seed, w.qk_mult)
         q, k, v = (wl.to_device(x, "bf16", dev) for x in (inp.q, inp.k, inp.v))
         o = torch.empty_like(q)
@@ -447,6 +449,7 @@ def main() -> int:
     bwd_ms = per_kernel["bwd_preprocess"] + per_kernel["bwd_dkdv"] + per_kernel["bwd_dq"]
     bwd_tf = bwd_f / (bwd_ms * 1e-3) / 1e12
     sweep = [] if args.no_sweep else gpu_forward_sweep(SWEEP)
+    wide = [] if args.no_sweep else gpu_forward_sweep(list(wl.WIDE_WORKLOADS))
     gqa = [] if args.no_sweep else gpu_gqa_timing(list(wl.GQA_WORKLOADS))
     decode = [] if args.no_sweep else gpu_decode_timing(list(wl.DECODE_WORKLOADS))
     rect = [] if args.no_sweep else gpu_rect_timing(list(wl.RECT_WORKLOADS))
@@ -471,6 +474,7 @@ def main() -> int:
         "roofline": roofline,
         "cpu_baseline": cpu,
         "forward_workloads": sweep,
+        "wide_workloads": wide,
         "gqa_workloads": gqa,
         "decode_workloads": decode,
         "rect_workloads": rect,

@@ -16,15 +16,16 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libfa.so")
-SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_bwd.hip", "fa_decode.hip"]
-# Per-source flags. The backward kernels keep their gradient accumulators in
-# AGPRs through inline assembly; every other matrix product there should
-# write VGPRs, where the VALU reads its results, rather than the compiler's
-# AGPR form for kernels that own a whole SIMD. Their per-tile software
-# pipeline is one fully unrolled loop, larger than the default size limit
-# for an unroll pragma.
-SOURCE_FLAGS = {"fa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1",
-                               "-mllvm", "-pragma-unroll-threshold=100000"]}
+SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_fwd256.hip", "fa_bwd.hip", "fa_decode.hip"]
+# Per-source flags. The backward kernels and the d = 256 forward keep their
+# accumulators in AGPRs through inline assembly; every other matrix product
+# there should write VGPRs, where the VALU reads its results, rather than the
+# compiler's AGPR form for kernels that own a whole SIMD. Their per-tile
+# software pipeline is one fully unrolled loop, larger than the default size
+# limit for an unroll pragma.
+_ONE_WAVE_PER_SIMD = ["-mllvm", "-amdgpu-mfma-vgpr-form=1",
+                      "-mllvm", "-pragma-unroll-threshold=100000"]
+SOURCE_FLAGS = {"fa_bwd.hip": _ONE_WAVE_PER_SIMD, "fa_fwd256.hip": _ONE_WAVE_PER_SIMD}
 ARCH = "gfx950"
 
 

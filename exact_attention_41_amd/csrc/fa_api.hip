@@ -15,11 +15,15 @@ constexpr int kMaxN = 1 << 26;
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
+// Head sizes with kernels: 64 and 128 everywhere, 256 for the bf16 forward
+// and decoding.
+bool head_dim_ok(int d, bool wide) { return d == 64 || d == 128 || (wide && d == 256); }
+
 // Shared size/scale checks. Returns FA_OK and sets *empty when B*H*N == 0.
-fa_status_t check_common(int B, int H, int N, int d, float scale, bool* empty) {
+fa_status_t check_common(int B, int H, int N, int d, float scale, bool wide, bool* empty) {
     if (B < 0 || H < 0 || N < 0) return FA_ERR_INVALID_ARG;
     if (!isfinite(scale) || scale < 0.f) return FA_ERR_INVALID_ARG;
-    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (!head_dim_ok(d, wide)) return FA_ERR_UNSUPPORTED;
     *empty = (B == 0 || H == 0 || N == 0);
     if (*empty) return FA_OK;
     if (N > kMaxN) return FA_ERR_UNSUPPORTED;
@@ -56,8 +60,9 @@ fa_status_t check_lse(const void* p) {
     } while (0)
 
 fa_status_t check_fwd(const void* q, const void* k, const void* v, const void* o,
-                      const void* lse, int B, int H, int N, int d, float scale, bool* empty) {
-    FA_TRY(check_common(B, H, N, d, scale, empty));
+                      const void* lse, int B, int H, int N, int d, float scale, bool wide,
+                      bool* empty) {
+    FA_TRY(check_common(B, H, N, d, scale, wide, empty));
     if (*empty) return FA_OK;
     // Null pointers are argument errors, checked before alignment.
     if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
@@ -89,7 +94,7 @@ fa_status_t fa_fwd_rect(const void* q, const void* k, const void* v, void* o, fl
                         hipStream_t stream) {
     bool empty = false;
     if (Nk < 0) return FA_ERR_INVALID_ARG;
-    FA_TRY(check_fwd(q, k, v, o, lse, B, H, Nq, d, scale, &empty));
+    FA_TRY(check_fwd(q, k, v, o, lse, B, H, Nq, d, scale, true, &empty));
     FA_TRY(check_heads(H, Hkv));
     if (empty) return FA_OK;
     if (Nk == 0) return FA_ERR_INVALID_ARG;      // query rows but no keys
@@ -112,14 +117,14 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
 fa_status_t fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                        int B, int H, int N, int d, int causal, float scale, hipStream_t stream) {
     bool empty = false;
-    FA_TRY(check_fwd(q, k, v, o, lse, B, H, N, d, scale, &empty));
+    FA_TRY(check_fwd(q, k, v, o, lse, B, H, N, d, scale, false, &empty));
     if (empty) return FA_OK;
     fa::FwdArgs a{q, k, v, o, lse, B, H, H, N, N, d, causal != 0, scale, stream};
     return fa::launch_fwd_f32(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 size_t fa_bwd_gqa_workspace_size(int B, int H, int Hkv, int N, int d) {
-    if (B <= 0 || H <= 0 || N <= 0 || (d != 64 && d != 128)) return 0;
+    if (B <= 0 || H <= 0 || N <= 0 || !head_dim_ok(d, false)) return 0;
     if (Hkv <= 0 || H % Hkv != 0) return 0;
     return fa::bwd_workspace_layout(B, H, Hkv, N, d).total;
 }
@@ -138,7 +143,7 @@ namespace {
 fa_status_t check_bwd(std::initializer_list<const void*> tensors, bool need_lse, const void* lse,
                       const void* workspace, size_t workspace_bytes, int B, int H, int Hkv,
                       int N, int d, float scale, bool* empty) {
-    FA_TRY(check_common(B, H, N, d, scale, empty));
+    FA_TRY(check_common(B, H, N, d, scale, false, empty));
     FA_TRY(check_heads(H, Hkv));
     if (*empty) return FA_OK;
     for (const void* p : tensors)
@@ -226,7 +231,7 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o,
 }
 
 size_t fa_decode_workspace_size(int B, int H, int Hkv, int Nq, int Nk, int d) {
-    if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || (d != 64 && d != 128)) return 0;
+    if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || !head_dim_ok(d, true)) return 0;
     if (Hkv <= 0 || H % Hkv != 0 || Nq > Nk || (H / Hkv) * Nq > 32) return 0;
     return fa::decode_workspace_layout(B, Hkv, Nk, d).total;
 }
@@ -237,7 +242,7 @@ fa_status_t fa_decode(const void* q, const void* k, const void* v, void* o, floa
     if (B < 0 || H < 0 || Nq < 0 || Nk < 0) return FA_ERR_INVALID_ARG;
     if (!isfinite(scale) || scale < 0.f) return FA_ERR_INVALID_ARG;
     FA_TRY(check_heads(H, Hkv));
-    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (!head_dim_ok(d, true)) return FA_ERR_UNSUPPORTED;
     if (B == 0 || H == 0 || Nq == 0) return FA_OK;
     if (Nq > Nk) return FA_ERR_INVALID_ARG;
     if (Nk > kMaxN || (H / Hkv) * Nq > 32) return FA_ERR_UNSUPPORTED;

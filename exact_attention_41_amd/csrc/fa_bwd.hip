@@ -29,7 +29,7 @@
 // bf16 (8-bit), against the fp16 images: this keeps dQ, dK and dV within
 // 1e-2 of the exact gradients where bf16 operands do not.
 //
-// Every tile reaches LDS by direct buffer-to-LDS loads (row-major bf16 tiles
+// Every tile reaches LDS by direct global-to-LDS loads (row-major bf16 tiles
 // from the inputs, with the chunk swizzle applied through the source
 // addresses; transposed tiles as straight copies of their images), issued a
 // tile ahead into the second of two buffers; no tile passes through VGPRs.
@@ -311,19 +311,18 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
     // Key tile t into buffer buf: K and V rows (bf16, swizzled) and the
     // (sK K)^T image, BLK 1 KB blocks each, spread over the NW waves; part k
-    // of NPART is one block of this wave. Past the last tile nothing is read
-    // (the idle buffer is zero-filled).
+    // of NPART is one block of this wave. Past the last tile the buffer is
+    // filled from a valid tile and never read.
     constexpr int PPT = BLK / NW;            // blocks per wave and tensor
     constexpr int NPART = 3 * PPT;
     auto stage_part = [&](int t, int buf, int k) {
         lds_char* base = (lds_char*)(smem + buf * BUF);
         const int tensor = k / PPT, b = wave + NW * (k % PPT);
-        const bool live = t < n_tiles;
         if (tensor < 2)
             stage_tile_block<D>(tensor == 0 ? Kh : Vh, base + (tensor == 0 ? OFF_K : OFF_V),
-                                t * BC, live ? min(BC, N - t * BC) : 0, b, lane);
+                                t * BC, N, b, lane);
         else
-            stage_image_block(kt_h + (size_t)t * TB, live ? TB : 0, base + OFF_KT, b, lane);
+            stage_image_block(kt_h + (size_t)min(t, T - 1) * TB, TB, base + OFF_KT, b, lane);
     };
 
     // Lane-dependent LDS bases of buffer 0: pb[k], k < 8, for the row-major
@@ -546,7 +545,8 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     // Q and dO rows (bf16, swizzled) and the two transposed fp16 images, BLK
     // 1 KB blocks each spread over the NW waves (part k of NPART is one block
     // of this wave), and the tile's 128 statistics (wave 0). Past the last
-    // tile of the last member nothing is read.
+    // tile of the last member the buffer is filled from a valid tile and
+    // never read.
     constexpr int PPT = BLK / NW;
     constexpr int NPART = 4 * PPT;
     auto stage_part = [&](int gq, int t, int buf, int k) {
@@ -554,20 +554,20 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         const int tensor = k / PPT, b = wave + NW * (k % PPT);
         const bool live = gq < G && t < n_tiles;
         const size_t qh = (size_t)(qh0 + (live ? gq : 0));
+        const size_t ti = (size_t)(live ? t : 0);
         if (tensor < 2)
             stage_tile_block<D>((tensor == 0 ? Q : dO) + qh * N * D,
-                                base + (tensor == 0 ? OFF_Q : OFF_DO), t * BQ,
-                                live ? min(BQ, N - t * BQ) : 0, b, lane);
+                                base + (tensor == 0 ? OFF_Q : OFF_DO), (int)ti * BQ, N, b, lane);
         else
-            stage_image_block((tensor == 2 ? qt_img : ot_img) + (qh * T + t) * TB,
-                              live ? TB : 0, base + (tensor == 2 ? OFF_QT : OFF_DOT), b, lane);
+            stage_image_block((tensor == 2 ? qt_img : ot_img) + (qh * T + ti) * TB, TB,
+                              base + (tensor == 2 ? OFF_QT : OFF_DOT), b, lane);
     };
     auto stage_stats = [&](int gq, int t, int buf) {
         lds_char* base = (lds_char*)(smem + buf * BUF);
         const bool live = gq < G && t < n_tiles;
         const size_t qh = (size_t)(qh0 + (live ? gq : 0));
-        if (wave == 0) stage_image_block(stats + (qh * T + t) * 128, live ? 512 : 0,
-                                         base + OFF_ST, 0, lane);
+        const size_t ti = (size_t)(live ? t : 0);
+        if (wave == 0) stage_image_block(stats + (qh * T + ti) * 128, 512, base + OFF_ST, 0, lane);
     };
 
     // Lane-dependent LDS bases of buffer 0: pb[k], k < 8, for the row-major

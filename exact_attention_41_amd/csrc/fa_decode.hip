@@ -14,7 +14,7 @@
 // head, packed into one 32-row block: G * Nq <= 32). It walks the range in
 // 32-key tiles, loading tile t+1 while it computes tile t: K straight from
 // global memory into the registers of the MFMA A operand (its fragments are
-// row-major 16-byte chunks), V by buffer-to-LDS loads into the wave's own two
+// row-major 16-byte chunks), V by global-to-LDS loads into the wave's own two
 // 8 KiB buffers (row-major, V-type swizzle). It computes S^T = K Q^T on bf16
 // MFMA, the masked online softmax in fp32 and O^T += V^T P^T with V^T read
 // by transposing LDS reads, and writes (m, l, O) of its range's real query
@@ -54,8 +54,10 @@ DecodeWorkspace decode_workspace_layout(long long B, long long Hkv, long long Nk
     return w;
 }
 
+// Two workgroups per compute unit for d <= 128; at d = 256 the V buffers
+// (128 KiB per workgroup) and the 128-register output block allow one.
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(kDecWaves * 64, 2)
+__global__ void __launch_bounds__(kDecWaves * 64, D > 128 ? 1 : 2)
 decode_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                     const uint16_t* __restrict__ V, float* __restrict__ part_o,
                     float* __restrict__ part_ml, int G, int Nq, int Nk, int L, int nsplit,
@@ -105,7 +107,7 @@ decode_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
 
     const int k_begin = sp * L, k_end = min(k_begin + L, Nk);
     // Tile at key j0: V rows into an LDS buffer (rows at or past the range end
-    // read as zeros), then K fragments of rows j0 + l32 (clamped into the
+    // read the range's last row; they are masked), then K fragments of rows j0 + l32 (clamped into the
     // array; rows at or past the range end are masked) into registers.
     auto issue = [&](int j0, lds_char* vb, u32x4_t (&kf)[KS]) {
         stage_tile_lds<D, BLK, 1, true>(Vh, vb, j0, k_end, 0, lane);
@@ -252,8 +254,13 @@ decode_merge_kernel(const float* __restrict__ part_o, const float* __restrict__ 
             x[e] = (so[0][col] + so[1][col] + so[2][col] + so[3][col]) * inv;
         }
         uint16_t* orow = O + (size_t)R * D;
-        if (PER == 2) *(uint32_t*)(orow + 2 * lane) = pack_bf16x2(x[0], x[PER - 1]);
-        else orow[lane] = (uint16_t)(pack_bf16x2(x[0], 0.f) & 0xffffu);
+        if constexpr (PER == 1) {
+            orow[lane] = (uint16_t)(pack_bf16x2(x[0], 0.f) & 0xffffu);
+        } else {
+#pragma unroll
+            for (int e = 0; e < PER; e += 2)
+                *(uint32_t*)(orow + PER * lane + e) = pack_bf16x2(x[e], x[e + 1]);
+        }
         if (lane == 0) LSE[R] = (lt > 0.f) ? (m + fast_log2(lt)) * kLn2 : kNegInf;
     }
 }
@@ -278,6 +285,7 @@ static hipError_t launch_decode_t(const DecArgs& a) {
 }
 
 hipError_t launch_decode(const DecArgs& a) {
+    if (a.d == 256) return a.causal ? launch_decode_t<256, true>(a) : launch_decode_t<256, false>(a);
     if (a.d == 128) return a.causal ? launch_decode_t<128, true>(a) : launch_decode_t<128, false>(a);
     return a.causal ? launch_decode_t<64, true>(a) : launch_decode_t<64, false>(a);
 }

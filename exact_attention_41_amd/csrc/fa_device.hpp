@@ -21,6 +21,13 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_huge_valf();
 
+// Rescale threshold of the forward's online softmax, in log2 units: the
+// reference maximum of a row is moved only when a tile's maximum exceeds it
+// by more than this, so probabilities stay below 2^8 and the output
+// accumulator is rescaled rarely. The result is the same function (every
+// term and the normaliser carry the same factor); only the rounding differs.
+constexpr float kRescaleLog2 = 8.f;
+
 // D(32x32,f32) += A(32x16,bf16) * B(16x32,bf16).
 // Operand layout used throughout: lane l supplies row (A) / column (B)
 // l % 32 and eight consecutive-in-register values of the contraction index
@@ -60,6 +67,12 @@ typedef __attribute__((address_space(3))) f32x4_t lds_f32x4_t;
 // hardware. Read the accumulator only after agpr_settle().
 __device__ __forceinline__ void mfma_f16_agpr(f32x16_t& acc, const u32x4_t& a, const u32x4_t& b) {
     asm("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// bf16 product accumulated in place into an accumulator held in AGPRs, both
+// operands in VGPRs (otherwise as mfma_f16_agpr).
+__device__ __forceinline__ void mfma_bf16_agpr(f32x16_t& acc, const u32x4_t& a, const u32x4_t& b) {
+    asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
 // bf16 product into a VGPR accumulator with the B operand held in AGPRs (a
@@ -142,12 +155,13 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 // 16-byte-chunk XOR swizzle for a row-major [rows][D] bf16 tile in LDS.
-// D = 128: rows are 256 B (16 chunks); D = 64: rows are 128 B (8 chunks).
-// Sixteen consecutive rows reading the same logical chunk land on distinct
-// 16-byte bank groups (and so do eight).
+// D = 128 or 256: rows are 256 or 512 B (16 or 32 chunks), and the low four
+// bits of the chunk index are XORed with the row; D = 64: rows are 128 B
+// (8 chunks). Sixteen consecutive rows reading the same logical chunk land on
+// distinct 16-byte bank groups (and so do eight).
 template <int D>
 __device__ __forceinline__ int row_chunk_swizzle(int row) {
-    if constexpr (D == 128) return row & 15;
+    if constexpr (D >= 128) return row & 15;
     else return (row ^ (row >> 3)) & 7;
 }
 
@@ -175,99 +189,72 @@ __device__ __forceinline__ int tr_slot_offset(int n, int slot) {
 }
 
 // ---------------------------------------------------------------------------
-// Direct global -> LDS staging (buffer_load_dwordx4 ... lds) of a [64][D]
-// bf16 tile into a row-major LDS tile with XOR-swizzled 16-byte chunks. Each
-// wave instruction fills 1 KB of LDS contiguously, lane l writing bytes
-// [16l, 16l+16); the swizzle is applied by choosing which global chunk each
-// lane fetches. The buffer resource covers only the rows of the tile that
-// exist, so rows at or past N read as zeros.
+// Direct global -> LDS staging (global_load_lds_dwordx4) of a [64][D] bf16
+// tile into a row-major LDS tile with XOR-swizzled 16-byte chunks. Each wave
+// instruction fills 1 KB of LDS contiguously, lane l writing bytes
+// [16l, 16l+16); the source is a per-lane address, so the swizzle is applied
+// by choosing which global chunk each lane fetches. Rows at or past N read
+// row N - 1 (N >= 1): finite data in rows that every caller masks. The
+// compiler does not order these copies against LDS reads: wait on vmcnt (a
+// barrier does) before reading what they wrote.
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((ext_vector_type(4))) short i16x4_t;
 
-constexpr int kBufferFlags = 0x00020000;   // raw buffer, 32-bit data format
+// 16 bytes per lane from global address base + voff (base wave-uniform, so
+// the copy takes the scalar-base + 32-bit-offset form) into LDS bytes
+// [16 l, 16 l + 16) after the wave-uniform address `dst`.
+__device__ __forceinline__ void lds_dma16(const void* base, uint32_t voff, lds_char* dst) {
+    __builtin_amdgcn_global_load_lds(
+        (const __attribute__((address_space(1))) void*)((const char*)base + voff),
+        (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+}
 
 // K-type tiles: chunk c of row r is stored at chunk c ^ row_chunk_swizzle(r).
 // V-type tiles: chunk c of row r is stored at chunk c ^ (2 * (r & 3)), which
 // makes the transposed 8-byte reads below conflict-free.
 __device__ __forceinline__ int v_chunk_swizzle(int row) { return (row & 3) << 1; }
 
-// Byte offset, inside the global tile, of the chunk that lane `lane` of the
-// wave filling 1 KB block `b` must fetch.
+// 1 KB block b of the [64][D] tile at row row0 of `src` ([N][D] bf16, N >= 1)
+// into LDS: lane `lane` fetches the chunk whose swizzled place is bytes
+// [16 lane, 16 lane + 16) of the block. Rows past N read row N - 1; a tile
+// wholly past N reads row N - 1 throughout.
 template <int D, bool VTYPE>
-__device__ __forceinline__ uint32_t stage_src_offset(int b, int lane) {
+__device__ __forceinline__ void stage_block(const uint16_t* __restrict__ src, lds_char* tile,
+                                            int row0, int N, int b, int lane) {
     constexpr int DCH = D / 8;
     constexpr int RPK = 1024 / (2 * D);        // rows per 1 KB block
-    const int row = b * RPK + lane / DCH;
+    const int row = b * RPK + lane / DCH;      // row within the tile
     const int phys = lane % DCH;
     const int logical = phys ^ (VTYPE ? v_chunk_swizzle(row) : row_chunk_swizzle<D>(row));
-    return (uint32_t)(row * D + logical * 8) * 2u;
+    const int rb = min(row0, N - 1);           // uniform
+    const uint32_t voff = (uint32_t)(min(row, N - 1 - rb) * (2 * D) + logical * 16);
+    lds_dma16(src + (size_t)rb * D, voff, tile + b * 1024);
 }
 
-// Stage blocks b = first, first + stride, ... (< 64 * D * 2 / 1024) of the
-// tile starting at row row0 of `src` (a [N][D] bf16 array); rows at or past N
-// (all of them when row0 >= N) read as zeros.
+// Stage blocks b = first, first + STRIDE, ... (< 64 * D * 2 / 1024) of the
+// tile starting at row row0 of `src` (a [N][D] bf16 array).
 template <int D, int COUNT, int STRIDE, bool VTYPE>
 __device__ __forceinline__ void stage_tile_lds(const uint16_t* __restrict__ src, lds_char* tile,
                                                int row0, int N, int first, int lane) {
-#if defined(__HIP_DEVICE_COMPILE__)   // buffer resources exist only in the device pass
-    const int rows = max(0, min(64, N - row0));   // a tile past N reads nothing
-    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(src + (size_t)row0 * D), (short)0, rows * D * 2, kBufferFlags);
 #pragma unroll
-    for (int k = 0; k < COUNT; ++k) {
-        const int b = first + STRIDE * k;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rsrc, (__attribute__((address_space(3))) void*)(tile + b * 1024), 16,
-            stage_src_offset<D, VTYPE>(b, lane), 0, 0, 0);
-    }
-#endif
+    for (int k = 0; k < COUNT; ++k) stage_block<D, VTYPE>(src, tile, row0, N, first + STRIDE * k, lane);
 }
 
-// Stage 1 KB blocks b = first, first + STRIDE, ... of a tile image that is
-// already laid out as the LDS tile (a byte-for-byte copy of `bytes` bytes at
-// `src`); bytes past `bytes` read as zeros.
-template <int COUNT, int STRIDE>
-__device__ __forceinline__ void stage_image_lds(const void* src, int bytes, lds_char* tile,
-                                                int first, int lane) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    const __amdgpu_buffer_rsrc_t rsrc =
-        __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, bytes, kBufferFlags);
-#pragma unroll
-    for (int k = 0; k < COUNT; ++k) {
-        const int b = first + STRIDE * k;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rsrc, (__attribute__((address_space(3))) void*)(tile + b * 1024), 16,
-            (uint32_t)(b * 1024 + lane * 16), 0, 0, 0);
-    }
-#endif
-}
-
-// Single-block forms of the two staging helpers above, for spreading a
-// tile's loads over a longer stretch of other work: 1 KB block b of a
-// K-type tile with `rows` valid rows (rows <= 0: nothing is read and the
-// block is zero-filled), or of an image of `bytes` bytes.
+// Single-block forms, for spreading a tile's loads over a longer stretch of
+// other work: 1 KB block b of a K-type tile, or of a tile image that is
+// already laid out as the LDS tile (a byte-for-byte copy of the `bytes`
+// bytes at `src`, a multiple of 16; lanes past them re-read its last chunk
+// and fill LDS that no one reads).
 template <int D>
 __device__ __forceinline__ void stage_tile_block(const uint16_t* __restrict__ src, lds_char* tile,
-                                                 int row0, int rows, int b, int lane) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(src + (size_t)row0 * D), (short)0, max(rows, 0) * D * 2, kBufferFlags);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rsrc, (__attribute__((address_space(3))) void*)(tile + b * 1024), 16,
-        stage_src_offset<D, false>(b, lane), 0, 0, 0);
-#endif
+                                                 int row0, int N, int b, int lane) {
+    stage_block<D, false>(src, tile, row0, N, b, lane);
 }
 
 __device__ __forceinline__ void stage_image_block(const void* src, int bytes, lds_char* tile,
                                                   int b, int lane) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    const __amdgpu_buffer_rsrc_t rsrc =
-        __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, bytes, kBufferFlags);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rsrc, (__attribute__((address_space(3))) void*)(tile + b * 1024), 16,
-        (uint32_t)(b * 1024 + lane * 16), 0, 0, 0);
-#endif
+    lds_dma16(src, (uint32_t)min(b * 1024 + lane * 16, bytes - 16), tile + b * 1024);
 }
 
 // 16-byte A/B fragment of a K-type tile: row `row`, logical chunk `ch`.

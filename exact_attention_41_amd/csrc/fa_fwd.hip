@@ -45,12 +45,6 @@ namespace fa {
 // vector slot it writes V(t) to LDS, and both are first read in slot 2t+2.
 // ---------------------------------------------------------------------------
 
-// Rescale threshold of the online softmax, in log2 units: the reference
-// maximum of a row is moved only when a tile's maximum exceeds it by more than
-// this, so probabilities stay below 2^8 and the accumulator is rescaled rarely.
-// The result is the same function (every term and the normaliser carry the
-// same factor); only the rounding differs.
-constexpr float kRescaleLog2 = 8.f;
 constexpr int kFwdWaves = 8;
 
 __device__ __forceinline__ void wg_barrier() {
@@ -137,7 +131,7 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4) pf[t4] = u32x4_t{0u, 0u, 0u, 0u};
 
-    // K(t+1) goes straight into LDS (group A, buffer_load ... lds). V(t) goes
+    // K(t+1) goes straight into LDS (group A, global_load_lds). V(t) goes
     // through registers into a transposed layout ([d][64 keys], the permuted
     // key order of fa_device.hpp) so the matrix slot reads V^T fragments with
     // plain 16-byte LDS reads: each group moves half of the 4-key x 8-column
@@ -457,6 +451,7 @@ static hipError_t launch_fwd_bf16_t(const FwdArgs& a) {
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a) {
+    if (a.d == 256) return launch_fwd_d256(a);
     if (a.d == 128) return a.causal ? launch_fwd_bf16_t<128, true>(a) : launch_fwd_bf16_t<128, false>(a);
     return a.causal ? launch_fwd_bf16_t<64, true>(a) : launch_fwd_bf16_t<64, false>(a);
 }

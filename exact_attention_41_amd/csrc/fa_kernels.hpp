@@ -86,6 +86,7 @@ struct DecodeWorkspace {
 DecodeWorkspace decode_workspace_layout(long long B, long long Hkv, long long Nk, long long d);
 
 hipError_t launch_fwd_bf16(const FwdArgs& a);
+hipError_t launch_fwd_d256(const FwdArgs& a);   // bf16, d = 256 (one wave per SIMD)
 hipError_t launch_fwd_f32(const FwdArgs& a);
 hipError_t launch_bwd_prepare(const BwdArgs& a);
 hipError_t launch_bwd_dq(const BwdArgs& a);

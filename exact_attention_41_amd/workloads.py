@@ -92,6 +92,20 @@ GQA_WORKLOADS: Dict[str, Workload] = {
 }
 
 
+# Head size 256 (the largest the FlashAttention-2 page names), forward only:
+# 16384 tokens per batch as in that page's benchmark, 8 heads of 256 = 2048
+# model width; both masks on the same tensors.
+WIDE_WORKLOADS: Dict[str, Workload] = {
+    w.name: w
+    for w in [
+        Workload("bf16_b4h8n4096d256", 4, 8, 4096, 256, "bf16", False, 9,
+                 description="non-causal bf16 forward, head size 256"),
+        Workload("bf16_b4h8n4096d256_causal", 4, 8, 4096, 256, "bf16", True, 9,
+                 description="causal bf16 forward, head size 256, same tensors"),
+    ]
+}
+
+
 @dataclasses.dataclass(frozen=True)
 class DecodeWorkload:
     """Decoding: Nq query rows per head (the last Nq positions) against Nk keys,
@@ -127,6 +141,8 @@ DECODE_WORKLOADS: Dict[str, DecodeWorkload] = {
     for w in [
         DecodeWorkload("bf16_decode_b8h32kv8q1k32768d128", 8, 32, 8, 1, 32768, 128, False, 7,
                        "one new token per sequence, 8 sequences of 32768 cached keys"),
+        DecodeWorkload("bf16_decode_b8h16kv4q1k32768d256", 8, 16, 4, 1, 32768, 256, False, 10,
+                       "head size 256: 16 query heads over 4 K/V heads, 32768 cached keys"),
     ]
 }
 

@@ -27,7 +27,11 @@
  *   Scale      any finite scale >= 0 (1/sqrt(d) for the standard attention).
  *   Sizes      B, H, N >= 0; if any of them is 0 the call does nothing and
  *              returns FA_OK. N may be any positive value (no multiple of a
- *              tile size is required). d must be 64 or 128.
+ *              tile size is required). d must be 64 or 128; the bf16
+ *              forward entry points (fa_fwd, fa_fwd_gqa, fa_fwd_rect) and
+ *              fa_decode also take d = 256, the largest head size the
+ *              "FlashAttention-2" page (systems-analysis.info, section
+ *              "Performance") names for FlashAttention-2.
  *   Async      work is enqueued on `stream` (0 = the null stream) and the call
  *              returns; results are valid once the stream has synchronised.
  *   Errors     every argument is checked before anything is enqueued, so on
@@ -35,7 +39,7 @@
  *                FA_ERR_INVALID_ARG  null pointer with non-empty sizes,
  *                                    negative size, non-finite or negative
  *                                    scale;
- *                FA_ERR_UNSUPPORTED  d not 64/128, misaligned pointer, or a
+ *                FA_ERR_UNSUPPORTED  d not supported, misaligned pointer, or a
  *                                    size whose index arithmetic would
  *                                    overflow (grid or N beyond 2^26);
  *                FA_ERR_WORKSPACE    backward workspace too small, null or not
@@ -191,7 +195,7 @@ fa_status_t fa_bwd_gqa(const void* q, const void* k, const void* v, const void* 
  *   workspace (scratch) fa_decode_workspace_size(B, H, Hkv, Nq, Nk, d) bytes,
  *            256-byte aligned.
  * Limits: (H / Hkv) * Nq <= 32 (the query rows that read one K/V head are
- * packed into one 32-row block) and d in {64, 128}, else
+ * packed into one 32-row block) and d in {64, 128, 256}, else
  * FA_ERR_UNSUPPORTED; Nq > Nk or Hkv not dividing H -> FA_ERR_INVALID_ARG.
  * B, H or Nq == 0 is a no-op.
  */

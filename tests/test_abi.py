@@ -89,7 +89,9 @@ def test_forward_rejects_bad_arguments(lib, entry):
     assert fwd(lib, entry, scale=float("inf")) == INVALID
     assert fwd(lib, entry, scale=-0.5) == INVALID
     assert fwd(lib, entry, d=96) == UNSUPPORTED
-    assert fwd(lib, entry, d=256) == UNSUPPORTED
+    assert fwd(lib, entry, d=512) == UNSUPPORTED
+    if entry == "fa_fwd_f32":
+        assert fwd(lib, entry, d=256) == UNSUPPORTED     # d = 256: bf16 forward only
     assert fwd(lib, entry, q=MIS) == UNSUPPORTED
     assert fwd(lib, entry, o=MIS) == UNSUPPORTED
     assert fwd(lib, entry, lse=A + 2) == UNSUPPORTED
@@ -139,6 +141,7 @@ def test_grouped_heads_arguments(lib):
     assert lib.fa_fwd_gqa(A, A, A, A, A, 1, 4, 2, 64, 96, 0, 0.125, None) == UNSUPPORTED
     assert lib.fa_fwd_gqa(A, A, A, A, A, 0, 4, 2, 64, 64, 0, 0.125, None) == OK
     assert lib.fa_bwd_gqa_workspace_size(2, 32, 8, 4096, 128) > 0
+    assert lib.fa_bwd_gqa_workspace_size(2, 32, 8, 4096, 256) == 0     # no d = 256 backward
     assert lib.fa_bwd_gqa_workspace_size(2, 32, 5, 4096, 128) == 0
     assert lib.fa_bwd_gqa_workspace_size(2, 32, 0, 4096, 128) == 0
     assert lib.fa_bwd_gqa_workspace_size(4, 16, 16, 4096, 128) == \
@@ -162,6 +165,8 @@ def test_decode_arguments(lib):
     assert lib.fa_decode_workspace_size(2, 8, 2, 5, 4, 128) == 0      # Nq > Nk
     assert lib.fa_decode_workspace_size(2, 8, 3, 1, 100, 128) == 0     # Hkv does not divide H
     assert lib.fa_decode_workspace_size(1, 64, 1, 1, 100, 128) == 0    # 64 rows per K/V head
+    assert lib.fa_decode_workspace_size(2, 8, 2, 4, 1000, 256) > ws      # d = 256 is supported
+    assert lib.fa_decode_workspace_size(2, 8, 2, 4, 1000, 512) == 0
 
     def dec(B=2, H=8, Hkv=2, Nq=4, Nk=1000, d=128, ws_bytes=ws, o=A, wsp=0x200000, scale=0.1):
         return lib.fa_decode(A, A, A, o, A, wsp, ws_bytes, B, H, Hkv, Nq, Nk, d, 1, scale, None)
