@@ -14,8 +14,8 @@ Prints exactly one JSON line (on rank 0). Options:
   --warmup W      untimed warm-up steps (default 5)
   --no-sweep      skip the forward-only timing of the other workloads (head
                   sizes 64, 128 and 256), the shared-K/V-head (grouped-query)
-                  workload, decoding and the chunked-prefill (Nq != Nk)
-                  forward
+                  workload, decoding, the chunked-prefill (Nq != Nk) forward
+                  and the e4m3 (fp8) forward
   --no-cpu        skip the CPU oracle baseline
   --counters      instead: run two steps and a plain 512 MiB device copy and
                   exit (the program to run under rocprofv3 --pmc FETCH_SIZE,
@@ -299,6 +299,50 @@ def gpu_rect_timing(names, iters=10, warmup=3):
     return out
 
 
+PEAK_FP8_TFLOPS = 2 * PEAK_BF16_TFLOPS    # dense e4m3 MFMA (AMD's 5.0 PFLOP/s)
+
+
+def gpu_fp8_timing(names, iters=10, warmup=3):
+    """Forward with e4m3 operands (fa_fwd_fp8), median of ``iters`` calls;
+    flops counted as for the bf16 forward, against the fp8 MFMA peak."""
+    import torch
+
+    import exact_attention_41_amd as fa
+    from exact_attention_41_amd import workloads as wl
+
+    out = []
+    dev = torch.device("cuda:0")
+    for name in names:
+        w = wl.FP8_WORKLOADS[name]
+        inp = wl.make_fp8_inputs(w.B, w.H, w.H, w.N, w.N, w.d, w.seed)
+        q, k, v = (wl.fp8_to_device(x, dev) for x in (inp.q8, inp.k8, inp.v8))
+        o = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+
+        def call():
+            fa.fa_fwd_fp8(q, k, v, inp.dq, inp.dk, inp.dv, causal=w.causal, scale=w.scale,
+                          out=o, lse=lse)
+
+        for _ in range(warmup):
+            call()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
+        for i in range(iters):
+            ev[i].record()
+            call()
+            ev[i + 1].record()
+        torch.cuda.synchronize(dev)
+        times = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(iters))
+        med = times[len(times) // 2]
+        tf = w.fwd_flops() / (med * 1e-3) / 1e12
+        out.append({"workload": name, "pass": "fwd", "dtype": "e4m3", "ms": round(med, 4),
+                    "tflops": round(tf, 1), "peak": round(PEAK_FP8_TFLOPS, 1),
+                    "frac_peak": round(tf / PEAK_FP8_TFLOPS, 4)})
+        log(f"  fp8 {name}: {med:.3f} ms  {tf:.1f} TFLOP/s  {100 * tf / PEAK_FP8_TFLOPS:.1f}% "
+            "of the fp8 peak")
+        del q, k, v, o, lse
+    return out
+
+
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 
 
@@ -453,6 +497,7 @@ def main() -> int:
     gqa = [] if args.no_sweep else gpu_gqa_timing(list(wl.GQA_WORKLOADS))
     decode = [] if args.no_sweep else gpu_decode_timing(list(wl.DECODE_WORKLOADS))
     rect = [] if args.no_sweep else gpu_rect_timing(list(wl.RECT_WORKLOADS))
+    fp8 = [] if args.no_sweep else gpu_fp8_timing(list(wl.FP8_WORKLOADS))
     cpu = None
     if not args.no_cpu and rank == 0:
         log("bench: timing the fp64 oracle on host cores")
@@ -478,6 +523,7 @@ def main() -> int:
         "gqa_workloads": gqa,
         "decode_workloads": decode,
         "rect_workloads": rect,
+        "fp8_workloads": fp8,
         "kernel_source_sha": kernel_source_sha(),
     }
     if rank == 0:

@@ -12,6 +12,7 @@ If the library is not built, every call raises: there is no fallback.
     dq, dk, dv = fa_bwd_gqa(q, k, v, o, do, lse, causal=True)
     o, lse = fa_decode(q, k, v)          # q [B,H,Nq,d], k, v [B,Hkv,Nk,d]
     o, lse = fa_fwd_rect(q, k, v, causal=True)   # any Nq, Nk; bottom-right causal
+    o, lse = fa_fwd_fp8(q8, k8, v8, dq, dk, dv)  # e4m3 inputs with per-tensor factors
 """
 from __future__ import annotations
 
@@ -23,7 +24,7 @@ from . import _lib
 __all__ = ["fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_bwd_workspace_size", "fa_status_str",
            "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_gqa", "fa_bwd_gqa",
            "fa_bwd_gqa_workspace_size", "fa_decode", "fa_decode_workspace_size", "fa_fwd_rect",
-           "FAError", "library_path"]
+           "fa_fwd_fp8", "FAError", "library_path"]
 
 
 class FAError(RuntimeError):
@@ -313,4 +314,37 @@ def fa_fwd_rect(q, k, v, causal: bool = False, scale: Optional[float] = None, ou
                                      _scale(scale, d), _stream_ptr(q.device))
     if st != _lib.FA_OK:
         raise FAError(st, "fa_fwd_rect")
+    return out, lse
+
+
+def fa_fwd_fp8(q, k, v, descale_q: float = 1.0, descale_k: float = 1.0, descale_v: float = 1.0,
+               causal: bool = False, scale: Optional[float] = None, out=None, lse=None):
+    """Forward with e4m3 operands: q [B,H,Nq,d], k and v [B,Hkv,Nk,d] as
+    torch.float8_e4m3fn (or their uint8 bytes), the real values being
+    descale_x times the stored ones; d = 128. Rows aligned as in fa_fwd_rect.
+    Returns (O [B,H,Nq,d] bf16, lse [B,H,Nq] fp32). Calls fa_fwd_fp8 of
+    libfa.so."""
+    torch = _torch()
+    f8 = torch.float8_e4m3fn
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, H, Nq, d] and k, v [B, Hkv, Nk, d]")
+    dt = q.dtype if q.dtype in (f8, torch.uint8) else f8
+    _check(q, "q", dt)
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    _check(k, "k", dt, (B, Hkv, Nk, d), q.device)
+    _check(v, "v", dt, (B, Hkv, Nk, d), q.device)
+    if out is None:
+        out = torch.empty((B, H, Nq, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    _check(out, "out", torch.bfloat16, (B, H, Nq, d), q.device)
+    _check(lse, "lse", torch.float32, (B, H, Nq), q.device)
+    with torch.cuda.device(q.device):
+        st = _lib.load().fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                    lse.data_ptr(), B, H, Hkv, Nq, Nk, d, int(bool(causal)),
+                                    _scale(scale, d), float(descale_q), float(descale_k),
+                                    float(descale_v), _stream_ptr(q.device))
+    if st != _lib.FA_OK:
+        raise FAError(st, "fa_fwd_fp8")
     return out, lse

@@ -103,6 +103,24 @@ fa_status_t fa_fwd_rect(const void* q, const void* k, const void* v, void* o, fl
     return fa::launch_fwd_bf16(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+fa_status_t fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                       float descale_q, float descale_k, float descale_v, hipStream_t stream) {
+    bool empty = false;
+    if (Nk < 0) return FA_ERR_INVALID_ARG;
+    for (float x : {descale_q, descale_k, descale_v})
+        if (!isfinite(x) || !(x > 0.f)) return FA_ERR_INVALID_ARG;
+    FA_TRY(check_fwd(q, k, v, o, lse, B, H, Nq, d, scale, false, &empty));
+    FA_TRY(check_heads(H, Hkv));
+    if (d != 128) return FA_ERR_UNSUPPORTED;
+    if (empty) return FA_OK;
+    if (Nk == 0) return FA_ERR_INVALID_ARG;
+    if (Nk > kMaxN) return FA_ERR_UNSUPPORTED;
+    fa::FwdArgs a{q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, causal != 0, scale, stream,
+                  descale_q, descale_k, descale_v};
+    return fa::launch_fwd_fp8(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 fa_status_t fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
                        int B, int H, int Hkv, int N, int d, int causal, float scale,
                        hipStream_t stream) {

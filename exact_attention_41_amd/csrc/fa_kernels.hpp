@@ -21,6 +21,8 @@ struct FwdArgs {
     bool causal;
     float scale;
     hipStream_t stream;
+    // fp8 forward only: the real values are descale_x times the stored ones.
+    float descale_q = 1.f, descale_k = 1.f, descale_v = 1.f;
 };
 
 struct BwdArgs {
@@ -87,6 +89,7 @@ DecodeWorkspace decode_workspace_layout(long long B, long long Hkv, long long Nk
 
 hipError_t launch_fwd_bf16(const FwdArgs& a);
 hipError_t launch_fwd_d256(const FwdArgs& a);   // bf16, d = 256 (one wave per SIMD)
+hipError_t launch_fwd_fp8(const FwdArgs& a);    // fp8 e4m3 q, k, v; d = 128
 hipError_t launch_fwd_f32(const FwdArgs& a);
 hipError_t launch_bwd_prepare(const BwdArgs& a);
 hipError_t launch_bwd_dq(const BwdArgs& a);

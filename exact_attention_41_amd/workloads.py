@@ -11,7 +11,10 @@ Recipe (the same for every workload):
     q, k, v, then dO, each of shape [B, H, N, d] (row-major; k and v have
     [B, Hkv, N, d] when Hkv K/V heads are shared by the H query heads);
   * an optional fp32 multiplier on q and k (the sharpened-softmax workload);
-  * one round-to-nearest-even cast to bfloat16 (except fp32 workloads).
+  * one round-to-nearest-even cast to bfloat16 (except fp32 workloads);
+  * fp8 workloads instead divide each tensor by its own factor
+    fp32(max|x| / 448) and cast it to OCP e4m3 (round to nearest even); the
+    real inputs are factor * e4m3 value.
 
 The attention problem is the scaled dot-product attention of the
 "FlashAttention" page (systems-analysis.ru), section "Problem of standard
@@ -21,7 +24,7 @@ from __future__ import annotations
 
 import dataclasses
 import math
-from typing import Dict, Optional
+from typing import Dict, Optional, Tuple
 
 import numpy as np
 
@@ -102,6 +105,21 @@ WIDE_WORKLOADS: Dict[str, Workload] = {
                  description="non-causal bf16 forward, head size 256"),
         Workload("bf16_b4h8n4096d256_causal", 4, 8, 4096, 256, "bf16", True, 9,
                  description="causal bf16 forward, head size 256, same tensors"),
+    ]
+}
+
+
+# 8-bit floating-point forward (e4m3 q, k, v with one factor per tensor):
+# the headline shape, both masks on the same tensors, and a long sequence.
+FP8_WORKLOADS: Dict[str, Workload] = {
+    w.name: w
+    for w in [
+        Workload("fp8_b4h16n4096d128", 4, 16, 4096, 128, "fp8", False, 11,
+                 description="non-causal fp8 forward, e4m3 q, k, v, per-tensor factors"),
+        Workload("fp8_b4h16n4096d128_causal", 4, 16, 4096, 128, "fp8", True, 11,
+                 description="causal fp8 forward, same tensors"),
+        Workload("fp8_b1h16n16384d128_causal", 1, 16, 16384, 128, "fp8", True, 12,
+                 description="long-sequence causal fp8 forward"),
     ]
 }
 
@@ -251,3 +269,68 @@ def to_device(x: np.ndarray, dtype: str, device="cuda"):
     else:
         t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
     return t.to(device)
+
+
+# ---------------------------------------------------------------- fp8 inputs
+E4M3_MAX = 448.0     # largest finite OCP e4m3 value
+
+
+def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """float32 values with |x| <= 448 -> OCP e4m3 bytes, round to nearest even
+    (torch's float8_e4m3fn cast on the CPU)."""
+    import torch
+    x = np.asarray(x, dtype=np.float32)
+    if np.any(np.abs(x) > E4M3_MAX):
+        raise ValueError("e4m3_encode: values beyond 448")
+    return torch.from_numpy(np.ascontiguousarray(x)).to(torch.float8_e4m3fn).view(
+        torch.uint8).numpy()
+
+
+def e4m3_decode(b: np.ndarray) -> np.ndarray:
+    """OCP e4m3 bytes -> exact values as float64 (NaN for the two NaN codes)."""
+    import torch
+    b = np.ascontiguousarray(np.asarray(b, dtype=np.uint8))
+    return torch.from_numpy(b).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+@dataclasses.dataclass
+class Fp8Inputs:
+    """e4m3 bytes of q, k, v and their dequantisation factors (fp32): the
+    real inputs are descale * e4m3 value."""
+    q8: np.ndarray
+    k8: np.ndarray
+    v8: np.ndarray
+    dq: float
+    dk: float
+    dv: float
+
+    def as_float64(self):
+        """The real (dequantised) inputs, exact in float64."""
+        return (e4m3_decode(self.q8) * self.dq, e4m3_decode(self.k8) * self.dk,
+                e4m3_decode(self.v8) * self.dv)
+
+
+def quantize_e4m3(x: np.ndarray) -> Tuple[np.ndarray, float]:
+    """Per-tensor factor s = fp32(max|x| / 448) and the bytes of e4m3(x / s)."""
+    amax = float(np.max(np.abs(x)))
+    s = float(np.float32(amax / E4M3_MAX)) if amax > 0 else 1.0
+    y = np.clip(x.astype(np.float32) / np.float32(s), -E4M3_MAX, E4M3_MAX)
+    return e4m3_encode(y), s
+
+
+def make_fp8_inputs(B: int, H: int, Hkv: int, Nq: int, Nk: int, d: int, seed: int,
+                    qk_mult: float = 1.0) -> Fp8Inputs:
+    """q [B,H,Nq,d], then k and v [B,Hkv,Nk,d], drawn as standard normals in
+    that order (recipe of the module docstring; q and k multiplied by qk_mult)
+    and quantised per tensor with quantize_e4m3."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = rng.standard_normal((B, H, Nq, d), dtype=np.float32) * np.float32(qk_mult)
+    k = rng.standard_normal((B, Hkv, Nk, d), dtype=np.float32) * np.float32(qk_mult)
+    v = rng.standard_normal((B, Hkv, Nk, d), dtype=np.float32)
+    (q8, dq), (k8, dk), (v8, dv) = quantize_e4m3(q), quantize_e4m3(k), quantize_e4m3(v)
+    return Fp8Inputs(q8, k8, v8, dq, dk, dv)
+
+
+def fp8_to_device(b: np.ndarray, device="cuda"):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(b)).to(device).view(torch.float8_e4m3fn)

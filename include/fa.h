@@ -118,6 +118,30 @@ fa_status_t fa_fwd_rect(const void* q, const void* k, const void* v, void* o, fl
                         hipStream_t stream);
 
 /*
+ * Forward with 8-bit floating-point operands (the FP8 arithmetic the
+ * "FlashAttention" page, section "FlashAttention-2 (2023)", and the
+ * "FlashAttention-2" page, section "Performance", attribute to
+ * FlashAttention-3).
+ *   q        (in)  e4m3 (OCP FP8: 1 sign, 4 exponent bits with bias 7, 3
+ *                  mantissa bits, no infinities) [B][H][Nq][d], one byte each;
+ *                  real value = descale_q * stored value.
+ *   k, v     (in)  e4m3 [B][Hkv][Nk][d], real values descale_k * k and
+ *                  descale_v * v; heads shared and query rows aligned as in
+ *                  fa_fwd_rect (causal: bottom-right).
+ *   o        (out) bf16 [B][H][Nq][d]; lse (out) fp32 [B][H][Nq], as fa_fwd,
+ *                  of attention over the real (dequantised) values.
+ * Q K^T and P V run on e4m3 MFMA with fp32 accumulation; the softmax
+ * statistics are fp32; the probabilities are rounded to e4m3 (scaled by 2^4)
+ * only as the operand of P V, and O is normalised by the sum of those rounded
+ * probabilities. d must be 128 (else FA_ERR_UNSUPPORTED); descales must be
+ * finite and > 0 (else FA_ERR_INVALID_ARG). Tensor pointers 16-byte aligned.
+ * Everything else as for fa_fwd_rect.
+ */
+fa_status_t fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                       float descale_q, float descale_k, float descale_v, hipStream_t stream);
+
+/*
  * Forward, fp32 storage and fp32 arithmetic throughout (no reduced-precision
  * operands). Same layout, masking, outputs and errors as fa_fwd.
  */

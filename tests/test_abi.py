@@ -221,3 +221,20 @@ def test_backward_phases_reject_bad_arguments(lib):
     assert lib.fa_bwd_dkdv(A, A, None, A, W, ws, A, A, 1, 2, 100, 128, 1, 0.1, None) == INVALID
     assert lib.fa_bwd_dkdv(A, A, A, A, None, ws, A, A, 1, 2, 100, 128, 1, 0.1, None) == WORKSPACE
     assert lib.fa_bwd_dkdv(A, A, A, A, W, ws, A, A, 1, 2, 100, 128, 1, -1.0, None) == INVALID
+
+
+def test_fp8_forward_arguments(lib):
+    def f(B=1, H=2, Hkv=1, Nq=100, Nk=300, d=128, q=A, scale=0.1, dq=0.01, dk=0.01, dv=0.01):
+        return lib.fa_fwd_fp8(q, A, A, A, A, B, H, Hkv, Nq, Nk, d, 1, scale, dq, dk, dv, None)
+    assert f(dq=0.0) == INVALID
+    assert f(dk=-1.0) == INVALID
+    assert f(dv=float("inf")) == INVALID
+    assert f(dq=float("nan")) == INVALID
+    assert f(Nk=-1) == INVALID
+    assert f(Nk=0) == INVALID
+    assert f(Hkv=3) == INVALID
+    assert f(q=None) == INVALID
+    assert f(d=64) == UNSUPPORTED
+    assert f(d=256) == UNSUPPORTED
+    assert f(q=MIS) == UNSUPPORTED
+    assert f(B=0) == OK
