@@ -46,6 +46,10 @@ namespace fa {
 // ---------------------------------------------------------------------------
 
 constexpr int kFwdWaves = 8;
+#ifndef FA_FWD_AHEAD
+#define FA_FWD_AHEAD 4
+#endif
+constexpr int kFwdAhead = FA_FWD_AHEAD;   // LDS fragment reads in flight ahead of the MFMAs
 
 __device__ __forceinline__ void wg_barrier() {
     __builtin_amdgcn_sched_barrier(0);
@@ -209,14 +213,14 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 acc_o[nb] = mfma_32x32x16(vf, pf[t4], acc_o[nb]);
             }
         }
-        // One LDS read per MFMA: four reads ahead, then alternate.
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        // One LDS read per MFMA: kFwdAhead reads ahead, then alternate.
+        __builtin_amdgcn_sched_group_barrier(0x100, kFwdAhead, 0);
 #pragma unroll
-        for (int x = 0; x < NS + NP - 4; ++x) {
+        for (int x = 0; x < NS + NP - kFwdAhead; ++x) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, kFwdAhead, 0);
         __builtin_amdgcn_s_setprio(0);
         wait_lds();
     };

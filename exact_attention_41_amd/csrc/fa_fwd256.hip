@@ -32,7 +32,10 @@
 namespace fa {
 
 constexpr int kW256Waves = 4;
-constexpr int kW256Ahead = 4;     // LDS fragment reads in flight ahead of the MFMAs
+#ifndef FA_W256_AHEAD
+#define FA_W256_AHEAD 4
+#endif
+constexpr int kW256Ahead = FA_W256_AHEAD;   // LDS fragment reads in flight ahead of the MFMAs
 
 template <bool CAUSAL>
 __global__ void __launch_bounds__(kW256Waves * 64, 1)
@@ -244,6 +247,10 @@ fwd_d256_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 // v_j - O); lse uses the fp32 sum.
 #pragma unroll
                 for (int w = 0; w < 4; ++w) l_rnd = add_bf16x2(pf[t4][w], l_rnd);
+                // The sums are used from the next tile on: keep their
+                // computation between the products of this one.
+                keep_here(l_run);
+                keep_here(l_rnd);
             }
         };
         if (!NEXT) {
