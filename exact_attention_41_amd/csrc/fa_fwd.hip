@@ -296,21 +296,22 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     // loaded by A in slot 2t. All of them are first read in slot 2t+2.
     for (int t = 0; t <= n_tiles; ++t) {
         matrix_slot(t);
+        // Group A stages V(t), group B V(t+1). One call site for both: with
+        // two, the compiler loads into different registers and joins them
+        // with copies that wait for the loads before the barrier below.
+        const int tv = min(t + grp, n_tiles - 1);
         if (t < n_tiles) {
-            if (grp == 0) {
-                if (t + 1 < n_tiles)
-                    stage_tile_lds<D, BLOCKS / 4, 4, false>(Kh, Kb((t + 1) & 1), (t + 1) * BC, Nk,
-                                                            wave, lane);
-                v_load(t);
-            } else if (t + 1 < n_tiles) {
-                v_load(t + 1);
-            }
+            v_load(tv);
+            if (grp == 0 && t + 1 < n_tiles)
+                stage_tile_lds<D, BLOCKS / 4, 4, false>(Kh, Kb((t + 1) & 1), (t + 1) * BC, Nk,
+                                                        wave, lane);
         }
         wg_barrier();
         if (t < n_tiles) {
             vector_slot(t);
-            if (grp == 0) v_store(t);
-            else if (t + 1 < n_tiles) v_store(t + 1);
+            // The V writes wait for the loads: after the softmax, not in it.
+            __builtin_amdgcn_sched_barrier(0);
+            if (t + grp < n_tiles) v_store(tv);
             wait_vmem();
             wg_barrier();
         }
