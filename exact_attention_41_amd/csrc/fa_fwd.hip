@@ -138,51 +138,41 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     // K(t+1) goes straight into LDS (group A, global_load_lds). V(t) goes
     // through registers into a transposed layout ([d][64 keys], the permuted
     // key order of fa_device.hpp) so the matrix slot reads V^T fragments with
-    // plain 16-byte LDS reads: each group moves half of the 4-key x 8-column
-    // micro-tiles, loading them in its matrix slot and writing them in its
-    // next vector slot. Rows past N read row N-1 (masked keys).
-    constexpr int DCH = D / 8;
-    constexpr int V_UNITS = 16 * DCH;                  // 4-key x 8-column micro-tiles
-    constexpr int V_HALF = V_UNITS / 2;                // per group
-    constexpr int V_PER_LANE = (V_HALF + 255) / 256;
-    u32x4_t vreg[V_PER_LANE][4];
-    const int vbase = grp * V_HALF + (wave & 3) * 64 + lane;
+    // plain 16-byte LDS reads. The tile is cut into 512 micro-tiles of 4 keys
+    // x CW = d/32 columns, 256 per group, so that every thread of a group
+    // moves exactly one: it loads them in its matrix slot (4 rows of CW
+    // values) and writes them in its next vector slot (one 8-byte slot of 4
+    // keys per column). Rows past Nk read row Nk-1 (masked keys).
+    constexpr int CW = D / 32;                         // columns per micro-tile
+    constexpr int NCG = D / CW;                        // column groups (32)
+    static_assert(16 * NCG == 2 * kFwdWaves * 32, "one micro-tile per thread");
+    typedef __attribute__((ext_vector_type(CW / 2))) uint32_t vrow_t;   // CW bf16 values
+    vrow_t vreg[4];
+    const int vu = grp * 256 + (wave & 3) * 64 + lane;
+    const int v_cg = vu % NCG, v_rg = vu / NCG;
     auto v_load = [&](int t) {
 #pragma unroll
-        for (int k = 0; k < V_PER_LANE; ++k) {
-            const int u = vbase + 256 * k;
-            if (V_HALF % 256 != 0 && u >= grp * V_HALF + V_HALF) continue;
-            const int ch = u % DCH, rg = u / DCH;
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int j = min(t * BC + 4 * rg + rr, Nk - 1);
-                vreg[k][rr] = *(const u32x4_t*)(Vh + (size_t)j * D + ch * 8);
-            }
+        for (int rr = 0; rr < 4; ++rr) {
+            const int j = min(t * BC + 4 * v_rg + rr, Nk - 1);
+            vreg[rr] = *(const vrow_t*)(Vh + (size_t)j * D + v_cg * CW);
         }
     };
     auto v_store = [&](int t) {
         lds_char* vl = Vb(t & 1);
+        const int slot = tr_key_position(4 * v_rg) >> 2;
 #pragma unroll
-        for (int k = 0; k < V_PER_LANE; ++k) {
-            const int u = vbase + 256 * k;
-            if (V_HALF % 256 != 0 && u >= grp * V_HALF + V_HALF) continue;
-            const int ch = u % DCH, rg = u / DCH;
-            const int slot = tr_key_position(4 * rg) >> 2;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int w = e >> 1;
-                const uint32_t r0 = vreg[k][0][w], r1 = vreg[k][1][w];
-                const uint32_t r2 = vreg[k][2][w], r3 = vreg[k][3][w];
-                u32x2_t col;
-                if (e & 1) {
-                    col[0] = (r0 >> 16) | (r1 & 0xffff0000u);
-                    col[1] = (r2 >> 16) | (r3 & 0xffff0000u);
-                } else {
-                    col[0] = (r0 & 0xffffu) | (r1 << 16);
-                    col[1] = (r2 & 0xffffu) | (r3 << 16);
-                }
-                *(__attribute__((address_space(3))) u32x2_t*)(vl + tr_slot_offset(ch * 8 + e, slot)) = col;
+        for (int e = 0; e < CW; ++e) {
+            const int w = e >> 1;
+            const uint32_t r0 = vreg[0][w], r1 = vreg[1][w], r2 = vreg[2][w], r3 = vreg[3][w];
+            u32x2_t col;
+            if (e & 1) {
+                col[0] = (r0 >> 16) | (r1 & 0xffff0000u);
+                col[1] = (r2 >> 16) | (r3 & 0xffff0000u);
+            } else {
+                col[0] = (r0 & 0xffffu) | (r1 << 16);
+                col[1] = (r2 & 0xffffu) | (r3 << 16);
             }
+            *(__attribute__((address_space(3))) u32x2_t*)(vl + tr_slot_offset(v_cg * CW + e, slot)) = col;
         }
     };
 
