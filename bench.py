@@ -265,8 +265,9 @@ def gpu_gqa_timing(names, iters=10, warmup=3):
 
 
 def gpu_rect_timing(names, iters=10, warmup=3):
-    """Forward with Nq query rows against Nk keys (fa_fwd_rect), median of
-    ``iters`` calls; flops counted over the unmasked score elements."""
+    """Forward and backward with Nq query rows against Nk keys (fa_fwd_rect,
+    fa_bwd_rect), median of ``iters`` calls each; flops counted over the
+    unmasked score elements (the backward as 2.5x the forward)."""
     import torch
 
     import exact_attention_41_amd as fa
@@ -276,26 +277,44 @@ def gpu_rect_timing(names, iters=10, warmup=3):
     dev = torch.device("cuda:0")
     for name in names:
         w = wl.RECT_WORKLOADS[name]
-        inp = wl.make_decode_inputs(w.B, w.H, w.Hkv, w.Nq, w.Nk, w.d, w.seed)
-        q, k, v = (wl.to_device(x, "bf16", dev) for x in (inp.q, inp.k, inp.v))
+        inp = wl.make_decode_inputs(w.B, w.H, w.Hkv, w.Nq, w.Nk, w.d, w.seed, with_do=True)
+        q, k, v, do = (wl.to_device(x, "bf16", dev) for x in (inp.q, inp.k, inp.v, inp.do))
         o = torch.empty_like(q)
         lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
-        for _ in range(warmup):
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = torch.empty(fa.fa_bwd_rect_workspace_size(w.B, w.H, w.Hkv, w.Nq, w.Nk, w.d),
+                         dtype=torch.uint8, device=dev)
+
+        def fwd():
             fa.fa_fwd_rect(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
-        for i in range(iters):
-            ev[i].record()
-            fa.fa_fwd_rect(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
-            ev[i + 1].record()
-        torch.cuda.synchronize(dev)
-        times = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(iters))
-        med = times[len(times) // 2]
-        tf = wl.rect_flops(w) / (med * 1e-3) / 1e12
+
+        def bwd():
+            fa.fa_bwd_rect(q, k, v, o, do, lse, causal=w.causal, scale=w.scale, dq=dq, dk=dk,
+                           dv=dv, workspace=ws)
+
+        res = {}
+        for label, fn in (("fwd", fwd), ("bwd", bwd)):
+            for _ in range(warmup):
+                fn()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
+            for i in range(iters):
+                ev[i].record()
+                fn()
+                ev[i + 1].record()
+            torch.cuda.synchronize(dev)
+            times = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(iters))
+            res[label] = times[len(times) // 2]
+        ftf = wl.rect_flops(w) / (res["fwd"] * 1e-3) / 1e12
+        btf = 2.5 * wl.rect_flops(w) / (res["bwd"] * 1e-3) / 1e12
         out.append({"workload": name, "Nq": w.Nq, "Nk": w.Nk, "H": w.H, "Hkv": w.Hkv,
-                    "ms": round(med, 4), "tflops": round(tf, 1),
-                    "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
-        log(f"  rect {name}: {med:.3f} ms  {tf:.1f} TFLOP/s  {100 * tf / PEAK_BF16_TFLOPS:.1f}%")
-        del q, k, v, o, lse
+                    "ms": round(res["fwd"], 4), "tflops": round(ftf, 1),
+                    "frac_peak": round(ftf / PEAK_BF16_TFLOPS, 4),
+                    "bwd_ms": round(res["bwd"], 4), "bwd_tflops": round(btf, 1),
+                    "bwd_frac_peak": round(btf / PEAK_BF16_TFLOPS, 4)})
+        log(f"  rect {name}: fwd {res['fwd']:.3f} ms {ftf:.1f} TFLOP/s "
+            f"{100 * ftf / PEAK_BF16_TFLOPS:.1f}%, bwd {res['bwd']:.3f} ms {btf:.1f} TFLOP/s "
+            f"{100 * btf / PEAK_BF16_TFLOPS:.1f}%")
+        del q, k, v, do, o, lse, dq, dk, dv, ws
     return out
 
 

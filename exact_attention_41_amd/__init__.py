@@ -12,6 +12,7 @@ If the library is not built, every call raises: there is no fallback.
     dq, dk, dv = fa_bwd_gqa(q, k, v, o, do, lse, causal=True)
     o, lse = fa_decode(q, k, v)          # q [B,H,Nq,d], k, v [B,Hkv,Nk,d]
     o, lse = fa_fwd_rect(q, k, v, causal=True)   # any Nq, Nk; bottom-right causal
+    dq, dk, dv = fa_bwd_rect(q, k, v, o, do, lse, causal=True)
     o, lse = fa_fwd_fp8(q8, k8, v8, dq, dk, dv)  # e4m3 inputs with per-tensor factors
 """
 from __future__ import annotations
@@ -24,7 +25,8 @@ from . import _lib
 __all__ = ["fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_bwd_workspace_size", "fa_status_str",
            "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_gqa", "fa_bwd_gqa",
            "fa_bwd_gqa_workspace_size", "fa_decode", "fa_decode_workspace_size", "fa_fwd_rect",
-           "fa_fwd_fp8", "FAError", "library_path"]
+           "fa_fwd_fp8", "fa_bwd_rect", "fa_bwd_rect_workspace_size", "FAError",
+           "library_path"]
 
 
 class FAError(RuntimeError):
@@ -47,6 +49,10 @@ def fa_bwd_workspace_size(B: int, H: int, N: int, d: int) -> int:
 
 def fa_bwd_gqa_workspace_size(B: int, H: int, Hkv: int, N: int, d: int) -> int:
     return int(_lib.load().fa_bwd_gqa_workspace_size(B, H, Hkv, N, d))
+
+
+def fa_bwd_rect_workspace_size(B: int, H: int, Hkv: int, Nq: int, Nk: int, d: int) -> int:
+    return int(_lib.load().fa_bwd_rect_workspace_size(B, H, Hkv, Nq, Nk, d))
 
 
 def _torch():
@@ -135,15 +141,21 @@ def fa_fwd_f32(q, k, v, causal: bool = False, scale: Optional[float] = None,
     return _fwd("fa_fwd_f32", _torch().float32, q, k, v, causal, scale, out, lse)
 
 
-def _bwd(entry, q, k, v, o, do, lse, causal, scale, dq, dk, dv, workspace, grouped):
+def _bwd(entry, q, k, v, o, do, lse, causal, scale, dq, dk, dv, workspace, grouped,
+         rect=False):
     torch = _torch()
     bf = torch.bfloat16
     _check(q, "q", bf)
     if q.dim() != 4:
         raise ValueError("q must be [B, H, N, d]")
     B, H, N, d = q.shape
-    Hkv = _kv_heads(q, k, grouped)
-    kv_shape = (B, Hkv, N, d)
+    if rect:
+        if not isinstance(k, torch.Tensor) or k.dim() != 4:
+            raise ValueError("k must be [B, Hkv, Nk, d]")
+        Hkv, Nk = k.shape[1], k.shape[2]
+    else:
+        Hkv, Nk = _kv_heads(q, k, grouped), N
+    kv_shape = (B, Hkv, Nk, d)
     for t, n, shp in ((k, "k", kv_shape), (v, "v", kv_shape), (o, "o", q.shape),
                       (do, "do", q.shape)):
         _check(t, n, bf, shp, q.device)
@@ -153,16 +165,17 @@ def _bwd(entry, q, k, v, o, do, lse, causal, scale, dq, dk, dv, workspace, group
     dv = torch.empty_like(v) if dv is None else dv
     for t, n, shp in ((dq, "dq", q.shape), (dk, "dk", kv_shape), (dv, "dv", kv_shape)):
         _check(t, n, bf, shp, q.device)
-    need = fa_bwd_gqa_workspace_size(B, H, Hkv, N, d)
+    need = fa_bwd_rect_workspace_size(B, H, Hkv, N, Nk, d)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size()
-    heads = (B, H, Hkv) if grouped else (B, H)
+    heads = (B, H, Hkv) if grouped or rect else (B, H)
+    sizes = (N, Nk) if rect else (N,)
     fn = getattr(_lib.load(), entry)
     with torch.cuda.device(q.device):
         st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
                 lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                workspace.data_ptr(), ws_bytes, *heads, N, d, int(bool(causal)),
+                workspace.data_ptr(), ws_bytes, *heads, *sizes, d, int(bool(causal)),
                 _scale(scale, d), _stream_ptr(q.device))
     if st != _lib.FA_OK:
         raise FAError(st, entry)
@@ -186,6 +199,17 @@ def fa_bwd_gqa(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float]
     Calls fa_bwd_gqa of libfa.so; ``workspace`` as for fa_bwd, of
     fa_bwd_gqa_workspace_size(B, H, Hkv, N, d) bytes."""
     return _bwd("fa_bwd_gqa", q, k, v, o, do, lse, causal, scale, dq, dk, dv, workspace, True)
+
+
+def fa_bwd_rect(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = None,
+                dq=None, dk=None, dv=None, workspace=None):
+    """bf16 backward of fa_fwd_rect: q, o, do [B,H,Nq,d], lse [B,H,Nq], k and v
+    [B,Hkv,Nk,d]; returns (dQ [B,H,Nq,d], dK and dV [B,Hkv,Nk,d]). Query row i
+    sits at position Nk - Nq + i (bottom-right causal alignment). Calls
+    fa_bwd_rect of libfa.so; ``workspace`` as for fa_bwd, of
+    fa_bwd_rect_workspace_size(B, H, Hkv, Nq, Nk, d) bytes."""
+    return _bwd("fa_bwd_rect", q, k, v, o, do, lse, causal, scale, dq, dk, dv, workspace, True,
+                rect=True)
 
 
 def _bwd_common(ref, tensors, lse, workspace):

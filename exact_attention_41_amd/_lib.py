@@ -14,7 +14,7 @@ STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_INVALID_ARG", 2: "FA_ERR_UNSUPPORTED",
 EXPORTED = ("fa_status_str", "fa_fwd", "fa_fwd_f32", "fa_bwd_workspace_size", "fa_bwd",
             "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_gqa",
             "fa_bwd_gqa_workspace_size", "fa_bwd_gqa", "fa_decode_workspace_size", "fa_decode",
-            "fa_fwd_rect", "fa_fwd_fp8")
+            "fa_fwd_rect", "fa_fwd_fp8", "fa_bwd_rect_workspace_size", "fa_bwd_rect")
 
 _lock = threading.Lock()
 _lib = None
@@ -62,6 +62,11 @@ def load() -> ctypes.CDLL:
         lib.fa_bwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                    i, i, i, i, i, i, f, vp]
         lib.fa_bwd_gqa.restype = i
+        lib.fa_bwd_rect_workspace_size.argtypes = [i, i, i, i, i, i]
+        lib.fa_bwd_rect_workspace_size.restype = ctypes.c_size_t
+        lib.fa_bwd_rect.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                    i, i, i, i, i, i, i, f, vp]
+        lib.fa_bwd_rect.restype = i
         lib.fa_fwd_rect.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
         lib.fa_fwd_rect.restype = i
         lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, f, f, f, vp]

@@ -141,10 +141,14 @@ fa_status_t fa_fwd_f32(const float* q, const float* k, const float* v, float* o,
     return fa::launch_fwd_f32(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-size_t fa_bwd_gqa_workspace_size(int B, int H, int Hkv, int N, int d) {
-    if (B <= 0 || H <= 0 || N <= 0 || !head_dim_ok(d, false)) return 0;
+size_t fa_bwd_rect_workspace_size(int B, int H, int Hkv, int Nq, int Nk, int d) {
+    if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || !head_dim_ok(d, false)) return 0;
     if (Hkv <= 0 || H % Hkv != 0) return 0;
-    return fa::bwd_workspace_layout(B, H, Hkv, N, d).total;
+    return fa::bwd_workspace_layout(B, H, Hkv, Nq, Nk, d).total;
+}
+
+size_t fa_bwd_gqa_workspace_size(int B, int H, int Hkv, int N, int d) {
+    return fa_bwd_rect_workspace_size(B, H, Hkv, N, N, d);
 }
 
 size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
@@ -160,27 +164,33 @@ namespace {
 // the workspace is checked last.
 fa_status_t check_bwd(std::initializer_list<const void*> tensors, bool need_lse, const void* lse,
                       const void* workspace, size_t workspace_bytes, int B, int H, int Hkv,
-                      int N, int d, float scale, bool* empty) {
-    FA_TRY(check_common(B, H, N, d, scale, false, empty));
+                      int Nq, int Nk, int d, float scale, bool* empty) {
+    if (Nk < 0) return FA_ERR_INVALID_ARG;
+    FA_TRY(check_common(B, H, Nq, d, scale, false, empty));
     FA_TRY(check_heads(H, Hkv));
-    if (*empty) return FA_OK;
+    if (*empty && (B == 0 || H == 0 || Nk == 0)) return FA_OK;
+    // Rows without keys, or keys without rows (whose gradients are zero and
+    // left to the caller), are argument errors.
+    if (*empty || Nk == 0) return FA_ERR_INVALID_ARG;
+    bool unused = false;
+    FA_TRY(check_common(B, H, Nk, d, scale, false, &unused));
     for (const void* p : tensors)
         if (!p) return FA_ERR_INVALID_ARG;
     if (need_lse && !lse) return FA_ERR_INVALID_ARG;
     for (const void* p : tensors) FA_TRY(check_tensor(p));
     if (need_lse) FA_TRY(check_lse(lse));
     if (!workspace || !aligned(workspace, 256) ||
-        workspace_bytes < fa_bwd_gqa_workspace_size(B, H, Hkv, N, d))
+        workspace_bytes < fa_bwd_rect_workspace_size(B, H, Hkv, Nq, Nk, d))
         return FA_ERR_WORKSPACE;
     return FA_OK;
 }
 
 fa::BwdArgs bwd_args(const void* q, const void* k, const void* v, const void* dout,
                      const float* lse, void* dq, void* dk, void* dv, void* workspace, int B,
-                     int H, int Hkv, int N, int d, int causal, float scale,
+                     int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                      hipStream_t stream) {
     return fa::BwdArgs{q, k, v, dout, lse, dq, dk, dv, workspace,
-                       B, H, Hkv, N, d, causal != 0, scale, stream};
+                       B, H, Hkv, Nq, Nk, d, causal != 0, scale, stream};
 }
 
 }  // namespace
@@ -191,11 +201,11 @@ fa_status_t fa_bwd_preprocess(const void* q, const void* k, const void* v, const
                               void* workspace, size_t workspace_bytes, int B, int H, int N,
                               int d, hipStream_t stream) {
     bool empty = false;
-    FA_TRY(check_bwd({q, k, v, dout}, false, nullptr, workspace, workspace_bytes, B, H, H, N,
+    FA_TRY(check_bwd({q, k, v, dout}, false, nullptr, workspace, workspace_bytes, B, H, H, N, N,
                      d, 1.f, &empty));
     if (empty) return FA_OK;
     const fa::BwdArgs a = bwd_args(q, k, v, dout, nullptr, nullptr, nullptr, nullptr, workspace,
-                                   B, H, H, N, d, 0, 1.f, stream);
+                                   B, H, H, N, N, d, 0, 1.f, stream);
     return fa::launch_bwd_prepare(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -203,11 +213,11 @@ fa_status_t fa_bwd_dq(const void* q, const void* k, const void* v, const void* d
                       const float* lse, void* workspace, size_t workspace_bytes, void* dq,
                       int B, int H, int N, int d, int causal, float scale, hipStream_t stream) {
     bool empty = false;
-    FA_TRY(check_bwd({q, k, v, dout, dq}, true, lse, workspace, workspace_bytes, B, H, H, N, d,
-                     scale, &empty));
+    FA_TRY(check_bwd({q, k, v, dout, dq}, true, lse, workspace, workspace_bytes, B, H, H, N, N,
+                     d, scale, &empty));
     if (empty) return FA_OK;
     const fa::BwdArgs a = bwd_args(q, k, v, dout, lse, dq, nullptr, nullptr, workspace,
-                                   B, H, H, N, d, causal, scale, stream);
+                                   B, H, H, N, N, d, causal, scale, stream);
     return fa::launch_bwd_dq(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -216,28 +226,36 @@ fa_status_t fa_bwd_dkdv(const void* q, const void* k, const void* v, const void*
                         int B, int H, int N, int d, int causal, float scale, hipStream_t stream) {
     bool empty = false;
     FA_TRY(check_bwd({q, k, v, dout, dk, dv}, false, nullptr, workspace, workspace_bytes, B, H,
-                     H, N, d, scale, &empty));
+                     H, N, N, d, scale, &empty));
     if (empty) return FA_OK;
     const fa::BwdArgs a = bwd_args(q, k, v, dout, nullptr, nullptr, dk, dv,
-                                   const_cast<void*>(workspace), B, H, H, N, d, causal, scale,
+                                   const_cast<void*>(workspace), B, H, H, N, N, d, causal, scale,
                                    stream);
     return fa::launch_bwd_dkdv(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status_t fa_bwd_rect(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        void* workspace, size_t workspace_bytes, int B, int H, int Hkv, int Nq,
+                        int Nk, int d, int causal, float scale, hipStream_t stream) {
+    bool empty = false;
+    FA_TRY(check_bwd({q, k, v, o, dout, dq, dk, dv}, true, lse, workspace, workspace_bytes, B, H,
+                     Hkv, Nq, Nk, d, scale, &empty));
+    if (empty) return FA_OK;
+    const fa::BwdArgs a = bwd_args(q, k, v, dout, lse, dq, dk, dv, workspace, B, H, Hkv, Nq, Nk,
+                                   d, causal, scale, stream);
+    if (fa::launch_bwd_prepare(a) != hipSuccess) return FA_ERR_HIP;
+    if (fa::launch_bwd_dq(a) != hipSuccess) return FA_ERR_HIP;
+    if (fa::launch_bwd_dkdv(a) != hipSuccess) return FA_ERR_HIP;
+    return FA_OK;
 }
 
 fa_status_t fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o,
                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
                        void* workspace, size_t workspace_bytes, int B, int H, int Hkv, int N,
                        int d, int causal, float scale, hipStream_t stream) {
-    bool empty = false;
-    FA_TRY(check_bwd({q, k, v, o, dout, dq, dk, dv}, true, lse, workspace, workspace_bytes, B, H,
-                     Hkv, N, d, scale, &empty));
-    if (empty) return FA_OK;
-    const fa::BwdArgs a = bwd_args(q, k, v, dout, lse, dq, dk, dv, workspace, B, H, Hkv, N, d,
-                                   causal, scale, stream);
-    if (fa::launch_bwd_prepare(a) != hipSuccess) return FA_ERR_HIP;
-    if (fa::launch_bwd_dq(a) != hipSuccess) return FA_ERR_HIP;
-    if (fa::launch_bwd_dkdv(a) != hipSuccess) return FA_ERR_HIP;
-    return FA_OK;
+    return fa_bwd_rect(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, Hkv,
+                       N, N, d, causal, scale, stream);
 }
 
 fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o,

@@ -49,38 +49,45 @@ constexpr int kFragAhead = FA_BWD_FRAG_AHEAD;
 // ---------------------------------------------------------------------------
 static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-BwdWorkspace bwd_workspace_layout(long long B, long long H, long long Hkv, long long N,
-                                  long long d) {
+int bwd_scale_chunks(long long Nq, long long Nk) {
+    const long long n = Nq > Nk ? Nq : Nk;
+    return (int)((n + kScaleRows - 1) / kScaleRows);
+}
+
+BwdWorkspace bwd_workspace_layout(long long B, long long H, long long Hkv, long long Nq,
+                                  long long Nk, long long d) {
     BwdWorkspace w;
     const size_t bh = (size_t)(B * H), bhkv = (size_t)(B * Hkv);
-    const size_t chunks = (size_t)((N + kScaleRows - 1) / kScaleRows);
-    const size_t tiles = (size_t)((N + 63) / 64);
-    const size_t image = tiles * 64 * (size_t)d * 2;     // per head
+    const size_t chunks = (size_t)bwd_scale_chunks(Nq, Nk);
+    const size_t tq = (size_t)((Nq + 63) / 64), tk = (size_t)((Nk + 63) / 64);
+    const size_t tile = 64 * (size_t)d * 2;             // one transposed 64-row tile
     w.scales = 0;
     w.partial = w.scales + align256(bh * 4 * 4);
     w.stats = w.partial + align256((bh + bhkv) * chunks * 2 * 4);
-    w.qt = w.stats + align256(bh * tiles * 128 * 4);
-    w.ot = w.qt + align256(bh * image);
-    w.kt = w.ot + align256(bh * image);
-    w.total = w.kt + align256(bhkv * image);
+    w.qt = w.stats + align256(bh * tq * 128 * 4);
+    w.ot = w.qt + align256(bh * tq * tile);
+    w.kt = w.ot + align256(bh * tq * tile);
+    w.total = w.kt + align256(bhkv * tk * tile);
     return w;
 }
 
 // ---------------------------------------------------------------------------
 // Phase 1a: per (head, chunk of kScaleRows rows), the largest |x| of two
 // tensors, as bf16 magnitude bits (for finite values the integer order of
-// (bits & 0x7fff) is the order of |x|): Q and dO for the BH query heads
-// (rows r < BH of the grid), K and V for the BHkv K/V heads (rows r >= BH).
+// (bits & 0x7fff) is the order of |x|): Q and dO (Nq rows) for the BH query
+// heads (rows r < BH of the grid), K and V (Nk rows) for the BHkv K/V heads
+// (rows r >= BH). Chunks past a tensor's rows record 0.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ void __launch_bounds__(256)
 bwd_absmax_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                   const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-                  uint32_t* __restrict__ partial, int BH, int N, int chunks) {
+                  uint32_t* __restrict__ partial, int BH, int Nq, int Nk, int chunks) {
     constexpr int DCH = D / 8;
     const int bid = blockIdx.x;
     const int r = bid / chunks, ch = bid % chunks;
     const bool kv = r >= BH;
+    const int N = kv ? Nk : Nq;
     const int row0 = ch * kScaleRows;
     const int nrows = min(kScaleRows, N - row0);
     const size_t base = ((size_t)(kv ? r - BH : r) * N + row0) * D;
@@ -210,19 +217,21 @@ struct Tile64 {
 
 
 // Phase 1c: fp16 transposed images. One workgroup per (head, 64-row tile):
-// grid rows r < BH are the Q images of the query heads, the next BH the dO
-// images, the last BHkv the K images of the K/V heads.
+// the first BH*Tq workgroups make the Q images of the query heads, the next
+// BH*Tq the dO images, the last BHkv*Tk the K images of the K/V heads.
 template <int D>
 __global__ void __launch_bounds__(256)
 bwd_image_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                  const uint16_t* __restrict__ dO, const float* __restrict__ scales,
                  char* __restrict__ qt, char* __restrict__ ot, char* __restrict__ kt, int BH,
-                 int G, int N, int T) {
+                 int G, int Nq, int Nk, int Tq, int Tk) {
     using TileT = Tile64<D, 256>;
     const int bid = blockIdx.x;
-    const int r = bid / T, tile = bid % T;
-    const int which = r < BH ? 0 : (r < 2 * BH ? 1 : 2);
-    const int head = r - which * BH;           // query head (Q, dO) or K/V head (K)
+    const int qblocks = BH * Tq;
+    const int which = bid < qblocks ? 0 : (bid < 2 * qblocks ? 1 : 2);
+    const int rel = bid - (which < 2 ? which * qblocks : 2 * qblocks);
+    const int T = which < 2 ? Tq : Tk, N = which < 2 ? Nq : Nk;
+    const int head = rel / T, tile = rel % T;  // query head (Q, dO) or K/V head (K)
     const uint16_t* src = which == 0 ? Q : (which == 1 ? dO : K);
     char* dst = which == 0 ? qt : (which == 1 ? ot : kt);
     const float s = which == 0 ? scales[head * 4 + 0]
@@ -249,8 +258,8 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
               const float* __restrict__ LSE, const float* __restrict__ scales,
               const char* __restrict__ kt_img, float* __restrict__ stats,
-              uint16_t* __restrict__ dQ, int BH, int G, int N, int T, float c, float scale,
-              int nqb) {
+              uint16_t* __restrict__ dQ, int BH, int G, int N, int Nk, int T, int Tk,
+              float c, float scale, int nqb) {
     constexpr int BC = 64;
     constexpr int BQ = NW * 32;
     constexpr int KS = D / 16;
@@ -268,13 +277,14 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const int bh = bid % BH;
     const int qb = CAUSAL ? (nqb - 1 - bid / BH) : bid / BH;
     const size_t head = (size_t)bh * (size_t)N * D;
-    const size_t kvhead = (size_t)(bh / G) * (size_t)N * D;   // K/V head of this query head
+    const size_t kvhead = (size_t)(bh / G) * (size_t)Nk * D;  // K/V head of this query head
     const uint16_t* Kh = K + kvhead;
     const uint16_t* Vh = V + kvhead;
-    const char* kt_h = kt_img + (size_t)(bh / G) * T * TB;
+    const char* kt_h = kt_img + (size_t)(bh / G) * Tk * TB;
     const int q0 = qb * BQ;
     const int wq0 = q0 + wave * 32;
     const int qi = wq0 + l32;             // this lane's query row
+    const int off = Nk - N;               // query row i sits at key position i + off
 
     const float sK = scales[bh * 4 + 1];
     const float sV = scales[bh * 4 + 2], sDO = scales[bh * 4 + 3];
@@ -296,7 +306,10 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         park_in_agprs(qf[s]);
         park_in_agprs(of[s]);
     }
-    const float lse2 = (qi < N) ? LSE[(size_t)bh * N + qi] * kLog2e : __builtin_huge_valf();
+    // Rows past N, and rows that see no key (lse = -inf), take +inf: every
+    // probability of theirs is then exactly 0.
+    const float lse_i = (qi < N) ? LSE[(size_t)bh * N + qi] : kNegInf;
+    const float lse2 = (lse_i == kNegInf) ? __builtin_huge_valf() : lse_i * kLog2e;
 
     f32x16_t acc_a[NB], acc_b[NB];
 #pragma unroll
@@ -305,9 +318,9 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         for (int r = 0; r < 16; ++r) acc_a[nb][r] = acc_b[nb][r] = 0.f;
     float dsum = 0.f;
 
-    const int n_all = (N + BC - 1) / BC;
-    const int q_last = min(q0 + BQ, N) - 1;
-    const int n_tiles = CAUSAL ? min(n_all, q_last / BC + 1) : n_all;
+    const int n_all = (Nk + BC - 1) / BC;
+    const int q_last = min(q0 + BQ, N) - 1 + off;      // last key position of the block
+    const int n_tiles = CAUSAL ? min(n_all, max(q_last, 0) / BC + 1) : n_all;
 
     // Key tile t into buffer buf: K and V rows (bf16, swizzled) and the
     // (sK K)^T image, BLK 1 KB blocks each, spread over the NW waves; part k
@@ -320,9 +333,9 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         const int tensor = k / PPT, b = wave + NW * (k % PPT);
         if (tensor < 2)
             stage_tile_block<D>(tensor == 0 ? Kh : Vh, base + (tensor == 0 ? OFF_K : OFF_V),
-                                t * BC, N, b, lane);
+                                t * BC, Nk, b, lane);
         else
-            stage_image_block(kt_h + (size_t)min(t, T - 1) * TB, TB, base + OFF_KT, b, lane);
+            stage_image_block(kt_h + (size_t)min(t, Tk - 1) * TB, TB, base + OFF_KT, b, lane);
     };
 
     // Lane-dependent LDS bases of buffer 0: pb[k], k < 8, for the row-major
@@ -382,7 +395,7 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             auto softmax_elem = [&](int jb, int r) {
                 const int j = j0 + 32 * jb + 8 * (r >> 2) + 4 * g + (r & 3);
                 float p = fast_exp2(__builtin_fmaf(sa[jb][r], c, -lse2));
-                if (MASK && (j >= N || (CAUSAL && j > qi))) p = 0.f;
+                if (MASK && (j >= Nk || (CAUSAL && j > qi + off))) p = 0.f;
                 const float e = p * da[jb][r];
                 dsum += e;
                 pv[r] = p;
@@ -436,9 +449,11 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
         __syncthreads();   // tile t+1 has landed; every wave is done with tile t
     };
-    // Tiles from t_mask on cross N or reach past the block's first row (a
-    // wave whose rows all precede such a tile computes it fully masked).
-    const int t_mask = min(CAUSAL ? (q0 + 1) / BC : n_tiles, N / BC);
+    // Tiles from t_mask on cross Nk or reach past the key position of the
+    // block's first row (a wave whose rows all precede such a tile computes
+    // it fully masked).
+    const int first_free = q0 + off + 1;       // keys below this are seen by every row
+    const int t_mask = min(CAUSAL ? (first_free > 0 ? first_free / BC : 0) : n_tiles, Nk / BC);
     for (int t = 0; t < min(t_mask, n_tiles); ++t) iteration(t, BoolTag<false>{});
     for (int t = max(t_mask, 0); t < n_tiles; ++t) iteration(t, BoolTag<true>{});
 
@@ -490,7 +505,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const float* __restrict__ scales, const float* __restrict__ stats,
                 const char* __restrict__ qt_img, const char* __restrict__ ot_img,
                 uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int BHkv, int G, int N,
-                int T, float c, float scale) {
+                int Nk, int T, float c, float scale) {
     constexpr int BQ = 64;
     constexpr int BKV = NW * 32;
     constexpr int KS = D / 16;
@@ -507,7 +522,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const int bid = blockIdx.x;
     const int bkv = bid % BHkv;           // K/V head
     const int kb = bid / BHkv;            // low key blocks see the most queries: first
-    const size_t head = (size_t)bkv * (size_t)N * D;
+    const size_t head = (size_t)bkv * (size_t)Nk * D;
     const int qh0 = bkv * G;              // its first query head; the group is qh0 .. qh0+G-1
 
     // One factor each for Q and dO serves the whole group of query heads.
@@ -518,11 +533,13 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const int k0 = kb * BKV;
     const int kw0 = k0 + wave * 32;
     const int kj = kw0 + l32;             // this lane's key
+    const int off = Nk - N;               // query row i sits at key position i + off
+    const int kq = kj - off;              // causal: the first query row that sees key kj
 
     u32x4_t kf[KS], vf[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-        if (kj < N) {
+        if (kj < Nk) {
             kf[s] = *(const u32x4_t*)(K + head + (size_t)kj * D + 16 * s + 8 * g);
             vf[s] = *(const u32x4_t*)(V + head + (size_t)kj * D + 16 * s + 8 * g);
         } else {
@@ -539,7 +556,9 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         for (int r = 0; r < 16; ++r) acc_dk[nb][r] = acc_dv[nb][r] = 0.f;
 
     const int n_tiles = (N + BQ - 1) / BQ;
-    const int t0 = CAUSAL ? (k0 / BQ) : 0;
+    // Causal: query tiles before t0 see no key of this block (t0 may reach
+    // n_tiles: then no query sees it and dK = dV = 0).
+    const int t0 = CAUSAL ? min(max(k0 - off, 0) / BQ, n_tiles) : 0;
 
     // Query tile t of group member gq (query head qh0 + gq) into buffer buf:
     // Q and dO rows (bf16, swizzled) and the two transposed fp16 images, BLK
@@ -642,7 +661,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             auto softmax_elem = [&](int ib, int r) {
                 const int q4 = r >> 2, r4 = r & 3;
                 float p = fast_exp2(__builtin_fmaf(sa[ib][r], c, -l4[q4][r4]));
-                if (MASK && kj > i0 + 32 * ib + 8 * q4 + 4 * g + r4) p = 0.f;
+                if (MASK && kq > i0 + 32 * ib + 8 * q4 + 4 * g + r4) p = 0.f;
                 pv[r] = p;
                 dsv[r] = p * __builtin_fmaf(da[ib][r], sE, -d4[q4][r4]);
                 if (ib == 0 && r4 == 3) read_stats(1, q4);
@@ -701,10 +720,12 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
         __syncthreads();   // tile t+1 has landed; every wave is done with tile t
     };
-    // Causal: only the first two query tiles reach above some wave's keys
-    // (a wave whose keys all follow such a tile computes it fully masked).
+    // Causal: only tiles whose first row precedes the block's last key
+    // position reach above some wave's keys (two tiles when Nq = Nk; a wave
+    // whose keys all follow such a tile computes it fully masked).
     // dK and dV sum over the G query heads that share this K/V head.
-    const int t_free = CAUSAL ? min(t0 + 2, n_tiles) : t0;
+    const int last_kq = k0 + BKV - 1 - off;
+    const int t_free = CAUSAL ? min(max((max(last_kq, 0) + BQ - 1) / BQ, t0), n_tiles) : t0;
     for (int gq = 0; gq < G; ++gq) {
         for (int t = t0; t < t_free; ++t) iteration(gq, t, BoolTag<true>{});
         for (int t = t_free; t < n_tiles; ++t) iteration(gq, t, BoolTag<false>{});
@@ -715,7 +736,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         agpr_settle(acc_dk[nb]);
         agpr_settle(acc_dv[nb]);
     }
-    if (kj < N) {
+    if (kj < Nk) {
         const float fk = scale / (sQ * sE), fv = 1.f / sDO;
         uint16_t* dkrow = dK + head + (size_t)kj * D;
         uint16_t* dvrow = dV + head + (size_t)kj * D;
@@ -740,35 +761,37 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 constexpr int kBwdWaves = 4;
 
 static BwdWorkspace ws_of(const BwdArgs& a) {
-    return bwd_workspace_layout(a.B, a.H, a.Hkv, a.N, a.d);
+    return bwd_workspace_layout(a.B, a.H, a.Hkv, a.N, a.Nk, a.d);
 }
 
 template <typename T>
 static T* ws_ptr(const BwdArgs& a, size_t off) { return (T*)((char*)a.workspace + off); }
 
-static int n_tiles64(const BwdArgs& a) { return (a.N + 63) / 64; }
+static int q_tiles64(const BwdArgs& a) { return (a.N + 63) / 64; }
+static int k_tiles64(const BwdArgs& a) { return (a.Nk + 63) / 64; }
 
 template <int D>
 static hipError_t launch_prepare_t(const BwdArgs& a) {
     const BwdWorkspace w = ws_of(a);
     const int BH = a.B * a.H, BHkv = a.B * a.Hkv, G = a.H / a.Hkv;
-    const int chunks = (a.N + kScaleRows - 1) / kScaleRows;
-    const int T = n_tiles64(a);
+    const int chunks = bwd_scale_chunks(a.N, a.Nk);
+    const int Tq = q_tiles64(a), Tk = k_tiles64(a);
     uint32_t* partial = ws_ptr<uint32_t>(a, w.partial);
     hipLaunchKernelGGL((bwd_absmax_kernel<D>), dim3((BH + BHkv) * chunks), dim3(256), 0,
                        a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                       (const uint16_t*)a.v, (const uint16_t*)a.dout, partial, BH, a.N, chunks);
+                       (const uint16_t*)a.v, (const uint16_t*)a.dout, partial, BH, a.N, a.Nk,
+                       chunks);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_scale_kernel, dim3((BH + 63) / 64), dim3(64), 0, a.stream,
                        (const uint32_t*)partial, ws_ptr<float>(a, w.scales), BH, G, chunks);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_image_kernel<D>), dim3((2 * BH + BHkv) * T), dim3(256), 0,
+    hipLaunchKernelGGL((bwd_image_kernel<D>), dim3(2 * BH * Tq + BHkv * Tk), dim3(256), 0,
                        a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                        (const uint16_t*)a.dout, ws_ptr<const float>(a, w.scales),
                        ws_ptr<char>(a, w.qt), ws_ptr<char>(a, w.ot), ws_ptr<char>(a, w.kt), BH,
-                       G, a.N, T);
+                       G, a.N, a.Nk, Tq, Tk);
     return hipGetLastError();
 }
 
@@ -782,8 +805,8 @@ static hipError_t launch_dq_t(const BwdArgs& a) {
                        a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                        (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse,
                        ws_ptr<const float>(a, w.scales), ws_ptr<const char>(a, w.kt),
-                       ws_ptr<float>(a, w.stats), (uint16_t*)a.dq, BH, a.H / a.Hkv, a.N,
-                       n_tiles64(a), a.scale * kLog2e, a.scale, nqb);
+                       ws_ptr<float>(a, w.stats), (uint16_t*)a.dq, BH, a.H / a.Hkv, a.N, a.Nk,
+                       q_tiles64(a), k_tiles64(a), a.scale * kLog2e, a.scale, nqb);
     return hipGetLastError();
 }
 
@@ -792,14 +815,14 @@ static hipError_t launch_dkdv_t(const BwdArgs& a) {
     constexpr int NW = kBwdWaves;
     const BwdWorkspace w = ws_of(a);
     const int BHkv = a.B * a.Hkv;
-    const int nkb = (a.N + NW * 32 - 1) / (NW * 32);
+    const int nkb = (a.Nk + NW * 32 - 1) / (NW * 32);
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, CAUSAL>), dim3(nkb * BHkv), dim3(NW * 64), 0,
                        a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                        (const uint16_t*)a.v, (const uint16_t*)a.dout,
                        ws_ptr<const float>(a, w.scales), ws_ptr<const float>(a, w.stats),
                        ws_ptr<const char>(a, w.qt), ws_ptr<const char>(a, w.ot),
-                       (uint16_t*)a.dk, (uint16_t*)a.dv, BHkv, a.H / a.Hkv, a.N, n_tiles64(a),
-                       a.scale * kLog2e, a.scale);
+                       (uint16_t*)a.dk, (uint16_t*)a.dv, BHkv, a.H / a.Hkv, a.N, a.Nk,
+                       q_tiles64(a), a.scale * kLog2e, a.scale);
     return hipGetLastError();
 }
 

@@ -35,7 +35,7 @@ struct BwdArgs {
     void* dk;
     void* dv;
     void* workspace;
-    int B, H, Hkv, N, d;
+    int B, H, Hkv, N, Nk, d;   // N query rows, Nk keys (bottom-right causal alignment)
     bool causal;
     float scale;
     hipStream_t stream;
@@ -44,25 +44,27 @@ struct BwdArgs {
 // Rows per chunk of the max-abs pre-pass of the backward.
 constexpr int kScaleRows = 256;
 
-// Byte offsets of the backward workspace blocks (T = ceil(N / 64) tiles of
-// 64 rows per head; an image is the byte layout of one transposed LDS tile;
-// BH = B*H query heads, BHkv = B*Hkv K/V heads):
+// Byte offsets of the backward workspace blocks (Tq = ceil(Nq / 64) and
+// Tk = ceil(Nk / 64) tiles of 64 rows per head; an image is the byte layout
+// of one transposed LDS tile; BH = B*H query heads, BHkv = B*Hkv K/V heads;
+// chunks = ceil(max(Nq, Nk) / kScaleRows)):
 //   scales  fp32 [BH][4]             power-of-two factors for Q, K, V, dO as
 //                                    seen by each query head (Q and dO common
 //                                    to the query heads of one K/V head)
 //   partial u32  [BH + BHkv][chunks][2] per-chunk largest |x| (bf16 magnitude
 //                                    bits): (Q, dO) per query head, then (K, V)
 //                                    per K/V head
-//   stats   fp32 [BH][T][128]        per query tile: lse*log2(e) of its 64 rows,
+//   stats   fp32 [BH][Tq][128]       per query tile: lse*log2(e) of its 64 rows,
 //                                    then sE*D (sE = s_dO*s_V); from the dQ pass
-//   qt      fp16 [BH][T][64*d]       images of (s_Q Q)^T, one per 64-row tile
-//   ot      fp16 [BH][T][64*d]       images of (s_dO dO)^T
-//   kt      fp16 [BHkv][T][64*d]     images of (s_K K)^T
+//   qt      fp16 [BH][Tq][64*d]      images of (s_Q Q)^T, one per 64-row tile
+//   ot      fp16 [BH][Tq][64*d]      images of (s_dO dO)^T
+//   kt      fp16 [BHkv][Tk][64*d]    images of (s_K K)^T
 struct BwdWorkspace {
     size_t scales, partial, stats, qt, ot, kt, total;
 };
-BwdWorkspace bwd_workspace_layout(long long B, long long H, long long Hkv, long long N,
-                                  long long d);
+BwdWorkspace bwd_workspace_layout(long long B, long long H, long long Hkv, long long Nq,
+                                  long long Nk, long long d);
+int bwd_scale_chunks(long long Nq, long long Nk);
 
 // Decoding: Nq query rows per query head (the last Nq positions) against Nk
 // keys; q, o [B][H][Nq][d], k, v [B][Hkv][Nk][d], lse [B][H][Nq].

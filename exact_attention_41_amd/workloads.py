@@ -187,14 +187,17 @@ def rect_flops(w: DecodeWorkload) -> float:
     return 4.0 * w.d * w.B * w.H * elems
 
 
-def make_decode_inputs(B: int, H: int, Hkv: int, Nq: int, Nk: int, d: int, seed: int) -> Inputs:
-    """Decoding inputs: q [B,H,Nq,d], then k and v [B,Hkv,Nk,d], drawn in that
-    order with the recipe of the module docstring and rounded to bf16."""
+def make_decode_inputs(B: int, H: int, Hkv: int, Nq: int, Nk: int, d: int, seed: int,
+                       with_do: bool = False) -> Inputs:
+    """Decoding (and rectangular) inputs: q [B,H,Nq,d], then k and v
+    [B,Hkv,Nk,d] (then dO [B,H,Nq,d]), drawn in that order with the recipe of
+    the module docstring and rounded to bf16."""
     rng = np.random.Generator(np.random.PCG64(seed))
     q = rng.standard_normal((B, H, Nq, d), dtype=np.float32)
     k = rng.standard_normal((B, Hkv, Nk, d), dtype=np.float32)
     v = rng.standard_normal((B, Hkv, Nk, d), dtype=np.float32)
-    return Inputs(bf16_round(q), bf16_round(k), bf16_round(v), None, "bf16")
+    do = bf16_round(rng.standard_normal((B, H, Nq, d), dtype=np.float32)) if with_do else None
+    return Inputs(bf16_round(q), bf16_round(k), bf16_round(v), do, "bf16")
 
 
 def bf16_round(x: np.ndarray) -> np.ndarray:

@@ -205,6 +205,30 @@ fa_status_t fa_bwd_gqa(const void* q, const void* k, const void* v, const void* 
                        hipStream_t stream);
 
 /*
+ * Backward of fa_fwd_rect: Nq query rows against Nk keys per head, query row
+ * i at sequence position Nk - Nq + i (causal: bottom-right alignment).
+ *   q, o, dout, dq  bf16 [B][H][Nq][d]; lse fp32 [B][H][Nq], fa_fwd_rect's
+ *                   (rows that keep no key have lse = -inf and get dq = 0).
+ *   k, v, dk, dv    bf16 [B][Hkv][Nk][d]; dk and dv of a K/V head sum over
+ *                   its query heads as in fa_bwd_gqa.
+ *   workspace       fa_bwd_rect_workspace_size(B, H, Hkv, Nq, Nk, d) bytes
+ *                   (0 if a size is not positive, d unsupported or Hkv does
+ *                   not divide H), 256-byte aligned.
+ * Nq == Nk is fa_bwd_gqa. B or H == 0 (or Nq == Nk == 0) is a no-op; exactly
+ * one of Nq, Nk zero, or Nk < 0 -> FA_ERR_INVALID_ARG (with no query rows
+ * the gradients of k and v are zero: the library leaves them to the
+ * caller); Nk beyond 2^26 -> FA_ERR_UNSUPPORTED. Everything else as for
+ * fa_bwd.
+ */
+size_t fa_bwd_rect_workspace_size(int B, int H, int Hkv, int Nq, int Nk, int d);
+
+fa_status_t fa_bwd_rect(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        void* workspace, size_t workspace_bytes,
+                        int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                        hipStream_t stream);
+
+/*
  * Decoding: attention of the last Nq positions of a sequence against all of
  * its Nk keys (Nq <= Nk), the step an inference system repeats per token,
  * with the keys split into ranges whose partial results are merged with the

@@ -109,16 +109,18 @@ def head_probs(q: np.ndarray, k: np.ndarray, causal: bool, scale: float) -> np.n
 
 
 def head_bwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
-             causal: bool, scale: float
+             causal: bool, scale: float, pos0: int = 0
              ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
-    """Backward for one head: returns (dq, dk, dv), each [N, d]."""
+    """Backward for one head: q, do [Nq, d], k, v [Nk, d]; returns (dq, dk, dv)
+    shaped like q, k, v. Query row i sits at position pos0 + i as in head_fwd
+    (a row that keeps no key has P = 0 and contributes nothing)."""
     n = q.shape[0]
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
     for r0 in range(0, n, ROW_BLOCK):
         rr = np.arange(r0, min(n, r0 + ROW_BLOCK))
-        p, _ = _softmax_rows(_scores(q[rr], k, rr, causal, scale))
+        p, _ = _softmax_rows(_scores(q[rr], k, rr + pos0, causal, scale))
         dv += p.T @ do[rr]
         dp = do[rr] @ v.T
         dsum = np.sum(p * dp, axis=1)
@@ -129,14 +131,15 @@ def head_bwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
 
 
 def head_dq_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
-                 causal: bool, scale: float, rows: np.ndarray) -> np.ndarray:
+                 causal: bool, scale: float, rows: np.ndarray, pos0: int = 0) -> np.ndarray:
     """dQ of selected query rows of one head (the backward formulas above,
-    restricted to those rows: row i of dQ only needs row i of P and dP)."""
+    restricted to those rows: row i of dQ only needs row i of P and dP).
+    Query row i sits at position pos0 + i as in head_fwd."""
     rows = np.asarray(rows)
     dq = np.zeros((len(rows), q.shape[1]))
     for r0 in range(0, len(rows), ROW_BLOCK):
         rr = rows[r0:r0 + ROW_BLOCK]
-        p, _ = _softmax_rows(_scores(q[rr], k, rr, causal, scale))
+        p, _ = _softmax_rows(_scores(q[rr], k, rr + pos0, causal, scale))
         dp = do[rr] @ v.T
         dsum = np.sum(p * dp, axis=1)
         ds = p * (dp - dsum[:, None])
@@ -247,6 +250,35 @@ def rect_fwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool, scale: f
     if heads is None:
         return o.reshape(B, H, Nq, v.shape[-1]), lse.reshape(B, H, Nq)
     return o, lse
+
+
+def rect_bwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, causal: bool,
+             scale: float, heads: Optional[Sequence[Tuple[int, int]]] = None,
+             workers: Optional[int] = 1):
+    """Backward of rect_fwd: q, do [B, H, Nq, d], k, v [B, Hkv, Nk, d], query
+    row i at position Nk - Nq + i. Without ``heads``: dQ [B, H, Nq, d] and
+    dK, dV [B, Hkv, Nk, d] (a shared K/V head's gradient summed over its query
+    heads); with ``heads``: each listed query head's own dQ, dK, dV, stacked,
+    before any summing."""
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    G = _group(H, k)
+    hs = _heads(B, H, heads)
+
+    def one(bh):
+        b, h = bh
+        return head_bwd(q[b, h], k[b, h // G], v[b, h // G], do[b, h], causal, scale,
+                        pos0=Nk - Nq)
+
+    res = _pool_map(one, hs, workers)
+    dq = np.stack([r[0] for r in res])
+    dk = np.stack([r[1] for r in res])
+    dv = np.stack([r[2] for r in res])
+    if heads is None:
+        kv_shape = (B, H // G, G, Nk, d)
+        return (dq.reshape(B, H, Nq, d), dk.reshape(kv_shape).sum(axis=2),
+                dv.reshape(kv_shape).sum(axis=2))
+    return dq, dk, dv
 
 
 def decode_fwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool, scale: float,

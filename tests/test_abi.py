@@ -196,6 +196,37 @@ def test_rect_forward_arguments(lib):
     assert f(B=0) == OK
 
 
+def test_rect_backward_arguments(lib):
+    """fa_bwd_rect: sizes of the rectangular backward and its argument errors."""
+    ws = lib.fa_bwd_rect_workspace_size(1, 4, 2, 100, 300, 128)
+    assert ws > 0 and ws % 256 == 0
+    assert lib.fa_bwd_rect_workspace_size(2, 32, 8, 4096, 4096, 128) == \
+        lib.fa_bwd_gqa_workspace_size(2, 32, 8, 4096, 128)
+    # more keys: more K images; more query rows: more Q/dO images and statistics
+    assert lib.fa_bwd_rect_workspace_size(1, 4, 2, 100, 3000, 128) > ws
+    assert lib.fa_bwd_rect_workspace_size(1, 4, 2, 1000, 300, 128) > ws
+    assert lib.fa_bwd_rect_workspace_size(1, 4, 2, 0, 300, 128) == 0
+    assert lib.fa_bwd_rect_workspace_size(1, 4, 2, 100, 0, 128) == 0
+    assert lib.fa_bwd_rect_workspace_size(1, 4, 3, 100, 300, 128) == 0
+    assert lib.fa_bwd_rect_workspace_size(1, 4, 2, 100, 300, 256) == 0
+
+    def b(B=1, H=4, Hkv=2, Nq=100, Nk=300, d=128, ws_bytes=ws, wsp=0x200000, dk=A):
+        return lib.fa_bwd_rect(A, A, A, A, A, A, A, dk, A, wsp, ws_bytes, B, H, Hkv, Nq, Nk, d,
+                               1, 0.088, None)
+    assert b(Nk=-1) == INVALID
+    assert b(Nk=0) == INVALID                   # query rows but no keys
+    assert b(Nq=0) == INVALID                   # keys whose gradients would be left unwritten
+    assert b(Hkv=3) == INVALID
+    assert b(dk=None) == INVALID
+    assert b(d=256) == UNSUPPORTED
+    assert b(Nk=(1 << 26) + 1) == UNSUPPORTED
+    assert b(dk=MIS) == UNSUPPORTED
+    assert b(ws_bytes=ws - 1) == WORKSPACE
+    assert b(wsp=None) == WORKSPACE
+    assert b(Nq=0, Nk=0, wsp=None, ws_bytes=0) == OK
+    assert b(B=0, wsp=None, ws_bytes=0) == OK
+
+
 def test_python_binding_refuses_without_gpu_tensors():
     torch = pytest.importorskip("torch")
     import exact_attention_41_amd as fa

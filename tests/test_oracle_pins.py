@@ -448,6 +448,121 @@ def test_rect_against_square_problem(causal, Nq, Nk):
             np.testing.assert_allclose(lse[0, h], lb, atol=1e-13)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Nq,Nk", [(3, 8), (8, 3), (1, 5), (5, 1), (6, 6)])
+def test_rect_gradients_match_finite_differences(causal, Nq, Nk):
+    """The rectangular backward against central differences of the
+    rectangular forward's loss sum(O * dO), shared K/V head included (two
+    query heads on one K/V head), every element of dQ, dK, dV."""
+    r = _rng(500 + 10 * Nq + Nk + int(causal))
+    B, H, Hkv, d = 1, 2, 1, 3
+    q, do = r.standard_normal((B, H, Nq, d)), r.standard_normal((B, H, Nq, d))
+    k, v = r.standard_normal((B, Hkv, Nk, d)), r.standard_normal((B, Hkv, Nk, d))
+    scale = 0.6
+    dq, dk, dv = ora.rect_bwd(q, k, v, do, causal, scale)
+
+    def loss(qq, kk, vv):
+        o, _ = ora.rect_fwd(qq, kk, vv, causal, scale)
+        return float(np.sum(o * do))
+
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for idx in np.ndindex(*x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            a_p = {"q": q, "k": k, "v": v}
+            a_m = dict(a_p)
+            a_p[name], a_m[name] = xp, xm
+            fd = (loss(a_p["q"], a_p["k"], a_p["v"]) - loss(a_m["q"], a_m["k"], a_m["v"])) / (2 * h)
+            assert abs(fd - g[idx]) <= 1e-6 * max(1.0, abs(g[idx])), (name, idx, fd, g[idx])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Nq,Nk", [(3, 9), (1, 4), (7, 7), (2, 16)])
+def test_rect_backward_against_square_problem(causal, Nq, Nk):
+    """Nq <= Nk: the gradients of the square problem of size Nk whose last Nq
+    query rows are these and whose other rows carry dO = 0: dK, dV equal, dQ
+    equals its last Nq rows (and its other rows are 0)."""
+    r = _rng(600 + 10 * Nq + Nk)
+    B, H, Hkv, d = 1, 4, 2, 5
+    q, do = r.standard_normal((B, H, Nq, d)), r.standard_normal((B, H, Nq, d))
+    k, v = r.standard_normal((B, Hkv, Nk, d)), r.standard_normal((B, Hkv, Nk, d))
+    dq, dk, dv = ora.rect_bwd(q, k, v, do, causal, 0.45)
+    fq = r.standard_normal((B, H, Nk, d))
+    fq[:, :, Nk - Nq:] = q
+    fdo = np.zeros((B, H, Nk, d))
+    fdo[:, :, Nk - Nq:] = do
+    sq, sk, sv = ora.attention_bwd(fq, k, v, fdo, causal, 0.45)
+    np.testing.assert_allclose(dq, sq[:, :, Nk - Nq:], atol=1e-13)
+    np.testing.assert_array_equal(sq[:, :, :Nk - Nq], 0.0)
+    np.testing.assert_allclose(dk, sk, atol=1e-13)
+    np.testing.assert_allclose(dv, sv, atol=1e-13)
+
+
+@pytest.mark.parametrize("Nq,Nk", [(5, 12), (12, 12), (1, 7)])
+def test_rect_backward_against_torch_sdpa_bottom_right_mask(Nq, Nk):
+    """torch fp64 scaled_dot_product_attention with an explicit boolean mask
+    that keeps key j for query row i iff j <= Nk - Nq + i, and autograd."""
+    torch = pytest.importorskip("torch")
+    r = _rng(700 + Nq + Nk)
+    B, H, d = 2, 2, 6
+    q, do = r.standard_normal((B, H, Nq, d)), r.standard_normal((B, H, Nq, d))
+    k, v = r.standard_normal((B, H, Nk, d)), r.standard_normal((B, H, Nk, d))
+    scale = 1.0 / math.sqrt(d)
+    keep = torch.tensor(np.arange(Nk)[None, :] <= (Nk - Nq + np.arange(Nq))[:, None])
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    to = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=keep, scale=scale)
+    to.backward(torch.tensor(do))
+    o, _ = ora.rect_fwd(q, k, v, True, scale)
+    dq, dk, dv = ora.rect_bwd(q, k, v, do, True, scale)
+    np.testing.assert_allclose(o, to.detach().numpy(), atol=1e-12)
+    np.testing.assert_allclose(dq, tq.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), atol=1e-12)
+
+
+def test_rect_backward_rows_without_keys():
+    """Causal with Nq > Nk: the first Nq - Nk rows keep no key, so their dQ is
+    0 and they add nothing to dK, dV; the rest is the square problem of size
+    Nk."""
+    r = _rng(710)
+    Nq, Nk, d = 11, 4, 3
+    q, do = r.standard_normal((1, 1, Nq, d)), r.standard_normal((1, 1, Nq, d))
+    k, v = r.standard_normal((1, 1, Nk, d)), r.standard_normal((1, 1, Nk, d))
+    dq, dk, dv = ora.rect_bwd(q, k, v, do, True, 0.8)
+    np.testing.assert_array_equal(dq[:, :, :Nq - Nk], 0.0)
+    sq, sk, sv = ora.attention_bwd(q[:, :, Nq - Nk:], k, v, do[:, :, Nq - Nk:], True, 0.8)
+    np.testing.assert_allclose(dq[:, :, Nq - Nk:], sq, atol=1e-13)
+    np.testing.assert_allclose(dk, sk, atol=1e-13)
+    np.testing.assert_allclose(dv, sv, atol=1e-13)
+
+
+def test_rect_pins_catch_top_left_alignment(monkeypatch):
+    """A backward that aligns the mask top-left (ignores the row offset)
+    fails the finite-difference pin."""
+    orig = ora.head_bwd
+
+    def head_bwd(q, k, v, do, causal, scale, pos0=0):
+        return orig(q, k, v, do, causal, scale, 0)
+
+    monkeypatch.setattr(ora, "head_bwd", head_bwd)
+    with pytest.raises(AssertionError):
+        test_rect_gradients_match_finite_differences(True, 3, 8)
+
+
+def test_rect_dq_rows_match_full_backward():
+    r = _rng(711)
+    Nq, Nk, d = 9, 30, 4
+    q, do = r.standard_normal((Nq, d)), r.standard_normal((Nq, d))
+    k, v = r.standard_normal((Nk, d)), r.standard_normal((Nk, d))
+    rows = np.array([0, 4, 8])
+    for causal in (False, True):
+        dq, _, _ = ora.head_bwd(q, k, v, do, causal, 0.4, pos0=Nk - Nq)
+        got = ora.head_dq_rows(q, k, v, do, causal, 0.4, rows, pos0=Nk - Nq)
+        np.testing.assert_allclose(got, dq[rows], rtol=0, atol=1e-13)
+
+
 # ------------------------------------------------------ planted-mistake checks
 def _brute_mismatch():
     r = _rng(16)
