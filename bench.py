@@ -12,10 +12,13 @@ Prints exactly one JSON line (on rank 0). Options:
   --gpus N        only N=1 is meaningful: this path runs on one GPU
   --steps K       timed steps (default 20)
   --warmup W      untimed warm-up steps (default 5)
-  --no-sweep      skip the forward-only timing of the other workloads (head
-                  sizes 64, 128 and 256), the shared-K/V-head (grouped-query)
-                  workload, decoding, the chunked-prefill (Nq != Nk) forward
-                  and the e4m3 (fp8) forward
+  --no-sweep      skip the timing of the other workloads: the forward at head
+                  sizes 64, 128 and 256, the shared-K/V-head (grouped-query)
+                  forward and backward, decoding, the chunked-prefill
+                  (Nq != Nk) forward and backward, and the e4m3 (fp8) forward.
+                  Each is timed warm and cold (CallTimer: median over >= 20
+                  calls and >= 200 ms, the cold run with 512 MiB written
+                  between calls)
   --no-cpu        skip the CPU oracle baseline
   --counters      instead: run two steps and a plain 512 MiB device copy and
                   exit (the program to run under rocprofv3 --pmc FETCH_SIZE,
@@ -64,6 +67,57 @@ def kernel_source_sha() -> str:
 
 def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
+
+
+WARMUP_CALLS = 5
+MIN_CALLS = 20
+MIN_TIMED_MS = 200.0
+FLUSH_BYTES = 512 << 20         # written between calls for the cold (L2/MALL-flushed) time
+
+
+class CallTimer:
+    """Median device time of one call: WARMUP_CALLS untimed calls, then at
+    least MIN_CALLS timed ones covering at least MIN_TIMED_MS in total, each
+    bracketed by events on the current stream. ``cold`` writes FLUSH_BYTES
+    before every timed call (outside its events), so the call starts with the
+    2nd-level caches and the last-level cache holding nothing of its inputs."""
+
+    def __init__(self, dev):
+        import torch
+        self.torch = torch
+        self.dev = dev
+        self.flush_buf = None
+
+    def _calls(self, fn, n, flush):
+        torch = self.torch
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+        for i in range(n):
+            if flush:
+                self.flush_buf.fill_(i & 0xFF)
+            ev[i][0].record()
+            fn()
+            ev[i][1].record()
+        torch.cuda.synchronize(self.dev)
+        return [a.elapsed_time(b) for a, b in ev]
+
+    def median(self, fn, cold: bool = False):
+        torch = self.torch
+        if cold and self.flush_buf is None:
+            self.flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=self.dev)
+        for _ in range(WARMUP_CALLS):
+            fn()
+        probe = self._calls(fn, 3, cold)
+        est = max(sorted(probe)[1], 1e-3)
+        n = min(max(MIN_CALLS, int(MIN_TIMED_MS / est) + 1), 5000)
+        times = sorted(self._calls(fn, n, cold))
+        return times[len(times) // 2], n
+
+    def both(self, fn):
+        """(warm median ms, cold median ms, timed calls of the warm run)."""
+        warm, n = self.median(fn)
+        cold, _ = self.median(fn, cold=True)
+        return warm, cold, n
 
 
 # ---------------------------------------------------------------------------
@@ -117,7 +171,11 @@ def gpu_step_timing(w, steps: int, warmup: int):
     return ms_per_step, per_kernel
 
 
-def gpu_forward_sweep(names, iters=10, warmup=3):
+def gpu_forward_sweep(names):
+    """bf16 forward of each workload: warm and cold medians (CallTimer), and
+    the device memory one call takes beyond its inputs and outputs (free
+    memory before and after the call, and torch's allocation peak): the
+    forward keeps no N x N buffer, so both are expected to be 0."""
     import torch
 
     import exact_attention_41_amd as fa
@@ -125,27 +183,35 @@ def gpu_forward_sweep(names, iters=10, warmup=3):
 
     out = []
     dev = torch.device("cuda:0")
+    timer = CallTimer(dev)
     for name in names:
         w = wl.WORKLOADS[name] if name in wl.WORKLOADS else wl.WIDE_WORKLOADS[name]
         inp = wl.make_inputs(w.B, w.H, w.N, w.d, "bf16", w.seed, w.qk_mult)
         q, k, v = (wl.to_device(x, "bf16", dev) for x in (inp.q, inp.k, inp.v))
         o = torch.empty_like(q)
         lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
-        for _ in range(warmup):
+
+        def call():
             fa.fa_fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
-        times = []
-        for i in range(iters):
-            ev[i].record()
-            fa.fa_fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
-            ev[i + 1].record()
+
+        med, cold, n = timer.both(call)
         torch.cuda.synchronize(dev)
-        times = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(iters))
-        med = times[len(times) // 2]
+        torch.cuda.reset_peak_memory_stats(dev)
+        alloc0 = torch.cuda.memory_allocated(dev)
+        free0 = torch.cuda.mem_get_info(dev)[0]
+        call()
+        torch.cuda.synchronize(dev)
+        free1 = torch.cuda.mem_get_info(dev)[0]
+        extra = {"free_bytes_delta": int(free0 - free1),
+                 "torch_peak_delta": int(torch.cuda.max_memory_allocated(dev) - alloc0)}
         tf = w.fwd_flops() / (med * 1e-3) / 1e12
+        ctf = w.fwd_flops() / (cold * 1e-3) / 1e12
         out.append({"workload": name, "pass": "fwd", "ms": round(med, 4),
-                    "tflops": round(tf, 1), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
-        log(f"  fwd {name}: {med:.3f} ms  {tf:.1f} TFLOP/s  {100 * tf / PEAK_BF16_TFLOPS:.1f}%")
+                    "tflops": round(tf, 1), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                    "cold_ms": round(cold, 4), "cold_tflops": round(ctf, 1), "calls": n,
+                    "extra_device_memory": extra})
+        log(f"  fwd {name}: {med:.3f} ms  {tf:.1f} TFLOP/s  {100 * tf / PEAK_BF16_TFLOPS:.1f}%  "
+            f"(cold {cold:.3f} ms; extra memory {extra})")
         del q, k, v, o, lse
     return out
 
@@ -211,9 +277,9 @@ def write_traffic(fetch_dir: str, write_dir: str) -> int:
     return 0
 
 
-def gpu_gqa_timing(names, iters=10, warmup=3):
+def gpu_gqa_timing(names):
     """Forward and backward of the shared-K/V-head workloads (fa_fwd_gqa,
-    fa_bwd_gqa), median of ``iters`` calls each; flops counted as for the
+    fa_bwd_gqa), warm and cold medians (CallTimer); flops counted as for the
     other workloads (over the H query heads)."""
     import torch
 
@@ -222,6 +288,7 @@ def gpu_gqa_timing(names, iters=10, warmup=3):
 
     out = []
     dev = torch.device("cuda:0")
+    timer = CallTimer(dev)
     for name in names:
         w = wl.GQA_WORKLOADS[name]
         inp = wl.workload_inputs(w)
@@ -239,34 +306,26 @@ def gpu_gqa_timing(names, iters=10, warmup=3):
             fa.fa_bwd_gqa(q, k, v, o, do, lse, causal=w.causal, scale=w.scale, dq=dq, dk=dk,
                           dv=dv, workspace=ws)
 
-        res = {}
-        for label, fn in (("fwd", fwd), ("bwd", bwd)):
-            for _ in range(warmup):
-                fn()
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
-            for i in range(iters):
-                ev[i].record()
-                fn()
-                ev[i + 1].record()
-            torch.cuda.synchronize(dev)
-            times = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(iters))
-            res[label] = times[len(times) // 2]
-        ftf = w.fwd_flops() / (res["fwd"] * 1e-3) / 1e12
-        btf = w.bwd_flops() / (res["bwd"] * 1e-3) / 1e12
+        res = {label: timer.both(fn) for label, fn in (("fwd", fwd), ("bwd", bwd))}
+        ftf = w.fwd_flops() / (res["fwd"][0] * 1e-3) / 1e12
+        btf = w.bwd_flops() / (res["bwd"][0] * 1e-3) / 1e12
         out.append({"workload": name, "H": w.H, "Hkv": w.kv_heads,
-                    "fwd_ms": round(res["fwd"], 4), "fwd_tflops": round(ftf, 1),
+                    "fwd_ms": round(res["fwd"][0], 4), "fwd_tflops": round(ftf, 1),
                     "fwd_frac_peak": round(ftf / PEAK_BF16_TFLOPS, 4),
-                    "bwd_ms": round(res["bwd"], 4), "bwd_tflops": round(btf, 1),
-                    "bwd_frac_peak": round(btf / PEAK_BF16_TFLOPS, 4)})
-        log(f"  gqa {name}: fwd {res['fwd']:.3f} ms {ftf:.1f} TFLOP/s, "
-            f"bwd {res['bwd']:.3f} ms {btf:.1f} TFLOP/s")
+                    "fwd_cold_ms": round(res["fwd"][1], 4),
+                    "bwd_ms": round(res["bwd"][0], 4), "bwd_tflops": round(btf, 1),
+                    "bwd_frac_peak": round(btf / PEAK_BF16_TFLOPS, 4),
+                    "bwd_cold_ms": round(res["bwd"][1], 4)})
+        log(f"  gqa {name}: fwd {res['fwd'][0]:.3f} ms {ftf:.1f} TFLOP/s, "
+            f"bwd {res['bwd'][0]:.3f} ms {btf:.1f} TFLOP/s (cold {res['fwd'][1]:.3f}, "
+            f"{res['bwd'][1]:.3f} ms)")
         del q, k, v, do, o, lse, dq, dk, dv, ws
     return out
 
 
-def gpu_rect_timing(names, iters=10, warmup=3):
+def gpu_rect_timing(names):
     """Forward and backward with Nq query rows against Nk keys (fa_fwd_rect,
-    fa_bwd_rect), median of ``iters`` calls each; flops counted over the
+    fa_bwd_rect), warm and cold medians (CallTimer); flops counted over the
     unmasked score elements (the backward as 2.5x the forward)."""
     import torch
 
@@ -275,6 +334,7 @@ def gpu_rect_timing(names, iters=10, warmup=3):
 
     out = []
     dev = torch.device("cuda:0")
+    timer = CallTimer(dev)
     for name in names:
         w = wl.RECT_WORKLOADS[name]
         inp = wl.make_decode_inputs(w.B, w.H, w.Hkv, w.Nq, w.Nk, w.d, w.seed, with_do=True)
@@ -292,27 +352,18 @@ def gpu_rect_timing(names, iters=10, warmup=3):
             fa.fa_bwd_rect(q, k, v, o, do, lse, causal=w.causal, scale=w.scale, dq=dq, dk=dk,
                            dv=dv, workspace=ws)
 
-        res = {}
-        for label, fn in (("fwd", fwd), ("bwd", bwd)):
-            for _ in range(warmup):
-                fn()
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
-            for i in range(iters):
-                ev[i].record()
-                fn()
-                ev[i + 1].record()
-            torch.cuda.synchronize(dev)
-            times = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(iters))
-            res[label] = times[len(times) // 2]
-        ftf = wl.rect_flops(w) / (res["fwd"] * 1e-3) / 1e12
-        btf = 2.5 * wl.rect_flops(w) / (res["bwd"] * 1e-3) / 1e12
+        res = {label: timer.both(fn) for label, fn in (("fwd", fwd), ("bwd", bwd))}
+        ftf = wl.rect_flops(w) / (res["fwd"][0] * 1e-3) / 1e12
+        btf = 2.5 * wl.rect_flops(w) / (res["bwd"][0] * 1e-3) / 1e12
         out.append({"workload": name, "Nq": w.Nq, "Nk": w.Nk, "H": w.H, "Hkv": w.Hkv,
-                    "ms": round(res["fwd"], 4), "tflops": round(ftf, 1),
+                    "ms": round(res["fwd"][0], 4), "tflops": round(ftf, 1),
                     "frac_peak": round(ftf / PEAK_BF16_TFLOPS, 4),
-                    "bwd_ms": round(res["bwd"], 4), "bwd_tflops": round(btf, 1),
-                    "bwd_frac_peak": round(btf / PEAK_BF16_TFLOPS, 4)})
-        log(f"  rect {name}: fwd {res['fwd']:.3f} ms {ftf:.1f} TFLOP/s "
-            f"{100 * ftf / PEAK_BF16_TFLOPS:.1f}%, bwd {res['bwd']:.3f} ms {btf:.1f} TFLOP/s "
+                    "cold_ms": round(res["fwd"][1], 4),
+                    "bwd_ms": round(res["bwd"][0], 4), "bwd_tflops": round(btf, 1),
+                    "bwd_frac_peak": round(btf / PEAK_BF16_TFLOPS, 4),
+                    "bwd_cold_ms": round(res["bwd"][1], 4)})
+        log(f"  rect {name}: fwd {res['fwd'][0]:.3f} ms {ftf:.1f} TFLOP/s "
+            f"{100 * ftf / PEAK_BF16_TFLOPS:.1f}%, bwd {res['bwd'][0]:.3f} ms {btf:.1f} TFLOP/s "
             f"{100 * btf / PEAK_BF16_TFLOPS:.1f}%")
         del q, k, v, do, o, lse, dq, dk, dv, ws
     return out
@@ -321,8 +372,8 @@ def gpu_rect_timing(names, iters=10, warmup=3):
 PEAK_FP8_TFLOPS = 2 * PEAK_BF16_TFLOPS    # dense e4m3 MFMA (AMD's 5.0 PFLOP/s)
 
 
-def gpu_fp8_timing(names, iters=10, warmup=3):
-    """Forward with e4m3 operands (fa_fwd_fp8), median of ``iters`` calls;
+def gpu_fp8_timing(names):
+    """Forward with e4m3 operands (fa_fwd_fp8), warm and cold medians;
     flops counted as for the bf16 forward, against the fp8 MFMA peak."""
     import torch
 
@@ -331,6 +382,7 @@ def gpu_fp8_timing(names, iters=10, warmup=3):
 
     out = []
     dev = torch.device("cuda:0")
+    timer = CallTimer(dev)
     for name in names:
         w = wl.FP8_WORKLOADS[name]
         inp = wl.make_fp8_inputs(w.B, w.H, w.H, w.N, w.N, w.d, w.seed)
@@ -342,20 +394,12 @@ def gpu_fp8_timing(names, iters=10, warmup=3):
             fa.fa_fwd_fp8(q, k, v, inp.dq, inp.dk, inp.dv, causal=w.causal, scale=w.scale,
                           out=o, lse=lse)
 
-        for _ in range(warmup):
-            call()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
-        for i in range(iters):
-            ev[i].record()
-            call()
-            ev[i + 1].record()
-        torch.cuda.synchronize(dev)
-        times = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(iters))
-        med = times[len(times) // 2]
+        med, cold, n = timer.both(call)
         tf = w.fwd_flops() / (med * 1e-3) / 1e12
         out.append({"workload": name, "pass": "fwd", "dtype": "e4m3", "ms": round(med, 4),
                     "tflops": round(tf, 1), "peak": round(PEAK_FP8_TFLOPS, 1),
-                    "frac_peak": round(tf / PEAK_FP8_TFLOPS, 4)})
+                    "frac_peak": round(tf / PEAK_FP8_TFLOPS, 4), "cold_ms": round(cold, 4),
+                    "calls": n})
         log(f"  fp8 {name}: {med:.3f} ms  {tf:.1f} TFLOP/s  {100 * tf / PEAK_FP8_TFLOPS:.1f}% "
             "of the fp8 peak")
         del q, k, v, o, lse
@@ -365,8 +409,9 @@ def gpu_fp8_timing(names, iters=10, warmup=3):
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 
 
-def gpu_decode_timing(names, iters=20, warmup=5):
-    """Split-K/V decoding (fa_decode): median time per call and the rate at
+def gpu_decode_timing(names):
+    """Split-K/V decoding (fa_decode): median time per call (warm; cold as
+    well) and the rate at
     which it moves its algorithmic bytes (K and V once, q, O, lse), against
     the HBM roof."""
     import torch
@@ -376,6 +421,7 @@ def gpu_decode_timing(names, iters=20, warmup=5):
 
     out = []
     dev = torch.device("cuda:0")
+    timer = CallTimer(dev)
     for name in names:
         w = wl.DECODE_WORKLOADS[name]
         inp = wl.make_decode_inputs(w.B, w.H, w.Hkv, w.Nq, w.Nk, w.d, w.seed)
@@ -384,26 +430,42 @@ def gpu_decode_timing(names, iters=20, warmup=5):
         lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
         ws = torch.empty(fa.fa_decode_workspace_size(w.B, w.H, w.Hkv, w.Nq, w.Nk, w.d),
                          dtype=torch.uint8, device=dev)
-        for _ in range(warmup):
+        def call():
             fa.fa_decode(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, workspace=ws)
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
-        for i in range(iters):
-            ev[i].record()
-            fa.fa_decode(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, workspace=ws)
-            ev[i + 1].record()
-        torch.cuda.synchronize(dev)
-        times = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(iters))
-        med = times[len(times) // 2]
+
+        med, cold, n = timer.both(call)
         gbs = w.io_bytes() / (med * 1e-3) / 1e9
         out.append({"workload": name, "B": w.B, "H": w.H, "Hkv": w.Hkv, "Nq": w.Nq, "Nk": w.Nk,
                     "d": w.d, "ms": round(med, 4), "bytes": w.io_bytes(),
                     "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
                                  "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                 "frac": round(gbs / HBM_PEAK_GBS, 4)}})
+                                 "frac": round(gbs / HBM_PEAK_GBS, 4)},
+                    "cold_ms": round(cold, 4), "calls": n})
         log(f"  decode {name}: {med * 1000:.1f} us  {gbs:.0f} GB/s  "
             f"{100 * gbs / HBM_PEAK_GBS:.1f}% of HBM")
         del q, k, v, o, lse, ws
     return out
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def environment() -> dict:
+    """Versions and hardware the numbers were taken with."""
+    import numpy
+    import torch
+    props = torch.cuda.get_device_properties(0)
+    return {"numpy": numpy.__version__, "torch": torch.__version__, "hip": torch.version.hip,
+            "gpu": props.gcnArchName, "compute_units": props.multi_processor_count,
+            "cpu_model": cpu_model()}
 
 
 # ---------------------------------------------------------------------------
@@ -446,6 +508,7 @@ def cpu_baseline(w, min_seconds: float = 10.0):
     per_head = (w.fwd_flops() + w.bwd_flops()) / len(heads)
     tflops = per_head * done / elapsed / 1e12
     return {"value": round(tflops, 5), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{done} of {len(heads)} heads of {w.name} (fwd+bwd, fp64 numpy, "
                       f"S/P materialised), {elapsed:.1f} s wall; counted flops as on the GPU"}
 
@@ -544,6 +607,10 @@ def main() -> int:
         "rect_workloads": rect,
         "fp8_workloads": fp8,
         "kernel_source_sha": kernel_source_sha(),
+        "timing": {"warmup_calls": WARMUP_CALLS, "min_calls": MIN_CALLS,
+                   "min_timed_ms": MIN_TIMED_MS, "statistic": "median",
+                   "cold": f"{FLUSH_BYTES >> 20} MiB written before each call"},
+        "environment": environment(),
     }
     if rank == 0:
         print(json.dumps(line), flush=True)
