@@ -13,7 +13,7 @@ Prints exactly one JSON line (on rank 0). Options:
   --steps K       timed steps (default 20)
   --warmup W      untimed warm-up steps (default 5)
   --no-sweep      skip the timing of the other workloads: the forward at head
-                  sizes 64, 128 and 256, the shared-K/V-head (grouped-query)
+                  sizes 64, 128 and 256, the backward at 256, the shared-K/V-head (grouped-query)
                   forward and backward, decoding, the chunked-prefill
                   (Nq != Nk) forward and backward, and the e4m3 (fp8) forward.
                   Each is timed warm and cold (CallTimer: median over >= 20
@@ -323,6 +323,43 @@ def gpu_gqa_timing(names):
     return out
 
 
+def gpu_wide_bwd_timing(names):
+    """Backward at head size 256 (fa_bwd, d = 256), warm and cold medians;
+    flops counted as 2.5x the forward's."""
+    import torch
+
+    import exact_attention_41_amd as fa
+    from exact_attention_41_amd import workloads as wl
+
+    out = []
+    dev = torch.device("cuda:0")
+    timer = CallTimer(dev)
+    for name in names:
+        w = wl.WIDE_WORKLOADS[name]
+        inp = wl.make_inputs(w.B, w.H, w.N, w.d, "bf16", w.seed, with_do=True)
+        q, k, v, do = (wl.to_device(x, "bf16", dev) for x in (inp.q, inp.k, inp.v, inp.do))
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+        fa.fa_fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = torch.empty(fa.fa_bwd_workspace_size(w.B, w.H, w.N, w.d), dtype=torch.uint8,
+                         device=dev)
+
+        def call():
+            fa.fa_bwd(q, k, v, o, do, lse, causal=w.causal, scale=w.scale, dq=dq, dk=dk, dv=dv,
+                      workspace=ws)
+
+        med, cold, n = timer.both(call)
+        tf = w.bwd_flops() / (med * 1e-3) / 1e12
+        out.append({"workload": name, "pass": "bwd", "ms": round(med, 4), "tflops": round(tf, 1),
+                    "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4), "cold_ms": round(cold, 4),
+                    "calls": n})
+        log(f"  bwd {name}: {med:.3f} ms  {tf:.1f} TFLOP/s  {100 * tf / PEAK_BF16_TFLOPS:.1f}% "
+            f"(cold {cold:.3f} ms)")
+        del q, k, v, do, o, lse, dq, dk, dv, ws
+    return out
+
+
 def gpu_rect_timing(names):
     """Forward and backward with Nq query rows against Nk keys (fa_fwd_rect,
     fa_bwd_rect), warm and cold medians (CallTimer); flops counted over the
@@ -576,6 +613,7 @@ def main() -> int:
     bwd_tf = bwd_f / (bwd_ms * 1e-3) / 1e12
     sweep = [] if args.no_sweep else gpu_forward_sweep(SWEEP)
     wide = [] if args.no_sweep else gpu_forward_sweep(list(wl.WIDE_WORKLOADS))
+    wide_bwd = [] if args.no_sweep else gpu_wide_bwd_timing(list(wl.WIDE_WORKLOADS))
     gqa = [] if args.no_sweep else gpu_gqa_timing(list(wl.GQA_WORKLOADS))
     decode = [] if args.no_sweep else gpu_decode_timing(list(wl.DECODE_WORKLOADS))
     rect = [] if args.no_sweep else gpu_rect_timing(list(wl.RECT_WORKLOADS))
@@ -602,6 +640,7 @@ def main() -> int:
         "cpu_baseline": cpu,
         "forward_workloads": sweep,
         "wide_workloads": wide,
+        "wide_bwd_workloads": wide_bwd,
         "gqa_workloads": gqa,
         "decode_workloads": decode,
         "rect_workloads": rect,

@@ -15,8 +15,8 @@ constexpr int kMaxN = 1 << 26;
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
-// Head sizes with kernels: 64 and 128 everywhere, 256 for the bf16 forward
-// and decoding.
+// Head sizes with kernels: 64 and 128 everywhere, 256 for everything but
+// the fp32 and fp8 forwards.
 bool head_dim_ok(int d, bool wide) { return d == 64 || d == 128 || (wide && d == 256); }
 
 // Shared size/scale checks. Returns FA_OK and sets *empty when B*H*N == 0.
@@ -142,7 +142,7 @@ fa_status_t fa_fwd_f32(const float* q, const float* k, const float* v, float* o,
 }
 
 size_t fa_bwd_rect_workspace_size(int B, int H, int Hkv, int Nq, int Nk, int d) {
-    if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || !head_dim_ok(d, false)) return 0;
+    if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || !head_dim_ok(d, true)) return 0;
     if (Hkv <= 0 || H % Hkv != 0) return 0;
     return fa::bwd_workspace_layout(B, H, Hkv, Nq, Nk, d).total;
 }
@@ -166,14 +166,14 @@ fa_status_t check_bwd(std::initializer_list<const void*> tensors, bool need_lse,
                       const void* workspace, size_t workspace_bytes, int B, int H, int Hkv,
                       int Nq, int Nk, int d, float scale, bool* empty) {
     if (Nk < 0) return FA_ERR_INVALID_ARG;
-    FA_TRY(check_common(B, H, Nq, d, scale, false, empty));
+    FA_TRY(check_common(B, H, Nq, d, scale, true, empty));
     FA_TRY(check_heads(H, Hkv));
     if (*empty && (B == 0 || H == 0 || Nk == 0)) return FA_OK;
     // Rows without keys, or keys without rows (whose gradients are zero and
     // left to the caller), are argument errors.
     if (*empty || Nk == 0) return FA_ERR_INVALID_ARG;
     bool unused = false;
-    FA_TRY(check_common(B, H, Nk, d, scale, false, &unused));
+    FA_TRY(check_common(B, H, Nk, d, scale, true, &unused));
     for (const void* p : tensors)
         if (!p) return FA_ERR_INVALID_ARG;
     if (need_lse && !lse) return FA_ERR_INVALID_ARG;

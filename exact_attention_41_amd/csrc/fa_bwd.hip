@@ -153,14 +153,14 @@ bwd_scale_kernel(const uint32_t* __restrict__ partial, float* __restrict__ scale
 }
 
 // ---------------------------------------------------------------------------
-// A 64-row, 16-bit tile [64][D] read as 4-row x 8-column micro-tiles and
-// written transposed ([D][64], the permuted row order and slot swizzle of
-// fa_device.hpp), to LDS or to a global image of that layout. With CVT the
-// source is bf16 and the copy is fp16 of the value times a power of two.
-// Rows at or past N repeat row N-1 (finite values that the consumers' masks
-// multiply by zero).
+// A 64-row, 16-bit tile [64][D] (source rows LD values apart) read as 4-row
+// x 8-column micro-tiles and written transposed ([D][64], the permuted row
+// order and slot swizzle of fa_device.hpp), to LDS or to a global image of
+// that layout. With CVT the source is bf16 and the copy is fp16 of the value
+// times a power of two. Rows at or past N repeat row N-1 (finite values that
+// the consumers' masks multiply by zero).
 // ---------------------------------------------------------------------------
-template <int D, int NT>
+template <int D, int NT, int LD = D>
 struct Tile64 {
     static constexpr int DCH = D / 8;
     static constexpr int UNITS = 16 * DCH;                 // 4x8 micro-tiles
@@ -177,7 +177,7 @@ struct Tile64 {
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) {
                     const int row = min(row0 + 4 * rg + rr, N - 1);
-                    r[it][rr] = *(const u32x4_t*)(src + (size_t)row * D + ch * 8);
+                    r[it][rr] = *(const u32x4_t*)(src + (size_t)row * LD + ch * 8);
                 }
             }
         }
@@ -216,17 +216,22 @@ struct Tile64 {
 };
 
 
-// Phase 1c: fp16 transposed images. One workgroup per (head, 64-row tile):
-// the first BH*Tq workgroups make the Q images of the query heads, the next
-// BH*Tq the dO images, the last BHkv*Tk the K images of the K/V heads.
-template <int D>
+// Phase 1c: fp16 transposed images. One workgroup per (head, 64-row tile,
+// column part): the first BH*Tq tiles are the Q images of the query heads,
+// the next BH*Tq the dO images, the last BHkv*Tk the K images of the K/V
+// heads. A head size DT above 128 is cut into NP = DT/128 parts of 128
+// columns, each imaged on its own ([tile][part] order), as the passes below
+// stage them.
+template <int DT>
 __global__ void __launch_bounds__(256)
 bwd_image_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                  const uint16_t* __restrict__ dO, const float* __restrict__ scales,
                  char* __restrict__ qt, char* __restrict__ ot, char* __restrict__ kt, int BH,
                  int G, int Nq, int Nk, int Tq, int Tk) {
-    using TileT = Tile64<D, 256>;
-    const int bid = blockIdx.x;
+    constexpr int D = DT > 128 ? 128 : DT;
+    constexpr int NP = DT / D;
+    using TileT = Tile64<D, 256, DT>;
+    const int bid = blockIdx.x / NP, part = blockIdx.x % NP;
     const int qblocks = BH * Tq;
     const int which = bid < qblocks ? 0 : (bid < 2 * qblocks ? 1 : 2);
     const int rel = bid - (which < 2 ? which * qblocks : 2 * qblocks);
@@ -237,8 +242,8 @@ bwd_image_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const float s = which == 0 ? scales[head * 4 + 0]
                   : (which == 1 ? scales[head * 4 + 3] : scales[head * G * 4 + 1]);
     TileT tl;
-    tl.load(src + (size_t)head * N * D, tile * 64, N, threadIdx.x);
-    tl.template store_transposed<true>(dst + ((size_t)head * T + tile) * TileT::BYTES,
+    tl.load(src + (size_t)head * N * DT + part * D, tile * 64, N, threadIdx.x);
+    tl.template store_transposed<true>(dst + (((size_t)head * T + tile) * NP + part) * TileT::BYTES,
                                        threadIdx.x, s);
 }
 
@@ -251,8 +256,12 @@ bwd_image_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 //   A~^T += K~^T (P*dP~)^T     A = (sK K)^T (LDS, fp16)    B = P*dP~ (fp16)
 //   B~^T += K~^T P^T           A = (sK K)^T (LDS, fp16)    B = P (fp16)
 // with sE = s_dO * s_V; finally dQ = scale/(sK sE) (A~ - D~ B~), D~ = sE D.
+// A head size DT above 128 runs as NC = DT/128 column parts: each key tile
+// is staged as NC steps of 128 columns of K and V, S and dP accumulate over
+// all of them, and each workgroup forms the dQ columns of one part (the
+// grid holds NC workgroups per query block; the first writes lse and D).
 // ---------------------------------------------------------------------------
-template <int D, int NW, bool CAUSAL>
+template <int DT, int NW, bool CAUSAL>
 __global__ void __launch_bounds__(NW * 64, 1)
 bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
@@ -260,9 +269,15 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               const char* __restrict__ kt_img, float* __restrict__ stats,
               uint16_t* __restrict__ dQ, int BH, int G, int N, int Nk, int T, int Tk,
               float c, float scale, int nqb) {
+    constexpr int D = DT > 128 ? 128 : DT;  // columns of one staged tile and of one dQ part
+    constexpr int NC = DT / D;              // column steps per key tile = dQ parts
+    // Above d = 128 the parked Q and dO fill the AGPR file with the sums:
+    // products that read them carry the VALU-write wait states.
+    constexpr bool WS = DT > 128;
     constexpr int BC = 64;
     constexpr int BQ = NW * 32;
-    constexpr int KS = D / 16;
+    constexpr int KS = D / 16;              // S (or dP) products per step and 32-key half
+    constexpr int KST = DT / 16;
     constexpr int NB = D / 32;
     constexpr int TB = 64 * D * 2;         // bytes of one 64-row tile
     constexpr int BLK = TB / 1024;         // its 1 KB staging blocks
@@ -275,12 +290,14 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const int g = lane >> 5, l32 = lane & 31;
     const int bid = blockIdx.x;
     const int bh = bid % BH;
-    const int qb = CAUSAL ? (nqb - 1 - bid / BH) : bid / BH;
-    const size_t head = (size_t)bh * (size_t)N * D;
-    const size_t kvhead = (size_t)(bh / G) * (size_t)Nk * D;  // K/V head of this query head
+    const int part = (bid / BH) % NC;      // dQ columns [D part, D part + D)
+    const int qbi = bid / (BH * NC);
+    const int qb = CAUSAL ? (nqb - 1 - qbi) : qbi;
+    const size_t head = (size_t)bh * (size_t)N * DT;
+    const size_t kvhead = (size_t)(bh / G) * (size_t)Nk * DT;  // K/V head of this query head
     const uint16_t* Kh = K + kvhead;
     const uint16_t* Vh = V + kvhead;
-    const char* kt_h = kt_img + (size_t)(bh / G) * Tk * TB;
+    const char* kt_h = kt_img + (size_t)(bh / G) * Tk * NC * TB;
     const int q0 = qb * BQ;
     const int wq0 = q0 + wave * 32;
     const int qi = wq0 + l32;             // this lane's query row
@@ -290,11 +307,11 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const float sV = scales[bh * 4 + 2], sDO = scales[bh * 4 + 3];
     const float sE = sDO * sV;
 
-    u32x4_t qf[KS], of[KS];
+    u32x4_t qf[KST], of[KST];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
+    for (int s = 0; s < KST; ++s) {
         if (qi < N) {
-            const size_t off = head + (size_t)qi * D + 16 * s + 8 * g;
+            const size_t off = head + (size_t)qi * DT + 16 * s + 8 * g;
             const u32x4_t qv = *(const u32x4_t*)(Q + off);
             const u32x4_t ov = *(const u32x4_t*)(dO + off);
 #pragma unroll
@@ -322,20 +339,21 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const int q_last = min(q0 + BQ, N) - 1 + off;      // last key position of the block
     const int n_tiles = CAUSAL ? min(n_all, max(q_last, 0) / BC + 1) : n_all;
 
-    // Key tile t into buffer buf: K and V rows (bf16, swizzled) and the
-    // (sK K)^T image, BLK 1 KB blocks each, spread over the NW waves; part k
-    // of NPART is one block of this wave. Past the last tile the buffer is
-    // filled from a valid tile and never read.
+    // Column step cs of key tile t into buffer buf: K and V rows (bf16,
+    // swizzled) and, for the last step, this part's (sK K)^T image, BLK 1 KB
+    // blocks each, spread over the NW waves; part k of the step's parts is
+    // one block of this wave. Past the last tile the buffer is filled from a
+    // valid tile and never read.
     constexpr int PPT = BLK / NW;            // blocks per wave and tensor
-    constexpr int NPART = 3 * PPT;
-    auto stage_part = [&](int t, int buf, int k) {
+    auto stage_part = [&](int t, int cs, int buf, int k) {
         lds_char* base = (lds_char*)(smem + buf * BUF);
         const int tensor = k / PPT, b = wave + NW * (k % PPT);
         if (tensor < 2)
-            stage_tile_block<D>(tensor == 0 ? Kh : Vh, base + (tensor == 0 ? OFF_K : OFF_V),
-                                t * BC, Nk, b, lane);
+            stage_tile_block<D, DT>((tensor == 0 ? Kh : Vh) + cs * D,
+                                    base + (tensor == 0 ? OFF_K : OFF_V), t * BC, Nk, b, lane);
         else
-            stage_image_block(kt_h + (size_t)min(t, Tk - 1) * TB, TB, base + OFF_KT, b, lane);
+            stage_image_block(kt_h + ((size_t)min(t, Tk - 1) * NC + part) * TB, TB,
+                              base + OFF_KT, b, lane);
     };
 
     // Lane-dependent LDS bases of buffer 0: pb[k], k < 8, for the row-major
@@ -351,27 +369,42 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         pb[8 + k] = s0 + tr_slot_offset(32 * (k & 1) + l32, 2 * (2 * (k >> 1) + g));
     }
 
+    {
+        constexpr int NP0 = (NC == 1 ? 3 : 2) * PPT;
 #pragma unroll
-    for (int k = 0; k < NPART; ++k) stage_part(0, 0, k);
+        for (int k = 0; k < NP0; ++k) stage_part(0, 0, 0, k);
+    }
     __syncthreads();
 
-    // One key tile: stage the next one, run the pipeline, move the bases.
+    // One key tile: NC column steps, each staging the next step (the next
+    // column step of this tile, or the first of the next tile), running its
+    // products and moving the bases to the other buffer.
     auto iteration = [&](int t, auto mask_tag) {
         const int j0 = t * BC;
+        f32x16_t sa[2], da[2];
 
-        // One software pipeline per key tile: S, dP of key half 0, then of
-        // half 1 (while half 0 is exponentiated), then the two dQ sums over
-        // four 16-key steps (the first two while half 1 is exponentiated);
-        // a dQ step's K~^T fragment feeds both sums. Fragments are read LA
-        // steps ahead; sched_barrier keeps that order. Only tiles that cross
-        // N or reach past a wave's first row take the mask.
-        auto tile_body = [&](auto mask_tag) {
+        // One column step as a software pipeline: S, dP of key half 0, then
+        // of half 1; in the last step (S and dP complete) half 0 is
+        // exponentiated under half 1's products, and the two dQ sums follow
+        // in four 16-key steps (the first two while half 1 is
+        // exponentiated); a dQ step's K~^T fragment feeds both sums.
+        // Fragments are read LA steps ahead; sched_barrier keeps that order.
+        // Only tiles that cross Nk or reach past a wave's first row take the
+        // mask.
+        auto step = [&](auto cs_tag, auto mask_tag) {
+            constexpr int CS = decltype(cs_tag)::value;
+            constexpr bool LAST = CS == NC - 1;
             constexpr bool MASK = decltype(mask_tag)::value;
             constexpr int NSD = 2 * KS;
-            constexpr int NOPS = 2 * NSD + 4 * NB;
+            constexpr int NOPS = LAST ? 2 * NSD + 4 * NB : 2 * NSD;
             constexpr int LA = kFragAhead;
             constexpr int EPO_A = 16 / NSD;
             constexpr int EPO_B = 16 / (2 * NB);
+            // the step staged meanwhile and its parts
+            constexpr int NCS = LAST ? 0 : CS + 1;
+            constexpr int NPART = (NCS == NC - 1 ? 3 : 2) * PPT;
+            const int nt = LAST ? t + 1 : t;
+            const int sidx = t * NC + CS;
             lds_char* const* bb = pb;
             auto frag = [&](int o) -> u32x4_t {
                 if (o < 2 * NSD) {
@@ -389,7 +422,6 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
             for (int o = 0; o < LA; ++o) fr[o] = frag(o);
 
-            f32x16_t sa[2], da[2];
             float pv[16], ev[16];
             u32x4_t pf[4], ef[4];
             auto softmax_elem = [&](int jb, int r) {
@@ -416,11 +448,13 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 if (o < 2 * NSD) {
                     const int jb = o / NSD, w = o % NSD, st = w >> 1;
                     f32x16_t& acc = (w & 1) ? da[jb] : sa[jb];
-                    const u32x4_t& bop = (w & 1) ? of[st] : qf[st];
-                    if (st == 0) mfma_bf16_first(acc, a, bop);
-                    else if (st == KS - 1) mfma_bf16_last(acc, a, bop);
-                    else mfma_bf16_next(acc, a, bop);
-                    if (jb == 1) {
+                    const u32x4_t& bop = (w & 1) ? of[CS * KS + st] : qf[CS * KS + st];
+                    // A chain's last product of a step carries the wait
+                    // states a VALU read of its result needs.
+                    if (CS == 0 && st == 0) mfma_bf16_first<WS>(acc, a, bop);
+                    else if (st == KS - 1) mfma_bf16_last<WS>(acc, a, bop);
+                    else mfma_bf16_next<WS>(acc, a, bop);
+                    if (LAST && jb == 1) {
 #pragma unroll
                         for (int e = 0; e < EPO_A; ++e) softmax_elem(0, w * EPO_A + e);
                     }
@@ -433,21 +467,23 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                         for (int e = 0; e < EPO_B; ++e) softmax_elem(1, w * EPO_B + e);
                     }
                 }
-                // The next tile's loads, in the VALU-free dQ steps.
-                constexpr int O0 = 2 * NSD + 2 * NB;
+                // The next step's loads: in the VALU-free dQ steps of the
+                // last column step, else among the S/dP products.
+                constexpr int O0 = LAST ? 2 * NSD + 2 * NB : 0;
 #pragma unroll
                 for (int k = 0; k < NPART; ++k)
-                    if (o == O0 + k * (NOPS - O0) / NPART) stage_part(t + 1, (t + 1) & 1, k);
+                    if (o == O0 + k * (NOPS - O0) / NPART) stage_part(nt, NCS, (sidx + 1) & 1, k);
                 __builtin_amdgcn_sched_barrier(0);
             }
-        };
-        tile_body(mask_tag);
-        // the bases move to the other buffer
-        const int step = (t & 1) ? -BUF : BUF;
+            // the bases move to the other buffer
+            const int stp = (sidx & 1) ? -BUF : BUF;
 #pragma unroll
-        for (int k = 0; k < 16; ++k) pb[k] += step;
+            for (int k = 0; k < 16; ++k) pb[k] += stp;
 
-        __syncthreads();   // tile t+1 has landed; every wave is done with tile t
+            __syncthreads();   // the next step has landed; every wave is done with this one
+        };
+        step(IntTag<0>{}, mask_tag);
+        if constexpr (NC > 1) step(IntTag<1>{}, mask_tag);
     };
     // Tiles from t_mask on cross Nk or reach past the key position of the
     // block's first row (a wave whose rows all precede such a tile computes
@@ -463,14 +499,14 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         agpr_settle(acc_b[nb]);
     }
     const float dt = sum_with_partner32(dsum);    // D~ = sE * D
-    if (g == 0 && qi < T * 64) {
+    if (part == 0 && g == 0 && qi < T * 64) {
         float* st = stats + ((size_t)bh * T + (qi >> 6)) * 128;
         st[qi & 63] = lse2;
         st[64 + (qi & 63)] = (qi < N) ? dt : 0.f;
     }
     if (qi < N) {
         const float f = scale / (sK * sE);
-        uint16_t* row = dQ + head + (size_t)qi * D;
+        uint16_t* row = dQ + head + (size_t)qi * DT + D * part;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -497,8 +533,12 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 //   dP  = dO V^T             A = dO tile (LDS, bf16)        B = V^T (VGPRs)
 //   dV^T += dO~^T P          A = (s_dO dO)^T (LDS, fp16)    B = P (fp16)
 //   dK^T += Q~^T dS~         A = (s_Q Q)^T (LDS, fp16)      B = dS~ = P (sE dP - sE D)
+// A head size DT above 128 runs as NC = DT/128 column parts, as in the dQ
+// pass: each query tile is staged as NC steps of 128 columns of Q and dO, S
+// and dP accumulate over all of them, and each workgroup forms the dK and dV
+// columns of one part.
 // ---------------------------------------------------------------------------
-template <int D, int NW, bool CAUSAL>
+template <int DT, int NW, bool CAUSAL>
 __global__ void __launch_bounds__(NW * 64, 1)
 bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
@@ -506,9 +546,16 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const char* __restrict__ qt_img, const char* __restrict__ ot_img,
                 uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int BHkv, int G, int N,
                 int Nk, int T, float c, float scale) {
+    constexpr int D = DT > 128 ? 128 : DT;  // columns of one staged tile and of one dK/dV part
+    constexpr int NC = DT / D;
+    // Above d = 128 the parked K and V fill the AGPR file with the sums: the
+    // compiler then copies some of them into AGPRs just before their
+    // products, which carry the VALU-write wait states.
+    constexpr bool WS = DT > 128;
     constexpr int BQ = 64;
     constexpr int BKV = NW * 32;
     constexpr int KS = D / 16;
+    constexpr int KST = DT / 16;
     constexpr int NB = D / 32;
     constexpr int TB = 64 * D * 2;
     constexpr int BLK = TB / 1024;
@@ -521,8 +568,9 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const int g = lane >> 5, l32 = lane & 31;
     const int bid = blockIdx.x;
     const int bkv = bid % BHkv;           // K/V head
-    const int kb = bid / BHkv;            // low key blocks see the most queries: first
-    const size_t head = (size_t)bkv * (size_t)Nk * D;
+    const int part = (bid / BHkv) % NC;   // dK, dV columns [D part, D part + D)
+    const int kb = bid / (BHkv * NC);     // low key blocks see the most queries: first
+    const size_t head = (size_t)bkv * (size_t)Nk * DT;
     const int qh0 = bkv * G;              // its first query head; the group is qh0 .. qh0+G-1
 
     // One factor each for Q and dO serves the whole group of query heads.
@@ -536,12 +584,12 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const int off = Nk - N;               // query row i sits at key position i + off
     const int kq = kj - off;              // causal: the first query row that sees key kj
 
-    u32x4_t kf[KS], vf[KS];
+    u32x4_t kf[KST], vf[KST];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
+    for (int s = 0; s < KST; ++s) {
         if (kj < Nk) {
-            kf[s] = *(const u32x4_t*)(K + head + (size_t)kj * D + 16 * s + 8 * g);
-            vf[s] = *(const u32x4_t*)(V + head + (size_t)kj * D + 16 * s + 8 * g);
+            kf[s] = *(const u32x4_t*)(K + head + (size_t)kj * DT + 16 * s + 8 * g);
+            vf[s] = *(const u32x4_t*)(V + head + (size_t)kj * DT + 16 * s + 8 * g);
         } else {
             kf[s] = vf[s] = u32x4_t{0u, 0u, 0u, 0u};
         }
@@ -560,26 +608,26 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     // n_tiles: then no query sees it and dK = dV = 0).
     const int t0 = CAUSAL ? min(max(k0 - off, 0) / BQ, n_tiles) : 0;
 
-    // Query tile t of group member gq (query head qh0 + gq) into buffer buf:
-    // Q and dO rows (bf16, swizzled) and the two transposed fp16 images, BLK
-    // 1 KB blocks each spread over the NW waves (part k of NPART is one block
-    // of this wave), and the tile's 128 statistics (wave 0). Past the last
-    // tile of the last member the buffer is filled from a valid tile and
-    // never read.
+    // Column step cs of query tile t of group member gq (query head qh0 + gq)
+    // into buffer buf: Q and dO rows (bf16, swizzled) and, for the last step,
+    // this part's two transposed fp16 images, BLK 1 KB blocks each spread over
+    // the NW waves (part k of the step's parts is one block of this wave), and
+    // the tile's 128 statistics (wave 0). Past the last tile of the last
+    // member the buffer is filled from a valid tile and never read.
     constexpr int PPT = BLK / NW;
-    constexpr int NPART = 4 * PPT;
-    auto stage_part = [&](int gq, int t, int buf, int k) {
+    auto stage_part = [&](int gq, int t, int cs, int buf, int k) {
         lds_char* base = (lds_char*)(smem + buf * BUF);
         const int tensor = k / PPT, b = wave + NW * (k % PPT);
         const bool live = gq < G && t < n_tiles;
         const size_t qh = (size_t)(qh0 + (live ? gq : 0));
         const size_t ti = (size_t)(live ? t : 0);
         if (tensor < 2)
-            stage_tile_block<D>((tensor == 0 ? Q : dO) + qh * N * D,
-                                base + (tensor == 0 ? OFF_Q : OFF_DO), (int)ti * BQ, N, b, lane);
+            stage_tile_block<D, DT>((tensor == 0 ? Q : dO) + qh * N * DT + cs * D,
+                                    base + (tensor == 0 ? OFF_Q : OFF_DO), (int)ti * BQ, N, b,
+                                    lane);
         else
-            stage_image_block((tensor == 2 ? qt_img : ot_img) + (qh * T + ti) * TB, TB,
-                              base + (tensor == 2 ? OFF_QT : OFF_DOT), b, lane);
+            stage_image_block((tensor == 2 ? qt_img : ot_img) + ((qh * T + ti) * NC + part) * TB,
+                              TB, base + (tensor == 2 ? OFF_QT : OFF_DOT), b, lane);
     };
     auto stage_stats = [&](int gq, int t, int buf) {
         lds_char* base = (lds_char*)(smem + buf * BUF);
@@ -593,7 +641,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     // S/dP fragments (chunk step s; for d = 64 also the query half) and
     // pb[8 + 2 t4 + (nb & 1)] for the transposed dV/dK fragments; everything
     // else in a fragment address is a compile-time offset, so each read is
-    // one ds_read with an immediate offset from a base moved once per tile.
+    // one ds_read with an immediate offset from a base moved once per step.
     lds_char* const s0 = (lds_char*)smem;
     lds_char* pb[16];
 #pragma unroll
@@ -604,34 +652,47 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
     lds_char* pst = s0 + OFF_ST + 16 * g;
 
+    {
+        constexpr int NP0 = (NC == 1 ? 4 : 2) * PPT;
 #pragma unroll
-    for (int k = 0; k < NPART; ++k) stage_part(0, t0, 0, k);
-    stage_stats(0, t0, 0);
+        for (int k = 0; k < NP0; ++k) stage_part(0, t0, 0, 0, k);
+        if (NC == 1) stage_stats(0, t0, 0);
+    }
     __syncthreads();
 
-    // One query tile of group member gq: stage the next tile (the member's
-    // next, or the next member's first), run the pipeline, move the bases.
+    // One query tile of group member gq: NC column steps, each staging the
+    // next step (the next column step of this tile, or the first of the
+    // member's next tile, or of the next member's first), running its
+    // products and moving the bases.
     const int nt = n_tiles - t0;
     auto iteration = [&](int gq, int t, auto mask_tag) {
         const int i0 = t * BQ;
-        const int buf = (gq * nt + t - t0) & 1;
         const int ngq = (t + 1 < n_tiles) ? gq : gq + 1;
         const int nt1 = (t + 1 < n_tiles) ? t + 1 : t0;
+        f32x16_t sa[2], da[2];
 
-        // The tile's 2*NSD + 4*NG products run as one software pipeline:
-        // S, dP of query half 0, then of half 1 (while half 0 is
-        // exponentiated), then dV, dK over four 16-query steps (the first
-        // two while half 1 is exponentiated). Each product's LDS fragment
-        // is read LA products ahead; sched_barrier keeps that order. Only
-        // tiles that reach above a wave's first key take the causal mask.
-        auto tile_body = [&](auto mask_tag) {
+        // One column step as a software pipeline: S, dP of query half 0, then
+        // of half 1; in the last step (S and dP complete) half 0 is
+        // exponentiated under half 1's products, then dV, dK run over four
+        // 16-query steps (the first two while half 1 is exponentiated). Each
+        // product's LDS fragment is read LA products ahead; sched_barrier
+        // keeps that order. Only tiles that reach above a wave's first key
+        // take the causal mask.
+        auto step = [&](auto cs_tag, auto mask_tag) {
+            constexpr int CS = decltype(cs_tag)::value;
+            constexpr bool LAST = CS == NC - 1;
             constexpr bool MASK = decltype(mask_tag)::value;
             constexpr int NSD = 2 * KS;
             constexpr int NG = 2 * NB;
-            constexpr int NOPS = 2 * NSD + 4 * NG;
+            constexpr int NOPS = LAST ? 2 * NSD + 4 * NG : 2 * NSD;
             constexpr int LA = kFragAhead;
             constexpr int EPO_A = 16 / NSD;
             constexpr int EPO_B = 16 / (2 * NG);
+            constexpr int NCS = LAST ? 0 : CS + 1;
+            constexpr bool NLAST = NCS == NC - 1;
+            constexpr int NPART = (NLAST ? 4 : 2) * PPT;
+            const int sgq = LAST ? ngq : gq, st_t = LAST ? nt1 : t;
+            const int buf = (((gq * nt + t - t0) * NC) + CS) & 1;
             lds_char* const* bb = pb;
             lds_char* const bst = pst;
             auto frag = [&](int o) -> u32x4_t {
@@ -650,7 +711,6 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
             for (int o = 0; o < LA; ++o) fr[o] = frag(o);
 
-            f32x16_t sa[2], da[2];
             f32x4_t l4[4], d4[4];     // lse*log2e and sE*D of the half being exponentiated
             float pv[16], dsv[16];
             u32x4_t pp[4], dsp[4];
@@ -678,18 +738,20 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             for (int o = 0; o < NOPS; ++o) {
                 if (o + LA < NOPS) fr[(o + LA) % (LA + 1)] = frag(o + LA);
                 const u32x4_t a = fr[o % (LA + 1)];
-                if (o == 0) {
+                if (LAST && o == 0) {
 #pragma unroll
                     for (int q4 = 0; q4 < 4; ++q4) read_stats(0, q4);
                 }
                 if (o < 2 * NSD) {
                     const int ib = o / NSD, w = o % NSD, st = w >> 1;
                     f32x16_t& acc = (w & 1) ? da[ib] : sa[ib];
-                    const u32x4_t& bop = (w & 1) ? vf[st] : kf[st];
-                    if (st == 0) mfma_bf16_first(acc, a, bop);
-                    else if (st == KS - 1) mfma_bf16_last(acc, a, bop);
-                    else mfma_bf16_next(acc, a, bop);
-                    if (ib == 1) {
+                    const u32x4_t& bop = (w & 1) ? vf[CS * KS + st] : kf[CS * KS + st];
+                    // A chain's last product of a step carries the wait
+                    // states a VALU read of its result needs.
+                    if (CS == 0 && st == 0) mfma_bf16_first<WS>(acc, a, bop);
+                    else if (st == KS - 1) mfma_bf16_last<WS>(acc, a, bop);
+                    else mfma_bf16_next<WS>(acc, a, bop);
+                    if (LAST && ib == 1) {
 #pragma unroll
                         for (int e = 0; e < EPO_A; ++e) softmax_elem(0, w * EPO_A + e);
                     }
@@ -702,23 +764,25 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                         for (int e = 0; e < EPO_B; ++e) softmax_elem(1, w * EPO_B + e);
                     }
                 }
-                // The next tile's loads, in the VALU-free dV/dK steps.
-                constexpr int O0 = 2 * NSD + 2 * NG;
+                // The next step's loads: in the VALU-free dV/dK steps of the
+                // last column step, else among the S/dP products.
+                constexpr int O0 = LAST ? 2 * NSD + 2 * NG : 0;
 #pragma unroll
                 for (int k = 0; k < NPART; ++k)
-                    if (o == O0 + k * (NOPS - O0) / NPART) stage_part(ngq, nt1, buf ^ 1, k);
-                if (o == O0 + 1) stage_stats(ngq, nt1, buf ^ 1);
+                    if (o == O0 + k * (NOPS - O0) / NPART) stage_part(sgq, st_t, NCS, buf ^ 1, k);
+                if (NLAST && o == O0 + 1) stage_stats(sgq, st_t, buf ^ 1);
                 __builtin_amdgcn_sched_barrier(0);
             }
-        };
-        tile_body(mask_tag);
-        // the bases move to the other buffer
-        const int step = buf ? -BUF : BUF;
+            // the bases move to the other buffer
+            const int stp = buf ? -BUF : BUF;
 #pragma unroll
-        for (int k = 0; k < 16; ++k) pb[k] += step;
-        pst += step;
+            for (int k = 0; k < 16; ++k) pb[k] += stp;
+            pst += stp;
 
-        __syncthreads();   // tile t+1 has landed; every wave is done with tile t
+            __syncthreads();   // the next step has landed; every wave is done with this one
+        };
+        step(IntTag<0>{}, mask_tag);
+        if constexpr (NC > 1) step(IntTag<1>{}, mask_tag);
     };
     // Causal: only tiles whose first row precedes the block's last key
     // position reach above some wave's keys (two tiles when Nq = Nk; a wave
@@ -738,8 +802,8 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
     if (kj < Nk) {
         const float fk = scale / (sQ * sE), fv = 1.f / sDO;
-        uint16_t* dkrow = dK + head + (size_t)kj * D;
-        uint16_t* dvrow = dV + head + (size_t)kj * D;
+        uint16_t* dkrow = dK + head + (size_t)kj * DT + D * part;
+        uint16_t* dvrow = dV + head + (size_t)kj * DT + D * part;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -769,6 +833,8 @@ static T* ws_ptr(const BwdArgs& a, size_t off) { return (T*)((char*)a.workspace 
 
 static int q_tiles64(const BwdArgs& a) { return (a.N + 63) / 64; }
 static int k_tiles64(const BwdArgs& a) { return (a.Nk + 63) / 64; }
+// Column parts of a head (128 columns each above d = 128).
+static int col_parts(int d) { return d > 128 ? d / 128 : 1; }
 
 template <int D>
 static hipError_t launch_prepare_t(const BwdArgs& a) {
@@ -787,7 +853,8 @@ static hipError_t launch_prepare_t(const BwdArgs& a) {
                        (const uint32_t*)partial, ws_ptr<float>(a, w.scales), BH, G, chunks);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_image_kernel<D>), dim3(2 * BH * Tq + BHkv * Tk), dim3(256), 0,
+    hipLaunchKernelGGL((bwd_image_kernel<D>), dim3((2 * BH * Tq + BHkv * Tk) * col_parts(D)),
+                       dim3(256), 0,
                        a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                        (const uint16_t*)a.dout, ws_ptr<const float>(a, w.scales),
                        ws_ptr<char>(a, w.qt), ws_ptr<char>(a, w.ot), ws_ptr<char>(a, w.kt), BH,
@@ -801,7 +868,8 @@ static hipError_t launch_dq_t(const BwdArgs& a) {
     const BwdWorkspace w = ws_of(a);
     const int BH = a.B * a.H;
     const int nqb = (a.N + NW * 32 - 1) / (NW * 32);
-    hipLaunchKernelGGL((bwd_dq_kernel<D, NW, CAUSAL>), dim3(nqb * BH), dim3(NW * 64), 0,
+    hipLaunchKernelGGL((bwd_dq_kernel<D, NW, CAUSAL>), dim3(nqb * BH * col_parts(D)),
+                       dim3(NW * 64), 0,
                        a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                        (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse,
                        ws_ptr<const float>(a, w.scales), ws_ptr<const char>(a, w.kt),
@@ -816,7 +884,8 @@ static hipError_t launch_dkdv_t(const BwdArgs& a) {
     const BwdWorkspace w = ws_of(a);
     const int BHkv = a.B * a.Hkv;
     const int nkb = (a.Nk + NW * 32 - 1) / (NW * 32);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, CAUSAL>), dim3(nkb * BHkv), dim3(NW * 64), 0,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, CAUSAL>), dim3(nkb * BHkv * col_parts(D)),
+                       dim3(NW * 64), 0,
                        a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                        (const uint16_t*)a.v, (const uint16_t*)a.dout,
                        ws_ptr<const float>(a, w.scales), ws_ptr<const float>(a, w.stats),
@@ -827,15 +896,18 @@ static hipError_t launch_dkdv_t(const BwdArgs& a) {
 }
 
 hipError_t launch_bwd_prepare(const BwdArgs& a) {
+    if (a.d == 256) return launch_prepare_t<256>(a);
     return a.d == 128 ? launch_prepare_t<128>(a) : launch_prepare_t<64>(a);
 }
 
 hipError_t launch_bwd_dq(const BwdArgs& a) {
+    if (a.d == 256) return a.causal ? launch_dq_t<256, true>(a) : launch_dq_t<256, false>(a);
     if (a.d == 128) return a.causal ? launch_dq_t<128, true>(a) : launch_dq_t<128, false>(a);
     return a.causal ? launch_dq_t<64, true>(a) : launch_dq_t<64, false>(a);
 }
 
 hipError_t launch_bwd_dkdv(const BwdArgs& a) {
+    if (a.d == 256) return a.causal ? launch_dkdv_t<256, true>(a) : launch_dkdv_t<256, false>(a);
     if (a.d == 128) return a.causal ? launch_dkdv_t<128, true>(a) : launch_dkdv_t<128, false>(a);
     return a.causal ? launch_dkdv_t<64, true>(a) : launch_dkdv_t<64, false>(a);
 }

@@ -54,6 +54,12 @@ struct BoolTag {
     static constexpr bool value = B;
 };
 
+// Compile-time integer carried into a generic lambda.
+template <int I>
+struct IntTag {
+    static constexpr int value = I;
+};
+
 typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
 typedef __attribute__((address_space(3))) f32x4_t lds_f32x4_t;
 
@@ -81,16 +87,33 @@ __device__ __forceinline__ void mfma_bf16_agpr(f32x16_t& acc, const u32x4_t& a, 
 // mfma_bf16_last; SrcC = vDst within the chain, which dependent products
 // forward in hardware, and the last one is followed by the wait states the
 // VALU needs before it may read a matrix result (more than an 8-pass
-// product requires).
+// product requires). With WS set, each product is preceded by the two wait
+// states a matrix instruction needs after a VALU write of a source: for
+// kernels whose AGPR file is full, where the compiler may copy a parked
+// operand into an AGPR just before the product (it does not see that the
+// assembly is a matrix instruction, so it adds no wait states of its own).
+template <bool WS = false>
 __device__ __forceinline__ void mfma_bf16_first(f32x16_t& acc, const u32x4_t& a, const u32x4_t& b) {
-    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "a"(b));
+    if constexpr (WS)
+        asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "a"(b));
+    else
+        asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "a"(b));
 }
+template <bool WS = false>
 __device__ __forceinline__ void mfma_bf16_next(f32x16_t& acc, const u32x4_t& a, const u32x4_t& b) {
-    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
+    if constexpr (WS)
+        asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
+    else
+        asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
 }
+template <bool WS = false>
 __device__ __forceinline__ void mfma_bf16_last(f32x16_t& acc, const u32x4_t& a, const u32x4_t& b) {
-    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7"
-        : "+v"(acc) : "v"(a), "a"(b));
+    if constexpr (WS)
+        asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7"
+            : "+v"(acc) : "v"(a), "a"(b));
+    else
+        asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7"
+            : "+v"(acc) : "v"(a), "a"(b));
 }
 
 // Pins a value computed for a later tile at this point of the schedule: the
@@ -221,11 +244,12 @@ __device__ __forceinline__ void lds_dma16(const void* base, uint32_t voff, lds_c
 // makes the transposed 8-byte reads below conflict-free.
 __device__ __forceinline__ int v_chunk_swizzle(int row) { return (row & 3) << 1; }
 
-// 1 KB block b of the [64][D] tile at row row0 of `src` ([N][D] bf16, N >= 1)
-// into LDS: lane `lane` fetches the chunk whose swizzled place is bytes
-// [16 lane, 16 lane + 16) of the block. Rows past N read row N - 1; a tile
-// wholly past N reads row N - 1 throughout.
-template <int D, bool VTYPE>
+// 1 KB block b of the [64][D] tile at row row0 of `src` (N >= 1 rows of D
+// bf16 values, consecutive rows LD >= D values apart) into LDS: lane `lane`
+// fetches the chunk whose swizzled place is bytes [16 lane, 16 lane + 16) of
+// the block. Rows past N read row N - 1; a tile wholly past N reads row N - 1
+// throughout.
+template <int D, bool VTYPE, int LD = D>
 __device__ __forceinline__ void stage_block(const uint16_t* __restrict__ src, lds_char* tile,
                                             int row0, int N, int b, int lane) {
     constexpr int DCH = D / 8;
@@ -234,8 +258,8 @@ __device__ __forceinline__ void stage_block(const uint16_t* __restrict__ src, ld
     const int phys = lane % DCH;
     const int logical = phys ^ (VTYPE ? v_chunk_swizzle(row) : row_chunk_swizzle<D>(row));
     const int rb = min(row0, N - 1);           // uniform
-    const uint32_t voff = (uint32_t)(min(row, N - 1 - rb) * (2 * D) + logical * 16);
-    lds_dma16(src + (size_t)rb * D, voff, tile + b * 1024);
+    const uint32_t voff = (uint32_t)(min(row, N - 1 - rb) * (2 * LD) + logical * 16);
+    lds_dma16(src + (size_t)rb * LD, voff, tile + b * 1024);
 }
 
 // Stage blocks b = first, first + STRIDE, ... (< 64 * D * 2 / 1024) of the
@@ -252,10 +276,10 @@ __device__ __forceinline__ void stage_tile_lds(const uint16_t* __restrict__ src,
 // already laid out as the LDS tile (a byte-for-byte copy of the `bytes`
 // bytes at `src`, a multiple of 16; lanes past them re-read its last chunk
 // and fill LDS that no one reads).
-template <int D>
+template <int D, int LD = D>
 __device__ __forceinline__ void stage_tile_block(const uint16_t* __restrict__ src, lds_char* tile,
                                                  int row0, int N, int b, int lane) {
-    stage_block<D, false>(src, tile, row0, N, b, lane);
+    stage_block<D, false, LD>(src, tile, row0, N, b, lane);
 }
 
 __device__ __forceinline__ void stage_image_block(const void* src, int bytes, lds_char* tile,

@@ -27,11 +27,11 @@
  *   Scale      any finite scale >= 0 (1/sqrt(d) for the standard attention).
  *   Sizes      B, H, N >= 0; if any of them is 0 the call does nothing and
  *              returns FA_OK. N may be any positive value (no multiple of a
- *              tile size is required). d must be 64 or 128; the bf16
- *              forward entry points (fa_fwd, fa_fwd_gqa, fa_fwd_rect) and
- *              fa_decode also take d = 256, the largest head size the
- *              "FlashAttention-2" page (systems-analysis.info, section
- *              "Performance") names for FlashAttention-2.
+ *              tile size is required). d must be 64, 128 or 256 (the
+ *              largest head size the "FlashAttention-2" page,
+ *              systems-analysis.info, section "Performance", names for
+ *              FlashAttention-2); fa_fwd_f32 takes 64 and 128 only and
+ *              fa_fwd_fp8 128 only.
  *   Async      work is enqueued on `stream` (0 = the null stream) and the call
  *              returns; results are valid once the stream has synchronised.
  *   Errors     every argument is checked before anything is enqueued, so on

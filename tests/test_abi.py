@@ -141,7 +141,9 @@ def test_grouped_heads_arguments(lib):
     assert lib.fa_fwd_gqa(A, A, A, A, A, 1, 4, 2, 64, 96, 0, 0.125, None) == UNSUPPORTED
     assert lib.fa_fwd_gqa(A, A, A, A, A, 0, 4, 2, 64, 64, 0, 0.125, None) == OK
     assert lib.fa_bwd_gqa_workspace_size(2, 32, 8, 4096, 128) > 0
-    assert lib.fa_bwd_gqa_workspace_size(2, 32, 8, 4096, 256) == 0     # no d = 256 backward
+    # d = 256: twice the images of d = 128 (one per 128-column part)
+    assert lib.fa_bwd_gqa_workspace_size(2, 32, 8, 4096, 256) > \
+        lib.fa_bwd_gqa_workspace_size(2, 32, 8, 4096, 128)
     assert lib.fa_bwd_gqa_workspace_size(2, 32, 5, 4096, 128) == 0
     assert lib.fa_bwd_gqa_workspace_size(2, 32, 0, 4096, 128) == 0
     assert lib.fa_bwd_gqa_workspace_size(4, 16, 16, 4096, 128) == \
@@ -208,7 +210,8 @@ def test_rect_backward_arguments(lib):
     assert lib.fa_bwd_rect_workspace_size(1, 4, 2, 0, 300, 128) == 0
     assert lib.fa_bwd_rect_workspace_size(1, 4, 2, 100, 0, 128) == 0
     assert lib.fa_bwd_rect_workspace_size(1, 4, 3, 100, 300, 128) == 0
-    assert lib.fa_bwd_rect_workspace_size(1, 4, 2, 100, 300, 256) == 0
+    assert lib.fa_bwd_rect_workspace_size(1, 4, 2, 100, 300, 256) > ws
+    assert lib.fa_bwd_rect_workspace_size(1, 4, 2, 100, 300, 512) == 0
 
     def b(B=1, H=4, Hkv=2, Nq=100, Nk=300, d=128, ws_bytes=ws, wsp=0x200000, dk=A):
         return lib.fa_bwd_rect(A, A, A, A, A, A, A, dk, A, wsp, ws_bytes, B, H, Hkv, Nq, Nk, d,
@@ -218,7 +221,8 @@ def test_rect_backward_arguments(lib):
     assert b(Nq=0) == INVALID                   # keys whose gradients would be left unwritten
     assert b(Hkv=3) == INVALID
     assert b(dk=None) == INVALID
-    assert b(d=256) == UNSUPPORTED
+    assert b(d=512) == UNSUPPORTED
+    assert b(d=96) == UNSUPPORTED
     assert b(Nk=(1 << 26) + 1) == UNSUPPORTED
     assert b(dk=MIS) == UNSUPPORTED
     assert b(ws_bytes=ws - 1) == WORKSPACE
