@@ -75,6 +75,39 @@ MIN_TIMED_MS = 200.0
 FLUSH_BYTES = 512 << 20         # written between calls for the cold (L2/MALL-flushed) time
 
 
+PROBE_SAMPLES = 4000            # one every ~8128 shader clocks: ~15-25 ms of samples
+
+
+def measure_sclk(fn, dev, min_ms: float = 50.0):
+    """Shader clock (MHz) while ``fn`` runs back to back: fa_clock_probe's wave
+    samples the shader-clock and 100 MHz counters on a second stream (default
+    priority) while the calls run on the current one. The calls go on for at
+    least min_ms, longer than the probe's samples take, and the middle 80% of
+    the samples give the clock. None if the counters did not advance."""
+    import torch
+
+    import exact_attention_41_amd as fa
+    samples = torch.zeros((PROBE_SAMPLES, 2), dtype=torch.int64, device=dev)
+    side = torch.cuda.Stream(device=dev)
+    fn()
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    fn()
+    torch.cuda.synchronize(dev)
+    est_ms = max((time.perf_counter() - t0) * 1e3, 1e-3)
+    calls = max(1, int(min_ms / est_ms) + 1)
+    fa.fa_clock_probe(samples, sleep_units=1, stream=side)
+    for _ in range(calls):
+        fn()
+    torch.cuda.synchronize(dev)
+    x = samples.cpu().numpy()
+    a, b = int(0.1 * len(x)), int(0.9 * len(x)) - 1
+    dt, dr = int(x[b, 0] - x[a, 0]), int(x[b, 1] - x[a, 1])
+    if dt <= 0 or dr <= 0:
+        return None
+    return round(dt / dr * 100.0, 1)
+
+
 class CallTimer:
     """Median device time of one call: WARMUP_CALLS untimed calls, then at
     least MIN_CALLS timed ones covering at least MIN_TIMED_MS in total, each
@@ -121,7 +154,7 @@ class CallTimer:
 
 
 # ---------------------------------------------------------------------------
-def gpu_step_timing(w, steps: int, warmup: int):
+def gpu_step_timing(w, steps: int, warmup: int, with_clock: bool = True):
     import torch
 
     import exact_attention_41_amd as fa
@@ -168,7 +201,24 @@ def gpu_step_timing(w, steps: int, warmup: int):
             per_kernel[n] += ev[i].elapsed_time(ev[i + 1])
     per_kernel = {n: t / steps for n, t in per_kernel.items()}
     ms_per_step = (t1 - t0) * 1000.0 / steps
-    return ms_per_step, per_kernel
+    # The shader clock while the whole step runs, and while each kernel runs
+    # on its own (back to back; the workspace holds what the later phases
+    # read).
+    kernels = {
+        "fwd": lambda: fa.fa_fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse),
+        "bwd_preprocess": lambda: fa.fa_bwd_preprocess(q, k, v, do, ws),
+        "bwd_dq": lambda: fa.fa_bwd_dq(q, k, v, do, lse, ws, dq, causal=w.causal,
+                                       scale=w.scale),
+        "bwd_dkdv": lambda: fa.fa_bwd_dkdv(q, k, v, do, ws, dk, dv, causal=w.causal,
+                                           scale=w.scale),
+    }
+    clocks = {}
+    if with_clock:
+        clocks["step"] = measure_sclk(step, dev)
+        for n in names:
+            clocks[n] = measure_sclk(kernels[n], dev)
+    log("bench: shader clock (MHz) " + ", ".join(f"{k}={v}" for k, v in clocks.items()))
+    return ms_per_step, per_kernel, clocks
 
 
 def gpu_forward_sweep(names):
@@ -195,6 +245,7 @@ def gpu_forward_sweep(names):
             fa.fa_fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
 
         med, cold, n = timer.both(call)
+        sclk = measure_sclk(call, dev)
         torch.cuda.synchronize(dev)
         torch.cuda.reset_peak_memory_stats(dev)
         alloc0 = torch.cuda.memory_allocated(dev)
@@ -209,9 +260,11 @@ def gpu_forward_sweep(names):
         out.append({"workload": name, "pass": "fwd", "ms": round(med, 4),
                     "tflops": round(tf, 1), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
                     "cold_ms": round(cold, 4), "cold_tflops": round(ctf, 1), "calls": n,
+                    "sclk_mhz": sclk,
+                    "frac_at_sclk": (round(tf / (256 * 4096 * sclk * 1e-6), 4) if sclk else None),
                     "extra_device_memory": extra})
         log(f"  fwd {name}: {med:.3f} ms  {tf:.1f} TFLOP/s  {100 * tf / PEAK_BF16_TFLOPS:.1f}%  "
-            f"(cold {cold:.3f} ms; extra memory {extra})")
+            f"(cold {cold:.3f} ms; shader clock {sclk} MHz; extra memory {extra})")
         del q, k, v, o, lse
     return out
 
@@ -222,7 +275,7 @@ def counter_pass(w) -> int:
     HBM byte counts."""
     import torch
 
-    ms, _ = gpu_step_timing(w, steps=2, warmup=1)
+    ms, _, _ = gpu_step_timing(w, steps=2, warmup=1, with_clock=False)
     src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda:0")
     dst = torch.empty_like(src)
     for _ in range(2):
@@ -583,7 +636,7 @@ def main() -> int:
     if args.counters:
         return counter_pass(w)
     log(f"bench: workload {w.name} steps={args.steps} warmup={args.warmup}")
-    ms, per_kernel = gpu_step_timing(w, args.steps, args.warmup)
+    ms, per_kernel, clocks = gpu_step_timing(w, args.steps, args.warmup)
     fwd_f, bwd_f = w.fwd_flops(), w.bwd_flops()
     value = (fwd_f + bwd_f) / (ms * 1e-3) / 1e12
     log(f"bench: {ms:.3f} ms/step, {value:.1f} TFLOP/s; per kernel (ms): "
@@ -607,6 +660,13 @@ def main() -> int:
     roofline = {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 1),
                 "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
+    sclk = clocks.get(dominant)
+    if sclk:
+        # the same peak at the shader clock measured while the kernel ran
+        peak_at = 256 * 4096 * sclk * 1e6 / 1e12
+        roofline["sclk_mhz"] = sclk
+        roofline["peak_at_sclk"] = round(peak_at, 1)
+        roofline["frac_at_sclk"] = round(achieved / peak_at, 4)
 
     fwd_tf = fwd_f / (per_kernel["fwd"] * 1e-3) / 1e12
     bwd_ms = per_kernel["bwd_preprocess"] + per_kernel["bwd_dkdv"] + per_kernel["bwd_dq"]
@@ -636,6 +696,7 @@ def main() -> int:
         "bwd": {"ms": round(bwd_ms, 4), "tflops": round(bwd_tf, 1),
                 "frac_peak": round(bwd_tf / PEAK_BF16_TFLOPS, 4)},
         "kernel_ms": {k: round(v, 4) for k, v in per_kernel.items()},
+        "sclk_mhz": clocks,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "forward_workloads": sweep,

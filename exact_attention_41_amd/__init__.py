@@ -25,8 +25,8 @@ from . import _lib
 __all__ = ["fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_bwd_workspace_size", "fa_status_str",
            "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_gqa", "fa_bwd_gqa",
            "fa_bwd_gqa_workspace_size", "fa_decode", "fa_decode_workspace_size", "fa_fwd_rect",
-           "fa_fwd_fp8", "fa_bwd_rect", "fa_bwd_rect_workspace_size", "FAError",
-           "library_path"]
+           "fa_fwd_fp8", "fa_bwd_rect", "fa_bwd_rect_workspace_size", "fa_clock_probe",
+           "FAError", "library_path"]
 
 
 class FAError(RuntimeError):
@@ -372,3 +372,23 @@ def fa_fwd_fp8(q, k, v, descale_q: float = 1.0, descale_k: float = 1.0, descale_
     if st != _lib.FA_OK:
         raise FAError(st, "fa_fwd_fp8")
     return out, lse
+
+
+def fa_clock_probe(samples, sleep_units: int = 1, stream=None) -> None:
+    """Measurement utility: enqueue on ``stream`` (a torch stream; default the
+    current one) one wave that fills ``samples`` (an int64 device tensor
+    [n, 2]) with (shader-clock counter, 100 MHz real-time counter) pairs,
+    about sleep_units x 8128 shader clocks apart. Calls fa_clock_probe of
+    libfa.so."""
+    torch = _torch()
+    if not isinstance(samples, torch.Tensor) or samples.dtype != torch.int64 or \
+            samples.dim() != 2 or samples.shape[1] != 2 or not samples.is_contiguous():
+        raise ValueError("samples must be a contiguous int64 tensor of shape [n, 2]")
+    if samples.device.type != "cuda":
+        raise ValueError("samples must be on a GPU")
+    st = stream if stream is not None else torch.cuda.current_stream(samples.device)
+    with torch.cuda.device(samples.device):
+        rc = _lib.load().fa_clock_probe(samples.data_ptr(), samples.shape[0], int(sleep_units),
+                                        st.cuda_stream)
+    if rc != _lib.FA_OK:
+        raise FAError(rc, "fa_clock_probe")

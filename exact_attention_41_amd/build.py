@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libfa.so")
 SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_fwd256.hip", "fa_fwd_fp8.hip", "fa_bwd.hip",
-           "fa_decode.hip"]
+           "fa_decode.hip", "fa_clock.hip"]
 # Per-source flags. The backward kernels and the d = 256 forward keep their
 # accumulators in AGPRs through inline assembly; every other matrix product
 # there should write VGPRs, where the VALU reads its results, rather than the

@@ -4,6 +4,7 @@ Only calls that the library rejects during validation (before any HIP call)
 or that are empty no-ops are made here; nothing is launched.
 """
 import ctypes
+import glob
 import os
 import re
 import subprocess
@@ -14,6 +15,7 @@ from exact_attention_41_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fa.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
 
@@ -27,15 +29,20 @@ def lib():
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+    """Every function that a header under include/ declares."""
+    names = set()
+    for h in HEADERS:
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_compiles_as_c_and_cpp(tmp_path):
     for lang, std in (("c", "-std=c99"), ("c++", "-std=c++11")):
         src = tmp_path / ("t.c" if lang == "c" else "t.cpp")
-        src.write_text('#include "fa.h"\nint main(void){ return (int)FA_OK; }\n')
+        src.write_text('#include "fa.h"\n#include "fa_measure.h"\n'
+                       'int main(void){ return (int)FA_OK; }\n')
         cc = "gcc" if lang == "c" else "g++"
         res = subprocess.run([cc, std, "-Wall", "-Werror", "-fsyntax-only", "-I",
                               os.path.join(ROOT, "include"), str(src)],
@@ -273,3 +280,17 @@ def test_fp8_forward_arguments(lib):
     assert f(d=256) == UNSUPPORTED
     assert f(q=MIS) == UNSUPPORTED
     assert f(B=0) == OK
+
+
+def test_clock_probe_arguments(lib):
+    """fa_clock_probe validates before launching (n = 0 launches nothing)."""
+    import ctypes
+    f = lib.fa_clock_probe
+    assert f(None, 0, 1, None) == OK
+    assert f(A, -1, 1, None) == INVALID
+    assert f(A, 4, -1, None) == INVALID
+    assert f(None, 4, 1, None) == INVALID
+    assert f(A + 8, 4, 1, None) == UNSUPPORTED
+    assert f(A, (1 << 20) + 1, 1, None) == UNSUPPORTED
+    assert f(A, 4, 1025, None) == UNSUPPORTED
+    assert isinstance(ctypes.c_int(f(A, 0, 0, None)).value, int)
