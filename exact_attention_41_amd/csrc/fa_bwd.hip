@@ -352,8 +352,8 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             stage_tile_block<D, DT>((tensor == 0 ? Kh : Vh) + cs * D,
                                     base + (tensor == 0 ? OFF_K : OFF_V), t * BC, Nk, b, lane);
         else
-            stage_image_block(kt_h + ((size_t)min(t, Tk - 1) * NC + part) * TB, TB,
-                              base + OFF_KT, b, lane);
+            stage_image_block_full(kt_h + ((size_t)min(t, Tk - 1) * NC + part) * TB,
+                                   base + OFF_KT, b, lane);
     };
 
     // Lane-dependent LDS bases of buffer 0: pb[k], k < 8, for the row-major
@@ -626,8 +626,8 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                                     base + (tensor == 0 ? OFF_Q : OFF_DO), (int)ti * BQ, N, b,
                                     lane);
         else
-            stage_image_block((tensor == 2 ? qt_img : ot_img) + ((qh * T + ti) * NC + part) * TB,
-                              TB, base + (tensor == 2 ? OFF_QT : OFF_DOT), b, lane);
+            stage_image_block_full((tensor == 2 ? qt_img : ot_img) + ((qh * T + ti) * NC + part) * TB,
+                                   base + (tensor == 2 ? OFF_QT : OFF_DOT), b, lane);
     };
     auto stage_stats = [&](int gq, int t, int buf) {
         lds_char* base = (lds_char*)(smem + buf * BUF);

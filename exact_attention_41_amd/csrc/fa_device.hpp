@@ -230,12 +230,26 @@ __device__ __forceinline__ int tr_slot_offset(int n, int slot) {
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((ext_vector_type(4))) short i16x4_t;
 
+// A wave-uniform pointer, held in scalar registers: the compiler may
+// otherwise fold a per-lane offset into it early and add the two with a
+// 64-bit vector instruction before every copy.
+__device__ __forceinline__ const char* uniform_ptr(const void* p) {
+    const uint64_t u = (uint64_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    return (const char*)(((uint64_t)hi << 32) | lo);
+}
+
 // 16 bytes per lane from global address base + voff (base wave-uniform, so
 // the copy takes the scalar-base + 32-bit-offset form) into LDS bytes
 // [16 l, 16 l + 16) after the wave-uniform address `dst`.
 __device__ __forceinline__ void lds_dma16(const void* base, uint32_t voff, lds_char* dst) {
+    // An offset that is the same on every call (a loop invariant) would be
+    // widened to 64 bits once, outside the loop, and the wide sum would then
+    // miss the scalar-base form: the empty asm keeps it a 32-bit value here.
+    asm volatile("" : "+v"(voff));
     __builtin_amdgcn_global_load_lds(
-        (const __attribute__((address_space(1))) void*)((const char*)base + voff),
+        (const __attribute__((address_space(1))) void*)(uniform_ptr(base) + voff),
         (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
 }
 
@@ -285,6 +299,13 @@ __device__ __forceinline__ void stage_tile_block(const uint16_t* __restrict__ sr
 __device__ __forceinline__ void stage_image_block(const void* src, int bytes, lds_char* tile,
                                                   int b, int lane) {
     lds_dma16(src, (uint32_t)min(b * 1024 + lane * 16, bytes - 16), tile + b * 1024);
+}
+
+// The same for a block wholly inside the image (bytes >= 1024 (b + 1)): the
+// block's start goes into the uniform base, each lane's offset is 16 lane.
+__device__ __forceinline__ void stage_image_block_full(const void* src, lds_char* tile, int b,
+                                                       int lane) {
+    lds_dma16((const char*)src + b * 1024, (uint32_t)(lane * 16), tile + b * 1024);
 }
 
 // 16-byte A/B fragment of a K-type tile: row `row`, logical chunk `ch`.
