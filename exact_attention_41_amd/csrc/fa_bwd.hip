@@ -241,10 +241,17 @@ bwd_image_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     char* dst = which == 0 ? qt : (which == 1 ? ot : kt);
     const float s = which == 0 ? scales[head * 4 + 0]
                   : (which == 1 ? scales[head * 4 + 3] : scales[head * G * 4 + 1]);
+    // Transposed into LDS first (8-byte writes spread over the tile), then
+    // copied out in 16-byte chunks that consecutive threads take in order.
+    __shared__ __attribute__((aligned(16))) char img[TileT::BYTES];
     TileT tl;
     tl.load(src + (size_t)head * N * DT + part * D, tile * 64, N, threadIdx.x);
-    tl.template store_transposed<true>(dst + (((size_t)head * T + tile) * NP + part) * TileT::BYTES,
-                                       threadIdx.x, s);
+    tl.template store_transposed<true>(img, threadIdx.x, s);
+    __syncthreads();
+    char* out = dst + (((size_t)head * T + tile) * NP + part) * TileT::BYTES;
+#pragma unroll
+    for (int i = threadIdx.x; i < TileT::BYTES / 16; i += 256)
+        *(u32x4_t*)(out + 16 * i) = *(const u32x4_t*)(img + 16 * i);
 }
 
 // ---------------------------------------------------------------------------
