@@ -40,9 +40,12 @@ DecodeWorkspace decode_workspace_layout(long long B, long long Hkv, long long Nk
     DecodeWorkspace w;
     const long long bhkv = B * Hkv;
     const long long tiles = (Nk + kDecTile - 1) / kDecTile;
-    // About 4096 waves in all (two rounds of eight per compute unit), at
-    // least one tile per range.
-    long long ns = (4096 + bhkv - 1) / bhkv;
+    // One round of waves: as many ranges as the compute units hold at once
+    // (256 units x 16, 8 or 4 waves at d = 64, 128, 256: the register and LDS
+    // budgets of the split kernel), at least one tile per range. A second
+    // round only adds a tail.
+    const long long waves = 256LL * (d <= 64 ? 16 : (d <= 128 ? 8 : 4));
+    long long ns = (waves + bhkv - 1) / bhkv;
     ns = ns < 1 ? 1 : (ns > tiles ? tiles : ns);
     const long long per = (tiles + ns - 1) / ns;          // tiles per range
     w.split_len = (int)(per * kDecTile);
