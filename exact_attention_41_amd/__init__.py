@@ -14,6 +14,7 @@ If the library is not built, every call raises: there is no fallback.
     o, lse = fa_fwd_rect(q, k, v, causal=True)   # any Nq, Nk; bottom-right causal
     dq, dk, dv = fa_bwd_rect(q, k, v, o, do, lse, causal=True)
     o, lse = fa_fwd_fp8(q8, k8, v8, dq, dk, dv)  # e4m3 inputs with per-tensor factors
+    o = fa_attention(q, k, v, causal=True)       # autograd: backward through fa_bwd_rect
 """
 from __future__ import annotations
 
@@ -26,7 +27,7 @@ __all__ = ["fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_bwd_workspace_size", "fa_status
            "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_gqa", "fa_bwd_gqa",
            "fa_bwd_gqa_workspace_size", "fa_decode", "fa_decode_workspace_size", "fa_fwd_rect",
            "fa_fwd_fp8", "fa_bwd_rect", "fa_bwd_rect_workspace_size", "fa_clock_probe",
-           "FAError", "library_path"]
+           "fa_attention", "FAError", "library_path"]
 
 
 class FAError(RuntimeError):
@@ -392,3 +393,40 @@ def fa_clock_probe(samples, sleep_units: int = 1, stream=None) -> None:
                                         st.cuda_stream)
     if rc != _lib.FA_OK:
         raise FAError(rc, "fa_clock_probe")
+
+
+_AUTOGRAD_FN = None
+
+
+def _autograd_fn():
+    """torch.autograd.Function over fa_fwd_rect / fa_bwd_rect (built once)."""
+    global _AUTOGRAD_FN
+    if _AUTOGRAD_FN is None:
+        torch = _torch()
+
+        class _Attention(torch.autograd.Function):
+            @staticmethod
+            def forward(ctx, q, k, v, causal, scale):
+                o, lse = fa_fwd_rect(q, k, v, causal=causal, scale=scale)
+                ctx.save_for_backward(q, k, v, o, lse)
+                ctx.causal, ctx.scale = causal, scale
+                return o
+
+            @staticmethod
+            def backward(ctx, do):
+                q, k, v, o, lse = ctx.saved_tensors
+                dq, dk, dv = fa_bwd_rect(q, k, v, o, do.contiguous(), lse, causal=ctx.causal,
+                                         scale=ctx.scale)
+                return dq, dk, dv, None, None
+
+        _AUTOGRAD_FN = _Attention
+    return _AUTOGRAD_FN
+
+
+def fa_attention(q, k, v, causal: bool = False, scale: Optional[float] = None):
+    """Attention with autograd: O = softmax(scale Q K^T) V for bf16 q [B,H,Nq,d]
+    and k, v [B,Hkv,Nk,d] on a GPU (Hkv dividing H; query row i at position
+    Nk - Nq + i, bottom-right causal). The forward is fa_fwd_rect; the
+    gradient of a loss with respect to q, k and v is fa_bwd_rect, fed the
+    saved O and logsumexp. Both run in libfa.so."""
+    return _autograd_fn().apply(q, k, v, bool(causal), _scale(scale, q.shape[-1]))
