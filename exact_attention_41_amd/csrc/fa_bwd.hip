@@ -43,6 +43,24 @@ namespace fa {
 #endif
 // LDS fragments are read this many products ahead of their use.
 constexpr int kFragAhead = FA_BWD_FRAG_AHEAD;
+#ifndef FA_BWD_DQ_FRAG_AHEAD
+#define FA_BWD_DQ_FRAG_AHEAD 7
+#endif
+// The same for the dQ pass, whose fragment ring (one more than this) runs
+// on across steps and so must divide the products of every step.
+constexpr int kDqFragAhead = FA_BWD_DQ_FRAG_AHEAD;
+
+// Vector-memory wait (the global-to-LDS copies) and a workgroup barrier that
+// lets LDS reads stay in flight across it (__syncthreads waits for them). The
+// empty asm statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void wait_copies() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+__device__ __forceinline__ void step_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+}
 
 // ---------------------------------------------------------------------------
 // Workspace layout (byte offsets; every block 256-byte aligned).
@@ -290,7 +308,11 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     constexpr int BLK = TB / 1024;         // its 1 KB staging blocks
     constexpr int OFF_K = 0, OFF_V = TB, OFF_KT = 2 * TB;
     constexpr int BUF = 3 * TB;
-    __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
+    // Three buffers: while step s is computed from buffer s % 3, step s + 1
+    // is staged into the next one, and the last fragments of step s - 1 may
+    // still be in flight from the third.
+    constexpr int NBUF = 3;
+    __shared__ __attribute__((aligned(16))) char smem[NBUF * BUF];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -376,16 +398,43 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         pb[8 + k] = s0 + tr_slot_offset(32 * (k & 1) + l32, 2 * (2 * (k >> 1) + g));
     }
 
+    // Fragment o of a step (o < 2 NSD: the S/dP fragments, in product
+    // order; then the K~^T fragments of the dQ sums) in the buffer `delta`
+    // bytes past the current bases.
+    constexpr int NSD = 2 * KS;
+    constexpr int LA = kDqFragAhead;
+    auto frag = [&](int o, int delta) -> u32x4_t {
+        if (o < 2 * NSD) {
+            const int jb = o / NSD, w = o % NSD, st = w >> 1;
+            const int k = (D == 64) ? jb * KS + st : st;
+            const int off = ((w & 1) ? OFF_V : OFF_K) + ((D == 64) ? 0 : jb * 32 * D * 2);
+            return *(const lds_u32x4_t*)(pb[k] + delta + off);
+        }
+        const int w = o - 2 * NSD, t4 = w / NB, nb = w % NB;
+        const int off = OFF_KT + (nb - (nb & 1)) * 32 * 128;
+        return *(const lds_u32x4_t*)(pb[8 + 2 * t4 + (nb & 1)] + delta + off);
+    };
+
     {
         constexpr int NP0 = (NC == 1 ? 3 : 2) * PPT;
 #pragma unroll
         for (int k = 0; k < NP0; ++k) stage_part(0, 0, 0, k);
     }
     __syncthreads();
+    // The fragment ring, carried from step to step: product o of a step
+    // takes fr[o % (LA + 1)], and the first LA fragments of the next step
+    // are read during the last LA products of this one.
+    u32x4_t fr[LA + 1];
+#pragma unroll
+    for (int o = 0; o < LA; ++o) fr[o] = frag(o, 0);
 
     // One key tile: NC column steps, each staging the next step (the next
-    // column step of this tile, or the first of the next tile), running its
-    // products and moving the bases to the other buffer.
+    // column step of this tile, or the first of the next tile) into the next
+    // buffer, running its products and moving the bases to that buffer.
+    // Every wave waits at one barrier per step, LA products before the
+    // step's end: by then its copies of the next step have landed, so after
+    // it every wave may read the next step, and every wave has read all of
+    // the previous step, whose buffer the step after the next one reuses.
     auto iteration = [&](int t, auto mask_tag) {
         const int j0 = t * BC;
         f32x16_t sa[2], da[2];
@@ -402,32 +451,19 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             constexpr int CS = decltype(cs_tag)::value;
             constexpr bool LAST = CS == NC - 1;
             constexpr bool MASK = decltype(mask_tag)::value;
-            constexpr int NSD = 2 * KS;
             constexpr int NOPS = LAST ? 2 * NSD + 4 * NB : 2 * NSD;
-            constexpr int LA = kFragAhead;
+            static_assert(NOPS % (LA + 1) == 0, "the fragment ring must wrap at a step's end");
+            static_assert(LA < 2 * NSD, "the next step's first fragments are S/dP fragments");
             constexpr int EPO_A = 16 / NSD;
             constexpr int EPO_B = 16 / (2 * NB);
             // the step staged meanwhile and its parts
             constexpr int NCS = LAST ? 0 : CS + 1;
             constexpr int NPART = (NCS == NC - 1 ? 3 : 2) * PPT;
+            static_assert(NPART <= NSD, "the copies go among the first S/dP products");
             const int nt = LAST ? t + 1 : t;
             const int sidx = t * NC + CS;
-            lds_char* const* bb = pb;
-            auto frag = [&](int o) -> u32x4_t {
-                if (o < 2 * NSD) {
-                    const int jb = o / NSD, w = o % NSD, st = w >> 1;
-                    const int k = (D == 64) ? jb * KS + st : st;
-                    const int off = ((w & 1) ? OFF_V : OFF_K) + ((D == 64) ? 0 : jb * 32 * D * 2);
-                    return *(const lds_u32x4_t*)(bb[k] + off);
-                }
-                const int w = o - 2 * NSD, t4 = w / NB, nb = w % NB;
-                const int off = OFF_KT + (nb - (nb & 1)) * 32 * 128;
-                return *(const lds_u32x4_t*)(bb[8 + 2 * t4 + (nb & 1)] + off);
-            };
-
-            u32x4_t fr[LA + 1];
-#pragma unroll
-            for (int o = 0; o < LA; ++o) fr[o] = frag(o);
+            const int cur = sidx % NBUF;
+            const int nxt = (cur == NBUF - 1) ? -(NBUF - 1) * BUF : BUF;   // to the next buffer
 
             float pv[16], ev[16];
             u32x4_t pf[4], ef[4];
@@ -450,7 +486,14 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
 #pragma unroll
             for (int o = 0; o < NOPS; ++o) {
-                if (o + LA < NOPS) fr[(o + LA) % (LA + 1)] = frag(o + LA);
+                if (o == NOPS - LA) {
+                    // this wave's copies of the next step have landed; after
+                    // the barrier everyone's have
+                    wait_copies();
+                    step_barrier();
+                }
+                if (o + LA < NOPS) fr[(o + LA) % (LA + 1)] = frag(o + LA, 0);
+                else fr[(o + LA) % (LA + 1)] = frag(o + LA - NOPS, nxt);
                 const u32x4_t a = fr[o % (LA + 1)];
                 if (o < 2 * NSD) {
                     const int jb = o / NSD, w = o % NSD, st = w >> 1;
@@ -474,20 +517,16 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                         for (int e = 0; e < EPO_B; ++e) softmax_elem(1, w * EPO_B + e);
                     }
                 }
-                // The next step's loads: in the VALU-free dQ steps of the
-                // last column step, else among the S/dP products.
-                constexpr int O0 = LAST ? 2 * NSD + 2 * NB : 0;
+                // The next step's copies, among the first S/dP products
+                // (VALU-free in every step), well before the barrier.
 #pragma unroll
                 for (int k = 0; k < NPART; ++k)
-                    if (o == O0 + k * (NOPS - O0) / NPART) stage_part(nt, NCS, (sidx + 1) & 1, k);
+                    if (o == k * NSD / NPART) stage_part(nt, NCS, (cur + 1) % NBUF, k);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            // the bases move to the other buffer
-            const int stp = (sidx & 1) ? -BUF : BUF;
+            // the bases move to the next buffer
 #pragma unroll
-            for (int k = 0; k < 16; ++k) pb[k] += stp;
-
-            __syncthreads();   // the next step has landed; every wave is done with this one
+            for (int k = 0; k < 16; ++k) pb[k] += nxt;
         };
         step(IntTag<0>{}, mask_tag);
         if constexpr (NC > 1) step(IntTag<1>{}, mask_tag);
