@@ -38,22 +38,23 @@
 
 namespace fa {
 
-#ifndef FA_BWD_FRAG_AHEAD
-#define FA_BWD_FRAG_AHEAD 4
-#endif
-// LDS fragments are read this many products ahead of their use.
-constexpr int kFragAhead = FA_BWD_FRAG_AHEAD;
+// LDS fragments are read this many products ahead of their use, in the dQ
+// and the dK/dV pass. The ring of fragment registers (one more than this)
+// runs on from step to step, so it must divide the products of every step.
 #ifndef FA_BWD_DQ_FRAG_AHEAD
 #define FA_BWD_DQ_FRAG_AHEAD 7
 #endif
-// The same for the dQ pass, whose fragment ring (one more than this) runs
-// on across steps and so must divide the products of every step.
 constexpr int kDqFragAhead = FA_BWD_DQ_FRAG_AHEAD;
+#ifndef FA_BWD_DKDV_FRAG_AHEAD
+#define FA_BWD_DKDV_FRAG_AHEAD 7
+#endif
+constexpr int kDkdvFragAhead = FA_BWD_DKDV_FRAG_AHEAD;
 
 // Vector-memory wait (the global-to-LDS copies) and a workgroup barrier that
 // lets LDS reads stay in flight across it (__syncthreads waits for them). The
 // empty asm statements keep the compiler from moving memory accesses across.
 __device__ __forceinline__ void wait_copies() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }     // lgkmcnt(0)
 __device__ __forceinline__ void step_barrier() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
@@ -605,9 +606,19 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     constexpr int NB = D / 32;
     constexpr int TB = 64 * D * 2;
     constexpr int BLK = TB / 1024;
-    constexpr int OFF_Q = 0, OFF_DO = TB, OFF_QT = 2 * TB, OFF_DOT = 3 * TB, OFF_ST = 4 * TB;
-    constexpr int BUF = 4 * TB + 1024;
-    __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
+    // LDS: two buffers of row-major Q and dO tiles (read by the S and dP
+    // products; one per column step), two of transposed images (read by the
+    // dV and dK products; one per query tile) and three of statistics. The
+    // row-major and image buffers turn over at different points of a step,
+    // which is what lets one barrier per step, between the S/dP and the
+    // gradient products, serve both (see the loop below).
+    constexpr int OFF_Q = 0, OFF_DO = TB;        // within a row-major buffer
+    constexpr int OFF_QT = 0, OFF_DOT = TB;      // within an image buffer
+    // (A statistics copy fills 1 KB of LDS: 512 bytes of values, then the
+    // lanes past them repeat the last chunk.)
+    constexpr int RBUF = 2 * TB, IBUF = 2 * TB, TBUF = 1024;
+    constexpr int OFF_R = 0, OFF_I = 2 * RBUF, OFF_T = 2 * RBUF + 2 * IBUF;
+    __shared__ __attribute__((aligned(16))) char smem[OFF_T + 3 * TBUF];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -654,67 +665,128 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     // n_tiles: then no query sees it and dK = dV = 0).
     const int t0 = CAUSAL ? min(max(k0 - off, 0) / BQ, n_tiles) : 0;
 
-    // Column step cs of query tile t of group member gq (query head qh0 + gq)
-    // into buffer buf: Q and dO rows (bf16, swizzled) and, for the last step,
-    // this part's two transposed fp16 images, BLK 1 KB blocks each spread over
-    // the NW waves (part k of the step's parts is one block of this wave), and
-    // the tile's 128 statistics (wave 0). Past the last tile of the last
-    // member the buffer is filled from a valid tile and never read.
+    // Column step cs of query tile t of group member gq (query head qh0 + gq):
+    // stage_r puts its Q and dO rows (bf16, swizzled) into row-major buffer
+    // rb, stage_i the tile's two transposed fp16 images (this part's columns)
+    // into image buffer ib, BLK 1 KB blocks each spread over the NW waves
+    // (part k is one block of this wave); stage_stats the tile's 128
+    // statistics into statistics buffer sb (wave 0). Tiles past the last of
+    // the last member are filled from a valid tile and never read.
     constexpr int PPT = BLK / NW;
-    auto stage_part = [&](int gq, int t, int cs, int buf, int k) {
-        lds_char* base = (lds_char*)(smem + buf * BUF);
-        const int tensor = k / PPT, b = wave + NW * (k % PPT);
-        const bool live = gq < G && t < n_tiles;
-        const size_t qh = (size_t)(qh0 + (live ? gq : 0));
-        const size_t ti = (size_t)(live ? t : 0);
-        if (tensor < 2)
-            stage_tile_block<D, DT>((tensor == 0 ? Q : dO) + qh * N * DT + cs * D,
-                                    base + (tensor == 0 ? OFF_Q : OFF_DO), (int)ti * BQ, N, b,
-                                    lane);
-        else
-            stage_image_block_full((tensor == 2 ? qt_img : ot_img) + ((qh * T + ti) * NC + part) * TB,
-                                   base + (tensor == 2 ? OFF_QT : OFF_DOT), b, lane);
+    auto live_head = [&](int gq, int t) -> size_t {
+        return (size_t)(qh0 + ((gq < G && t < n_tiles) ? gq : 0));
     };
-    auto stage_stats = [&](int gq, int t, int buf) {
-        lds_char* base = (lds_char*)(smem + buf * BUF);
-        const bool live = gq < G && t < n_tiles;
-        const size_t qh = (size_t)(qh0 + (live ? gq : 0));
-        const size_t ti = (size_t)(live ? t : 0);
-        if (wave == 0) stage_image_block(stats + (qh * T + ti) * 128, 512, base + OFF_ST, 0, lane);
+    auto live_tile = [&](int gq, int t) -> size_t { return (size_t)((gq < G && t < n_tiles) ? t : 0); };
+    auto stage_r = [&](int gq, int t, int cs, int rb, int k) {
+        lds_char* base = (lds_char*)(smem + OFF_R + rb * RBUF);
+        const int tensor = k / PPT, b = wave + NW * (k % PPT);
+        const size_t qh = live_head(gq, t), ti = live_tile(gq, t);
+        stage_tile_block<D, DT>((tensor == 0 ? Q : dO) + qh * N * DT + cs * D,
+                                base + (tensor == 0 ? OFF_Q : OFF_DO), (int)ti * BQ, N, b, lane);
+    };
+    auto stage_i = [&](int gq, int t, int ib, int k) {
+        lds_char* base = (lds_char*)(smem + OFF_I + ib * IBUF);
+        const int tensor = k / PPT, b = wave + NW * (k % PPT);
+        const size_t qh = live_head(gq, t), ti = live_tile(gq, t);
+        stage_image_block_full((tensor == 0 ? qt_img : ot_img) + ((qh * T + ti) * NC + part) * TB,
+                               base + (tensor == 0 ? OFF_QT : OFF_DOT), b, lane);
+    };
+    auto stage_stats = [&](int gq, int t, int sb) {
+        lds_char* base = (lds_char*)(smem + OFF_T + sb * TBUF);
+        const size_t qh = live_head(gq, t), ti = live_tile(gq, t);
+        if (wave == 0) stage_image_block(stats + (qh * T + ti) * 128, 512, base, 0, lane);
+    };
+    // The query tile after (gq, t): the member's next tile, else the next
+    // member's first.
+    auto next_tile = [&](int& gq, int& t) {
+        if (t + 1 < n_tiles) {
+            ++t;
+        } else {
+            ++gq;
+            t = t0;
+        }
     };
 
-    // Lane-dependent LDS bases of buffer 0: pb[k], k < 8, for the row-major
-    // S/dP fragments (chunk step s; for d = 64 also the query half) and
-    // pb[8 + 2 t4 + (nb & 1)] for the transposed dV/dK fragments; everything
-    // else in a fragment address is a compile-time offset, so each read is
-    // one ds_read with an immediate offset from a base moved once per step.
+    // Lane-dependent LDS bases: pb[k], k < 8, for the row-major S/dP
+    // fragments of row-major buffer 0 (chunk step s; for d = 64 also the
+    // query half) and pb[8 + 2 t4 + (nb & 1)] for the transposed dV/dK
+    // fragments of image buffer 0; everything else in a fragment address is
+    // a compile-time offset, so each read is one ds_read with an immediate
+    // offset from a base moved once per step (row-major) or per query tile
+    // (images, statistics).
     lds_char* const s0 = (lds_char*)smem;
     lds_char* pb[16];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
         const int ib = (D == 64) ? k / KS : 0, st = (D == 64) ? k % KS : k;
-        pb[k] = s0 + row_chunk_offset<D>(32 * ib + l32, 2 * st + g);
-        pb[8 + k] = s0 + tr_slot_offset(32 * (k & 1) + l32, 2 * (2 * (k >> 1) + g));
+        pb[k] = s0 + OFF_R + row_chunk_offset<D>(32 * ib + l32, 2 * st + g);
+        pb[8 + k] = s0 + OFF_I + tr_slot_offset(32 * (k & 1) + l32, 2 * (2 * (k >> 1) + g));
     }
-    lds_char* pst = s0 + OFF_ST + 16 * g;
+    lds_char* pst = s0 + OFF_T + 16 * g;
 
+    constexpr int NSD = 2 * KS;
+    constexpr int NG = 2 * NB;
+    constexpr int LA = kDkdvFragAhead;
+    // Fragment o of a step (o < 2 NSD: S/dP fragments in product order, from
+    // the row-major buffer `dr` bytes past the current one; then the dV/dK
+    // fragments from the current image buffer).
+    auto frag = [&](int o, int dr) -> u32x4_t {
+        if (o < 2 * NSD) {
+            const int ib = o / NSD, w = o % NSD, st = w >> 1;
+            const int k = (D == 64) ? ib * KS + st : st;
+            const int off = ((w & 1) ? OFF_DO : OFF_Q) + ((D == 64) ? 0 : ib * 32 * D * 2);
+            return *(const lds_u32x4_t*)(pb[k] + dr + off);
+        }
+        const int w = o - 2 * NSD, t4 = w / NG, nb = (w % NG) >> 1;
+        const int off = ((w & 1) ? OFF_QT : OFF_DOT) + (nb - (nb & 1)) * 32 * 128;
+        return *(const lds_u32x4_t*)(pb[8 + 2 * t4 + (nb & 1)] + off);
+    };
+
+    // Prologue: the first two column steps' rows, the first tile's images
+    // and statistics (and, with one step per tile, the second tile's
+    // statistics): everything read before the first step's barrier or right
+    // after it.
     {
-        constexpr int NP0 = (NC == 1 ? 4 : 2) * PPT;
+        int g1 = 0, t1 = t0;
+        next_tile(g1, t1);
 #pragma unroll
-        for (int k = 0; k < NP0; ++k) stage_part(0, t0, 0, 0, k);
-        if (NC == 1) stage_stats(0, t0, 0);
+        for (int k = 0; k < 2 * PPT; ++k) {
+            stage_r(0, t0, 0, 0, k);
+            if (NC == 1) stage_r(g1, t1, 0, 1, k);
+            else stage_r(0, t0, 1, 1, k);
+            stage_i(0, t0, 0, k);
+        }
+        stage_stats(0, t0, 0);
+        if (NC == 1) stage_stats(g1, t1, 1);
     }
     __syncthreads();
+    // The fragment ring, carried from step to step: product o of a step
+    // takes fr[o % (LA + 1)], and the first LA fragments of the next step
+    // are read during the last LA products of this one.
+    u32x4_t fr[LA + 1];
+#pragma unroll
+    for (int o = 0; o < LA; ++o) fr[o] = frag(o, 0);
 
-    // One query tile of group member gq: NC column steps, each staging the
-    // next step (the next column step of this tile, or the first of the
-    // member's next tile, or of the next member's first), running its
-    // products and moving the bases.
+    // One query tile of group member gq: NC column steps. Step s (counting
+    // column steps from the first) has one barrier, LA products before its
+    // last S/dP product. Before it each wave waits for its own copies and
+    // for its LDS reads of the row-major buffer; so after it the next step's
+    // rows, this tile's images and the next tile's statistics have landed
+    // for every wave, and no wave reads step s's rows any more. Then each
+    // wave copies step s + 2's rows into step s's row-major buffer and, in
+    // the last step of a tile, the next tile's images into the other image
+    // buffer (the previous tile's, finished in the previous step) and the
+    // statistics of the tile that step s + 2 belongs to into the third
+    // statistics buffer. The fragment reads run on through the barrier (the
+    // dV/dK fragments of this step) and into the next step.
     const int nt = n_tiles - t0;
     auto iteration = [&](int gq, int t, auto mask_tag) {
         const int i0 = t * BQ;
-        const int ngq = (t + 1 < n_tiles) ? gq : gq + 1;
-        const int nt1 = (t + 1 < n_tiles) ? t + 1 : t0;
+        const int L = gq * nt + t - t0;    // query tiles before this one
+        int ga = gq, ta = t;               // the next tile
+        next_tile(ga, ta);
+        int gb = ga, tb = ta;              // the one after
+        next_tile(gb, tb);
         f32x16_t sa[2], da[2];
 
         // One column step as a software pipeline: S, dP of query half 0, then
@@ -728,41 +800,31 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             constexpr int CS = decltype(cs_tag)::value;
             constexpr bool LAST = CS == NC - 1;
             constexpr bool MASK = decltype(mask_tag)::value;
-            constexpr int NSD = 2 * KS;
-            constexpr int NG = 2 * NB;
             constexpr int NOPS = LAST ? 2 * NSD + 4 * NG : 2 * NSD;
-            constexpr int LA = kFragAhead;
+            static_assert(NOPS % (LA + 1) == 0, "the fragment ring must wrap at a step's end");
+            static_assert(LA < 2 * NSD, "the barrier falls among the S/dP products");
             constexpr int EPO_A = 16 / NSD;
             constexpr int EPO_B = 16 / (2 * NG);
-            constexpr int NCS = LAST ? 0 : CS + 1;
-            constexpr bool NLAST = NCS == NC - 1;
-            constexpr int NPART = (NLAST ? 4 : 2) * PPT;
-            const int sgq = LAST ? ngq : gq, st_t = LAST ? nt1 : t;
-            const int buf = (((gq * nt + t - t0) * NC) + CS) & 1;
-            lds_char* const* bb = pb;
-            lds_char* const bst = pst;
-            auto frag = [&](int o) -> u32x4_t {
-                if (o < 2 * NSD) {
-                    const int ib = o / NSD, w = o % NSD, st = w >> 1;
-                    const int k = (D == 64) ? ib * KS + st : st;
-                    const int off = ((w & 1) ? OFF_DO : OFF_Q) + ((D == 64) ? 0 : ib * 32 * D * 2);
-                    return *(const lds_u32x4_t*)(bb[k] + off);
-                }
-                const int w = o - 2 * NSD, t4 = w / NG, nb = (w % NG) >> 1;
-                const int off = ((w & 1) ? OFF_QT : OFF_DOT) + (nb - (nb & 1)) * 32 * 128;
-                return *(const lds_u32x4_t*)(bb[8 + 2 * t4 + (nb & 1)] + off);
-            };
-
-            u32x4_t fr[LA + 1];
-#pragma unroll
-            for (int o = 0; o < LA; ++o) fr[o] = frag(o);
+            constexpr int OB = 2 * NSD - LA;      // the barrier, before product OB
+            // Copies after the barrier: in the VALU-free dV/dK products of a
+            // last step, else among the products left after the barrier.
+            constexpr int O0 = LAST ? 2 * NSD + 2 * NG : OB;
+            constexpr int NPR = 2 * PPT;          // row-major parts of a step
+            constexpr int NPI = LAST ? 2 * PPT : 0;
+            constexpr int NPART = NPR + NPI;
+            const int sidx = L * NC + CS;
+            const int rcur = sidx & 1;
+            const int rnxt = rcur ? -RBUF : RBUF;  // to the other row-major buffer
+            // Step s + 2: the same column step of the tile after the next
+            // (one step per tile) or of the next tile.
+            const int g2 = NC == 1 ? gb : ga, t2 = NC == 1 ? tb : ta;
 
             f32x4_t l4[4], d4[4];     // lse*log2e and sE*D of the half being exponentiated
             float pv[16], dsv[16];
             u32x4_t pp[4], dsp[4];
             auto read_stats = [&](int ib, int q4) {
-                l4[q4] = *(const lds_f32x4_t*)(bst + (32 * ib + 8 * q4) * 4);
-                d4[q4] = *(const lds_f32x4_t*)(bst + 256 + (32 * ib + 8 * q4) * 4);
+                l4[q4] = *(const lds_f32x4_t*)(pst + (32 * ib + 8 * q4) * 4);
+                d4[q4] = *(const lds_f32x4_t*)(pst + 256 + (32 * ib + 8 * q4) * 4);
             };
             auto softmax_elem = [&](int ib, int r) {
                 const int q4 = r >> 2, r4 = r & 3;
@@ -782,7 +844,13 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
 #pragma unroll
             for (int o = 0; o < NOPS; ++o) {
-                if (o + LA < NOPS) fr[(o + LA) % (LA + 1)] = frag(o + LA);
+                if (o == OB) {
+                    wait_copies();
+                    wait_lds();
+                    step_barrier();
+                }
+                if (o + LA < NOPS) fr[(o + LA) % (LA + 1)] = frag(o + LA, 0);
+                else fr[(o + LA) % (LA + 1)] = frag(o + LA - NOPS, rnxt);
                 const u32x4_t a = fr[o % (LA + 1)];
                 if (LAST && o == 0) {
 #pragma unroll
@@ -810,22 +878,25 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                         for (int e = 0; e < EPO_B; ++e) softmax_elem(1, w * EPO_B + e);
                     }
                 }
-                // The next step's loads: in the VALU-free dV/dK steps of the
-                // last column step, else among the S/dP products.
-                constexpr int O0 = LAST ? 2 * NSD + 2 * NG : 0;
 #pragma unroll
                 for (int k = 0; k < NPART; ++k)
-                    if (o == O0 + k * (NOPS - O0) / NPART) stage_part(sgq, st_t, NCS, buf ^ 1, k);
-                if (NLAST && o == O0 + 1) stage_stats(sgq, st_t, buf ^ 1);
+                    if (o == O0 + k * (NOPS - O0) / NPART) {
+                        if (k < NPR) stage_r(g2, t2, CS, rcur, k);
+                        else stage_i(ga, ta, (L + 1) & 1, k - NPR);
+                    }
+                if (LAST && o == O0 + 1) stage_stats(g2, t2, (L + (NC == 1 ? 2 : 1)) % 3);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            // the bases move to the other buffer
-            const int stp = buf ? -BUF : BUF;
+            // the row-major bases move to the other buffer; after a tile's
+            // last step the image and statistics bases move to the next tile's
 #pragma unroll
-            for (int k = 0; k < 16; ++k) pb[k] += stp;
-            pst += stp;
-
-            __syncthreads();   // the next step has landed; every wave is done with this one
+            for (int k = 0; k < 8; ++k) pb[k] += rnxt;
+            if constexpr (LAST) {
+                const int inxt = (L & 1) ? -IBUF : IBUF;
+#pragma unroll
+                for (int k = 8; k < 16; ++k) pb[k] += inxt;
+                pst += (L % 3 == 2) ? -2 * TBUF : TBUF;
+            }
         };
         step(IntTag<0>{}, mask_tag);
         if constexpr (NC > 1) step(IntTag<1>{}, mask_tag);
