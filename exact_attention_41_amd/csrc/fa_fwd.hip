@@ -277,6 +277,7 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         v_load(0);                         // writes its half of V(0) meanwhile
         v_store(0);
         wait_vmem();
+        wait_lds();
         wg_barrier();
     }
 
@@ -303,6 +304,7 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             __builtin_amdgcn_sched_barrier(0);
             if (t + grp < n_tiles) v_store(tv);
             wait_vmem();
+            wait_lds();     // the V writes are complete before the barrier publishes them
             wg_barrier();
         }
     }

@@ -268,6 +268,7 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
         v_load(0);
         v_store(0);
         __builtin_amdgcn_s_waitcnt(0x0F70);
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the V writes are complete
         wg_barrier8();
     }
 
@@ -290,6 +291,7 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
             if (grp == 0) v_store(t);
             else if (t + 1 < n_tiles) v_store(t + 1);
             __builtin_amdgcn_s_waitcnt(0x0F70);
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the V writes are complete
             wg_barrier8();
         }
     }
