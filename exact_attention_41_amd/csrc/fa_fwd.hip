@@ -277,7 +277,6 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         v_load(0);                         // writes its half of V(0) meanwhile
         v_store(0);
         wait_vmem();
-        wait_lds();
         wg_barrier();
     }
 
@@ -304,7 +303,11 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             __builtin_amdgcn_sched_barrier(0);
             if (t + grp < n_tiles) v_store(tv);
             wait_vmem();
-            wait_lds();     // the V writes are complete before the barrier publishes them
+            // Group A's half of V(t) is read right after this barrier: its
+            // writes must be complete. Group B's half, V(t+1), is first read
+            // two barriers on, and the wait_lds at the end of B's next matrix
+            // slot completes it before the second.
+            if (grp == 0) wait_lds();
             wg_barrier();
         }
     }

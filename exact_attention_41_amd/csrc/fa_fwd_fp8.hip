@@ -268,7 +268,6 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
         v_load(0);
         v_store(0);
         __builtin_amdgcn_s_waitcnt(0x0F70);
-        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the V writes are complete
         wg_barrier8();
     }
 
@@ -291,7 +290,10 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
             if (grp == 0) v_store(t);
             else if (t + 1 < n_tiles) v_store(t + 1);
             __builtin_amdgcn_s_waitcnt(0x0F70);
-            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the V writes are complete
+            // Group A's V(t) is read right after this barrier: its writes must
+            // be complete (lgkmcnt(0)). Group B's V(t+1) is first read two
+            // barriers on, after the LDS wait that ends B's next matrix slot.
+            if (grp == 0) __builtin_amdgcn_s_waitcnt(0xC07F);
             wg_barrier8();
         }
     }
