@@ -274,6 +274,18 @@ def to_device(x: np.ndarray, dtype: str, device="cuda"):
     return t.to(device)
 
 
+def device_normal_bf16(shape, seed: int, device="cuda"):
+    """Seeded N(0, 1) draws made on the device by torch's generator for that
+    device (seeded with ``seed``), rounded once to bfloat16: for tensors too
+    large to draw on the host. Whatever the oracle is given of them is copied
+    back from the device, so both sides see the same values."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    x = torch.randn(tuple(shape), generator=g, device=device, dtype=torch.float32)
+    return x.to(torch.bfloat16)
+
+
 # ---------------------------------------------------------------- fp8 inputs
 E4M3_MAX = 448.0     # largest finite OCP e4m3 value
 
