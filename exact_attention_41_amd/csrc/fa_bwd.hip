@@ -31,8 +31,11 @@
 //
 // Every tile reaches LDS by direct global-to-LDS loads (row-major bf16 tiles
 // from the inputs, with the chunk swizzle applied through the source
-// addresses; transposed tiles as straight copies of their images), issued a
-// tile ahead into the second of two buffers; no tile passes through VGPRs.
+// addresses; transposed tiles as straight copies of their images), issued
+// ahead into LDS buffers of their own (three in the dQ pass; separate
+// row-major, image and statistics buffers in the dK/dV pass), so that each
+// pass needs one barrier per step and its fragment reads run on through it;
+// no tile passes through VGPRs.
 #include "fa_kernels.hpp"
 #include "fa_device.hpp"
 
