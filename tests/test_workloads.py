@@ -41,3 +41,18 @@ def test_workload_registry():
     assert w.fwd_flops() == 4 * 4 * 16 * 4096 ** 2 * 128 / 2
     assert w.bwd_flops() == 2.5 * w.fwd_flops()
     assert wl.WORKLOADS["bf16_b8h16n2048d64"].scale == 0.125
+
+
+def test_device_normal_bf16_is_seeded():
+    """The device-side generator (used for inputs too large for the host): the
+    same seed gives the same bits, another seed other values; bf16 draws of a
+    standard normal (exercised here on the CPU device)."""
+    import torch
+    a = wl.device_normal_bf16((4, 1000), 51, device="cpu")
+    b = wl.device_normal_bf16((4, 1000), 51, device="cpu")
+    c = wl.device_normal_bf16((4, 1000), 52, device="cpu")
+    assert a.dtype == torch.bfloat16 and tuple(a.shape) == (4, 1000)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert not torch.equal(a, c)
+    x = a.float()
+    assert abs(float(x.mean())) < 0.1 and abs(float(x.std()) - 1.0) < 0.1
