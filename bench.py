@@ -47,8 +47,8 @@ PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
 HEADLINE = "bf16_b4h16n4096d128_causal_bwd"
 SWEEP = ["bf16_b8h16n2048d64", "bf16_b8h16n2048d64_causal", "bf16_b2h32n8192d128_causal_x3",
          "bf16_b1h16n16384d128_causal", "bf16_b4h16n4096d128_causal_bwd"]
-KERNEL_SOURCES = ["fa_device.hpp", "fa_kernels.hpp", "fa_fwd.hip", "fa_fwd256.hip", "fa_bwd.hip",
-                  "fa_decode.hip"]
+KERNEL_SOURCES = ["fa_device.hpp", "fa_kernels.hpp", "fa_api.hip", "fa_fwd.hip", "fa_fwd256.hip",
+                  "fa_fwd_fp8.hip", "fa_bwd.hip", "fa_decode.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 COPY_BYTES = 512 << 20          # the calibration copy reads and writes this much
 # Kernel-name fragments -> the step's kernel names.
@@ -175,7 +175,7 @@ def gpu_step_timing(w, steps: int, warmup: int, with_clock: bool = True):
         fa.fa_fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
         if ev is not None:
             ev[1].record()
-        fa.fa_bwd_preprocess(q, k, v, do, ws)
+        fa.fa_bwd_preprocess(q, k, v, o, do, ws)
         if ev is not None:
             ev[2].record()
         fa.fa_bwd_dq(q, k, v, do, lse, ws, dq, causal=w.causal, scale=w.scale)
@@ -206,7 +206,7 @@ def gpu_step_timing(w, steps: int, warmup: int, with_clock: bool = True):
     # read).
     kernels = {
         "fwd": lambda: fa.fa_fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse),
-        "bwd_preprocess": lambda: fa.fa_bwd_preprocess(q, k, v, do, ws),
+        "bwd_preprocess": lambda: fa.fa_bwd_preprocess(q, k, v, o, do, ws),
         "bwd_dq": lambda: fa.fa_bwd_dq(q, k, v, do, lse, ws, dq, causal=w.causal,
                                        scale=w.scale),
         "bwd_dkdv": lambda: fa.fa_bwd_dkdv(q, k, v, do, ws, dk, dv, causal=w.causal,
@@ -572,7 +572,10 @@ def cpu_baseline(w, min_seconds: float = 10.0):
         from threadpoolctl import threadpool_limits
     except ImportError:  # pragma: no cover
         threadpool_limits = None
-    cores = min(len(os.sched_getaffinity(0)), 16)
+    # The host's cores available to this process, and the threads used: at
+    # most 16, one GPU's share of a host whose other GPUs may be busy.
+    host_cores = len(os.sched_getaffinity(0))
+    cores = min(host_cores, 16)
     inp = wl.workload_inputs(w)
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
 
@@ -598,7 +601,7 @@ def cpu_baseline(w, min_seconds: float = 10.0):
     per_head = (w.fwd_flops() + w.bwd_flops()) / len(heads)
     tflops = per_head * done / elapsed / 1e12
     return {"value": round(tflops, 5), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "cpu_model": cpu_model(),
+            "host_cores": host_cores, "host_cpu_count": os.cpu_count(), "cpu_model": cpu_model(),
             "sample": f"{done} of {len(heads)} heads of {w.name} (fwd+bwd, fp64 numpy, "
                       f"S/P materialised), {elapsed:.1f} s wall; counted flops as on the GPU"}
 

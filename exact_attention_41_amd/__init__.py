@@ -77,6 +77,18 @@ def _check(t, name, dtype, shape=None, device=None):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
+def _check_workspace(ws, device) -> int:
+    """A caller's workspace: a contiguous tensor on ``device``; returns its bytes."""
+    torch = _torch()
+    if not isinstance(ws, torch.Tensor):
+        raise TypeError("workspace must be a torch.Tensor")
+    if ws.device != device:
+        raise ValueError(f"workspace is on {ws.device}, expected {device}")
+    if not ws.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    return ws.numel() * ws.element_size()
+
+
 def _stream_ptr(device):
     return _torch().cuda.current_stream(device).cuda_stream
 
@@ -169,7 +181,7 @@ def _bwd(entry, q, k, v, o, do, lse, causal, scale, dq, dk, dv, workspace, group
     need = fa_bwd_rect_workspace_size(B, H, Hkv, N, Nk, d)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    ws_bytes = workspace.numel() * workspace.element_size()
+    ws_bytes = _check_workspace(workspace, q.device)
     heads = (B, H, Hkv) if grouped or rect else (B, H)
     sizes = (N, Nk) if rect else (N,)
     fn = getattr(_lib.load(), entry)
@@ -227,19 +239,17 @@ def _bwd_common(ref, tensors, lse, workspace):
     if workspace is None:
         raise ValueError("workspace is required (a uint8 device tensor of "
                          "fa_bwd_workspace_size(B, H, N, d) bytes)")
-    if workspace.device != ref.device:
-        raise ValueError("workspace must be on the device of the inputs")
-    return B, H, N, d, workspace.numel() * workspace.element_size()
+    return B, H, N, d, _check_workspace(workspace, ref.device)
 
 
-def fa_bwd_preprocess(q, k, v, do, workspace):
-    """Phase 1 of fa_bwd: per-head scale factors and the scaled fp16 transposed
-    copies of q, dO and k into ``workspace``."""
+def fa_bwd_preprocess(q, k, v, o, do, workspace):
+    """Phase 1 of fa_bwd: per-head scale factors, D^ = rowsum(dO * O) and the
+    scaled fp16 transposed copies of q, dO and k into ``workspace``."""
     torch = _torch()
-    B, H, N, d, ws = _bwd_common(k, [(q, "q"), (v, "v"), (do, "do")], None, workspace)
+    B, H, N, d, ws = _bwd_common(k, [(q, "q"), (v, "v"), (o, "o"), (do, "do")], None, workspace)
     with torch.cuda.device(k.device):
         st = _lib.load().fa_bwd_preprocess(q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                                           do.data_ptr(), workspace.data_ptr(), ws,
+                                           o.data_ptr(), do.data_ptr(), workspace.data_ptr(), ws,
                                            B, H, N, d, _stream_ptr(k.device))
     if st != _lib.FA_OK:
         raise FAError(st, "fa_bwd_preprocess")
@@ -301,7 +311,7 @@ def fa_decode(q, k, v, causal: bool = False, scale: Optional[float] = None, out=
     if workspace is None:
         need = fa_decode_workspace_size(B, H, Hkv, Nq, Nk, d)
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    ws_bytes = workspace.numel() * workspace.element_size()
+    ws_bytes = _check_workspace(workspace, q.device)
     with torch.cuda.device(q.device):
         st = _lib.load().fa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                    lse.data_ptr(), workspace.data_ptr(), ws_bytes, B, H, Hkv,

@@ -48,7 +48,7 @@ def load() -> ctypes.CDLL:
         lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                i, i, i, i, i, f, vp]
         lib.fa_bwd.restype = i
-        lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, vp, vp, ctypes.c_size_t, i, i, i, i, vp]
+        lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i, i, i, i, vp]
         lib.fa_bwd_preprocess.restype = i
         lib.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, ctypes.c_size_t, vp, vp,
                                     i, i, i, i, i, f, vp]

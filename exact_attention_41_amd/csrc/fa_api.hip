@@ -22,7 +22,9 @@ bool head_dim_ok(int d, bool wide) { return d == 64 || d == 128 || (wide && d ==
 // Shared size/scale checks. Returns FA_OK and sets *empty when B*H*N == 0.
 fa_status_t check_common(int B, int H, int N, int d, float scale, bool wide, bool* empty) {
     if (B < 0 || H < 0 || N < 0) return FA_ERR_INVALID_ARG;
-    if (!isfinite(scale) || scale < 0.f) return FA_ERR_INVALID_ARG;
+    // scale > 0: the kernels mask a score by making it -inf before scaling,
+    // which a zero scale would turn into NaN.
+    if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
     if (!head_dim_ok(d, wide)) return FA_ERR_UNSUPPORTED;
     *empty = (B == 0 || H == 0 || N == 0);
     if (*empty) return FA_OK;
@@ -185,11 +187,11 @@ fa_status_t check_bwd(std::initializer_list<const void*> tensors, bool need_lse,
     return FA_OK;
 }
 
-fa::BwdArgs bwd_args(const void* q, const void* k, const void* v, const void* dout,
-                     const float* lse, void* dq, void* dk, void* dv, void* workspace, int B,
-                     int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
-                     hipStream_t stream) {
-    return fa::BwdArgs{q, k, v, dout, lse, dq, dk, dv, workspace,
+fa::BwdArgs bwd_args(const void* q, const void* k, const void* v, const void* o,
+                     const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                     void* workspace, int B, int H, int Hkv, int Nq, int Nk, int d, int causal,
+                     float scale, hipStream_t stream) {
+    return fa::BwdArgs{q, k, v, o, dout, lse, dq, dk, dv, workspace,
                        B, H, Hkv, Nq, Nk, d, causal != 0, scale, stream};
 }
 
@@ -197,15 +199,15 @@ fa::BwdArgs bwd_args(const void* q, const void* k, const void* v, const void* do
 
 extern "C" {
 
-fa_status_t fa_bwd_preprocess(const void* q, const void* k, const void* v, const void* dout,
-                              void* workspace, size_t workspace_bytes, int B, int H, int N,
-                              int d, hipStream_t stream) {
+fa_status_t fa_bwd_preprocess(const void* q, const void* k, const void* v, const void* o,
+                              const void* dout, void* workspace, size_t workspace_bytes, int B,
+                              int H, int N, int d, hipStream_t stream) {
     bool empty = false;
-    FA_TRY(check_bwd({q, k, v, dout}, false, nullptr, workspace, workspace_bytes, B, H, H, N, N,
-                     d, 1.f, &empty));
+    FA_TRY(check_bwd({q, k, v, o, dout}, false, nullptr, workspace, workspace_bytes, B, H, H, N,
+                     N, d, 1.f, &empty));
     if (empty) return FA_OK;
-    const fa::BwdArgs a = bwd_args(q, k, v, dout, nullptr, nullptr, nullptr, nullptr, workspace,
-                                   B, H, H, N, N, d, 0, 1.f, stream);
+    const fa::BwdArgs a = bwd_args(q, k, v, o, dout, nullptr, nullptr, nullptr, nullptr,
+                                   workspace, B, H, H, N, N, d, 0, 1.f, stream);
     return fa::launch_bwd_prepare(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -216,7 +218,7 @@ fa_status_t fa_bwd_dq(const void* q, const void* k, const void* v, const void* d
     FA_TRY(check_bwd({q, k, v, dout, dq}, true, lse, workspace, workspace_bytes, B, H, H, N, N,
                      d, scale, &empty));
     if (empty) return FA_OK;
-    const fa::BwdArgs a = bwd_args(q, k, v, dout, lse, dq, nullptr, nullptr, workspace,
+    const fa::BwdArgs a = bwd_args(q, k, v, nullptr, dout, lse, dq, nullptr, nullptr, workspace,
                                    B, H, H, N, N, d, causal, scale, stream);
     return fa::launch_bwd_dq(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
@@ -228,7 +230,7 @@ fa_status_t fa_bwd_dkdv(const void* q, const void* k, const void* v, const void*
     FA_TRY(check_bwd({q, k, v, dout, dk, dv}, false, nullptr, workspace, workspace_bytes, B, H,
                      H, N, N, d, scale, &empty));
     if (empty) return FA_OK;
-    const fa::BwdArgs a = bwd_args(q, k, v, dout, nullptr, nullptr, dk, dv,
+    const fa::BwdArgs a = bwd_args(q, k, v, nullptr, dout, nullptr, nullptr, dk, dv,
                                    const_cast<void*>(workspace), B, H, H, N, N, d, causal, scale,
                                    stream);
     return fa::launch_bwd_dkdv(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
@@ -242,8 +244,8 @@ fa_status_t fa_bwd_rect(const void* q, const void* k, const void* v, const void*
     FA_TRY(check_bwd({q, k, v, o, dout, dq, dk, dv}, true, lse, workspace, workspace_bytes, B, H,
                      Hkv, Nq, Nk, d, scale, &empty));
     if (empty) return FA_OK;
-    const fa::BwdArgs a = bwd_args(q, k, v, dout, lse, dq, dk, dv, workspace, B, H, Hkv, Nq, Nk,
-                                   d, causal, scale, stream);
+    const fa::BwdArgs a = bwd_args(q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H, Hkv, Nq,
+                                   Nk, d, causal, scale, stream);
     if (fa::launch_bwd_prepare(a) != hipSuccess) return FA_ERR_HIP;
     if (fa::launch_bwd_dq(a) != hipSuccess) return FA_ERR_HIP;
     if (fa::launch_bwd_dkdv(a) != hipSuccess) return FA_ERR_HIP;
@@ -276,7 +278,7 @@ fa_status_t fa_decode(const void* q, const void* k, const void* v, void* o, floa
                       void* workspace, size_t workspace_bytes, int B, int H, int Hkv, int Nq,
                       int Nk, int d, int causal, float scale, hipStream_t stream) {
     if (B < 0 || H < 0 || Nq < 0 || Nk < 0) return FA_ERR_INVALID_ARG;
-    if (!isfinite(scale) || scale < 0.f) return FA_ERR_INVALID_ARG;
+    if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
     FA_TRY(check_heads(H, Hkv));
     if (!head_dim_ok(d, true)) return FA_ERR_UNSUPPORTED;
     if (B == 0 || H == 0 || Nq == 0) return FA_OK;

@@ -13,16 +13,22 @@
 // systems-analysis.info, section "Performance", calls the method exact and
 // deterministic):
 //   1. prepare: per head, the largest |x| of Q, K, V and dO, turned into
-//      power-of-two factors so that every fp16 operand below is exact (the
-//      bf16 inputs scaled by a power of two) and in range; then, per 64-row
+//      power-of-two factors so that every fp16 operand below (a bf16 input
+//      scaled by a power of two) is in range, and exact for |x| down to
+//      2^-17 of the head's largest (smaller values round, by at most 2^-24
+//      of the largest: fp16's subnormal step); then, per 64-row
 //      tile, fp16 images of (s_Q Q)^T, (s_dO dO)^T and (s_K K)^T laid out
 //      exactly as the transposed LDS tiles the next phases read.
+//      The same pass takes D^_i = dO_i . O_i from the bf16 O: not D itself
+//      (the rounding of O moves it too far), only a centre for step 2.
 //   2. dQ pass: one workgroup per query block, over the key tiles. D_i is not
-//      known before the pass, so it uses
-//          dQ_i = scale * (sum_j P_ij dP_ij K_j - D_i sum_j P_ij K_j)
-//      and accumulates both sums and D_i = sum_j P_ij dP_ij in the same pass;
-//      D is exact (not taken from the rounded O). It leaves lse and D per
-//      query tile in the workspace for the next pass.
+//      known before the pass, so with E_ij = P_ij (dP_ij - D^_i) it uses
+//          dQ_i = scale * (sum_j E_ij K_j - (D_i - D^_i) sum_j P_ij K_j)
+//      and accumulates both sums and D_i - D^_i = sum_j E_ij in the same
+//      pass; D is exact. Subtracting the centre before E is rounded keeps
+//      its rounding error proportional to |dP - D| rather than |dP| (large
+//      when V has a large mean). It leaves lse and D per query tile in the
+//      workspace for the next pass.
 //   3. dK/dV pass: one workgroup per key block, over the query tiles.
 // S and dP are products of the bf16 inputs themselves. The probabilities and
 // dS enter the gradient products as fp16 (11-bit significand) rather than
@@ -85,7 +91,8 @@ BwdWorkspace bwd_workspace_layout(long long B, long long H, long long Hkv, long 
     const size_t tile = 64 * (size_t)d * 2;             // one transposed 64-row tile
     w.scales = 0;
     w.partial = w.scales + align256(bh * 4 * 4);
-    w.stats = w.partial + align256((bh + bhkv) * chunks * 2 * 4);
+    w.dhat = w.partial + align256((bh + bhkv) * chunks * 2 * 4);
+    w.stats = w.dhat + align256(bh * (size_t)Nq * 4);
     w.qt = w.stats + align256(bh * tq * 128 * 4);
     w.ot = w.qt + align256(bh * tq * tile);
     w.kt = w.ot + align256(bh * tq * tile);
@@ -98,13 +105,15 @@ BwdWorkspace bwd_workspace_layout(long long B, long long H, long long Hkv, long 
 // tensors, as bf16 magnitude bits (for finite values the integer order of
 // (bits & 0x7fff) is the order of |x|): Q and dO (Nq rows) for the BH query
 // heads (rows r < BH of the grid), K and V (Nk rows) for the BHkv K/V heads
-// (rows r >= BH). Chunks past a tensor's rows record 0.
+// (rows r >= BH). Chunks past a tensor's rows record 0. For the query heads
+// it also forms D^_i = dO_i . O_i (fp32) of every row of the chunk.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ void __launch_bounds__(256)
 bwd_absmax_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                   const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-                  uint32_t* __restrict__ partial, int BH, int Nq, int Nk, int chunks) {
+                  const uint16_t* __restrict__ O, uint32_t* __restrict__ partial,
+                  float* __restrict__ dhat, int BH, int Nq, int Nk, int chunks) {
     constexpr int DCH = D / 8;
     const int bid = blockIdx.x;
     const int r = bid / chunks, ch = bid % chunks;
@@ -117,11 +126,26 @@ bwd_absmax_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
     uint32_t m[2] = {0u, 0u};
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
+        // Thread idx holds chunk idx % DCH of row idx / DCH (256 is a multiple
+        // of DCH, so a row's DCH chunks sit in DCH consecutive lanes, all in
+        // or all out of the loop together).
         for (int idx = threadIdx.x; idx < nrows * DCH; idx += 256) {
             const u32x4_t w = *(const u32x4_t*)(src[t] + (size_t)idx * 8);
 #pragma unroll
             for (int c = 0; c < 4; ++c)
                 m[t] = max(m[t], max(w[c] & 0x7fffu, (w[c] >> 16) & 0x7fffu));
+            if (t == 1 && !kv) {
+                const u32x4_t ow = *(const u32x4_t*)(O + base + (size_t)idx * 8);
+                float s = 0.f;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    s = __builtin_fmaf(bf16_lo(w[c]), bf16_lo(ow[c]), s);
+                    s = __builtin_fmaf(bf16_hi(w[c]), bf16_hi(ow[c]), s);
+                }
+#pragma unroll
+                for (int off = DCH / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
+                if (idx % DCH == 0) dhat[(size_t)r * Nq + row0 + idx / DCH] = s;
+            }
         }
     }
     __shared__ uint32_t red[4][2];
@@ -284,7 +308,9 @@ bwd_image_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 //   dP~^T = V (sE dO)^T        A = V tile (LDS, bf16)      B = sE dO^T (VGPRs)
 //   A~^T += K~^T (P*dP~)^T     A = (sK K)^T (LDS, fp16)    B = P*dP~ (fp16)
 //   B~^T += K~^T P^T           A = (sK K)^T (LDS, fp16)    B = P (fp16)
-// with sE = s_dO * s_V; finally dQ = scale/(sK sE) (A~ - D~ B~), D~ = sE D.
+// with sE = s_dO * s_V and the dP~ chain started from -sE D^ (so that the
+// accumulator holds dP~ - sE D^); finally dQ = scale/(sK sE) (A~ - D~ B~),
+// D~ = sE (D - D^) = sum_j P*dP~.
 // A head size DT above 128 runs as NC = DT/128 column parts: each key tile
 // is staged as NC steps of 128 columns of K and V, S and dP accumulate over
 // all of them, and each workgroup forms the dQ columns of one part (the
@@ -295,7 +321,8 @@ __global__ void __launch_bounds__(NW * 64, 1)
 bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
               const float* __restrict__ LSE, const float* __restrict__ scales,
-              const char* __restrict__ kt_img, float* __restrict__ stats,
+              const float* __restrict__ dhat, const char* __restrict__ kt_img,
+              float* __restrict__ stats,
               uint16_t* __restrict__ dQ, int BH, int G, int N, int Nk, int T, int Tk,
               float c, float scale, int nqb) {
     constexpr int D = DT > 128 ? 128 : DT;  // columns of one staged tile and of one dQ part
@@ -360,6 +387,12 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     // probability of theirs is then exactly 0.
     const float lse_i = (qi < N) ? LSE[(size_t)bh * N + qi] : kNegInf;
     const float lse2 = (lse_i == kNegInf) ? __builtin_huge_valf() : lse_i * kLog2e;
+    // The centre sE D^ of this row's dP~ (0 past N), as the start value of
+    // every dP~ chain.
+    const float dhs = (qi < N) ? sE * dhat[(size_t)bh * N + qi] : 0.f;
+    f32x16_t dinit;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dinit[r] = -dhs;
 
     f32x16_t acc_a[NB], acc_b[NB];
 #pragma unroll
@@ -505,9 +538,14 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                     const u32x4_t& bop = (w & 1) ? of[CS * KS + st] : qf[CS * KS + st];
                     // A chain's last product of a step carries the wait
                     // states a VALU read of its result needs.
-                    if (CS == 0 && st == 0) mfma_bf16_first<WS>(acc, a, bop);
-                    else if (st == KS - 1) mfma_bf16_last<WS>(acc, a, bop);
-                    else mfma_bf16_next<WS>(acc, a, bop);
+                    if (CS == 0 && st == 0) {
+                        if (w & 1) mfma_bf16_first_c<WS>(acc, a, bop, dinit);
+                        else mfma_bf16_first<WS>(acc, a, bop);
+                    } else if (st == KS - 1) {
+                        mfma_bf16_last<WS>(acc, a, bop);
+                    } else {
+                        mfma_bf16_next<WS>(acc, a, bop);
+                    }
                     if (LAST && jb == 1) {
 #pragma unroll
                         for (int e = 0; e < EPO_A; ++e) softmax_elem(0, w * EPO_A + e);
@@ -548,11 +586,11 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         agpr_settle(acc_a[nb]);
         agpr_settle(acc_b[nb]);
     }
-    const float dt = sum_with_partner32(dsum);    // D~ = sE * D
+    const float dt = sum_with_partner32(dsum);    // D~ = sE * (D - D^)
     if (part == 0 && g == 0 && qi < T * 64) {
         float* st = stats + ((size_t)bh * T + (qi >> 6)) * 128;
         st[qi & 63] = lse2;
-        st[64 + (qi & 63)] = (qi < N) ? dt : 0.f;
+        st[64 + (qi & 63)] = (qi < N) ? dhs + dt : 0.f;   // sE * D
     }
     if (qi < N) {
         const float f = scale / (sK * sE);
@@ -965,8 +1003,8 @@ static hipError_t launch_prepare_t(const BwdArgs& a) {
     uint32_t* partial = ws_ptr<uint32_t>(a, w.partial);
     hipLaunchKernelGGL((bwd_absmax_kernel<D>), dim3((BH + BHkv) * chunks), dim3(256), 0,
                        a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                       (const uint16_t*)a.v, (const uint16_t*)a.dout, partial, BH, a.N, a.Nk,
-                       chunks);
+                       (const uint16_t*)a.v, (const uint16_t*)a.dout, (const uint16_t*)a.o,
+                       partial, ws_ptr<float>(a, w.dhat), BH, a.N, a.Nk, chunks);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_scale_kernel, dim3((BH + 63) / 64), dim3(64), 0, a.stream,
@@ -992,7 +1030,8 @@ static hipError_t launch_dq_t(const BwdArgs& a) {
                        dim3(NW * 64), 0,
                        a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                        (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse,
-                       ws_ptr<const float>(a, w.scales), ws_ptr<const char>(a, w.kt),
+                       ws_ptr<const float>(a, w.scales), ws_ptr<const float>(a, w.dhat),
+                       ws_ptr<const char>(a, w.kt),
                        ws_ptr<float>(a, w.stats), (uint16_t*)a.dq, BH, a.H / a.Hkv, a.N, a.Nk,
                        q_tiles64(a), k_tiles64(a), a.scale * kLog2e, a.scale, nqb);
     return hipGetLastError();

@@ -1,9 +1,9 @@
 // Split-K/V decoding for gfx950: a few query rows per head (the last Nq
 // positions of a sequence) against a long K/V sequence of Nk keys.
 //
-// The work is split over the keys, as the inference systems the
-// "FlashAttention-2" page lists among its successors do (section
-// "Performance": FlashDecoding++, FlashInfer), and the partial results are
+// The work is split over the keys, as the inference engines among the
+// "FlashAttention-2" page's References (FlashDecoding++, FlashInfer) do, and
+// the partial results are
 // merged with the two statistics of the online softmax (the "FlashAttention"
 // page, systems-analysis.ru, section "Online softmax"): a key range r gives
 // the row maximum m_r, the exp-sum l_r and the unnormalised O_r, and
@@ -36,15 +36,28 @@ constexpr int kDecTile = 32;   // keys per tile
 
 static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Compute units of the current device (256 on an MI355X; also the value used
+// when no device answers, e.g. for a size query on a host without a GPU).
+static long long device_compute_units() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0) {
+        (void)hipGetLastError();   // leave no error of this query behind
+        return 256;
+    }
+    return n;
+}
+
 DecodeWorkspace decode_workspace_layout(long long B, long long Hkv, long long Nk, long long d) {
     DecodeWorkspace w;
     const long long bhkv = B * Hkv;
     const long long tiles = (Nk + kDecTile - 1) / kDecTile;
     // One round of waves: as many ranges as the compute units hold at once
-    // (256 units x 16, 8 or 4 waves at d = 64, 128, 256: the register and LDS
+    // (16, 8 or 4 waves per unit at d = 64, 128, 256: the register and LDS
     // budgets of the split kernel), at least one tile per range. A second
     // round only adds a tail.
-    const long long waves = 256LL * (d <= 64 ? 16 : (d <= 128 ? 8 : 4));
+    const long long waves = device_compute_units() * (d <= 64 ? 16 : (d <= 128 ? 8 : 4));
     long long ns = (waves + bhkv - 1) / bhkv;
     ns = ns < 1 ? 1 : (ns > tiles ? tiles : ns);
     const long long per = (tiles + ns - 1) / ns;          // tiles per range
@@ -109,6 +122,7 @@ decode_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
     float m_run = kNegInf, l_run = 0.f;    // m in scaled log2 units (score * c)
 
     const int k_begin = sp * L, k_end = min(k_begin + L, Nk);
+    const int k_lim = CAUSAL ? min(k_end, last_key + 1) : k_end;   // keys below this are kept
     // Tile at key j0: V rows into an LDS buffer (rows at or past the range end
     // read the range's last row; they are masked), then K fragments of rows j0 + l32 (clamped into the
     // array; rows at or past the range end are masked) into registers.
@@ -130,7 +144,7 @@ decode_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
         for (int e = 0; e < 16; ++e) {
             const int j = j0 + 8 * (e >> 2) + 4 * g + (e & 3);
             float x = sa[e] * c;
-            if (j >= k_end || (CAUSAL && j > last_key)) x = kNegInf;
+            if (j >= k_lim) x = kNegInf;
             sa[e] = x;
             mt = fmaxf(mt, x);
         }
@@ -139,10 +153,14 @@ decode_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
         const float mc = (m_new == kNegInf) ? 0.f : m_new;
         const float alpha = fast_exp2(m_run - mc);      // 0 while nothing was kept
         l_run *= alpha;
+        // O changes only where the maximum moved: skip the rescale when no
+        // row of the wave needs it.
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
+            for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc_o[nb][e] *= alpha;
+                for (int e = 0; e < 16; ++e) acc_o[nb][e] *= alpha;
+        }
         m_run = m_new;
 
         u32x4_t pp[2];

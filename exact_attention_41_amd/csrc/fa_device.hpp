@@ -99,6 +99,16 @@ __device__ __forceinline__ void mfma_bf16_first(f32x16_t& acc, const u32x4_t& a,
     else
         asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "a"(b));
 }
+// The first product of a chain that starts from the accumulator value c
+// instead of 0 (SrcC = c, a separate VGPR block).
+template <bool WS = false>
+__device__ __forceinline__ void mfma_bf16_first_c(f32x16_t& acc, const u32x4_t& a, const u32x4_t& b,
+                                                  const f32x16_t& c) {
+    if constexpr (WS)
+        asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(acc) : "v"(a), "a"(b), "v"(c));
+    else
+        asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(acc) : "v"(a), "a"(b), "v"(c));
+}
 template <bool WS = false>
 __device__ __forceinline__ void mfma_bf16_next(f32x16_t& acc, const u32x4_t& a, const u32x4_t& b) {
     if constexpr (WS)

@@ -7,8 +7,8 @@
 // kernel"), the output normalised once at the end and each wave owning whole
 // query rows ("FlashAttention-2" page, systems-analysis.info, sections
 // "1. Reducing non-matrix operations" and "3. Improved work partitioning
-// within the block"). The head-size extension to 256 is the one that page
-// names among the changes of FlashAttention-2 (section "Performance").
+// within the block"). Head size 256 is the extension that the "FlashAttention"
+// page (section "FlashAttention-2 (2023)") names among FlashAttention-2's.
 //
 // The register plan differs. A 32-row block of O^T is 32 x 256 fp32, 128
 // registers per lane, and the resident Q^T fragments take 64 more, which does

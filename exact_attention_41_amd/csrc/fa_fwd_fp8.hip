@@ -3,7 +3,8 @@
 //
 // The "FlashAttention" page (systems-analysis.ru, section "FlashAttention-2
 // (2023)") and the "FlashAttention-2" page (systems-analysis.info, section
-// "Performance") name FP8 arithmetic among the FlashAttention-3 changes. Here
+// "Comparison with later versions / FlashAttention-3") name FP8 arithmetic
+// among the FlashAttention-3 changes. Here
 // q, k and v are stored as e4m3 with one dequantisation factor per tensor
 // (real value = descale * stored value); both products run on the fp8 MFMA
 // (v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales, fp32

@@ -29,6 +29,7 @@ struct BwdArgs {
     const void* q;
     const void* k;
     const void* v;
+    const void* o;      // the forward's output (read by the preprocess only)
     const void* dout;
     const float* lse;
     void* dq;
@@ -54,13 +55,16 @@ constexpr int kScaleRows = 256;
 //   partial u32  [BH + BHkv][chunks][2] per-chunk largest |x| (bf16 magnitude
 //                                    bits): (Q, dO) per query head, then (K, V)
 //                                    per K/V head
+//   dhat    fp32 [BH][Nq]            D^_i = dO_i . O_i from the bf16 O: the
+//                                    centre the dQ pass subtracts from dP before
+//                                    rounding (D itself is formed exactly there)
 //   stats   fp32 [BH][Tq][128]       per query tile: lse*log2(e) of its 64 rows,
 //                                    then sE*D (sE = s_dO*s_V); from the dQ pass
 //   qt      fp16 [BH][Tq][64*d]      images of (s_Q Q)^T, one per 64-row tile
 //   ot      fp16 [BH][Tq][64*d]      images of (s_dO dO)^T
 //   kt      fp16 [BHkv][Tk][64*d]    images of (s_K K)^T
 struct BwdWorkspace {
-    size_t scales, partial, stats, qt, ot, kt, total;
+    size_t scales, partial, dhat, stats, qt, ot, kt, total;
 };
 BwdWorkspace bwd_workspace_layout(long long B, long long H, long long Hkv, long long Nq,
                                   long long Nk, long long d);

@@ -95,9 +95,10 @@ GQA_WORKLOADS: Dict[str, Workload] = {
 }
 
 
-# Head size 256 (the largest the FlashAttention-2 page names), forward only:
-# 16384 tokens per batch as in that page's benchmark, 8 heads of 256 = 2048
-# model width; both masks on the same tensors.
+# Head size 256 (the largest the "FlashAttention" page, section
+# "FlashAttention-2 (2023)", names): 16384 tokens per batch (a batch size
+# chosen here; the pages give no benchmark shape), 8 heads of 256 =
+# 2048 model width; both masks on the same tensors.
 WIDE_WORKLOADS: Dict[str, Workload] = {
     w.name: w
     for w in [
@@ -237,8 +238,9 @@ class Inputs:
 
 def make_inputs(B: int, H: int, N: int, d: int, dtype: str, seed: int,
                 qk_mult: float = 1.0, with_do: bool = False,
-                Hkv: Optional[int] = None) -> Inputs:
-    """Draw q, k, v (and dO) following the recipe in the module docstring."""
+                Hkv: Optional[int] = None, v_mean: float = 0.0) -> Inputs:
+    """Draw q, k, v (and dO) following the recipe in the module docstring;
+    ``v_mean`` (stress inputs only) is added to v in fp32 before rounding."""
     rng = np.random.Generator(np.random.PCG64(seed))
     shape = (B, H, N, d)
     kv_shape = (B, H if Hkv is None else Hkv, N, d)
@@ -249,6 +251,8 @@ def make_inputs(B: int, H: int, N: int, d: int, dtype: str, seed: int,
     if qk_mult != 1.0:
         q = q * np.float32(qk_mult)
         k = k * np.float32(qk_mult)
+    if v_mean != 0.0:
+        v = v + np.float32(v_mean)
     if dtype == "bf16":
         q, k, v = bf16_round(q), bf16_round(k), bf16_round(v)
         if do is not None:

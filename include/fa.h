@@ -24,21 +24,22 @@
  *   Alignment  tensor pointers must be 16-byte aligned, lse 4-byte aligned.
  *   Masking    causal != 0 keeps key j for query i only when j <= i (square,
  *              top-left aligned); causal == 0 keeps every key.
- *   Scale      any finite scale >= 0 (1/sqrt(d) for the standard attention).
+ *   Scale      any finite scale > 0 (1/sqrt(d) for the standard attention).
+ *              Zero is refused: masked scores are -inf before scaling.
  *   Sizes      B, H, N >= 0; if any of them is 0 the call does nothing and
  *              returns FA_OK. N may be any positive value (no multiple of a
  *              tile size is required). d must be 64, 128 or 256 (the
- *              largest head size the "FlashAttention-2" page,
- *              systems-analysis.info, section "Performance", names for
- *              FlashAttention-2); fa_fwd_f32 takes 64 and 128 only and
- *              fa_fwd_fp8 128 only.
+ *              largest head size the "FlashAttention" page, section
+ *              "FlashAttention-2 (2023)", names among FlashAttention-2's
+ *              extensions); fa_fwd_f32 takes 64 and 128 only and fa_fwd_fp8
+ *              128 only.
  *   Async      work is enqueued on `stream` (0 = the null stream) and the call
  *              returns; results are valid once the stream has synchronised.
  *   Errors     every argument is checked before anything is enqueued, so on
  *              an error status nothing has been launched:
  *                FA_ERR_INVALID_ARG  null pointer with non-empty sizes,
- *                                    negative size, non-finite or negative
- *                                    scale;
+ *                                    negative size, non-finite scale or
+ *                                    scale <= 0;
  *                FA_ERR_UNSUPPORTED  d not supported, misaligned pointer, or a
  *                                    size whose index arithmetic would
  *                                    overflow (grid or N beyond 2^26);
@@ -118,10 +119,10 @@ fa_status_t fa_fwd_rect(const void* q, const void* k, const void* v, void* o, fl
                         hipStream_t stream);
 
 /*
- * Forward with 8-bit floating-point operands (the FP8 arithmetic the
+ * Forward with 8-bit floating-point operands (the FP8 arithmetic that the
  * "FlashAttention" page, section "FlashAttention-2 (2023)", and the
- * "FlashAttention-2" page, section "Performance", attribute to
- * FlashAttention-3).
+ * "FlashAttention-2" page, section "Comparison with later versions /
+ * FlashAttention-3", attribute to FlashAttention-3).
  *   q        (in)  e4m3 (OCP FP8: 1 sign, 4 exponent bits with bias 7, 3
  *                  mantissa bits, no infinities) [B][H][Nq][d], one byte each;
  *                  real value = descale_q * stored value.
@@ -153,8 +154,8 @@ fa_status_t fa_fwd_f32(const float* q, const float* k, const float* v, float* o,
  * Bytes of device workspace fa_bwd needs for these sizes (0 if a size is not
  * positive or d is unsupported). The workspace is O(B*H*N*d): per row it
  * holds power-of-two-scaled fp16 copies of that row of q, dout and k (stored
- * transposed per 64-row tile) and, per query row, lse and D_i (fp32), plus a
- * few values per head (see fa_bwd).
+ * transposed per 64-row tile) and, per query row, lse, D_i and dout_i . o_i
+ * (fp32), plus a few values per head (see fa_bwd).
  */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d);
 
@@ -166,10 +167,11 @@ size_t fa_bwd_gqa_workspace_size(int B, int H, int Hkv, int N, int d);
  * Backward, bfloat16 storage: the gradients of the scalar
  * L = sum_{b,h,i,c} O_bhic dO_bhic with respect to q, k and v.
  *   q, k, v   (in)  bf16 [B][H][N][d], the forward inputs.
- *   o         (in)  bf16 [B][H][N][d], the forward output. Checked like the
- *                   other tensors but not read: D_i = sum_j P_ij dP_ij is
- *                   recomputed exactly from P and dP = dO V^T instead of as
- *                   dO_i . O_i from the rounded bf16 O.
+ *   o         (in)  bf16 [B][H][N][d], the forward output. Only the centre
+ *                   D^_i = dO_i . O_i is taken from it: D_i = sum_j P_ij dP_ij
+ *                   itself is formed exactly from P and dP = dO V^T (the
+ *                   rounded bf16 O would move it too far), and dP - D^ is
+ *                   what gets rounded for the dQ products.
  *   dout      (in)  bf16 [B][H][N][d], dL/dO.
  *   lse       (in)  fp32 [B][H][N], the forward's logsumexp.
  *   dq,dk,dv  (out) bf16 [B][H][N][d].
@@ -177,8 +179,9 @@ size_t fa_bwd_gqa_workspace_size(int B, int H, int Hkv, int N, int d);
  *             fa_bwd_workspace_size(B, H, N, d) bytes, 256-byte aligned; its
  *             contents on entry do not matter and are overwritten.
  * P = exp(scale Q K^T - lse) is recomputed, never stored. The products that
- * form dQ, dK and dV take P and dS = P * (dP - D) as fp16 operands and q, k,
- * v, dout multiplied by per-head powers of two (exact), fp32 accumulation.
+ * form dQ, dK and dV take fp16 operands: P, dS = P * (dP - D) for dK, and
+ * P * (dP - D^) for dQ (with the exact correction -(D - D^) sum_j P_ij k_j),
+ * against q, k, dout multiplied by per-head powers of two; fp32 accumulation.
  * The result is deterministic: no floating-point atomics are used, so
  * repeated calls give identical bits. causal and scale must match the
  * forward call. The inputs must be finite.
@@ -233,8 +236,9 @@ fa_status_t fa_bwd_rect(const void* q, const void* k, const void* v, const void*
  * its Nk keys (Nq <= Nk), the step an inference system repeats per token,
  * with the keys split into ranges whose partial results are merged with the
  * online-softmax statistics (the "FlashAttention" page, section "Online
- * softmax"; split-K/V decoding is what the inference systems that the
- * "FlashAttention-2" page lists under "Performance" do).
+ * softmax"; split-K/V decoding is what inference engines such as
+ * FlashDecoding++ and FlashInfer, in the "FlashAttention-2" page's
+ * References, do).
  *   q        (in)  bf16 [B][H][Nq][d]; row i is position Nk - Nq + i.
  *   k, v     (in)  bf16 [B][Hkv][Nk][d]; K/V heads shared as in fa_fwd_gqa.
  *   o        (out) bf16 [B][H][Nq][d]; lse (out) fp32 [B][H][Nq], as fa_fwd.
@@ -261,15 +265,16 @@ fa_status_t fa_decode(const void* q, const void* k, const void* v, void* o, floa
  * previous ones left in the workspace, so they must run in this order.
  * Arguments mean what they mean for fa_bwd.
  *   fa_bwd_preprocess  per-head largest magnitudes of q, k, v, dout, the
- *                      power-of-two factors derived from them, and the scaled
- *                      fp16 transposed copies of q, dout and k -> workspace.
+ *                      power-of-two factors derived from them, dout_i . o_i
+ *                      per query row, and the scaled fp16 transposed copies of
+ *                      q, dout and k -> workspace.
  *   fa_bwd_dq          writes dq; leaves lse and D per query row in the
  *                      workspace.
  *   fa_bwd_dkdv        writes dk and dv from q, k, v, dout and the workspace
  *                      (lse is taken from the workspace).
  */
-fa_status_t fa_bwd_preprocess(const void* q, const void* k, const void* v, const void* dout,
-                              void* workspace, size_t workspace_bytes,
+fa_status_t fa_bwd_preprocess(const void* q, const void* k, const void* v, const void* o,
+                              const void* dout, void* workspace, size_t workspace_bytes,
                               int B, int H, int N, int d, hipStream_t stream);
 
 fa_status_t fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout,

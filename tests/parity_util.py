@@ -1,17 +1,36 @@
-"""Helpers shared by the GPU parity tests (tolerances, sampling, device copies).
+"""Helpers shared by the GPU parity tests (tolerances, sampling, device copies,
+and the parity report).
 
 Tolerances (max-abs, against the fp64 oracle):
-  * bf16 O, dQ, dK, dV: an element passes when |gpu - oracle| <= max(1e-2,
-    ulp_bf16(|oracle|)). For |x| >= 4 one bf16 ulp is 2^-5 > 1e-2, so even the
-    correctly rounded oracle can miss a plain 1e-2 there; the plain max-abs
-    error, the rounding floor max|bf16(oracle) - oracle| and the number of
-    elements that pass only through the ulp clause are always reported.
+  * bf16 O, dQ, dK, dV: an element whose exact value has |x| < 4 passes when
+    |gpu - oracle| <= 1e-2 (plain). From |x| = 4 on, half a bf16 ulp is
+    2^-6 = 0.0156 > 1e-2, so even the correctly rounded exact value can miss
+    a plain 1e-2 there; such an element passes when the GPU value is the bf16
+    rounding of some value within 1e-2 of the exact one, i.e. when
+    |gpu - oracle| <= 1e-2 + ulp_bf16/2 (the half ulp taken at the larger of
+    |gpu| and |oracle|, so that a result rounded up to the next binade is
+    measured by its own spacing).
+  * bf16, "rounded" rule (stress inputs outside the five specified
+    workloads: sharpened scores with values of large mean): the GPU value must
+    be the bf16 rounding of some value within 1e-2 of the exact one at every
+    magnitude, |gpu - oracle| <= 1e-2 + ulp_bf16/2. Below |x| = 4 this is
+    looser than the plain rule: where half an ulp is 2^-7 (|x| in [2, 4)), a
+    computed value 2.2e-3 off can round to the far neighbour and land 1e-2
+    away from an exact value that sits near a bf16 number.
   * fp32 O: 1e-5 plain max-abs.
   * logsumexp: 1e-3 plain max-abs.
+
+Every check records, per output: the plain max-abs error (the number the
+1e-2 target speaks of), the rounding floor max|bf16(oracle) - oracle|, how
+many elements exceed the plain 1e-2 (they can only pass through the |x| >= 4
+clause) and the largest ratio error / allowed. tests/conftest.py writes the
+records of a session to a parity report (Markdown and JSON).
 """
 from __future__ import annotations
 
+import os
 import sys
+from contextlib import contextmanager
 
 import numpy as np
 
@@ -20,6 +39,11 @@ from exact_attention_41_amd import workloads as wl
 BF16_ATOL = 1e-2
 F32_ATOL = 1e-5
 LSE_ATOL = 1e-3
+# From this magnitude on, half a bf16 ulp exceeds the 1e-2 target.
+BF16_HALF_ULP_FROM = 4.0
+
+# Records of the checks made in this process (see tests/conftest.py).
+RECORDS: list = []
 
 
 def say(msg: str) -> None:
@@ -28,28 +52,57 @@ def say(msg: str) -> None:
 
 
 def bf16_ulp(x: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 numbers at |x| (normal range)."""
     ax = np.abs(x)
     e = np.floor(np.log2(np.maximum(ax, 2.0 ** -126)))
     return 2.0 ** (e - 7)
 
 
-def check_bf16(name: str, gpu: np.ndarray, ref: np.ndarray, atol: float = BF16_ATOL) -> dict:
+def bf16_allowed(gpu: np.ndarray, ref: np.ndarray, atol: float = BF16_ATOL,
+                 rule: str = "plain") -> np.ndarray:
+    """Per-element allowance of the bf16 rules in the module docstring
+    ("plain" or "rounded")."""
+    half = 0.5 * bf16_ulp(np.maximum(np.abs(gpu), np.abs(ref)))
+    if rule == "rounded":
+        return atol + half
+    assert rule == "plain", rule
+    big = np.abs(ref) >= BF16_HALF_ULP_FROM
+    return np.where(big, atol + half, atol)
+
+
+def _test_id() -> str:
+    cur = os.environ.get("PYTEST_CURRENT_TEST", "")
+    return cur.rsplit(" ", 1)[0] if cur else "(no test)"
+
+
+def _record(**kw) -> None:
+    RECORDS.append({"test": _test_id(), **kw})
+
+
+def check_bf16(name: str, gpu: np.ndarray, ref: np.ndarray, atol: float = BF16_ATOL,
+               rule: str = "plain") -> dict:
     gpu = np.asarray(gpu, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert gpu.shape == ref.shape, (name, gpu.shape, ref.shape)
     assert np.all(np.isfinite(gpu)), f"{name}: non-finite values"
     err = np.abs(gpu - ref)
-    bound = np.maximum(atol, bf16_ulp(ref))
+    bound = bf16_allowed(gpu, ref, atol, rule)
     floor = np.abs(wl.bf16_round(ref.astype(np.float32)).astype(np.float64) - ref)
     stats = {
         "max_abs": float(err.max()) if err.size else 0.0,
         "floor": float(floor.max()) if floor.size else 0.0,
-        "ulp_clause_only": int(np.sum((err > atol) & (err <= bound))),
+        "beyond_plain": int(np.sum(err > atol)),
+        "max_ratio": float((err / bound).max()) if err.size else 0.0,
+        "max_ref": float(np.abs(ref).max()) if ref.size else 0.0,
         "n": int(err.size),
     }
     say(f"  {name}: max_abs={stats['max_abs']:.3e} bf16_floor={stats['floor']:.3e} "
-        f"ulp_only={stats['ulp_clause_only']} n={stats['n']}")
+        f"beyond_1e-2={stats['beyond_plain']} max_err/allowed={stats['max_ratio']:.3f} "
+        f"n={stats['n']}")
     bad = err > bound
+    tol = (f"{atol:g} (|x|<4); {atol:g}+ulp/2 (|x|>=4)" if rule == "plain"
+           else f"{atol:g}+ulp/2")
+    _record(output=name, kind="bf16", tol=tol, passed=not bool(np.any(bad)), **stats)
     if np.any(bad):
         idx = np.argwhere(bad)[:5]
         raise AssertionError(f"{name}: {int(bad.sum())} elements out of tolerance; first "
@@ -65,9 +118,20 @@ def check_abs(name: str, gpu: np.ndarray, ref: np.ndarray, atol: float) -> float
     err = np.where(both_inf, 0.0, np.abs(gpu - ref))
     m = float(np.nanmax(err)) if err.size else 0.0
     say(f"  {name}: max_abs={m:.3e} (tol {atol:g}) n={err.size}")
+    ok = bool(np.all(np.isfinite(err))) and m <= atol
+    _record(output=name, kind="abs", tol=f"{atol:g}", passed=ok, max_abs=m,
+            max_ratio=m / atol, n=int(err.size))
     assert np.all(np.isfinite(err)), f"{name}: non-finite mismatch"
     assert m <= atol, f"{name}: max abs error {m} > {atol}"
     return m
+
+
+def record_model_check(name: str, err: np.ndarray, tol: np.ndarray, passed: bool) -> None:
+    """Record a check against a per-element tolerance array (the fp8 model)."""
+    err = np.asarray(err, dtype=np.float64)
+    _record(output=name, kind="model", tol="fp8 error model", passed=passed,
+            max_abs=float(np.nanmax(err)) if err.size else 0.0,
+            max_ratio=float(np.nanmax(err / tol)) if err.size else 0.0, n=int(err.size))
 
 
 def sample_rows(N: int, count: int, seed: int) -> np.ndarray:
@@ -78,6 +142,24 @@ def sample_rows(N: int, count: int, seed: int) -> np.ndarray:
     rnd = r.integers(0, N, size=max(0, count - len(fixed)))
     rows = np.unique(np.clip(np.array(fixed + rnd.tolist()), 0, N - 1))
     return rows
+
+
+def oracle_workers() -> int:
+    """Threads for the oracle at full size: the host's cores, at most 16 (one
+    GPU's share of a shared host)."""
+    return max(1, min(len(os.sched_getaffinity(0)), 16))
+
+
+@contextmanager
+def single_threaded_blas():
+    """BLAS single-threaded inside the oracle's own thread pool."""
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        yield
+        return
+    with threadpool_limits(1):
+        yield
 
 
 def to_np(t) -> np.ndarray:

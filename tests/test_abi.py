@@ -95,6 +95,9 @@ def test_forward_rejects_bad_arguments(lib, entry):
     assert fwd(lib, entry, scale=float("nan")) == INVALID
     assert fwd(lib, entry, scale=float("inf")) == INVALID
     assert fwd(lib, entry, scale=-0.5) == INVALID
+    # 0 too: a masked score is -inf before scaling, and -inf * 0 is NaN
+    assert fwd(lib, entry, scale=0.0) == INVALID
+    assert fwd(lib, entry, scale=-0.0) == INVALID
     assert fwd(lib, entry, d=96) == UNSUPPORTED
     assert fwd(lib, entry, d=512) == UNSUPPORTED
     if entry == "fa_fwd_f32":
@@ -182,6 +185,7 @@ def test_decode_arguments(lib):
     assert dec(Hkv=3) == INVALID
     assert dec(Nq=1001) == INVALID
     assert dec(scale=float("nan")) == INVALID
+    assert dec(scale=0.0) == INVALID
     assert dec(o=None) == INVALID
     assert dec(d=96) == UNSUPPORTED
     assert dec(H=64, Hkv=1, Nq=1) == UNSUPPORTED
@@ -199,6 +203,7 @@ def test_rect_forward_arguments(lib):
     assert f(Nk=0) == INVALID
     assert f(Hkv=3) == INVALID
     assert f(q=None) == INVALID
+    assert f(scale=0.0) == INVALID
     assert f(d=256 + 32) == UNSUPPORTED
     assert f(Nk=(1 << 26) + 1) == UNSUPPORTED
     assert f(Nq=0, Nk=0, q=None) == OK          # nothing to compute
@@ -248,13 +253,32 @@ def test_python_binding_refuses_without_gpu_tensors():
         fa.fa_fwd(x.float(), x.float(), x.float())
 
 
+def test_binding_checks_caller_workspaces():
+    """A caller's workspace must be a contiguous tensor on the inputs' device:
+    its byte count is what the library is told it may write."""
+    torch = pytest.importorskip("torch")
+    import exact_attention_41_amd as fa
+    cpu = torch.device("cpu")
+    ws = torch.zeros(64, dtype=torch.uint8)
+    assert fa._check_workspace(ws, cpu) == 64
+    assert fa._check_workspace(torch.zeros(8, dtype=torch.float32), cpu) == 32
+    with pytest.raises(ValueError):
+        fa._check_workspace(ws[::2], cpu)                    # not contiguous
+    with pytest.raises(ValueError):
+        fa._check_workspace(ws, torch.device("cuda", 0))     # another device
+    with pytest.raises(TypeError):
+        fa._check_workspace(bytearray(64), cpu)
+
+
 def test_backward_phases_reject_bad_arguments(lib):
     ws = lib.fa_bwd_workspace_size(1, 2, 100, 128)
     W = 0x200000     # 256-byte aligned fake workspace
-    assert lib.fa_bwd_preprocess(None, A, A, A, W, ws, 1, 2, 100, 128, None) == INVALID
-    assert lib.fa_bwd_preprocess(A, A, A, A, W, ws - 4, 1, 2, 100, 128, None) == WORKSPACE
-    assert lib.fa_bwd_preprocess(A, A, A, A, W + 16, ws, 1, 2, 100, 128, None) == WORKSPACE
-    assert lib.fa_bwd_preprocess(A, MIS, A, A, W, ws, 1, 2, 100, 128, None) == UNSUPPORTED
+    assert lib.fa_bwd_preprocess(None, A, A, A, A, W, ws, 1, 2, 100, 128, None) == INVALID
+    assert lib.fa_bwd_preprocess(A, A, A, None, A, W, ws, 1, 2, 100, 128, None) == INVALID
+    assert lib.fa_bwd_preprocess(A, A, A, A, A, W, ws - 4, 1, 2, 100, 128, None) == WORKSPACE
+    assert lib.fa_bwd_preprocess(A, A, A, A, A, W + 16, ws, 1, 2, 100, 128, None) == WORKSPACE
+    assert lib.fa_bwd_preprocess(A, MIS, A, A, A, W, ws, 1, 2, 100, 128, None) == UNSUPPORTED
+    assert lib.fa_bwd_preprocess(A, A, A, MIS, A, W, ws, 1, 2, 100, 128, None) == UNSUPPORTED
     assert lib.fa_bwd_dq(A, A, A, A, None, W, ws, A, 1, 2, 100, 128, 1, 0.1, None) == INVALID
     assert lib.fa_bwd_dq(A, A, A, A, A, W, ws, MIS, 1, 2, 100, 128, 1, 0.1, None) == UNSUPPORTED
     assert lib.fa_bwd_dq(A, A, A, A, A, W, ws, A, 1, 2, 100, 96, 1, 0.1, None) == UNSUPPORTED
@@ -263,6 +287,7 @@ def test_backward_phases_reject_bad_arguments(lib):
     assert lib.fa_bwd_dkdv(A, A, None, A, W, ws, A, A, 1, 2, 100, 128, 1, 0.1, None) == INVALID
     assert lib.fa_bwd_dkdv(A, A, A, A, None, ws, A, A, 1, 2, 100, 128, 1, 0.1, None) == WORKSPACE
     assert lib.fa_bwd_dkdv(A, A, A, A, W, ws, A, A, 1, 2, 100, 128, 1, -1.0, None) == INVALID
+    assert lib.fa_bwd_dq(A, A, A, A, A, W, ws, A, 1, 2, 100, 128, 1, 0.0, None) == INVALID
 
 
 def test_fp8_forward_arguments(lib):

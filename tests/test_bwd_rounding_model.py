@@ -1,0 +1,90 @@
+"""A numpy model of the dQ pass's rounding, against the fp64 oracle (CPU).
+
+The dQ pass forms, per query row i (sE, sK: the per-head powers of two that
+put the fp16 operands in range; K~ = sK k exactly; dP~ = sE dP in fp32):
+    E_ij  = P_ij (dP~_ij - c_i)              rounded to fp16 as a product operand
+    A~_i  = sum_j fp16(E_ij) K~_j,   B~_i = sum_j fp16(P_ij) K~_j      (fp32)
+    t_i   = sum_j E_ij                        (fp32, unrounded E)
+    dQ_i  = scale / (sK sE) (A~_i - t_i B~_i)  rounded to bf16
+which is the exact gradient for any centre c_i, since
+sum_j P_ij (dP_ij - D_i) k_j = sum_j E_ij k_j - (D_i - c_i) sum_j P_ij k_j with
+D_i - c_i = sum_j E_ij. Only the rounding of E depends on c: with c = 0 its
+error scales with |dP|, with c_i = sE dO_i . O_i (O the bf16 forward output)
+with |dP - D|. Sharpened scores (q, k x3) and values with a large mean make
+|dP| much larger than |dP - D|; this model shows that the centred form stays
+within the bf16 tolerance there ("rounded" rule: these are stress inputs,
+not one of the specified workloads) and the uncentred one does not.
+"""
+import numpy as np
+import pytest
+
+from exact_attention_41_amd import workloads as wl
+from oracle import attention as ora
+from parity_util import bf16_allowed
+
+
+def _f16(x):
+    return np.asarray(x, np.float64).astype(np.float16).astype(np.float64)
+
+
+def _f32(x):
+    return np.asarray(x, np.float64).astype(np.float32).astype(np.float64)
+
+
+def _pow2_factor(x):
+    m = float(np.max(np.abs(x)))
+    return 1.0 if m == 0 else 2.0 ** -(np.floor(np.log2(m)) + 1)
+
+
+def _bf16(x):
+    return wl.bf16_round(np.asarray(x, np.float32)).astype(np.float64)
+
+
+def model_dq(q, k, v, do, causal, scale, centred):
+    """dQ of one head as the pass forms it (module docstring)."""
+    N = q.shape[0]
+    P = ora.head_probs(q, k, causal, scale)
+    P = _f32(P)
+    o = _bf16(P @ v)                                   # the forward's bf16 output
+    sE = _pow2_factor(do) * _pow2_factor(v)
+    sK = _pow2_factor(k)
+    dPt = _f32(sE * (do @ v.T))
+    c = _f32(sE * np.sum(do * o, axis=1)) if centred else np.zeros(N)
+    E = _f32(P * (dPt - c[:, None]))
+    A = E.astype(np.float16).astype(np.float64) @ (sK * k)
+    Bt = _f16(P) @ (sK * k)
+    t = np.sum(E, axis=1)
+    return _bf16(scale / (sK * sE) * (A - t[:, None] * Bt))
+
+
+@pytest.mark.parametrize("vmean", [0.0, 8.0, 32.0])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_centred_dq_model_within_tolerance(causal, vmean):
+    N, d = 512, 128
+    r = np.random.Generator(np.random.PCG64(31 + int(vmean)))
+    q = _bf16(3.0 * r.standard_normal((N, d), dtype=np.float32))
+    k = _bf16(3.0 * r.standard_normal((N, d), dtype=np.float32))
+    v = _bf16(r.standard_normal((N, d), dtype=np.float32) + vmean)
+    do = _bf16(r.standard_normal((N, d), dtype=np.float32))
+    scale = float(np.float32(1 / np.sqrt(d)))
+    ref, _, _ = ora.head_bwd(q, k, v, do, causal, scale)
+    got = model_dq(q, k, v, do, causal, scale, centred=True)
+    ratio = np.max(np.abs(got - ref) / bf16_allowed(got, ref, rule="rounded"))
+    assert ratio <= 0.85, ratio
+
+
+@pytest.mark.parametrize("vmean", [8.0, 32.0])
+def test_uncentred_dq_model_fails_with_large_value_mean(vmean):
+    """The form without the centre (E = P dP~) leaves the tolerance on the same
+    inputs: the rounding of E is what the centre is there for."""
+    N, d = 512, 128
+    r = np.random.Generator(np.random.PCG64(31 + int(vmean)))
+    q = _bf16(3.0 * r.standard_normal((N, d), dtype=np.float32))
+    k = _bf16(3.0 * r.standard_normal((N, d), dtype=np.float32))
+    v = _bf16(r.standard_normal((N, d), dtype=np.float32) + vmean)
+    do = _bf16(r.standard_normal((N, d), dtype=np.float32))
+    scale = float(np.float32(1 / np.sqrt(d)))
+    ref, _, _ = ora.head_bwd(q, k, v, do, True, scale)
+    got = model_dq(q, k, v, do, True, scale, centred=False)
+    ratio = np.max(np.abs(got - ref) / bf16_allowed(got, ref, rule="rounded"))
+    assert ratio > 2.0, ratio

@@ -34,6 +34,9 @@ def test_forward_backward_past_2_31_elements(fa):
     scale = float(np.float32(1 / np.sqrt(d)))
     say(f"fa_fwd/fa_bwd B={B} H={H} N={N} d={d} causal={causal} seeds 51-54 "
         f"({B * H * N * d} elements per tensor)")
+    # the device generator: the same seed gives the same bits on the GPU too
+    a, b = (wl.device_normal_bf16((3, 1000), 51) for _ in range(2))
+    assert a.is_cuda and torch.equal(a.view(torch.int16), b.view(torch.int16))
     q, k, v, do = (wl.device_normal_bf16((B, H, N, d), seed) for seed in (51, 52, 53, 54))
     o, lse = fa.fa_fwd(q, k, v, causal=causal, scale=scale)
     dq, dk, dv = fa.fa_bwd(q, k, v, o, do, lse, causal=causal, scale=scale)

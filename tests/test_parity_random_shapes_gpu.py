@@ -69,7 +69,7 @@ def test_backward_phases_equal_fa_bwd_at_d256(fa):
     dq1, dk1, dv1 = fa.fa_bwd(q, k, v, o, do, lse, causal=True)
     ws = torch.empty(fa.fa_bwd_workspace_size(B, H, N, d), dtype=torch.uint8, device=q.device)
     dq2, dk2, dv2 = (torch.empty_like(q) for _ in range(3))
-    fa.fa_bwd_preprocess(q, k, v, do, ws)
+    fa.fa_bwd_preprocess(q, k, v, o, do, ws)
     fa.fa_bwd_dq(q, k, v, do, lse, ws, dq2, causal=True)
     fa.fa_bwd_dkdv(q, k, v, do, ws, dk2, dv2, causal=True)
     torch.cuda.synchronize()

@@ -43,10 +43,10 @@ def test_workload_registry():
     assert wl.WORKLOADS["bf16_b8h16n2048d64"].scale == 0.125
 
 
-def test_device_normal_bf16_is_seeded():
-    """The device-side generator (used for inputs too large for the host): the
-    same seed gives the same bits, another seed other values; bf16 draws of a
-    standard normal (exercised here on the CPU device)."""
+def test_normal_bf16_generator_is_seeded_on_the_cpu():
+    """device_normal_bf16 with device="cpu" (torch's CPU generator; the GPU
+    generator's determinism is checked by a GPU test): the same seed gives the
+    same bits, another seed other values; bf16 draws of a standard normal."""
     import torch
     a = wl.device_normal_bf16((4, 1000), 51, device="cpu")
     b = wl.device_normal_bf16((4, 1000), 51, device="cpu")
