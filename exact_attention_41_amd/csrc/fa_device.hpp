@@ -345,6 +345,12 @@ __device__ __forceinline__ u32x4_t lds_vt_frag(const lds_char* tile, int n0, int
     return u32x4_t{ua[0], ua[1], ub[0], ub[1]};
 }
 
+// Sum of a packed fp16 pair added to acc (v_dot2_f32_f16 with (1, 1)).
+__device__ __forceinline__ float add_f16x2(uint32_t w, float acc) {
+    const f16x2_t one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, w), one, acc, false);
+}
+
 // Sum of a packed bf16 pair added to acc (v_dot2_f32_bf16 with (1, 1)).
 __device__ __forceinline__ float add_bf16x2(uint32_t w, float acc) {
     const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};

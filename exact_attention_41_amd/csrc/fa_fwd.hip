@@ -27,8 +27,16 @@ namespace fa {
 //   S^T (keys x queries) = K * Q^T      A = K tile (LDS), B = Q^T (VGPRs)
 //   P^T = exp2(S^T*c - m*c)             row max/sum: registers + one
 //                                        v_permlane32_swap per row and tile
-//   O^T (d x queries)   += V^T * P^T    A = V^T (LDS, transposed reads),
-//                                        B = P^T from the S^T accumulators (bf16)
+//   O^T (d x queries)   += V^T * P^T    A = V^T (LDS, transposed, fp16),
+//                                        B = P^T from the S^T accumulators (fp16)
+//
+// The P V product takes fp16 operands (11-bit significand, against bf16's
+// 8): with a sharp softmax the rounding of P in bf16 alone moves O by a few
+// 1e-3. V enters as fp16(2^-8 V) (exact for 2^-6 <= |v| < 65504 * 2^8; below,
+// an absolute error of at most 2^-17; at or above 65504 * 2^8 it overflows)
+// and P as fp16(2^7 P) (P <= 2^8 by the rescale rule below, so 2^7 P stays
+// in range and its small values keep their precision); the epilogue takes
+// both factors out again.
 //
 // Schedule ("ping-pong"): waves 0-3 (group A) and 4-7 (group B) share the
 // four SIMDs, one of each per SIMD. Time is cut into slots separated by
@@ -46,6 +54,12 @@ namespace fa {
 // ---------------------------------------------------------------------------
 
 constexpr int kFwdWaves = 8;
+// Powers of two on the fp16 operands of the P V product: P is formed as
+// 2^kPShift P, V enters as 2^-kVShift V.
+constexpr float kPShift = 7.f;
+constexpr float kVScale = 1.f / 256.f;      // 2^-8
+// O = 2^8 acc / sum(fp16 P): the P factor cancels in the ratio, V's does not.
+constexpr float kOScale = 256.f;
 #ifndef FA_FWD_AHEAD
 #define FA_FWD_AHEAD 4
 #endif
@@ -123,7 +137,8 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     auto Vb = [&](int i) { return i ? (lds_char*)vb1 : (lds_char*)vb0; };
 
     // m_ref: reference maximum (raw score units) of this lane's row; the
-    // probabilities of a tile are exp2((s - m_ref) c) <= 2^kRescaleLog2.
+    // probabilities of a tile are exp2((s - m_ref) c) <= 2^kRescaleLog2, and
+    // they are formed as 2^kPShift times that (the fp16 operand's factor).
     const float thresh = kRescaleLog2 / c;
     float m_ref = kNegInf, l_run = 0.f, l_rnd = 0.f;
     f32x16_t acc_o[NB], acc_s[2];
@@ -160,10 +175,16 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     auto v_store = [&](int t) {
         lds_char* vl = Vb(t & 1);
         const int slot = tr_key_position(4 * v_rg) >> 2;
+        // bf16 pairs -> fp16 pairs of 2^-8 v (same packing)
+        vrow_t hreg[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+            for (int w = 0; w < CW / 2; ++w) hreg[rr][w] = bf16x2_to_f16x2(vreg[rr][w], kVScale);
 #pragma unroll
         for (int e = 0; e < CW; ++e) {
             const int w = e >> 1;
-            const uint32_t r0 = vreg[0][w], r1 = vreg[1][w], r2 = vreg[2][w], r3 = vreg[3][w];
+            const uint32_t r0 = hreg[0][w], r1 = hreg[1][w], r2 = hreg[2][w], r3 = hreg[3][w];
             u32x2_t col;
             if (e & 1) {
                 col[0] = (r0 >> 16) | (r1 & 0xffff0000u);
@@ -200,7 +221,7 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const int t4 = x / NB, nb = x % NB;
                 const u32x4_t vf = *(const __attribute__((address_space(3))) u32x4_t*)(
                     vt + tr_slot_offset(32 * nb + l32, 4 * t4 + 2 * g));
-                acc_o[nb] = mfma_32x32x16(vf, pf[t4], acc_o[nb]);
+                acc_o[nb] = mfma_32x32x16_f16(vf, pf[t4], acc_o[nb]);
             }
         }
         // One LDS read per MFMA: kFwdAhead reads ahead, then alternate.
@@ -247,7 +268,8 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 for (int r = 0; r < 16; ++r) acc_o[nb][r] *= alpha;
             m_ref = m_new;
         }
-        const float mc = (m_ref == kNegInf) ? 0.f : m_ref * c;
+        // exp2(s c - m_ref c + kPShift) = 2^kPShift P
+        const float mc = ((m_ref == kNegInf) ? 0.f : m_ref * c) - kPShift;
 #pragma unroll
         for (int t4 = 0; t4 < 4; ++t4) {
             const int jb = t4 >> 1, rb = 8 * (t4 & 1);
@@ -257,13 +279,13 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 p[e] = fast_exp2(__builtin_fmaf(acc_s[jb][rb + e], c, -mc));
                 l_run += p[e];      // fp32 sum of the unrounded probabilities (lse)
             }
-            pf[t4] = u32x4_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                             pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
-            // Sum of the bf16 probabilities that multiply V: normalising O by
+            pf[t4] = u32x4_t{pack_f16x2(p[0], p[1]), pack_f16x2(p[2], p[3]),
+                             pack_f16x2(p[4], p[5]), pack_f16x2(p[6], p[7])};
+            // Sum of the fp16 probabilities that multiply V: normalising O by
             // it makes the rounding error of P scale with (v_j - O) instead of
             // v_j (zero for a row dominated by one key).
 #pragma unroll
-            for (int w = 0; w < 4; ++w) l_rnd = add_bf16x2(pf[t4][w], l_rnd);
+            for (int w = 0; w < 4; ++w) l_rnd = add_f16x2(pf[t4][w], l_rnd);
         }
     };
 
@@ -317,10 +339,10 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const float l = sum_with_partner32(l_run);
     const float lr = sum_with_partner32(l_rnd);
     if (qi < N) {
-        const float inv = (lr > 0.f) ? 1.f / lr : 0.f;
+        const float inv = (lr > 0.f) ? kOScale / lr : 0.f;
         const float mc = (m_ref == kNegInf) ? 0.f : m_ref * c;
         if (g == 0)
-            LSE[(size_t)bh * N + qi] = (l > 0.f) ? (mc + fast_log2(l)) * kLn2 : kNegInf;
+            LSE[(size_t)bh * N + qi] = (l > 0.f) ? (mc + (fast_log2(l) - kPShift)) * kLn2 : kNegInf;
         uint16_t* orow = O + head + (size_t)qi * D;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)

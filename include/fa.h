@@ -79,9 +79,13 @@ const char* fa_status_str(fa_status_t status);
  *   lse      (out) fp32 [B][H][N]: natural-log logsumexp of the scaled,
  *                  masked logits of each query row, ln sum_j exp(scale q_i.k_j);
  *                  the backward consumes it.
- * Products run on bf16 MFMA with fp32 accumulation; the softmax statistics,
- * probabilities and the output accumulator are fp32; P is rounded to bf16
- * only as the operand of the P V product.
+ * Q K^T runs on bf16 MFMA with fp32 accumulation; the softmax statistics,
+ * probabilities and the output accumulator are fp32. The P V product takes
+ * fp16 operands (more significand bits than bf16, for a sharp softmax):
+ * 2^7 P and 2^-8 v, fp32 accumulation. So for d = 64 and 128 the values must
+ * satisfy |v| < 65504 * 2^8 (about 1.68e7; larger ones overflow the fp16
+ * operand and give non-finite output); at d = 256 P V takes bf16 operands
+ * and any finite v is allowed.
  */
 fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                    int B, int H, int N, int d, int causal, float scale,
