@@ -27,7 +27,7 @@ __all__ = ["fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_bwd_workspace_size", "fa_status
            "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_gqa", "fa_bwd_gqa",
            "fa_bwd_gqa_workspace_size", "fa_decode", "fa_decode_workspace_size", "fa_fwd_rect",
            "fa_fwd_fp8", "fa_bwd_rect", "fa_bwd_rect_workspace_size", "fa_clock_probe",
-           "fa_attention", "FAError", "library_path"]
+           "fa_attention", "fa_decode_noalloc", "FAError", "library_path"]
 
 
 class FAError(RuntimeError):
@@ -319,6 +319,39 @@ def fa_decode(q, k, v, causal: bool = False, scale: Optional[float] = None, out=
                                    _stream_ptr(q.device))
     if st != _lib.FA_OK:
         raise FAError(st, "fa_decode")
+    return out, lse
+
+
+def fa_decode_noalloc(q, k, v, causal: bool = False, scale: Optional[float] = None, out=None,
+                      lse=None):
+    """fa_decode with the library's fixed device buffer in place of a
+    workspace (no device allocation inside the call; ``out`` and ``lse``
+    are allocated here only when not given). Same results as fa_decode;
+    problems whose partial results exceed the buffer raise FAError
+    (FA_ERR_WORKSPACE). Calls that overlap on one GPU race. Calls
+    fa_decode_noalloc of libfa.so."""
+    torch = _torch()
+    bf = torch.bfloat16
+    _check(q, "q", bf)
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, H, Nq, d] and k, v [B, Hkv, Nk, d]")
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    _check(k, "k", bf, (B, Hkv, Nk, d), q.device)
+    _check(v, "v", bf, (B, Hkv, Nk, d), q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    _check(out, "out", bf, q.shape, q.device)
+    _check(lse, "lse", torch.float32, (B, H, Nq), q.device)
+    with torch.cuda.device(q.device):
+        st = _lib.load().fa_decode_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                           out.data_ptr(), lse.data_ptr(), B, H, Hkv, Nq, Nk, d,
+                                           int(bool(causal)), _scale(scale, d),
+                                           _stream_ptr(q.device))
+    if st != _lib.FA_OK:
+        raise FAError(st, "fa_decode_noalloc")
     return out, lse
 
 

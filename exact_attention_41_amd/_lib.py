@@ -15,7 +15,7 @@ EXPORTED = ("fa_status_str", "fa_fwd", "fa_fwd_f32", "fa_bwd_workspace_size", "f
             "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_gqa",
             "fa_bwd_gqa_workspace_size", "fa_bwd_gqa", "fa_decode_workspace_size", "fa_decode",
             "fa_fwd_rect", "fa_fwd_fp8", "fa_bwd_rect_workspace_size", "fa_bwd_rect",
-            "fa_clock_probe")
+            "fa_clock_probe", "fa_decode_noalloc")
 
 _lock = threading.Lock()
 _lib = None
@@ -77,6 +77,8 @@ def load() -> ctypes.CDLL:
         lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                   i, i, i, i, i, i, i, f, vp]
         lib.fa_decode.restype = i
+        lib.fa_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
+        lib.fa_decode_noalloc.restype = i
         lib.fa_clock_probe.argtypes = [vp, i, i, vp]
         lib.fa_clock_probe.restype = i
         _lib = lib

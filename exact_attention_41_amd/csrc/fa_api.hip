@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <initializer_list>
+#include <mutex>
 
 #include "fa.h"
 #include "fa_kernels.hpp"
@@ -274,14 +275,24 @@ size_t fa_decode_workspace_size(int B, int H, int Hkv, int Nq, int Nk, int d) {
     return fa::decode_workspace_layout(B, Hkv, Nk, d).total;
 }
 
-fa_status_t fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
-                      void* workspace, size_t workspace_bytes, int B, int H, int Hkv, int Nq,
-                      int Nk, int d, int causal, float scale, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Every check of fa_decode except the workspace's. Sets *empty when there is
+// nothing to compute.
+fa_status_t check_decode(const void* q, const void* k, const void* v, const void* o,
+                         const float* lse, int B, int H, int Hkv, int Nq, int Nk, int d,
+                         float scale, bool* empty) {
+    *empty = false;
     if (B < 0 || H < 0 || Nq < 0 || Nk < 0) return FA_ERR_INVALID_ARG;
     if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
     FA_TRY(check_heads(H, Hkv));
     if (!head_dim_ok(d, true)) return FA_ERR_UNSUPPORTED;
-    if (B == 0 || H == 0 || Nq == 0) return FA_OK;
+    if (B == 0 || H == 0 || Nq == 0) {
+        *empty = true;
+        return FA_OK;
+    }
     if (Nq > Nk) return FA_ERR_INVALID_ARG;
     if (Nk > kMaxN || (H / Hkv) * Nq > 32) return FA_ERR_UNSUPPORTED;
     if ((long long)B * H > (1LL << 30) || (long long)B * Hkv > 65535) return FA_ERR_UNSUPPORTED;
@@ -291,11 +302,71 @@ fa_status_t fa_decode(const void* q, const void* k, const void* v, void* o, floa
     FA_TRY(check_tensor(v));
     FA_TRY(check_tensor(o));
     FA_TRY(check_lse(lse));
+    return FA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Fixed device scratch of fa_decode_noalloc: the split phase's partial
+// results live here instead of in a caller's workspace. One copy per device
+// (each GPU that runs the entry point holds it until the process ends); in
+// host code `scratch` only names the symbol, so its device address is taken
+// once per device with hipGetSymbolAddress and only that address is passed
+// to kernels.
+// ---------------------------------------------------------------------------
+constexpr size_t kNoAllocScratchBytes = (size_t)40 << 20;   // 40 MiB
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of the current device's scratch (looked up on its first use
+// on that device, with that device current).
+hipError_t current_device_scratch(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::call_once(g_scratch_once[dev], [dev] {
+        void* p = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = p;
+    });
+    if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status_t fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                      void* workspace, size_t workspace_bytes, int B, int H, int Hkv, int Nq,
+                      int Nk, int d, int causal, float scale, hipStream_t stream) {
+    bool empty = false;
+    FA_TRY(check_decode(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, &empty));
+    if (empty) return FA_OK;
     if (!workspace || !aligned(workspace, 256) ||
         workspace_bytes < fa_decode_workspace_size(B, H, Hkv, Nq, Nk, d))
         return FA_ERR_WORKSPACE;
     const fa::DecArgs a{q, k, v, o, lse, workspace, B, H, Hkv, Nq, Nk, d, causal != 0, scale,
                         stream};
+    return fa::launch_decode(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status_t fa_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int B, int H, int Hkv, int Nq, int Nk, int d, int causal,
+                              float scale, hipStream_t stream) {
+    bool empty = false;
+    FA_TRY(check_decode(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, &empty));
+    if (empty) return FA_OK;
+    if (fa_decode_workspace_size(B, H, Hkv, Nq, Nk, d) > kNoAllocScratchBytes)
+        return FA_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (current_device_scratch(&ws) != hipSuccess) return FA_ERR_HIP;
+    const fa::DecArgs a{q, k, v, o, lse, ws, B, H, Hkv, Nq, Nk, d, causal != 0, scale, stream};
     return fa::launch_decode(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

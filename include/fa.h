@@ -263,6 +263,28 @@ fa_status_t fa_decode(const void* q, const void* k, const void* v, void* o, floa
                       hipStream_t stream);
 
 /*
+ * fa_decode without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). It makes no allocation of any kind: the
+ * partial results go to a fixed device buffer of the library, 40 MiB per
+ * GPU, which each GPU that runs this entry point holds until the process
+ * ends. Arguments, layouts, limits and results are those of fa_decode, with
+ * the same kernels and the same key ranges (the output has the same bits).
+ *   Limit    problems with fa_decode_workspace_size(B, H, Hkv, Nq, Nk, d) >
+ *            40 MiB (more K/V heads than the compute units hold in one round
+ *            of waves, roughly B * Hkv > 1024 at d = 128) -> FA_ERR_WORKSPACE,
+ *            before anything is enqueued.
+ *   Sharing  every call on one GPU uses that GPU's single buffer: calls that
+ *            overlap in time on one GPU (other streams, other threads) race
+ *            and give wrong results. Calls on one stream are ordered and safe.
+ *            Nothing in the buffer needs to be zero: each call writes every
+ *            value it later reads.
+ */
+fa_status_t fa_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int B, int H, int Hkv, int Nq, int Nk, int d, int causal,
+                              float scale, hipStream_t stream);
+
+/*
  * The three phases of fa_bwd, for callers that schedule or time them
  * separately. fa_bwd(...) is exactly fa_bwd_preprocess, fa_bwd_dq and
  * fa_bwd_dkdv, in this order, on one stream; each phase reads what the

@@ -196,6 +196,25 @@ def test_decode_arguments(lib):
     assert dec(Nq=0, wsp=None, ws_bytes=0) == OK
 
 
+def test_decode_noalloc_arguments(lib):
+    """fa_decode_noalloc validates like fa_decode (no workspace argument) and
+    refuses problems whose partial results exceed its fixed 40 MiB buffer,
+    all before any HIP call."""
+    def dec(B=2, H=8, Hkv=2, Nq=4, Nk=1000, d=128, o=A, scale=0.1):
+        return lib.fa_decode_noalloc(A, A, A, o, A, B, H, Hkv, Nq, Nk, d, 1, scale, None)
+    assert dec(Hkv=3) == INVALID
+    assert dec(Nq=1001) == INVALID
+    assert dec(scale=0.0) == INVALID
+    assert dec(o=None) == INVALID
+    assert dec(d=96) == UNSUPPORTED
+    assert dec(o=MIS) == UNSUPPORTED
+    assert dec(B=0) == OK
+    assert dec(Nq=0) == OK
+    # 2047 K/V heads at d = 128: about 65 MiB of partial results
+    assert lib.fa_decode_workspace_size(2047, 1, 1, 1, 64, 128) > 40 << 20
+    assert dec(B=2047, H=1, Hkv=1, Nq=1, Nk=64) == WORKSPACE
+
+
 def test_rect_forward_arguments(lib):
     def f(B=1, H=2, Hkv=1, Nq=100, Nk=300, d=128, q=A, scale=0.1):
         return lib.fa_fwd_rect(q, A, A, A, A, B, H, Hkv, Nq, Nk, d, 1, scale, None)
