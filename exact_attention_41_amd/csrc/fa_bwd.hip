@@ -200,11 +200,12 @@ bwd_scale_kernel(const uint32_t* __restrict__ partial, float* __restrict__ scale
 
 // ---------------------------------------------------------------------------
 // A 64-row, 16-bit tile [64][D] (source rows LD values apart) read as 4-row
-// x 8-column micro-tiles and written transposed ([D][64], the permuted row
-// order and slot swizzle of fa_device.hpp), to LDS or to a global image of
-// that layout. With CVT the source is bf16 and the copy is fp16 of the value
-// times a power of two. Rows at or past N repeat row N-1 (finite values that
-// the consumers' masks multiply by zero).
+// x 8-column micro-tiles and written transposed ([D][64], with the slot
+// swizzle of fa_device.hpp; the rows in the permuted order of fa_device.hpp,
+// or with NATURAL in their own order), to LDS or to a global image of that
+// layout. With CVT the source is bf16 and the copy is fp16 of the value times
+// a power of two. Rows at or past N repeat row N-1 (finite values that the
+// consumers' masks multiply by zero).
 // ---------------------------------------------------------------------------
 template <int D, int NT, int LD = D>
 struct Tile64 {
@@ -229,14 +230,14 @@ struct Tile64 {
         }
     }
 
-    template <bool CVT>
+    template <bool CVT, bool NATURAL = false>
     __device__ __forceinline__ void store_transposed(char* dst, int tid, float s = 1.f) const {
 #pragma unroll
         for (int it = 0; it < LOADS; ++it) {
             const int u = tid + it * NT;
             if (UNITS % NT == 0 || u < UNITS) {
                 const int ch = u % DCH, rg = u / DCH;
-                const int slot = tr_key_position(4 * rg) >> 2;
+                const int slot = NATURAL ? rg : (tr_key_position(4 * rg) >> 2);
                 u32x4_t x[4];
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr)
@@ -267,13 +268,16 @@ struct Tile64 {
 // the next BH*Tq the dO images, the last BHkv*Tk the K images of the K/V
 // heads. A head size DT above 128 is cut into NP = DT/128 parts of 128
 // columns, each imaged on its own ([tile][part] order), as the passes below
-// stage them.
+// stage them. With `natural`, the Q and dO images of head sizes up to 128
+// keep the rows in their own order (for the 64-keys-per-wave dK/dV pass,
+// which reads eight consecutive query rows per lane); every other image uses
+// the permuted row order.
 template <int DT>
 __global__ void __launch_bounds__(256)
 bwd_image_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                  const uint16_t* __restrict__ dO, const float* __restrict__ scales,
                  char* __restrict__ qt, char* __restrict__ ot, char* __restrict__ kt, int BH,
-                 int G, int Nq, int Nk, int Tq, int Tk) {
+                 int G, int Nq, int Nk, int Tq, int Tk, int natural) {
     constexpr int D = DT > 128 ? 128 : DT;
     constexpr int NP = DT / D;
     using TileT = Tile64<D, 256, DT>;
@@ -292,7 +296,8 @@ bwd_image_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     __shared__ __attribute__((aligned(16))) char img[TileT::BYTES];
     TileT tl;
     tl.load(src + (size_t)head * N * DT + part * D, tile * 64, N, threadIdx.x);
-    tl.template store_transposed<true>(img, threadIdx.x, s);
+    if (DT <= 128 && which < 2 && natural) tl.template store_transposed<true, true>(img, threadIdx.x, s);
+    else tl.template store_transposed<true, false>(img, threadIdx.x, s);
     __syncthreads();
     char* out = dst + (((size_t)head * T + tile) * NP + part) * TileT::BYTES;
 #pragma unroll
@@ -415,11 +420,12 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         lds_char* base = (lds_char*)(smem + buf * BUF);
         const int tensor = k / PPT, b = wave + NW * (k % PPT);
         if (tensor < 2)
-            stage_tile_block<D, DT>((tensor == 0 ? Kh : Vh) + cs * D,
-                                    base + (tensor == 0 ? OFF_K : OFF_V), t * BC, Nk, b, lane);
+            stage_tile_block_async<D, DT>((tensor == 0 ? Kh : Vh) + cs * D,
+                                          base + (tensor == 0 ? OFF_K : OFF_V), t * BC, Nk, b,
+                                          lane);
         else
-            stage_image_block_full(kt_h + ((size_t)min(t, Tk - 1) * NC + part) * TB,
-                                   base + OFF_KT, b, lane);
+            stage_image_block_full_async(kt_h + ((size_t)min(t, Tk - 1) * NC + part) * TB,
+                                         base + OFF_KT, b, lane);
     };
 
     // Lane-dependent LDS bases of buffer 0: pb[k], k < 8, for the row-major
@@ -457,6 +463,8 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
         for (int k = 0; k < NP0; ++k) stage_part(0, 0, 0, k);
     }
+    // (the copies are not visible to the compiler: wait for them explicitly)
+    wait_copies();
     __syncthreads();
     // The fragment ring, carried from step to step: product o of a step
     // takes fr[o % (LA + 1)], and the first LA fragments of the next step
@@ -722,20 +730,22 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         lds_char* base = (lds_char*)(smem + OFF_R + rb * RBUF);
         const int tensor = k / PPT, b = wave + NW * (k % PPT);
         const size_t qh = live_head(gq, t), ti = live_tile(gq, t);
-        stage_tile_block<D, DT>((tensor == 0 ? Q : dO) + qh * N * DT + cs * D,
-                                base + (tensor == 0 ? OFF_Q : OFF_DO), (int)ti * BQ, N, b, lane);
+        stage_tile_block_async<D, DT>((tensor == 0 ? Q : dO) + qh * N * DT + cs * D,
+                                      base + (tensor == 0 ? OFF_Q : OFF_DO), (int)ti * BQ, N, b,
+                                      lane);
     };
     auto stage_i = [&](int gq, int t, int ib, int k) {
         lds_char* base = (lds_char*)(smem + OFF_I + ib * IBUF);
         const int tensor = k / PPT, b = wave + NW * (k % PPT);
         const size_t qh = live_head(gq, t), ti = live_tile(gq, t);
-        stage_image_block_full((tensor == 0 ? qt_img : ot_img) + ((qh * T + ti) * NC + part) * TB,
-                               base + (tensor == 0 ? OFF_QT : OFF_DOT), b, lane);
+        stage_image_block_full_async(
+            (tensor == 0 ? qt_img : ot_img) + ((qh * T + ti) * NC + part) * TB,
+            base + (tensor == 0 ? OFF_QT : OFF_DOT), b, lane);
     };
     auto stage_stats = [&](int gq, int t, int sb) {
         lds_char* base = (lds_char*)(smem + OFF_T + sb * TBUF);
         const size_t qh = live_head(gq, t), ti = live_tile(gq, t);
-        if (wave == 0) stage_image_block(stats + (qh * T + ti) * 128, 512, base, 0, lane);
+        if (wave == 0) stage_image_block_async(stats + (qh * T + ti) * 128, 512, base, 0, lane);
     };
     // The query tile after (gq, t): the member's next tile, else the next
     // member's first.
@@ -800,6 +810,8 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         stage_stats(0, t0, 0);
         if (NC == 1) stage_stats(g1, t1, 1);
     }
+    // (the copies are not visible to the compiler: wait for them explicitly)
+    wait_copies();
     __syncthreads();
     // The fragment ring, carried from step to step: product o of a step
     // takes fr[o % (LA + 1)], and the first LA fragments of the next step
@@ -978,6 +990,376 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 }
 
 // ---------------------------------------------------------------------------
+// Phase 3 for head sizes 64 and 128: dK, dV with 64 keys per wave.
+// One workgroup per block of 256 keys (4 waves x 64); it walks the query
+// tiles (64 rows) that see them, each as four steps of 16 query rows, so
+// every LDS fragment feeds several products (the 32-key form above reads a
+// fresh fragment for each):
+//   S, dP (16 queries x 64 keys): v_mfma_f32_16x16x32_bf16, A = a 16-row
+//     slice of the Q (dO) tile from LDS, read once for four 16-key blocks;
+//     B = K^T (V^T), resident in VGPRs. Accumulator lane l: key 16j + l%16,
+//     queries 4(l/16) .. +3.
+//   P and dS = P (sE dP - sE D) are formed there, packed to fp16, and one
+//     v_permlane16_swap per pair of registers brings each lane the eight
+//     queries 8g .. 8g+7 (g = l/32) of key l%32 of a 32-key block: the B
+//     operand layout of the 32x32x16 product.
+//   dV^T += dO~^T P, dK^T += Q~^T dS~ (32 dims x 32 keys per product, fp16,
+//     AGPR accumulators), A = the 16-query slice of the transposed fp16
+//     image, read once for both 32-key blocks.
+// Step s's softmax runs between the products of step s-1's dV/dK. Every
+// query tile is staged whole (rows and images, double-buffered) with one
+// barrier per tile.
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(256, 1)
+bwd_dkdv64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                  const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+                  const float* __restrict__ scales, const float* __restrict__ stats,
+                  const char* __restrict__ qt_img, const char* __restrict__ ot_img,
+                  uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int BHkv, int G, int N,
+                  int Nk, int T, float c, float scale) {
+    static_assert(D == 64 || D == 128, "64 keys per wave fit the registers up to d = 128");
+    constexpr int NW = 4;
+    constexpr int BQ = 64;               // query rows per tile
+    constexpr int BKV = NW * 64;         // keys per workgroup
+    constexpr int KC = D / 32;           // 32-wide contraction chunks of S and dP
+    constexpr int NB = D / 32;           // 32-wide row blocks of dV^T and dK^T
+    constexpr int TB = BQ * D * 2;       // bytes of one tile (rows or image)
+    constexpr int BLK = TB / 1024;       // its 1 KB copy blocks
+    constexpr int PPT = BLK / NW;        // blocks per wave and tensor
+    constexpr int OFF_Q = 0, OFF_DO = TB, OFF_QT = 2 * TB, OFF_DOT = 3 * TB;
+    constexpr int BUF = 4 * TB;          // one tile: Q and dO rows, then their images
+    // A statistics copy fills 1 KB of LDS (512 bytes of values, then lanes
+    // repeating the last chunk).
+    constexpr int SBUF = 1024;
+    constexpr int OFF_S = 2 * BUF;
+    __shared__ __attribute__((aligned(16))) char smem[2 * BUF + 2 * SBUF];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, q4 = lane >> 4;   // 16x16 products: key l16, query rows 4 q4 ..
+    const int g = lane >> 5, l32 = lane & 31;    // 32x32 products
+    const int bid = blockIdx.x;
+    const int bkv = bid % BHkv;                  // K/V head
+    const int kb = bid / BHkv;                   // low key blocks see the most queries: first
+    const size_t head = (size_t)bkv * (size_t)Nk * D;
+    const int qh0 = bkv * G;
+
+    const float sQ = scales[qh0 * 4 + 0];
+    const float sV = scales[qh0 * 4 + 2], sDO = scales[qh0 * 4 + 3];
+    const float sE = sDO * sV;
+
+    const int k0 = kb * BKV;
+    const int kw0 = k0 + wave * 64;
+    const int off = Nk - N;                      // query row i sits at key position i + off
+
+    // K^T and (sE V)^T operands of the 16x16x32 products (sE a power of two,
+    // so sE V is exact; keys past Nk read key Nk-1, whose gradients are not
+    // stored).
+    u32x4_t kr[KC][4], vr[KC][4];
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const size_t row = (size_t)min(kw0 + 16 * j + l16, Nk - 1);
+            kr[kc][j] = *(const u32x4_t*)(K + head + row * D + 32 * kc + 8 * q4);
+            const u32x4_t v = *(const u32x4_t*)(V + head + row * D + 32 * kc + 8 * q4);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) vr[kc][j][w] = bf16x2_scale(v[w], sE);
+        }
+
+    // dV^T, dK^T of the wave's two 32-key blocks (AGPRs)
+    f32x16_t acc_dv[2][NB], acc_dk[2][NB];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc_dv[h][nb][r] = acc_dk[h][nb][r] = 0.f;
+
+    const int n_tiles = (N + BQ - 1) / BQ;
+    const int t0 = CAUSAL ? min(max(k0 - off, 0) / BQ, n_tiles) : 0;
+
+    auto live_head = [&](int gq, int t) -> size_t {
+        return (size_t)(qh0 + ((gq < G && t < n_tiles) ? gq : 0));
+    };
+    auto live_tile = [&](int gq, int t) -> size_t { return (size_t)((gq < G && t < n_tiles) ? t : 0); };
+    // Part k (< 4 PPT) of query tile (gq, t) into buffer b: Q rows, dO rows,
+    // the Q~^T image, the dO~^T image, PPT 1 KB blocks each per wave. A tile
+    // past the last is filled from a valid one and never read. (Copies that
+    // the compiler does not see as LDS writes; the barrier at each tile's
+    // start, after every wave has waited for its own copies and for its LDS
+    // reads of the buffer's previous tile, orders them.)
+    auto stage = [&](int gq, int t, int b, int k) {
+        lds_char* base = (lds_char*)(smem + b * BUF);
+        const int tensor = k / PPT, blk = wave + NW * (k % PPT);
+        const size_t qh = live_head(gq, t), ti = live_tile(gq, t);
+        if (tensor < 2)
+            stage_tile_block_async<D, D>((tensor == 0 ? Q : dO) + qh * N * D,
+                                         base + (tensor == 0 ? OFF_Q : OFF_DO), (int)ti * BQ, N,
+                                         blk, lane);
+        else
+            stage_image_block_full_async((tensor == 2 ? qt_img : ot_img) + (qh * T + ti) * TB,
+                                         base + (tensor == 2 ? OFF_QT : OFF_DOT), blk, lane);
+    };
+    auto stage_stats = [&](int gq, int t, int b) {
+        const size_t qh = live_head(gq, t), ti = live_tile(gq, t);
+        if (wave == 0)
+            stage_image_block_async(stats + (qh * T + ti) * 128, 512,
+                                    (lds_char*)(smem + OFF_S + b * SBUF), 0, lane);
+    };
+    auto next_tile = [&](int& gq, int& t) {
+        if (t + 1 < n_tiles) {
+            ++t;
+        } else {
+            ++gq;
+            t = t0;
+        }
+    };
+
+    // Fragment of the row-major Q (dO) tile for step s, chunk kc: row
+    // 16 s + l16, 16-byte chunk 4 kc + q4.
+    auto frag_rm = [&](int b, int off_t, int s, int kc) -> u32x4_t {
+        return *(const lds_u32x4_t*)((lds_char*)smem + b * BUF + off_t +
+                                     row_chunk_offset<D>(16 * s + l16, 4 * kc + q4));
+    };
+    // Fragment of a transposed image for step s, row block nb: row (dim)
+    // 32 nb + l32, queries 16 s + 8 g .. +7 (16-byte chunk 2 s + g).
+    auto frag_tr = [&](int b, int off_t, int s, int nb) -> u32x4_t {
+        return *(const lds_u32x4_t*)((lds_char*)smem + b * BUF + off_t +
+                                     tr_slot_offset(32 * nb + l32, 2 * (2 * s + g)));
+    };
+
+    // One query tile of group member gq, buffer b, as one fully unrolled
+    // sequence of fragment operations. Step s (16 query rows) has three
+    // segments:
+    //   A(s): S(s) = Q K^T, fragments Q(kc), four 16x16x32 products each;
+    //         under it the swaps of step s-1 into the B operands.
+    //   B(s): dP(s) - D = dO V~^T - D (V~ = sE V; the chain starts from
+    //         -sE D), fragments dO(kc).
+    //   C(s): dV and dK of step s-1, fragments dO~^T(nb), Q~^T(nb), two
+    //         32x32x16 products each; under them P(s) = exp2(S c - lse)
+    //         (written over S), dS(s) = P (dP - D) and the fp16 packing of
+    //         P(s) and dS(s). (A 32x32x16 product leaves room for a few vector
+    //         instructions; the 16x16x32 products of A and B hardly any.)
+    // Step 0's C has no products (its vector work runs alone) and step 3's dV,
+    // dK follow the last C. The swaps write the B operands only after the
+    // products that read the previous ones have issued (a matrix product
+    // reads A and B when it issues). Each fragment is read LA operations
+    // ahead through a ring of registers that starts again at every tile.
+    // Causal runs mask the tiles that reach above some of the block's keys,
+    // behind a uniform branch: two copies of this code (masked and not) do
+    // not fit the registers together.
+    constexpr int NS = KC, NGR = 2 * NB;
+    constexpr int NOPS = 4 * (2 * NS) + 4 * NGR;
+    constexpr int LA = 2;
+    // Operation o: kind (0 Q, 1 dO, 2 dO~^T, 3 Q~^T), step, chunk or block.
+    struct Op { int kind, s, x; };
+    auto op_of = [](int o) constexpr -> Op {
+        // per step s < 3: A(s) NS, B(s) NS, then grad(s-1) NGR for s >= 1;
+        // finally grad(3)
+        int base = 0;
+        for (int s = 0; s < 4; ++s) {
+            if (o < base + NS) return Op{0, s, o - base};
+            base += NS;
+            if (o < base + NS) return Op{1, s, o - base};
+            base += NS;
+            if (s >= 1) {
+                if (o < base + NGR) return Op{2 + ((o - base) & 1), s - 1, (o - base) >> 1};
+                base += NGR;
+            }
+        }
+        return Op{2 + ((o - base) & 1), 3, (o - base) >> 1};
+    };
+    auto tile = [&](int gq, int t, int b, bool mask_tile) {
+        const int i0 = t * BQ;
+        const lds_char* st = (lds_char*)smem + OFF_S + b * SBUF;
+        int ga = gq, ta = t;
+        next_tile(ga, ta);
+        f32x4_t sa[4], da[4];           // S then P, and dP - D, of the current step
+        u32x4_t pk[2], dk2[2];          // B operands (P, dS) of the 32-key blocks
+        float lse4[4];
+        f32x4_t dinit;                  // -sE D of the step's four rows
+        uint32_t pp[4][2], dp[4][2];    // packed P, dS of the four 16-key blocks
+        // Causal: key kw0 + 16 j + l16 is above query row i0 + 16 s + 4 q4 + i
+        // when dlt > 16 (s - j) + i.
+        const int dlt = kw0 + l16 - i0 - 4 * q4 - off;
+
+        auto frag = [&](int o) -> u32x4_t {
+            const Op op = op_of(o);
+            const lds_char* base = (lds_char*)smem + b * BUF;
+            if (op.kind < 2)
+                return *(const lds_u32x4_t*)(base + (op.kind == 0 ? OFF_Q : OFF_DO) +
+                                             row_chunk_offset<D>(16 * op.s + l16, 4 * op.x + q4));
+            return *(const lds_u32x4_t*)(base + (op.kind == 2 ? OFF_DOT : OFF_QT) +
+                                         tr_slot_offset(32 * op.x + l32, 2 * (2 * op.s + g)));
+        };
+        auto load_stats = [&](int s) {
+            const f32x4_t a = *(const lds_f32x4_t*)(st + 4 * (16 * s + 4 * q4));
+            const f32x4_t d = *(const lds_f32x4_t*)(st + 4 * (64 + 16 * s + 4 * q4));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                lse4[i] = a[i];
+                dinit[i] = -d[i];
+            }
+        };
+        // P of step s, key block j, over S: element (j, i) is key kw0 + 16 j +
+        // l16 and query row i0 + 16 s + 4 q4 + i.
+        auto exp_block = [&](int s, int j) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sa[j][i] = fast_exp2(__builtin_fmaf(sa[j][i], c, -lse4[i]));
+            if (CAUSAL && mask_tile) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (dlt > 16 * (s - j) + i) sa[j][i] = 0.f;
+            }
+        };
+        // dS = P (dP - D) of key block j, and both packed to fp16
+        auto ds_block = [&](int j) {
+            pp[j][0] = pack_f16x2(sa[j][0], sa[j][1]);
+            pp[j][1] = pack_f16x2(sa[j][2], sa[j][3]);
+            dp[j][0] = pack_f16x2(sa[j][0] * da[j][0], sa[j][1] * da[j][1]);
+            dp[j][1] = pack_f16x2(sa[j][2] * da[j][2], sa[j][3] * da[j][3]);
+        };
+        // Key blocks 2h, 2h+1 -> the 32-key block h in the 32x32 B layout.
+        auto swap_block = [&](int h) {
+#pragma unroll
+            for (int w = 0; w < 2; ++w) {
+                const auto rp = __builtin_amdgcn_permlane16_swap(pp[2 * h][w], pp[2 * h + 1][w],
+                                                                 false, false);
+                const auto rd = __builtin_amdgcn_permlane16_swap(dp[2 * h][w], dp[2 * h + 1][w],
+                                                                 false, false);
+                pk[h][w] = rp[0];
+                pk[h][2 + w] = rp[1];
+                dk2[h][w] = rd[0];
+                dk2[h][2 + w] = rd[1];
+            }
+        };
+
+        u32x4_t fr[LA + 1];
+#pragma unroll
+        for (int o = 0; o < LA; ++o) fr[o] = frag(o);
+        load_stats(0);
+#pragma unroll
+        for (int o = 0; o < NOPS; ++o) {
+            const Op op = op_of(o);
+            if (o + LA < NOPS) fr[(o + LA) % (LA + 1)] = frag(o + LA);
+            const u32x4_t a = fr[o % (LA + 1)];
+            if (op.kind == 0) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (op.x == 0) sa[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                    sa[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, kr[op.x][j]),
+                        sa[j], 0, 0, 0);
+                }
+                // A(s): the swaps of step s-1
+                if (op.s >= 1 && op.x == 0) swap_block(0);
+                if (op.s >= 1 && op.x == NS - 1) swap_block(1);
+            } else if (op.kind == 1) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (op.x == 0) da[j] = dinit;
+                    da[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, vr[op.x][j]),
+                        da[j], 0, 0, 0);
+                }
+                if (op.x == NS - 1 && op.s == 0) {
+                    // C(0): no products to run under
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) exp_block(0, j);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) ds_block(j);
+                    load_stats(1);
+                }
+            } else {
+                if (op.kind == 2) {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) mfma_f16_agpr(acc_dv[h][op.x], a, pk[h]);
+                } else {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) mfma_f16_agpr(acc_dk[h][op.x], a, dk2[h]);
+                }
+                // C(s) = grad(s-1): P, dS and packing of step s = op.s + 1, one
+                // key block's exponentials after each dO~^T operation's
+                // products and its dS after the following Q~^T operation's
+                if (op.s < 3) {
+                    const int sn = op.s + 1;
+#pragma unroll
+                    for (int j = op.x * 4 / NB; j < (op.x + 1) * 4 / NB; ++j) {
+                        if (op.kind == 2) exp_block(sn, j);
+                        else ds_block(j);
+                    }
+                    if (op.kind == 3 && op.x == NB - 1 && sn < 3) load_stats(sn + 1);
+                }
+                // before grad(3): step 3's swaps (no S segment follows)
+                if (op.s == 2 && op.kind == 3 && op.x == NB - 1) {
+                    swap_block(0);
+                    swap_block(1);
+                }
+            }
+            // the next tile's copies, one every third operation from the fourth on
+#pragma unroll
+            for (int k = 0; k < 4 * PPT; ++k)
+                if (o == 3 + 3 * k) stage(ga, ta, b ^ 1, k);
+            if (o == 4) stage_stats(ga, ta, b ^ 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // Causal: tiles whose first row precedes the block's last key position
+    // reach above some of its keys.
+    const int last_kq = k0 + BKV - 1 - off;
+    const int t_free = CAUSAL ? min(max((max(last_kq, 0) + BQ - 1) / BQ, t0), n_tiles) : t0;
+    if (t0 < n_tiles) {
+#pragma unroll
+        for (int k = 0; k < 4 * PPT; ++k) stage(0, t0, 0, k);
+        stage_stats(0, t0, 0);
+        int L = 0;
+        for (int gq = 0; gq < G; ++gq) {
+            for (int t = t0; t < n_tiles; ++t, ++L) {
+                // this wave's copies of tile L have landed and its reads of
+                // tile L-1 are done; after the barrier everyone's are
+                wait_copies();
+                wait_lds();
+                step_barrier();
+                tile(gq, t, L & 1, t < t_free);
+            }
+        }
+        wait_copies();
+    }
+
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            agpr_settle(acc_dk[h][nb]);
+            agpr_settle(acc_dv[h][nb]);
+        }
+    const float fk = scale / (sQ * sE), fv = 1.f / sDO;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int kj = kw0 + 32 * h + l32;
+        if (kj < Nk) {
+            uint16_t* dkrow = dK + head + (size_t)kj * D;
+            uint16_t* dvrow = dV + head + (size_t)kj * D;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    u32x2_t wk, wv;
+                    wk[0] = pack_bf16x2(acc_dk[h][nb][4 * q + 0] * fk, acc_dk[h][nb][4 * q + 1] * fk);
+                    wk[1] = pack_bf16x2(acc_dk[h][nb][4 * q + 2] * fk, acc_dk[h][nb][4 * q + 3] * fk);
+                    wv[0] = pack_bf16x2(acc_dv[h][nb][4 * q + 0] * fv, acc_dv[h][nb][4 * q + 1] * fv);
+                    wv[1] = pack_bf16x2(acc_dv[h][nb][4 * q + 2] * fv, acc_dv[h][nb][4 * q + 3] * fv);
+                    *(u32x2_t*)(dkrow + 32 * nb + 8 * q + 4 * g) = wk;
+                    *(u32x2_t*)(dvrow + 32 * nb + 8 * q + 4 * g) = wv;
+                }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Launchers (arguments already validated by the C-ABI layer).
 // ---------------------------------------------------------------------------
 constexpr int kBwdWaves = 4;
@@ -990,6 +1372,14 @@ template <typename T>
 static T* ws_ptr(const BwdArgs& a, size_t off) { return (T*)((char*)a.workspace + off); }
 
 static int q_tiles64(const BwdArgs& a) { return (a.N + 63) / 64; }
+// The dK/dV pass with 64 keys per wave (256 per workgroup) for head sizes up
+// to 128, when its grid still has two workgroups per compute unit of an
+// MI355X; otherwise (few K/V heads or short sequences, where 256-key blocks
+// leave the longest causal block alone at the end) the 32-keys-per-wave
+// pass. The preprocess lays the Q and dO images out for the pass chosen here.
+static bool use_dkdv64(const BwdArgs& a) {
+    return a.d <= 128 && (long long)((a.Nk + 255) / 256) * a.B * a.Hkv >= 512;
+}
 static int k_tiles64(const BwdArgs& a) { return (a.Nk + 63) / 64; }
 // Column parts of a head (128 columns each above d = 128).
 static int col_parts(int d) { return d > 128 ? d / 128 : 1; }
@@ -1016,7 +1406,7 @@ static hipError_t launch_prepare_t(const BwdArgs& a) {
                        a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                        (const uint16_t*)a.dout, ws_ptr<const float>(a, w.scales),
                        ws_ptr<char>(a, w.qt), ws_ptr<char>(a, w.ot), ws_ptr<char>(a, w.kt), BH,
-                       G, a.N, a.Nk, Tq, Tk);
+                       G, a.N, a.Nk, Tq, Tk, use_dkdv64(a) ? 1 : 0);
     return hipGetLastError();
 }
 
@@ -1039,18 +1429,31 @@ static hipError_t launch_dq_t(const BwdArgs& a) {
 
 template <int D, bool CAUSAL>
 static hipError_t launch_dkdv_t(const BwdArgs& a) {
-    constexpr int NW = kBwdWaves;
     const BwdWorkspace w = ws_of(a);
     const int BHkv = a.B * a.Hkv;
-    const int nkb = (a.Nk + NW * 32 - 1) / (NW * 32);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, CAUSAL>), dim3(nkb * BHkv * col_parts(D)),
-                       dim3(NW * 64), 0,
-                       a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                       (const uint16_t*)a.v, (const uint16_t*)a.dout,
-                       ws_ptr<const float>(a, w.scales), ws_ptr<const float>(a, w.stats),
-                       ws_ptr<const char>(a, w.qt), ws_ptr<const char>(a, w.ot),
-                       (uint16_t*)a.dk, (uint16_t*)a.dv, BHkv, a.H / a.Hkv, a.N, a.Nk,
-                       q_tiles64(a), a.scale * kLog2e, a.scale);
+    if (D <= 128 && use_dkdv64(a)) {
+        // 64 keys per wave, 256 per workgroup
+        const int nkb = (a.Nk + 255) / 256;
+        hipLaunchKernelGGL((bwd_dkdv64_kernel<(D <= 128 ? D : 128), CAUSAL>), dim3(nkb * BHkv),
+                           dim3(256), 0,
+                           a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                           (const uint16_t*)a.v, (const uint16_t*)a.dout,
+                           ws_ptr<const float>(a, w.scales), ws_ptr<const float>(a, w.stats),
+                           ws_ptr<const char>(a, w.qt), ws_ptr<const char>(a, w.ot),
+                           (uint16_t*)a.dk, (uint16_t*)a.dv, BHkv, a.H / a.Hkv, a.N, a.Nk,
+                           q_tiles64(a), a.scale * kLog2e, a.scale);
+    } else {
+        constexpr int NW = kBwdWaves;
+        const int nkb = (a.Nk + NW * 32 - 1) / (NW * 32);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, CAUSAL>), dim3(nkb * BHkv * col_parts(D)),
+                           dim3(NW * 64), 0,
+                           a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                           (const uint16_t*)a.v, (const uint16_t*)a.dout,
+                           ws_ptr<const float>(a, w.scales), ws_ptr<const float>(a, w.stats),
+                           ws_ptr<const char>(a, w.qt), ws_ptr<const char>(a, w.ot),
+                           (uint16_t*)a.dk, (uint16_t*)a.dv, BHkv, a.H / a.Hkv, a.N, a.Nk,
+                           q_tiles64(a), a.scale * kLog2e, a.scale);
+    }
     return hipGetLastError();
 }
 

@@ -263,6 +263,23 @@ __device__ __forceinline__ void lds_dma16(const void* base, uint32_t voff, lds_c
         (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
 }
 
+// The same copy as one inline-assembly block (M0 = the LDS destination, then
+// the load). The compiler then does not see an LDS write: it would otherwise
+// wait for every outstanding LDS read before each copy (it cannot prove that
+// the copy's destination does not overlap them), which empties a kernel's
+// ring of fragment reads at every copy. The caller orders the copies against
+// LDS reads itself: each copy goes to a buffer that no wave reads until the
+// next barrier, and each wave waits for its copies (vmcnt) before that
+// barrier. No VGPR is written.
+__device__ __forceinline__ void lds_dma16_async(const void* base, uint32_t voff, lds_char* dst) {
+    const uint64_t b = (uint64_t)uniform_ptr(base);
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(b), "s"(m0)
+                 : "memory", "m0");
+}
+
 // K-type tiles: chunk c of row r is stored at chunk c ^ row_chunk_swizzle(r).
 // V-type tiles: chunk c of row r is stored at chunk c ^ (2 * (r & 3)), which
 // makes the transposed 8-byte reads below conflict-free.
@@ -304,6 +321,30 @@ template <int D, int LD = D>
 __device__ __forceinline__ void stage_tile_block(const uint16_t* __restrict__ src, lds_char* tile,
                                                  int row0, int N, int b, int lane) {
     stage_block<D, false, LD>(src, tile, row0, N, b, lane);
+}
+
+template <int D, int LD = D>
+__device__ __forceinline__ void stage_tile_block_async(const uint16_t* __restrict__ src,
+                                                       lds_char* tile, int row0, int N, int b,
+                                                       int lane) {
+    constexpr int DCH = D / 8;
+    constexpr int RPK = 1024 / (2 * D);
+    const int row = b * RPK + lane / DCH;
+    const int phys = lane % DCH;
+    const int logical = phys ^ row_chunk_swizzle<D>(row);
+    const int rb = min(row0, N - 1);
+    const uint32_t voff = (uint32_t)(min(row, N - 1 - rb) * (2 * LD) + logical * 16);
+    lds_dma16_async(src + (size_t)rb * LD, voff, tile + b * 1024);
+}
+
+__device__ __forceinline__ void stage_image_block_full_async(const void* src, lds_char* tile,
+                                                             int b, int lane) {
+    lds_dma16_async((const char*)src + b * 1024, (uint32_t)(lane * 16), tile + b * 1024);
+}
+
+__device__ __forceinline__ void stage_image_block_async(const void* src, int bytes,
+                                                        lds_char* tile, int b, int lane) {
+    lds_dma16_async(src, (uint32_t)min(b * 1024 + lane * 16, bytes - 16), tile + b * 1024);
 }
 
 __device__ __forceinline__ void stage_image_block(const void* src, int bytes, lds_char* tile,

@@ -108,6 +108,35 @@ def test_bf16_backward_sharp_scores_large_value_mean(fa, causal, v_mean):
     check_bf16("dV", to_np(dv), rv, rule="rounded")
 
 
+# Shapes whose 256-key blocks give at least 512 workgroups, so that dK and dV
+# come from the pass with 64 keys per wave (smaller grids take the pass with
+# 32 keys per wave, which the tests above cover): ragged lengths, both masks,
+# d = 64 and 128, shared K/V heads, and fewer query rows than keys.
+WIDE_GRID = [(2, 256, 256, 300, 300, 128), (1, 512, 512, 65, 65, 64), (4, 256, 128, 257, 257, 128),
+             (1, 512, 256, 100, 333, 128), (2, 256, 256, 700, 700, 64)]
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("B,H,Hkv,Nq,Nk,d", WIDE_GRID)
+def test_bf16_backward_64key_pass(fa, B, H, Hkv, Nq, Nk, d, causal):
+    import torch
+    assert ((Nk + 255) // 256) * B * Hkv >= 512
+    say(f"fa_bwd_rect (64 keys per wave) B={B} H={H} Hkv={Hkv} Nq={Nq} Nk={Nk} d={d} "
+        f"causal={causal} seed=25")
+    inp = wl.make_decode_inputs(B, H, Hkv, Nq, Nk, d, seed=25, with_do=True)
+    scale = float(np.float32(1 / np.sqrt(d)))
+    q, k, v, do = (wl.to_device(x, "bf16") for x in (inp.q, inp.k, inp.v, inp.do))
+    o, lse = fa.fa_fwd_rect(q, k, v, causal=causal, scale=scale)
+    dq, dk, dv = fa.fa_bwd_rect(q, k, v, o, do, lse, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    q64, k64, v64, do64 = inp.as_float64()
+    with single_threaded_blas():
+        rq, rk, rv = ora.rect_bwd(q64, k64, v64, do64, causal, scale, workers=oracle_workers())
+    check_bf16("dQ", to_np(dq), rq)
+    check_bf16("dK", to_np(dk), rk)
+    check_bf16("dV", to_np(dv), rv)
+
+
 def test_backward_phases_equal_fa_bwd(fa):
     """fa_bwd is exactly its three phases, and repeated calls give equal bits."""
     import torch
