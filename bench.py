@@ -2,9 +2,10 @@
 """Benchmark of the fused exact-attention hot path on one MI355X.
 
 One step = one pass of the whole path over one batch of seeded synthetic
-input: the fused forward (fa_fwd) and the backward (fa_bwd's three phases:
-per-head scale factors and fp16 tile images, dQ with D, dK/dV) on the causal bf16 workload B=4 H=16 N=4096
-d=128 with upstream gradient dO. ``value`` is counted TFLOP/s of that step,
+input: the fused forward (fa_fwd, keeping O's rounding residual for the
+backward) and the backward (fa_bwd's three phases: per-head scale factors,
+D = rowsum(dO * O) and fp16 tile images; dQ; dK/dV) on the causal bf16
+workload B=4 H=16 N=4096 d=128 with upstream gradient dO. ``value`` is counted TFLOP/s of that step,
 with the counted flops 4*B*H*N^2*d (halved for causal) for the forward and
 2.5x that for the backward. Inputs are resident in HBM before timing starts.
 
@@ -164,7 +165,7 @@ def gpu_step_timing(w, steps: int, warmup: int, with_clock: bool = True):
     dev = torch.device("cuda:0")
     inp = wl.workload_inputs(w)
     q, k, v, do = (wl.to_device(x, "bf16", dev) for x in (inp.q, inp.k, inp.v, inp.do))
-    o = torch.empty_like(q)
+    o, o_res = torch.empty_like(q), torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
     ws = torch.empty(fa.fa_bwd_workspace_size(w.B, w.H, w.N, w.d), dtype=torch.uint8, device=dev)
@@ -173,13 +174,13 @@ def gpu_step_timing(w, steps: int, warmup: int, with_clock: bool = True):
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        fa.fa_fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+        fa.fa_fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, o_res=o_res)
         if ev is not None:
             ev[1].record()
-        fa.fa_bwd_preprocess(q, k, v, o, do, ws)
+        fa.fa_bwd_preprocess(q, k, v, o, do, ws, o_res=o_res)
         if ev is not None:
             ev[2].record()
-        fa.fa_bwd_dq(q, k, v, do, lse, ws, dq, causal=w.causal, scale=w.scale)
+        fa.fa_bwd_dq(q, k, v, do, lse, ws, dq, causal=w.causal, scale=w.scale, d_ready=True)
         if ev is not None:
             ev[3].record()
         fa.fa_bwd_dkdv(q, k, v, do, ws, dk, dv, causal=w.causal, scale=w.scale)
@@ -206,10 +207,11 @@ def gpu_step_timing(w, steps: int, warmup: int, with_clock: bool = True):
     # on its own (back to back; the workspace holds what the later phases
     # read).
     kernels = {
-        "fwd": lambda: fa.fa_fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse),
-        "bwd_preprocess": lambda: fa.fa_bwd_preprocess(q, k, v, o, do, ws),
+        "fwd": lambda: fa.fa_fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse,
+                                 o_res=o_res),
+        "bwd_preprocess": lambda: fa.fa_bwd_preprocess(q, k, v, o, do, ws, o_res=o_res),
         "bwd_dq": lambda: fa.fa_bwd_dq(q, k, v, do, lse, ws, dq, causal=w.causal,
-                                       scale=w.scale),
+                                       scale=w.scale, d_ready=True),
         "bwd_dkdv": lambda: fa.fa_bwd_dkdv(q, k, v, do, ws, dk, dv, causal=w.causal,
                                            scale=w.scale),
     }
@@ -219,6 +221,15 @@ def gpu_step_timing(w, steps: int, warmup: int, with_clock: bool = True):
         for n in names:
             clocks[n] = measure_sclk(kernels[n], dev)
     log("bench: shader clock (MHz) " + ", ".join(f"{k}={v}" for k, v in clocks.items()))
+    if with_clock:
+        # For comparison (not part of the step): the preprocess and dQ pass of
+        # a backward given no residual, where the dQ pass forms D itself.
+        timer = CallTimer(dev)
+        per_kernel["bwd_preprocess_no_res"] = timer.median(
+            lambda: fa.fa_bwd_preprocess(q, k, v, o, do, ws))[0]
+        per_kernel["bwd_dq_no_res"] = timer.median(
+            lambda: fa.fa_bwd_dq(q, k, v, do, lse, ws, dq, causal=w.causal, scale=w.scale,
+                                 d_ready=False))[0]
     return ms_per_step, per_kernel, clocks
 
 
@@ -347,18 +358,18 @@ def gpu_gqa_timing(names):
         w = wl.GQA_WORKLOADS[name]
         inp = wl.workload_inputs(w)
         q, k, v, do = (wl.to_device(x, "bf16", dev) for x in (inp.q, inp.k, inp.v, inp.do))
-        o = torch.empty_like(q)
+        o, o_res = torch.empty_like(q), torch.empty_like(q)
         lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         ws = torch.empty(fa.fa_bwd_gqa_workspace_size(w.B, w.H, w.kv_heads, w.N, w.d),
                          dtype=torch.uint8, device=dev)
 
         def fwd():
-            fa.fa_fwd_gqa(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+            fa.fa_fwd_gqa(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, o_res=o_res)
 
         def bwd():
             fa.fa_bwd_gqa(q, k, v, o, do, lse, causal=w.causal, scale=w.scale, dq=dq, dk=dk,
-                          dv=dv, workspace=ws)
+                          dv=dv, workspace=ws, o_res=o_res)
 
         res = {label: timer.both(fn) for label, fn in (("fwd", fwd), ("bwd", bwd))}
         ftf = w.fwd_flops() / (res["fwd"][0] * 1e-3) / 1e12
@@ -373,7 +384,7 @@ def gpu_gqa_timing(names):
         log(f"  gqa {name}: fwd {res['fwd'][0]:.3f} ms {ftf:.1f} TFLOP/s, "
             f"bwd {res['bwd'][0]:.3f} ms {btf:.1f} TFLOP/s (cold {res['fwd'][1]:.3f}, "
             f"{res['bwd'][1]:.3f} ms)")
-        del q, k, v, do, o, lse, dq, dk, dv, ws
+        del q, k, v, do, o, o_res, lse, dq, dk, dv, ws
     return out
 
 
@@ -392,16 +403,16 @@ def gpu_wide_bwd_timing(names):
         w = wl.WIDE_WORKLOADS[name]
         inp = wl.make_inputs(w.B, w.H, w.N, w.d, "bf16", w.seed, with_do=True)
         q, k, v, do = (wl.to_device(x, "bf16", dev) for x in (inp.q, inp.k, inp.v, inp.do))
-        o = torch.empty_like(q)
+        o, o_res = torch.empty_like(q), torch.empty_like(q)
         lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
-        fa.fa_fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+        fa.fa_fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, o_res=o_res)
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         ws = torch.empty(fa.fa_bwd_workspace_size(w.B, w.H, w.N, w.d), dtype=torch.uint8,
                          device=dev)
 
         def call():
             fa.fa_bwd(q, k, v, o, do, lse, causal=w.causal, scale=w.scale, dq=dq, dk=dk, dv=dv,
-                      workspace=ws)
+                      workspace=ws, o_res=o_res)
 
         med, cold, n = timer.both(call)
         tf = w.bwd_flops() / (med * 1e-3) / 1e12
@@ -410,7 +421,7 @@ def gpu_wide_bwd_timing(names):
                     "calls": n})
         log(f"  bwd {name}: {med:.3f} ms  {tf:.1f} TFLOP/s  {100 * tf / PEAK_BF16_TFLOPS:.1f}% "
             f"(cold {cold:.3f} ms)")
-        del q, k, v, do, o, lse, dq, dk, dv, ws
+        del q, k, v, do, o, o_res, lse, dq, dk, dv, ws
     return out
 
 
@@ -430,18 +441,18 @@ def gpu_rect_timing(names):
         w = wl.RECT_WORKLOADS[name]
         inp = wl.make_decode_inputs(w.B, w.H, w.Hkv, w.Nq, w.Nk, w.d, w.seed, with_do=True)
         q, k, v, do = (wl.to_device(x, "bf16", dev) for x in (inp.q, inp.k, inp.v, inp.do))
-        o = torch.empty_like(q)
+        o, o_res = torch.empty_like(q), torch.empty_like(q)
         lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         ws = torch.empty(fa.fa_bwd_rect_workspace_size(w.B, w.H, w.Hkv, w.Nq, w.Nk, w.d),
                          dtype=torch.uint8, device=dev)
 
         def fwd():
-            fa.fa_fwd_rect(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+            fa.fa_fwd_rect(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, o_res=o_res)
 
         def bwd():
             fa.fa_bwd_rect(q, k, v, o, do, lse, causal=w.causal, scale=w.scale, dq=dq, dk=dk,
-                           dv=dv, workspace=ws)
+                           dv=dv, workspace=ws, o_res=o_res)
 
         res = {label: timer.both(fn) for label, fn in (("fwd", fwd), ("bwd", bwd))}
         ftf = wl.rect_flops(w) / (res["fwd"][0] * 1e-3) / 1e12
@@ -456,7 +467,7 @@ def gpu_rect_timing(names):
         log(f"  rect {name}: fwd {res['fwd'][0]:.3f} ms {ftf:.1f} TFLOP/s "
             f"{100 * ftf / PEAK_BF16_TFLOPS:.1f}%, bwd {res['bwd'][0]:.3f} ms {btf:.1f} TFLOP/s "
             f"{100 * btf / PEAK_BF16_TFLOPS:.1f}%")
-        del q, k, v, do, o, lse, dq, dk, dv, ws
+        del q, k, v, do, o, o_res, lse, dq, dk, dv, ws
     return out
 
 
@@ -648,9 +659,9 @@ def main() -> int:
 
     # Algorithmic MFMA flops each kernel performs over the unmasked score
     # elements (counted convention N^2/2 when causal): 4d per score forward
-    # (Q K^T, P V), 8d for dQ (S, dP, sum P*dP*K, sum P*K), 8d for dK/dV
-    # (S, dP, dV, dK).
-    alg = {"fwd": fwd_f, "bwd_dq": 2.0 * fwd_f, "bwd_dkdv": 2.0 * fwd_f}
+    # (Q K^T, P V), 6d for dQ (S, dP, dS K: D comes from the preprocess), 8d
+    # for dK/dV (S, dP, dV, dK).
+    alg = {"fwd": fwd_f, "bwd_dq": 1.5 * fwd_f, "bwd_dkdv": 2.0 * fwd_f}
     dominant = max(alg, key=lambda n: per_kernel[n])
     achieved = alg[dominant] / (per_kernel[dominant] * 1e-3) / 1e12
     traffic = None

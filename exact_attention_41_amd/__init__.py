@@ -6,8 +6,10 @@ calls; every step of the computation runs in the HIP kernels of libfa.so.
 If the library is not built, every call raises: there is no fallback.
 
     o, lse = fa_fwd(q, k, v, causal=True)                  # bf16 [B,H,N,d]
+    o, lse = fa_fwd(q, k, v, causal=True, o_res=r)         # also O's rounding residual
     o, lse = fa_fwd_f32(q, k, v, causal=False)             # fp32 [B,H,N,d]
     dq, dk, dv = fa_bwd(q, k, v, o, do, lse, causal=True)  # bf16
+    dq, dk, dv = fa_bwd(q, k, v, o, do, lse, causal=True, o_res=r)
     o, lse = fa_fwd_gqa(q, k, v, causal=True)              # k, v: [B,Hkv,N,d]
     dq, dk, dv = fa_bwd_gqa(q, k, v, o, do, lse, causal=True)
     o, lse = fa_decode(q, k, v)          # q [B,H,Nq,d], k, v [B,Hkv,Nk,d]
@@ -108,7 +110,15 @@ def _kv_heads(q, k, grouped):
     return Hkv
 
 
-def _fwd(entry, dtype, q, k, v, causal, scale, out, lse, grouped=False):
+def _o_res_ptr(o_res, q):
+    """Device pointer of an optional o_res tensor (bf16, q's shape), or None."""
+    if o_res is None:
+        return None
+    _check(o_res, "o_res", _torch().bfloat16, q.shape, q.device)
+    return o_res.data_ptr()
+
+
+def _fwd(entry, dtype, q, k, v, causal, scale, out, lse, grouped=False, o_res=None):
     torch = _torch()
     _check(q, "q", dtype)
     if q.dim() != 4:
@@ -126,8 +136,9 @@ def _fwd(entry, dtype, q, k, v, causal, scale, out, lse, grouped=False):
     _check(lse, "lse", torch.float32, (B, H, N), q.device)
     fn = getattr(_lib.load(), entry)
     heads = (B, H, Hkv) if grouped else (B, H)
+    res = () if entry == "fa_fwd_f32" else (_o_res_ptr(o_res, q),)
     with torch.cuda.device(q.device):
-        st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+        st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), *res, lse.data_ptr(),
                 *heads, N, d, int(bool(causal)), _scale(scale, d), _stream_ptr(q.device))
     if st != _lib.FA_OK:
         raise FAError(st, entry)
@@ -135,17 +146,20 @@ def _fwd(entry, dtype, q, k, v, causal, scale, out, lse, grouped=False):
 
 
 def fa_fwd(q, k, v, causal: bool = False, scale: Optional[float] = None,
-           out=None, lse=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
-    """bf16 forward: returns (O, logsumexp). Calls fa_fwd of libfa.so."""
-    return _fwd("fa_fwd", _torch().bfloat16, q, k, v, causal, scale, out, lse)
+           out=None, lse=None, o_res=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
+    """bf16 forward: returns (O, logsumexp). ``o_res``, a bf16 tensor of q's
+    shape, receives O's rounding residual when given (for fa_bwd). Calls
+    fa_fwd of libfa.so."""
+    return _fwd("fa_fwd", _torch().bfloat16, q, k, v, causal, scale, out, lse, o_res=o_res)
 
 
 def fa_fwd_gqa(q, k, v, causal: bool = False, scale: Optional[float] = None,
-               out=None, lse=None):
+               out=None, lse=None, o_res=None):
     """bf16 forward with shared K/V heads: q [B,H,N,d], k and v [B,Hkv,N,d]
     (Hkv dividing H; query head h uses K/V head h // (H // Hkv)). Returns
-    (O, logsumexp). Calls fa_fwd_gqa of libfa.so."""
-    return _fwd("fa_fwd_gqa", _torch().bfloat16, q, k, v, causal, scale, out, lse, grouped=True)
+    (O, logsumexp); ``o_res`` as for fa_fwd. Calls fa_fwd_gqa of libfa.so."""
+    return _fwd("fa_fwd_gqa", _torch().bfloat16, q, k, v, causal, scale, out, lse, grouped=True,
+                o_res=o_res)
 
 
 def fa_fwd_f32(q, k, v, causal: bool = False, scale: Optional[float] = None,
@@ -155,7 +169,7 @@ def fa_fwd_f32(q, k, v, causal: bool = False, scale: Optional[float] = None,
 
 
 def _bwd(entry, q, k, v, o, do, lse, causal, scale, dq, dk, dv, workspace, grouped,
-         rect=False):
+         rect=False, o_res=None):
     torch = _torch()
     bf = torch.bfloat16
     _check(q, "q", bf)
@@ -186,8 +200,8 @@ def _bwd(entry, q, k, v, o, do, lse, causal, scale, dq, dk, dv, workspace, group
     sizes = (N, Nk) if rect else (N,)
     fn = getattr(_lib.load(), entry)
     with torch.cuda.device(q.device):
-        st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
-                lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+        st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _o_res_ptr(o_res, q),
+                do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                 workspace.data_ptr(), ws_bytes, *heads, *sizes, d, int(bool(causal)),
                 _scale(scale, d), _stream_ptr(q.device))
     if st != _lib.FA_OK:
@@ -196,33 +210,37 @@ def _bwd(entry, q, k, v, o, do, lse, causal, scale, dq, dk, dv, workspace, group
 
 
 def fa_bwd(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = None,
-           dq=None, dk=None, dv=None, workspace=None):
+           dq=None, dk=None, dv=None, workspace=None, o_res=None):
     """bf16 backward: returns (dQ, dK, dV). Calls fa_bwd of libfa.so.
 
     ``workspace`` may be a uint8 device tensor of at least
     fa_bwd_workspace_size(B, H, N, d) bytes; one is allocated otherwise.
+    ``o_res``: the forward's rounding residual of O, if it kept one (then D
+    comes from O in the preprocess and the dQ pass is cheaper).
     """
-    return _bwd("fa_bwd", q, k, v, o, do, lse, causal, scale, dq, dk, dv, workspace, False)
+    return _bwd("fa_bwd", q, k, v, o, do, lse, causal, scale, dq, dk, dv, workspace, False,
+                o_res=o_res)
 
 
 def fa_bwd_gqa(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = None,
-               dq=None, dk=None, dv=None, workspace=None):
+               dq=None, dk=None, dv=None, workspace=None, o_res=None):
     """bf16 backward of fa_fwd_gqa: returns (dQ [B,H,N,d], dK and dV [B,Hkv,N,d],
     each K/V head's gradient summed over the query heads that share it).
     Calls fa_bwd_gqa of libfa.so; ``workspace`` as for fa_bwd, of
     fa_bwd_gqa_workspace_size(B, H, Hkv, N, d) bytes."""
-    return _bwd("fa_bwd_gqa", q, k, v, o, do, lse, causal, scale, dq, dk, dv, workspace, True)
+    return _bwd("fa_bwd_gqa", q, k, v, o, do, lse, causal, scale, dq, dk, dv, workspace, True,
+                o_res=o_res)
 
 
 def fa_bwd_rect(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = None,
-                dq=None, dk=None, dv=None, workspace=None):
+                dq=None, dk=None, dv=None, workspace=None, o_res=None):
     """bf16 backward of fa_fwd_rect: q, o, do [B,H,Nq,d], lse [B,H,Nq], k and v
     [B,Hkv,Nk,d]; returns (dQ [B,H,Nq,d], dK and dV [B,Hkv,Nk,d]). Query row i
     sits at position Nk - Nq + i (bottom-right causal alignment). Calls
     fa_bwd_rect of libfa.so; ``workspace`` as for fa_bwd, of
     fa_bwd_rect_workspace_size(B, H, Hkv, Nq, Nk, d) bytes."""
     return _bwd("fa_bwd_rect", q, k, v, o, do, lse, causal, scale, dq, dk, dv, workspace, True,
-                rect=True)
+                rect=True, o_res=o_res)
 
 
 def _bwd_common(ref, tensors, lse, workspace):
@@ -242,21 +260,24 @@ def _bwd_common(ref, tensors, lse, workspace):
     return B, H, N, d, _check_workspace(workspace, ref.device)
 
 
-def fa_bwd_preprocess(q, k, v, o, do, workspace):
-    """Phase 1 of fa_bwd: per-head scale factors, D^ = rowsum(dO * O) and the
-    scaled fp16 transposed copies of q, dO and k into ``workspace``."""
+def fa_bwd_preprocess(q, k, v, o, do, workspace, o_res=None):
+    """Phase 1 of fa_bwd: per-head scale factors, rowsum(dO * O) (O = o, or
+    o + o_res when ``o_res`` is given) and the scaled fp16 transposed copies of
+    q, dO and k into ``workspace``."""
     torch = _torch()
     B, H, N, d, ws = _bwd_common(k, [(q, "q"), (v, "v"), (o, "o"), (do, "do")], None, workspace)
     with torch.cuda.device(k.device):
         st = _lib.load().fa_bwd_preprocess(q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                                           o.data_ptr(), do.data_ptr(), workspace.data_ptr(), ws,
-                                           B, H, N, d, _stream_ptr(k.device))
+                                           o.data_ptr(), _o_res_ptr(o_res, q), do.data_ptr(),
+                                           workspace.data_ptr(), ws, B, H, N, d,
+                                           _stream_ptr(k.device))
     if st != _lib.FA_OK:
         raise FAError(st, "fa_bwd_preprocess")
 
 
-def fa_bwd_dq(q, k, v, do, lse, workspace, dq, causal=False, scale=None):
-    """Phase 2 of fa_bwd: dQ (plus lse and D per query row in ``workspace``)."""
+def fa_bwd_dq(q, k, v, do, lse, workspace, dq, causal=False, scale=None, d_ready=False):
+    """Phase 2 of fa_bwd: dQ (plus lse and D per query row in ``workspace``).
+    ``d_ready``: the preprocess was given o_res (D is in the workspace)."""
     torch = _torch()
     B, H, N, d, ws = _bwd_common(k, [(q, "q"), (v, "v"), (do, "do"), (dq, "dq")], lse,
                                  workspace)
@@ -264,7 +285,7 @@ def fa_bwd_dq(q, k, v, do, lse, workspace, dq, causal=False, scale=None):
         st = _lib.load().fa_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(),
                                    lse.data_ptr(), workspace.data_ptr(), ws, dq.data_ptr(),
                                    B, H, N, d, int(bool(causal)), _scale(scale, d),
-                                   _stream_ptr(k.device))
+                                   int(bool(d_ready)), _stream_ptr(k.device))
     if st != _lib.FA_OK:
         raise FAError(st, "fa_bwd_dq")
 
@@ -356,11 +377,11 @@ def fa_decode_noalloc(q, k, v, causal: bool = False, scale: Optional[float] = No
 
 
 def fa_fwd_rect(q, k, v, causal: bool = False, scale: Optional[float] = None, out=None,
-                lse=None):
+                lse=None, o_res=None):
     """bf16 forward with Nq query rows against Nk keys: q [B,H,Nq,d], k and v
     [B,Hkv,Nk,d] (Hkv dividing H). Query row i sits at position Nk - Nq + i
-    (bottom-right causal alignment). Returns (O [B,H,Nq,d], lse [B,H,Nq]).
-    Calls fa_fwd_rect of libfa.so."""
+    (bottom-right causal alignment). Returns (O [B,H,Nq,d], lse [B,H,Nq]);
+    ``o_res`` as for fa_fwd. Calls fa_fwd_rect of libfa.so."""
     torch = _torch()
     bf = torch.bfloat16
     _check(q, "q", bf)
@@ -378,8 +399,8 @@ def fa_fwd_rect(q, k, v, causal: bool = False, scale: Optional[float] = None, ou
     _check(lse, "lse", torch.float32, (B, H, Nq), q.device)
     with torch.cuda.device(q.device):
         st = _lib.load().fa_fwd_rect(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                                     lse.data_ptr(), B, H, Hkv, Nq, Nk, d, int(bool(causal)),
-                                     _scale(scale, d), _stream_ptr(q.device))
+                                     _o_res_ptr(o_res, q), lse.data_ptr(), B, H, Hkv, Nq, Nk, d,
+                                     int(bool(causal)), _scale(scale, d), _stream_ptr(q.device))
     if st != _lib.FA_OK:
         raise FAError(st, "fa_fwd_rect")
     return out, lse
@@ -450,16 +471,17 @@ def _autograd_fn():
         class _Attention(torch.autograd.Function):
             @staticmethod
             def forward(ctx, q, k, v, causal, scale):
-                o, lse = fa_fwd_rect(q, k, v, causal=causal, scale=scale)
-                ctx.save_for_backward(q, k, v, o, lse)
+                o_res = torch.empty_like(q)
+                o, lse = fa_fwd_rect(q, k, v, causal=causal, scale=scale, o_res=o_res)
+                ctx.save_for_backward(q, k, v, o, o_res, lse)
                 ctx.causal, ctx.scale = causal, scale
                 return o
 
             @staticmethod
             def backward(ctx, do):
-                q, k, v, o, lse = ctx.saved_tensors
+                q, k, v, o, o_res, lse = ctx.saved_tensors
                 dq, dk, dv = fa_bwd_rect(q, k, v, o, do.contiguous(), lse, causal=ctx.causal,
-                                         scale=ctx.scale)
+                                         scale=ctx.scale, o_res=o_res)
                 return dq, dk, dv, None, None
 
         _AUTOGRAD_FN = _Attention
@@ -469,7 +491,8 @@ def _autograd_fn():
 def fa_attention(q, k, v, causal: bool = False, scale: Optional[float] = None):
     """Attention with autograd: O = softmax(scale Q K^T) V for bf16 q [B,H,Nq,d]
     and k, v [B,Hkv,Nk,d] on a GPU (Hkv dividing H; query row i at position
-    Nk - Nq + i, bottom-right causal). The forward is fa_fwd_rect; the
-    gradient of a loss with respect to q, k and v is fa_bwd_rect, fed the
-    saved O and logsumexp. Both run in libfa.so."""
+    Nk - Nq + i, bottom-right causal). The forward is fa_fwd_rect (keeping O's
+    rounding residual); the gradient of a loss with respect to q, k and v is
+    fa_bwd_rect, fed the saved O, its residual and the logsumexp. Both run in
+    libfa.so."""
     return _autograd_fn().apply(q, k, v, bool(causal), _scale(scale, q.shape[-1]))

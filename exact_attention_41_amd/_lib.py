@@ -39,36 +39,37 @@ def load() -> ctypes.CDLL:
         vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
         lib.fa_status_str.argtypes = [i]
         lib.fa_status_str.restype = ctypes.c_char_p
-        lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+        lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
         lib.fa_fwd.restype = i
         lib.fa_fwd_f32.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
         lib.fa_fwd_f32.restype = i
         lib.fa_bwd_workspace_size.argtypes = [i, i, i, i]
         lib.fa_bwd_workspace_size.restype = ctypes.c_size_t
-        lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+        lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                i, i, i, i, i, f, vp]
         lib.fa_bwd.restype = i
-        lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i, i, i, i, vp]
+        lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                          i, i, i, i, vp]
         lib.fa_bwd_preprocess.restype = i
         lib.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, ctypes.c_size_t, vp, vp,
                                     i, i, i, i, i, f, vp]
         lib.fa_bwd_dkdv.restype = i
         lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp,
-                                  i, i, i, i, i, f, vp]
+                                  i, i, i, i, i, f, i, vp]
         lib.fa_bwd_dq.restype = i
-        lib.fa_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+        lib.fa_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
         lib.fa_fwd_gqa.restype = i
         lib.fa_bwd_gqa_workspace_size.argtypes = [i, i, i, i, i]
         lib.fa_bwd_gqa_workspace_size.restype = ctypes.c_size_t
-        lib.fa_bwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+        lib.fa_bwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                    i, i, i, i, i, i, f, vp]
         lib.fa_bwd_gqa.restype = i
         lib.fa_bwd_rect_workspace_size.argtypes = [i, i, i, i, i, i]
         lib.fa_bwd_rect_workspace_size.restype = ctypes.c_size_t
-        lib.fa_bwd_rect.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
-                                    i, i, i, i, i, i, i, f, vp]
+        lib.fa_bwd_rect.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                    ctypes.c_size_t, i, i, i, i, i, i, i, f, vp]
         lib.fa_bwd_rect.restype = i
-        lib.fa_fwd_rect.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
+        lib.fa_fwd_rect.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
         lib.fa_fwd_rect.restype = i
         lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, f, f, f, vp]
         lib.fa_fwd_fp8.restype = i

@@ -92,17 +92,19 @@ const char* fa_status_str(fa_status_t status) {
     return "FA_ERR_UNKNOWN";
 }
 
-fa_status_t fa_fwd_rect(const void* q, const void* k, const void* v, void* o, float* lse,
-                        int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
-                        hipStream_t stream) {
+fa_status_t fa_fwd_rect(const void* q, const void* k, const void* v, void* o, void* o_res,
+                        float* lse, int B, int H, int Hkv, int Nq, int Nk, int d, int causal,
+                        float scale, hipStream_t stream) {
     bool empty = false;
     if (Nk < 0) return FA_ERR_INVALID_ARG;
     FA_TRY(check_fwd(q, k, v, o, lse, B, H, Nq, d, scale, true, &empty));
     FA_TRY(check_heads(H, Hkv));
     if (empty) return FA_OK;
+    if (o_res) FA_TRY(check_tensor(o_res));
     if (Nk == 0) return FA_ERR_INVALID_ARG;      // query rows but no keys
     if (Nk > kMaxN) return FA_ERR_UNSUPPORTED;
     fa::FwdArgs a{q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, causal != 0, scale, stream};
+    a.o_res = o_res;
     return fa::launch_fwd_bf16(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -124,15 +126,16 @@ fa_status_t fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, flo
     return fa::launch_fwd_fp8(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-fa_status_t fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
-                       int B, int H, int Hkv, int N, int d, int causal, float scale,
+fa_status_t fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, void* o_res,
+                       float* lse, int B, int H, int Hkv, int N, int d, int causal, float scale,
                        hipStream_t stream) {
-    return fa_fwd_rect(q, k, v, o, lse, B, H, Hkv, N, N, d, causal, scale, stream);
+    return fa_fwd_rect(q, k, v, o, o_res, lse, B, H, Hkv, N, N, d, causal, scale, stream);
 }
 
-fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                   int B, int H, int N, int d, int causal, float scale, hipStream_t stream) {
-    return fa_fwd_gqa(q, k, v, o, lse, B, H, H, N, d, causal, scale, stream);
+fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, void* o_res,
+                   float* lse, int B, int H, int N, int d, int causal, float scale,
+                   hipStream_t stream) {
+    return fa_fwd_gqa(q, k, v, o, o_res, lse, B, H, H, N, d, causal, scale, stream);
 }
 
 fa_status_t fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
@@ -189,11 +192,13 @@ fa_status_t check_bwd(std::initializer_list<const void*> tensors, bool need_lse,
 }
 
 fa::BwdArgs bwd_args(const void* q, const void* k, const void* v, const void* o,
-                     const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                     void* workspace, int B, int H, int Hkv, int Nq, int Nk, int d, int causal,
-                     float scale, hipStream_t stream) {
-    return fa::BwdArgs{q, k, v, o, dout, lse, dq, dk, dv, workspace,
-                       B, H, Hkv, Nq, Nk, d, causal != 0, scale, stream};
+                     const void* o_res, const void* dout, const float* lse, void* dq, void* dk,
+                     void* dv, void* workspace, int B, int H, int Hkv, int Nq, int Nk, int d,
+                     int causal, float scale, hipStream_t stream) {
+    fa::BwdArgs a{q, k, v, o, o_res, dout, lse, dq, dk, dv, workspace,
+                  B, H, Hkv, Nq, Nk, d, causal != 0, scale, stream};
+    a.d_known = o_res != nullptr;
+    return a;
 }
 
 }  // namespace
@@ -201,26 +206,30 @@ fa::BwdArgs bwd_args(const void* q, const void* k, const void* v, const void* o,
 extern "C" {
 
 fa_status_t fa_bwd_preprocess(const void* q, const void* k, const void* v, const void* o,
-                              const void* dout, void* workspace, size_t workspace_bytes, int B,
-                              int H, int N, int d, hipStream_t stream) {
+                              const void* o_res, const void* dout, void* workspace,
+                              size_t workspace_bytes, int B, int H, int N, int d,
+                              hipStream_t stream) {
     bool empty = false;
     FA_TRY(check_bwd({q, k, v, o, dout}, false, nullptr, workspace, workspace_bytes, B, H, H, N,
                      N, d, 1.f, &empty));
     if (empty) return FA_OK;
-    const fa::BwdArgs a = bwd_args(q, k, v, o, dout, nullptr, nullptr, nullptr, nullptr,
+    if (o_res) FA_TRY(check_tensor(o_res));
+    const fa::BwdArgs a = bwd_args(q, k, v, o, o_res, dout, nullptr, nullptr, nullptr, nullptr,
                                    workspace, B, H, H, N, N, d, 0, 1.f, stream);
     return fa::launch_bwd_prepare(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 fa_status_t fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
                       const float* lse, void* workspace, size_t workspace_bytes, void* dq,
-                      int B, int H, int N, int d, int causal, float scale, hipStream_t stream) {
+                      int B, int H, int N, int d, int causal, float scale, int d_ready,
+                      hipStream_t stream) {
     bool empty = false;
     FA_TRY(check_bwd({q, k, v, dout, dq}, true, lse, workspace, workspace_bytes, B, H, H, N, N,
                      d, scale, &empty));
     if (empty) return FA_OK;
-    const fa::BwdArgs a = bwd_args(q, k, v, nullptr, dout, lse, dq, nullptr, nullptr, workspace,
-                                   B, H, H, N, N, d, causal, scale, stream);
+    fa::BwdArgs a = bwd_args(q, k, v, nullptr, nullptr, dout, lse, dq, nullptr, nullptr,
+                             workspace, B, H, H, N, N, d, causal, scale, stream);
+    a.d_known = d_ready != 0;
     return fa::launch_bwd_dq(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -231,22 +240,24 @@ fa_status_t fa_bwd_dkdv(const void* q, const void* k, const void* v, const void*
     FA_TRY(check_bwd({q, k, v, dout, dk, dv}, false, nullptr, workspace, workspace_bytes, B, H,
                      H, N, N, d, scale, &empty));
     if (empty) return FA_OK;
-    const fa::BwdArgs a = bwd_args(q, k, v, nullptr, dout, nullptr, nullptr, dk, dv,
+    const fa::BwdArgs a = bwd_args(q, k, v, nullptr, nullptr, dout, nullptr, nullptr, dk, dv,
                                    const_cast<void*>(workspace), B, H, H, N, N, d, causal, scale,
                                    stream);
     return fa::launch_bwd_dkdv(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 fa_status_t fa_bwd_rect(const void* q, const void* k, const void* v, const void* o,
-                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                        void* workspace, size_t workspace_bytes, int B, int H, int Hkv, int Nq,
-                        int Nk, int d, int causal, float scale, hipStream_t stream) {
+                        const void* o_res, const void* dout, const float* lse, void* dq,
+                        void* dk, void* dv, void* workspace, size_t workspace_bytes, int B,
+                        int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                        hipStream_t stream) {
     bool empty = false;
     FA_TRY(check_bwd({q, k, v, o, dout, dq, dk, dv}, true, lse, workspace, workspace_bytes, B, H,
                      Hkv, Nq, Nk, d, scale, &empty));
     if (empty) return FA_OK;
-    const fa::BwdArgs a = bwd_args(q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H, Hkv, Nq,
-                                   Nk, d, causal, scale, stream);
+    if (o_res) FA_TRY(check_tensor(o_res));
+    const fa::BwdArgs a = bwd_args(q, k, v, o, o_res, dout, lse, dq, dk, dv, workspace, B, H,
+                                   Hkv, Nq, Nk, d, causal, scale, stream);
     if (fa::launch_bwd_prepare(a) != hipSuccess) return FA_ERR_HIP;
     if (fa::launch_bwd_dq(a) != hipSuccess) return FA_ERR_HIP;
     if (fa::launch_bwd_dkdv(a) != hipSuccess) return FA_ERR_HIP;
@@ -254,19 +265,19 @@ fa_status_t fa_bwd_rect(const void* q, const void* k, const void* v, const void*
 }
 
 fa_status_t fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o,
-                       const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                       void* workspace, size_t workspace_bytes, int B, int H, int Hkv, int N,
-                       int d, int causal, float scale, hipStream_t stream) {
-    return fa_bwd_rect(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, Hkv,
-                       N, N, d, causal, scale, stream);
+                       const void* o_res, const void* dout, const float* lse, void* dq, void* dk,
+                       void* dv, void* workspace, size_t workspace_bytes, int B, int H, int Hkv,
+                       int N, int d, int causal, float scale, hipStream_t stream) {
+    return fa_bwd_rect(q, k, v, o, o_res, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H,
+                       Hkv, N, N, d, causal, scale, stream);
 }
 
 fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o,
-                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                   void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                   const void* o_res, const void* dout, const float* lse, void* dq, void* dk,
+                   void* dv, void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
                    int causal, float scale, hipStream_t stream) {
-    return fa_bwd_gqa(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, H, N,
-                      d, causal, scale, stream);
+    return fa_bwd_gqa(q, k, v, o, o_res, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H,
+                      H, N, d, causal, scale, stream);
 }
 
 size_t fa_decode_workspace_size(int B, int H, int Hkv, int Nq, int Nk, int d) {

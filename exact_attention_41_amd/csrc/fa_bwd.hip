@@ -106,13 +106,15 @@ BwdWorkspace bwd_workspace_layout(long long B, long long H, long long Hkv, long 
 // (bits & 0x7fff) is the order of |x|): Q and dO (Nq rows) for the BH query
 // heads (rows r < BH of the grid), K and V (Nk rows) for the BHkv K/V heads
 // (rows r >= BH). Chunks past a tensor's rows record 0. For the query heads
-// it also forms D^_i = dO_i . O_i (fp32) of every row of the chunk.
+// it also forms D_i = dO_i . O_i (fp32) of every row of the chunk, with O the
+// bf16 output, or that plus its bf16 rounding residual when ORes is given.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ void __launch_bounds__(256)
 bwd_absmax_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                   const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-                  const uint16_t* __restrict__ O, uint32_t* __restrict__ partial,
+                  const uint16_t* __restrict__ O, const uint16_t* __restrict__ ORes,
+                  uint32_t* __restrict__ partial,
                   float* __restrict__ dhat, int BH, int Nq, int Nk, int chunks) {
     constexpr int DCH = D / 8;
     const int bid = blockIdx.x;
@@ -137,10 +139,20 @@ bwd_absmax_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
             if (t == 1 && !kv) {
                 const u32x4_t ow = *(const u32x4_t*)(O + base + (size_t)idx * 8);
                 float s = 0.f;
+                if (ORes != nullptr) {
+                    // bf16(O) + its residual: exact in fp32
+                    const u32x4_t rw = *(const u32x4_t*)(ORes + base + (size_t)idx * 8);
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    s = __builtin_fmaf(bf16_lo(w[c]), bf16_lo(ow[c]), s);
-                    s = __builtin_fmaf(bf16_hi(w[c]), bf16_hi(ow[c]), s);
+                    for (int c = 0; c < 4; ++c) {
+                        s = __builtin_fmaf(bf16_lo(w[c]), bf16_lo(ow[c]) + bf16_lo(rw[c]), s);
+                        s = __builtin_fmaf(bf16_hi(w[c]), bf16_hi(ow[c]) + bf16_hi(rw[c]), s);
+                    }
+                } else {
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        s = __builtin_fmaf(bf16_lo(w[c]), bf16_lo(ow[c]), s);
+                        s = __builtin_fmaf(bf16_hi(w[c]), bf16_hi(ow[c]), s);
+                    }
                 }
 #pragma unroll
                 for (int off = DCH / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
@@ -316,12 +328,15 @@ bwd_image_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 // with sE = s_dO * s_V and the dP~ chain started from -sE D^ (so that the
 // accumulator holds dP~ - sE D^); finally dQ = scale/(sK sE) (A~ - D~ B~),
 // D~ = sE (D - D^) = sum_j P*dP~.
+// With DK (the preprocess formed D itself, from O and its rounding residual)
+// the chain starts from -sE D, there is no B~ sum and no D~, and
+// dQ = scale/(sK sE) A~: three products per score instead of four.
 // A head size DT above 128 runs as NC = DT/128 column parts: each key tile
 // is staged as NC steps of 128 columns of K and V, S and dP accumulate over
 // all of them, and each workgroup forms the dQ columns of one part (the
 // grid holds NC workgroups per query block; the first writes lse and D).
 // ---------------------------------------------------------------------------
-template <int DT, int NW, bool CAUSAL>
+template <int DT, int NW, bool CAUSAL, bool DK>
 __global__ void __launch_bounds__(NW * 64, 1)
 bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
@@ -392,8 +407,8 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     // probability of theirs is then exactly 0.
     const float lse_i = (qi < N) ? LSE[(size_t)bh * N + qi] : kNegInf;
     const float lse2 = (lse_i == kNegInf) ? __builtin_huge_valf() : lse_i * kLog2e;
-    // The centre sE D^ of this row's dP~ (0 past N), as the start value of
-    // every dP~ chain.
+    // The centre sE D^ (or sE D) of this row's dP~ (0 past N), as the start
+    // value of every dP~ chain.
     const float dhs = (qi < N) ? sE * dhat[(size_t)bh * N + qi] : 0.f;
     f32x16_t dinit;
 #pragma unroll
@@ -517,13 +532,14 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 float p = fast_exp2(__builtin_fmaf(sa[jb][r], c, -lse2));
                 if (MASK && (j >= Nk || (CAUSAL && j > qi + off))) p = 0.f;
                 const float e = p * da[jb][r];
-                dsum += e;
+                if constexpr (!DK) dsum += e;
                 pv[r] = p;
                 ev[r] = e;
                 if ((r & 7) == 7) {
                     const int h = r >> 3, rb = 8 * h;
-                    pf[2 * jb + h] = u32x4_t{pack_f16x2(pv[rb + 0], pv[rb + 1]), pack_f16x2(pv[rb + 2], pv[rb + 3]),
-                                             pack_f16x2(pv[rb + 4], pv[rb + 5]), pack_f16x2(pv[rb + 6], pv[rb + 7])};
+                    if constexpr (!DK)
+                        pf[2 * jb + h] = u32x4_t{pack_f16x2(pv[rb + 0], pv[rb + 1]), pack_f16x2(pv[rb + 2], pv[rb + 3]),
+                                                 pack_f16x2(pv[rb + 4], pv[rb + 5]), pack_f16x2(pv[rb + 6], pv[rb + 7])};
                     ef[2 * jb + h] = u32x4_t{pack_f16x2(ev[rb + 0], ev[rb + 1]), pack_f16x2(ev[rb + 2], ev[rb + 3]),
                                              pack_f16x2(ev[rb + 4], ev[rb + 5]), pack_f16x2(ev[rb + 6], ev[rb + 7])};
                 }
@@ -561,7 +577,7 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 } else {
                     const int w = o - 2 * NSD, t4 = w / NB, nb = w % NB;
                     mfma_f16_agpr(acc_a[nb], a, ef[t4]);
-                    mfma_f16_agpr(acc_b[nb], a, pf[t4]);
+                    if constexpr (!DK) mfma_f16_agpr(acc_b[nb], a, pf[t4]);
                     if (t4 < 2) {
 #pragma unroll
                         for (int e = 0; e < EPO_B; ++e) softmax_elem(1, w * EPO_B + e);
@@ -592,9 +608,9 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         agpr_settle(acc_a[nb]);
-        agpr_settle(acc_b[nb]);
+        if constexpr (!DK) agpr_settle(acc_b[nb]);
     }
-    const float dt = sum_with_partner32(dsum);    // D~ = sE * (D - D^)
+    const float dt = DK ? 0.f : sum_with_partner32(dsum);    // D~ = sE * (D - D^)
     if (part == 0 && g == 0 && qi < T * 64) {
         float* st = stats + ((size_t)bh * T + (qi >> 6)) * 128;
         st[qi & 63] = lse2;
@@ -611,7 +627,7 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
                 for (int r4 = 0; r4 < 4; ++r4) {
                     const int r = 4 * q4 + r4;
-                    x[r4] = f * __builtin_fmaf(-dt, acc_b[nb][r], acc_a[nb][r]);
+                    x[r4] = DK ? f * acc_a[nb][r] : f * __builtin_fmaf(-dt, acc_b[nb][r], acc_a[nb][r]);
                 }
                 u32x2_t w;
                 w[0] = pack_bf16x2(x[0], x[1]);
@@ -1394,7 +1410,8 @@ static hipError_t launch_prepare_t(const BwdArgs& a) {
     hipLaunchKernelGGL((bwd_absmax_kernel<D>), dim3((BH + BHkv) * chunks), dim3(256), 0,
                        a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                        (const uint16_t*)a.v, (const uint16_t*)a.dout, (const uint16_t*)a.o,
-                       partial, ws_ptr<float>(a, w.dhat), BH, a.N, a.Nk, chunks);
+                       (const uint16_t*)a.o_res, partial, ws_ptr<float>(a, w.dhat), BH, a.N,
+                       a.Nk, chunks);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_scale_kernel, dim3((BH + 63) / 64), dim3(64), 0, a.stream,
@@ -1416,9 +1433,9 @@ static hipError_t launch_dq_t(const BwdArgs& a) {
     const BwdWorkspace w = ws_of(a);
     const int BH = a.B * a.H;
     const int nqb = (a.N + NW * 32 - 1) / (NW * 32);
-    hipLaunchKernelGGL((bwd_dq_kernel<D, NW, CAUSAL>), dim3(nqb * BH * col_parts(D)),
-                       dim3(NW * 64), 0,
-                       a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+    auto kernel = a.d_known ? bwd_dq_kernel<D, NW, CAUSAL, true>
+                            : bwd_dq_kernel<D, NW, CAUSAL, false>;
+    hipLaunchKernelGGL(kernel, dim3(nqb * BH * col_parts(D)), dim3(NW * 64), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                        (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse,
                        ws_ptr<const float>(a, w.scales), ws_ptr<const float>(a, w.dhat),
                        ws_ptr<const char>(a, w.kt),

@@ -171,6 +171,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// The rounding residuals of a pair packed as w = pack_bf16x2(lo, hi), again as
+// a bf16 pair: x - bf16(x) is exact in fp32, and bf16(x) + bf16(x - bf16(x))
+// keeps about 16 significant bits of x.
+__device__ __forceinline__ uint32_t pack_bf16x2_residual(float lo, float hi, uint32_t w) {
+    return pack_bf16x2(lo - bf16_lo(w), hi - bf16_hi(w));
+}
+
 // Value of x held by the lane 32 positions away (l ^ 32), via v_permlane32_swap.
 __device__ __forceinline__ float partner32(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

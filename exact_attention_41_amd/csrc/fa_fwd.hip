@@ -77,7 +77,8 @@ template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(kFwdWaves * 64, 1)
 fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
-                float* __restrict__ LSE, int BH, int G, int N, int Nk, float c, int nqb) {
+                uint16_t* __restrict__ ORes, float* __restrict__ LSE, int BH, int G, int N,
+                int Nk, float c, int nqb) {
     constexpr int BC = 64;                 // keys per tile
     constexpr int BR = kFwdWaves * 32;     // query rows per workgroup
     constexpr int KS = D / 16;             // MFMA k-steps over d
@@ -335,7 +336,8 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
     if (grp == 0) wg_barrier();            // same number of barriers in both groups
 
-    // ---- epilogue: deferred normalisation, logsumexp, bf16 store ------------
+    // ---- epilogue: deferred normalisation, logsumexp, bf16 store (and, when
+    // ORes is given, the bf16 rounding residual of each stored value) --------
     const float l = sum_with_partner32(l_run);
     const float lr = sum_with_partner32(l_rnd);
     if (qi < N) {
@@ -348,10 +350,20 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
+                float x[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[e] = acc_o[nb][4 * q4 + e] * inv;
                 u32x2_t w;
-                w[0] = pack_bf16x2(acc_o[nb][4 * q4 + 0] * inv, acc_o[nb][4 * q4 + 1] * inv);
-                w[1] = pack_bf16x2(acc_o[nb][4 * q4 + 2] * inv, acc_o[nb][4 * q4 + 3] * inv);
-                *(u32x2_t*)(orow + 32 * nb + 8 * q4 + 4 * g) = w;
+                w[0] = pack_bf16x2(x[0], x[1]);
+                w[1] = pack_bf16x2(x[2], x[3]);
+                const size_t col = 32 * nb + 8 * q4 + 4 * g;
+                *(u32x2_t*)(orow + col) = w;
+                if (ORes != nullptr) {
+                    u32x2_t r;
+                    r[0] = pack_bf16x2_residual(x[0], x[1], w[0]);
+                    r[1] = pack_bf16x2_residual(x[2], x[3], w[1]);
+                    *(u32x2_t*)(ORes + head + (size_t)qi * D + col) = r;
+                }
             }
     }
 }
@@ -467,7 +479,8 @@ static hipError_t launch_fwd_bf16_t(const FwdArgs& a) {
     const float c = a.scale * kLog2e;
     hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3(nqb * BH), dim3(kFwdWaves * 64), 0,
                        a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                       (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, BH, a.H / a.Hkv, a.N, a.Nk,
+                       (const uint16_t*)a.v, (uint16_t*)a.o, (uint16_t*)a.o_res, a.lse, BH, a.H / a.Hkv,
+                       a.N, a.Nk,
                        c, nqb);
     return hipGetLastError();
 }

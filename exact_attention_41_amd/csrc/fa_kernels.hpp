@@ -23,6 +23,8 @@ struct FwdArgs {
     hipStream_t stream;
     // fp8 forward only: the real values are descale_x times the stored ones.
     float descale_q = 1.f, descale_k = 1.f, descale_v = 1.f;
+    // bf16 forwards only: where to store O - bf16(O) as bf16 (nullptr: not stored).
+    void* o_res = nullptr;
 };
 
 struct BwdArgs {
@@ -30,6 +32,7 @@ struct BwdArgs {
     const void* k;
     const void* v;
     const void* o;      // the forward's output (read by the preprocess only)
+    const void* o_res;  // its rounding residual O - bf16(O), or nullptr (preprocess only)
     const void* dout;
     const float* lse;
     void* dq;
@@ -40,6 +43,9 @@ struct BwdArgs {
     bool causal;
     float scale;
     hipStream_t stream;
+    // The preprocess formed D_i = dO_i . O_i from O and its residual (the dQ
+    // pass then takes D from the workspace instead of forming it).
+    bool d_known = false;
 };
 
 // Rows per chunk of the max-abs pre-pass of the backward.
@@ -55,9 +61,10 @@ constexpr int kScaleRows = 256;
 //   partial u32  [BH + BHkv][chunks][2] per-chunk largest |x| (bf16 magnitude
 //                                    bits): (Q, dO) per query head, then (K, V)
 //                                    per K/V head
-//   dhat    fp32 [BH][Nq]            D^_i = dO_i . O_i from the bf16 O: the
+//   dhat    fp32 [BH][Nq]            D_i = dO_i . O_i: from the bf16 O alone, the
 //                                    centre the dQ pass subtracts from dP before
-//                                    rounding (D itself is formed exactly there)
+//                                    rounding (D itself is formed exactly there);
+//                                    from O plus its residual, D itself
 //   stats   fp32 [BH][Tq][128]       per query tile: lse*log2(e) of its 64 rows,
 //                                    then sE*D (sE = s_dO*s_V); from the dQ pass
 //   qt      fp16 [BH][Tq][64*d]      images of (s_Q Q)^T, one per 64-row tile

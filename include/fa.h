@@ -76,6 +76,12 @@ const char* fa_status_str(fa_status_t status);
  *   q, k, v  (in)  bf16 [B][H][N][d].
  *   o        (out) bf16 [B][H][N][d]: O = P V with P = softmax(scale Q K^T)
  *                  (masked when causal), rounded to nearest even once.
+ *   o_res    (out, optional) bf16 [B][H][N][d] or NULL: the rounding
+ *                  residual of o, o_res = bf16(O - o) with O the fp32 value
+ *                  that o rounds. o + o_res carries O to about 16 significant
+ *                  bits; the backward uses it to form D_i = dO_i . O_i
+ *                  without the error of o's rounding (see fa_bwd). Like lse it
+ *                  is an O(N) side output of the forward for training.
  *   lse      (out) fp32 [B][H][N]: natural-log logsumexp of the scaled,
  *                  masked logits of each query row, ln sum_j exp(scale q_i.k_j);
  *                  the backward consumes it.
@@ -87,23 +93,23 @@ const char* fa_status_str(fa_status_t status);
  * operand and give non-finite output); at d = 256 P V takes bf16 operands
  * and any finite v is allowed.
  */
-fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                   int B, int H, int N, int d, int causal, float scale,
+fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, void* o_res,
+                   float* lse, int B, int H, int N, int d, int causal, float scale,
                    hipStream_t stream);
 
 /*
  * Forward with shared K/V heads (multi-query and grouped-query attention; the
  * "FlashAttention" page, systems-analysis.ru, section "FlashAttention-2
  * (2023)", names multi-query attention among the extensions).
- *   q, o     bf16 [B][H][N][d], lse fp32 [B][H][N], as for fa_fwd.
+ *   q, o     bf16 [B][H][N][d], o_res (optional) and lse as for fa_fwd.
  *   k, v     bf16 [B][Hkv][N][d]: Hkv K/V heads, Hkv >= 1 dividing H.
  * Query head h attends with K/V head h / (H / Hkv): consecutive groups of
  * H / Hkv query heads share one K/V head (Hkv == 1 is multi-query attention,
  * Hkv == H is fa_fwd). Hkv < 1 or not dividing H -> FA_ERR_INVALID_ARG.
  * Everything else as for fa_fwd.
  */
-fa_status_t fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
-                       int B, int H, int Hkv, int N, int d, int causal, float scale,
+fa_status_t fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, void* o_res,
+                       float* lse, int B, int H, int Hkv, int N, int d, int causal, float scale,
                        hipStream_t stream);
 
 /*
@@ -112,21 +118,21 @@ fa_status_t fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, flo
  * reverse). Query row i sits at sequence position Nk - Nq + i, so with
  * causal set it keeps the keys j <= Nk - Nq + i (bottom-right alignment; if
  * Nq > Nk the first Nq - Nk rows keep no key and get O = 0, lse = -inf).
- *   q, o     bf16 [B][H][Nq][d], lse fp32 [B][H][Nq].
+ *   q, o     bf16 [B][H][Nq][d], o_res (optional) likewise, lse fp32 [B][H][Nq].
  *   k, v     bf16 [B][Hkv][Nk][d], K/V heads shared as in fa_fwd_gqa.
  * Nq == Nk is fa_fwd_gqa. Nk < 0, or Nk == 0 with query rows to compute ->
  * FA_ERR_INVALID_ARG; Nk beyond 2^26 -> FA_ERR_UNSUPPORTED. Everything else
  * as for fa_fwd.
  */
-fa_status_t fa_fwd_rect(const void* q, const void* k, const void* v, void* o, float* lse,
-                        int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
-                        hipStream_t stream);
+fa_status_t fa_fwd_rect(const void* q, const void* k, const void* v, void* o, void* o_res,
+                        float* lse, int B, int H, int Hkv, int Nq, int Nk, int d, int causal,
+                        float scale, hipStream_t stream);
 
 /*
  * Forward with 8-bit floating-point operands (the FP8 arithmetic that the
- * "FlashAttention" page, section "FlashAttention-2 (2023)", and the
  * "FlashAttention-2" page, section "Comparison with later versions /
- * FlashAttention-3", attribute to FlashAttention-3).
+ * FlashAttention-3", and the "FlashAttention" page, section
+ * "FlashAttention-3 (2024)", attribute to FlashAttention-3).
  *   q        (in)  e4m3 (OCP FP8: 1 sign, 4 exponent bits with bias 7, 3
  *                  mantissa bits, no infinities) [B][H][Nq][d], one byte each;
  *                  real value = descale_q * stored value.
@@ -171,11 +177,16 @@ size_t fa_bwd_gqa_workspace_size(int B, int H, int Hkv, int N, int d);
  * Backward, bfloat16 storage: the gradients of the scalar
  * L = sum_{b,h,i,c} O_bhic dO_bhic with respect to q, k and v.
  *   q, k, v   (in)  bf16 [B][H][N][d], the forward inputs.
- *   o         (in)  bf16 [B][H][N][d], the forward output. Only the centre
- *                   D^_i = dO_i . O_i is taken from it: D_i = sum_j P_ij dP_ij
- *                   itself is formed exactly from P and dP = dO V^T (the
- *                   rounded bf16 O would move it too far), and dP - D^ is
- *                   what gets rounded for the dQ products.
+ *   o         (in)  bf16 [B][H][N][d], the forward output.
+ *   o_res     (in, optional) bf16 [B][H][N][d], the forward's o_res, or NULL.
+ *             D_i = sum_j P_ij dP_ij = dO_i . O_i is needed for every dS.
+ *             With o_res, D_i = dO_i . (o_i + o_res_i) is formed in the
+ *             preprocess and the dQ pass runs three products per score. With
+ *             NULL the bf16 o alone would move D too far (its rounding error
+ *             times |dO| reaches the 1e-2 scale of the gradients), so only a
+ *             centre D^_i = dO_i . o_i is taken from it and the dQ pass forms
+ *             D exactly from P and dP = dO V^T (a fourth product per score:
+ *             the correction -(D - D^) sum_j P_ij k_j).
  *   dout      (in)  bf16 [B][H][N][d], dL/dO.
  *   lse       (in)  fp32 [B][H][N], the forward's logsumexp.
  *   dq,dk,dv  (out) bf16 [B][H][N][d].
@@ -184,15 +195,16 @@ size_t fa_bwd_gqa_workspace_size(int B, int H, int Hkv, int N, int d);
  *             contents on entry do not matter and are overwritten.
  * P = exp(scale Q K^T - lse) is recomputed, never stored. The products that
  * form dQ, dK and dV take fp16 operands: P, dS = P * (dP - D) for dK, and
- * P * (dP - D^) for dQ (with the exact correction -(D - D^) sum_j P_ij k_j),
- * against q, k, dout multiplied by per-head powers of two; fp32 accumulation.
+ * P * (dP - D) for dQ (P * (dP - D^) plus the correction when o_res is
+ * NULL), against q, k, dout multiplied by per-head powers of two; fp32
+ * accumulation.
  * The result is deterministic: no floating-point atomics are used, so
  * repeated calls give identical bits. causal and scale must match the
  * forward call. The inputs must be finite.
  */
 fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o,
-                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                   void* workspace, size_t workspace_bytes,
+                   const void* o_res, const void* dout, const float* lse, void* dq, void* dk,
+                   void* dv, void* workspace, size_t workspace_bytes,
                    int B, int H, int N, int d, int causal, float scale,
                    hipStream_t stream);
 
@@ -206,15 +218,16 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o,
  * fa_bwd; fa_bwd is this with Hkv == H.
  */
 fa_status_t fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o,
-                       const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                       void* workspace, size_t workspace_bytes,
+                       const void* o_res, const void* dout, const float* lse, void* dq,
+                       void* dk, void* dv, void* workspace, size_t workspace_bytes,
                        int B, int H, int Hkv, int N, int d, int causal, float scale,
                        hipStream_t stream);
 
 /*
  * Backward of fa_fwd_rect: Nq query rows against Nk keys per head, query row
  * i at sequence position Nk - Nq + i (causal: bottom-right alignment).
- *   q, o, dout, dq  bf16 [B][H][Nq][d]; lse fp32 [B][H][Nq], fa_fwd_rect's
+ *   q, o, dout, dq  bf16 [B][H][Nq][d], o_res (optional) likewise, as for
+ *                   fa_bwd; lse fp32 [B][H][Nq], fa_fwd_rect's
  *                   (rows that keep no key have lse = -inf and get dq = 0).
  *   k, v, dk, dv    bf16 [B][Hkv][Nk][d]; dk and dv of a K/V head sum over
  *                   its query heads as in fa_bwd_gqa.
@@ -230,8 +243,8 @@ fa_status_t fa_bwd_gqa(const void* q, const void* k, const void* v, const void* 
 size_t fa_bwd_rect_workspace_size(int B, int H, int Hkv, int Nq, int Nk, int d);
 
 fa_status_t fa_bwd_rect(const void* q, const void* k, const void* v, const void* o,
-                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                        void* workspace, size_t workspace_bytes,
+                        const void* o_res, const void* dout, const float* lse, void* dq,
+                        void* dk, void* dv, void* workspace, size_t workspace_bytes,
                         int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                         hipStream_t stream);
 
@@ -292,20 +305,27 @@ fa_status_t fa_decode_noalloc(const void* q, const void* k, const void* v, void*
  * Arguments mean what they mean for fa_bwd.
  *   fa_bwd_preprocess  per-head largest magnitudes of q, k, v, dout, the
  *                      power-of-two factors derived from them, dout_i . o_i
- *                      per query row, and the scaled fp16 transposed copies of
- *                      q, dout and k -> workspace.
- *   fa_bwd_dq          writes dq; leaves lse and D per query row in the
+ *                      per query row (o_i + o_res_i when o_res is given), and
+ *                      the scaled fp16 transposed copies of q, dout and k ->
  *                      workspace.
+ *   fa_bwd_dq          writes dq; leaves lse and D per query row in the
+ *                      workspace. d_ready must be nonzero exactly when the
+ *                      preprocess of this workspace was given o_res (it
+ *                      selects the pass that takes D from the workspace;
+ *                      nonzero without o_res gives gradients off by the
+ *                      rounding of o, zero with o_res costs a fourth product
+ *                      per score but is exact).
  *   fa_bwd_dkdv        writes dk and dv from q, k, v, dout and the workspace
  *                      (lse is taken from the workspace).
  */
 fa_status_t fa_bwd_preprocess(const void* q, const void* k, const void* v, const void* o,
-                              const void* dout, void* workspace, size_t workspace_bytes,
-                              int B, int H, int N, int d, hipStream_t stream);
+                              const void* o_res, const void* dout, void* workspace,
+                              size_t workspace_bytes, int B, int H, int N, int d,
+                              hipStream_t stream);
 
 fa_status_t fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
                       const float* lse, void* workspace, size_t workspace_bytes, void* dq,
-                      int B, int H, int N, int d, int causal, float scale,
+                      int B, int H, int N, int d, int causal, float scale, int d_ready,
                       hipStream_t stream);
 
 fa_status_t fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,

@@ -82,8 +82,11 @@ A = 0x100000          # 16-byte aligned
 MIS = 0x100008        # 8-byte aligned only
 
 
-def fwd(lib, entry, q=A, k=A, v=A, o=A, lse=A, B=1, H=1, N=64, d=64, causal=0, scale=0.125):
-    return getattr(lib, entry)(q, k, v, o, lse, B, H, N, d, causal, scale, None)
+def fwd(lib, entry, q=A, k=A, v=A, o=A, lse=A, B=1, H=1, N=64, d=64, causal=0, scale=0.125,
+        o_res=None):
+    # the bf16 forward takes the optional o_res after o
+    res = () if entry == "fa_fwd_f32" else (o_res,)
+    return getattr(lib, entry)(q, k, v, o, *res, lse, B, H, N, d, causal, scale, None)
 
 
 @pytest.mark.parametrize("entry", ["fa_fwd", "fa_fwd_f32"])
@@ -104,6 +107,8 @@ def test_forward_rejects_bad_arguments(lib, entry):
         assert fwd(lib, entry, d=256) == UNSUPPORTED     # d = 256: bf16 forward only
     assert fwd(lib, entry, q=MIS) == UNSUPPORTED
     assert fwd(lib, entry, o=MIS) == UNSUPPORTED
+    if entry == "fa_fwd":
+        assert fwd(lib, entry, o_res=MIS) == UNSUPPORTED
     assert fwd(lib, entry, lse=A + 2) == UNSUPPORTED
     assert fwd(lib, entry, N=(1 << 26) + 1) == UNSUPPORTED
     assert fwd(lib, entry, B=1 << 16, H=1 << 16, N=64) == UNSUPPORTED
@@ -118,12 +123,12 @@ def test_forward_empty_problem_is_a_no_op(lib, entry):
 
 
 def bwd(lib, ws=0x200000, ws_bytes=None, B=1, H=2, N=100, d=128, **ptrs):
-    p = dict(q=A, k=A, v=A, o=A, do=A, lse=A, dq=A, dk=A, dv=A)
+    p = dict(q=A, k=A, v=A, o=A, o_res=None, do=A, lse=A, dq=A, dk=A, dv=A)
     p.update(ptrs)
     if ws_bytes is None:
         ws_bytes = lib.fa_bwd_workspace_size(B, H, N, d)
-    return lib.fa_bwd(p["q"], p["k"], p["v"], p["o"], p["do"], p["lse"], p["dq"], p["dk"],
-                      p["dv"], ws, ws_bytes, B, H, N, d, 1, 0.088, None)
+    return lib.fa_bwd(p["q"], p["k"], p["v"], p["o"], p["o_res"], p["do"], p["lse"], p["dq"],
+                      p["dk"], p["dv"], ws, ws_bytes, B, H, N, d, 1, 0.088, None)
 
 
 def test_backward_rejects_bad_arguments(lib):
@@ -132,6 +137,7 @@ def test_backward_rejects_bad_arguments(lib):
     assert bwd(lib, H=-2) == INVALID
     assert bwd(lib, d=32) == UNSUPPORTED
     assert bwd(lib, dk=MIS) == UNSUPPORTED
+    assert bwd(lib, o_res=MIS) == UNSUPPORTED
     assert bwd(lib, ws=None) == WORKSPACE
     assert bwd(lib, ws=MIS) == WORKSPACE
     assert bwd(lib, ws=0x200000 + 128) == WORKSPACE
@@ -142,14 +148,14 @@ def test_backward_rejects_bad_arguments(lib):
 def test_grouped_heads_arguments(lib):
     """fa_fwd_gqa / fa_bwd_gqa: Hkv must be >= 1 and divide H."""
     def f(Hkv, H=4, **kw):
-        return lib.fa_fwd_gqa(A, A, A, A, A, 1, H, Hkv, 64, 64, 0, 0.125, None)
+        return lib.fa_fwd_gqa(A, A, A, A, None, A, 1, H, Hkv, 64, 64, 0, 0.125, None)
     assert f(0) == INVALID
     assert f(-1) == INVALID
     assert f(3) == INVALID
     assert f(8) == INVALID
-    assert lib.fa_fwd_gqa(None, A, A, A, A, 1, 4, 2, 64, 64, 0, 0.125, None) == INVALID
-    assert lib.fa_fwd_gqa(A, A, A, A, A, 1, 4, 2, 64, 96, 0, 0.125, None) == UNSUPPORTED
-    assert lib.fa_fwd_gqa(A, A, A, A, A, 0, 4, 2, 64, 64, 0, 0.125, None) == OK
+    assert lib.fa_fwd_gqa(None, A, A, A, None, A, 1, 4, 2, 64, 64, 0, 0.125, None) == INVALID
+    assert lib.fa_fwd_gqa(A, A, A, A, None, A, 1, 4, 2, 64, 96, 0, 0.125, None) == UNSUPPORTED
+    assert lib.fa_fwd_gqa(A, A, A, A, None, A, 0, 4, 2, 64, 64, 0, 0.125, None) == OK
     assert lib.fa_bwd_gqa_workspace_size(2, 32, 8, 4096, 128) > 0
     # d = 256: twice the images of d = 128 (one per 128-column part)
     assert lib.fa_bwd_gqa_workspace_size(2, 32, 8, 4096, 256) > \
@@ -164,8 +170,8 @@ def test_grouped_heads_arguments(lib):
     ws = lib.fa_bwd_gqa_workspace_size(1, 4, 2, 100, 128)
 
     def b(Hkv=2, ws_bytes=ws, **kw):
-        return lib.fa_bwd_gqa(A, A, A, A, A, A, A, A, A, 0x200000, ws_bytes, 1, 4, Hkv, 100, 128,
-                              1, 0.088, None)
+        return lib.fa_bwd_gqa(A, A, A, A, None, A, A, A, A, A, 0x200000, ws_bytes, 1, 4, Hkv,
+                              100, 128, 1, 0.088, None)
     assert b(Hkv=3) == INVALID
     assert b(Hkv=0) == INVALID
     assert b(ws_bytes=ws - 1) == WORKSPACE
@@ -217,7 +223,7 @@ def test_decode_noalloc_arguments(lib):
 
 def test_rect_forward_arguments(lib):
     def f(B=1, H=2, Hkv=1, Nq=100, Nk=300, d=128, q=A, scale=0.1):
-        return lib.fa_fwd_rect(q, A, A, A, A, B, H, Hkv, Nq, Nk, d, 1, scale, None)
+        return lib.fa_fwd_rect(q, A, A, A, None, A, B, H, Hkv, Nq, Nk, d, 1, scale, None)
     assert f(Nk=-1) == INVALID
     assert f(Nk=0) == INVALID
     assert f(Hkv=3) == INVALID
@@ -245,8 +251,8 @@ def test_rect_backward_arguments(lib):
     assert lib.fa_bwd_rect_workspace_size(1, 4, 2, 100, 300, 512) == 0
 
     def b(B=1, H=4, Hkv=2, Nq=100, Nk=300, d=128, ws_bytes=ws, wsp=0x200000, dk=A):
-        return lib.fa_bwd_rect(A, A, A, A, A, A, A, dk, A, wsp, ws_bytes, B, H, Hkv, Nq, Nk, d,
-                               1, 0.088, None)
+        return lib.fa_bwd_rect(A, A, A, A, None, A, A, A, dk, A, wsp, ws_bytes, B, H, Hkv, Nq,
+                               Nk, d, 1, 0.088, None)
     assert b(Nk=-1) == INVALID
     assert b(Nk=0) == INVALID                   # query rows but no keys
     assert b(Nq=0) == INVALID                   # keys whose gradients would be left unwritten
@@ -292,21 +298,22 @@ def test_binding_checks_caller_workspaces():
 def test_backward_phases_reject_bad_arguments(lib):
     ws = lib.fa_bwd_workspace_size(1, 2, 100, 128)
     W = 0x200000     # 256-byte aligned fake workspace
-    assert lib.fa_bwd_preprocess(None, A, A, A, A, W, ws, 1, 2, 100, 128, None) == INVALID
-    assert lib.fa_bwd_preprocess(A, A, A, None, A, W, ws, 1, 2, 100, 128, None) == INVALID
-    assert lib.fa_bwd_preprocess(A, A, A, A, A, W, ws - 4, 1, 2, 100, 128, None) == WORKSPACE
-    assert lib.fa_bwd_preprocess(A, A, A, A, A, W + 16, ws, 1, 2, 100, 128, None) == WORKSPACE
-    assert lib.fa_bwd_preprocess(A, MIS, A, A, A, W, ws, 1, 2, 100, 128, None) == UNSUPPORTED
-    assert lib.fa_bwd_preprocess(A, A, A, MIS, A, W, ws, 1, 2, 100, 128, None) == UNSUPPORTED
-    assert lib.fa_bwd_dq(A, A, A, A, None, W, ws, A, 1, 2, 100, 128, 1, 0.1, None) == INVALID
-    assert lib.fa_bwd_dq(A, A, A, A, A, W, ws, MIS, 1, 2, 100, 128, 1, 0.1, None) == UNSUPPORTED
-    assert lib.fa_bwd_dq(A, A, A, A, A, W, ws, A, 1, 2, 100, 96, 1, 0.1, None) == UNSUPPORTED
-    assert lib.fa_bwd_dq(A, A, A, A, A, W, ws, A, 0, 2, 100, 128, 1, 0.1, None) == OK
+    assert lib.fa_bwd_preprocess(None, A, A, A, None, A, W, ws, 1, 2, 100, 128, None) == INVALID
+    assert lib.fa_bwd_preprocess(A, A, A, None, None, A, W, ws, 1, 2, 100, 128, None) == INVALID
+    assert lib.fa_bwd_preprocess(A, A, A, A, None, A, W, ws - 4, 1, 2, 100, 128, None) == WORKSPACE
+    assert lib.fa_bwd_preprocess(A, A, A, A, None, A, W + 16, ws, 1, 2, 100, 128, None) == WORKSPACE
+    assert lib.fa_bwd_preprocess(A, MIS, A, A, None, A, W, ws, 1, 2, 100, 128, None) == UNSUPPORTED
+    assert lib.fa_bwd_preprocess(A, A, A, MIS, None, A, W, ws, 1, 2, 100, 128, None) == UNSUPPORTED
+    assert lib.fa_bwd_preprocess(A, A, A, A, MIS, A, W, ws, 1, 2, 100, 128, None) == UNSUPPORTED
+    assert lib.fa_bwd_dq(A, A, A, A, None, W, ws, A, 1, 2, 100, 128, 1, 0.1, 0, None) == INVALID
+    assert lib.fa_bwd_dq(A, A, A, A, A, W, ws, MIS, 1, 2, 100, 128, 1, 0.1, 0, None) == UNSUPPORTED
+    assert lib.fa_bwd_dq(A, A, A, A, A, W, ws, A, 1, 2, 100, 96, 1, 0.1, 0, None) == UNSUPPORTED
+    assert lib.fa_bwd_dq(A, A, A, A, A, W, ws, A, 0, 2, 100, 128, 1, 0.1, 0, None) == OK
     assert lib.fa_bwd_dkdv(A, A, A, A, W, ws, A, None, 1, 2, 100, 128, 1, 0.1, None) == INVALID
     assert lib.fa_bwd_dkdv(A, A, None, A, W, ws, A, A, 1, 2, 100, 128, 1, 0.1, None) == INVALID
     assert lib.fa_bwd_dkdv(A, A, A, A, None, ws, A, A, 1, 2, 100, 128, 1, 0.1, None) == WORKSPACE
     assert lib.fa_bwd_dkdv(A, A, A, A, W, ws, A, A, 1, 2, 100, 128, 1, -1.0, None) == INVALID
-    assert lib.fa_bwd_dq(A, A, A, A, A, W, ws, A, 1, 2, 100, 128, 1, 0.0, None) == INVALID
+    assert lib.fa_bwd_dq(A, A, A, A, A, W, ws, A, 1, 2, 100, 128, 1, 0.0, 0, None) == INVALID
 
 
 def test_fp8_forward_arguments(lib):

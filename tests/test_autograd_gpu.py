@@ -1,6 +1,7 @@
-"""fa_attention (torch autograd over fa_fwd_rect / fa_bwd_rect): the output
-and the gradients torch computes through it are the entry points' own bits,
-and they match the fp64 oracle."""
+"""fa_attention (torch autograd over fa_fwd_rect / fa_bwd_rect, with O's
+rounding residual passed from the one to the other): the output and the
+gradients torch computes through it are the entry points' own bits, and they
+match the fp64 oracle."""
 import numpy as np
 import pytest
 
@@ -23,8 +24,10 @@ def test_autograd_matches_entry_points_and_oracle(causal):
     qa, ka, va = (t.clone().requires_grad_(True) for t in (q, k, v))
     o = fa.fa_attention(qa, ka, va, causal=causal)
     (o.float() * do.float()).sum().backward()
-    o2, lse2 = fa.fa_fwd_rect(q, k, v, causal=causal)
-    g2 = fa.fa_bwd_rect(q, k, v, o2, do, lse2, causal=causal)
+    # fa_attention keeps O's rounding residual in the forward and hands it to the backward
+    o_res = torch.empty_like(q)
+    o2, lse2 = fa.fa_fwd_rect(q, k, v, causal=causal, o_res=o_res)
+    g2 = fa.fa_bwd_rect(q, k, v, o2, do, lse2, causal=causal, o_res=o_res)
     torch.cuda.synchronize()
     assert torch.equal(o.detach(), o2)
     for a, b in zip((qa.grad, ka.grad, va.grad), g2):

@@ -1,5 +1,8 @@
 """A numpy model of the dQ pass's rounding, against the fp64 oracle (CPU).
 
+Two ways of forming D_i = dO_i . O_i are modelled. Without the forward's
+rounding residual of O:
+
 The dQ pass forms, per query row i (sE, sK: the per-head powers of two that
 put the fp16 operands in range; K~ = sK k exactly; dP~ = sE dP in fp32):
     E_ij  = P_ij (dP~_ij - c_i)              rounded to fp16 as a product operand
@@ -14,6 +17,13 @@ with |dP - D|. Sharpened scores (q, k x3) and values with a large mean make
 |dP| much larger than |dP - D|; this model shows that the centred form stays
 within the bf16 tolerance there ("rounded" rule: these are stress inputs,
 not one of the specified workloads) and the uncentred one does not.
+
+With the residual (the forward stores bf16(O) and bf16(O - bf16(O))), the
+preprocess forms D = dO . (bf16(O) + residual) in fp32, the dQ pass uses it as
+the centre c = sE D with no correction term (A~ alone), and dK uses the same
+E. The model shows that this stays within the tolerance on the same stress
+inputs, while D from the bf16 O alone does not (the reason the residual is
+kept).
 """
 import numpy as np
 import pytest
@@ -88,3 +98,65 @@ def test_uncentred_dq_model_fails_with_large_value_mean(vmean):
     got = model_dq(q, k, v, do, True, scale, centred=False)
     ratio = np.max(np.abs(got - ref) / bf16_allowed(got, ref, rule="rounded"))
     assert ratio > 2.0, ratio
+
+
+def model_forward_o(q, k, v, causal, scale):
+    """The forward's fp32 O before its bf16 store: fp16 probabilities 2^7 P
+    (relative to the row maximum) against fp16 2^-8 v, normalised by the sum
+    of the rounded probabilities."""
+    s = scale * (q @ k.T)
+    if causal:
+        n = q.shape[0]
+        s = np.where(np.tril(np.ones((n, n), bool)), s, -np.inf)
+    p = _f16(np.exp(s - s.max(axis=1, keepdims=True)) * 128.0)
+    return _f32((p @ _f16(v / 256.0)) * 256.0 / p.sum(axis=1, keepdims=True))
+
+
+def model_dq_dk_known_d(q, k, v, do, causal, scale, residual):
+    """dQ and dK with D formed before the passes: from bf16(O) plus its bf16
+    residual (residual=True) or from bf16(O) alone."""
+    P = _f32(ora.head_probs(q, k, causal, scale))
+    of = model_forward_o(q, k, v, causal, scale)
+    hi = _bf16(of)
+    o = hi + _bf16(of - hi) if residual else hi
+    D = _f32(np.sum(do * o, axis=1))
+    sE = _pow2_factor(do) * _pow2_factor(v)
+    sK, sQ = _pow2_factor(k), _pow2_factor(q)
+    dPt = _f32(sE * (do @ v.T))
+    E = _f16(_f32(P * (dPt - _f32(sE * D)[:, None])))
+    dq = _bf16(scale / (sK * sE) * (E @ (sK * k)))
+    dk = _bf16(scale / (sQ * sE) * (E.T @ (sQ * q)))
+    return dq, dk
+
+
+def _stress_inputs(vmean):
+    N, d = 512, 128
+    r = np.random.Generator(np.random.PCG64(31 + int(vmean)))
+    q = _bf16(3.0 * r.standard_normal((N, d), dtype=np.float32))
+    k = _bf16(3.0 * r.standard_normal((N, d), dtype=np.float32))
+    v = _bf16(r.standard_normal((N, d), dtype=np.float32) + vmean)
+    do = _bf16(r.standard_normal((N, d), dtype=np.float32))
+    return q, k, v, do, float(np.float32(1 / np.sqrt(d)))
+
+
+@pytest.mark.parametrize("vmean", [0.0, 8.0, 32.0])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_d_from_o_and_residual_within_tolerance(causal, vmean):
+    q, k, v, do, scale = _stress_inputs(vmean)
+    rq, rk, _ = ora.head_bwd(q, k, v, do, causal, scale)
+    gq, gk = model_dq_dk_known_d(q, k, v, do, causal, scale, residual=True)
+    for got, ref in ((gq, rq), (gk, rk)):
+        ratio = np.max(np.abs(got - ref) / bf16_allowed(got, ref, rule="rounded"))
+        assert ratio <= 0.85, ratio
+
+
+@pytest.mark.parametrize("vmean", [0.0, 8.0])
+def test_d_from_bf16_o_alone_fails(vmean):
+    """Without the residual the rounding of O moves D by up to 2^-9 |O| |dO|
+    per term: dQ and dK leave the tolerance even with zero-mean values."""
+    q, k, v, do, scale = _stress_inputs(vmean)
+    rq, rk, _ = ora.head_bwd(q, k, v, do, True, scale)
+    gq, gk = model_dq_dk_known_d(q, k, v, do, True, scale, residual=False)
+    for got, ref in ((gq, rq), (gk, rk)):
+        ratio = np.max(np.abs(got - ref) / bf16_allowed(got, ref, rule="rounded"))
+        assert ratio > 2.0, ratio

@@ -5,7 +5,8 @@ The GPU backward consumes the GPU forward's O and logsumexp. Small shapes
 (several query blocks and key tiles, ragged tails, Nq != Nk with bottom-right
 causal alignment and rows that see no key, shared K/V heads) are compared on
 every element; the head-size-256 benchmark workload on two whole heads plus dQ
-on sampled rows of every head.
+on sampled rows of every head. Both ways of forming D are tested: from O and
+the forward's rounding residual ("o_res"), and in the dQ pass ("exact").
 """
 import concurrent.futures as cf
 
@@ -31,11 +32,15 @@ def fa():
     return fa
 
 
-def _fwd_bwd(fa, inp, causal, scale):
+MODES = ["o_res", "exact"]
+
+
+def _fwd_bwd(fa, inp, causal, scale, mode):
     import torch
     q, k, v, do = (wl.to_device(x, "bf16") for x in (inp.q, inp.k, inp.v, inp.do))
-    o, lse = fa.fa_fwd_rect(q, k, v, causal=causal, scale=scale)
-    dq, dk, dv = fa.fa_bwd_rect(q, k, v, o, do, lse, causal=causal, scale=scale)
+    o_res = torch.empty_like(q) if mode == "o_res" else None
+    o, lse = fa.fa_fwd_rect(q, k, v, causal=causal, scale=scale, o_res=o_res)
+    dq, dk, dv = fa.fa_bwd_rect(q, k, v, o, do, lse, causal=causal, scale=scale, o_res=o_res)
     torch.cuda.synchronize()
     return to_np(dq), to_np(dk), to_np(dv)
 
@@ -44,13 +49,15 @@ SMALL = [(1, 2, 2, 300, 300), (2, 2, 1, 129, 129), (1, 4, 2, 200, 517), (1, 2, 1
          (1, 1, 1, 1, 1), (1, 1, 1, 64, 64), (1, 2, 2, 520, 520)]
 
 
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
 @pytest.mark.parametrize("B,H,Hkv,Nq,Nk", SMALL)
-def test_d256_backward_small(fa, B, H, Hkv, Nq, Nk, causal):
-    say(f"d=256 backward B={B} H={H} Hkv={Hkv} Nq={Nq} Nk={Nk} causal={causal} seed=93")
+def test_d256_backward_small(fa, B, H, Hkv, Nq, Nk, causal, mode):
+    say(f"d=256 backward B={B} H={H} Hkv={Hkv} Nq={Nq} Nk={Nk} causal={causal} D from {mode} "
+        f"seed=93")
     inp = wl.make_decode_inputs(B, H, Hkv, Nq, Nk, D, seed=93, with_do=True)
     scale = float(np.float32(1 / np.sqrt(D)))
-    dq, dk, dv = _fwd_bwd(fa, inp, causal, scale)
+    dq, dk, dv = _fwd_bwd(fa, inp, causal, scale, mode)
     q64, k64, v64, do64 = inp.as_float64()
     rq, rk, rv = ora.rect_bwd(q64, k64, v64, do64, causal, scale, workers=None)
     check_bf16("dQ", dq, rq)
@@ -75,14 +82,16 @@ def test_d256_backward_square_entries_agree(fa):
         assert torch.equal(x, y) and torch.equal(x, z)
 
 
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("name", list(wl.WIDE_WORKLOADS))
-def test_d256_backward_workload(fa, name):
+def test_d256_backward_workload(fa, name, mode):
     """B=4 H=8 N=4096 d=256 (both masks): two whole heads element by element,
     plus dQ on sampled rows of every head."""
     w = wl.WIDE_WORKLOADS[name]
-    say(f"d=256 backward workload {w.name}: B={w.B} H={w.H} N={w.N} causal={w.causal}")
+    say(f"d=256 backward workload {w.name}: B={w.B} H={w.H} N={w.N} causal={w.causal} "
+        f"D from {mode}")
     inp = wl.make_inputs(w.B, w.H, w.N, w.d, "bf16", w.seed, with_do=True)
-    dq, dk, dv = _fwd_bwd(fa, inp, w.causal, w.scale)
+    dq, dk, dv = _fwd_bwd(fa, inp, w.causal, w.scale, mode)
     gq, gk, gv = (x.reshape(w.B * w.H, w.N, w.d) for x in (dq, dk, dv))
     q64, k64, v64, do64 = inp.as_float64()
     heads = [(0, 3), (3, 6)]

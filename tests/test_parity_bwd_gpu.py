@@ -4,6 +4,11 @@ The GPU backward consumes the GPU forward's O and logsumexp, as a caller
 would; the oracle computes the exact gradients of sum(O * dO) from q, k, v
 and dO alone. One isolation case feeds the GPU backward the oracle's own O
 (rounded to bf16) and logsumexp (rounded to fp32) instead.
+
+Both ways of forming D_i = dO_i . O_i are tested: "o_res" (the forward keeps
+O's rounding residual and the preprocess forms D from O plus residual; the
+dQ pass takes D from the workspace) and "exact" (no residual: the dQ pass
+forms D from P and dP itself).
 """
 import numpy as np
 import pytest
@@ -25,11 +30,15 @@ def fa():
     return fa
 
 
-def _gpu_fwd_bwd(fa, inp, causal, scale):
+MODES = ["o_res", "exact"]
+
+
+def _gpu_fwd_bwd(fa, inp, causal, scale, mode):
     import torch
     q, k, v, do = (wl.to_device(x, "bf16") for x in (inp.q, inp.k, inp.v, inp.do))
-    o, lse = fa.fa_fwd(q, k, v, causal=causal, scale=scale)
-    dq, dk, dv = fa.fa_bwd(q, k, v, o, do, lse, causal=causal, scale=scale)
+    o_res = torch.empty_like(q) if mode == "o_res" else None
+    o, lse = fa.fa_fwd(q, k, v, causal=causal, scale=scale, o_res=o_res)
+    dq, dk, dv = fa.fa_bwd(q, k, v, o, do, lse, causal=causal, scale=scale, o_res=o_res)
     torch.cuda.synchronize()
     return dq, dk, dv
 
@@ -38,13 +47,14 @@ SMALL = [(1, 1, 1, 64), (1, 1, 40, 128), (2, 2, 64, 64), (1, 2, 129, 128), (2, 1
          (1, 2, 300, 128), (1, 1, 700, 128)]
 
 
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
 @pytest.mark.parametrize("B,H,N,d", SMALL)
-def test_bf16_backward_small(fa, B, H, N, d, causal):
-    say(f"fa_bwd bf16 B={B} H={H} N={N} d={d} causal={causal} seed=21")
+def test_bf16_backward_small(fa, B, H, N, d, causal, mode):
+    say(f"fa_bwd bf16 B={B} H={H} N={N} d={d} causal={causal} D from {mode} seed=21")
     inp = wl.make_inputs(B, H, N, d, "bf16", seed=21, with_do=True)
     scale = float(np.float32(1 / np.sqrt(d)))
-    dq, dk, dv = _gpu_fwd_bwd(fa, inp, causal, scale)
+    dq, dk, dv = _gpu_fwd_bwd(fa, inp, causal, scale, mode)
     q64, k64, v64, do64 = inp.as_float64()
     rq, rk, rv = ora.attention_bwd(q64, k64, v64, do64, causal, scale, workers=None)
     check_bf16("dQ", to_np(dq), rq)
@@ -74,33 +84,38 @@ def test_bf16_backward_with_oracle_forward_outputs(fa):
 
 def test_bf16_backward_workload(fa):
     """Causal fwd+bwd, B=4 H=16 N=4096 d=128: every element of dQ, dK and dV
-    of every head."""
+    of every head, with D from O and its residual (the training step the
+    benchmark times) and with D formed in the dQ pass."""
     w = wl.WORKLOADS["bf16_b4h16n4096d128_causal_bwd"]
-    say(f"fa_bwd workload {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} seed={w.seed}")
     inp = wl.workload_inputs(w)
-    dq, dk, dv = _gpu_fwd_bwd(fa, inp, w.causal, w.scale)
     q64, k64, v64, do64 = (x.astype(np.float64) for x in (inp.q, inp.k, inp.v, inp.do))
     say(f"  oracle on {oracle_workers()} threads")
     with single_threaded_blas():
         rq, rk, rv = ora.attention_bwd(q64, k64, v64, do64, w.causal, w.scale,
                                        workers=oracle_workers())
-    check_bf16(f"dQ {w.name}", to_np(dq), rq)
-    check_bf16(f"dK {w.name}", to_np(dk), rk)
-    check_bf16(f"dV {w.name}", to_np(dv), rv)
+    for mode in MODES:
+        say(f"fa_bwd workload {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} seed={w.seed} "
+            f"D from {mode}")
+        dq, dk, dv = _gpu_fwd_bwd(fa, inp, w.causal, w.scale, mode)
+        check_bf16(f"dQ {w.name} ({mode})", to_np(dq), rq)
+        check_bf16(f"dK {w.name} ({mode})", to_np(dk), rk)
+        check_bf16(f"dV {w.name} ({mode})", to_np(dv), rv)
 
 
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("v_mean", [8.0, 32.0])
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
-def test_bf16_backward_sharp_scores_large_value_mean(fa, causal, v_mean):
+def test_bf16_backward_sharp_scores_large_value_mean(fa, causal, v_mean, mode):
     """Stress inputs outside the specified workloads: q, k x3 (sharp rows) and
     values with a large mean, so |dP| is far larger than |dP - D| (the dQ pass
     subtracts a centre before rounding). Every element of dQ, dK, dV, under
     the "rounded" bf16 rule."""
     B, H, N, d = 1, 4, 1024, 128
-    say(f"fa_bwd stress B={B} H={H} N={N} d={d} causal={causal} qk x3 v_mean={v_mean} seed=24")
+    say(f"fa_bwd stress B={B} H={H} N={N} d={d} causal={causal} qk x3 v_mean={v_mean} "
+        f"D from {mode} seed=24")
     inp = wl.make_inputs(B, H, N, d, "bf16", seed=24, qk_mult=3.0, with_do=True, v_mean=v_mean)
     scale = float(np.float32(1 / np.sqrt(d)))
-    dq, dk, dv = _gpu_fwd_bwd(fa, inp, causal, scale)
+    dq, dk, dv = _gpu_fwd_bwd(fa, inp, causal, scale, mode)
     q64, k64, v64, do64 = inp.as_float64()
     rq, rk, rv = ora.attention_bwd(q64, k64, v64, do64, causal, scale, workers=None)
     check_bf16("dQ", to_np(dq), rq, rule="rounded")
@@ -126,15 +141,19 @@ def test_bf16_backward_64key_pass(fa, B, H, Hkv, Nq, Nk, d, causal):
     inp = wl.make_decode_inputs(B, H, Hkv, Nq, Nk, d, seed=25, with_do=True)
     scale = float(np.float32(1 / np.sqrt(d)))
     q, k, v, do = (wl.to_device(x, "bf16") for x in (inp.q, inp.k, inp.v, inp.do))
-    o, lse = fa.fa_fwd_rect(q, k, v, causal=causal, scale=scale)
-    dq, dk, dv = fa.fa_bwd_rect(q, k, v, o, do, lse, causal=causal, scale=scale)
-    torch.cuda.synchronize()
     q64, k64, v64, do64 = inp.as_float64()
     with single_threaded_blas():
         rq, rk, rv = ora.rect_bwd(q64, k64, v64, do64, causal, scale, workers=oracle_workers())
-    check_bf16("dQ", to_np(dq), rq)
-    check_bf16("dK", to_np(dk), rk)
-    check_bf16("dV", to_np(dv), rv)
+    for mode in MODES:
+        say(f"  D from {mode}")
+        o_res = torch.empty_like(q) if mode == "o_res" else None
+        o, lse = fa.fa_fwd_rect(q, k, v, causal=causal, scale=scale, o_res=o_res)
+        dq, dk, dv = fa.fa_bwd_rect(q, k, v, o, do, lse, causal=causal, scale=scale,
+                                    o_res=o_res)
+        torch.cuda.synchronize()
+        check_bf16(f"dQ ({mode})", to_np(dq), rq)
+        check_bf16(f"dK ({mode})", to_np(dk), rk)
+        check_bf16(f"dV ({mode})", to_np(dv), rv)
 
 
 def test_backward_phases_equal_fa_bwd(fa):
@@ -151,6 +170,18 @@ def test_backward_phases_equal_fa_bwd(fa):
     dq3, dk3, dv3 = (torch.empty_like(q) for _ in range(3))
     fa.fa_bwd_preprocess(q, k, v, o, do, ws)
     fa.fa_bwd_dq(q, k, v, do, lse, ws, dq3, causal=causal)
+    fa.fa_bwd_dkdv(q, k, v, do, ws, dk3, dv3, causal=causal)
+    torch.cuda.synchronize()
+    for a, b, c in ((dq1, dq2, dq3), (dk1, dk2, dk3), (dv1, dv2, dv3)):
+        assert torch.equal(a, b) and torch.equal(a, c)
+    # the same with O's residual (D from the preprocess)
+    o_res = torch.empty_like(q)
+    o2, lse2 = fa.fa_fwd(q, k, v, causal=causal, o_res=o_res)
+    assert torch.equal(o2, o) and torch.equal(lse2, lse)   # the residual changes nothing else
+    dq1, dk1, dv1 = fa.fa_bwd(q, k, v, o, do, lse, causal=causal, o_res=o_res)
+    dq2, dk2, dv2 = fa.fa_bwd(q, k, v, o, do, lse, causal=causal, o_res=o_res)
+    fa.fa_bwd_preprocess(q, k, v, o, do, ws, o_res=o_res)
+    fa.fa_bwd_dq(q, k, v, do, lse, ws, dq3, causal=causal, d_ready=True)
     fa.fa_bwd_dkdv(q, k, v, do, ws, dk3, dv3, causal=causal)
     torch.cuda.synchronize()
     for a, b, c in ((dq1, dq2, dq3), (dk1, dk2, dk3), (dv1, dv2, dv3)):
