@@ -280,10 +280,11 @@ struct Tile64 {
 // the next BH*Tq the dO images, the last BHkv*Tk the K images of the K/V
 // heads. A head size DT above 128 is cut into NP = DT/128 parts of 128
 // columns, each imaged on its own ([tile][part] order), as the passes below
-// stage them. With `natural`, the Q and dO images of head sizes up to 128
-// keep the rows in their own order (for the 64-keys-per-wave dK/dV pass,
-// which reads eight consecutive query rows per lane); every other image uses
-// the permuted row order.
+// stage them. For head sizes up to 128, bit 0 of `natural` keeps the rows of
+// the Q and dO images in their own order (for the dK/dV pass with 64 keys
+// per wave, which reads eight consecutive query rows per lane) and bit 1
+// those of the K images (for the dQ pass with 64 query rows per wave); every
+// other image uses the permuted row order.
 template <int DT>
 __global__ void __launch_bounds__(256)
 bwd_image_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -308,7 +309,8 @@ bwd_image_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     __shared__ __attribute__((aligned(16))) char img[TileT::BYTES];
     TileT tl;
     tl.load(src + (size_t)head * N * DT + part * D, tile * 64, N, threadIdx.x);
-    if (DT <= 128 && which < 2 && natural) tl.template store_transposed<true, true>(img, threadIdx.x, s);
+    if (DT <= 128 && (natural & (which < 2 ? 1 : 2)))
+        tl.template store_transposed<true, true>(img, threadIdx.x, s);
     else tl.template store_transposed<true, false>(img, threadIdx.x, s);
     __syncthreads();
     char* out = dst + (((size_t)head * T + tile) * NP + part) * TileT::BYTES;
@@ -1376,6 +1378,305 @@ bwd_dkdv64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
 }
 
 // ---------------------------------------------------------------------------
+// Phase 2 for head sizes 64 and 128 when D is known before the pass (formed by
+// the preprocess from O and its rounding residual): dQ with 64 query rows per
+// wave, the dK/dV pass above with the roles of queries and keys exchanged.
+// One workgroup per block of 256 query rows (4 waves x 64); it walks the key
+// tiles (64 keys) its rows see, each as four steps of 16 keys:
+//   S, dP (16 keys x 64 queries): v_mfma_f32_16x16x32_bf16, A = a 16-row
+//     slice of the K (V) tile from LDS, read once for four 16-query blocks;
+//     B = Q^T ((sE dO)^T), resident in VGPRs. Accumulator lane l: query
+//     16j + l%16, keys 4(l/16) .. +3 of the step.
+//   dS = P (sE dP - sE D) is formed there (the dP chain starts from -sE D),
+//     packed to fp16, and one v_permlane16_swap per pair of registers brings
+//     each lane the eight keys 8g .. 8g+7 (g = l/32) of query l%32 of a
+//     32-query block: the B operand layout of the 32x32x16 product.
+//   dQ^T += K~^T dS~ (32 dims x 32 queries per product, fp16, AGPR
+//     accumulators), A = the 16-key slice of the transposed K~ image (rows in
+//     their own order), read once for both 32-query blocks.
+// lse and D belong to a lane's query columns and are loaded once. Step s's
+// dS runs between the products of step s-1's dQ. Every key tile is staged
+// whole (K and V rows and the K~^T image, double-buffered) with one barrier
+// per tile. The pass also leaves lse and D per query tile for the dK/dV pass.
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(256, 1)
+bwd_dq64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+                const float* __restrict__ LSE, const float* __restrict__ scales,
+                const float* __restrict__ dvals, const char* __restrict__ kt_img,
+                float* __restrict__ stats, uint16_t* __restrict__ dQ, int BH, int G, int N,
+                int Nk, int T, int Tk, float c, float scale, int nqb) {
+    static_assert(D == 64 || D == 128, "64 query rows per wave fit the registers up to d = 128");
+    constexpr int NW = 4;
+    constexpr int BC = 64;               // keys per tile
+    constexpr int BQ = NW * 64;          // query rows per workgroup
+    constexpr int KC = D / 32;           // 32-wide contraction chunks of S and dP
+    constexpr int NB = D / 32;           // 32-wide row blocks of dQ^T
+    constexpr int TB = BC * D * 2;       // bytes of one tile (rows or image)
+    constexpr int BLK = TB / 1024;       // its 1 KB copy blocks
+    constexpr int PPT = BLK / NW;        // blocks per wave and tensor
+    constexpr int OFF_K = 0, OFF_V = TB, OFF_KT = 2 * TB;
+    constexpr int BUF = 3 * TB;          // one tile: K and V rows, then the K~^T image
+    __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, q4 = lane >> 4;   // 16x16 products: query l16, keys 4 q4 ..
+    const int g = lane >> 5, l32 = lane & 31;    // 32x32 products
+    const int bid = blockIdx.x;
+    const int bh = bid % BH;
+    const int qbi = bid / BH;
+    const int qb = CAUSAL ? (nqb - 1 - qbi) : qbi;   // causal: longest blocks first
+    const size_t head = (size_t)bh * (size_t)N * D;
+    const size_t kvhead = (size_t)(bh / G) * (size_t)Nk * D;  // K/V head of this query head
+    const uint16_t* Kh = K + kvhead;
+    const uint16_t* Vh = V + kvhead;
+    const char* kt_h = kt_img + (size_t)(bh / G) * Tk * TB;
+    const int q0 = qb * BQ;
+    const int qw0 = q0 + wave * 64;
+    const int off = Nk - N;              // query row i sits at key position i + off
+
+    const float sK = scales[bh * 4 + 1];
+    const float sV = scales[bh * 4 + 2], sDO = scales[bh * 4 + 3];
+    const float sE = sDO * sV;
+
+    // Q^T and (sE dO)^T operands of the 16x16x32 products (rows past N read
+    // row N-1: finite values whose probabilities are 0 and whose dQ is not
+    // stored), and the statistics of the lane's four query columns. Rows
+    // past N, and rows that see no key (lse = -inf), take +inf as lse log2 e:
+    // each of their probabilities is then exactly 0.
+    u32x4_t qr[KC][4], orr[KC][4];
+    float lse2[4], dhs[4];
+    f32x4_t dinit[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int qi = qw0 + 16 * j + l16;
+        const size_t row = (size_t)min(qi, N - 1);
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+            qr[kc][j] = *(const u32x4_t*)(Q + head + row * D + 32 * kc + 8 * q4);
+            const u32x4_t v = *(const u32x4_t*)(dO + head + row * D + 32 * kc + 8 * q4);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) orr[kc][j][w] = bf16x2_scale(v[w], sE);
+        }
+        const float lse_i = (qi < N) ? LSE[(size_t)bh * N + qi] : kNegInf;
+        lse2[j] = (lse_i == kNegInf) ? __builtin_huge_valf() : lse_i * kLog2e;
+        dhs[j] = (qi < N) ? sE * dvals[(size_t)bh * N + qi] : 0.f;
+        dinit[j] = f32x4_t{-dhs[j], -dhs[j], -dhs[j], -dhs[j]};
+    }
+
+    // dQ^T of the wave's two 32-query blocks (AGPRs)
+    f32x16_t acc[2][NB];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[h][nb][r] = 0.f;
+
+    const int n_all = (Nk + BC - 1) / BC;
+    const int q_last = min(q0 + BQ, N) - 1 + off;      // last key position of the block
+    const int n_tiles = CAUSAL ? min(n_all, max(q_last, 0) / BC + 1) : n_all;
+    // Tiles from t_mask on cross Nk or reach past the key position of the
+    // block's first row (a wave whose rows all precede such a tile computes
+    // it fully masked).
+    const int first_free = q0 + off + 1;       // keys below this are seen by every row
+    const int t_mask = min(CAUSAL ? (first_free > 0 ? first_free / BC : 0) : n_tiles, Nk / BC);
+
+    // Part k (< 3 PPT) of key tile t into buffer b: K rows, V rows, the K~^T
+    // image, PPT 1 KB blocks each per wave. A tile past the last is filled
+    // from tile 0 and never read. (Copies that the compiler does not see as
+    // LDS writes; the barrier at each tile's start, after every wave has
+    // waited for its own copies and for its LDS reads of the buffer's
+    // previous tile, orders them.)
+    auto stage = [&](int t, int b, int k) {
+        lds_char* base = (lds_char*)(smem + b * BUF);
+        const int tensor = k / PPT, blk = wave + NW * (k % PPT);
+        const int ti = t < n_tiles ? t : 0;
+        if (tensor < 2)
+            stage_tile_block_async<D, D>(tensor == 0 ? Kh : Vh, base + (tensor == 0 ? OFF_K : OFF_V),
+                                         ti * BC, Nk, blk, lane);
+        else
+            stage_image_block_full_async(kt_h + (size_t)ti * TB, base + OFF_KT, blk, lane);
+    };
+
+    // One key tile in buffer b as one fully unrolled sequence of fragment
+    // operations. Step s (16 keys) has three segments:
+    //   A(s): S(s) = K Q^T, fragments K(kc), four 16x16x32 products each;
+    //         under it the swaps of step s-1 into the B operands.
+    //   B(s): dP(s) - D = V~ (sE dO)^T - sE D, fragments V(kc).
+    //   C(s): dQ of step s-1, fragments K~^T(nb), two 32x32x16 products
+    //         each; under them P(s) = exp2(S c - lse) and dS(s) = P (dP - D)
+    //         with its fp16 packing, one 16-query block per operation (d =
+    //         128) or two (d = 64).
+    // Step 0's C has no products (its vector work runs alone) and step 3's dQ
+    // follows the last C. Each fragment is read LA operations ahead through a
+    // ring of registers that starts again at every tile. Tiles that need a
+    // mask run it behind a uniform branch.
+    constexpr int NS = KC, NGR = NB;
+    constexpr int NOPS = 4 * (2 * NS) + 4 * NGR;
+    constexpr int LA = 2;
+    static_assert(3 + 3 * (3 * PPT - 1) < NOPS, "the next tile's copies fit in the operations");
+    // Operation o: kind (0 K, 1 V, 2 K~^T), step, chunk or block.
+    struct Op { int kind, s, x; };
+    auto op_of = [](int o) constexpr -> Op {
+        int base = 0;
+        for (int s = 0; s < 4; ++s) {
+            if (o < base + NS) return Op{0, s, o - base};
+            base += NS;
+            if (o < base + NS) return Op{1, s, o - base};
+            base += NS;
+            if (s >= 1) {
+                if (o < base + NGR) return Op{2, s - 1, o - base};
+                base += NGR;
+            }
+        }
+        return Op{2, 3, o - base};
+    };
+    auto tile = [&](int t, int b, bool mask_tile) {
+        const int j0 = t * BC;
+        f32x4_t sa[4], da[4];           // S then P, and dP - D, of the current step
+        u32x4_t ds2[2];                 // B operands (dS) of the 32-query blocks
+        uint32_t dp[4][2];              // packed dS of the four 16-query blocks
+        // key j0 + 16 s + 4 q4 + i against query qw0 + 16 j + l16: masked when
+        // past Nk, or (causal) when dlt + 16 (s - j) + i > 0
+        const int dlt = j0 + 4 * q4 - qw0 - l16 - off;
+        const int kq = j0 + 4 * q4;
+
+        auto fragment = [&](int o) -> u32x4_t {
+            const Op op = op_of(o);
+            const lds_char* base = (lds_char*)smem + b * BUF;
+            if (op.kind < 2)
+                return *(const lds_u32x4_t*)(base + (op.kind == 0 ? OFF_K : OFF_V) +
+                                             row_chunk_offset<D>(16 * op.s + l16, 4 * op.x + q4));
+            return *(const lds_u32x4_t*)(base + OFF_KT +
+                                         tr_slot_offset(32 * op.x + l32, 2 * (2 * op.s + g)));
+        };
+        // P of step s, query block j (over S), then dS = P (dP - D) packed
+        auto ds_block = [&](int s, int j) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sa[j][i] = fast_exp2(__builtin_fmaf(sa[j][i], c, -lse2[j]));
+            if (mask_tile) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (kq + 16 * s + i >= Nk || (CAUSAL && dlt + 16 * (s - j) + i > 0))
+                        sa[j][i] = 0.f;
+            }
+            dp[j][0] = pack_f16x2(sa[j][0] * da[j][0], sa[j][1] * da[j][1]);
+            dp[j][1] = pack_f16x2(sa[j][2] * da[j][2], sa[j][3] * da[j][3]);
+        };
+        // Query blocks 2h, 2h+1 -> the 32-query block h in the 32x32 B layout.
+        auto swap_block = [&](int h) {
+#pragma unroll
+            for (int w = 0; w < 2; ++w) {
+                const auto rd = __builtin_amdgcn_permlane16_swap(dp[2 * h][w], dp[2 * h + 1][w],
+                                                                 false, false);
+                ds2[h][w] = rd[0];
+                ds2[h][2 + w] = rd[1];
+            }
+        };
+
+        u32x4_t fr[LA + 1];
+#pragma unroll
+        for (int o = 0; o < LA; ++o) fr[o] = fragment(o);
+#pragma unroll
+        for (int o = 0; o < NOPS; ++o) {
+            const Op op = op_of(o);
+            if (o + LA < NOPS) fr[(o + LA) % (LA + 1)] = fragment(o + LA);
+            const u32x4_t a = fr[o % (LA + 1)];
+            if (op.kind == 0) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (op.x == 0) sa[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                    sa[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, qr[op.x][j]),
+                        sa[j], 0, 0, 0);
+                }
+                // A(s): the swaps of step s-1
+                if (op.s >= 1 && op.x == 0) swap_block(0);
+                if (op.s >= 1 && op.x == NS - 1) swap_block(1);
+            } else if (op.kind == 1) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (op.x == 0) da[j] = dinit[j];
+                    da[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, orr[op.x][j]),
+                        da[j], 0, 0, 0);
+                }
+                if (op.x == NS - 1 && op.s == 0) {
+                    // C(0): no products to run under
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) ds_block(0, j);
+                }
+            } else {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) mfma_f16_agpr(acc[h][op.x], a, ds2[h]);
+                // C(s) = dQ(s-1): dS of step s = op.s + 1
+                if (op.s < 3) {
+#pragma unroll
+                    for (int j = op.x * 4 / NB; j < (op.x + 1) * 4 / NB; ++j) ds_block(op.s + 1, j);
+                }
+                // before dQ(3): step 3's swaps (no S segment follows)
+                if (op.s == 2 && op.x == NB - 1) {
+                    swap_block(0);
+                    swap_block(1);
+                }
+            }
+            // the next tile's copies, one every third operation from the fourth on
+#pragma unroll
+            for (int k = 0; k < 3 * PPT; ++k)
+                if (o == 3 + 3 * k) stage(t + 1, b ^ 1, k);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+#pragma unroll
+    for (int k = 0; k < 3 * PPT; ++k) stage(0, 0, k);
+    for (int t = 0; t < n_tiles; ++t) {
+        // this wave's copies of tile t have landed and its reads of tile t-1
+        // are done; after the barrier everyone's are
+        wait_copies();
+        wait_lds();
+        step_barrier();
+        tile(t, t & 1, t >= t_mask);
+    }
+    wait_copies();
+
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) agpr_settle(acc[h][nb]);
+    // lse log2 e and sE D of the wave's 64 rows: one query tile
+    const int tq = qw0 >> 6;
+    if (q4 == 0 && tq < T) {
+        float* st = stats + ((size_t)bh * T + tq) * 128;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            st[16 * j + l16] = lse2[j];
+            st[64 + 16 * j + l16] = dhs[j];
+        }
+    }
+    const float f = scale / (sK * sE);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int qi = qw0 + 32 * h + l32;
+        if (qi < N) {
+            uint16_t* row = dQ + head + (size_t)qi * D;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    u32x2_t w;
+                    w[0] = pack_bf16x2(acc[h][nb][4 * q + 0] * f, acc[h][nb][4 * q + 1] * f);
+                    w[1] = pack_bf16x2(acc[h][nb][4 * q + 2] * f, acc[h][nb][4 * q + 3] * f);
+                    *(u32x2_t*)(row + 32 * nb + 8 * q + 4 * g) = w;
+                }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Launchers (arguments already validated by the C-ABI layer).
 // ---------------------------------------------------------------------------
 constexpr int kBwdWaves = 4;
@@ -1395,6 +1696,12 @@ static int q_tiles64(const BwdArgs& a) { return (a.N + 63) / 64; }
 // pass. The preprocess lays the Q and dO images out for the pass chosen here.
 static bool use_dkdv64(const BwdArgs& a) {
     return a.d <= 128 && (long long)((a.Nk + 255) / 256) * a.B * a.Hkv >= 512;
+}
+// The dQ pass with 64 query rows per wave: D known, d <= 128, and at least
+// 512 workgroups of 256 rows (smaller grids keep more workgroups per compute
+// unit with the 32-row pass).
+static bool use_dq64(const BwdArgs& a) {
+    return a.d_known && a.d <= 128 && (long long)((a.N + 255) / 256) * a.B * a.H >= 512;
 }
 static int k_tiles64(const BwdArgs& a) { return (a.Nk + 63) / 64; }
 // Column parts of a head (128 columns each above d = 128).
@@ -1423,7 +1730,7 @@ static hipError_t launch_prepare_t(const BwdArgs& a) {
                        a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                        (const uint16_t*)a.dout, ws_ptr<const float>(a, w.scales),
                        ws_ptr<char>(a, w.qt), ws_ptr<char>(a, w.ot), ws_ptr<char>(a, w.kt), BH,
-                       G, a.N, a.Nk, Tq, Tk, use_dkdv64(a) ? 1 : 0);
+                       G, a.N, a.Nk, Tq, Tk, (use_dkdv64(a) ? 1 : 0) | (use_dq64(a) ? 2 : 0));
     return hipGetLastError();
 }
 
@@ -1432,6 +1739,17 @@ static hipError_t launch_dq_t(const BwdArgs& a) {
     constexpr int NW = kBwdWaves;
     const BwdWorkspace w = ws_of(a);
     const int BH = a.B * a.H;
+    if (D <= 128 && use_dq64(a)) {
+        const int nqb = (a.N + 255) / 256;
+        hipLaunchKernelGGL((bwd_dq64_kernel<(D <= 128 ? D : 128), CAUSAL>), dim3(nqb * BH),
+                           dim3(256), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                           (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse,
+                           ws_ptr<const float>(a, w.scales), ws_ptr<const float>(a, w.dhat),
+                           ws_ptr<const char>(a, w.kt), ws_ptr<float>(a, w.stats),
+                           (uint16_t*)a.dq, BH, a.H / a.Hkv, a.N, a.Nk, q_tiles64(a),
+                           k_tiles64(a), a.scale * kLog2e, a.scale, nqb);
+        return hipGetLastError();
+    }
     const int nqb = (a.N + NW * 32 - 1) / (NW * 32);
     auto kernel = a.d_known ? bwd_dq_kernel<D, NW, CAUSAL, true>
                             : bwd_dq_kernel<D, NW, CAUSAL, false>;

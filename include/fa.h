@@ -310,11 +310,10 @@ fa_status_t fa_decode_noalloc(const void* q, const void* k, const void* v, void*
  *                      workspace.
  *   fa_bwd_dq          writes dq; leaves lse and D per query row in the
  *                      workspace. d_ready must be nonzero exactly when the
- *                      preprocess of this workspace was given o_res (it
- *                      selects the pass that takes D from the workspace;
- *                      nonzero without o_res gives gradients off by the
- *                      rounding of o, zero with o_res costs a fourth product
- *                      per score but is exact).
+ *                      preprocess of this workspace was given o_res: it
+ *                      selects the pass that takes D from the workspace, and
+ *                      the preprocess lays out the workspace for that pass
+ *                      (a mismatch gives wrong dq).
  *   fa_bwd_dkdv        writes dk and dv from q, k, v, dout and the workspace
  *                      (lse is taken from the workspace).
  */

@@ -124,8 +124,9 @@ def test_bf16_backward_sharp_scores_large_value_mean(fa, causal, v_mean, mode):
 
 
 # Shapes whose 256-key blocks give at least 512 workgroups, so that dK and dV
-# come from the pass with 64 keys per wave (smaller grids take the pass with
-# 32 keys per wave, which the tests above cover): ragged lengths, both masks,
+# come from the pass with 64 keys per wave, and (with O's residual) dQ from
+# the pass with 64 query rows per wave (smaller grids take the passes with 32
+# rows per wave, which the tests above cover): ragged lengths, both masks,
 # d = 64 and 128, shared K/V heads, and fewer query rows than keys.
 WIDE_GRID = [(2, 256, 256, 300, 300, 128), (1, 512, 512, 65, 65, 64), (4, 256, 128, 257, 257, 128),
              (1, 512, 256, 100, 333, 128), (2, 256, 256, 700, 700, 64)]
@@ -154,6 +155,26 @@ def test_bf16_backward_64key_pass(fa, B, H, Hkv, Nq, Nk, d, causal):
         check_bf16(f"dQ ({mode})", to_np(dq), rq)
         check_bf16(f"dK ({mode})", to_np(dk), rk)
         check_bf16(f"dV ({mode})", to_np(dv), rv)
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_bf16_backward_wide_grid_stress(fa, causal):
+    """The stress inputs (q, k x3, values of mean 32) on a grid wide enough for
+    the 64-row passes, D from O and its residual: every element, "rounded"
+    rule."""
+    B, H, N, d = 1, 128, 1024, 128
+    assert ((N + 255) // 256) * B * H >= 512
+    say(f"fa_bwd wide-grid stress B={B} H={H} N={N} d={d} causal={causal} v_mean=32 seed=26")
+    inp = wl.make_inputs(B, H, N, d, "bf16", seed=26, qk_mult=3.0, with_do=True, v_mean=32.0)
+    scale = float(np.float32(1 / np.sqrt(d)))
+    dq, dk, dv = _gpu_fwd_bwd(fa, inp, causal, scale, "o_res")
+    q64, k64, v64, do64 = inp.as_float64()
+    with single_threaded_blas():
+        rq, rk, rv = ora.attention_bwd(q64, k64, v64, do64, causal, scale,
+                                       workers=oracle_workers())
+    check_bf16("dQ", to_np(dq), rq, rule="rounded")
+    check_bf16("dK", to_np(dk), rk, rule="rounded")
+    check_bf16("dV", to_np(dv), rv, rule="rounded")
 
 
 def test_backward_phases_equal_fa_bwd(fa):
