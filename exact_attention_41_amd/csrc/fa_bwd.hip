@@ -1126,12 +1126,15 @@ bwd_dkdv64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
             stage_image_block_async(stats + (qh * T + ti) * 128, 512,
                                     (lds_char*)(smem + OFF_S + b * SBUF), 0, lane);
     };
+    // Query tiles run from the last down: the workgroups of one K/V head
+    // that run together (on one XCD) then read the same tile at about the
+    // same time, whatever their first tile, and share it through L2.
     auto next_tile = [&](int& gq, int& t) {
-        if (t + 1 < n_tiles) {
-            ++t;
+        if (t > t0) {
+            --t;
         } else {
             ++gq;
-            t = t0;
+            t = n_tiles - 1;
         }
     };
 
@@ -1331,11 +1334,11 @@ bwd_dkdv64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
     const int t_free = CAUSAL ? min(max((max(last_kq, 0) + BQ - 1) / BQ, t0), n_tiles) : t0;
     if (t0 < n_tiles) {
 #pragma unroll
-        for (int k = 0; k < 4 * PPT; ++k) stage(0, t0, 0, k);
-        stage_stats(0, t0, 0);
+        for (int k = 0; k < 4 * PPT; ++k) stage(0, n_tiles - 1, 0, k);
+        stage_stats(0, n_tiles - 1, 0);
         int L = 0;
         for (int gq = 0; gq < G; ++gq) {
-            for (int t = t0; t < n_tiles; ++t, ++L) {
+            for (int t = n_tiles - 1; t >= t0; --t, ++L) {
                 // this wave's copies of tile L have landed and its reads of
                 // tile L-1 are done; after the barrier everyone's are
                 wait_copies();
