@@ -124,40 +124,38 @@ bwd_absmax_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
     const int row0 = ch * kScaleRows;
     const int nrows = min(kScaleRows, N - row0);
     const size_t base = ((size_t)(kv ? r - BH : r) * N + row0) * D;
-    const uint16_t* src[2] = {(kv ? K : Q) + base, (kv ? V : dO) + base};
+    const uint16_t* src0 = (kv ? K : Q) + base;
+    const uint16_t* src1 = (kv ? V : dO) + base;
+    const bool with_d = !kv, with_res = !kv && ORes != nullptr;
     uint32_t m[2] = {0u, 0u};
+    // Thread idx holds chunk idx % DCH of row idx / DCH (256 is a multiple
+    // of DCH, so a row's DCH chunks sit in DCH consecutive lanes, all in or
+    // all out of the loop together). Every load of an iteration is issued
+    // before any is used, two iterations at a time.
+#pragma unroll 2
+    for (int idx = threadIdx.x; idx < nrows * DCH; idx += 256) {
+        const size_t e = (size_t)idx * 8;
+        const u32x4_t w0 = *(const u32x4_t*)(src0 + e);
+        const u32x4_t w1 = *(const u32x4_t*)(src1 + e);
+        u32x4_t ow = {0u, 0u, 0u, 0u}, rw = {0u, 0u, 0u, 0u};
+        if (with_d) ow = *(const u32x4_t*)(O + base + e);
+        if (with_res) rw = *(const u32x4_t*)(ORes + base + e);
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        // Thread idx holds chunk idx % DCH of row idx / DCH (256 is a multiple
-        // of DCH, so a row's DCH chunks sit in DCH consecutive lanes, all in
-        // or all out of the loop together).
-        for (int idx = threadIdx.x; idx < nrows * DCH; idx += 256) {
-            const u32x4_t w = *(const u32x4_t*)(src[t] + (size_t)idx * 8);
+        for (int c = 0; c < 4; ++c) {
+            m[0] = max(m[0], max(w0[c] & 0x7fffu, (w0[c] >> 16) & 0x7fffu));
+            m[1] = max(m[1], max(w1[c] & 0x7fffu, (w1[c] >> 16) & 0x7fffu));
+        }
+        if (with_d) {
+            // D = dO . O with O = bf16(O) (+ its residual: the sum is exact in fp32)
+            float s = 0.f;
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-                m[t] = max(m[t], max(w[c] & 0x7fffu, (w[c] >> 16) & 0x7fffu));
-            if (t == 1 && !kv) {
-                const u32x4_t ow = *(const u32x4_t*)(O + base + (size_t)idx * 8);
-                float s = 0.f;
-                if (ORes != nullptr) {
-                    // bf16(O) + its residual: exact in fp32
-                    const u32x4_t rw = *(const u32x4_t*)(ORes + base + (size_t)idx * 8);
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        s = __builtin_fmaf(bf16_lo(w[c]), bf16_lo(ow[c]) + bf16_lo(rw[c]), s);
-                        s = __builtin_fmaf(bf16_hi(w[c]), bf16_hi(ow[c]) + bf16_hi(rw[c]), s);
-                    }
-                } else {
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        s = __builtin_fmaf(bf16_lo(w[c]), bf16_lo(ow[c]), s);
-                        s = __builtin_fmaf(bf16_hi(w[c]), bf16_hi(ow[c]), s);
-                    }
-                }
-#pragma unroll
-                for (int off = DCH / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
-                if (idx % DCH == 0) dhat[(size_t)r * Nq + row0 + idx / DCH] = s;
+            for (int c = 0; c < 4; ++c) {
+                s = __builtin_fmaf(bf16_lo(w1[c]), bf16_lo(ow[c]) + bf16_lo(rw[c]), s);
+                s = __builtin_fmaf(bf16_hi(w1[c]), bf16_hi(ow[c]) + bf16_hi(rw[c]), s);
             }
+#pragma unroll
+            for (int off = DCH / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
+            if (idx % DCH == 0) dhat[(size_t)r * Nq + row0 + idx / DCH] = s;
         }
     }
     __shared__ uint32_t red[4][2];
