@@ -14,7 +14,7 @@ import pytest
 
 from exact_attention_41_amd import workloads as wl
 from oracle import attention as ora
-from parity_util import say, sample_rows, to_np
+from parity_util import record_model_check, say, sample_rows, to_np
 import fp8_tolerance as ft
 
 pytestmark = pytest.mark.gpu
@@ -54,9 +54,18 @@ def _check_rows(name, o, lse, ro, rl, q64, k64, v64, pairs, rows, Nq, Nk, causal
         res = list(ex.map(one, range(len(pairs))))
     tol = np.stack([r[0] for r in res])
     tol_lse = np.stack([r[1] for r in res])
+    sigma = np.stack([r[2] for r in res])
+    err_o = np.abs(np.asarray(o, np.float64) - ro)
+    record_model_check(f"O {name}", err_o, tol, bool(np.all(err_o <= tol)))
     ft.check_fp8(f"O {name}", o, ro, tol, say=say)
+    rms = float(np.sqrt(np.mean(((np.asarray(o, np.float64) - ro) / sigma) ** 2)))
+    record_model_check(f"O {name}: rms of error / sigma", np.array([rms]),
+                       np.array([ft.RMS_LIMIT]), rms <= ft.RMS_LIMIT)
+    ft.check_fp8_rms(f"O {name}", o, ro, sigma, say=say)
     both_inf = np.isneginf(lse) & np.isneginf(rl)
     err = np.where(both_inf, 0.0, np.abs(lse - rl))
+    record_model_check(f"lse {name}", err, np.broadcast_to(tol_lse, err.shape),
+                       bool(np.all(np.isfinite(err)) and np.all(err <= tol_lse)))
     say(f"  lse {name}: max_abs={np.nanmax(err):.3e} max_tol={tol_lse.max():.3e}")
     assert np.all(np.isfinite(err)) and np.all(err <= tol_lse)
 
