@@ -88,7 +88,10 @@ const char* fa_status_str(fa_status_t status);
  * Q K^T runs on bf16 MFMA with fp32 accumulation; the softmax statistics,
  * probabilities and the output accumulator are fp32. The P V product takes
  * fp16 operands (more significand bits than bf16, for a sharp softmax):
- * 2^7 P and 2^-8 v, fp32 accumulation. So for d = 64 and 128 the values must
+ * 2^7 P and 2^-8 v, fp32 accumulation. For d = 64 and 128 the row sum that
+ * normalises O and gives lse adds those fp16 probabilities in fp32, so lse
+ * is within ln(1 + 2^-11) < 5e-4 of its exact value (d = 256 sums the fp32
+ * probabilities for lse). So for d = 64 and 128 the values must
  * satisfy |v| < 65504 * 2^8 (about 1.68e7; larger ones overflow the fp16
  * operand and give non-finite output); at d = 256 P V takes bf16 operands
  * and any finite v is allowed.
