@@ -25,24 +25,33 @@ def _fmt(x):
     return f"{x:.3e}" if isinstance(x, float) else str(x)
 
 
+def _row(r):
+    return "| " + " | ".join([
+        r["test"].split("::", 1)[-1], r["output"], str(r["n"]), _fmt(r["max_abs"]), r["tol"],
+        _fmt(r["floor"]) if "floor" in r else "-",
+        str(r["beyond_plain"]) if "beyond_plain" in r else "-",
+        f"{r['max_ratio']:.3f}", "yes" if r["passed"] else "**NO**"]) + " |"
+
+
 def write_parity_report(records, path):
     """One table row per check: the test, the output, its element count, the
     plain max-abs error, the tolerance rule, the bf16 rounding floor, the
     elements beyond a plain 1e-2, the largest error / allowed ratio, and the
-    verdict."""
+    verdict. The checks of the named benchmark workloads come first."""
     os.makedirs(os.path.dirname(path), exist_ok=True)
     with open(os.path.splitext(path)[0] + ".json", "w") as f:
         json.dump(records, f, indent=1)
+    head = ["| test | output | n | max-abs | tolerance | bf16 floor | beyond 1e-2 | "
+            "max err/allowed | pass |",
+            "|---|---|---|---|---|---|---|---|---|"]
+    named = [r for r in records if "workload" in r["test"]]
+    failed = sum(1 for r in records if not r["passed"])
     lines = ["# Parity report (GPU results against the fp64 oracle)", "",
-             "| test | output | n | max-abs | tolerance | bf16 floor | beyond 1e-2 | "
-             "max err/allowed | pass |",
-             "|---|---|---|---|---|---|---|---|---|"]
+             f"{len(records)} checks, {failed} failed.", "",
+             "## The named workloads", ""] + head + [_row(r) for r in named] + [
+             "", "## Every check", ""] + head
     for r in records:
-        lines.append("| " + " | ".join([
-            r["test"].split("::", 1)[-1], r["output"], str(r["n"]), _fmt(r["max_abs"]), r["tol"],
-            _fmt(r["floor"]) if "floor" in r else "-",
-            str(r["beyond_plain"]) if "beyond_plain" in r else "-",
-            f"{r['max_ratio']:.3f}", "yes" if r["passed"] else "**NO**"]) + " |")
+        lines.append(_row(r))
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
 
