@@ -281,7 +281,7 @@ struct Tile64 {
 // stage them. For head sizes up to 128, bit 0 of `natural` keeps the rows of
 // the Q and dO images in their own order (for the dK/dV pass with 64 keys
 // per wave, which reads eight consecutive query rows per lane) and bit 1
-// those of the K images (for the dQ pass with 64 query rows per wave); every
+// those of the K images (for the dQ pass with 256-row workgroups); every
 // other image uses the permuted row order.
 template <int DT>
 __global__ void __launch_bounds__(256)
@@ -1380,12 +1380,13 @@ bwd_dkdv64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
 
 // ---------------------------------------------------------------------------
 // Phase 2 for head sizes 64 and 128 when D is known before the pass (formed by
-// the preprocess from O and its rounding residual): dQ with 64 query rows per
-// wave, the dK/dV pass above with the roles of queries and keys exchanged.
-// One workgroup per block of 256 query rows (4 waves x 64); it walks the key
-// tiles (64 keys) its rows see, each as four steps of 16 keys:
-//   S, dP (16 keys x 64 queries): v_mfma_f32_16x16x32_bf16, A = a 16-row
-//     slice of the K (V) tile from LDS, read once for four 16-query blocks;
+// the preprocess from O and its rounding residual): dQ with QW = 64 query rows
+// per wave (4 waves, one per SIMD) or 32 (8 waves, two per SIMD), the dK/dV
+// pass above with the roles of queries and keys exchanged. One workgroup per
+// block of 256 query rows; it walks the key tiles (64 keys) its rows see, each
+// as four steps of 16 keys:
+//   S, dP (16 keys x QW queries): v_mfma_f32_16x16x32_bf16, A = a 16-row
+//     slice of the K (V) tile from LDS, read once for the QW/16 query blocks;
 //     B = Q^T ((sE dO)^T), resident in VGPRs. Accumulator lane l: query
 //     16j + l%16, keys 4(l/16) .. +3 of the step.
 //   dS = P (sE dP - sE D) is formed there (the dP chain starts from -sE D),
@@ -1394,24 +1395,27 @@ bwd_dkdv64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
 //     32-query block: the B operand layout of the 32x32x16 product.
 //   dQ^T += K~^T dS~ (32 dims x 32 queries per product, fp16, AGPR
 //     accumulators), A = the 16-key slice of the transposed K~ image (rows in
-//     their own order), read once for both 32-query blocks.
+//     their own order), read once for the wave's 32-query blocks.
 // lse and D belong to a lane's query columns and are loaded once. Step s's
 // dS runs between the products of step s-1's dQ. Every key tile is staged
 // whole (K and V rows and the K~^T image, double-buffered) with one barrier
 // per tile. The pass also leaves lse and D per query tile for the dK/dV pass.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(256, 1)
-bwd_dq64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+template <int D, bool CAUSAL, int QW>
+__global__ void __launch_bounds__(256 / QW * 64, 1)
+bwd_dq16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                 const float* __restrict__ LSE, const float* __restrict__ scales,
                 const float* __restrict__ dvals, const char* __restrict__ kt_img,
                 float* __restrict__ stats, uint16_t* __restrict__ dQ, int BH, int G, int N,
                 int Nk, int T, int Tk, float c, float scale, int nqb) {
-    static_assert(D == 64 || D == 128, "64 query rows per wave fit the registers up to d = 128");
-    constexpr int NW = 4;
+    static_assert(D == 64 || D == 128, "the dQ sums and resident Q, dO fit up to d = 128");
+    static_assert(QW == 64 || QW == 32, "query rows per wave");
+    constexpr int NW = 256 / QW;         // waves: 4 (one per SIMD) or 8 (two per SIMD)
+    constexpr int NJ = QW / 16;          // 16-query blocks of a wave
+    constexpr int NH = QW / 32;          // 32-query blocks of a wave
     constexpr int BC = 64;               // keys per tile
-    constexpr int BQ = NW * 64;          // query rows per workgroup
+    constexpr int BQ = 256;              // query rows per workgroup
     constexpr int KC = D / 32;           // 32-wide contraction chunks of S and dP
     constexpr int NB = D / 32;           // 32-wide row blocks of dQ^T
     constexpr int TB = BC * D * 2;       // bytes of one tile (rows or image)
@@ -1435,7 +1439,7 @@ bwd_dq64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* Vh = V + kvhead;
     const char* kt_h = kt_img + (size_t)(bh / G) * Tk * TB;
     const int q0 = qb * BQ;
-    const int qw0 = q0 + wave * 64;
+    const int qw0 = q0 + wave * QW;
     const int off = Nk - N;              // query row i sits at key position i + off
 
     const float sK = scales[bh * 4 + 1];
@@ -1447,11 +1451,11 @@ bwd_dq64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     // stored), and the statistics of the lane's four query columns. Rows
     // past N, and rows that see no key (lse = -inf), take +inf as lse log2 e:
     // each of their probabilities is then exactly 0.
-    u32x4_t qr[KC][4], orr[KC][4];
-    float lse2[4], dhs[4];
-    f32x4_t dinit[4];
+    u32x4_t qr[KC][NJ], orr[KC][NJ];
+    float lse2[NJ], dhs[NJ];
+    f32x4_t dinit[NJ];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NJ; ++j) {
         const int qi = qw0 + 16 * j + l16;
         const size_t row = (size_t)min(qi, N - 1);
 #pragma unroll
@@ -1467,10 +1471,10 @@ bwd_dq64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         dinit[j] = f32x4_t{-dhs[j], -dhs[j], -dhs[j], -dhs[j]};
     }
 
-    // dQ^T of the wave's two 32-query blocks (AGPRs)
-    f32x16_t acc[2][NB];
+    // dQ^T of the wave's 32-query blocks (AGPRs)
+    f32x16_t acc[NH][NB];
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < NH; ++h)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -1537,9 +1541,9 @@ bwd_dq64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     };
     auto tile = [&](int t, int b, bool mask_tile) {
         const int j0 = t * BC;
-        f32x4_t sa[4], da[4];           // S then P, and dP - D, of the current step
-        u32x4_t ds2[2];                 // B operands (dS) of the 32-query blocks
-        uint32_t dp[4][2];              // packed dS of the four 16-query blocks
+        f32x4_t sa[NJ], da[NJ];         // S then P, and dP - D, of the current step
+        u32x4_t ds2[NH];                // B operands (dS) of the 32-query blocks
+        uint32_t dp[NJ][2];             // packed dS of the 16-query blocks
         // key j0 + 16 s + 4 q4 + i against query qw0 + 16 j + l16: masked when
         // past Nk, or (causal) when dlt + 16 (s - j) + i > 0
         const int dlt = j0 + 4 * q4 - qw0 - l16 - off;
@@ -1588,7 +1592,7 @@ bwd_dq64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             const u32x4_t a = fr[o % (LA + 1)];
             if (op.kind == 0) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
+                for (int j = 0; j < NJ; ++j) {
                     if (op.x == 0) sa[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
                     sa[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                         __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, qr[op.x][j]),
@@ -1596,10 +1600,10 @@ bwd_dq64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 }
                 // A(s): the swaps of step s-1
                 if (op.s >= 1 && op.x == 0) swap_block(0);
-                if (op.s >= 1 && op.x == NS - 1) swap_block(1);
+                if (NH > 1 && op.s >= 1 && op.x == NS - 1) swap_block(NH - 1);
             } else if (op.kind == 1) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
+                for (int j = 0; j < NJ; ++j) {
                     if (op.x == 0) da[j] = dinit[j];
                     da[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                         __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, orr[op.x][j]),
@@ -1608,20 +1612,20 @@ bwd_dq64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 if (op.x == NS - 1 && op.s == 0) {
                     // C(0): no products to run under
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) ds_block(0, j);
+                    for (int j = 0; j < NJ; ++j) ds_block(0, j);
                 }
             } else {
 #pragma unroll
-                for (int h = 0; h < 2; ++h) mfma_f16_agpr(acc[h][op.x], a, ds2[h]);
+                for (int h = 0; h < NH; ++h) mfma_f16_agpr(acc[h][op.x], a, ds2[h]);
                 // C(s) = dQ(s-1): dS of step s = op.s + 1
                 if (op.s < 3) {
 #pragma unroll
-                    for (int j = op.x * 4 / NB; j < (op.x + 1) * 4 / NB; ++j) ds_block(op.s + 1, j);
+                    for (int j = op.x * NJ / NB; j < (op.x + 1) * NJ / NB; ++j) ds_block(op.s + 1, j);
                 }
                 // before dQ(3): step 3's swaps (no S segment follows)
                 if (op.s == 2 && op.x == NB - 1) {
-                    swap_block(0);
-                    swap_block(1);
+#pragma unroll
+                    for (int h = 0; h < NH; ++h) swap_block(h);
                 }
             }
             // the next tile's copies, one every third operation from the fourth on
@@ -1645,22 +1649,22 @@ bwd_dq64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     wait_copies();
 
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < NH; ++h)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) agpr_settle(acc[h][nb]);
-    // lse log2 e and sE D of the wave's 64 rows: one query tile
+    // lse log2 e and sE D of the wave's rows, into their query tile
     const int tq = qw0 >> 6;
     if (q4 == 0 && tq < T) {
-        float* st = stats + ((size_t)bh * T + tq) * 128;
+        float* st = stats + ((size_t)bh * T + tq) * 128 + (qw0 & 63);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < NJ; ++j) {
             st[16 * j + l16] = lse2[j];
             st[64 + 16 * j + l16] = dhs[j];
         }
     }
     const float f = scale / (sK * sE);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < NH; ++h) {
         const int qi = qw0 + 32 * h + l32;
         if (qi < N) {
             uint16_t* row = dQ + head + (size_t)qi * D;
@@ -1698,10 +1702,10 @@ static int q_tiles64(const BwdArgs& a) { return (a.N + 63) / 64; }
 static bool use_dkdv64(const BwdArgs& a) {
     return a.d <= 128 && (long long)((a.Nk + 255) / 256) * a.B * a.Hkv >= 512;
 }
-// The dQ pass with 64 query rows per wave: D known, d <= 128, and at least
-// 512 workgroups of 256 rows (smaller grids keep more workgroups per compute
-// unit with the 32-row pass).
-static bool use_dq64(const BwdArgs& a) {
+// The dQ pass with 256-row workgroups (bwd_dq16_kernel): D known, d <= 128,
+// and at least 512 workgroups (smaller grids keep more workgroups per compute
+// unit with the 128-row pass).
+static bool use_dq16(const BwdArgs& a) {
     return a.d_known && a.d <= 128 && (long long)((a.N + 255) / 256) * a.B * a.H >= 512;
 }
 static int k_tiles64(const BwdArgs& a) { return (a.Nk + 63) / 64; }
@@ -1731,7 +1735,7 @@ static hipError_t launch_prepare_t(const BwdArgs& a) {
                        a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                        (const uint16_t*)a.dout, ws_ptr<const float>(a, w.scales),
                        ws_ptr<char>(a, w.qt), ws_ptr<char>(a, w.ot), ws_ptr<char>(a, w.kt), BH,
-                       G, a.N, a.Nk, Tq, Tk, (use_dkdv64(a) ? 1 : 0) | (use_dq64(a) ? 2 : 0));
+                       G, a.N, a.Nk, Tq, Tk, (use_dkdv64(a) ? 1 : 0) | (use_dq16(a) ? 2 : 0));
     return hipGetLastError();
 }
 
@@ -1740,10 +1744,13 @@ static hipError_t launch_dq_t(const BwdArgs& a) {
     constexpr int NW = kBwdWaves;
     const BwdWorkspace w = ws_of(a);
     const int BH = a.B * a.H;
-    if (D <= 128 && use_dq64(a)) {
+    if (D <= 128 && use_dq16(a)) {
         const int nqb = (a.N + 255) / 256;
-        hipLaunchKernelGGL((bwd_dq64_kernel<(D <= 128 ? D : 128), CAUSAL>), dim3(nqb * BH),
-                           dim3(256), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+        // d = 128: 32 rows per wave, two waves per SIMD (each wave's vector work
+        // can run under the other's products); d = 64: 64 rows, one wave per SIMD
+        constexpr int QW = D == 128 ? 32 : 64;
+        hipLaunchKernelGGL((bwd_dq16_kernel<(D <= 128 ? D : 128), CAUSAL, QW>), dim3(nqb * BH),
+                           dim3(256 / QW * 64), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                            (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse,
                            ws_ptr<const float>(a, w.scales), ws_ptr<const float>(a, w.dhat),
                            ws_ptr<const char>(a, w.kt), ws_ptr<float>(a, w.stats),

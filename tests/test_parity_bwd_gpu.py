@@ -125,9 +125,10 @@ def test_bf16_backward_sharp_scores_large_value_mean(fa, causal, v_mean, mode):
 
 # Shapes whose 256-key blocks give at least 512 workgroups, so that dK and dV
 # come from the pass with 64 keys per wave, and (with O's residual) dQ from
-# the pass with 64 query rows per wave (smaller grids take the passes with 32
-# rows per wave, which the tests above cover): ragged lengths, both masks,
-# d = 64 and 128, shared K/V heads, and fewer query rows than keys.
+# the pass with 256-row workgroups (64 rows per wave at d = 64, 32 at d = 128;
+# smaller grids take the passes with 128-row workgroups, which the tests above
+# cover): ragged lengths, both masks, d = 64 and 128, shared K/V heads, and
+# fewer query rows than keys.
 WIDE_GRID = [(2, 256, 256, 300, 300, 128), (1, 512, 512, 65, 65, 64), (4, 256, 128, 257, 257, 128),
              (1, 512, 256, 100, 333, 128), (2, 256, 256, 700, 700, 64)]
 
