@@ -54,7 +54,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 COPY_BYTES = 512 << 20          # the calibration copy reads and writes this much
 # Kernel-name fragments -> the step's kernel names.
 KERNEL_KEYS = {"fwd_bf16_kernel": "fwd", "bwd_dq_kernel": "bwd_dq", "bwd_dkdv_kernel": "bwd_dkdv",
-               "bwd_dkdv64_kernel": "bwd_dkdv", "bwd_dq16_kernel": "bwd_dq",
+               "bwd_dkdv16_kernel": "bwd_dkdv", "bwd_dq16_kernel": "bwd_dq",
                "bwd_absmax_kernel": "bwd_absmax", "bwd_scale_kernel": "bwd_scale",
                "bwd_image_kernel": "bwd_image"}
 

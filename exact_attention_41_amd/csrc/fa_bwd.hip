@@ -1006,13 +1006,13 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 }
 
 // ---------------------------------------------------------------------------
-// Phase 3 for head sizes 64 and 128: dK, dV with 64 keys per wave.
-// One workgroup per block of 256 keys (4 waves x 64); it walks the query
-// tiles (64 rows) that see them, each as four steps of 16 query rows, so
-// every LDS fragment feeds several products (the 32-key form above reads a
-// fresh fragment for each):
-//   S, dP (16 queries x 64 keys): v_mfma_f32_16x16x32_bf16, A = a 16-row
-//     slice of the Q (dO) tile from LDS, read once for four 16-key blocks;
+// Phase 3 for head sizes 64 and 128: dK, dV with KW = 64 keys per wave (4
+// waves, one per SIMD) or 32 (8 waves, two per SIMD). One workgroup per block
+// of 256 keys; it walks the query tiles (64 rows) that see them, each as four
+// steps of 16 query rows, so every LDS fragment feeds several products (the
+// 32-key form above reads a fresh fragment for each):
+//   S, dP (16 queries x KW keys): v_mfma_f32_16x16x32_bf16, A = a 16-row
+//     slice of the Q (dO) tile from LDS, read once for the KW/16 key blocks;
 //     B = K^T (V^T), resident in VGPRs. Accumulator lane l: key 16j + l%16,
 //     queries 4(l/16) .. +3.
 //   P and dS = P (sE dP - sE D) are formed there, packed to fp16, and one
@@ -1021,23 +1021,26 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 //     operand layout of the 32x32x16 product.
 //   dV^T += dO~^T P, dK^T += Q~^T dS~ (32 dims x 32 keys per product, fp16,
 //     AGPR accumulators), A = the 16-query slice of the transposed fp16
-//     image, read once for both 32-key blocks.
+//     image, read once for the wave's 32-key blocks.
 // Step s's softmax runs between the products of step s-1's dV/dK. Every
 // query tile is staged whole (rows and images, double-buffered) with one
 // barrier per tile.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(256, 1)
-bwd_dkdv64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+template <int D, bool CAUSAL, int KW>
+__global__ void __launch_bounds__(256 / KW * 64, 1)
+bwd_dkdv16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                   const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                   const float* __restrict__ scales, const float* __restrict__ stats,
                   const char* __restrict__ qt_img, const char* __restrict__ ot_img,
                   uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int BHkv, int G, int N,
                   int Nk, int T, float c, float scale) {
-    static_assert(D == 64 || D == 128, "64 keys per wave fit the registers up to d = 128");
-    constexpr int NW = 4;
+    static_assert(D == 64 || D == 128, "the dK, dV sums and resident K, V fit up to d = 128");
+    static_assert(KW == 64 || KW == 32, "keys per wave");
+    constexpr int NW = 256 / KW;         // waves: 4 (one per SIMD) or 8 (two per SIMD)
+    constexpr int NJ = KW / 16;          // 16-key blocks of a wave
+    constexpr int NH = KW / 32;          // 32-key blocks of a wave
     constexpr int BQ = 64;               // query rows per tile
-    constexpr int BKV = NW * 64;         // keys per workgroup
+    constexpr int BKV = 256;             // keys per workgroup
     constexpr int KC = D / 32;           // 32-wide contraction chunks of S and dP
     constexpr int NB = D / 32;           // 32-wide row blocks of dV^T and dK^T
     constexpr int TB = BQ * D * 2;       // bytes of one tile (rows or image)
@@ -1066,17 +1069,17 @@ bwd_dkdv64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
     const float sE = sDO * sV;
 
     const int k0 = kb * BKV;
-    const int kw0 = k0 + wave * 64;
+    const int kw0 = k0 + wave * KW;
     const int off = Nk - N;                      // query row i sits at key position i + off
 
     // K^T and (sE V)^T operands of the 16x16x32 products (sE a power of two,
     // so sE V is exact; keys past Nk read key Nk-1, whose gradients are not
     // stored).
-    u32x4_t kr[KC][4], vr[KC][4];
+    u32x4_t kr[KC][NJ], vr[KC][NJ];
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < NJ; ++j) {
             const size_t row = (size_t)min(kw0 + 16 * j + l16, Nk - 1);
             kr[kc][j] = *(const u32x4_t*)(K + head + row * D + 32 * kc + 8 * q4);
             const u32x4_t v = *(const u32x4_t*)(V + head + row * D + 32 * kc + 8 * q4);
@@ -1084,10 +1087,10 @@ bwd_dkdv64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
             for (int w = 0; w < 4; ++w) vr[kc][j][w] = bf16x2_scale(v[w], sE);
         }
 
-    // dV^T, dK^T of the wave's two 32-key blocks (AGPRs)
-    f32x16_t acc_dv[2][NB], acc_dk[2][NB];
+    // dV^T, dK^T of the wave's 32-key blocks (AGPRs)
+    f32x16_t acc_dv[NH][NB], acc_dk[NH][NB];
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < NH; ++h)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -1171,7 +1174,7 @@ bwd_dkdv64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
     // not fit the registers together.
     constexpr int NS = KC, NGR = 2 * NB;
     constexpr int NOPS = 4 * (2 * NS) + 4 * NGR;
-    constexpr int LA = 2;
+    constexpr int LA = KW == 32 ? 1 : 2;
     // Operation o: kind (0 Q, 1 dO, 2 dO~^T, 3 Q~^T), step, chunk or block.
     struct Op { int kind, s, x; };
     auto op_of = [](int o) constexpr -> Op {
@@ -1195,11 +1198,11 @@ bwd_dkdv64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
         const lds_char* st = (lds_char*)smem + OFF_S + b * SBUF;
         int ga = gq, ta = t;
         next_tile(ga, ta);
-        f32x4_t sa[4], da[4];           // S then P, and dP - D, of the current step
-        u32x4_t pk[2], dk2[2];          // B operands (P, dS) of the 32-key blocks
+        f32x4_t sa[NJ], da[NJ];         // S then P, and dP - D, of the current step
+        u32x4_t pk[NH], dk2[NH];        // B operands (P, dS) of the 32-key blocks
         float lse4[4];
         f32x4_t dinit;                  // -sE D of the step's four rows
-        uint32_t pp[4][2], dp[4][2];    // packed P, dS of the four 16-key blocks
+        uint32_t pp[NJ][2], dp[NJ][2];  // packed P, dS of the 16-key blocks
         // Causal: key kw0 + 16 j + l16 is above query row i0 + 16 s + 4 q4 + i
         // when dlt > 16 (s - j) + i.
         const int dlt = kw0 + l16 - i0 - 4 * q4 - off;
@@ -1266,7 +1269,7 @@ bwd_dkdv64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
             const u32x4_t a = fr[o % (LA + 1)];
             if (op.kind == 0) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
+                for (int j = 0; j < NJ; ++j) {
                     if (op.x == 0) sa[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
                     sa[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                         __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, kr[op.x][j]),
@@ -1274,10 +1277,10 @@ bwd_dkdv64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
                 }
                 // A(s): the swaps of step s-1
                 if (op.s >= 1 && op.x == 0) swap_block(0);
-                if (op.s >= 1 && op.x == NS - 1) swap_block(1);
+                if (NH > 1 && op.s >= 1 && op.x == NS - 1) swap_block(NH - 1);
             } else if (op.kind == 1) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
+                for (int j = 0; j < NJ; ++j) {
                     if (op.x == 0) da[j] = dinit;
                     da[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                         __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, vr[op.x][j]),
@@ -1286,18 +1289,18 @@ bwd_dkdv64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
                 if (op.x == NS - 1 && op.s == 0) {
                     // C(0): no products to run under
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) exp_block(0, j);
+                    for (int j = 0; j < NJ; ++j) exp_block(0, j);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) ds_block(j);
+                    for (int j = 0; j < NJ; ++j) ds_block(j);
                     load_stats(1);
                 }
             } else {
                 if (op.kind == 2) {
 #pragma unroll
-                    for (int h = 0; h < 2; ++h) mfma_f16_agpr(acc_dv[h][op.x], a, pk[h]);
+                    for (int h = 0; h < NH; ++h) mfma_f16_agpr(acc_dv[h][op.x], a, pk[h]);
                 } else {
 #pragma unroll
-                    for (int h = 0; h < 2; ++h) mfma_f16_agpr(acc_dk[h][op.x], a, dk2[h]);
+                    for (int h = 0; h < NH; ++h) mfma_f16_agpr(acc_dk[h][op.x], a, dk2[h]);
                 }
                 // C(s) = grad(s-1): P, dS and packing of step s = op.s + 1, one
                 // key block's exponentials after each dO~^T operation's
@@ -1305,7 +1308,7 @@ bwd_dkdv64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
                 if (op.s < 3) {
                     const int sn = op.s + 1;
 #pragma unroll
-                    for (int j = op.x * 4 / NB; j < (op.x + 1) * 4 / NB; ++j) {
+                    for (int j = op.x * NJ / NB; j < (op.x + 1) * NJ / NB; ++j) {
                         if (op.kind == 2) exp_block(sn, j);
                         else ds_block(j);
                     }
@@ -1313,8 +1316,8 @@ bwd_dkdv64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
                 }
                 // before grad(3): step 3's swaps (no S segment follows)
                 if (op.s == 2 && op.kind == 3 && op.x == NB - 1) {
-                    swap_block(0);
-                    swap_block(1);
+#pragma unroll
+                    for (int h = 0; h < NH; ++h) swap_block(h);
                 }
             }
             // the next tile's copies, one every third operation from the fourth on
@@ -1349,7 +1352,7 @@ bwd_dkdv64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
     }
 
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < NH; ++h)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             agpr_settle(acc_dk[h][nb]);
@@ -1357,7 +1360,7 @@ bwd_dkdv64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
         }
     const float fk = scale / (sQ * sE), fv = 1.f / sDO;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < NH; ++h) {
         const int kj = kw0 + 32 * h + l32;
         if (kj < Nk) {
             uint16_t* dkrow = dK + head + (size_t)kj * D;
@@ -1694,12 +1697,12 @@ template <typename T>
 static T* ws_ptr(const BwdArgs& a, size_t off) { return (T*)((char*)a.workspace + off); }
 
 static int q_tiles64(const BwdArgs& a) { return (a.N + 63) / 64; }
-// The dK/dV pass with 64 keys per wave (256 per workgroup) for head sizes up
-// to 128, when its grid still has two workgroups per compute unit of an
+// The dK/dV pass with 256-key workgroups (bwd_dkdv16_kernel) for head sizes
+// up to 128, when its grid still has two workgroups per compute unit of an
 // MI355X; otherwise (few K/V heads or short sequences, where 256-key blocks
-// leave the longest causal block alone at the end) the 32-keys-per-wave
-// pass. The preprocess lays the Q and dO images out for the pass chosen here.
-static bool use_dkdv64(const BwdArgs& a) {
+// leave the longest causal block alone at the end) the 128-key pass. The
+// preprocess lays the Q and dO images out for the pass chosen here.
+static bool use_dkdv16(const BwdArgs& a) {
     return a.d <= 128 && (long long)((a.Nk + 255) / 256) * a.B * a.Hkv >= 512;
 }
 // The dQ pass with 256-row workgroups (bwd_dq16_kernel): D known, d <= 128,
@@ -1735,7 +1738,7 @@ static hipError_t launch_prepare_t(const BwdArgs& a) {
                        a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                        (const uint16_t*)a.dout, ws_ptr<const float>(a, w.scales),
                        ws_ptr<char>(a, w.qt), ws_ptr<char>(a, w.ot), ws_ptr<char>(a, w.kt), BH,
-                       G, a.N, a.Nk, Tq, Tk, (use_dkdv64(a) ? 1 : 0) | (use_dq16(a) ? 2 : 0));
+                       G, a.N, a.Nk, Tq, Tk, (use_dkdv16(a) ? 1 : 0) | (use_dq16(a) ? 2 : 0));
     return hipGetLastError();
 }
 
@@ -1774,11 +1777,16 @@ template <int D, bool CAUSAL>
 static hipError_t launch_dkdv_t(const BwdArgs& a) {
     const BwdWorkspace w = ws_of(a);
     const int BHkv = a.B * a.Hkv;
-    if (D <= 128 && use_dkdv64(a)) {
-        // 64 keys per wave, 256 per workgroup
+    if (D <= 128 && use_dkdv16(a)) {
+        // 256 keys per workgroup
         const int nkb = (a.Nk + 255) / 256;
-        hipLaunchKernelGGL((bwd_dkdv64_kernel<(D <= 128 ? D : 128), CAUSAL>), dim3(nkb * BHkv),
-                           dim3(256), 0,
+        // d = 64: 32 keys per wave, two waves per SIMD (each wave's vector work
+        // can run under the other's products); d = 128: 64 keys, one wave per
+        // SIMD (the dK and dV sums and the resident K and V of 32 keys, 192
+        // registers, leave too few for a second wave)
+        constexpr int KW = D == 64 ? 32 : 64;
+        hipLaunchKernelGGL((bwd_dkdv16_kernel<(D <= 128 ? D : 128), CAUSAL, KW>), dim3(nkb * BHkv),
+                           dim3(256 / KW * 64), 0,
                            a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                            (const uint16_t*)a.v, (const uint16_t*)a.dout,
                            ws_ptr<const float>(a, w.scales), ws_ptr<const float>(a, w.stats),

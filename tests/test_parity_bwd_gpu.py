@@ -124,21 +124,21 @@ def test_bf16_backward_sharp_scores_large_value_mean(fa, causal, v_mean, mode):
 
 
 # Shapes whose 256-key blocks give at least 512 workgroups, so that dK and dV
-# come from the pass with 64 keys per wave, and (with O's residual) dQ from
-# the pass with 256-row workgroups (64 rows per wave at d = 64, 32 at d = 128;
-# smaller grids take the passes with 128-row workgroups, which the tests above
-# cover): ragged lengths, both masks, d = 64 and 128, shared K/V heads, and
-# fewer query rows than keys.
+# come from the pass with 256-key workgroups (32 keys per wave at d = 64, 64 at
+# d = 128), and (with O's residual) dQ from the pass with 256-row workgroups (64
+# rows per wave at d = 64, 32 at d = 128); smaller grids take the passes with
+# 128-row workgroups, which the tests above cover: ragged lengths, both masks,
+# d = 64 and 128, shared K/V heads, and fewer query rows than keys.
 WIDE_GRID = [(2, 256, 256, 300, 300, 128), (1, 512, 512, 65, 65, 64), (4, 256, 128, 257, 257, 128),
              (1, 512, 256, 100, 333, 128), (2, 256, 256, 700, 700, 64)]
 
 
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
 @pytest.mark.parametrize("B,H,Hkv,Nq,Nk,d", WIDE_GRID)
-def test_bf16_backward_64key_pass(fa, B, H, Hkv, Nq, Nk, d, causal):
+def test_bf16_backward_wide_grid_passes(fa, B, H, Hkv, Nq, Nk, d, causal):
     import torch
     assert ((Nk + 255) // 256) * B * Hkv >= 512
-    say(f"fa_bwd_rect (64 keys per wave) B={B} H={H} Hkv={Hkv} Nq={Nq} Nk={Nk} d={d} "
+    say(f"fa_bwd_rect (256-key workgroups) B={B} H={H} Hkv={Hkv} Nq={Nq} Nk={Nk} d={d} "
         f"causal={causal} seed=25")
     inp = wl.make_decode_inputs(B, H, Hkv, Nq, Nk, d, seed=25, with_do=True)
     scale = float(np.float32(1 / np.sqrt(d)))
