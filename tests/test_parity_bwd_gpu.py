@@ -130,7 +130,8 @@ def test_bf16_backward_sharp_scores_large_value_mean(fa, causal, v_mean, mode):
 # 128-row workgroups, which the tests above cover: ragged lengths, both masks,
 # d = 64 and 128, shared K/V heads, and fewer query rows than keys.
 WIDE_GRID = [(2, 256, 256, 300, 300, 128), (1, 512, 512, 65, 65, 64), (4, 256, 128, 257, 257, 128),
-             (1, 512, 256, 100, 333, 128), (2, 256, 256, 700, 700, 64)]
+             (1, 512, 256, 100, 333, 128), (2, 256, 256, 700, 700, 64), (2, 512, 256, 300, 300, 64),
+             (1, 1024, 512, 200, 333, 64)]
 
 
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
