@@ -2,10 +2,12 @@
 """Benchmark of the fused exact-attention hot path on one MI355X.
 
 One step = one pass of the whole path over one batch of seeded synthetic
-input: the fused forward (fa_fwd, keeping O's rounding residual for the
-backward) and the backward (fa_bwd's three phases: per-head scale factors,
-D = rowsum(dO * O) and fp16 tile images; dQ; dK/dV) on the causal bf16
-workload B=4 H=16 N=4096 d=128 with upstream gradient dO. ``value`` is counted TFLOP/s of that step,
+input, as a training step runs it: the fused forward that keeps O's
+rounding residual for the backward (fa_fwd_train), then the backward's three
+phases as fa_bwd_train runs them (per-head scale factors, D = rowsum(dO * O)
+and fp16 tile images; dQ; dK/dV), on the causal bf16 workload B=4 H=16 N=4096
+d=128 with upstream gradient dO. The line also gives the time of the same step
+through fa_fwd and fa_bwd (no residual: the dQ pass then forms D itself). ``value`` is counted TFLOP/s of that step,
 with the counted flops 4*B*H*N^2*d (halved for causal) for the forward and
 2.5x that for the backward. Inputs are resident in HBM before timing starts.
 
@@ -230,6 +232,12 @@ def gpu_step_timing(w, steps: int, warmup: int, with_clock: bool = True):
         per_kernel["bwd_dq_no_res"] = timer.median(
             lambda: fa.fa_bwd_dq(q, k, v, do, lse, ws, dq, causal=w.causal, scale=w.scale,
                                  d_ready=False))[0]
+
+        def plain_step():
+            fa.fa_fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+            fa.fa_bwd(q, k, v, o, do, lse, causal=w.causal, scale=w.scale, dq=dq, dk=dk,
+                      dv=dv, workspace=ws)
+        per_kernel["step_fa_fwd_fa_bwd"] = timer.median(plain_step)[0]
     return ms_per_step, per_kernel, clocks
 
 
@@ -652,6 +660,7 @@ def main() -> int:
         return counter_pass(w)
     log(f"bench: workload {w.name} steps={args.steps} warmup={args.warmup}")
     ms, per_kernel, clocks = gpu_step_timing(w, args.steps, args.warmup)
+    plain_ms = per_kernel.pop("step_fa_fwd_fa_bwd", None)
     fwd_f, bwd_f = w.fwd_flops(), w.bwd_flops()
     value = (fwd_f + bwd_f) / (ms * 1e-3) / 1e12
     log(f"bench: {ms:.3f} ms/step, {value:.1f} TFLOP/s; per kernel (ms): "
@@ -711,6 +720,11 @@ def main() -> int:
         "bwd": {"ms": round(bwd_ms, 4), "tflops": round(bwd_tf, 1),
                 "frac_peak": round(bwd_tf / PEAK_BF16_TFLOPS, 4)},
         "kernel_ms": {k: round(v, 4) for k, v in per_kernel.items()},
+        # the same step through fa_fwd and fa_bwd (no residual kept), median
+        # of single steps
+        "step_fa_fwd_fa_bwd": None if plain_ms is None else {
+            "ms": round(plain_ms, 4),
+            "tflops": round((fwd_f + bwd_f) / (plain_ms * 1e-3) / 1e12, 2)},
         "sclk_mhz": clocks,
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -6,10 +6,10 @@ calls; every step of the computation runs in the HIP kernels of libfa.so.
 If the library is not built, every call raises: there is no fallback.
 
     o, lse = fa_fwd(q, k, v, causal=True)                  # bf16 [B,H,N,d]
-    o, lse = fa_fwd(q, k, v, causal=True, o_res=r)         # also O's rounding residual
+    o, lse = fa_fwd(q, k, v, causal=True, o_res=r)         # fa_fwd_train: also O's residual
     o, lse = fa_fwd_f32(q, k, v, causal=False)             # fp32 [B,H,N,d]
     dq, dk, dv = fa_bwd(q, k, v, o, do, lse, causal=True)  # bf16
-    dq, dk, dv = fa_bwd(q, k, v, o, do, lse, causal=True, o_res=r)
+    dq, dk, dv = fa_bwd(q, k, v, o, do, lse, causal=True, o_res=r)   # fa_bwd_train
     o, lse = fa_fwd_gqa(q, k, v, causal=True)              # k, v: [B,Hkv,N,d]
     dq, dk, dv = fa_bwd_gqa(q, k, v, o, do, lse, causal=True)
     o, lse = fa_decode(q, k, v)          # q [B,H,Nq,d], k, v [B,Hkv,Nk,d]
@@ -29,7 +29,8 @@ __all__ = ["fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_bwd_workspace_size", "fa_status
            "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_gqa", "fa_bwd_gqa",
            "fa_bwd_gqa_workspace_size", "fa_decode", "fa_decode_workspace_size", "fa_fwd_rect",
            "fa_fwd_fp8", "fa_bwd_rect", "fa_bwd_rect_workspace_size", "fa_clock_probe",
-           "fa_attention", "fa_decode_noalloc", "FAError", "library_path"]
+           "fa_attention", "fa_decode_noalloc", "fa_fwd_train", "fa_bwd_train", "FAError",
+           "library_path"]
 
 
 class FAError(RuntimeError):
@@ -134,11 +135,21 @@ def _fwd(entry, dtype, q, k, v, causal, scale, out, lse, grouped=False, o_res=No
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     _check(out, "out", dtype, q.shape, q.device)
     _check(lse, "lse", torch.float32, (B, H, N), q.device)
+    if o_res is not None:
+        # the training forward: fa_fwd_train with Nq = Nk = N
+        entry = "fa_fwd_train"
+        with torch.cuda.device(q.device):
+            st = _lib.load().fa_fwd_train(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                          out.data_ptr(), _o_res_ptr(o_res, q), lse.data_ptr(),
+                                          B, H, Hkv, N, N, d, int(bool(causal)),
+                                          _scale(scale, d), _stream_ptr(q.device))
+        if st != _lib.FA_OK:
+            raise FAError(st, entry)
+        return out, lse
     fn = getattr(_lib.load(), entry)
     heads = (B, H, Hkv) if grouped else (B, H)
-    res = () if entry == "fa_fwd_f32" else (_o_res_ptr(o_res, q),)
     with torch.cuda.device(q.device):
-        st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), *res, lse.data_ptr(),
+        st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                 *heads, N, d, int(bool(causal)), _scale(scale, d), _stream_ptr(q.device))
     if st != _lib.FA_OK:
         raise FAError(st, entry)
@@ -147,9 +158,9 @@ def _fwd(entry, dtype, q, k, v, causal, scale, out, lse, grouped=False, o_res=No
 
 def fa_fwd(q, k, v, causal: bool = False, scale: Optional[float] = None,
            out=None, lse=None, o_res=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
-    """bf16 forward: returns (O, logsumexp). ``o_res``, a bf16 tensor of q's
-    shape, receives O's rounding residual when given (for fa_bwd). Calls
-    fa_fwd of libfa.so."""
+    """bf16 forward: returns (O, logsumexp). Calls fa_fwd of libfa.so, or, when
+    ``o_res`` (a bf16 tensor of q's shape) is given, fa_fwd_train, which also
+    stores O's rounding residual there for the backward."""
     return _fwd("fa_fwd", _torch().bfloat16, q, k, v, causal, scale, out, lse, o_res=o_res)
 
 
@@ -198,9 +209,13 @@ def _bwd(entry, q, k, v, o, do, lse, causal, scale, dq, dk, dv, workspace, group
     ws_bytes = _check_workspace(workspace, q.device)
     heads = (B, H, Hkv) if grouped or rect else (B, H)
     sizes = (N, Nk) if rect else (N,)
+    res = ()
+    if o_res is not None:
+        # the training backward: fa_bwd_train (general heads and lengths)
+        entry, heads, sizes, res = "fa_bwd_train", (B, H, Hkv), (N, Nk), (_o_res_ptr(o_res, q),)
     fn = getattr(_lib.load(), entry)
     with torch.cuda.device(q.device):
-        st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _o_res_ptr(o_res, q),
+        st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), *res,
                 do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                 workspace.data_ptr(), ws_bytes, *heads, *sizes, d, int(bool(causal)),
                 _scale(scale, d), _stream_ptr(q.device))
@@ -215,8 +230,8 @@ def fa_bwd(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = N
 
     ``workspace`` may be a uint8 device tensor of at least
     fa_bwd_workspace_size(B, H, N, d) bytes; one is allocated otherwise.
-    ``o_res``: the forward's rounding residual of O, if it kept one (then D
-    comes from O in the preprocess and the dQ pass is cheaper).
+    ``o_res``: the forward's rounding residual of O, if it kept one; then this
+    calls fa_bwd_train (D from O in the preprocess, a cheaper dQ pass).
     """
     return _bwd("fa_bwd", q, k, v, o, do, lse, causal, scale, dq, dk, dv, workspace, False,
                 o_res=o_res)
@@ -380,8 +395,9 @@ def fa_fwd_rect(q, k, v, causal: bool = False, scale: Optional[float] = None, ou
                 lse=None, o_res=None):
     """bf16 forward with Nq query rows against Nk keys: q [B,H,Nq,d], k and v
     [B,Hkv,Nk,d] (Hkv dividing H). Query row i sits at position Nk - Nq + i
-    (bottom-right causal alignment). Returns (O [B,H,Nq,d], lse [B,H,Nq]);
-    ``o_res`` as for fa_fwd. Calls fa_fwd_rect of libfa.so."""
+    (bottom-right causal alignment). Returns (O [B,H,Nq,d], lse [B,H,Nq]).
+    Calls fa_fwd_rect of libfa.so, or fa_fwd_train when ``o_res`` is given (as
+    for fa_fwd)."""
     torch = _torch()
     bf = torch.bfloat16
     _check(q, "q", bf)
@@ -397,13 +413,37 @@ def fa_fwd_rect(q, k, v, causal: bool = False, scale: Optional[float] = None, ou
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
     _check(out, "out", bf, q.shape, q.device)
     _check(lse, "lse", torch.float32, (B, H, Nq), q.device)
+    entry = "fa_fwd_rect" if o_res is None else "fa_fwd_train"
+    res = () if o_res is None else (_o_res_ptr(o_res, q),)
     with torch.cuda.device(q.device):
-        st = _lib.load().fa_fwd_rect(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                                     _o_res_ptr(o_res, q), lse.data_ptr(), B, H, Hkv, Nq, Nk, d,
-                                     int(bool(causal)), _scale(scale, d), _stream_ptr(q.device))
+        st = getattr(_lib.load(), entry)(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                         out.data_ptr(), *res, lse.data_ptr(), B, H, Hkv, Nq,
+                                         Nk, d, int(bool(causal)), _scale(scale, d),
+                                         _stream_ptr(q.device))
     if st != _lib.FA_OK:
-        raise FAError(st, "fa_fwd_rect")
+        raise FAError(st, entry)
     return out, lse
+
+
+def fa_fwd_train(q, k, v, o_res, causal: bool = False, scale: Optional[float] = None,
+                 out=None, lse=None):
+    """Forward for training (fa_fwd_train of libfa.so): fa_fwd_rect that also
+    stores O's rounding residual in ``o_res`` (bf16, q's shape). Returns
+    (O, lse)."""
+    if o_res is None:
+        raise ValueError("fa_fwd_train needs o_res")
+    return fa_fwd_rect(q, k, v, causal=causal, scale=scale, out=out, lse=lse, o_res=o_res)
+
+
+def fa_bwd_train(q, k, v, o, o_res, do, lse, causal: bool = False,
+                 scale: Optional[float] = None, dq=None, dk=None, dv=None, workspace=None):
+    """Backward for training (fa_bwd_train of libfa.so): the gradients of
+    fa_fwd_train's output, with D formed from o and ``o_res``. Shapes as for
+    fa_bwd_rect."""
+    if o_res is None:
+        raise ValueError("fa_bwd_train needs o_res")
+    return fa_bwd_rect(q, k, v, o, do, lse, causal=causal, scale=scale, dq=dq, dk=dk, dv=dv,
+                       workspace=workspace, o_res=o_res)
 
 
 def fa_fwd_fp8(q, k, v, descale_q: float = 1.0, descale_k: float = 1.0, descale_v: float = 1.0,
@@ -463,7 +503,7 @@ _AUTOGRAD_FN = None
 
 
 def _autograd_fn():
-    """torch.autograd.Function over fa_fwd_rect / fa_bwd_rect (built once)."""
+    """torch.autograd.Function over fa_fwd_train / fa_bwd_train (built once)."""
     global _AUTOGRAD_FN
     if _AUTOGRAD_FN is None:
         torch = _torch()
@@ -491,8 +531,8 @@ def _autograd_fn():
 def fa_attention(q, k, v, causal: bool = False, scale: Optional[float] = None):
     """Attention with autograd: O = softmax(scale Q K^T) V for bf16 q [B,H,Nq,d]
     and k, v [B,Hkv,Nk,d] on a GPU (Hkv dividing H; query row i at position
-    Nk - Nq + i, bottom-right causal). The forward is fa_fwd_rect (keeping O's
-    rounding residual); the gradient of a loss with respect to q, k and v is
-    fa_bwd_rect, fed the saved O, its residual and the logsumexp. Both run in
-    libfa.so."""
+    Nk - Nq + i, bottom-right causal). The forward is fa_fwd_train (fa_fwd_rect
+    keeping O's rounding residual); the gradient of a loss with respect to q,
+    k and v is fa_bwd_train, fed the saved O, its residual and the logsumexp.
+    Both run in libfa.so."""
     return _autograd_fn().apply(q, k, v, bool(causal), _scale(scale, q.shape[-1]))

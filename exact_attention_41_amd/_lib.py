@@ -15,7 +15,7 @@ EXPORTED = ("fa_status_str", "fa_fwd", "fa_fwd_f32", "fa_bwd_workspace_size", "f
             "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_gqa",
             "fa_bwd_gqa_workspace_size", "fa_bwd_gqa", "fa_decode_workspace_size", "fa_decode",
             "fa_fwd_rect", "fa_fwd_fp8", "fa_bwd_rect_workspace_size", "fa_bwd_rect",
-            "fa_clock_probe", "fa_decode_noalloc")
+            "fa_clock_probe", "fa_decode_noalloc", "fa_fwd_train", "fa_bwd_train")
 
 _lock = threading.Lock()
 _lib = None
@@ -39,13 +39,13 @@ def load() -> ctypes.CDLL:
         vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
         lib.fa_status_str.argtypes = [i]
         lib.fa_status_str.restype = ctypes.c_char_p
-        lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+        lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
         lib.fa_fwd.restype = i
         lib.fa_fwd_f32.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
         lib.fa_fwd_f32.restype = i
         lib.fa_bwd_workspace_size.argtypes = [i, i, i, i]
         lib.fa_bwd_workspace_size.restype = ctypes.c_size_t
-        lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+        lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                i, i, i, i, i, f, vp]
         lib.fa_bwd.restype = i
         lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
@@ -57,19 +57,26 @@ def load() -> ctypes.CDLL:
         lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp,
                                   i, i, i, i, i, f, i, vp]
         lib.fa_bwd_dq.restype = i
-        lib.fa_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+        lib.fa_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
         lib.fa_fwd_gqa.restype = i
         lib.fa_bwd_gqa_workspace_size.argtypes = [i, i, i, i, i]
         lib.fa_bwd_gqa_workspace_size.restype = ctypes.c_size_t
-        lib.fa_bwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+        lib.fa_bwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                    i, i, i, i, i, i, f, vp]
         lib.fa_bwd_gqa.restype = i
         lib.fa_bwd_rect_workspace_size.argtypes = [i, i, i, i, i, i]
         lib.fa_bwd_rect_workspace_size.restype = ctypes.c_size_t
-        lib.fa_bwd_rect.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
-                                    ctypes.c_size_t, i, i, i, i, i, i, i, f, vp]
+        lib.fa_bwd_rect.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                    i, i, i, i, i, i, i, f, vp]
         lib.fa_bwd_rect.restype = i
-        lib.fa_fwd_rect.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
+        lib.fa_bwd_train.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                     ctypes.c_size_t, i, i, i, i, i, i, i, f, vp]
+        lib.fa_bwd_train.restype = i
+        lib.fa_bwd_rect.restype = i
+        lib.fa_fwd_rect.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
+        lib.fa_fwd_rect.restype = i
+        lib.fa_fwd_train.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
+        lib.fa_fwd_train.restype = i
         lib.fa_fwd_rect.restype = i
         lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, f, f, f, vp]
         lib.fa_fwd_fp8.restype = i

@@ -92,9 +92,15 @@ const char* fa_status_str(fa_status_t status) {
     return "FA_ERR_UNKNOWN";
 }
 
-fa_status_t fa_fwd_rect(const void* q, const void* k, const void* v, void* o, void* o_res,
-                        float* lse, int B, int H, int Hkv, int Nq, int Nk, int d, int causal,
-                        float scale, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The bf16 forward of every entry point; o_res (the rounding residual of O)
+// is stored when it is not null.
+fa_status_t fwd_bf16(const void* q, const void* k, const void* v, void* o, void* o_res,
+                     float* lse, int B, int H, int Hkv, int Nq, int Nk, int d, int causal,
+                     float scale, hipStream_t stream) {
     bool empty = false;
     if (Nk < 0) return FA_ERR_INVALID_ARG;
     FA_TRY(check_fwd(q, k, v, o, lse, B, H, Nq, d, scale, true, &empty));
@@ -106,6 +112,23 @@ fa_status_t fa_fwd_rect(const void* q, const void* k, const void* v, void* o, vo
     fa::FwdArgs a{q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, causal != 0, scale, stream};
     a.o_res = o_res;
     return fa::launch_fwd_bf16(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status_t fa_fwd_rect(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                        hipStream_t stream) {
+    return fwd_bf16(q, k, v, o, nullptr, lse, B, H, Hkv, Nq, Nk, d, causal, scale, stream);
+}
+
+fa_status_t fa_fwd_train(const void* q, const void* k, const void* v, void* o, void* o_res,
+                         float* lse, int B, int H, int Hkv, int Nq, int Nk, int d, int causal,
+                         float scale, hipStream_t stream) {
+    if (!o_res && B > 0 && H > 0 && Nq > 0) return FA_ERR_INVALID_ARG;
+    return fwd_bf16(q, k, v, o, o_res, lse, B, H, Hkv, Nq, Nk, d, causal, scale, stream);
 }
 
 fa_status_t fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -126,16 +149,15 @@ fa_status_t fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, flo
     return fa::launch_fwd_fp8(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-fa_status_t fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, void* o_res,
-                       float* lse, int B, int H, int Hkv, int N, int d, int causal, float scale,
+fa_status_t fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int B, int H, int Hkv, int N, int d, int causal, float scale,
                        hipStream_t stream) {
-    return fa_fwd_rect(q, k, v, o, o_res, lse, B, H, Hkv, N, N, d, causal, scale, stream);
+    return fa_fwd_rect(q, k, v, o, lse, B, H, Hkv, N, N, d, causal, scale, stream);
 }
 
-fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, void* o_res,
-                   float* lse, int B, int H, int N, int d, int causal, float scale,
-                   hipStream_t stream) {
-    return fa_fwd_gqa(q, k, v, o, o_res, lse, B, H, H, N, d, causal, scale, stream);
+fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int N, int d, int causal, float scale, hipStream_t stream) {
+    return fa_fwd_gqa(q, k, v, o, lse, B, H, H, N, d, causal, scale, stream);
 }
 
 fa_status_t fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
@@ -246,11 +268,16 @@ fa_status_t fa_bwd_dkdv(const void* q, const void* k, const void* v, const void*
     return fa::launch_bwd_dkdv(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-fa_status_t fa_bwd_rect(const void* q, const void* k, const void* v, const void* o,
-                        const void* o_res, const void* dout, const float* lse, void* dq,
-                        void* dk, void* dv, void* workspace, size_t workspace_bytes, int B,
-                        int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
-                        hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The backward of every entry point; with o_res, D comes from O and its
+// residual in the preprocess.
+fa_status_t bwd_bf16(const void* q, const void* k, const void* v, const void* o,
+                     const void* o_res, const void* dout, const float* lse, void* dq, void* dk,
+                     void* dv, void* workspace, size_t workspace_bytes, int B, int H, int Hkv,
+                     int Nq, int Nk, int d, int causal, float scale, hipStream_t stream) {
     bool empty = false;
     FA_TRY(check_bwd({q, k, v, o, dout, dq, dk, dv}, true, lse, workspace, workspace_bytes, B, H,
                      Hkv, Nq, Nk, d, scale, &empty));
@@ -264,20 +291,42 @@ fa_status_t fa_bwd_rect(const void* q, const void* k, const void* v, const void*
     return FA_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+fa_status_t fa_bwd_rect(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        void* workspace, size_t workspace_bytes, int B, int H, int Hkv, int Nq,
+                        int Nk, int d, int causal, float scale, hipStream_t stream) {
+    return bwd_bf16(q, k, v, o, nullptr, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H,
+                    Hkv, Nq, Nk, d, causal, scale, stream);
+}
+
+fa_status_t fa_bwd_train(const void* q, const void* k, const void* v, const void* o,
+                         const void* o_res, const void* dout, const float* lse, void* dq,
+                         void* dk, void* dv, void* workspace, size_t workspace_bytes, int B,
+                         int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                         hipStream_t stream) {
+    if (!o_res && B > 0 && H > 0 && (Nq > 0 || Nk > 0)) return FA_ERR_INVALID_ARG;
+    return bwd_bf16(q, k, v, o, o_res, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H,
+                    Hkv, Nq, Nk, d, causal, scale, stream);
+}
+
 fa_status_t fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o,
-                       const void* o_res, const void* dout, const float* lse, void* dq, void* dk,
-                       void* dv, void* workspace, size_t workspace_bytes, int B, int H, int Hkv,
-                       int N, int d, int causal, float scale, hipStream_t stream) {
-    return fa_bwd_rect(q, k, v, o, o_res, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H,
-                       Hkv, N, N, d, causal, scale, stream);
+                       const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                       void* workspace, size_t workspace_bytes, int B, int H, int Hkv, int N,
+                       int d, int causal, float scale, hipStream_t stream) {
+    return fa_bwd_rect(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, Hkv,
+                       N, N, d, causal, scale, stream);
 }
 
 fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o,
-                   const void* o_res, const void* dout, const float* lse, void* dq, void* dk,
-                   void* dv, void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                   void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
                    int causal, float scale, hipStream_t stream) {
-    return fa_bwd_gqa(q, k, v, o, o_res, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H,
-                      H, N, d, causal, scale, stream);
+    return fa_bwd_gqa(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, H, N,
+                      d, causal, scale, stream);
 }
 
 size_t fa_decode_workspace_size(int B, int H, int Hkv, int Nq, int Nk, int d) {

@@ -76,12 +76,6 @@ const char* fa_status_str(fa_status_t status);
  *   q, k, v  (in)  bf16 [B][H][N][d].
  *   o        (out) bf16 [B][H][N][d]: O = P V with P = softmax(scale Q K^T)
  *                  (masked when causal), rounded to nearest even once.
- *   o_res    (out, optional) bf16 [B][H][N][d] or NULL: the rounding
- *                  residual of o, o_res = bf16(O - o) with O the fp32 value
- *                  that o rounds. o + o_res carries O to about 16 significant
- *                  bits; the backward uses it to form D_i = dO_i . O_i
- *                  without the error of o's rounding (see fa_bwd). Like lse it
- *                  is an O(N) side output of the forward for training.
  *   lse      (out) fp32 [B][H][N]: natural-log logsumexp of the scaled,
  *                  masked logits of each query row, ln sum_j exp(scale q_i.k_j);
  *                  the backward consumes it.
@@ -96,23 +90,23 @@ const char* fa_status_str(fa_status_t status);
  * operand and give non-finite output); at d = 256 P V takes bf16 operands
  * and any finite v is allowed.
  */
-fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, void* o_res,
-                   float* lse, int B, int H, int N, int d, int causal, float scale,
+fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int N, int d, int causal, float scale,
                    hipStream_t stream);
 
 /*
  * Forward with shared K/V heads (multi-query and grouped-query attention; the
  * "FlashAttention" page, systems-analysis.ru, section "FlashAttention-2
  * (2023)", names multi-query attention among the extensions).
- *   q, o     bf16 [B][H][N][d], o_res (optional) and lse as for fa_fwd.
+ *   q, o     bf16 [B][H][N][d], lse fp32 [B][H][N], as for fa_fwd.
  *   k, v     bf16 [B][Hkv][N][d]: Hkv K/V heads, Hkv >= 1 dividing H.
  * Query head h attends with K/V head h / (H / Hkv): consecutive groups of
  * H / Hkv query heads share one K/V head (Hkv == 1 is multi-query attention,
  * Hkv == H is fa_fwd). Hkv < 1 or not dividing H -> FA_ERR_INVALID_ARG.
  * Everything else as for fa_fwd.
  */
-fa_status_t fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, void* o_res,
-                       float* lse, int B, int H, int Hkv, int N, int d, int causal, float scale,
+fa_status_t fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int B, int H, int Hkv, int N, int d, int causal, float scale,
                        hipStream_t stream);
 
 /*
@@ -121,15 +115,31 @@ fa_status_t fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, voi
  * reverse). Query row i sits at sequence position Nk - Nq + i, so with
  * causal set it keeps the keys j <= Nk - Nq + i (bottom-right alignment; if
  * Nq > Nk the first Nq - Nk rows keep no key and get O = 0, lse = -inf).
- *   q, o     bf16 [B][H][Nq][d], o_res (optional) likewise, lse fp32 [B][H][Nq].
+ *   q, o     bf16 [B][H][Nq][d], lse fp32 [B][H][Nq].
  *   k, v     bf16 [B][Hkv][Nk][d], K/V heads shared as in fa_fwd_gqa.
  * Nq == Nk is fa_fwd_gqa. Nk < 0, or Nk == 0 with query rows to compute ->
  * FA_ERR_INVALID_ARG; Nk beyond 2^26 -> FA_ERR_UNSUPPORTED. Everything else
  * as for fa_fwd.
  */
-fa_status_t fa_fwd_rect(const void* q, const void* k, const void* v, void* o, void* o_res,
-                        float* lse, int B, int H, int Hkv, int Nq, int Nk, int d, int causal,
-                        float scale, hipStream_t stream);
+fa_status_t fa_fwd_rect(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                        hipStream_t stream);
+
+/*
+ * Forward for training: fa_fwd_rect (so also fa_fwd and fa_fwd_gqa, with
+ * Nq == Nk and Hkv == H as needed) that also stores O's rounding residual.
+ *   o_res    (out) bf16 [B][H][Nq][d]: o_res = bf16(O - o), with O the fp32
+ *            value that o rounds. o + o_res carries O to about 16 significant
+ *            bits. fa_bwd_train uses it to form D_i = dO_i . O_i without the
+ *            error of o's rounding. Like lse, it is an O(N) side output kept
+ *            for the backward. NULL with rows to compute -> FA_ERR_INVALID_ARG;
+ *            16-byte aligned.
+ * o and lse are bit for bit those of fa_fwd_rect. Everything else as for
+ * fa_fwd_rect.
+ */
+fa_status_t fa_fwd_train(const void* q, const void* k, const void* v, void* o, void* o_res,
+                         float* lse, int B, int H, int Hkv, int Nq, int Nk, int d, int causal,
+                         float scale, hipStream_t stream);
 
 /*
  * Forward with 8-bit floating-point operands (the FP8 arithmetic that the
@@ -180,16 +190,15 @@ size_t fa_bwd_gqa_workspace_size(int B, int H, int Hkv, int N, int d);
  * Backward, bfloat16 storage: the gradients of the scalar
  * L = sum_{b,h,i,c} O_bhic dO_bhic with respect to q, k and v.
  *   q, k, v   (in)  bf16 [B][H][N][d], the forward inputs.
- *   o         (in)  bf16 [B][H][N][d], the forward output.
- *   o_res     (in, optional) bf16 [B][H][N][d], the forward's o_res, or NULL.
- *             D_i = sum_j P_ij dP_ij = dO_i . O_i is needed for every dS.
- *             With o_res, D_i = dO_i . (o_i + o_res_i) is formed in the
- *             preprocess and the dQ pass runs three products per score. With
- *             NULL the bf16 o alone would move D too far (its rounding error
- *             times |dO| reaches the 1e-2 scale of the gradients), so only a
- *             centre D^_i = dO_i . o_i is taken from it and the dQ pass forms
- *             D exactly from P and dP = dO V^T (a fourth product per score:
- *             the correction -(D - D^) sum_j P_ij k_j).
+ *   o         (in)  bf16 [B][H][N][d], the forward output. D_i = sum_j P_ij
+ *                   dP_ij = dO_i . O_i is needed for every dS, and the bf16 o
+ *                   alone would move it too far (its rounding error times |dO|
+ *                   reaches the 1e-2 scale of the gradients). So only a centre
+ *                   D^_i = dO_i . o_i is taken from o, and the dQ pass forms D
+ *                   exactly from P and dP = dO V^T (a fourth product per
+ *                   score: the correction -(D - D^) sum_j P_ij k_j).
+ *                   fa_bwd_train, given the forward's rounding residual of o,
+ *                   forms D in the preprocess instead.
  *   dout      (in)  bf16 [B][H][N][d], dL/dO.
  *   lse       (in)  fp32 [B][H][N], the forward's logsumexp.
  *   dq,dk,dv  (out) bf16 [B][H][N][d].
@@ -198,16 +207,15 @@ size_t fa_bwd_gqa_workspace_size(int B, int H, int Hkv, int N, int d);
  *             contents on entry do not matter and are overwritten.
  * P = exp(scale Q K^T - lse) is recomputed, never stored. The products that
  * form dQ, dK and dV take fp16 operands: P, dS = P * (dP - D) for dK, and
- * P * (dP - D) for dQ (P * (dP - D^) plus the correction when o_res is
- * NULL), against q, k, dout multiplied by per-head powers of two; fp32
- * accumulation.
+ * P * (dP - D^) for dQ (with the exact correction), against q, k, dout
+ * multiplied by per-head powers of two; fp32 accumulation.
  * The result is deterministic: no floating-point atomics are used, so
  * repeated calls give identical bits. causal and scale must match the
  * forward call. The inputs must be finite.
  */
 fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o,
-                   const void* o_res, const void* dout, const float* lse, void* dq, void* dk,
-                   void* dv, void* workspace, size_t workspace_bytes,
+                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                   void* workspace, size_t workspace_bytes,
                    int B, int H, int N, int d, int causal, float scale,
                    hipStream_t stream);
 
@@ -221,16 +229,15 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o,
  * fa_bwd; fa_bwd is this with Hkv == H.
  */
 fa_status_t fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o,
-                       const void* o_res, const void* dout, const float* lse, void* dq,
-                       void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                       const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                       void* workspace, size_t workspace_bytes,
                        int B, int H, int Hkv, int N, int d, int causal, float scale,
                        hipStream_t stream);
 
 /*
  * Backward of fa_fwd_rect: Nq query rows against Nk keys per head, query row
  * i at sequence position Nk - Nq + i (causal: bottom-right alignment).
- *   q, o, dout, dq  bf16 [B][H][Nq][d], o_res (optional) likewise, as for
- *                   fa_bwd; lse fp32 [B][H][Nq], fa_fwd_rect's
+ *   q, o, dout, dq  bf16 [B][H][Nq][d]; lse fp32 [B][H][Nq], fa_fwd_rect's
  *                   (rows that keep no key have lse = -inf and get dq = 0).
  *   k, v, dk, dv    bf16 [B][Hkv][Nk][d]; dk and dv of a K/V head sum over
  *                   its query heads as in fa_bwd_gqa.
@@ -246,10 +253,27 @@ fa_status_t fa_bwd_gqa(const void* q, const void* k, const void* v, const void* 
 size_t fa_bwd_rect_workspace_size(int B, int H, int Hkv, int Nq, int Nk, int d);
 
 fa_status_t fa_bwd_rect(const void* q, const void* k, const void* v, const void* o,
-                        const void* o_res, const void* dout, const float* lse, void* dq,
-                        void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        void* workspace, size_t workspace_bytes,
                         int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                         hipStream_t stream);
+
+/*
+ * Backward for training: fa_bwd_rect given the forward's rounding residual of
+ * o (fa_fwd_train's o_res, bf16 [B][H][Nq][d], 16-byte aligned; NULL with
+ * rows or keys to compute -> FA_ERR_INVALID_ARG). D_i = dO_i . (o_i + o_res_i)
+ * is formed in the preprocess, where o + o_res is exact in fp32, and the dQ
+ * pass takes it from there: dQ = scale sum_j P_ij (dP_ij - D_i) k_j, three
+ * products per score instead of four. Same gradients within the same
+ * tolerances as fa_bwd_rect (not the same bits), same workspace
+ * (fa_bwd_rect_workspace_size), same determinism. Everything else as for
+ * fa_bwd_rect.
+ */
+fa_status_t fa_bwd_train(const void* q, const void* k, const void* v, const void* o,
+                         const void* o_res, const void* dout, const float* lse, void* dq,
+                         void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                         int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                         hipStream_t stream);
 
 /*
  * Decoding: attention of the last Nq positions of a sequence against all of
@@ -302,10 +326,12 @@ fa_status_t fa_decode_noalloc(const void* q, const void* k, const void* v, void*
 
 /*
  * The three phases of fa_bwd, for callers that schedule or time them
- * separately. fa_bwd(...) is exactly fa_bwd_preprocess, fa_bwd_dq and
- * fa_bwd_dkdv, in this order, on one stream; each phase reads what the
- * previous ones left in the workspace, so they must run in this order.
- * Arguments mean what they mean for fa_bwd.
+ * separately. fa_bwd(...) is exactly fa_bwd_preprocess (o_res NULL),
+ * fa_bwd_dq (d_ready 0) and fa_bwd_dkdv, in this order, on one stream;
+ * fa_bwd_train with Nq == Nk and Hkv == H is the same with o_res given and
+ * d_ready 1. Each phase reads what the previous ones left in the workspace,
+ * so they must run in this order. Arguments mean what they mean for fa_bwd
+ * and fa_bwd_train.
  *   fa_bwd_preprocess  per-head largest magnitudes of q, k, v, dout, the
  *                      power-of-two factors derived from them, dout_i . o_i
  *                      per query row (o_i + o_res_i when o_res is given), and

@@ -82,11 +82,8 @@ A = 0x100000          # 16-byte aligned
 MIS = 0x100008        # 8-byte aligned only
 
 
-def fwd(lib, entry, q=A, k=A, v=A, o=A, lse=A, B=1, H=1, N=64, d=64, causal=0, scale=0.125,
-        o_res=None):
-    # the bf16 forward takes the optional o_res after o
-    res = () if entry == "fa_fwd_f32" else (o_res,)
-    return getattr(lib, entry)(q, k, v, o, *res, lse, B, H, N, d, causal, scale, None)
+def fwd(lib, entry, q=A, k=A, v=A, o=A, lse=A, B=1, H=1, N=64, d=64, causal=0, scale=0.125):
+    return getattr(lib, entry)(q, k, v, o, lse, B, H, N, d, causal, scale, None)
 
 
 @pytest.mark.parametrize("entry", ["fa_fwd", "fa_fwd_f32"])
@@ -107,8 +104,6 @@ def test_forward_rejects_bad_arguments(lib, entry):
         assert fwd(lib, entry, d=256) == UNSUPPORTED     # d = 256: bf16 forward only
     assert fwd(lib, entry, q=MIS) == UNSUPPORTED
     assert fwd(lib, entry, o=MIS) == UNSUPPORTED
-    if entry == "fa_fwd":
-        assert fwd(lib, entry, o_res=MIS) == UNSUPPORTED
     assert fwd(lib, entry, lse=A + 2) == UNSUPPORTED
     assert fwd(lib, entry, N=(1 << 26) + 1) == UNSUPPORTED
     assert fwd(lib, entry, B=1 << 16, H=1 << 16, N=64) == UNSUPPORTED
@@ -123,12 +118,12 @@ def test_forward_empty_problem_is_a_no_op(lib, entry):
 
 
 def bwd(lib, ws=0x200000, ws_bytes=None, B=1, H=2, N=100, d=128, **ptrs):
-    p = dict(q=A, k=A, v=A, o=A, o_res=None, do=A, lse=A, dq=A, dk=A, dv=A)
+    p = dict(q=A, k=A, v=A, o=A, do=A, lse=A, dq=A, dk=A, dv=A)
     p.update(ptrs)
     if ws_bytes is None:
         ws_bytes = lib.fa_bwd_workspace_size(B, H, N, d)
-    return lib.fa_bwd(p["q"], p["k"], p["v"], p["o"], p["o_res"], p["do"], p["lse"], p["dq"],
-                      p["dk"], p["dv"], ws, ws_bytes, B, H, N, d, 1, 0.088, None)
+    return lib.fa_bwd(p["q"], p["k"], p["v"], p["o"], p["do"], p["lse"], p["dq"], p["dk"],
+                      p["dv"], ws, ws_bytes, B, H, N, d, 1, 0.088, None)
 
 
 def test_backward_rejects_bad_arguments(lib):
@@ -137,7 +132,6 @@ def test_backward_rejects_bad_arguments(lib):
     assert bwd(lib, H=-2) == INVALID
     assert bwd(lib, d=32) == UNSUPPORTED
     assert bwd(lib, dk=MIS) == UNSUPPORTED
-    assert bwd(lib, o_res=MIS) == UNSUPPORTED
     assert bwd(lib, ws=None) == WORKSPACE
     assert bwd(lib, ws=MIS) == WORKSPACE
     assert bwd(lib, ws=0x200000 + 128) == WORKSPACE
@@ -148,14 +142,14 @@ def test_backward_rejects_bad_arguments(lib):
 def test_grouped_heads_arguments(lib):
     """fa_fwd_gqa / fa_bwd_gqa: Hkv must be >= 1 and divide H."""
     def f(Hkv, H=4, **kw):
-        return lib.fa_fwd_gqa(A, A, A, A, None, A, 1, H, Hkv, 64, 64, 0, 0.125, None)
+        return lib.fa_fwd_gqa(A, A, A, A, A, 1, H, Hkv, 64, 64, 0, 0.125, None)
     assert f(0) == INVALID
     assert f(-1) == INVALID
     assert f(3) == INVALID
     assert f(8) == INVALID
-    assert lib.fa_fwd_gqa(None, A, A, A, None, A, 1, 4, 2, 64, 64, 0, 0.125, None) == INVALID
-    assert lib.fa_fwd_gqa(A, A, A, A, None, A, 1, 4, 2, 64, 96, 0, 0.125, None) == UNSUPPORTED
-    assert lib.fa_fwd_gqa(A, A, A, A, None, A, 0, 4, 2, 64, 64, 0, 0.125, None) == OK
+    assert lib.fa_fwd_gqa(None, A, A, A, A, 1, 4, 2, 64, 64, 0, 0.125, None) == INVALID
+    assert lib.fa_fwd_gqa(A, A, A, A, A, 1, 4, 2, 64, 96, 0, 0.125, None) == UNSUPPORTED
+    assert lib.fa_fwd_gqa(A, A, A, A, A, 0, 4, 2, 64, 64, 0, 0.125, None) == OK
     assert lib.fa_bwd_gqa_workspace_size(2, 32, 8, 4096, 128) > 0
     # d = 256: twice the images of d = 128 (one per 128-column part)
     assert lib.fa_bwd_gqa_workspace_size(2, 32, 8, 4096, 256) > \
@@ -170,8 +164,8 @@ def test_grouped_heads_arguments(lib):
     ws = lib.fa_bwd_gqa_workspace_size(1, 4, 2, 100, 128)
 
     def b(Hkv=2, ws_bytes=ws, **kw):
-        return lib.fa_bwd_gqa(A, A, A, A, None, A, A, A, A, A, 0x200000, ws_bytes, 1, 4, Hkv,
-                              100, 128, 1, 0.088, None)
+        return lib.fa_bwd_gqa(A, A, A, A, A, A, A, A, A, 0x200000, ws_bytes, 1, 4, Hkv, 100, 128,
+                              1, 0.088, None)
     assert b(Hkv=3) == INVALID
     assert b(Hkv=0) == INVALID
     assert b(ws_bytes=ws - 1) == WORKSPACE
@@ -223,7 +217,7 @@ def test_decode_noalloc_arguments(lib):
 
 def test_rect_forward_arguments(lib):
     def f(B=1, H=2, Hkv=1, Nq=100, Nk=300, d=128, q=A, scale=0.1):
-        return lib.fa_fwd_rect(q, A, A, A, None, A, B, H, Hkv, Nq, Nk, d, 1, scale, None)
+        return lib.fa_fwd_rect(q, A, A, A, A, B, H, Hkv, Nq, Nk, d, 1, scale, None)
     assert f(Nk=-1) == INVALID
     assert f(Nk=0) == INVALID
     assert f(Hkv=3) == INVALID
@@ -251,8 +245,8 @@ def test_rect_backward_arguments(lib):
     assert lib.fa_bwd_rect_workspace_size(1, 4, 2, 100, 300, 512) == 0
 
     def b(B=1, H=4, Hkv=2, Nq=100, Nk=300, d=128, ws_bytes=ws, wsp=0x200000, dk=A):
-        return lib.fa_bwd_rect(A, A, A, A, None, A, A, A, dk, A, wsp, ws_bytes, B, H, Hkv, Nq,
-                               Nk, d, 1, 0.088, None)
+        return lib.fa_bwd_rect(A, A, A, A, A, A, A, dk, A, wsp, ws_bytes, B, H, Hkv, Nq, Nk, d,
+                               1, 0.088, None)
     assert b(Nk=-1) == INVALID
     assert b(Nk=0) == INVALID                   # query rows but no keys
     assert b(Nq=0) == INVALID                   # keys whose gradients would be left unwritten
@@ -266,6 +260,30 @@ def test_rect_backward_arguments(lib):
     assert b(wsp=None) == WORKSPACE
     assert b(Nq=0, Nk=0, wsp=None, ws_bytes=0) == OK
     assert b(B=0, wsp=None, ws_bytes=0) == OK
+
+
+def test_training_entry_points_arguments(lib):
+    """fa_fwd_train / fa_bwd_train: fa_fwd_rect / fa_bwd_rect plus the
+    rounding residual of O, which they need (NULL is an argument error)."""
+    def f(o_res=A, q=A, B=1, H=2, Hkv=1, Nq=100, Nk=300, d=128):
+        return lib.fa_fwd_train(q, A, A, A, o_res, A, B, H, Hkv, Nq, Nk, d, 1, 0.1, None)
+    assert f(o_res=None) == INVALID
+    assert f(q=None) == INVALID
+    assert f(o_res=MIS) == UNSUPPORTED
+    assert f(Hkv=3) == INVALID
+    assert f(d=96) == UNSUPPORTED
+    assert f(o_res=None, B=0) == OK                 # nothing to compute
+    ws = lib.fa_bwd_rect_workspace_size(1, 2, 1, 100, 300, 128)
+
+    def b(o_res=A, ws_bytes=ws, wsp=0x200000, B=1, Nq=100, Nk=300, dk=A):
+        return lib.fa_bwd_train(A, A, A, A, o_res, A, A, A, dk, A, wsp, ws_bytes, B, 2, 1, Nq,
+                                Nk, 128, 1, 0.088, None)
+    assert b(o_res=None) == INVALID
+    assert b(o_res=MIS) == UNSUPPORTED
+    assert b(dk=None) == INVALID
+    assert b(ws_bytes=ws - 1) == WORKSPACE
+    assert b(Nq=0) == INVALID
+    assert b(o_res=None, B=0, wsp=None, ws_bytes=0) == OK
 
 
 def test_python_binding_refuses_without_gpu_tensors():
