@@ -340,12 +340,23 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     // ---- epilogue: deferred normalisation, logsumexp, bf16 store (and, when
     // ORes is given, the bf16 rounding residual of each stored value) --------
     const float lr = sum_with_partner32(l_rnd);
-    if (qi < N) {
-        const float inv = (lr > 0.f) ? kOScale / lr : 0.f;
+    const float inv = (lr > 0.f) ? kOScale / lr : 0.f;
+    if (qi < N && g == 0) {
         const float mc = (m_ref == kNegInf) ? 0.f : m_ref * c;
-        if (g == 0)
-            LSE[(size_t)bh * N + qi] = (lr > 0.f) ? (mc + (fast_log2(lr) - kPShift)) * kLn2 : kNegInf;
-        uint16_t* orow = O + head + (size_t)qi * D;
+        LSE[(size_t)bh * N + qi] = (lr > 0.f) ? (mc + (fast_log2(lr) - kPShift)) * kLn2 : kNegInf;
+    }
+    // O goes out through LDS: each wave writes its 32 rows into a region of the
+    // K/V buffers (16-byte chunks of a row swizzled by the row), then stores
+    // whole rows, consecutive lanes taking consecutive 16-byte chunks. Every
+    // copy into the buffers has landed and every read of them is done first.
+    wait_vmem();
+    wait_lds();
+    __syncthreads();
+    constexpr int RB = D * 2;              // bytes per row
+    constexpr int CH = RB / 16;            // 16-byte chunks per row
+    lds_char* region = ((wave >> 1) == 0 ? Kb(0) : (wave >> 1) == 1 ? Kb(1)
+                        : (wave >> 1) == 2 ? Vb(0) : Vb(1)) + (wave & 1) * 32 * RB;
+    auto put = [&](bool residual) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -356,15 +367,31 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 u32x2_t w;
                 w[0] = pack_bf16x2(x[0], x[1]);
                 w[1] = pack_bf16x2(x[2], x[3]);
-                const size_t col = 32 * nb + 8 * q4 + 4 * g;
-                *(u32x2_t*)(orow + col) = w;
-                if (ORes != nullptr) {
-                    u32x2_t r;
-                    r[0] = pack_bf16x2_residual(x[0], x[1], w[0]);
-                    r[1] = pack_bf16x2_residual(x[2], x[3], w[1]);
-                    *(u32x2_t*)(ORes + head + (size_t)qi * D + col) = r;
+                if (residual) {
+                    w[0] = pack_bf16x2_residual(x[0], x[1], w[0]);
+                    w[1] = pack_bf16x2_residual(x[2], x[3], w[1]);
                 }
+                const int ch = 4 * nb + q4;    // columns 32 nb + 8 q4 .. +7
+                *(__attribute__((address_space(3))) u32x2_t*)(
+                    region + l32 * RB + ((ch ^ (l32 & (CH - 1))) * 16) + 8 * g) = w;
             }
+    };
+    auto out = [&](uint16_t* __restrict__ dst) {
+        wait_lds();
+#pragma unroll
+        for (int i = 0; i < 32 * CH / 64; ++i) {
+            const int idx = i * 64 + lane, row = idx / CH, ch = idx % CH;
+            const u32x4_t v = *(const __attribute__((address_space(3))) u32x4_t*)(
+                region + row * RB + ((ch ^ (row & (CH - 1))) * 16));
+            if (wq0 + row < N) *(u32x4_t*)(dst + head + (size_t)(wq0 + row) * D + 8 * ch) = v;
+        }
+    };
+    put(false);
+    out(O);
+    if (ORes != nullptr) {
+        wait_lds();
+        put(true);
+        out(ORes);
     }
 }
 
