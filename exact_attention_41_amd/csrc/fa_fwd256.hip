@@ -337,12 +337,23 @@ fwd_d256_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     for (int nb = 0; nb < NB; ++nb) agpr_settle(acc_o[nb]);
     const float l = sum_with_partner32(l_run);
     const float lr = sum_with_partner32(l_rnd);
-    if (qi < N) {
-        const float inv = (lr > 0.f) ? 1.f / lr : 0.f;
+    const float inv = (lr > 0.f) ? 1.f / lr : 0.f;
+    if (qi < N && g == 0) {
         const float mc = (m_ref == kNegInf) ? 0.f : m_ref * c;
-        if (g == 0)
-            LSE[(size_t)bh * N + qi] = (l > 0.f) ? (mc + fast_log2(l)) * kLn2 : kNegInf;
-        uint16_t* orow = O + head + (size_t)qi * D;
+        LSE[(size_t)bh * N + qi] = (l > 0.f) ? (mc + fast_log2(l)) * kLn2 : kNegInf;
+    }
+    // O goes out through LDS: each wave writes its 32 rows (16 KiB) into its
+    // quarter of the first 64 KiB (16-byte chunks of a row swizzled by the
+    // row), then stores whole rows, consecutive lanes taking consecutive
+    // 16-byte chunks. Every copy into the buffers (the last K staging reaches
+    // past the final tile) has landed and every read of them is done first.
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    __syncthreads();
+    constexpr int RB = D * 2;              // bytes per row
+    constexpr int CH = RB / 16;            // 16-byte chunks per row
+    lds_char* const region = s0 + wave * 32 * RB;
+    auto put = [&](bool residual) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -353,15 +364,31 @@ fwd_d256_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 u32x2_t w;
                 w[0] = pack_bf16x2(x[0], x[1]);
                 w[1] = pack_bf16x2(x[2], x[3]);
-                const size_t col = 32 * nb + 8 * q4 + 4 * g;
-                *(u32x2_t*)(orow + col) = w;
-                if (ORes != nullptr) {
-                    u32x2_t r;
-                    r[0] = pack_bf16x2_residual(x[0], x[1], w[0]);
-                    r[1] = pack_bf16x2_residual(x[2], x[3], w[1]);
-                    *(u32x2_t*)(ORes + head + (size_t)qi * D + col) = r;
+                if (residual) {
+                    w[0] = pack_bf16x2_residual(x[0], x[1], w[0]);
+                    w[1] = pack_bf16x2_residual(x[2], x[3], w[1]);
                 }
+                const int ch = 4 * nb + q4;    // columns 32 nb + 8 q4 .. +7
+                *(__attribute__((address_space(3))) u32x2_t*)(
+                    region + l32 * RB + ((ch ^ (l32 & (CH - 1))) * 16) + 8 * g) = w;
             }
+    };
+    auto out = [&](uint16_t* __restrict__ dst) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+#pragma unroll
+        for (int i = 0; i < 32 * CH / 64; ++i) {
+            const int idx = i * 64 + lane, row = idx / CH, ch = idx % CH;
+            const u32x4_t v = *(const __attribute__((address_space(3))) u32x4_t*)(
+                region + row * RB + ((ch ^ (row & (CH - 1))) * 16));
+            if (wq0 + row < N) *(u32x4_t*)(dst + head + (size_t)(wq0 + row) * D + 8 * ch) = v;
+        }
+    };
+    put(false);
+    out(O);
+    if (ORes != nullptr) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        put(true);
+        out(ORes);
     }
 }
 
