@@ -272,17 +272,25 @@ struct Tile64 {
     }
 };
 
+// The d = 256 images of Q and dO hold each 32-row half of a 64-row tile as a
+// [256][32] block of its own (64-byte rows of four 16-byte chunks): chunk c of
+// row n (rows 8c .. 8c+7 of the half) sits at chunk c ^ ((n >> 2) & 3), so
+// that 16 consecutive rows reading one chunk cover every bank once.
+__device__ __forceinline__ int img32_offset(int n, int c) { return 64 * n + 16 * (c ^ ((n >> 2) & 3)); }
+
 
 // Phase 1c: fp16 transposed images. One workgroup per (head, 64-row tile,
 // column part): the first BH*Tq tiles are the Q images of the query heads,
 // the next BH*Tq the dO images, the last BHkv*Tk the K images of the K/V
 // heads. A head size DT above 128 is cut into NP = DT/128 parts of 128
 // columns, each imaged on its own ([tile][part] order), as the passes below
-// stage them. For head sizes up to 128, bit 0 of `natural` keeps the rows of
-// the Q and dO images in their own order (for the dK/dV pass with 64 keys
-// per wave, which reads eight consecutive query rows per lane) and bit 1
-// those of the K images (for the dQ pass with 256-row workgroups); every
-// other image uses the permuted row order.
+// stage them. Bit 0 of `natural` is set when the dK/dV pass is the one with
+// 16-row steps (bwd_dkdv16_kernel), which reads eight consecutive query rows
+// per lane: for head sizes up to 128 it keeps the rows of the Q and dO images
+// in their own order, and at d = 256 it writes them as the [256][32] halves
+// of img32_offset. Bit 1 does the same for the K images when the dQ pass is
+// the one with 16-row steps (bwd_dq16_kernel). Every other image uses the
+// permuted row order.
 template <int DT>
 __global__ void __launch_bounds__(256)
 bwd_image_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -307,10 +315,27 @@ bwd_image_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     __shared__ __attribute__((aligned(16))) char img[TileT::BYTES];
     TileT tl;
     tl.load(src + (size_t)head * N * DT + part * D, tile * 64, N, threadIdx.x);
-    if (DT <= 128 && (natural & (which < 2 ? 1 : 2)))
+    // (d = 256: Q and dO in the half-tile layout of img32_offset)
+    const bool halves = DT > 128 && (natural & (which < 2 ? 1 : 2));
+    if (halves || (DT <= 128 && (natural & (which < 2 ? 1 : 2))))
         tl.template store_transposed<true, true>(img, threadIdx.x, s);
     else tl.template store_transposed<true, false>(img, threadIdx.x, s);
     __syncthreads();
+    if (DT > 128 && halves) {
+        // rows 128 part .. +127 of the tile's two [256][32] halves: 16-byte
+        // chunk position cc of row n of half h holds chunk c = cc ^ ((n >> 2)
+        // & 3), i.e. rows 32 h + 8 c .. +7 of the transposed part
+        static_assert(DT <= 128 || TileT::BYTES == 16384, "two halves of 128 rows x 32 per part");
+        char* out = dst + ((size_t)head * T + tile) * NP * TileT::BYTES;
+#pragma unroll
+        for (int i = threadIdx.x; i < TileT::BYTES / 16; i += 256) {
+            const int h = i >> 9, n = (i >> 2) & 127, cc = i & 3;
+            const int c = cc ^ ((n >> 2) & 3);
+            *(u32x4_t*)(out + h * TileT::BYTES + img32_offset(128 * part + n, c)) =
+                *(const u32x4_t*)(img + tr_slot_offset(n, 8 * h + 2 * c));
+        }
+        return;
+    }
     char* out = dst + (((size_t)head * T + tile) * NP + part) * TileT::BYTES;
 #pragma unroll
     for (int i = threadIdx.x; i < TileT::BYTES / 16; i += 256)
@@ -1005,12 +1030,21 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
 }
 
+// Waves of the pass below: one per SIMD with 64 keys per wave or at d = 256,
+// two per SIMD with 32 keys per wave at d <= 128.
+constexpr int dkdv16_waves(int D, int KW) { return D == 256 ? 4 : 256 / KW; }
+
 // ---------------------------------------------------------------------------
-// Phase 3 for head sizes 64 and 128: dK, dV with KW = 64 keys per wave (4
-// waves, one per SIMD) or 32 (8 waves, two per SIMD). One workgroup per block
-// of 256 keys; it walks the query tiles (64 rows) that see them, each as four
-// steps of 16 query rows, so every LDS fragment feeds several products (the
-// 32-key form above reads a fresh fragment for each):
+// Phase 3 with 16-row steps: dK, dV. For head sizes 64 and 128, KW = 64 keys
+// per wave (4 waves, one per SIMD) or 32 (8 waves, two per SIMD), one
+// workgroup per block of 256 keys, query tiles of 64 rows (four steps). At
+// d = 256, 32 keys per wave (4 waves, one per SIMD: the dK and dV sums of all
+// 256 columns take the 256 AGPRs, the resident K and V 128 VGPRs), one
+// workgroup per block of 128 keys, query tiles of 32 rows (two steps, so that
+// a tile's rows and images, 64 KiB, are double-buffered in LDS): S and dP are
+// formed once for all 256 columns of dK and dV. Each workgroup walks the
+// query tiles that see its keys in 16-row steps, so every LDS fragment feeds
+// several products (the 32-key form above reads a fresh fragment for each):
 //   S, dP (16 queries x KW keys): v_mfma_f32_16x16x32_bf16, A = a 16-row
 //     slice of the Q (dO) tile from LDS, read once for the KW/16 key blocks;
 //     B = K^T (V^T), resident in VGPRs. Accumulator lane l: key 16j + l%16,
@@ -1027,20 +1061,22 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 // barrier per tile.
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL, int KW>
-__global__ void __launch_bounds__(256 / KW * 64, 1)
+__global__ void __launch_bounds__(dkdv16_waves(D, KW) * 64, 1)
 bwd_dkdv16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                   const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                   const float* __restrict__ scales, const float* __restrict__ stats,
                   const char* __restrict__ qt_img, const char* __restrict__ ot_img,
                   uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int BHkv, int G, int N,
                   int Nk, int T, float c, float scale) {
-    static_assert(D == 64 || D == 128, "the dK, dV sums and resident K, V fit up to d = 128");
+    static_assert(D == 64 || D == 128 || (D == 256 && KW == 32),
+                  "the dK, dV sums and the resident K, V of a wave fit its registers");
     static_assert(KW == 64 || KW == 32, "keys per wave");
-    constexpr int NW = 256 / KW;         // waves: 4 (one per SIMD) or 8 (two per SIMD)
+    constexpr int NW = dkdv16_waves(D, KW);   // 4 (one per SIMD) or 8 (two per SIMD)
     constexpr int NJ = KW / 16;          // 16-key blocks of a wave
     constexpr int NH = KW / 32;          // 32-key blocks of a wave
-    constexpr int BQ = 64;               // query rows per tile
-    constexpr int BKV = 256;             // keys per workgroup
+    constexpr int BQ = D == 256 ? 32 : 64;    // query rows per tile
+    constexpr int NSTEP = BQ / 16;       // 16-row steps per tile
+    constexpr int BKV = NW * KW;         // keys per workgroup
     constexpr int KC = D / 32;           // 32-wide contraction chunks of S and dP
     constexpr int NB = D / 32;           // 32-wide row blocks of dV^T and dK^T
     constexpr int TB = BQ * D * 2;       // bytes of one tile (rows or image)
@@ -1118,13 +1154,14 @@ bwd_dkdv16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
                                          base + (tensor == 0 ? OFF_Q : OFF_DO), (int)ti * BQ, N,
                                          blk, lane);
         else
-            stage_image_block_full_async((tensor == 2 ? qt_img : ot_img) + (qh * T + ti) * TB,
+            stage_image_block_full_async((tensor == 2 ? qt_img : ot_img) + (qh * (T * 64 / BQ) + ti) * TB,
                                          base + (tensor == 2 ? OFF_QT : OFF_DOT), blk, lane);
     };
+    // (statistics are kept per 64-row tile: a 32-row tile takes half of one)
     auto stage_stats = [&](int gq, int t, int b) {
         const size_t qh = live_head(gq, t), ti = live_tile(gq, t);
         if (wave == 0)
-            stage_image_block_async(stats + (qh * T + ti) * 128, 512,
+            stage_image_block_async(stats + (qh * T + ti * BQ / 64) * 128, 512,
                                     (lds_char*)(smem + OFF_S + b * SBUF), 0, lane);
     };
     // Query tiles run from the last down: the workgroups of one K/V head
@@ -1139,17 +1176,10 @@ bwd_dkdv16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
         }
     };
 
-    // Fragment of the row-major Q (dO) tile for step s, chunk kc: row
-    // 16 s + l16, 16-byte chunk 4 kc + q4.
-    auto frag_rm = [&](int b, int off_t, int s, int kc) -> u32x4_t {
-        return *(const lds_u32x4_t*)((lds_char*)smem + b * BUF + off_t +
-                                     row_chunk_offset<D>(16 * s + l16, 4 * kc + q4));
-    };
-    // Fragment of a transposed image for step s, row block nb: row (dim)
-    // 32 nb + l32, queries 16 s + 8 g .. +7 (16-byte chunk 2 s + g).
-    auto frag_tr = [&](int b, int off_t, int s, int nb) -> u32x4_t {
-        return *(const lds_u32x4_t*)((lds_char*)smem + b * BUF + off_t +
-                                     tr_slot_offset(32 * nb + l32, 2 * (2 * s + g)));
+    // Byte offset of 16-byte chunk c (rows 8c .. 8c+7 of the tile) of row n
+    // of a transposed image.
+    auto img_offset = [](int n, int c) -> int {
+        return D == 256 ? img32_offset(n, c) : tr_slot_offset(n, 2 * c);
     };
 
     // One query tile of group member gq, buffer b, as one fully unrolled
@@ -1173,7 +1203,7 @@ bwd_dkdv16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
     // behind a uniform branch: two copies of this code (masked and not) do
     // not fit the registers together.
     constexpr int NS = KC, NGR = 2 * NB;
-    constexpr int NOPS = 4 * (2 * NS) + 4 * NGR;
+    constexpr int NOPS = NSTEP * (2 * NS) + NSTEP * NGR;
     constexpr int LA = KW == 32 ? 1 : 2;
     // Operation o: kind (0 Q, 1 dO, 2 dO~^T, 3 Q~^T), step, chunk or block.
     struct Op { int kind, s, x; };
@@ -1181,7 +1211,7 @@ bwd_dkdv16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
         // per step s < 3: A(s) NS, B(s) NS, then grad(s-1) NGR for s >= 1;
         // finally grad(3)
         int base = 0;
-        for (int s = 0; s < 4; ++s) {
+        for (int s = 0; s < NSTEP; ++s) {
             if (o < base + NS) return Op{0, s, o - base};
             base += NS;
             if (o < base + NS) return Op{1, s, o - base};
@@ -1191,11 +1221,12 @@ bwd_dkdv16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
                 base += NGR;
             }
         }
-        return Op{2 + ((o - base) & 1), 3, (o - base) >> 1};
+        return Op{2 + ((o - base) & 1), NSTEP - 1, (o - base) >> 1};
     };
     auto tile = [&](int gq, int t, int b, bool mask_tile) {
         const int i0 = t * BQ;
-        const lds_char* st = (lds_char*)smem + OFF_S + b * SBUF;
+        // (the tile's rows within its 64-row statistics block)
+        const lds_char* st = (lds_char*)smem + OFF_S + b * SBUF + 4 * ((t * BQ) & 63);
         int ga = gq, ta = t;
         next_tile(ga, ta);
         f32x4_t sa[NJ], da[NJ];         // S then P, and dP - D, of the current step
@@ -1214,7 +1245,7 @@ bwd_dkdv16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
                 return *(const lds_u32x4_t*)(base + (op.kind == 0 ? OFF_Q : OFF_DO) +
                                              row_chunk_offset<D>(16 * op.s + l16, 4 * op.x + q4));
             return *(const lds_u32x4_t*)(base + (op.kind == 2 ? OFF_DOT : OFF_QT) +
-                                         tr_slot_offset(32 * op.x + l32, 2 * (2 * op.s + g)));
+                                         img_offset(32 * op.x + l32, 2 * op.s + g));
         };
         auto load_stats = [&](int s) {
             const f32x4_t a = *(const lds_f32x4_t*)(st + 4 * (16 * s + 4 * q4));
@@ -1305,17 +1336,17 @@ bwd_dkdv16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
                 // C(s) = grad(s-1): P, dS and packing of step s = op.s + 1, one
                 // key block's exponentials after each dO~^T operation's
                 // products and its dS after the following Q~^T operation's
-                if (op.s < 3) {
+                if (op.s < NSTEP - 1) {
                     const int sn = op.s + 1;
 #pragma unroll
                     for (int j = op.x * NJ / NB; j < (op.x + 1) * NJ / NB; ++j) {
                         if (op.kind == 2) exp_block(sn, j);
                         else ds_block(j);
                     }
-                    if (op.kind == 3 && op.x == NB - 1 && sn < 3) load_stats(sn + 1);
+                    if (op.kind == 3 && op.x == NB - 1 && sn < NSTEP - 1) load_stats(sn + 1);
                 }
-                // before grad(3): step 3's swaps (no S segment follows)
-                if (op.s == 2 && op.kind == 3 && op.x == NB - 1) {
+                // before the last step's grad: its swaps (no S segment follows)
+                if (op.s == NSTEP - 2 && op.kind == 3 && op.x == NB - 1) {
 #pragma unroll
                     for (int h = 0; h < NH; ++h) swap_block(h);
                 }
@@ -1381,13 +1412,21 @@ bwd_dkdv16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
     }
 }
 
+// Waves of the pass below: one per SIMD with 64 rows per wave or at d = 256,
+// two per SIMD with 32 rows per wave at d <= 128.
+constexpr int dq16_waves(int D, int QW) { return D == 256 ? 4 : 256 / QW; }
+
 // ---------------------------------------------------------------------------
-// Phase 2 for head sizes 64 and 128 when D is known before the pass (formed by
-// the preprocess from O and its rounding residual): dQ with QW = 64 query rows
-// per wave (4 waves, one per SIMD) or 32 (8 waves, two per SIMD), the dK/dV
-// pass above with the roles of queries and keys exchanged. One workgroup per
-// block of 256 query rows; it walks the key tiles (64 keys) its rows see, each
-// as four steps of 16 keys:
+// Phase 2 with 16-row steps, when D is known before the pass (formed by the
+// preprocess from O and its rounding residual): dQ, the dK/dV pass above with
+// the roles of queries and keys exchanged. For head sizes 64 and 128, QW = 64
+// query rows per wave (4 waves, one per SIMD) or 32 (8 waves, two per SIMD),
+// one workgroup per block of 256 query rows, key tiles of 64 keys (four
+// steps). At d = 256, 32 rows per wave (4 waves, one per SIMD), one workgroup
+// per block of 128 rows, key tiles of 32 keys (two steps, so that a tile's K
+// and V rows and its K~^T image, 48 KiB, are double-buffered in LDS): S and
+// dP are formed once for all 256 columns of dQ. Each workgroup walks the key
+// tiles its rows see in 16-key steps:
 //   S, dP (16 keys x QW queries): v_mfma_f32_16x16x32_bf16, A = a 16-row
 //     slice of the K (V) tile from LDS, read once for the QW/16 query blocks;
 //     B = Q^T ((sE dO)^T), resident in VGPRs. Accumulator lane l: query
@@ -1405,20 +1444,22 @@ bwd_dkdv16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
 // per tile. The pass also leaves lse and D per query tile for the dK/dV pass.
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL, int QW>
-__global__ void __launch_bounds__(256 / QW * 64, 1)
+__global__ void __launch_bounds__(dq16_waves(D, QW) * 64, 1)
 bwd_dq16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                 const float* __restrict__ LSE, const float* __restrict__ scales,
                 const float* __restrict__ dvals, const char* __restrict__ kt_img,
                 float* __restrict__ stats, uint16_t* __restrict__ dQ, int BH, int G, int N,
                 int Nk, int T, int Tk, float c, float scale, int nqb) {
-    static_assert(D == 64 || D == 128, "the dQ sums and resident Q, dO fit up to d = 128");
+    static_assert(D == 64 || D == 128 || (D == 256 && QW == 32),
+                  "the dQ sums and the resident Q, dO of a wave fit its registers");
     static_assert(QW == 64 || QW == 32, "query rows per wave");
-    constexpr int NW = 256 / QW;         // waves: 4 (one per SIMD) or 8 (two per SIMD)
+    constexpr int NW = dq16_waves(D, QW);     // 4 (one per SIMD) or 8 (two per SIMD)
     constexpr int NJ = QW / 16;          // 16-query blocks of a wave
     constexpr int NH = QW / 32;          // 32-query blocks of a wave
-    constexpr int BC = 64;               // keys per tile
-    constexpr int BQ = 256;              // query rows per workgroup
+    constexpr int BC = D == 256 ? 32 : 64;    // keys per tile
+    constexpr int NSTEP = BC / 16;       // 16-key steps per tile
+    constexpr int BQ = NW * QW;          // query rows per workgroup
     constexpr int KC = D / 32;           // 32-wide contraction chunks of S and dP
     constexpr int NB = D / 32;           // 32-wide row blocks of dQ^T
     constexpr int TB = BC * D * 2;       // bytes of one tile (rows or image)
@@ -1440,7 +1481,7 @@ bwd_dq16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const size_t kvhead = (size_t)(bh / G) * (size_t)Nk * D;  // K/V head of this query head
     const uint16_t* Kh = K + kvhead;
     const uint16_t* Vh = V + kvhead;
-    const char* kt_h = kt_img + (size_t)(bh / G) * Tk * TB;
+    const char* kt_h = kt_img + (size_t)(bh / G) * (Tk * 64 / BC) * TB;
     const int q0 = qb * BQ;
     const int qw0 = q0 + wave * QW;
     const int off = Nk - N;              // query row i sits at key position i + off
@@ -1523,14 +1564,14 @@ bwd_dq16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     // ring of registers that starts again at every tile. Tiles that need a
     // mask run it behind a uniform branch.
     constexpr int NS = KC, NGR = NB;
-    constexpr int NOPS = 4 * (2 * NS) + 4 * NGR;
+    constexpr int NOPS = NSTEP * (2 * NS) + NSTEP * NGR;
     constexpr int LA = 2;
     static_assert(3 + 3 * (3 * PPT - 1) < NOPS, "the next tile's copies fit in the operations");
     // Operation o: kind (0 K, 1 V, 2 K~^T), step, chunk or block.
     struct Op { int kind, s, x; };
     auto op_of = [](int o) constexpr -> Op {
         int base = 0;
-        for (int s = 0; s < 4; ++s) {
+        for (int s = 0; s < NSTEP; ++s) {
             if (o < base + NS) return Op{0, s, o - base};
             base += NS;
             if (o < base + NS) return Op{1, s, o - base};
@@ -1540,7 +1581,12 @@ bwd_dq16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 base += NGR;
             }
         }
-        return Op{2, 3, o - base};
+        return Op{2, NSTEP - 1, o - base};
+    };
+    // Byte offset of 16-byte chunk c (keys 8c .. 8c+7 of the tile) of row n of
+    // the K~^T image.
+    auto img_offset = [](int n, int c) -> int {
+        return D == 256 ? img32_offset(n, c) : tr_slot_offset(n, 2 * c);
     };
     auto tile = [&](int t, int b, bool mask_tile) {
         const int j0 = t * BC;
@@ -1558,8 +1604,7 @@ bwd_dq16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             if (op.kind < 2)
                 return *(const lds_u32x4_t*)(base + (op.kind == 0 ? OFF_K : OFF_V) +
                                              row_chunk_offset<D>(16 * op.s + l16, 4 * op.x + q4));
-            return *(const lds_u32x4_t*)(base + OFF_KT +
-                                         tr_slot_offset(32 * op.x + l32, 2 * (2 * op.s + g)));
+            return *(const lds_u32x4_t*)(base + OFF_KT + img_offset(32 * op.x + l32, 2 * op.s + g));
         };
         // P of step s, query block j (over S), then dS = P (dP - D) packed
         auto ds_block = [&](int s, int j) {
@@ -1621,12 +1666,12 @@ bwd_dq16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
                 for (int h = 0; h < NH; ++h) mfma_f16_agpr(acc[h][op.x], a, ds2[h]);
                 // C(s) = dQ(s-1): dS of step s = op.s + 1
-                if (op.s < 3) {
+                if (op.s < NSTEP - 1) {
 #pragma unroll
                     for (int j = op.x * NJ / NB; j < (op.x + 1) * NJ / NB; ++j) ds_block(op.s + 1, j);
                 }
-                // before dQ(3): step 3's swaps (no S segment follows)
-                if (op.s == 2 && op.x == NB - 1) {
+                // before the last step's dQ: its swaps (no S segment follows)
+                if (op.s == NSTEP - 2 && op.x == NB - 1) {
 #pragma unroll
                     for (int h = 0; h < NH; ++h) swap_block(h);
                 }
@@ -1697,19 +1742,25 @@ template <typename T>
 static T* ws_ptr(const BwdArgs& a, size_t off) { return (T*)((char*)a.workspace + off); }
 
 static int q_tiles64(const BwdArgs& a) { return (a.N + 63) / 64; }
-// The dK/dV pass with 256-key workgroups (bwd_dkdv16_kernel) for head sizes
-// up to 128, when its grid still has two workgroups per compute unit of an
-// MI355X; otherwise (few K/V heads or short sequences, where 256-key blocks
-// leave the longest causal block alone at the end) the 128-key pass. The
-// preprocess lays the Q and dO images out for the pass chosen here.
+// The dK/dV pass with 16-row steps (bwd_dkdv16_kernel): for head sizes up to
+// 128 (256-key workgroups) when its grid still has two workgroups per compute
+// unit of an MI355X, at d = 256 (128-key workgroups) when it has one;
+// otherwise (few K/V heads or short sequences, where large key blocks leave
+// the longest causal block alone at the end, or at d = 256 too few
+// workgroups to fill the chip without the column parts) the 128-key pass.
+// The preprocess lays the Q and dO images out for the pass chosen here.
 static bool use_dkdv16(const BwdArgs& a) {
-    return a.d <= 128 && (long long)((a.Nk + 255) / 256) * a.B * a.Hkv >= 512;
+    if (a.d == 256) return (long long)((a.Nk + 127) / 128) * a.B * a.Hkv >= 256;
+    return (long long)((a.Nk + 255) / 256) * a.B * a.Hkv >= 512;
 }
-// The dQ pass with 256-row workgroups (bwd_dq16_kernel): D known, d <= 128,
-// and at least 512 workgroups (smaller grids keep more workgroups per compute
-// unit with the 128-row pass).
+// The dQ pass with 16-row steps (bwd_dq16_kernel): D known, and for head sizes
+// up to 128 (256-row workgroups) at least 512 workgroups, at d = 256 (128-row
+// workgroups) at least 256 (smaller grids keep more workgroups per compute
+// unit with the 128-row pass, and at d = 256 its column parts).
 static bool use_dq16(const BwdArgs& a) {
-    return a.d_known && a.d <= 128 && (long long)((a.N + 255) / 256) * a.B * a.H >= 512;
+    if (!a.d_known) return false;
+    if (a.d == 256) return (long long)((a.N + 127) / 128) * a.B * a.H >= 256;
+    return (long long)((a.N + 255) / 256) * a.B * a.H >= 512;
 }
 static int k_tiles64(const BwdArgs& a) { return (a.Nk + 63) / 64; }
 // Column parts of a head (128 columns each above d = 128).
@@ -1747,13 +1798,15 @@ static hipError_t launch_dq_t(const BwdArgs& a) {
     constexpr int NW = kBwdWaves;
     const BwdWorkspace w = ws_of(a);
     const int BH = a.B * a.H;
-    if (D <= 128 && use_dq16(a)) {
-        const int nqb = (a.N + 255) / 256;
+    if (use_dq16(a)) {
         // d = 128: 32 rows per wave, two waves per SIMD (each wave's vector work
-        // can run under the other's products); d = 64: 64 rows, one wave per SIMD
-        constexpr int QW = D == 128 ? 32 : 64;
-        hipLaunchKernelGGL((bwd_dq16_kernel<(D <= 128 ? D : 128), CAUSAL, QW>), dim3(nqb * BH),
-                           dim3(256 / QW * 64), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+        // can run under the other's products); d = 64: 64 rows, one wave per
+        // SIMD; d = 256: 32 rows, one wave per SIMD
+        constexpr int QW = D == 64 ? 64 : 32;
+        constexpr int NWQ = dq16_waves(D, QW);
+        const int nqb = (a.N + NWQ * QW - 1) / (NWQ * QW);
+        hipLaunchKernelGGL((bwd_dq16_kernel<D, CAUSAL, QW>), dim3(nqb * BH),
+                           dim3(NWQ * 64), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                            (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse,
                            ws_ptr<const float>(a, w.scales), ws_ptr<const float>(a, w.dhat),
                            ws_ptr<const char>(a, w.kt), ws_ptr<float>(a, w.stats),
@@ -1777,16 +1830,17 @@ template <int D, bool CAUSAL>
 static hipError_t launch_dkdv_t(const BwdArgs& a) {
     const BwdWorkspace w = ws_of(a);
     const int BHkv = a.B * a.Hkv;
-    if (D <= 128 && use_dkdv16(a)) {
-        // 256 keys per workgroup
-        const int nkb = (a.Nk + 255) / 256;
-        // d = 64: 32 keys per wave, two waves per SIMD (each wave's vector work
-        // can run under the other's products); d = 128: 64 keys, one wave per
-        // SIMD (the dK and dV sums and the resident K and V of 32 keys, 192
-        // registers, leave too few for a second wave)
-        constexpr int KW = D == 64 ? 32 : 64;
-        hipLaunchKernelGGL((bwd_dkdv16_kernel<(D <= 128 ? D : 128), CAUSAL, KW>), dim3(nkb * BHkv),
-                           dim3(256 / KW * 64), 0,
+    if (use_dkdv16(a)) {
+        // d <= 128: 256 keys per workgroup; d = 64: 32 keys per wave, two
+        // waves per SIMD (each wave's vector work can run under the other's
+        // products); d = 128: 64 keys, one wave per SIMD (the dK and dV sums
+        // and the resident K and V of 32 keys, 192 registers, leave too few
+        // for a second wave). d = 256: 32 keys per wave, one wave per SIMD,
+        // 128 keys per workgroup, every column of dK and dV from one pass.
+        constexpr int KW = D == 128 ? 64 : 32;
+        constexpr int NW = dkdv16_waves(D, KW);
+        const int nkb = (a.Nk + NW * KW - 1) / (NW * KW);
+        hipLaunchKernelGGL((bwd_dkdv16_kernel<D, CAUSAL, KW>), dim3(nkb * BHkv), dim3(NW * 64), 0,
                            a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                            (const uint16_t*)a.v, (const uint16_t*)a.dout,
                            ws_ptr<const float>(a, w.scales), ws_ptr<const float>(a, w.stats),

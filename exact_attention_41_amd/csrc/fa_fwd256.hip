@@ -36,6 +36,15 @@ constexpr int kW256Waves = 4;
 #define FA_W256_AHEAD 4
 #endif
 constexpr int kW256Ahead = FA_W256_AHEAD;   // LDS fragment reads in flight ahead of the MFMAs
+// The P V product takes fp16 operands, as in the d = 64 / 128 forward: P as
+// fp16(2^7 P) (P <= 2^8 by the rescale rule, so 2^7 P stays in range) and V
+// as fp16(2^-8 V) (exact for 2^-6 <= |v| < 65504 * 2^8; below, an absolute
+// error of at most 2^-17); the epilogue takes both factors out again. With
+// bf16 P the output's rounding moves D = dO . O of the backward by a few
+// 1e-3 of |dO| |V| on short causal rows, enough to take dK past 1e-2.
+constexpr float kP256Shift = 7.f;
+constexpr float kV256Scale = 1.f / 256.f;
+constexpr float kO256Scale = 256.f;
 
 template <bool CAUSAL>
 __global__ void __launch_bounds__(kW256Waves * 64, 1)
@@ -109,6 +118,11 @@ fwd_d256_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         const int ch = u % DCH, rg = u / DCH;
         const int slot = tr_key_position(4 * rg) >> 2;
         const int w = e >> 1;
+        // bf16 pair -> fp16 pair of 2^-8 v, once per word (its two elements)
+        if ((e & 1) == 0) {
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) vreg[k][rr][w] = bf16x2_to_f16x2(vreg[k][rr][w], kV256Scale);
+        }
         const uint32_t r0 = vreg[k][0][w], r1 = vreg[k][1][w];
         const uint32_t r2 = vreg[k][2][w], r3 = vreg[k][3][w];
         u32x2_t col;
@@ -230,9 +244,10 @@ fwd_d256_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         u32x4_t fr[LA + 1];
 #pragma unroll
         for (int o = 0; o < LA; ++o) fr[o] = frag(o);
-        const float mc = (m_ref == kNegInf) ? 0.f : m_ref * c;
+        // exp2(s c - m_ref c + 7) = 2^7 P
+        const float mc = ((m_ref == kNegInf) ? 0.f : m_ref * c) - kP256Shift;
 
-        // Element e of P(t): key half e/16, accumulator register e%16.
+        // Element e of P(t) (times 2^7): key half e/16, accumulator register e%16.
         float pv[16];
         u32x4_t pf[4];
         auto p_elem = [&](int e) {
@@ -241,13 +256,13 @@ fwd_d256_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             l_run += pv[r];
             if ((r & 7) == 7) {
                 const int t4 = e >> 3, rb = r - 7;
-                pf[t4] = u32x4_t{pack_bf16x2(pv[rb + 0], pv[rb + 1]), pack_bf16x2(pv[rb + 2], pv[rb + 3]),
-                                 pack_bf16x2(pv[rb + 4], pv[rb + 5]), pack_bf16x2(pv[rb + 6], pv[rb + 7])};
-                // O is normalised by the sum of the bf16 probabilities that
+                pf[t4] = u32x4_t{pack_f16x2(pv[rb + 0], pv[rb + 1]), pack_f16x2(pv[rb + 2], pv[rb + 3]),
+                                 pack_f16x2(pv[rb + 4], pv[rb + 5]), pack_f16x2(pv[rb + 6], pv[rb + 7])};
+                // O is normalised by the sum of the fp16 probabilities that
                 // multiply V (the rounding error of P then scales with
                 // v_j - O); lse uses the fp32 sum.
 #pragma unroll
-                for (int w = 0; w < 4; ++w) l_rnd = add_bf16x2(pf[t4][w], l_rnd);
+                for (int w = 0; w < 4; ++w) l_rnd = add_f16x2(pf[t4][w], l_rnd);
                 // The sums are used from the next tile on: keep their
                 // computation between the products of this one.
                 keep_here(l_run);
@@ -279,7 +294,7 @@ fwd_d256_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 else if (o < KPW + 4 * VU) v_load_part(t + 1, (o - KPW) >> 2, (o - KPW) & 3);
             } else {
                 const int w = o - NS, t4 = w / NB, nb = w % NB;
-                mfma_bf16_agpr(acc_o[nb], a, pf[t4]);
+                mfma_f16_agpr(acc_o[nb], a, pf[t4]);
                 if (NEXT && (w & 1) == 0 && (w >> 1) < 8 * VU)
                     v_store_part(vdst, (w >> 1) >> 3, (w >> 1) & 7);
             }
@@ -337,10 +352,10 @@ fwd_d256_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     for (int nb = 0; nb < NB; ++nb) agpr_settle(acc_o[nb]);
     const float l = sum_with_partner32(l_run);
     const float lr = sum_with_partner32(l_rnd);
-    const float inv = (lr > 0.f) ? 1.f / lr : 0.f;
+    const float inv = (lr > 0.f) ? kO256Scale / lr : 0.f;
     if (qi < N && g == 0) {
         const float mc = (m_ref == kNegInf) ? 0.f : m_ref * c;
-        LSE[(size_t)bh * N + qi] = (l > 0.f) ? (mc + fast_log2(l)) * kLn2 : kNegInf;
+        LSE[(size_t)bh * N + qi] = (l > 0.f) ? (mc + (fast_log2(l) - kP256Shift)) * kLn2 : kNegInf;
     }
     // O goes out through LDS: each wave writes its 32 rows (16 KiB) into its
     // quarter of the first 64 KiB (16-byte chunks of a row swizzled by the

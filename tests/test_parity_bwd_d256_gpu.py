@@ -65,6 +65,29 @@ def test_d256_backward_small(fa, B, H, Hkv, Nq, Nk, causal, mode):
     check_bf16("dV", dv, rv)
 
 
+# Grids large enough for the passes with 16-row steps (at least 256
+# workgroups of 128 keys for dK/dV, of 128 query rows for dQ when D comes
+# from the residual): ragged key blocks and query tiles, shared K/V heads,
+# Nq < Nk and Nq > Nk with bottom-right causal alignment.
+LARGE_GRID = [(1, 128, 128, 300, 300), (1, 256, 128, 200, 517), (2, 64, 64, 333, 190)]
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("B,H,Hkv,Nq,Nk", LARGE_GRID)
+def test_d256_backward_large_grid(fa, B, H, Hkv, Nq, Nk, causal, mode):
+    say(f"d=256 backward (16-row-step passes) B={B} H={H} Hkv={Hkv} Nq={Nq} Nk={Nk} "
+        f"causal={causal} D from {mode} seed=95")
+    inp = wl.make_decode_inputs(B, H, Hkv, Nq, Nk, D, seed=95, with_do=True)
+    scale = float(np.float32(1 / np.sqrt(D)))
+    dq, dk, dv = _fwd_bwd(fa, inp, causal, scale, mode)
+    q64, k64, v64, do64 = inp.as_float64()
+    rq, rk, rv = ora.rect_bwd(q64, k64, v64, do64, causal, scale, workers=None)
+    check_bf16("dQ", dq, rq)
+    check_bf16("dK", dk, rk)
+    check_bf16("dV", dv, rv)
+
+
 def test_d256_backward_square_entries_agree(fa):
     """fa_bwd and fa_bwd_rect (Nq = Nk) give identical bits at d = 256, and
     repeated calls give identical bits."""
