@@ -58,6 +58,21 @@ constexpr int kDqFragAhead = FA_BWD_DQ_FRAG_AHEAD;
 #define FA_BWD_DKDV_FRAG_AHEAD 7
 #endif
 constexpr int kDkdvFragAhead = FA_BWD_DKDV_FRAG_AHEAD;
+// The dK/dV pass with 16-row steps reads fp16 rows of s_Q Q and s_dO dO and
+// takes the transposed operands of its dV, dK products from them
+// (ds_read_b64_tr_b16); 0: bf16 rows plus transposed fp16 images.
+#ifndef FA_DKDV_TR
+#define FA_DKDV_TR 1
+#endif
+// The dQ pass with 16-row steps at d = 256 reads fp16 rows of s_K K and takes
+// the transposed operand of its dQ product from them; at d <= 128 (and with
+// 0) it reads bf16 K rows plus the transposed fp16 K image. (Same-box A/B:
+// the rows at d = 256 causal 0.452 -> 0.432 ms, at d = 128 3% slower, at
+// d = 64 32% slower.)
+#ifndef FA_DQ_TR
+#define FA_DQ_TR 1
+#endif
+constexpr bool dq16_tr(int D) { return FA_DQ_TR != 0 && D == 256; }
 
 // Vector-memory wait (the global-to-LDS copies) and a workgroup barrier that
 // lets LDS reads stay in flight across it (__syncthreads waits for them). The
@@ -77,16 +92,16 @@ __device__ __forceinline__ void step_barrier() {
 // ---------------------------------------------------------------------------
 static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-int bwd_scale_chunks(long long Nq, long long Nk) {
-    const long long n = Nq > Nk ? Nq : Nk;
-    return (int)((n + kScaleRows - 1) / kScaleRows);
+int bwd_scale_chunks(long long Nq, long long Nk, long long d) {
+    const long long n = Nq > Nk ? Nq : Nk, rows = scale_chunk_rows(d);
+    return (int)((n + rows - 1) / rows);
 }
 
 BwdWorkspace bwd_workspace_layout(long long B, long long H, long long Hkv, long long Nq,
                                   long long Nk, long long d) {
     BwdWorkspace w;
     const size_t bh = (size_t)(B * H), bhkv = (size_t)(B * Hkv);
-    const size_t chunks = (size_t)bwd_scale_chunks(Nq, Nk);
+    const size_t chunks = (size_t)bwd_scale_chunks(Nq, Nk, d);
     const size_t tq = (size_t)((Nq + 63) / 64), tk = (size_t)((Nk + 63) / 64);
     const size_t tile = 64 * (size_t)d * 2;             // one transposed 64-row tile
     w.scales = 0;
@@ -101,7 +116,7 @@ BwdWorkspace bwd_workspace_layout(long long B, long long H, long long Hkv, long 
 }
 
 // ---------------------------------------------------------------------------
-// Phase 1a: per (head, chunk of kScaleRows rows), the largest |x| of two
+// Phase 1a: per (head, chunk of scale_chunk_rows(D) rows), the largest |x| of two
 // tensors, as bf16 magnitude bits (for finite values the integer order of
 // (bits & 0x7fff) is the order of |x|): Q and dO (Nq rows) for the BH query
 // heads (rows r < BH of the grid), K and V (Nk rows) for the BHkv K/V heads
@@ -121,8 +136,9 @@ bwd_absmax_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
     const int r = bid / chunks, ch = bid % chunks;
     const bool kv = r >= BH;
     const int N = kv ? Nk : Nq;
-    const int row0 = ch * kScaleRows;
-    const int nrows = min(kScaleRows, N - row0);
+    constexpr int CR = scale_chunk_rows(D);
+    const int row0 = ch * CR;
+    const int nrows = min(CR, N - row0);
     const size_t base = ((size_t)(kv ? r - BH : r) * N + row0) * D;
     const uint16_t* src0 = (kv ? K : Q) + base;
     const uint16_t* src1 = (kv ? V : dO) + base;
@@ -240,6 +256,27 @@ struct Tile64 {
         }
     }
 
+    // The tile as rows again (row r at dst + r * row_bytes), fp16 of the value
+    // times s with CVT.
+    template <bool CVT>
+    __device__ __forceinline__ void store_rows(char* dst, int row_bytes, int tid, float s = 1.f) const {
+#pragma unroll
+        for (int it = 0; it < LOADS; ++it) {
+            const int u = tid + it * NT;
+            if (UNITS % NT == 0 || u < UNITS) {
+                const int ch = u % DCH, rg = u / DCH;
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    u32x4_t x;
+#pragma unroll
+                    for (int w = 0; w < 4; ++w)
+                        x[w] = CVT ? bf16x2_to_f16x2(r[it][rr][w], s) : r[it][rr][w];
+                    *(u32x4_t*)(dst + (size_t)(4 * rg + rr) * row_bytes + ch * 16) = x;
+                }
+            }
+        }
+    }
+
     template <bool CVT, bool NATURAL = false>
     __device__ __forceinline__ void store_transposed(char* dst, int tid, float s = 1.f) const {
 #pragma unroll
@@ -315,6 +352,14 @@ bwd_image_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     __shared__ __attribute__((aligned(16))) char img[TileT::BYTES];
     TileT tl;
     tl.load(src + (size_t)head * N * DT + part * D, tile * 64, N, threadIdx.x);
+    // Bit 2: Q and dO as fp16 rows ([Tq * 64][DT] per head, row-major), each
+    // thread converting the 4 x 8 micro-tiles it loaded; bit 3: K as fp16
+    // rows ([Tk * 64][DT] per K/V head).
+    if (natural & (which < 2 ? 4 : 8)) {
+        char* rows = dst + ((size_t)head * T + tile) * NP * TileT::BYTES;
+        tl.template store_rows<true>(rows + part * D * 2, DT * 2, threadIdx.x, s);
+        return;
+    }
     // (d = 256: Q and dO in the half-tile layout of img32_offset)
     const bool halves = DT > 128 && (natural & (which < 2 ? 1 : 2));
     if (halves || (DT <= 128 && (natural & (which < 2 ? 1 : 2))))
@@ -1030,6 +1075,39 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
 }
 
+// 16x16x32 product with bf16 operands, or fp16 with F16.
+template <bool F16>
+__device__ __forceinline__ f32x4_t mfma16x16x32(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c) {
+    if constexpr (F16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                      __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// A operand of a 32x32x16 product taken transposed from a row-major 16-bit
+// tile (rows r, 16-byte chunks swizzled as row_chunk_offset): lane l gets
+// column c0 + l%32 of rows r0 + 8 (l/32) .. +7, in row order; two
+// ds_read_b64_tr_b16. Within a group of 16 lanes, ds_read_b64_tr_b16 returns
+// to lane i element e of the 8 bytes addressed by lane 4e + i/4, at position
+// i%4; so lane i addresses row base + i/4, columns cb + 4 (i%4) .. +3, with
+// cb = c0 + 16 ((l/16) % 2) and base = r0 + 8 (l/32) (then + 4).
+template <int D>
+__device__ __forceinline__ u32x4_t rows_tr_frag(const lds_char* tile, int r0, int c0, int lane) {
+    const int i = lane & 15;
+    const int col = c0 + 16 * ((lane >> 4) & 1) + 4 * (i & 3);
+    const int r1 = r0 + (i >> 2), r2 = r1 + 4;
+    const int o1 = row_chunk_offset<D>(r1, col >> 3) + ((col & 7) << 1);
+    const int o2 = row_chunk_offset<D>(r2, col >> 3) + ((col & 7) << 1);
+    const i16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4_t*)(tile + o1));
+    const i16x4_t y = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4_t*)(tile + o2));
+    const u32x2_t ux = __builtin_bit_cast(u32x2_t, x), uy = __builtin_bit_cast(u32x2_t, y);
+    return u32x4_t{ux[0], ux[1], uy[0], uy[1]};
+}
+
 // Waves of the pass below: one per SIMD with 64 keys per wave or at d = 256,
 // two per SIMD with 32 keys per wave at d <= 128.
 constexpr int dkdv16_waves(int D, int KW) { return D == 256 ? 4 : 256 / KW; }
@@ -1060,7 +1138,7 @@ constexpr int dkdv16_waves(int D, int KW) { return D == 256 ? 4 : 256 / KW; }
 // query tile is staged whole (rows and images, double-buffered) with one
 // barrier per tile.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL, int KW>
+template <int D, bool CAUSAL, int KW, bool TR>
 __global__ void __launch_bounds__(dkdv16_waves(D, KW) * 64, 1)
 bwd_dkdv16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                   const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
@@ -1082,8 +1160,12 @@ bwd_dkdv16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
     constexpr int TB = BQ * D * 2;       // bytes of one tile (rows or image)
     constexpr int BLK = TB / 1024;       // its 1 KB copy blocks
     constexpr int PPT = BLK / NW;        // blocks per wave and tensor
+    // TR: the tile is the fp16 rows of s_Q Q and s_dO dO only, and the dV, dK
+    // products read their transposed operands from them (ds_read_b64_tr_b16);
+    // otherwise the bf16 rows of Q and dO, then their transposed fp16 images.
+    constexpr int NT = TR ? 2 : 4;       // tensors per tile
     constexpr int OFF_Q = 0, OFF_DO = TB, OFF_QT = 2 * TB, OFF_DOT = 3 * TB;
-    constexpr int BUF = 4 * TB;          // one tile: Q and dO rows, then their images
+    constexpr int BUF = NT * TB;
     // A statistics copy fills 1 KB of LDS (512 bytes of values, then lanes
     // repeating the last chunk).
     constexpr int SBUF = 1024;
@@ -1100,27 +1182,34 @@ bwd_dkdv16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
     const size_t head = (size_t)bkv * (size_t)Nk * D;
     const int qh0 = bkv * G;
 
-    const float sQ = scales[qh0 * 4 + 0];
+    const float sQ = scales[qh0 * 4 + 0], sK = scales[qh0 * 4 + 1];
     const float sV = scales[qh0 * 4 + 2], sDO = scales[qh0 * 4 + 3];
     const float sE = sDO * sV;
+    // TR: S is formed from s_Q Q and s_K K (powers of two), so the exponent
+    // factor takes them out.
+    const float cS = TR ? c / (sQ * sK) : c;
 
     const int k0 = kb * BKV;
     const int kw0 = k0 + wave * KW;
     const int off = Nk - N;                      // query row i sits at key position i + off
 
-    // K^T and (sE V)^T operands of the 16x16x32 products (sE a power of two,
-    // so sE V is exact; keys past Nk read key Nk-1, whose gradients are not
-    // stored).
+    // K^T and V^T operands of the 16x16x32 products: bf16 K and sE V (sE a
+    // power of two, so sE V is exact), or with TR fp16 of s_K K and s_V V
+    // (exact copies: the factors put the largest magnitude in [1/2, 1)). Keys
+    // past Nk read key Nk-1, whose gradients are not stored.
     u32x4_t kr[KC][NJ], vr[KC][NJ];
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             const size_t row = (size_t)min(kw0 + 16 * j + l16, Nk - 1);
-            kr[kc][j] = *(const u32x4_t*)(K + head + row * D + 32 * kc + 8 * q4);
+            const u32x4_t k = *(const u32x4_t*)(K + head + row * D + 32 * kc + 8 * q4);
             const u32x4_t v = *(const u32x4_t*)(V + head + row * D + 32 * kc + 8 * q4);
 #pragma unroll
-            for (int w = 0; w < 4; ++w) vr[kc][j][w] = bf16x2_scale(v[w], sE);
+            for (int w = 0; w < 4; ++w) {
+                kr[kc][j][w] = TR ? bf16x2_to_f16x2(k[w], sK) : k[w];
+                vr[kc][j][w] = TR ? bf16x2_to_f16x2(v[w], sV) : bf16x2_scale(v[w], sE);
+            }
         }
 
     // dV^T, dK^T of the wave's 32-key blocks (AGPRs)
@@ -1149,7 +1238,12 @@ bwd_dkdv16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
         lds_char* base = (lds_char*)(smem + b * BUF);
         const int tensor = k / PPT, blk = wave + NW * (k % PPT);
         const size_t qh = live_head(gq, t), ti = live_tile(gq, t);
-        if (tensor < 2)
+        if (TR)   // fp16 rows: [T * 64][D] per query head
+            stage_tile_block_async<D, D>((const uint16_t*)(tensor == 0 ? qt_img : ot_img) +
+                                             qh * (size_t)(T * 64) * D,
+                                         base + (tensor == 0 ? OFF_Q : OFF_DO), (int)ti * BQ, N,
+                                         blk, lane);
+        else if (tensor < 2)
             stage_tile_block_async<D, D>((tensor == 0 ? Q : dO) + qh * N * D,
                                          base + (tensor == 0 ? OFF_Q : OFF_DO), (int)ti * BQ, N,
                                          blk, lane);
@@ -1244,6 +1338,9 @@ bwd_dkdv16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
             if (op.kind < 2)
                 return *(const lds_u32x4_t*)(base + (op.kind == 0 ? OFF_Q : OFF_DO) +
                                              row_chunk_offset<D>(16 * op.s + l16, 4 * op.x + q4));
+            if (TR)   // dims 32 x + l32, rows 16 s + 8 g .. +7, from the rows
+                return rows_tr_frag<D>(base + (op.kind == 2 ? OFF_DO : OFF_Q), 16 * op.s + 8 * g,
+                                       32 * op.x, lane);
             return *(const lds_u32x4_t*)(base + (op.kind == 2 ? OFF_DOT : OFF_QT) +
                                          img_offset(32 * op.x + l32, 2 * op.s + g));
         };
@@ -1260,7 +1357,7 @@ bwd_dkdv16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
         // l16 and query row i0 + 16 s + 4 q4 + i.
         auto exp_block = [&](int s, int j) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sa[j][i] = fast_exp2(__builtin_fmaf(sa[j][i], c, -lse4[i]));
+            for (int i = 0; i < 4; ++i) sa[j][i] = fast_exp2(__builtin_fmaf(sa[j][i], cS, -lse4[i]));
             if (CAUSAL && mask_tile) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
@@ -1302,9 +1399,7 @@ bwd_dkdv16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) {
                     if (op.x == 0) sa[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                    sa[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, kr[op.x][j]),
-                        sa[j], 0, 0, 0);
+                    sa[j] = mfma16x16x32<TR>(a, kr[op.x][j], sa[j]);
                 }
                 // A(s): the swaps of step s-1
                 if (op.s >= 1 && op.x == 0) swap_block(0);
@@ -1313,9 +1408,7 @@ bwd_dkdv16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) {
                     if (op.x == 0) da[j] = dinit;
-                    da[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, vr[op.x][j]),
-                        da[j], 0, 0, 0);
+                    da[j] = mfma16x16x32<TR>(a, vr[op.x][j], da[j]);
                 }
                 if (op.x == NS - 1 && op.s == 0) {
                     // C(0): no products to run under
@@ -1353,7 +1446,7 @@ bwd_dkdv16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
             }
             // the next tile's copies, one every third operation from the fourth on
 #pragma unroll
-            for (int k = 0; k < 4 * PPT; ++k)
+            for (int k = 0; k < NT * PPT; ++k)
                 if (o == 3 + 3 * k) stage(ga, ta, b ^ 1, k);
             if (o == 4) stage_stats(ga, ta, b ^ 1);
             __builtin_amdgcn_sched_barrier(0);
@@ -1366,7 +1459,7 @@ bwd_dkdv16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
     const int t_free = CAUSAL ? min(max((max(last_kq, 0) + BQ - 1) / BQ, t0), n_tiles) : t0;
     if (t0 < n_tiles) {
 #pragma unroll
-        for (int k = 0; k < 4 * PPT; ++k) stage(0, n_tiles - 1, 0, k);
+        for (int k = 0; k < NT * PPT; ++k) stage(0, n_tiles - 1, 0, k);
         stage_stats(0, n_tiles - 1, 0);
         int L = 0;
         for (int gq = 0; gq < G; ++gq) {
@@ -1443,7 +1536,7 @@ constexpr int dq16_waves(int D, int QW) { return D == 256 ? 4 : 256 / QW; }
 // whole (K and V rows and the K~^T image, double-buffered) with one barrier
 // per tile. The pass also leaves lse and D per query tile for the dK/dV pass.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL, int QW>
+template <int D, bool CAUSAL, int QW, bool TR>
 __global__ void __launch_bounds__(dq16_waves(D, QW) * 64, 1)
 bwd_dq16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
@@ -1465,8 +1558,12 @@ bwd_dq16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     constexpr int TB = BC * D * 2;       // bytes of one tile (rows or image)
     constexpr int BLK = TB / 1024;       // its 1 KB copy blocks
     constexpr int PPT = BLK / NW;        // blocks per wave and tensor
+    // TR: the tile is the fp16 rows of s_K K and the bf16 rows of V, and the
+    // dQ product reads its transposed K operand from the first
+    // (ds_read_b64_tr_b16); otherwise K and V rows, then the K~^T image.
+    constexpr int NT = TR ? 2 : 3;       // tensors per tile
     constexpr int OFF_K = 0, OFF_V = TB, OFF_KT = 2 * TB;
-    constexpr int BUF = 3 * TB;          // one tile: K and V rows, then the K~^T image
+    constexpr int BUF = NT * TB;
     __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
 
     const int tid = threadIdx.x;
@@ -1481,14 +1578,18 @@ bwd_dq16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const size_t kvhead = (size_t)(bh / G) * (size_t)Nk * D;  // K/V head of this query head
     const uint16_t* Kh = K + kvhead;
     const uint16_t* Vh = V + kvhead;
-    const char* kt_h = kt_img + (size_t)(bh / G) * (Tk * 64 / BC) * TB;
+    // (TR: [Tk * 64][D] fp16 rows per K/V head; otherwise tile images)
+    const char* kt_h = kt_img + (size_t)(bh / G) * (TR ? (size_t)Tk * 64 * D * 2 : (size_t)(Tk * 64 / BC) * TB);
     const int q0 = qb * BQ;
     const int qw0 = q0 + wave * QW;
     const int off = Nk - N;              // query row i sits at key position i + off
 
-    const float sK = scales[bh * 4 + 1];
+    const float sQ = scales[bh * 4 + 0], sK = scales[bh * 4 + 1];
     const float sV = scales[bh * 4 + 2], sDO = scales[bh * 4 + 3];
     const float sE = sDO * sV;
+    // TR: S is formed from s_Q Q and s_K K (powers of two), so the exponent
+    // factor takes them out.
+    const float cS = TR ? c / (sQ * sK) : c;
 
     // Q^T and (sE dO)^T operands of the 16x16x32 products (rows past N read
     // row N-1: finite values whose probabilities are 0 and whose dQ is not
@@ -1504,7 +1605,9 @@ bwd_dq16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         const size_t row = (size_t)min(qi, N - 1);
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
-            qr[kc][j] = *(const u32x4_t*)(Q + head + row * D + 32 * kc + 8 * q4);
+            const u32x4_t qv = *(const u32x4_t*)(Q + head + row * D + 32 * kc + 8 * q4);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) qr[kc][j][w] = TR ? bf16x2_to_f16x2(qv[w], sQ) : qv[w];
             const u32x4_t v = *(const u32x4_t*)(dO + head + row * D + 32 * kc + 8 * q4);
 #pragma unroll
             for (int w = 0; w < 4; ++w) orr[kc][j][w] = bf16x2_scale(v[w], sE);
@@ -1543,7 +1646,9 @@ bwd_dq16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         lds_char* base = (lds_char*)(smem + b * BUF);
         const int tensor = k / PPT, blk = wave + NW * (k % PPT);
         const int ti = t < n_tiles ? t : 0;
-        if (tensor < 2)
+        if (TR && tensor == 0)
+            stage_tile_block_async<D, D>((const uint16_t*)kt_h, base + OFF_K, ti * BC, Nk, blk, lane);
+        else if (tensor < 2)
             stage_tile_block_async<D, D>(tensor == 0 ? Kh : Vh, base + (tensor == 0 ? OFF_K : OFF_V),
                                          ti * BC, Nk, blk, lane);
         else
@@ -1566,7 +1671,7 @@ bwd_dq16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     constexpr int NS = KC, NGR = NB;
     constexpr int NOPS = NSTEP * (2 * NS) + NSTEP * NGR;
     constexpr int LA = 2;
-    static_assert(3 + 3 * (3 * PPT - 1) < NOPS, "the next tile's copies fit in the operations");
+    static_assert(3 + 3 * (NT * PPT - 1) < NOPS, "the next tile's copies fit in the operations");
     // Operation o: kind (0 K, 1 V, 2 K~^T), step, chunk or block.
     struct Op { int kind, s, x; };
     auto op_of = [](int o) constexpr -> Op {
@@ -1604,12 +1709,14 @@ bwd_dq16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             if (op.kind < 2)
                 return *(const lds_u32x4_t*)(base + (op.kind == 0 ? OFF_K : OFF_V) +
                                              row_chunk_offset<D>(16 * op.s + l16, 4 * op.x + q4));
+            if (TR)   // dims 32 x + l32, keys 16 s + 8 g .. +7, from the K rows
+                return rows_tr_frag<D>(base + OFF_K, 16 * op.s + 8 * g, 32 * op.x, lane);
             return *(const lds_u32x4_t*)(base + OFF_KT + img_offset(32 * op.x + l32, 2 * op.s + g));
         };
         // P of step s, query block j (over S), then dS = P (dP - D) packed
         auto ds_block = [&](int s, int j) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sa[j][i] = fast_exp2(__builtin_fmaf(sa[j][i], c, -lse2[j]));
+            for (int i = 0; i < 4; ++i) sa[j][i] = fast_exp2(__builtin_fmaf(sa[j][i], cS, -lse2[j]));
             if (mask_tile) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
@@ -1642,9 +1749,7 @@ bwd_dq16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) {
                     if (op.x == 0) sa[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                    sa[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, qr[op.x][j]),
-                        sa[j], 0, 0, 0);
+                    sa[j] = mfma16x16x32<TR>(a, qr[op.x][j], sa[j]);
                 }
                 // A(s): the swaps of step s-1
                 if (op.s >= 1 && op.x == 0) swap_block(0);
@@ -1678,14 +1783,14 @@ bwd_dq16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             }
             // the next tile's copies, one every third operation from the fourth on
 #pragma unroll
-            for (int k = 0; k < 3 * PPT; ++k)
+            for (int k = 0; k < NT * PPT; ++k)
                 if (o == 3 + 3 * k) stage(t + 1, b ^ 1, k);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
 
 #pragma unroll
-    for (int k = 0; k < 3 * PPT; ++k) stage(0, 0, k);
+    for (int k = 0; k < NT * PPT; ++k) stage(0, 0, k);
     for (int t = 0; t < n_tiles; ++t) {
         // this wave's copies of tile t have landed and its reads of tile t-1
         // are done; after the barrier everyone's are
@@ -1770,7 +1875,7 @@ template <int D>
 static hipError_t launch_prepare_t(const BwdArgs& a) {
     const BwdWorkspace w = ws_of(a);
     const int BH = a.B * a.H, BHkv = a.B * a.Hkv, G = a.H / a.Hkv;
-    const int chunks = bwd_scale_chunks(a.N, a.Nk);
+    const int chunks = bwd_scale_chunks(a.N, a.Nk, a.d);
     const int Tq = q_tiles64(a), Tk = k_tiles64(a);
     uint32_t* partial = ws_ptr<uint32_t>(a, w.partial);
     hipLaunchKernelGGL((bwd_absmax_kernel<D>), dim3((BH + BHkv) * chunks), dim3(256), 0,
@@ -1789,7 +1894,9 @@ static hipError_t launch_prepare_t(const BwdArgs& a) {
                        a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                        (const uint16_t*)a.dout, ws_ptr<const float>(a, w.scales),
                        ws_ptr<char>(a, w.qt), ws_ptr<char>(a, w.ot), ws_ptr<char>(a, w.kt), BH,
-                       G, a.N, a.Nk, Tq, Tk, (use_dkdv16(a) ? 1 : 0) | (use_dq16(a) ? 2 : 0));
+                       G, a.N, a.Nk, Tq, Tk,
+                       (use_dkdv16(a) ? (FA_DKDV_TR ? 4 : 1) : 0) |
+                           (use_dq16(a) ? (dq16_tr(D) ? 8 : 2) : 0));
     return hipGetLastError();
 }
 
@@ -1805,7 +1912,7 @@ static hipError_t launch_dq_t(const BwdArgs& a) {
         constexpr int QW = D == 64 ? 64 : 32;
         constexpr int NWQ = dq16_waves(D, QW);
         const int nqb = (a.N + NWQ * QW - 1) / (NWQ * QW);
-        hipLaunchKernelGGL((bwd_dq16_kernel<D, CAUSAL, QW>), dim3(nqb * BH),
+        hipLaunchKernelGGL((bwd_dq16_kernel<D, CAUSAL, QW, dq16_tr(D)>), dim3(nqb * BH),
                            dim3(NWQ * 64), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                            (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse,
                            ws_ptr<const float>(a, w.scales), ws_ptr<const float>(a, w.dhat),
@@ -1840,7 +1947,8 @@ static hipError_t launch_dkdv_t(const BwdArgs& a) {
         constexpr int KW = D == 128 ? 64 : 32;
         constexpr int NW = dkdv16_waves(D, KW);
         const int nkb = (a.Nk + NW * KW - 1) / (NW * KW);
-        hipLaunchKernelGGL((bwd_dkdv16_kernel<D, CAUSAL, KW>), dim3(nkb * BHkv), dim3(NW * 64), 0,
+        hipLaunchKernelGGL((bwd_dkdv16_kernel<D, CAUSAL, KW, (FA_DKDV_TR != 0)>), dim3(nkb * BHkv),
+                           dim3(NW * 64), 0,
                            a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                            (const uint16_t*)a.v, (const uint16_t*)a.dout,
                            ws_ptr<const float>(a, w.scales), ws_ptr<const float>(a, w.stats),

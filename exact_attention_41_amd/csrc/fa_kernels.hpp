@@ -48,8 +48,11 @@ struct BwdArgs {
     bool d_known = false;
 };
 
-// Rows per chunk of the max-abs pre-pass of the backward.
+// Rows per chunk of the max-abs pre-pass of the backward: 256 up to d = 128,
+// 128 at d = 256 (the same bytes per chunk, so the same number of workgroups
+// per byte).
 constexpr int kScaleRows = 256;
+constexpr int scale_chunk_rows(long long d) { return d > 128 ? (int)(kScaleRows * 128 / d) : kScaleRows; }
 
 // Byte offsets of the backward workspace blocks (Tq = ceil(Nq / 64) and
 // Tk = ceil(Nk / 64) tiles of 64 rows per head; an image is the byte layout
@@ -70,12 +73,15 @@ constexpr int kScaleRows = 256;
 //   qt      fp16 [BH][Tq][64*d]      images of (s_Q Q)^T, one per 64-row tile
 //   ot      fp16 [BH][Tq][64*d]      images of (s_dO dO)^T
 //   kt      fp16 [BHkv][Tk][64*d]    images of (s_K K)^T
+// (at d = 256 a 64-row tile's image is either its two 128-column parts or,
+// for the passes with 16-row steps, its two 32-row halves, each a [256][32]
+// block; the preprocess writes the layout of the pass that reads it)
 struct BwdWorkspace {
     size_t scales, partial, dhat, stats, qt, ot, kt, total;
 };
 BwdWorkspace bwd_workspace_layout(long long B, long long H, long long Hkv, long long Nq,
                                   long long Nk, long long d);
-int bwd_scale_chunks(long long Nq, long long Nk);
+int bwd_scale_chunks(long long Nq, long long Nk, long long d);
 
 // Decoding: Nq query rows per query head (the last Nq positions) against Nk
 // keys; q, o [B][H][Nq][d], k, v [B][Hkv][Nk][d], lse [B][H][Nq].
