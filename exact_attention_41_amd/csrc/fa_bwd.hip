@@ -1087,7 +1087,7 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(const u32x4_t& a, const u32x4_t&
 }
 
 // A operand of a 32x32x16 product taken transposed from a row-major 16-bit
-// tile (rows r, 16-byte chunks swizzled as row_chunk_offset): lane l gets
+// tile (rows r, 16-byte chunks swizzled as tr_rows_swizzle): lane l gets
 // column c0 + l%32 of rows r0 + 8 (l/32) .. +7, in row order; two
 // ds_read_b64_tr_b16. Within a group of 16 lanes, ds_read_b64_tr_b16 returns
 // to lane i element e of the 8 bytes addressed by lane 4e + i/4, at position
@@ -1098,8 +1098,8 @@ __device__ __forceinline__ u32x4_t rows_tr_frag(const lds_char* tile, int r0, in
     const int i = lane & 15;
     const int col = c0 + 16 * ((lane >> 4) & 1) + 4 * (i & 3);
     const int r1 = r0 + (i >> 2), r2 = r1 + 4;
-    const int o1 = row_chunk_offset<D>(r1, col >> 3) + ((col & 7) << 1);
-    const int o2 = row_chunk_offset<D>(r2, col >> 3) + ((col & 7) << 1);
+    const int o1 = rows_offset<D, true>(r1, col >> 3) + ((col & 7) << 1);
+    const int o2 = rows_offset<D, true>(r2, col >> 3) + ((col & 7) << 1);
     const i16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (__attribute__((address_space(3))) i16x4_t*)(tile + o1));
     const i16x4_t y = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -1239,7 +1239,7 @@ bwd_dkdv16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
         const int tensor = k / PPT, blk = wave + NW * (k % PPT);
         const size_t qh = live_head(gq, t), ti = live_tile(gq, t);
         if (TR)   // fp16 rows: [T * 64][D] per query head
-            stage_tile_block_async<D, D>((const uint16_t*)(tensor == 0 ? qt_img : ot_img) +
+            stage_tile_block_async<D, D, true>((const uint16_t*)(tensor == 0 ? qt_img : ot_img) +
                                              qh * (size_t)(T * 64) * D,
                                          base + (tensor == 0 ? OFF_Q : OFF_DO), (int)ti * BQ, N,
                                          blk, lane);
@@ -1337,7 +1337,7 @@ bwd_dkdv16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
             const lds_char* base = (lds_char*)smem + b * BUF;
             if (op.kind < 2)
                 return *(const lds_u32x4_t*)(base + (op.kind == 0 ? OFF_Q : OFF_DO) +
-                                             row_chunk_offset<D>(16 * op.s + l16, 4 * op.x + q4));
+                                             rows_offset<D, TR>(16 * op.s + l16, 4 * op.x + q4));
             if (TR)   // dims 32 x + l32, rows 16 s + 8 g .. +7, from the rows
                 return rows_tr_frag<D>(base + (op.kind == 2 ? OFF_DO : OFF_Q), 16 * op.s + 8 * g,
                                        32 * op.x, lane);
@@ -1647,7 +1647,8 @@ bwd_dq16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         const int tensor = k / PPT, blk = wave + NW * (k % PPT);
         const int ti = t < n_tiles ? t : 0;
         if (TR && tensor == 0)
-            stage_tile_block_async<D, D>((const uint16_t*)kt_h, base + OFF_K, ti * BC, Nk, blk, lane);
+            stage_tile_block_async<D, D, true>((const uint16_t*)kt_h, base + OFF_K, ti * BC, Nk, blk,
+                                               lane);
         else if (tensor < 2)
             stage_tile_block_async<D, D>(tensor == 0 ? Kh : Vh, base + (tensor == 0 ? OFF_K : OFF_V),
                                          ti * BC, Nk, blk, lane);
@@ -1706,8 +1707,11 @@ bwd_dq16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         auto fragment = [&](int o) -> u32x4_t {
             const Op op = op_of(o);
             const lds_char* base = (lds_char*)smem + b * BUF;
-            if (op.kind < 2)
-                return *(const lds_u32x4_t*)(base + (op.kind == 0 ? OFF_K : OFF_V) +
+            if (op.kind == 0)
+                return *(const lds_u32x4_t*)(base + OFF_K +
+                                             rows_offset<D, TR>(16 * op.s + l16, 4 * op.x + q4));
+            if (op.kind == 1)
+                return *(const lds_u32x4_t*)(base + OFF_V +
                                              row_chunk_offset<D>(16 * op.s + l16, 4 * op.x + q4));
             if (TR)   // dims 32 x + l32, keys 16 s + 8 g .. +7, from the K rows
                 return rows_tr_frag<D>(base + OFF_K, 16 * op.s + 8 * g, 32 * op.x, lane);

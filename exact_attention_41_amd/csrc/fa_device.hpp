@@ -216,6 +216,26 @@ __device__ __forceinline__ int row_chunk_offset(int row, int chunk) {
     return row * (D * 2) + ((chunk ^ row_chunk_swizzle<D>(row)) << 4);
 }
 
+// Row-major tiles that are also read transposed (ds_read_b64_tr_b16: 32
+// lanes read four consecutive rows x 64 bytes). For 256- and 512-byte rows
+// the XOR takes the row's two low bits into chunk bits 2-3 (and bits 2-3
+// into bits 0-1): four consecutive rows then land in four different 64-byte
+// bank ranges, and 16 consecutive rows reading one chunk still cover every
+// bank once. 128-byte rows keep row_chunk_swizzle.
+template <int D>
+__device__ __forceinline__ int tr_rows_swizzle(int row) {
+    if constexpr (D >= 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+    else return row_chunk_swizzle<D>(row);
+}
+
+// Byte offset of 16-byte chunk `chunk` of row `row`: row_chunk_offset, or with
+// TRS the swizzle of tr_rows_swizzle.
+template <int D, bool TRS>
+__device__ __forceinline__ int rows_offset(int row, int chunk) {
+    return row * (D * 2) +
+           ((chunk ^ (TRS ? tr_rows_swizzle<D>(row) : row_chunk_swizzle<D>(row))) << 4);
+}
+
 // Transposed tile layout ("[n][key]"), 64 keys per row = 128 B = 16 slots of
 // 8 B. Within every group of 16 keys the order is permuted so that the eight
 // keys one MFMA lane group needs are contiguous (key 16t + 8a + 4g + c is
@@ -330,7 +350,7 @@ __device__ __forceinline__ void stage_tile_block(const uint16_t* __restrict__ sr
     stage_block<D, false, LD>(src, tile, row0, N, b, lane);
 }
 
-template <int D, int LD = D>
+template <int D, int LD = D, bool TRS = false>
 __device__ __forceinline__ void stage_tile_block_async(const uint16_t* __restrict__ src,
                                                        lds_char* tile, int row0, int N, int b,
                                                        int lane) {
@@ -338,7 +358,7 @@ __device__ __forceinline__ void stage_tile_block_async(const uint16_t* __restric
     constexpr int RPK = 1024 / (2 * D);
     const int row = b * RPK + lane / DCH;
     const int phys = lane % DCH;
-    const int logical = phys ^ row_chunk_swizzle<D>(row);
+    const int logical = phys ^ (TRS ? tr_rows_swizzle<D>(row) : row_chunk_swizzle<D>(row));
     const int rb = min(row0, N - 1);
     const uint32_t voff = (uint32_t)(min(row, N - 1 - rb) * (2 * LD) + logical * 16);
     lds_dma16_async(src + (size_t)rb * LD, voff, tile + b * 1024);
