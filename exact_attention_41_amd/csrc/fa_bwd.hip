@@ -16,13 +16,17 @@
 //      power-of-two factors so that every fp16 operand below (a bf16 input
 //      scaled by a power of two) is in range, and exact for |x| down to
 //      2^-17 of the head's largest (smaller values round, by at most 2^-24
-//      of the largest: fp16's subnormal step); then, per 64-row
-//      tile, fp16 images of (s_Q Q)^T, (s_dO dO)^T and (s_K K)^T laid out
-//      exactly as the transposed LDS tiles the next phases read.
-//      The same pass takes D^_i = dO_i . O_i from the bf16 O: not D itself
-//      (the rounding of O moves it too far), only a centre for step 2.
-//   2. dQ pass: one workgroup per query block, over the key tiles. D_i is not
-//      known before the pass, so with E_ij = P_ij (dP_ij - D^_i) it uses
+//      of the largest: fp16's subnormal step); then fp16 copies of s_Q Q,
+//      s_dO dO and s_K K, laid out for the pass that reads them: as rows
+//      (read transposed with ds_read_b64_tr_b16 where a product needs them
+//      so), or per 64-row tile exactly as a transposed LDS tile. The same
+//      pass forms D_i = dO_i . O_i per row: from O plus the forward's
+//      rounding residual of O when the caller has it (D itself), else from
+//      the bf16 O alone (the rounding of O moves that too far: only a
+//      centre D^ for step 2).
+//   2. dQ pass: one workgroup per query block, over the key tiles. With D
+//      known, dQ_i = scale * sum_j P_ij (dP_ij - D_i) K_j. Otherwise, with
+//      E_ij = P_ij (dP_ij - D^_i), it uses
 //          dQ_i = scale * (sum_j E_ij K_j - (D_i - D^_i) sum_j P_ij K_j)
 //      and accumulates both sums and D_i - D^_i = sum_j E_ij in the same
 //      pass; D is exact. Subtracting the centre before E is rounded keeps
@@ -30,18 +34,19 @@
 //      when V has a large mean). It leaves lse and D per query tile in the
 //      workspace for the next pass.
 //   3. dK/dV pass: one workgroup per key block, over the query tiles.
-// S and dP are products of the bf16 inputs themselves. The probabilities and
-// dS enter the gradient products as fp16 (11-bit significand) rather than
-// bf16 (8-bit), against the fp16 images: this keeps dQ, dK and dV within
-// 1e-2 of the exact gradients where bf16 operands do not.
+// S and dP are products of the inputs: the bf16 values themselves, or their
+// fp16 copies scaled by powers of two (the same values in the range above).
+// The probabilities and dS enter the gradient products as fp16 (11-bit
+// significand) rather than bf16 (8-bit), against fp16 copies of Q, dO or K:
+// this keeps dQ, dK and dV within 1e-2 of the exact gradients where bf16
+// operands do not.
 //
-// Every tile reaches LDS by direct global-to-LDS loads (row-major bf16 tiles
-// from the inputs, with the chunk swizzle applied through the source
-// addresses; transposed tiles as straight copies of their images), issued
-// ahead into LDS buffers of their own (three in the dQ pass; separate
-// row-major, image and statistics buffers in the dK/dV pass), so that each
-// pass needs one barrier per step and its fragment reads run on through it;
-// no tile passes through VGPRs.
+// Every tile reaches LDS by direct global-to-LDS loads (row-major tiles of
+// the bf16 inputs or of their fp16 copies, with the chunk swizzle applied
+// through the source addresses; transposed tiles as straight copies of
+// their images), issued ahead into LDS buffers of their own, so that each
+// pass needs one barrier per tile (per step in the 32-row passes) and its
+// fragment reads run on through it; no tile passes through VGPRs.
 #include "fa_kernels.hpp"
 #include "fa_device.hpp"
 
@@ -1123,20 +1128,23 @@ constexpr int dkdv16_waves(int D, int KW) { return D == 256 ? 4 : 256 / KW; }
 // formed once for all 256 columns of dK and dV. Each workgroup walks the
 // query tiles that see its keys in 16-row steps, so every LDS fragment feeds
 // several products (the 32-key form above reads a fresh fragment for each):
-//   S, dP (16 queries x KW keys): v_mfma_f32_16x16x32_bf16, A = a 16-row
-//     slice of the Q (dO) tile from LDS, read once for the KW/16 key blocks;
-//     B = K^T (V^T), resident in VGPRs. Accumulator lane l: key 16j + l%16,
-//     queries 4(l/16) .. +3.
+//   S, dP (16 queries x KW keys): 16x16x32 products, A = a 16-row slice of
+//     the Q (dO) rows from LDS, read once for the KW/16 key blocks; B = K^T
+//     (V^T), resident in VGPRs. With TR the rows are the fp16 copies of s_Q Q
+//     and s_dO dO and the products fp16 against fp16 s_K K and s_V V;
+//     otherwise bf16. Accumulator lane l: key 16j + l%16, queries 4(l/16) ..
+//     +3.
 //   P and dS = P (sE dP - sE D) are formed there, packed to fp16, and one
 //     v_permlane16_swap per pair of registers brings each lane the eight
 //     queries 8g .. 8g+7 (g = l/32) of key l%32 of a 32-key block: the B
 //     operand layout of the 32x32x16 product.
 //   dV^T += dO~^T P, dK^T += Q~^T dS~ (32 dims x 32 keys per product, fp16,
-//     AGPR accumulators), A = the 16-query slice of the transposed fp16
-//     image, read once for the wave's 32-key blocks.
+//     AGPR accumulators), A = the 16-query slice of dO~ (Q~) transposed: with
+//     TR read from the fp16 rows by ds_read_b64_tr_b16, otherwise from a
+//     transposed fp16 image staged beside the rows; read once for the wave's
+//     32-key blocks.
 // Step s's softmax runs between the products of step s-1's dV/dK. Every
-// query tile is staged whole (rows and images, double-buffered) with one
-// barrier per tile.
+// query tile is staged whole (double-buffered) with one barrier per tile.
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL, int KW, bool TR>
 __global__ void __launch_bounds__(dkdv16_waves(D, KW) * 64, 1)
@@ -1529,12 +1537,15 @@ constexpr int dq16_waves(int D, int QW) { return D == 256 ? 4 : 256 / QW; }
 //     each lane the eight keys 8g .. 8g+7 (g = l/32) of query l%32 of a
 //     32-query block: the B operand layout of the 32x32x16 product.
 //   dQ^T += K~^T dS~ (32 dims x 32 queries per product, fp16, AGPR
-//     accumulators), A = the 16-key slice of the transposed K~ image (rows in
-//     their own order), read once for the wave's 32-query blocks.
+//     accumulators), A = the 16-key slice of K~ transposed, read once for the
+//     wave's 32-query blocks: at d <= 128 from the transposed K~ image (rows
+//     in their own order), at d = 256 (TR) from the fp16 rows of s_K K by
+//     ds_read_b64_tr_b16, the same rows that S then takes (fp16 products
+//     against fp16 s_Q Q).
 // lse and D belong to a lane's query columns and are loaded once. Step s's
 // dS runs between the products of step s-1's dQ. Every key tile is staged
-// whole (K and V rows and the K~^T image, double-buffered) with one barrier
-// per tile. The pass also leaves lse and D per query tile for the dK/dV pass.
+// whole (double-buffered) with one barrier per tile. The pass also leaves lse
+// and D per query tile for the dK/dV pass.
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL, int QW, bool TR>
 __global__ void __launch_bounds__(dq16_waves(D, QW) * 64, 1)
