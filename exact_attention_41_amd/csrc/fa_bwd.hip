@@ -689,7 +689,7 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     if (part == 0 && g == 0 && qi < T * 64) {
         float* st = stats + ((size_t)bh * T + (qi >> 6)) * 128;
         st[qi & 63] = lse2;
-        st[64 + (qi & 63)] = (qi < N) ? dhs + dt : 0.f;   // sE * D
+        st[64 + (qi & 63)] = (qi < N) ? -(dhs + dt) : 0.f;   // -sE * D
     }
     if (qi < N) {
         const float f = scale / (sK * sE);
@@ -963,7 +963,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             // (one step per tile) or of the next tile.
             const int g2 = NC == 1 ? gb : ga, t2 = NC == 1 ? tb : ta;
 
-            f32x4_t l4[4], d4[4];     // lse*log2e and sE*D of the half being exponentiated
+            f32x4_t l4[4], d4[4];     // lse*log2e and -sE*D of the half being exponentiated
             float pv[16], dsv[16];
             u32x4_t pp[4], dsp[4];
             auto read_stats = [&](int ib, int q4) {
@@ -975,7 +975,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 float p = fast_exp2(__builtin_fmaf(sa[ib][r], c, -l4[q4][r4]));
                 if (MASK && kq > i0 + 32 * ib + 8 * q4 + 4 * g + r4) p = 0.f;
                 pv[r] = p;
-                dsv[r] = p * __builtin_fmaf(da[ib][r], sE, -d4[q4][r4]);
+                dsv[r] = p * __builtin_fmaf(da[ib][r], sE, d4[q4][r4]);
                 if (ib == 0 && r4 == 3) read_stats(1, q4);
                 if ((r & 7) == 7) {
                     const int h = r >> 3, rb = 8 * h;
@@ -1134,7 +1134,9 @@ constexpr int dkdv16_waves(int D, int KW) { return D == 256 ? 4 : 256 / KW; }
 //     and s_dO dO and the products fp16 against fp16 s_K K and s_V V;
 //     otherwise bf16. Accumulator lane l: key 16j + l%16, queries 4(l/16) ..
 //     +3.
-//   P and dS = P (sE dP - sE D) are formed there, packed to fp16, and one
+//   P and dS = P (sE dP - sE D) are formed there and packed to fp16 (dS as
+//     the packed fp16 product of the fp16 P and the fp16 sE (dP - D): one
+//     conversion and one v_pk_mul_f16 per pair of scores), and one
 //     v_permlane16_swap per pair of registers brings each lane the eight
 //     queries 8g .. 8g+7 (g = l/32) of key l%32 of a 32-key block: the B
 //     operand layout of the 32x32x16 product.
@@ -1358,7 +1360,7 @@ bwd_dkdv16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 lse4[i] = a[i];
-                dinit[i] = -d[i];
+                dinit[i] = d[i];
             }
         };
         // P of step s, key block j, over S: element (j, i) is key kw0 + 16 j +
@@ -1376,8 +1378,10 @@ bwd_dkdv16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
         auto ds_block = [&](int j) {
             pp[j][0] = pack_f16x2(sa[j][0], sa[j][1]);
             pp[j][1] = pack_f16x2(sa[j][2], sa[j][3]);
-            dp[j][0] = pack_f16x2(sa[j][0] * da[j][0], sa[j][1] * da[j][1]);
-            dp[j][1] = pack_f16x2(sa[j][2] * da[j][2], sa[j][3] * da[j][3]);
+            // (from the fp16 P: one conversion and one packed product per
+            // pair instead of two products and a conversion)
+            dp[j][0] = mul_f16x2(pp[j][0], pack_f16x2(da[j][0], da[j][1]));
+            dp[j][1] = mul_f16x2(pp[j][1], pack_f16x2(da[j][2], da[j][3]));
         };
         // Key blocks 2h, 2h+1 -> the 32-key block h in the 32x32 B layout.
         auto swap_block = [&](int h) {
@@ -1820,14 +1824,14 @@ bwd_dq16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     for (int h = 0; h < NH; ++h)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) agpr_settle(acc[h][nb]);
-    // lse log2 e and sE D of the wave's rows, into their query tile
+    // lse log2 e and -sE D of the wave's rows, into their query tile
     const int tq = qw0 >> 6;
     if (q4 == 0 && tq < T) {
         float* st = stats + ((size_t)bh * T + tq) * 128 + (qw0 & 63);
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             st[16 * j + l16] = lse2[j];
-            st[64 + 16 * j + l16] = dhs[j];
+            st[64 + 16 * j + l16] = -dhs[j];
         }
     }
     const float f = scale / (sK * sE);

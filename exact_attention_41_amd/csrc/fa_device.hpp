@@ -149,6 +149,11 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, p);
 }
 
+// Product of two packed fp16 pairs, lane by lane (v_pk_mul_f16).
+__device__ __forceinline__ uint32_t mul_f16x2(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, a) * __builtin_bit_cast(f16x2_t, b));
+}
+
 // A packed bf16 pair times s (a power of two), as a packed fp16 pair.
 __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w, float s) {
     return pack_f16x2(__uint_as_float(w << 16) * s, __uint_as_float(w & 0xffff0000u) * s);

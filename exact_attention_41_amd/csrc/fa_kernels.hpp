@@ -69,7 +69,7 @@ constexpr int scale_chunk_rows(long long d) { return d > 128 ? (int)(kScaleRows 
 //                                    rounding (D itself is formed exactly there);
 //                                    from O plus its residual, D itself
 //   stats   fp32 [BH][Tq][128]       per query tile: lse*log2(e) of its 64 rows,
-//                                    then sE*D (sE = s_dO*s_V); from the dQ pass
+//                                    then -sE*D (sE = s_dO*s_V); from the dQ pass
 //   qt      fp16 [BH][Tq][64*d]      images of (s_Q Q)^T, one per 64-row tile
 //   ot      fp16 [BH][Tq][64*d]      images of (s_dO dO)^T
 //   kt      fp16 [BHkv][Tk][64*d]    images of (s_K K)^T
