@@ -1304,8 +1304,8 @@ bwd_dkdv16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
     // reads A and B when it issues). Each fragment is read LA operations
     // ahead through a ring of registers that starts again at every tile.
     // Causal runs mask the tiles that reach above some of the block's keys,
-    // behind a uniform branch: two copies of this code (masked and not) do
-    // not fit the registers together.
+    // on S at the end of each step's A segment, behind a uniform branch: two
+    // copies of this code (masked and not) do not fit the registers together.
     constexpr int NS = KC, NGR = 2 * NB;
     constexpr int NOPS = NSTEP * (2 * NS) + NSTEP * NGR;
     constexpr int LA = KW == 32 ? 1 : 2;
@@ -1365,13 +1365,25 @@ bwd_dkdv16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
         };
         // P of step s, key block j, over S: element (j, i) is key kw0 + 16 j +
         // l16 and query row i0 + 16 s + 4 q4 + i.
-        auto exp_block = [&](int s, int j) {
+        auto exp_block = [&](int j) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) sa[j][i] = fast_exp2(__builtin_fmaf(sa[j][i], cS, -lse4[i]));
+        };
+        // Causal tiles that reach above some of the keys: S of step s set to
+        // -inf there (so that P = 0), all key blocks behind one uniform
+        // branch. The empty assembly gives each step's comparisons an operand
+        // of their own: equal thresholds of different steps would otherwise
+        // be merged into comparisons ahead of the first branch, on the path
+        // of the tiles that need no mask.
+        auto mask_step = [&](int s) {
             if (CAUSAL && mask_tile) {
+                int dl = dlt;
+                asm volatile("" : "+v"(dl));
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (dlt > 16 * (s - j) + i) sa[j][i] = 0.f;
+                for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (dl > 16 * (s - j) + i) sa[j][i] = kNegInf;
             }
         };
         // dS = P (dP - D) of key block j, and both packed to fp16
@@ -1416,6 +1428,7 @@ bwd_dkdv16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
                 // A(s): the swaps of step s-1
                 if (op.s >= 1 && op.x == 0) swap_block(0);
                 if (NH > 1 && op.s >= 1 && op.x == NS - 1) swap_block(NH - 1);
+                if (op.x == NS - 1) mask_step(op.s);
             } else if (op.kind == 1) {
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) {
@@ -1425,7 +1438,7 @@ bwd_dkdv16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
                 if (op.x == NS - 1 && op.s == 0) {
                     // C(0): no products to run under
 #pragma unroll
-                    for (int j = 0; j < NJ; ++j) exp_block(0, j);
+                    for (int j = 0; j < NJ; ++j) exp_block(j);
 #pragma unroll
                     for (int j = 0; j < NJ; ++j) ds_block(j);
                     load_stats(1);
@@ -1445,7 +1458,7 @@ bwd_dkdv16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
                     const int sn = op.s + 1;
 #pragma unroll
                     for (int j = op.x * NJ / NB; j < (op.x + 1) * NJ / NB; ++j) {
-                        if (op.kind == 2) exp_block(sn, j);
+                        if (op.kind == 2) exp_block(j);
                         else ds_block(j);
                     }
                     if (op.kind == 3 && op.x == NB - 1 && sn < NSTEP - 1) load_stats(sn + 1);
@@ -1683,7 +1696,8 @@ bwd_dq16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     // Step 0's C has no products (its vector work runs alone) and step 3's dQ
     // follows the last C. Each fragment is read LA operations ahead through a
     // ring of registers that starts again at every tile. Tiles that need a
-    // mask run it behind a uniform branch.
+    // mask run it on S at the end of each step's A segment, behind a uniform
+    // branch.
     constexpr int NS = KC, NGR = NB;
     constexpr int NOPS = NSTEP * (2 * NS) + NSTEP * NGR;
     constexpr int LA = 2;
@@ -1732,18 +1746,29 @@ bwd_dq16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 return rows_tr_frag<D>(base + OFF_K, 16 * op.s + 8 * g, 32 * op.x, lane);
             return *(const lds_u32x4_t*)(base + OFF_KT + img_offset(32 * op.x + l32, 2 * op.s + g));
         };
-        // P of step s, query block j (over S), then dS = P (dP - D) packed
-        auto ds_block = [&](int s, int j) {
+        // P of query block j (over S), then dS = P (dP - D) packed
+        auto ds_block = [&](int j) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) sa[j][i] = fast_exp2(__builtin_fmaf(sa[j][i], cS, -lse2[j]));
-            if (mask_tile) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (kq + 16 * s + i >= Nk || (CAUSAL && dlt + 16 * (s - j) + i > 0))
-                        sa[j][i] = 0.f;
-            }
             dp[j][0] = pack_f16x2(sa[j][0] * da[j][0], sa[j][1] * da[j][1]);
             dp[j][1] = pack_f16x2(sa[j][2] * da[j][2], sa[j][3] * da[j][3]);
+        };
+        // Tiles that need a mask: S of step s set to -inf where masked (so
+        // that P = 0), all query blocks behind one uniform branch. The empty
+        // assembly gives each step's comparisons operands of their own:
+        // equal thresholds of different steps would otherwise be merged into
+        // comparisons ahead of the first branch, on the path of the tiles
+        // that need no mask.
+        auto mask_step = [&](int s) {
+            if (mask_tile) {
+                int kl = Nk - kq, dl = dlt;
+                asm volatile("" : "+v"(kl), "+v"(dl));
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (16 * s + i >= kl || (CAUSAL && dl + 16 * (s - j) + i > 0)) sa[j][i] = kNegInf;
+            }
         };
         // Query blocks 2h, 2h+1 -> the 32-query block h in the 32x32 B layout.
         auto swap_block = [&](int h) {
@@ -1773,6 +1798,7 @@ bwd_dq16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 // A(s): the swaps of step s-1
                 if (op.s >= 1 && op.x == 0) swap_block(0);
                 if (NH > 1 && op.s >= 1 && op.x == NS - 1) swap_block(NH - 1);
+                if (op.x == NS - 1) mask_step(op.s);
             } else if (op.kind == 1) {
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) {
@@ -1784,7 +1810,7 @@ bwd_dq16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 if (op.x == NS - 1 && op.s == 0) {
                     // C(0): no products to run under
 #pragma unroll
-                    for (int j = 0; j < NJ; ++j) ds_block(0, j);
+                    for (int j = 0; j < NJ; ++j) ds_block(j);
                 }
             } else {
 #pragma unroll
@@ -1792,7 +1818,7 @@ bwd_dq16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 // C(s) = dQ(s-1): dS of step s = op.s + 1
                 if (op.s < NSTEP - 1) {
 #pragma unroll
-                    for (int j = op.x * NJ / NB; j < (op.x + 1) * NJ / NB; ++j) ds_block(op.s + 1, j);
+                    for (int j = op.x * NJ / NB; j < (op.x + 1) * NJ / NB; ++j) ds_block(j);
                 }
                 // before the last step's dQ: its swaps (no S segment follows)
                 if (op.s == NSTEP - 2 && op.x == NB - 1) {
