@@ -78,6 +78,11 @@ constexpr int kDkdvFragAhead = FA_BWD_DKDV_FRAG_AHEAD;
 #define FA_DQ_TR 1
 #endif
 constexpr bool dq16_tr(int D) { return FA_DQ_TR != 0 && D == 256; }
+// The dK/dV pass with 16-row steps forms its fragment addresses once per tile
+// at d = 128 and 256, the dQ pass with 16-row steps at d = 256.
+#ifndef FA_DKDV_PRE
+#define FA_DKDV_PRE 1
+#endif
 
 // Vector-memory wait (the global-to-LDS copies) and a workgroup barrier that
 // lets LDS reads stay in flight across it (__syncthreads waits for them). The
@@ -1099,18 +1104,21 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(const u32x4_t& a, const u32x4_t&
 // i%4; so lane i addresses row base + i/4, columns cb + 4 (i%4) .. +3, with
 // cb = c0 + 16 ((l/16) % 2) and base = r0 + 8 (l/32) (then + 4).
 template <int D>
-__device__ __forceinline__ u32x4_t rows_tr_frag(const lds_char* tile, int r0, int c0, int lane) {
+__device__ __forceinline__ int rows_tr_offset(int r0, int c0, int lane, int half) {
     const int i = lane & 15;
     const int col = c0 + 16 * ((lane >> 4) & 1) + 4 * (i & 3);
-    const int r1 = r0 + (i >> 2), r2 = r1 + 4;
-    const int o1 = rows_offset<D, true>(r1, col >> 3) + ((col & 7) << 1);
-    const int o2 = rows_offset<D, true>(r2, col >> 3) + ((col & 7) << 1);
-    const i16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) i16x4_t*)(tile + o1));
-    const i16x4_t y = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) i16x4_t*)(tile + o2));
+    return rows_offset<D, true>(r0 + (i >> 2) + 4 * half, col >> 3) + ((col & 7) << 1);
+}
+// The two reads at byte addresses p1, p2 of LDS.
+__device__ __forceinline__ u32x4_t tr_frag_at(const lds_char* p1, const lds_char* p2) {
+    const i16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)p1);
+    const i16x4_t y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)p2);
     const u32x2_t ux = __builtin_bit_cast(u32x2_t, x), uy = __builtin_bit_cast(u32x2_t, y);
     return u32x4_t{ux[0], ux[1], uy[0], uy[1]};
+}
+template <int D>
+__device__ __forceinline__ u32x4_t rows_tr_frag(const lds_char* tile, int r0, int c0, int lane) {
+    return tr_frag_at(tile + rows_tr_offset<D>(r0, c0, lane, 0), tile + rows_tr_offset<D>(r0, c0, lane, 1));
 }
 
 // Waves of the pass below: one per SIMD with 64 keys per wave or at d = 256,
@@ -1175,6 +1183,9 @@ bwd_dkdv16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
     // otherwise the bf16 rows of Q and dO, then their transposed fp16 images.
     constexpr int NT = TR ? 2 : 4;       // tensors per tile
     constexpr int OFF_Q = 0, OFF_DO = TB, OFF_QT = 2 * TB, OFF_DOT = 3 * TB;
+    // Fragment addresses formed once per tile (below; rows of 256 bytes or
+    // more)
+    constexpr bool PRE = TR && D >= 128 && FA_DKDV_PRE != 0;
     constexpr int BUF = NT * TB;
     // A statistics copy fills 1 KB of LDS (512 bytes of values, then lanes
     // repeating the last chunk).
@@ -1342,9 +1353,36 @@ bwd_dkdv16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
         // when dlt > 16 (s - j) + i.
         const int dlt = kw0 + l16 - i0 - 4 * q4 - off;
 
+        // PRE: the lane's fragment addresses of step 0 and of the first four
+        // 32-column blocks in this tile's buffer, once per tile. The
+        // swizzles of rows of 256 bytes or more take a row's four low bits
+        // into a chunk's four low bits, so a step's rows lie a constant 16
+        // rows further and column block x + 4 a constant 256 bytes further:
+        // each read is one instruction with an immediate offset. Pinned, so
+        // that they are kept rather than rebuilt at every read.
+        int pr[PRE ? 4 : 1], pt[PRE ? 4 : 1][2];
+        if constexpr (PRE) {
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                pr[x] = b * BUF + rows_offset<D, TR>(l16, 4 * x + q4);
+                keep_here(pr[x]);
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    pt[x][k] = b * BUF + rows_tr_offset<D>(8 * g, 32 * x, lane, k);
+                    keep_here(pt[x][k]);
+                }
+            }
+        }
         auto frag = [&](int o) -> u32x4_t {
             const Op op = op_of(o);
             const lds_char* base = (lds_char*)smem + b * BUF;
+            if constexpr (PRE) {
+                const lds_char* s0 = (lds_char*)smem + 16 * op.s * (D * 2) + 256 * (op.x >> 2);
+                if (op.kind < 2)
+                    return *(const lds_u32x4_t*)(s0 + pr[op.x & 3] + (op.kind == 0 ? OFF_Q : OFF_DO));
+                const int t0 = op.kind == 2 ? OFF_DO : OFF_Q;
+                return tr_frag_at(s0 + pt[op.x & 3][0] + t0, s0 + pt[op.x & 3][1] + t0);
+            }
             if (op.kind < 2)
                 return *(const lds_u32x4_t*)(base + (op.kind == 0 ? OFF_Q : OFF_DO) +
                                              rows_offset<D, TR>(16 * op.s + l16, 4 * op.x + q4));
@@ -1591,6 +1629,8 @@ bwd_dq16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     // (ds_read_b64_tr_b16); otherwise K and V rows, then the K~^T image.
     constexpr int NT = TR ? 2 : 3;       // tensors per tile
     constexpr int OFF_K = 0, OFF_V = TB, OFF_KT = 2 * TB;
+    // Fragment addresses formed once per tile (below)
+    constexpr bool PRE = TR && D == 256 && FA_DKDV_PRE != 0;
     constexpr int BUF = NT * TB;
     __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
 
@@ -1733,9 +1773,34 @@ bwd_dq16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         const int dlt = j0 + 4 * q4 - qw0 - l16 - off;
         const int kq = j0 + 4 * q4;
 
+        // PRE (d = 256): the lane's fragment addresses of step 0 and of the
+        // first four 32-column blocks in this tile's buffer, once per tile,
+        // as in the dK/dV pass (rows of 512 bytes: a step's rows lie 16 rows
+        // further, column block x + 4 256 bytes further). Pinned.
+        int pk_[PRE ? 4 : 1], pv_[PRE ? 4 : 1], pt[PRE ? 4 : 1][2];
+        if constexpr (PRE) {
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                pk_[x] = b * BUF + OFF_K + rows_offset<D, TR>(l16, 4 * x + q4);
+                pv_[x] = b * BUF + OFF_V + row_chunk_offset<D>(l16, 4 * x + q4);
+                keep_here(pk_[x]);
+                keep_here(pv_[x]);
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    pt[x][k] = b * BUF + OFF_K + rows_tr_offset<D>(8 * g, 32 * x, lane, k);
+                    keep_here(pt[x][k]);
+                }
+            }
+        }
         auto fragment = [&](int o) -> u32x4_t {
             const Op op = op_of(o);
             const lds_char* base = (lds_char*)smem + b * BUF;
+            if constexpr (PRE) {
+                const lds_char* s0 = (lds_char*)smem + 16 * op.s * (D * 2) + 256 * (op.x >> 2);
+                if (op.kind == 0) return *(const lds_u32x4_t*)(s0 + pk_[op.x & 3]);
+                if (op.kind == 1) return *(const lds_u32x4_t*)(s0 + pv_[op.x & 3]);
+                return tr_frag_at(s0 + pt[op.x & 3][0], s0 + pt[op.x & 3][1]);
+            }
             if (op.kind == 0)
                 return *(const lds_u32x4_t*)(base + OFF_K +
                                              rows_offset<D, TR>(16 * op.s + l16, 4 * op.x + q4));

@@ -131,6 +131,7 @@ __device__ __forceinline__ void mfma_bf16_last(f32x16_t& acc, const u32x4_t& a, 
 // where it is used, past the barriers and products it was interleaved with.
 __device__ __forceinline__ void keep_here(u32x4_t& x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ void keep_here(float& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void keep_here(int& x) { asm volatile("" : "+v"(x)); }
 
 // Moves a loop-invariant matrix operand into AGPRs once, so that products
 // taking it through an "a" operand read it there instead of copying it from
