@@ -325,6 +325,17 @@ struct Tile64 {
 // that 16 consecutive rows reading one chunk cover every bank once.
 __device__ __forceinline__ int img32_offset(int n, int c) { return 64 * n + 16 * (c ^ ((n >> 2) & 3)); }
 
+// The K images of the dQ pass with 16-row steps at d <= 128, in step order:
+// the 16-byte chunk c (keys 8c .. 8c+7 of the 64-key tile) of row n sits at
+// (c/2) 32 D + 32 n + 16 (c%2), i.e. the tile's four 16-key steps one after
+// the other, each a [D][16] block of 32-byte rows. Eight consecutive rows
+// reading one chunk cover every bank once, and a fragment of step s or of
+// row block 32 x lies a constant distance from that of step 0, row block 0.
+template <int D>
+__device__ __forceinline__ int kt_step_offset(int n, int c) {
+    return (c >> 1) * (32 * D) + 32 * n + 16 * (c & 1);
+}
+
 
 // Phase 1c: fp16 transposed images. One workgroup per (head, 64-row tile,
 // column part): the first BH*Tq tiles are the Q images of the query heads,
@@ -336,8 +347,8 @@ __device__ __forceinline__ int img32_offset(int n, int c) { return 64 * n + 16 *
 // per lane: for head sizes up to 128 it keeps the rows of the Q and dO images
 // in their own order, and at d = 256 it writes them as the [256][32] halves
 // of img32_offset. Bit 1 does the same for the K images when the dQ pass is
-// the one with 16-row steps (bwd_dq16_kernel). Every other image uses the
-// permuted row order.
+// the one with 16-row steps (bwd_dq16_kernel), at d <= 128 in the step order
+// of kt_step_offset. Every other image uses the permuted row order.
 template <int DT>
 __global__ void __launch_bounds__(256)
 bwd_image_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -392,6 +403,16 @@ bwd_image_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         return;
     }
     char* out = dst + (((size_t)head * T + tile) * NP + part) * TileT::BYTES;
+    if (DT <= 128 && which == 2 && (natural & 2)) {
+        // the K image of the dQ pass with 16-row steps, in the step order of
+        // kt_step_offset: chunk i holds step i / 2D, row (i % 2D) / 2, half i % 2
+#pragma unroll
+        for (int i = threadIdx.x; i < TileT::BYTES / 16; i += 256) {
+            const int st = i / (2 * D), n = (i % (2 * D)) >> 1, c = 2 * st + (i & 1);
+            *(u32x4_t*)(out + 16 * i) = *(const u32x4_t*)(img + tr_slot_offset(n, 2 * c));
+        }
+        return;
+    }
 #pragma unroll
     for (int i = threadIdx.x; i < TileT::BYTES / 16; i += 256)
         *(u32x4_t*)(out + 16 * i) = *(const u32x4_t*)(img + 16 * i);
@@ -1631,6 +1652,7 @@ bwd_dq16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     constexpr int OFF_K = 0, OFF_V = TB, OFF_KT = 2 * TB;
     // Fragment addresses formed once per tile (below)
     constexpr bool PRE = TR && D == 256 && FA_DKDV_PRE != 0;
+    constexpr bool PREI = !TR && D <= 128 && FA_DKDV_PRE != 0;
     constexpr int BUF = NT * TB;
     __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
 
@@ -1761,7 +1783,7 @@ bwd_dq16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     // Byte offset of 16-byte chunk c (keys 8c .. 8c+7 of the tile) of row n of
     // the K~^T image.
     auto img_offset = [](int n, int c) -> int {
-        return D == 256 ? img32_offset(n, c) : tr_slot_offset(n, 2 * c);
+        return D == 256 ? img32_offset(n, c) : kt_step_offset<D>(n, c);
     };
     auto tile = [&](int t, int b, bool mask_tile) {
         const int j0 = t * BC;
@@ -1777,6 +1799,22 @@ bwd_dq16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         // first four 32-column blocks in this tile's buffer, once per tile,
         // as in the dK/dV pass (rows of 512 bytes: a step's rows lie 16 rows
         // further, column block x + 4 256 bytes further). Pinned.
+        // PREI (d <= 128): the lane's K~^T image address of step 0, row
+        // block 0 (kt_step_offset), and at d = 128 its K and V row addresses
+        // of step 0 (the row swizzle of 256-byte rows acts on a row's four low
+        // bits, so a step's rows lie 16 rows further). Pinned.
+        int pr_[PREI && D == 128 ? 4 : 1], pim = 0;
+        if constexpr (PREI) {
+            pim = b * BUF + OFF_KT + 32 * l32 + 16 * g;
+            keep_here(pim);
+            if constexpr (D == 128) {
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    pr_[x] = b * BUF + row_chunk_offset<D>(l16, 4 * x + q4);
+                    keep_here(pr_[x]);
+                }
+            }
+        }
         int pk_[PRE ? 4 : 1], pv_[PRE ? 4 : 1], pt[PRE ? 4 : 1][2];
         if constexpr (PRE) {
 #pragma unroll
@@ -1800,6 +1838,13 @@ bwd_dq16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 if (op.kind == 0) return *(const lds_u32x4_t*)(s0 + pk_[op.x & 3]);
                 if (op.kind == 1) return *(const lds_u32x4_t*)(s0 + pv_[op.x & 3]);
                 return tr_frag_at(s0 + pt[op.x & 3][0], s0 + pt[op.x & 3][1]);
+            }
+            if constexpr (PREI) {
+                if (op.kind == 2)
+                    return *(const lds_u32x4_t*)((lds_char*)smem + pim + op.s * (32 * D) + op.x * 1024);
+                if constexpr (D == 128)
+                    return *(const lds_u32x4_t*)((lds_char*)smem + 16 * op.s * (D * 2) + pr_[op.x] +
+                                                 (op.kind == 0 ? OFF_K : OFF_V));
             }
             if (op.kind == 0)
                 return *(const lds_u32x4_t*)(base + OFF_K +
