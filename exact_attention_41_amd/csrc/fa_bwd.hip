@@ -80,6 +80,11 @@ constexpr int kDkdvFragAhead = FA_BWD_DKDV_FRAG_AHEAD;
 constexpr bool dq16_tr(int D) { return FA_DQ_TR != 0 && D == 256; }
 // The dK/dV pass with 16-row steps forms its fragment addresses once per tile
 // at d = 128 and 256, the dQ pass with 16-row steps at d = 256.
+// The dQ pass with 16-row steps writes the fp16 Q and dO rows of the dK/dV
+// pass (when both passes have 16-row steps); 0: the image pass does.
+#ifndef FA_ROWS_FROM_DQ
+#define FA_ROWS_FROM_DQ 1
+#endif
 #ifndef FA_DKDV_PRE
 #define FA_DKDV_PRE 1
 #endif
@@ -348,17 +353,19 @@ __device__ __forceinline__ int kt_step_offset(int n, int c) {
 // in their own order, and at d = 256 it writes them as the [256][32] halves
 // of img32_offset. Bit 1 does the same for the K images when the dQ pass is
 // the one with 16-row steps (bwd_dq16_kernel), at d <= 128 in the step order
-// of kt_step_offset. Every other image uses the permuted row order.
+// of kt_step_offset. Every other image uses the permuted row order. The grid
+// starts at tile bid0: 2 BH Tq for the K images alone (when the dQ pass
+// writes the Q and dO rows).
 template <int DT>
 __global__ void __launch_bounds__(256)
 bwd_image_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                  const uint16_t* __restrict__ dO, const float* __restrict__ scales,
                  char* __restrict__ qt, char* __restrict__ ot, char* __restrict__ kt, int BH,
-                 int G, int Nq, int Nk, int Tq, int Tk, int natural) {
+                 int G, int Nq, int Nk, int Tq, int Tk, int natural, int bid0) {
     constexpr int D = DT > 128 ? 128 : DT;
     constexpr int NP = DT / D;
     using TileT = Tile64<D, 256, DT>;
-    const int bid = blockIdx.x / NP, part = blockIdx.x % NP;
+    const int bid = bid0 + blockIdx.x / NP, part = blockIdx.x % NP;
     const int qblocks = BH * Tq;
     const int which = bid < qblocks ? 0 : (bid < 2 * qblocks ? 1 : 2);
     const int rel = bid - (which < 2 ? which * qblocks : 2 * qblocks);
@@ -1629,8 +1636,9 @@ bwd_dq16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                 const float* __restrict__ LSE, const float* __restrict__ scales,
                 const float* __restrict__ dvals, const char* __restrict__ kt_img,
-                float* __restrict__ stats, uint16_t* __restrict__ dQ, int BH, int G, int N,
-                int Nk, int T, int Tk, float c, float scale, int nqb) {
+                float* __restrict__ stats, uint16_t* __restrict__ dQ,
+                uint16_t* __restrict__ q_rows, uint16_t* __restrict__ do_rows, int BH, int G,
+                int N, int Nk, int T, int Tk, float c, float scale, int nqb) {
     static_assert(D == 64 || D == 128 || (D == 256 && QW == 32),
                   "the dQ sums and the resident Q, dO of a wave fit its registers");
     static_assert(QW == 64 || QW == 32, "query rows per wave");
@@ -1970,6 +1978,32 @@ bwd_dq16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             st[64 + 16 * j + l16] = -dhs[j];
         }
     }
+    // The fp16 rows of s_Q Q and s_dO dO for the dK/dV pass ([T * 64][D] per
+    // head), from the resident operands (s_dO dO = (sE dO) / s_V exactly).
+    // Written at the end rather than where the rows are loaded: a wave's
+    // first wait for its tile copies would also wait for these stores. (Not
+    // at d = 64: there the code alone takes registers that two waves per
+    // SIMD need.)
+    if (D >= 128 && q_rows != nullptr) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int qi = qw0 + 16 * j + l16;
+            if (qi < N) {
+#pragma unroll
+                for (int kc = 0; kc < KC; ++kc) {
+                    const size_t at = ((size_t)bh * T * 64 + qi) * D + 32 * kc + 8 * q4;
+                    u32x4_t fq, fo;
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        fq[w] = TR ? qr[kc][j][w] : bf16x2_to_f16x2(qr[kc][j][w], sQ);
+                        fo[w] = bf16x2_to_f16x2(orr[kc][j][w], 1.f / sV);
+                    }
+                    *(u32x4_t*)(q_rows + at) = fq;
+                    *(u32x4_t*)(do_rows + at) = fo;
+                }
+            }
+        }
+    }
     const float f = scale / (sK * sE);
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
@@ -2023,6 +2057,13 @@ static bool use_dq16(const BwdArgs& a) {
     return (long long)((a.N + 255) / 256) * a.B * a.H >= 512;
 }
 static int k_tiles64(const BwdArgs& a) { return (a.Nk + 63) / 64; }
+// The fp16 rows of s_Q Q and s_dO dO that the dK/dV pass with 16-row steps
+// reads are written by the dQ pass with 16-row steps, which loads those rows
+// anyway, when both passes run at d = 128 or 256 (otherwise by the image pass:
+// at d = 64 the stores cost the shorter dQ pass more than they save).
+static bool rows_from_dq(const BwdArgs& a) {
+    return FA_ROWS_FROM_DQ != 0 && FA_DKDV_TR != 0 && a.d >= 128 && use_dq16(a) && use_dkdv16(a);
+}
 // Column parts of a head (128 columns each above d = 128).
 static int col_parts(int d) { return d > 128 ? d / 128 : 1; }
 
@@ -2044,14 +2085,18 @@ static hipError_t launch_prepare_t(const BwdArgs& a) {
                        (const uint32_t*)partial, ws_ptr<float>(a, w.scales), BH, G, chunks);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_image_kernel<D>), dim3((2 * BH * Tq + BHkv * Tk) * col_parts(D)),
-                       dim3(256), 0,
+    // (the Q and dO rows come from the dQ pass when both passes have 16-row
+    // steps: then only the K images are made here)
+    const int first = rows_from_dq(a) ? 2 * BH * Tq : 0;
+    hipLaunchKernelGGL((bwd_image_kernel<D>),
+                       dim3((2 * BH * Tq + BHkv * Tk - first) * col_parts(D)), dim3(256), 0,
                        a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                        (const uint16_t*)a.dout, ws_ptr<const float>(a, w.scales),
                        ws_ptr<char>(a, w.qt), ws_ptr<char>(a, w.ot), ws_ptr<char>(a, w.kt), BH,
                        G, a.N, a.Nk, Tq, Tk,
                        (use_dkdv16(a) ? (FA_DKDV_TR ? 4 : 1) : 0) |
-                           (use_dq16(a) ? (dq16_tr(D) ? 8 : 2) : 0));
+                           (use_dq16(a) ? (dq16_tr(D) ? 8 : 2) : 0),
+                       first);
     return hipGetLastError();
 }
 
@@ -2072,7 +2117,10 @@ static hipError_t launch_dq_t(const BwdArgs& a) {
                            (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse,
                            ws_ptr<const float>(a, w.scales), ws_ptr<const float>(a, w.dhat),
                            ws_ptr<const char>(a, w.kt), ws_ptr<float>(a, w.stats),
-                           (uint16_t*)a.dq, BH, a.H / a.Hkv, a.N, a.Nk, q_tiles64(a),
+                           (uint16_t*)a.dq,
+                           rows_from_dq(a) ? ws_ptr<uint16_t>(a, w.qt) : (uint16_t*)nullptr,
+                           rows_from_dq(a) ? ws_ptr<uint16_t>(a, w.ot) : (uint16_t*)nullptr,
+                           BH, a.H / a.Hkv, a.N, a.Nk, q_tiles64(a),
                            k_tiles64(a), a.scale * kLog2e, a.scale, nqb);
         return hipGetLastError();
     }

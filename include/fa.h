@@ -338,7 +338,9 @@ fa_status_t fa_decode_noalloc(const void* q, const void* k, const void* v, void*
  *                      the scaled fp16 transposed copies of q, dout and k ->
  *                      workspace.
  *   fa_bwd_dq          writes dq; leaves lse and D per query row in the
- *                      workspace. d_ready must be nonzero exactly when the
+ *                      workspace (and, for some shapes, the scaled fp16 copies
+ *                      of q and dout that the preprocess then leaves out).
+ *                      d_ready must be nonzero exactly when the
  *                      preprocess of this workspace was given o_res: it
  *                      selects the pass that takes D from the workspace, and
  *                      the preprocess lays out the workspace for that pass
