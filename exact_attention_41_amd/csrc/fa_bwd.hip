@@ -1709,6 +1709,20 @@ bwd_dq16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             const u32x4_t v = *(const u32x4_t*)(dO + head + row * D + 32 * kc + 8 * q4);
 #pragma unroll
             for (int w = 0; w < 4; ++w) orr[kc][j][w] = bf16x2_scale(v[w], sE);
+            // The fp16 rows of s_Q Q and s_dO dO for the dK/dV pass ([T * 64][D]
+            // per head). (Not at d = 64: there the code takes registers that
+            // two waves per SIMD need.)
+            if (D >= 128 && q_rows != nullptr && qi < N) {
+                const size_t at = ((size_t)bh * T * 64 + qi) * D + 32 * kc + 8 * q4;
+                u32x4_t fq, fo;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    fq[w] = TR ? qr[kc][j][w] : bf16x2_to_f16x2(qv[w], sQ);
+                    fo[w] = bf16x2_to_f16x2(v[w], sDO);
+                }
+                *(u32x4_t*)(q_rows + at) = fq;
+                *(u32x4_t*)(do_rows + at) = fo;
+            }
         }
         const float lse_i = (qi < N) ? LSE[(size_t)bh * N + qi] : kNegInf;
         lse2[j] = (lse_i == kNegInf) ? __builtin_huge_valf() : lse_i * kLog2e;
@@ -1976,32 +1990,6 @@ bwd_dq16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         for (int j = 0; j < NJ; ++j) {
             st[16 * j + l16] = lse2[j];
             st[64 + 16 * j + l16] = -dhs[j];
-        }
-    }
-    // The fp16 rows of s_Q Q and s_dO dO for the dK/dV pass ([T * 64][D] per
-    // head), from the resident operands (s_dO dO = (sE dO) / s_V exactly).
-    // Written at the end rather than where the rows are loaded: a wave's
-    // first wait for its tile copies would also wait for these stores. (Not
-    // at d = 64: there the code alone takes registers that two waves per
-    // SIMD need.)
-    if (D >= 128 && q_rows != nullptr) {
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            const int qi = qw0 + 16 * j + l16;
-            if (qi < N) {
-#pragma unroll
-                for (int kc = 0; kc < KC; ++kc) {
-                    const size_t at = ((size_t)bh * T * 64 + qi) * D + 32 * kc + 8 * q4;
-                    u32x4_t fq, fo;
-#pragma unroll
-                    for (int w = 0; w < 4; ++w) {
-                        fq[w] = TR ? qr[kc][j][w] : bf16x2_to_f16x2(qr[kc][j][w], sQ);
-                        fo[w] = bf16x2_to_f16x2(orr[kc][j][w], 1.f / sV);
-                    }
-                    *(u32x4_t*)(q_rows + at) = fq;
-                    *(u32x4_t*)(do_rows + at) = fo;
-                }
-            }
         }
     }
     const float f = scale / (sK * sE);
