@@ -78,8 +78,9 @@ constexpr int kDkdvFragAhead = FA_BWD_DKDV_FRAG_AHEAD;
 #define FA_DQ_TR 1
 #endif
 constexpr bool dq16_tr(int D) { return FA_DQ_TR != 0 && D == 256; }
-// The dK/dV pass with 16-row steps forms its fragment addresses once per tile
-// at d = 128 and 256, the dQ pass with 16-row steps at d = 256.
+// The passes with 16-row steps form their fragment addresses once per tile
+// (the dK/dV pass at every head size, the dQ pass at d <= 128 for its K image
+// and at d = 128 and 256 for its rows).
 // The dQ pass with 16-row steps writes the fp16 Q and dO rows of the dK/dV
 // pass (when both passes have 16-row steps); 0: the image pass does.
 #ifndef FA_ROWS_FROM_DQ
@@ -1211,9 +1212,8 @@ bwd_dkdv16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
     // otherwise the bf16 rows of Q and dO, then their transposed fp16 images.
     constexpr int NT = TR ? 2 : 4;       // tensors per tile
     constexpr int OFF_Q = 0, OFF_DO = TB, OFF_QT = 2 * TB, OFF_DOT = 3 * TB;
-    // Fragment addresses formed once per tile (below; rows of 256 bytes or
-    // more)
-    constexpr bool PRE = TR && D >= 128 && FA_DKDV_PRE != 0;
+    // Fragment addresses formed once per tile (below)
+    constexpr bool PRE = TR && FA_DKDV_PRE != 0;
     constexpr int BUF = NT * TB;
     // A statistics copy fills 1 KB of LDS (512 bytes of values, then lanes
     // repeating the last chunk).
@@ -1381,25 +1381,29 @@ bwd_dkdv16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
         // when dlt > 16 (s - j) + i.
         const int dlt = kw0 + l16 - i0 - 4 * q4 - off;
 
-        // PRE: the lane's fragment addresses of step 0 and of the first four
-        // 32-column blocks in this tile's buffer, once per tile. The
-        // swizzles of rows of 256 bytes or more take a row's four low bits
-        // into a chunk's four low bits, so a step's rows lie a constant 16
-        // rows further and column block x + 4 a constant 256 bytes further:
-        // each read is one instruction with an immediate offset. Pinned, so
-        // that they are kept rather than rebuilt at every read.
-        int pr[PRE ? 4 : 1], pt[PRE ? 4 : 1][2];
+        // PRE: the lane's fragment addresses of step 0 and of the first (up
+        // to) four 32-column blocks in this tile's buffer, once per tile. The
+        // row swizzle depends on a row's four low bits only (and for rows of
+        // 256 bytes or more acts on a chunk's four low bits), so a step's
+        // rows lie a constant 16 rows further and column block x + 4 a
+        // constant 256 bytes further: each read is one instruction with an
+        // immediate offset. Pinned, so that they are kept rather than rebuilt
+        // at every read.
+        constexpr int NXS = NS < 4 ? NS : 4, NXB = NB < 4 ? NB : 4;
+        int pr[PRE ? NXS : 1], pt[PRE ? NXB : 1][2];
         if constexpr (PRE) {
 #pragma unroll
-            for (int x = 0; x < 4; ++x) {
+            for (int x = 0; x < NXS; ++x) {
                 pr[x] = b * BUF + rows_offset<D, TR>(l16, 4 * x + q4);
                 keep_here(pr[x]);
+            }
+#pragma unroll
+            for (int x = 0; x < NXB; ++x)
 #pragma unroll
                 for (int k = 0; k < 2; ++k) {
                     pt[x][k] = b * BUF + rows_tr_offset<D>(8 * g, 32 * x, lane, k);
                     keep_here(pt[x][k]);
                 }
-            }
         }
         auto frag = [&](int o) -> u32x4_t {
             const Op op = op_of(o);

@@ -227,11 +227,14 @@ __device__ __forceinline__ int row_chunk_offset(int row, int chunk) {
 // the XOR takes the row's two low bits into chunk bits 2-3 (and bits 2-3
 // into bits 0-1): four consecutive rows then land in four different 64-byte
 // bank ranges, and 16 consecutive rows reading one chunk still cover every
-// bank once. 128-byte rows keep row_chunk_swizzle.
+// bank once. 128-byte rows take row_chunk_swizzle's pattern of rows 0-15 for
+// every group of 16 rows (the same banks within a group). In both, a row's
+// XOR depends on its four low bits only, so a fragment 16 rows further lies
+// a constant distance further.
 template <int D>
 __device__ __forceinline__ int tr_rows_swizzle(int row) {
     if constexpr (D >= 128) return ((row & 3) << 2) | ((row >> 2) & 3);
-    else return row_chunk_swizzle<D>(row);
+    else return (row & 7) ^ ((row >> 3) & 1);
 }
 
 // Byte offset of 16-byte chunk `chunk` of row `row`: row_chunk_offset, or with
