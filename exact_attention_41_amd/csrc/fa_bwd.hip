@@ -333,13 +333,14 @@ __device__ __forceinline__ int img32_offset(int n, int c) { return 64 * n + 16 *
 
 // The K images of the dQ pass with 16-row steps at d <= 128, in step order:
 // the 16-byte chunk c (keys 8c .. 8c+7 of the 64-key tile) of row n sits at
-// (c/2) 32 D + 32 n + 16 (c%2), i.e. the tile's four 16-key steps one after
-// the other, each a [D][16] block of 32-byte rows. Eight consecutive rows
-// reading one chunk cover every bank once, and a fragment of step s or of
-// row block 32 x lies a constant distance from that of step 0, row block 0.
+// (c/2) 32 D + 32 n + 16 (c%2 ^ bit 3 of n), i.e. the tile's four 16-key
+// steps one after the other, each a [D][16] block of 32-byte rows whose two
+// halves swap every eight rows. Sixteen consecutive rows reading one chunk
+// then cover every bank once, and a fragment of step s or of row block 32 x
+// lies a constant distance from that of step 0, row block 0.
 template <int D>
 __device__ __forceinline__ int kt_step_offset(int n, int c) {
-    return (c >> 1) * (32 * D) + 32 * n + 16 * (c & 1);
+    return (c >> 1) * (32 * D) + 32 * n + 16 * ((c & 1) ^ ((n >> 3) & 1));
 }
 
 
@@ -413,10 +414,12 @@ bwd_image_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     char* out = dst + (((size_t)head * T + tile) * NP + part) * TileT::BYTES;
     if (DT <= 128 && which == 2 && (natural & 2)) {
         // the K image of the dQ pass with 16-row steps, in the step order of
-        // kt_step_offset: chunk i holds step i / 2D, row (i % 2D) / 2, half i % 2
+        // kt_step_offset: chunk i holds step i / 2D, row (i % 2D) / 2, half
+        // i % 2 (chunk c % 2 ^ bit 3 of the row)
 #pragma unroll
         for (int i = threadIdx.x; i < TileT::BYTES / 16; i += 256) {
-            const int st = i / (2 * D), n = (i % (2 * D)) >> 1, c = 2 * st + (i & 1);
+            const int st = i / (2 * D), n = (i % (2 * D)) >> 1;
+            const int c = 2 * st + ((i & 1) ^ ((n >> 3) & 1));
             *(u32x4_t*)(out + 16 * i) = *(const u32x4_t*)(img + tr_slot_offset(n, 2 * c));
         }
         return;
@@ -1831,7 +1834,7 @@ bwd_dq16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         // bits, so a step's rows lie 16 rows further). Pinned.
         int pr_[PREI && D == 128 ? 4 : 1], pim = 0;
         if constexpr (PREI) {
-            pim = b * BUF + OFF_KT + 32 * l32 + 16 * g;
+            pim = b * BUF + OFF_KT + kt_step_offset<D>(l32, g);
             keep_here(pim);
             if constexpr (D == 128) {
 #pragma unroll
