@@ -344,7 +344,7 @@ fa_status_t fa_decode_noalloc(const void* q, const void* k, const void* v, void*
  *                      preprocess of this workspace was given o_res: it
  *                      selects the pass that takes D from the workspace, and
  *                      the preprocess lays out the workspace for that pass
- *                      (a mismatch gives wrong dq).
+ *                      (a mismatch gives wrong gradients).
  *   fa_bwd_dkdv        writes dk and dv from q, k, v, dout and the workspace
  *                      (lse is taken from the workspace).
  */

@@ -209,3 +209,27 @@ def test_backward_phases_equal_fa_bwd(fa):
     torch.cuda.synchronize()
     for a, b, c in ((dq1, dq2, dq3), (dk1, dk2, dk3), (dv1, dv2, dv3)):
         assert torch.equal(a, b) and torch.equal(a, c)
+
+
+@pytest.mark.parametrize("B,H,N,d", [(1, 64, 2048, 128), (1, 32, 1024, 256)])
+def test_backward_phases_wide_grid_equal_fa_bwd(fa, B, H, N, d):
+    """At grids where both matrix passes have 16-row steps (the dQ pass then
+    writes the fp16 Q and dO rows of the dK/dV pass), the three phases with
+    O's residual are exactly fa_bwd with it, and repeated calls are equal."""
+    import torch
+    causal = True
+    say(f"fa_bwd phases wide grid B={B} H={H} N={N} d={d} causal seed=29")
+    inp = wl.make_inputs(B, H, N, d, "bf16", seed=29, with_do=True)
+    q, k, v, do = (wl.to_device(x, "bf16") for x in (inp.q, inp.k, inp.v, inp.do))
+    o_res = torch.empty_like(q)
+    o, lse = fa.fa_fwd(q, k, v, causal=causal, o_res=o_res)
+    dq1, dk1, dv1 = fa.fa_bwd(q, k, v, o, do, lse, causal=causal, o_res=o_res)
+    dq2, dk2, dv2 = fa.fa_bwd(q, k, v, o, do, lse, causal=causal, o_res=o_res)
+    ws = torch.empty(fa.fa_bwd_workspace_size(B, H, N, d), dtype=torch.uint8, device=q.device)
+    dq3, dk3, dv3 = (torch.empty_like(q) for _ in range(3))
+    fa.fa_bwd_preprocess(q, k, v, o, do, ws, o_res=o_res)
+    fa.fa_bwd_dq(q, k, v, do, lse, ws, dq3, causal=causal, d_ready=True)
+    fa.fa_bwd_dkdv(q, k, v, do, ws, dk3, dv3, causal=causal)
+    torch.cuda.synchronize()
+    for a, b, c in ((dq1, dq2, dq3), (dk1, dk2, dk3), (dv1, dv2, dv3)):
+        assert torch.equal(a, b) and torch.equal(a, c)
