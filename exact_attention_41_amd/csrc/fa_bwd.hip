@@ -82,7 +82,8 @@ constexpr bool dq16_tr(int D) { return FA_DQ_TR != 0 && D == 256; }
 // (the dK/dV pass at every head size, the dQ pass at d <= 128 for its K image
 // and at d = 128 and 256 for its rows).
 // The dQ pass with 16-row steps writes the fp16 Q and dO rows of the dK/dV
-// pass (when both passes have 16-row steps); 0: the image pass does.
+// pass (when both passes have 16-row steps, at d = 128 and 256); 0: the image
+// pass does.
 #ifndef FA_ROWS_FROM_DQ
 #define FA_ROWS_FROM_DQ 1
 #endif
@@ -2055,7 +2056,7 @@ static int k_tiles64(const BwdArgs& a) { return (a.Nk + 63) / 64; }
 // The fp16 rows of s_Q Q and s_dO dO that the dK/dV pass with 16-row steps
 // reads are written by the dQ pass with 16-row steps, which loads those rows
 // anyway, when both passes run at d = 128 or 256 (otherwise by the image pass:
-// at d = 64 the stores cost the shorter dQ pass more than they save).
+// at d = 64 the store code takes registers that two dQ waves per SIMD need).
 static bool rows_from_dq(const BwdArgs& a) {
     return FA_ROWS_FROM_DQ != 0 && FA_DKDV_TR != 0 && a.d >= 128 && use_dq16(a) && use_dkdv16(a);
 }
