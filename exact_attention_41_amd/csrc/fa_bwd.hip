@@ -1351,7 +1351,9 @@ bwd_dkdv16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
     // copies of this code (masked and not) do not fit the registers together.
     constexpr int NS = KC, NGR = 2 * NB;
     constexpr int NOPS = NSTEP * (2 * NS) + NSTEP * NGR;
-    constexpr int LA = KW == 32 ? 1 : 2;
+    // (look-ahead 3 at d = 256, where 128 keys per workgroup leave the
+    // registers for it; 2 otherwise)
+    constexpr int LA = D == 256 ? 3 : 2;
     // Operation o: kind (0 Q, 1 dO, 2 dO~^T, 3 Q~^T), step, chunk or block.
     struct Op { int kind, s, x; };
     auto op_of = [](int o) constexpr -> Op {
